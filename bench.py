@@ -1,0 +1,489 @@
+#!/usr/bin/env python3
+"""RMSNorm forward + backward benchmark on one MI355X.
+
+A step is one pass of the whole path over one batch: the forward
+(y, rstd), then the backward row kernel (dx and dW partials) and the
+fixed-order dW combine, all through the C ABI on one HIP stream.
+
+Measurement, following the Quack Hopper study ("What a tuned RMSNorm kernel
+actually costs on Hopper", section 02):
+  * the roofline denominator is measured in the same run: the best of a
+    copy, a pure write and a two-read-one-write probe over 2 GiB buffers,
+    probed again at the end; the closing/opening ratio flags a drifting
+    (shared) device;
+  * inputs rotate through R cloned sets that together exceed the last-level
+    caches, and the backward of step k uses a different set than its
+    forward, so no kernel reads data an earlier kernel just left in cache;
+  * outputs are validated against the fp64 oracle before and after timing;
+  * bytes are the algorithmic bytes the operation must touch (read x, w;
+    write y, rstd for the forward; read x, dy, w, rstd and write dx, dW for
+    the backward), never the dW partial traffic the kernels add.
+Per-kernel times come from HIP events recorded around each launch inside the
+timed region. A second, isolated measurement times single calls with a
+1 GiB cache-flushing copy before each (median of 50).
+
+`python bench.py` prints one JSON line. `--gpus N` with N > 1 exits: this
+build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RMSNorm fwd/bwd achieved GB/s and % of measured HBM roofline, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+GIB = 1 << 30
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="bf16_16384x4096")
+    ap.add_argument("--sets", type=int, default=0, help="rotation sets (0: enough to exceed 1.5 GiB, at least 4)")
+    ap.add_argument("--probe-gib", type=float, default=2.0)
+    ap.add_argument("--isolated-reps", type=int, default=50)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="time budget of the CPU-baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (profiling runs)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "kernels", "copy"],
+                    help="bench: full run; kernels: only the timed steps (for profilers); "
+                         "copy: one probe copy of --probe-gib (counter calibration)")
+    ap.add_argument("--out-dir", default=os.environ.get("RMSN_BENCH_OUT", os.path.join(ROOT, "bench_out")))
+    return ap.parse_args(argv)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources: counter-derived traffic is only reused for this exact code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "memory_bound_normalization_rmsnorm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def git_rev() -> str:
+    try:
+        return subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"], capture_output=True,
+                              text=True, check=True).stdout.strip()
+    except Exception:
+        return "unknown"
+
+
+def smi_snapshot() -> dict:
+    """GPU utilisation / VRAM as reported by the management tool (the run
+    records it; a busy device makes every ratio suspect)."""
+    for cmd in (["amd-smi", "metric", "--usage", "--mem-usage", "--json"],
+                ["rocm-smi", "--showuse", "--showmemuse", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            if r.returncode == 0 and r.stdout.strip():
+                return {"tool": cmd[0], "raw": r.stdout.strip()[:4000]}
+        except Exception:
+            continue
+    return {"tool": None, "raw": "unavailable"}
+
+
+def cpu_info() -> dict:
+    model = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except Exception:
+        avail = os.cpu_count()
+    return {"model": model, "logical_cpus_available": avail}
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def median_ms(self, fn, reps, warmup=3, between=None):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        times = []
+        for _ in range(reps):
+            if between is not None:
+                between()
+            s, e = self.event(), self.event()
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+        torch.cuda.synchronize()
+        return statistics.median(times), times
+
+
+def probe_roofline(torch, rn, timer, gib):
+    """Best of copy, pure write and 2-read-1-write over several grid sizes (GB/s)."""
+    nbytes = int(gib * GIB) // 256 * 256
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    c = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b.fill_(2)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grids = [0, cus * 4, cus * 8, cus * 16, cus * 32]
+    probes = {
+        "copy": (lambda g: rn.rmsn_probe_copy(a, c, nbytes, g), 2 * nbytes),
+        "write": (lambda g: rn.rmsn_probe_write(c, nbytes, g), nbytes),
+        "2r1w": (lambda g: rn.rmsn_probe_add(a, b, c, nbytes, g), 3 * nbytes),
+    }
+    out = {}
+    for name, (fn, moved) in probes.items():
+        best = None
+        for g in grids:
+            med, _ = timer.median_ms(lambda: fn(g), reps=15, warmup=2)
+            gbps = moved / (med * 1e-3) / 1e9
+            if best is None or gbps > best[0]:
+                best = (gbps, g, med)
+        out[name] = {"GBps": round(best[0], 1), "grid": best[1], "median_ms": round(best[2], 4)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    best_name = max(out, key=lambda k: out[k]["GBps"])
+    return {"best_GBps": out[best_name]["GBps"], "best_probe": best_name, "probes": out, "buffer_GiB": gib}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this RMSNorm build runs on one GPU only; "
+                                   "multi-GPU sharding is described in DESIGN.md and not run"}))
+        return 2
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs an MI355X (no GPU visible)")
+    import memory_bound_normalization_rmsnorm_amd as rn
+    import synthetic_inputs as si
+
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    props = torch.cuda.get_device_properties(0)
+
+    if args.mode == "copy":
+        nbytes = int(args.probe_gib * GIB) // 256 * 256
+        a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        c = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        rn.rmsn_probe_copy(a, c, nbytes, 0)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes}))
+        return 0
+
+    wl = si.WORKLOADS[args.workload]
+    dt = rn.F32 if wl.dtype == "f32" else rn.BF16
+    tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    M, N = wl.M, wl.N
+    eps = si.eps_f32(wl.eps)
+    fwd_bytes, bwd_bytes = wl.fwd_bytes(), wl.bwd_bytes()
+    es = 4 if wl.dtype == "f32" else 2
+    rows_bytes = 3 * M * N * es + N * es + 4 * M          # backward row kernel: x, dy, w, rstd in; dx out
+    combine_bytes = 4 * N                                  # algorithmic part of the combine: dW out
+
+    env = {
+        "device": props.name, "gcn_arch": getattr(props, "gcnArchName", "?"),
+        "compute_units": props.multi_processor_count, "hbm_GiB": round(props.total_memory / GIB, 1),
+        "torch": torch.__version__, "hip": torch.version.hip, "library": rn.LIB_PATH,
+        "build_info": rn.rmsnorm_build_info(), "git": git_rev(), "source_hash": source_hash(),
+        "cpu": cpu_info(), "smi_at_start": smi_snapshot(), "workload": wl.description,
+    }
+    log(f"device {props.name} ({props.multi_processor_count} CUs), library {rn.LIB_PATH}")
+
+    do_full = args.mode == "bench"
+    opening = probe_roofline(torch, rn, timer, args.probe_gib) if do_full else None
+    if opening:
+        log(f"opening roofline {opening['best_GBps']} GB/s ({opening['best_probe']})")
+
+    # ---- inputs -------------------------------------------------------------
+    t0 = time.time()
+    x_h, w_h, dy_h = si.make_inputs(wl)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if wl.dtype == "bf16" else torch.from_numpy(a)
+        return t.to("cuda")
+
+    set_bytes = 4 * M * N * es + 4 * M
+    R = args.sets or max(4, -(-int(1.5 * GIB) // set_bytes))
+    w_d = dev(w_h)
+    x0, dy0 = dev(x_h), dev(dy_h)
+    sets = []
+    for k in range(R):
+        sets.append({
+            "x": x0 if k == 0 else x0.clone(), "dy": dy0 if k == 0 else dy0.clone(),
+            "y": torch.empty((M, N), dtype=tdt, device="cuda"), "dx": torch.empty((M, N), dtype=tdt, device="cuda"),
+            "rstd": torch.empty(M, dtype=torch.float32, device="cuda"),
+        })
+    ws_bytes = rn.rmsnorm_bwd_workspace_bytes(M, N, dt)
+    ws = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device="cuda")
+    dw = torch.empty(N, dtype=torch.float32, device="cuda")
+    cfg_f = rn.rmsnorm_query_config(M, N, dt, 0).as_dict()
+    cfg_b = rn.rmsnorm_query_config(M, N, dt, 1).as_dict()
+    log(f"{R} rotation sets; fwd config {cfg_f}; bwd config {cfg_b}")
+
+    def fwd(s):
+        rn.rmsnorm_fwd(s["x"], w_d, eps, M, N, dt, s["y"], s["rstd"])
+
+    def bwd_rows(s):
+        return rn.rmsnorm_bwd_rows(s["x"], w_d, s["dy"], s["rstd"], M, N, dt, s["dx"], ws, ws_bytes)
+
+    def combine(p):
+        rn.rmsnorm_bwd_combine(ws, p, N, dw)
+
+    # rstd of every set (the backward reads the forward's rstd)
+    for s in sets:
+        fwd(s)
+    torch.cuda.synchronize()
+
+    validation = {}
+    cpu_baseline = None
+
+    def to_host(t):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if wl.dtype == "bf16" else t.numpy()
+
+    def snapshot():
+        s = sets[0]
+        fwd(s)
+        combine(bwd_rows(s))
+        torch.cuda.synchronize()
+        return to_host(s["y"]), s["rstd"].cpu().numpy(), to_host(s["dx"]), dw.cpu().numpy()
+
+    if do_full and not args.no_cpu_baseline:
+        before = snapshot()
+        cpu_baseline, oracle_ref = cpu_baseline_leg(wl, x_h, w_h, dy_h, eps, args.cpu_budget_s)
+        validation["before_timing"] = validate(wl, before, oracle_ref, (x_h, w_h, dy_h))
+        log(f"validation before timing: {validation['before_timing']}")
+
+    # ---- timed steps ----------------------------------------------------------
+    K, W = args.steps, args.warmup
+    for k in range(W):
+        fwd(sets[k % R])
+        combine(bwd_rows(sets[(k + R // 2) % R]))
+    torch.cuda.synchronize()
+    ev = [[timer.event() for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(K):
+        e = ev[k]
+        e[0].record()
+        fwd(sets[k % R])
+        e[1].record()
+        p = bwd_rows(sets[(k + R // 2) % R])
+        e[2].record()
+        combine(p)
+        e[3].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    rows_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    step_ms = [e[0].elapsed_time(e[3]) for e in ev]
+    ms_per_step = elapsed * 1e3 / K
+    log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step wall, fwd {statistics.mean(fwd_ms) * 1e3:.1f} us, "
+        f"bwd rows {statistics.mean(rows_ms) * 1e3:.1f} us, combine {statistics.mean(comb_ms) * 1e3:.1f} us")
+
+    if args.mode == "kernels":
+        print(json.dumps({"mode": "kernels", "steps": K, "fwd_us": statistics.mean(fwd_ms) * 1e3,
+                          "bwd_rows_us": statistics.mean(rows_ms) * 1e3, "combine_us": statistics.mean(comb_ms) * 1e3}))
+        return 0
+
+    # ---- isolated calls with a cache flush before each ------------------------
+    flush_n = GIB
+    fa = torch.empty(flush_n, dtype=torch.uint8, device="cuda")
+    fb = torch.empty(flush_n, dtype=torch.uint8, device="cuda")
+    fa.fill_(3)
+
+    def flush():
+        rn.rmsn_probe_copy(fa, fb, flush_n, 0)
+
+    iso_f, _ = timer.median_ms(lambda: fwd(sets[0]), args.isolated_reps, between=flush)
+    iso_b, _ = timer.median_ms(lambda: combine(bwd_rows(sets[0])), args.isolated_reps, between=flush)
+    del fa, fb
+
+    if do_full and not args.no_cpu_baseline:
+        validation["after_timing"] = validate(wl, snapshot(), oracle_ref, (x_h, w_h, dy_h))
+        log(f"validation after timing: {validation['after_timing']}")
+
+    closing = probe_roofline(torch, rn, timer, args.probe_gib)
+    drift = closing["best_GBps"] / opening["best_GBps"]
+    measured = opening["best_GBps"]
+
+    mean = statistics.mean
+    f_us, r_us, c_us = mean(fwd_ms) * 1e3, mean(rows_ms) * 1e3, mean(comb_ms) * 1e3
+    fwd_gbps = fwd_bytes / (f_us * 1e-6) / 1e9
+    bwd_call_us = r_us + c_us
+    bwd_gbps = bwd_bytes / (bwd_call_us * 1e-6) / 1e9
+    rows_gbps = rows_bytes / (r_us * 1e-6) / 1e9
+    value = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9
+
+    traffic = load_traffic(env["source_hash"], "bwd_rows", args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded PCG64 inputs on the host, uploaded once; rotated through cloned device buffers)",
+        "config": {"workload": f"RMSNorm fwd+bwd {wl.dtype} M={M} N={N} eps={wl.eps}", "M": M, "N": N,
+                   "eps": wl.eps, "rotation_sets": R, "fwd_launch": cfg_f, "bwd_launch": cfg_b},
+        "roofline": {
+            "kernel": "bwd_vec (backward row kernel)",
+            "bound": "hbm",
+            "achieved": round(rows_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(rows_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": rows_bytes,
+            "avg_launch_us": round(r_us, 2),
+        },
+        "measured_roofline": {"opening": opening, "closing_GBps": closing["best_GBps"], "drift": round(drift, 4),
+                              "drift_ok": 0.99 <= drift <= 1.01},
+        "fwd": {"avg_us": round(f_us, 2), "GBps": round(fwd_gbps, 1), "pct_measured_roofline": round(100 * fwd_gbps / measured, 1),
+                "algorithmic_bytes": fwd_bytes, "isolated_median_us": round(iso_f * 1e3, 2),
+                "isolated_GBps": round(fwd_bytes / (iso_f * 1e-3) / 1e9, 1)},
+        "bwd": {"avg_us": round(bwd_call_us, 2), "rows_kernel_us": round(r_us, 2), "combine_us": round(c_us, 2),
+                "GBps": round(bwd_gbps, 1), "pct_measured_roofline": round(100 * bwd_gbps / measured, 1),
+                "algorithmic_bytes": bwd_bytes, "isolated_median_us": round(iso_b * 1e3, 2),
+                "isolated_GBps": round(bwd_bytes / (iso_b * 1e-3) / 1e9, 1)},
+        "step_event_us": round(mean(step_ms) * 1e3, 2),
+        "pct_measured_roofline": round(100 * value / measured, 1),
+        "validation": validation,
+        "cpu_baseline": cpu_baseline,
+        "environment": {k: env[k] for k in ("device", "gcn_arch", "compute_units", "hip", "torch", "build_info",
+                                             "git", "source_hash")},
+    }
+    os.makedirs(args.out_dir, exist_ok=True)
+    env["smi_at_end"] = smi_snapshot()
+    with open(os.path.join(args.out_dir, "environment.json"), "w") as f:
+        json.dump(env, f, indent=1)
+    with open(os.path.join(args.out_dir, "result.json"), "w") as f:
+        json.dump(result, f, indent=1)
+    print(json.dumps(result))
+    return 0
+
+
+def load_traffic(src_hash, kernel, workload):
+    """HBM traffic per launch from committed rocprofv3 counter runs, only when
+    they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(f"{kernel}:{workload}")
+    if not entry or entry.get("source_hash") != src_hash:
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline_leg(wl, x, w, dy, eps, budget_s):
+    """The fp64 oracle, as it stands, on this host: forward (y, rstd) and
+    backward dx for consecutive blocks of rows until the time budget is spent
+    (single thread), plus dW over all rows. Its results also serve as the
+    reference the GPU outputs are validated against. Returns (baseline
+    record, reference)."""
+    import numpy as np
+
+    import oracle
+
+    block = 256
+    done = 0
+    t_rows = 0.0
+    ref_rows = {}
+    while done < wl.M and t_rows < budget_s:
+        rows = np.arange(done, min(done + block, wl.M), dtype=np.int64)
+        t0 = time.perf_counter()
+        oy, orr = oracle.fwd(x, w, eps, wl.dtype, rows=rows)
+        odx, _ = oracle.bwd_dx(x, w, dy, eps, wl.dtype, rows=rows)
+        t_rows += time.perf_counter() - t0
+        if len(ref_rows) < 4:  # keep a few blocks for validation
+            ref_rows[int(rows[0])] = (rows, oy, orr, odx)
+        done = int(rows[-1]) + 1
+    t0 = time.perf_counter()
+    _, r_all = oracle.fwd(x, w, eps, wl.dtype, want_y=False)
+    odw = oracle.bwd_dw(x, dy, eps, wl.dtype)
+    t_all = time.perf_counter() - t0
+    es = 4 if wl.dtype == "f32" else 2
+    per_row = (2 * wl.N * es + 4) + (3 * wl.N * es + 4)   # fwd + bwd algorithmic bytes of one row
+    gbps = done * per_row / t_rows / 1e9
+    record = {
+        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"fp64 oracle forward (y, rstd) and backward dx on the first {done} of {wl.M} rows "
+                  f"(bounded to ~{budget_s:.0f}s, single thread); x and w and the row bytes of fwd+bwd counted",
+        "seconds": round(t_rows, 2), "rows": done,
+        "dw_all_rows_seconds": round(t_all, 2),
+    }
+    log(f"cpu baseline: {record}")
+    return record, {"rows": ref_rows, "rstd": r_all, "dw": odw}
+
+
+def validate(wl, gpu, ref, inputs):
+    """Tolerance gates against the oracle: y and dx on the reference row blocks,
+    every rstd, every dW column. A failed gate raises: a wrong kernel gets no
+    number."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_util import check_dw, check_rows, check_rstd, term_rms
+
+    x, w, dy = inputs
+    y, rstd, dx, dw = gpu
+    stats = {"y_max_abs_err": 0.0, "dx_max_abs_err": 0.0}
+    for rows, oy, orr, odx in ref["rows"].values():
+        sy = check_rows(y[rows], oy, wl.dtype, "y")
+        sdx = check_rows(dx[rows], odx, wl.dtype, "dx", floor=term_rms(x, w, dy, orr, wl.dtype, rows=rows))
+        stats["y_max_abs_err"] = max(stats["y_max_abs_err"], sy["max_abs_err"])
+        stats["dx_max_abs_err"] = max(stats["dx_max_abs_err"], sdx["max_abs_err"])
+    check_rstd(rstd, ref["rstd"])
+    check_dw(dw, ref["dw"], wl.dtype)
+    stats["rstd_max_rel_err"] = float(np.max(np.abs(rstd - ref["rstd"]) / ref["rstd"]))
+    stats["dw_max_rel_err"] = float(np.max(np.abs(dw - ref["dw"]) / np.maximum(np.abs(ref["dw"]), 1e-30)))
+    stats["rows_checked"] = int(sum(len(v[0]) for v in ref["rows"].values()))
+    stats["passed"] = True
+    return stats
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,168 @@
+/*
+ * rmsnorm.h -- C ABI of the MI355X (gfx950) RMSNorm library.
+ *
+ * Forward: for each row i of an M x N row-major matrix x,
+ *     rstd_i = 1 / sqrt((1/N) * sum_j x_ij^2 + eps)      (eps inside the root,
+ *     y_ij   = x_ij * rstd_i * w_j                          N the true width)
+ * as defined in hello-gpu "Chapter 13 Fused RMSNorm", section 13.1, and in the
+ * profiling-kernels page, Problem 15 ("The concepts").
+ *
+ * Backward: with V_ij = dy_ij * w_j ("the incoming gradient after applying the
+ * gain", "RMSNorm backward (almost) without the column reduction", section
+ * "The backward pass"),
+ *     dx_ij = rstd_i * V_ij - x_ij * rstd_i^3 * (sum_j V_ij x_ij) / N
+ *     dW_j  = sum_i dy_ij * x_ij * rstd_i
+ * The page's formula images are lost; this is the derivative of the forward
+ * and matches the page's kernels. dW is reduced without atomics in a fixed
+ * order, so it is bit-identical from run to run on the same device (same
+ * page, section "The problem: summing across rows"). The backward reads the
+ * fp32 rstd the forward wrote, as the Quack study describes its backward
+ * ("What a tuned RMSNorm kernel actually costs on Hopper", section 05).
+ *
+ * Conventions for every entry point:
+ *   - x, w, y, dy, dx share one storage dtype (RMSN_F32 or RMSN_BF16); rstd,
+ *     dW and the workspace are always fp32.
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller. Matrices are row-major and contiguous (row stride = N
+ *     elements); w and dW have N elements; rstd has M elements.
+ *   - The library allocates nothing. Its only state is a per-device cache of
+ *     properties (compute-unit count, kernel occupancy).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream). Nothing synchronises the host.
+ *   - Argument checks run before any HIP call. M == 0 is a valid no-op.
+ *   - Any N >= 1 is accepted. 16-byte vector loads are used when
+ *     N * sizeof(elem) is a multiple of 16 and every matrix/vector pointer is
+ *     16-byte aligned; otherwise a scalar path of the same arithmetic runs.
+ *   - y must not alias x; dx must not alias x or dy (undefined behaviour).
+ *   - Return value: RMSN_OK (0) or a negative rmsn_status.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RMSN_F32 = 0,  /* IEEE fp32 storage */
+    RMSN_BF16 = 1  /* bfloat16 storage; outputs are rounded to nearest even */
+} rmsn_dtype;
+
+typedef enum {
+    RMSN_OK = 0,
+    RMSN_EINVAL = -1,      /* null pointer, M < 0, N < 1, eps < 0 or not finite, size overflow */
+    RMSN_EDTYPE = -2,      /* dtype is not an rmsn_dtype */
+    RMSN_EWORKSPACE = -3,  /* workspace null or smaller than rmsnorm_bwd_workspace_bytes() */
+    RMSN_EHIP = -4,        /* a HIP runtime call or kernel launch failed */
+    RMSN_ECONFIG = -5      /* an explicit launch configuration does not fit the shape */
+} rmsn_status;
+
+/*
+ * Launch configuration chosen by the library's ladder (keyed on the row
+ * width, as the Quack analytical ladder is: "What a tuned RMSNorm kernel
+ * actually costs on Hopper", section 03). Reported for logs and tests.
+ */
+typedef struct {
+    int32_t vector_path;     /* 1: 16-byte vector row kernel; 0: scalar row kernel */
+    int32_t lanes_per_row;   /* lanes that share one row (1..1024) */
+    int32_t vecs_per_lane;   /* 16-byte vectors each lane holds per row (vector path) */
+    int32_t wg_threads;      /* workgroup size */
+    int32_t rows_per_wg;     /* rows a workgroup works on at once */
+    int32_t reserved;
+    int64_t grid;            /* workgroups launched */
+    int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid) */
+    int64_t partial_stride;  /* backward: floats between consecutive partial rows */
+} rmsnorm_config;
+
+/*
+ * Forward. x: [M][N] input; w: [N] weight; y: [M][N] output (same dtype);
+ * rstd: [M] fp32 output, or NULL when the caller does not need it.
+ * eps must be finite and >= 0 (eps == 0 gives inf/NaN on an all-zero row).
+ */
+int rmsnorm_fwd(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype,
+                void *y, float *rstd, void *stream);
+
+/*
+ * Size in bytes of the fp32 workspace rmsnorm_bwd needs for this shape on the
+ * current device (the per-workgroup dW partial rows), or a negative
+ * rmsn_status. 0 when M == 0.
+ */
+int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype);
+
+/*
+ * Backward. x, dy: [M][N] (dtype); w: [N] (dtype); rstd: [M] fp32 as written
+ * by rmsnorm_fwd for the same x and eps. Outputs: dx [M][N] (dtype) and
+ * dW [N] fp32 (overwritten, not accumulated). workspace: device memory of at
+ * least rmsnorm_bwd_workspace_bytes(M, N, dtype) bytes, 256-byte aligned; its
+ * contents on entry do not matter. Enqueues two kernels on `stream`: the
+ * persistent row kernel (dx and per-workgroup dW partials) and a fixed-order
+ * combine of the partials ("RMSNorm backward (almost) without the column
+ * reduction", section "The persistent kernel"). With M == 0, dW is still
+ * written (zeros) when N >= 1 and dW is not NULL.
+ */
+int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
+                int64_t N, int dtype, void *dx, float *dw, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/*
+ * The two kernels of rmsnorm_bwd as separate calls, for callers that time or
+ * schedule them apart. rmsnorm_bwd_rows runs the persistent row kernel: dx,
+ * and one fp32 partial dW row per workgroup in the workspace (rows of
+ * round_up(N, 64) floats); *partial_rows receives how many (0 when M == 0).
+ * rmsnorm_bwd_combine then writes dW[j] = sum over p < partial_rows of
+ * partial[p][j] in a fixed order. Same arguments, checks and workspace
+ * contract as rmsnorm_bwd; rmsnorm_bwd(...) equals rows followed by combine.
+ */
+int rmsnorm_bwd_rows(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
+                     int64_t N, int dtype, void *dx, void *workspace, size_t workspace_bytes,
+                     int64_t *partial_rows, void *stream);
+int rmsnorm_bwd_combine(const void *workspace, int64_t partial_rows, int64_t N, float *dw, void *stream);
+
+/*
+ * Forward / backward with an explicit launch configuration instead of the
+ * ladder's choice: lanes_per_row, vecs_per_lane (vector path) or
+ * vector_path = 0 (scalar path), and grid (>= 1) are read; the other fields
+ * are derived. For searching the configuration space ("What a tuned RMSNorm
+ * kernel actually costs on Hopper", section 06: the memory-path knobs belong
+ * in the search space). Returns RMSN_ECONFIG when the configuration does not
+ * cover the row or its kernel is not built. The backward workspace must hold
+ * grid * partial_stride floats (partial_stride = N rounded up to 64). dW bits
+ * depend on the configuration.
+ */
+int rmsnorm_fwd_with_config(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype,
+                            void *y, float *rstd, const rmsnorm_config *cfg, void *stream);
+int rmsnorm_bwd_with_config(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
+                            int64_t N, int dtype, void *dx, float *dw, void *workspace,
+                            size_t workspace_bytes, const rmsnorm_config *cfg, void *stream);
+
+/* Static text for a status code ("ok", "invalid argument", ...). Never NULL. */
+const char *rmsnorm_status_str(int status);
+
+/*
+ * The ladder as a pure host function (no HIP call): the configuration for
+ * (M, N, dtype, direction) on a device with `num_cus` compute units when the
+ * chosen kernel fits `blocks_per_cu` workgroups per compute unit. `aligned`
+ * says whether the caller's pointers are 16-byte aligned. is_bwd: 0 forward,
+ * 1 backward. Returns RMSN_OK or RMSN_EINVAL / RMSN_EDTYPE.
+ */
+int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int aligned, int num_cus,
+                          int blocks_per_cu, rmsnorm_config *out);
+
+/*
+ * The configuration rmsnorm_fwd (is_bwd = 0) or rmsnorm_bwd (is_bwd = 1)
+ * would use on the current device for 16-byte aligned pointers, including
+ * the occupancy-derived grid. Queries the device (HIP calls).
+ */
+int rmsnorm_query_config(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config *out);
+
+/* Build identification: compiler, target and flags, as a static string. */
+const char *rmsnorm_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */

@@ -1,0 +1,36 @@
+/*
+ * rmsnorm_probe.h -- HBM roofline probes used by the benchmark.
+ *
+ * The achievable-bandwidth denominator is measured, not quoted: the best of
+ * a copy, a pure write and a two-read-one-write pattern ("What a tuned
+ * RMSNorm kernel actually costs on Hopper", section 02). Each probe streams
+ * 16-byte vectors over caller-owned device buffers; `bytes` must be a
+ * multiple of 16 and every pointer 16-byte aligned. `grid` is the number of
+ * 256-lane workgroups (0 = one vector per lane, no striding). Work is enqueued
+ * on `stream` (a hipStream_t; NULL = default stream). Returns 0 or a negative
+ * rmsn_status (see rmsnorm.h).
+ */
+#ifndef RMSNORM_MI355X_PROBE_H
+#define RMSNORM_MI355X_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dst[i] = src[i]: moves 2 * bytes (one read, one write). */
+int rmsn_probe_copy(const void *src, void *dst, size_t bytes, int64_t grid, void *stream);
+
+/* dst[i] = pattern: moves `bytes` (write only). */
+int rmsn_probe_write(void *dst, size_t bytes, int64_t grid, void *stream);
+
+/* c[i] = a[i] + b[i] as 32-bit integers: moves 3 * bytes (two reads, one write). */
+int rmsn_probe_add(const void *a, const void *b, void *c, size_t bytes, int64_t grid, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_PROBE_H */

@@ -1,0 +1,208 @@
+"""Python binding of the gfx950 RMSNorm library (``librmsnorm_mi355x.so``).
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name declared in ``include/rmsnorm.h`` (and ``include/rmsnorm_probe.h``
+for the roofline probes). Pointers may be given as integers (device
+addresses) or as torch tensors (their ``data_ptr()``); ``stream`` may be an
+integer hipStream_t, a ``torch.cuda.Stream``, or None for torch's current
+stream. A non-zero status raises ``RmsnormError``.
+
+torch is imported first so that the library binds to the HIP runtime torch
+already loaded (one runtime per process). Importing this package fails when
+the library has not been built: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library links against)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "librmsnorm_mi355x.so"
+LIB_PATH = os.path.join(_HERE, LIB_NAME)
+
+F32 = 0
+BF16 = 1
+
+OK = 0
+EINVAL = -1
+EDTYPE = -2
+EWORKSPACE = -3
+EHIP = -4
+ECONFIG = -5
+
+
+class RmsnormError(RuntimeError):
+    def __init__(self, name: str, status: int, text: str):
+        super().__init__(f"{name} failed: {text} (status {status})")
+        self.status = status
+
+
+class rmsnorm_config(ctypes.Structure):
+    _fields_ = [
+        ("vector_path", ctypes.c_int32),
+        ("lanes_per_row", ctypes.c_int32),
+        ("vecs_per_lane", ctypes.c_int32),
+        ("wg_threads", ctypes.c_int32),
+        ("rows_per_wg", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("partial_rows", ctypes.c_int64),
+        ("partial_stride", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_ if name != "reserved"}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc --offload-arch=gfx950). There is no CPU or eager fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    cfgp = ctypes.POINTER(rmsnorm_config)
+    sig = {
+        "rmsnorm_fwd": (i32, [vp, vp, f32, i64, i64, i32, vp, vp, vp]),
+        "rmsnorm_fwd_with_config": (i32, [vp, vp, f32, i64, i64, i32, vp, vp, cfgp, vp]),
+        "rmsnorm_bwd_workspace_bytes": (i64, [i64, i64, i32]),
+        "rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]),
+        "rmsnorm_bwd_with_config": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, cfgp, vp]),
+        "rmsnorm_bwd_rows": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, ctypes.POINTER(i64), vp]),
+        "rmsnorm_bwd_combine": (i32, [vp, i64, i64, vp, vp]),
+        "rmsnorm_status_str": (ctypes.c_char_p, [i32]),
+        "rmsnorm_select_config": (i32, [i64, i64, i32, i32, i32, i32, i32, cfgp]),
+        "rmsnorm_query_config": (i32, [i64, i64, i32, i32, cfgp]),
+        "rmsnorm_build_info": (ctypes.c_char_p, []),
+        "rmsn_probe_copy": (i32, [vp, vp, sz, i64, vp]),
+        "rmsn_probe_write": (i32, [vp, sz, i64, vp]),
+        "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+EXPORTED = (
+    "rmsnorm_fwd", "rmsnorm_fwd_with_config", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
+    "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_status_str", "rmsnorm_select_config", "rmsnorm_query_config",
+    "rmsnorm_build_info", "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_add",
+)
+
+
+def _ptr(p):
+    if p is None:
+        return None
+    if isinstance(p, int):
+        return p
+    return p.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != OK:
+        raise RmsnormError(name, rc, rmsnorm_status_str(rc))
+
+
+def dtype_code(torch_dtype) -> int:
+    """rmsn_dtype code of a torch dtype (float32 or bfloat16)."""
+    if torch_dtype == torch.float32:
+        return F32
+    if torch_dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {torch_dtype}")
+
+
+def rmsnorm_status_str(status: int) -> str:
+    return lib.rmsnorm_status_str(int(status)).decode()
+
+
+def rmsnorm_build_info() -> str:
+    return lib.rmsnorm_build_info().decode()
+
+
+def rmsnorm_fwd(x, w, eps, M, N, dtype, y, rstd, stream=None) -> None:
+    _check("rmsnorm_fwd", lib.rmsnorm_fwd(_ptr(x), _ptr(w), float(eps), int(M), int(N), int(dtype),
+                                          _ptr(y), _ptr(rstd), _stream(stream)))
+
+
+def rmsnorm_fwd_with_config(x, w, eps, M, N, dtype, y, rstd, cfg: rmsnorm_config, stream=None) -> None:
+    _check("rmsnorm_fwd_with_config",
+           lib.rmsnorm_fwd_with_config(_ptr(x), _ptr(w), float(eps), int(M), int(N), int(dtype), _ptr(y),
+                                       _ptr(rstd), ctypes.byref(cfg), _stream(stream)))
+
+
+def rmsnorm_bwd_workspace_bytes(M, N, dtype) -> int:
+    n = lib.rmsnorm_bwd_workspace_bytes(int(M), int(N), int(dtype))
+    _check("rmsnorm_bwd_workspace_bytes", n if n < 0 else OK)
+    return int(n)
+
+
+def rmsnorm_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream=None) -> None:
+    _check("rmsnorm_bwd", lib.rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N), int(dtype),
+                                          _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
+                                          _stream(stream)))
+
+
+def rmsnorm_bwd_with_config(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes,
+                            cfg: rmsnorm_config, stream=None) -> None:
+    _check("rmsnorm_bwd_with_config",
+           lib.rmsnorm_bwd_with_config(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N), int(dtype),
+                                       _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
+                                       ctypes.byref(cfg), _stream(stream)))
+
+
+def rmsnorm_bwd_rows(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, stream=None) -> int:
+    """Backward row kernel only; returns the number of partial dW rows written."""
+    p = ctypes.c_int64(0)
+    _check("rmsnorm_bwd_rows", lib.rmsnorm_bwd_rows(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N),
+                                                    int(dtype), _ptr(dx), _ptr(workspace), int(workspace_bytes),
+                                                    ctypes.byref(p), _stream(stream)))
+    return int(p.value)
+
+
+def rmsnorm_bwd_combine(workspace, partial_rows, N, dw, stream=None) -> None:
+    _check("rmsnorm_bwd_combine", lib.rmsnorm_bwd_combine(_ptr(workspace), int(partial_rows), int(N), _ptr(dw),
+                                                          _stream(stream)))
+
+
+def rmsnorm_select_config(M, N, dtype, is_bwd, aligned, num_cus, blocks_per_cu) -> rmsnorm_config:
+    cfg = rmsnorm_config()
+    _check("rmsnorm_select_config",
+           lib.rmsnorm_select_config(int(M), int(N), int(dtype), int(is_bwd), int(aligned), int(num_cus),
+                                     int(blocks_per_cu), ctypes.byref(cfg)))
+    return cfg
+
+
+def rmsnorm_query_config(M, N, dtype, is_bwd) -> rmsnorm_config:
+    cfg = rmsnorm_config()
+    _check("rmsnorm_query_config",
+           lib.rmsnorm_query_config(int(M), int(N), int(dtype), int(is_bwd), ctypes.byref(cfg)))
+    return cfg
+
+
+def rmsn_probe_copy(src, dst, nbytes, grid=0, stream=None) -> None:
+    _check("rmsn_probe_copy", lib.rmsn_probe_copy(_ptr(src), _ptr(dst), int(nbytes), int(grid), _stream(stream)))
+
+
+def rmsn_probe_write(dst, nbytes, grid=0, stream=None) -> None:
+    _check("rmsn_probe_write", lib.rmsn_probe_write(_ptr(dst), int(nbytes), int(grid), _stream(stream)))
+
+
+def rmsn_probe_add(a, b, c, nbytes, grid=0, stream=None) -> None:
+    _check("rmsn_probe_add", lib.rmsn_probe_add(_ptr(a), _ptr(b), _ptr(c), int(nbytes), int(grid),
+                                                _stream(stream)))

@@ -1,0 +1,90 @@
+"""Build the gfx950 RMSNorm library (``librmsnorm_mi355x.so``) in-tree with hipcc.
+
+Each source compiles to an object in ``_build/`` (in parallel); the objects
+link into a shared library next to this file, which the Python binding loads.
+The kernel resource report (VGPRs, SGPRs, LDS, occupancy per kernel) that
+hipcc prints is kept in ``_build/resource_usage.txt``.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB_NAME = "librmsnorm_mi355x.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+SOURCES = ["rmsn_fwd.hip", "rmsn_bwd.hip", "rmsn_probe.hip", "rmsn_api.cpp"]
+HEADERS = ["rmsn_device.h", "rmsn_tables.h"]
+ARCH = "gfx950"
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
+DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; the gfx950 library cannot be built")
+    return exe
+
+
+def _git_rev() -> str:
+    try:
+        return subprocess.run(["git", "-C", PKG, "rev-parse", "--short", "HEAD"], capture_output=True,
+                              text=True, check=True).stdout.strip()
+    except Exception:
+        return "nogit"
+
+
+def _compile(src: str, info: str) -> tuple[str, str]:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, f'-DRMSN_BUILD_INFO="{info}"', "-c", path, "-o", obj]
+    if src.endswith(".hip"):
+        cmd[1:1] = DEVICE_FLAGS + ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr[-6000:]}")
+    return obj, res.stderr
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link the shared library. Returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    info = f"rmsnorm-mi355x {_git_rev()} {ARCH} hipcc -O3 -packed-fp32-ops"
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(lambda s: _compile(s, info), SOURCES))
+    objs = [o for o, _ in results]
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for (o, log), s in zip(results, SOURCES):
+            f.write(f"==== {s}\n{log}\n")
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr[-4000:]}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+def is_stale() -> bool:
+    """True when the library is missing or older than one of its sources."""
+    if not os.path.exists(LIB_PATH):
+        return True
+    t = os.path.getmtime(LIB_PATH)
+    inc = os.path.join(os.path.dirname(PKG), "include")
+    deps = [os.path.join(CSRC, s) for s in SOURCES + HEADERS]
+    deps += [os.path.join(inc, h) for h in os.listdir(inc)] if os.path.isdir(inc) else []
+    return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
+
+
+if __name__ == "__main__":
+    build(verbose=True)

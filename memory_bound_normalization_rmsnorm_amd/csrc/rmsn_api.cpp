@@ -1,0 +1,387 @@
+// rmsn_api.cpp -- host side of the RMSNorm C ABI: argument checks, the
+// launch-configuration ladder, occupancy-sized grids and kernel launches.
+//
+// Every check runs before the first HIP call, so invalid arguments are
+// reported without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "../../include/rmsnorm.h"
+#include "rmsn_tables.h"
+
+#ifndef RMSN_BUILD_INFO
+#define RMSN_BUILD_INFO "unknown build"
+#endif
+
+extern "C" int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype);
+
+namespace {
+
+using rmsn::KernelEntry;
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int kMaxVecLanes = 1024;
+
+int elem_size(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
+bool valid_dtype(int dtype) { return dtype == RMSN_F32 || dtype == RMSN_BF16; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t next_pow2(int64_t v) {
+    int64_t p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+int check_shape(int64_t M, int64_t N, int dtype) {
+    if (!valid_dtype(dtype)) return RMSN_EDTYPE;
+    if (M < 0 || N < 1 || N > kMaxN) return RMSN_EINVAL;
+    if (M > INT64_MAX / N / 4) return RMSN_EINVAL;  // element and byte counts fit in int64
+    return RMSN_OK;
+}
+
+// The row-width ladder: which kernel shape serves a row of N elements.
+//   * rows of at most 32 vectors: one lane per vector, several rows per wave
+//     (QK-norm: 128 bf16 = 16 vectors -> 16 lanes, 4 rows per wavefront);
+//   * up to 64 * V vectors: one wavefront per row, up to V vectors per lane;
+//   * wider: a power-of-two number of wavefronts per row (up to 16, one
+//     1024-lane workgroup) so that each lane holds between V/2 and V vectors;
+//   * anything the vector kernels cannot take (N*elem not a multiple of 16
+//     bytes, unaligned pointers, more than 1024 * V vectors): the scalar kernel.
+// V is 8 for the forward (a lane holds x and w: 64 VGPRs at V = 8) and 4 for
+// the backward (x, dy, w and V * elems fp32 dW sums), so both keep at least
+// four wavefronts per SIMD on the common widths.
+int max_vecs_per_lane(int is_bwd) { return is_bwd ? 4 : 8; }
+
+void set_vector_shape(int64_t lpr, int64_t vpt, rmsnorm_config *c) {
+    c->vector_path = 1;
+    c->lanes_per_row = (int32_t)lpr;
+    c->vecs_per_lane = (int32_t)vpt;
+    c->wg_threads = rmsn::wg_for_lpr((int)lpr);
+    c->rows_per_wg = c->wg_threads / c->lanes_per_row;
+}
+
+void set_scalar_shape(rmsnorm_config *c) {
+    c->vector_path = 0;
+    c->lanes_per_row = rmsn::kScalarWG;
+    c->vecs_per_lane = 0;
+    c->wg_threads = rmsn::kScalarWG;
+    c->rows_per_wg = 1;
+}
+
+bool vector_ok(int64_t N, int dtype, bool aligned) { return aligned && (N * elem_size(dtype)) % 16 == 0; }
+
+void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config *c) {
+    const int64_t V = max_vecs_per_lane(is_bwd);
+    const int64_t nvec = N * elem_size(dtype) / 16;
+    if (!vector_ok(N, dtype, aligned) || nvec > kMaxVecLanes * V) {
+        set_scalar_shape(c);
+        return;
+    }
+    int64_t lpr, vpt;
+    if (nvec <= 32) {
+        lpr = next_pow2(nvec);
+        vpt = 1;
+    } else if (nvec <= 64 * V) {
+        lpr = 64;
+        vpt = (nvec + 63) / 64;
+    } else {
+        lpr = next_pow2((nvec + V - 1) / V);
+        vpt = (nvec + lpr - 1) / lpr;
+    }
+    set_vector_shape(lpr, vpt, c);
+}
+
+// Grid: as many workgroups as stay resident (num_cus * blocks_per_cu), never
+// more than there are row blocks. The backward writes one partial row per
+// workgroup.
+void ladder_grid(int64_t M, int64_t N, int num_cus, int blocks_per_cu, rmsnorm_config *c) {
+    const int64_t row_blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
+    int64_t resident = int64_t(num_cus) * (blocks_per_cu > 0 ? blocks_per_cu : 1);
+    if (resident < 1) resident = 1;
+    c->grid = row_blocks < resident ? row_blocks : resident;
+    c->partial_rows = c->grid;
+    c->partial_stride = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
+    c->reserved = 0;
+}
+
+// ---- per-device cache ----------------------------------------------------
+
+struct DeviceInfo {
+    int num_cus = 0;
+    std::unordered_map<const void *, int> occupancy;
+};
+
+std::mutex g_mu;
+std::unordered_map<int, DeviceInfo> g_devices;
+
+int device_info(int *num_cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RMSN_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceInfo &d = g_devices[dev];
+    if (d.num_cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return RMSN_EHIP;
+        d.num_cus = n;
+    }
+    *num_cus = d.num_cus;
+    return RMSN_OK;
+}
+
+int occupancy(const void *fn, int wg, int *blocks) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RMSN_EHIP;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto &occ = g_devices[dev].occupancy;
+        auto it = occ.find(fn);
+        if (it != occ.end()) {
+            *blocks = it->second;
+            return RMSN_OK;
+        }
+    }
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, wg, 0) != hipSuccess || b <= 0) return RMSN_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_devices[dev].occupancy[fn] = b;
+    *blocks = b;
+    return RMSN_OK;
+}
+
+const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd) {
+    if (!c.vector_path) return is_bwd ? rmsn::bwd_scalar_kernel(dtype) : rmsn::fwd_scalar_kernel(dtype);
+    const KernelEntry *e = is_bwd ? rmsn::bwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane)
+                                  : rmsn::fwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane);
+    return e ? e->fn : nullptr;
+}
+
+// Full configuration on the current device.
+int resolve(int64_t M, int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config *c,
+            const void **fn) {
+    std::memset(c, 0, sizeof *c);
+    ladder_shape(N, dtype, is_bwd, aligned, c);
+    const void *k = kernel_for(*c, dtype, is_bwd);
+    if (!k) return RMSN_ECONFIG;
+    int cus = 0, blocks = 0;
+    int st = device_info(&cus);
+    if (st != RMSN_OK) return st;
+    st = occupancy(k, c->wg_threads, &blocks);
+    if (st != RMSN_OK) return st;
+    ladder_grid(M, N, cus, blocks, c);
+    if (fn) *fn = k;
+    return RMSN_OK;
+}
+
+int64_t workspace_for(const rmsnorm_config &c) {
+    return c.partial_rows * c.partial_stride * int64_t(sizeof(float));
+}
+
+int launch(const void *fn, int64_t grid, int wg, void **args, hipStream_t stream) {
+    if (grid <= 0) return RMSN_OK;
+    if (grid > INT32_MAX) return RMSN_ECONFIG;
+    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)wg), args, 0, stream) != hipSuccess)
+        return RMSN_EHIP;
+    return RMSN_OK;
+}
+
+// An explicit configuration (config search, benchmarks) is checked against
+// the shape: the kernel must exist, cover the row, and the grid must be
+// positive. Shape fields derived from lanes_per_row are recomputed.
+int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, int is_bwd, bool aligned,
+                    rmsnorm_config *c, const void **fn) {
+    std::memset(c, 0, sizeof *c);
+    if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
+    if (req->vector_path) {
+        const int64_t nvec = N * elem_size(dtype) / 16;
+        if (!vector_ok(N, dtype, aligned)) return RMSN_ECONFIG;
+        if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
+        set_vector_shape(req->lanes_per_row, req->vecs_per_lane, c);
+    } else {
+        set_scalar_shape(c);
+    }
+    const void *k = kernel_for(*c, dtype, is_bwd);
+    if (!k) return RMSN_ECONFIG;
+    ladder_grid(M, N, 1, 1, c);
+    c->grid = req->grid;
+    c->partial_rows = req->grid;
+    *fn = k;
+    return RMSN_OK;
+}
+
+int fwd_impl(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype, void *y, float *rstd,
+             void *stream, const rmsnorm_config *req) {
+    int st = check_shape(M, N, dtype);
+    if (st != RMSN_OK) return st;
+    if (!std::isfinite(eps) || eps < 0.f) return RMSN_EINVAL;
+    if (M == 0) return RMSN_OK;
+    if (!x || !w || !y) return RMSN_EINVAL;
+    const bool aligned = aligned16(x) && aligned16(w) && aligned16(y);
+    rmsnorm_config c;
+    const void *fn = nullptr;
+    st = req ? explicit_config(req, M, N, dtype, 0, aligned, &c, &fn) : resolve(M, N, dtype, 0, aligned, &c, &fn);
+    if (st != RMSN_OK) return st;
+    int32_t n32 = (int32_t)N;
+    int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
+    void *args[] = {(void *)&x, (void *)&w, (void *)&y, (void *)&rstd, (void *)&eps,
+                    (void *)&M, (void *)&n32, (void *)&nvec};
+    return launch(fn, c.grid, c.wg_threads, args, static_cast<hipStream_t>(stream));
+}
+
+int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStream_t s) {
+    if (N < 1 || N > kMaxN || P < 0) return RMSN_EINVAL;
+    if (!dw) return RMSN_EINVAL;
+    if (P > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)) return RMSN_EWORKSPACE;
+    const float *cpartial = static_cast<const float *>(workspace);
+    int64_t ldp = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
+    int32_t n32 = (int32_t)N;
+    void *cargs[] = {(void *)&cpartial, (void *)&ldp, (void *)&P, (void *)&n32, (void *)&dw};
+    return launch(rmsn::dw_combine_kernel(), (N + rmsn::kCombineCols - 1) / rmsn::kCombineCols,
+                  rmsn::kCombineWG, cargs, s);
+}
+
+int rows_impl(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N, int dtype,
+              void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows, hipStream_t s,
+              const rmsnorm_config *req) {
+    int st = check_shape(M, N, dtype);
+    if (st != RMSN_OK) return st;
+    if (!partial_rows) return RMSN_EINVAL;
+    *partial_rows = 0;
+    if (M == 0) return RMSN_OK;
+    if (!x || !w || !dy || !rstd || !dx) return RMSN_EINVAL;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RMSN_EWORKSPACE;
+    const bool aligned = aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx);
+    rmsnorm_config c;
+    const void *fn = nullptr;
+    st = req ? explicit_config(req, M, N, dtype, 1, aligned, &c, &fn) : resolve(M, N, dtype, 1, aligned, &c, &fn);
+    if (st != RMSN_OK) return st;
+    if (req) {
+        if (workspace_bytes < (size_t)workspace_for(c)) return RMSN_EWORKSPACE;
+    } else {
+        // the documented contract: at least what rmsnorm_bwd_workspace_bytes reports
+        const int64_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype);
+        if (need < 0) return (int)need;
+        if (workspace_bytes < (size_t)need) return RMSN_EWORKSPACE;
+    }
+    int32_t n32 = (int32_t)N;
+    int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
+    float *partial = static_cast<float *>(workspace);
+    int64_t ldp = c.partial_stride;
+    void *args[] = {(void *)&x, (void *)&w, (void *)&dy, (void *)&rstd, (void *)&dx,
+                    (void *)&partial, (void *)&ldp, (void *)&M, (void *)&n32, (void *)&nvec};
+    st = launch(fn, c.grid, c.wg_threads, args, s);
+    if (st == RMSN_OK) *partial_rows = c.partial_rows;
+    return st;
+}
+
+int bwd_impl(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N, int dtype,
+             void *dx, float *dw, void *workspace, size_t workspace_bytes, void *stream,
+             const rmsnorm_config *req) {
+    int st = check_shape(M, N, dtype);
+    if (st != RMSN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 0) {
+        if (!dw) return RMSN_OK;
+        int64_t n = N;
+        void *args[] = {(void *)&dw, (void *)&n};
+        const int64_t grid = (N + 255) / 256 < 1024 ? (N + 255) / 256 : 1024;
+        return launch(rmsn::fill_zero_kernel(), grid, 256, args, s);
+    }
+    if (!dw) return RMSN_EINVAL;
+    int64_t P = 0;
+    st = rows_impl(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req);
+    if (st != RMSN_OK) return st;
+    return combine_impl(workspace, P, N, dw, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rmsnorm_status_str(int status) {
+    switch (status) {
+    case RMSN_OK: return "ok";
+    case RMSN_EINVAL: return "invalid argument";
+    case RMSN_EDTYPE: return "unsupported dtype";
+    case RMSN_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case RMSN_EHIP: return "HIP runtime error";
+    case RMSN_ECONFIG: return "launch configuration does not fit the shape";
+    default: return "unknown status";
+    }
+}
+
+const char *rmsnorm_build_info(void) { return RMSN_BUILD_INFO; }
+
+int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int aligned, int num_cus,
+                          int blocks_per_cu, rmsnorm_config *out) {
+    const int st = check_shape(M, N, dtype);
+    if (st != RMSN_OK) return st;
+    if (!out || num_cus < 1 || blocks_per_cu < 1 || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
+    std::memset(out, 0, sizeof *out);
+    ladder_shape(N, dtype, is_bwd, aligned != 0, out);
+    ladder_grid(M, N, num_cus, blocks_per_cu, out);
+    return RMSN_OK;
+}
+
+int rmsnorm_query_config(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config *out) {
+    const int st = check_shape(M, N, dtype);
+    if (st != RMSN_OK) return st;
+    if (!out || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
+    return resolve(M, N, dtype, is_bwd, true, out, nullptr);
+}
+
+int rmsnorm_fwd(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype, void *y,
+                float *rstd, void *stream) {
+    return fwd_impl(x, w, eps, M, N, dtype, y, rstd, stream, nullptr);
+}
+
+int rmsnorm_fwd_with_config(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype,
+                            void *y, float *rstd, const rmsnorm_config *cfg, void *stream) {
+    if (!cfg) return RMSN_EINVAL;
+    return fwd_impl(x, w, eps, M, N, dtype, y, rstd, stream, cfg);
+}
+
+int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype) {
+    const int st = check_shape(M, N, dtype);
+    if (st != RMSN_OK) return st;
+    if (M == 0) return 0;
+    // Enough for either row kernel, so a caller's alignment never changes the answer.
+    rmsnorm_config cv, cs;
+    int s1 = resolve(M, N, dtype, 1, true, &cv, nullptr);
+    if (s1 != RMSN_OK) return s1;
+    int s2 = resolve(M, N, dtype, 1, false, &cs, nullptr);
+    if (s2 != RMSN_OK) return s2;
+    const int64_t a = workspace_for(cv), b = workspace_for(cs);
+    return a > b ? a : b;
+}
+
+int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,
+                int dtype, void *dx, float *dw, void *workspace, size_t workspace_bytes, void *stream) {
+    return bwd_impl(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, nullptr);
+}
+
+int rmsnorm_bwd_with_config(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
+                            int64_t N, int dtype, void *dx, float *dw, void *workspace,
+                            size_t workspace_bytes, const rmsnorm_config *cfg, void *stream) {
+    if (!cfg) return RMSN_EINVAL;
+    return bwd_impl(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, cfg);
+}
+
+int rmsnorm_bwd_rows(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,
+                     int dtype, void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows,
+                     void *stream) {
+    return rows_impl(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, partial_rows,
+                     static_cast<hipStream_t>(stream), nullptr);
+}
+
+int rmsnorm_bwd_combine(const void *workspace, int64_t partial_rows, int64_t N, float *dw, void *stream) {
+    return combine_impl(workspace, partial_rows, N, dw, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// rmsn_device.h -- device helpers shared by the RMSNorm kernels (gfx950).
+//
+// * buffer-resource loads/stores: an access whose byte offset is at or past
+//   the resource's record count reads 0 and writes nothing, which masks row
+//   tails and missing rows without branches;
+// * 16-byte vector loads/stores and their unpacking into fp32 lanes;
+// * bf16 <-> fp32 conversion (bf16 stores round to nearest even with the
+//   hardware v_cvt_pk_bf16_f32);
+// * sums over a group of lanes that share one row: DPP within 16 lanes,
+//   ds_swizzle across 32, v_readlane across the 64-lane wavefront, and LDS
+//   across the wavefronts of a workgroup. Every sum has a fixed order, so
+//   results are bit-identical from run to run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t g32x4 __attribute__((vector_size(16)));  // the buffer builtins' vector type
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Bit reinterpretation goes through these by-value helpers. Applied directly
+// to an ext_vector element (`__builtin_bit_cast(float, v.y)`), clang reads
+// element 0 whatever the element named, so vector components are always
+// copied into a scalar first.
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// Storage types: fp32 is `float`; bf16 is carried as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static constexpr int kPerVec = 4;  // elements per 16-byte vector
+    static __device__ __forceinline__ float load(const float *p) { return *p; }
+    static __device__ __forceinline__ void store(float *p, float v) { *p = v; }
+    static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[4]) {
+        f[0] = as_float(v.x);
+        f[1] = as_float(v.y);
+        f[2] = as_float(v.z);
+        f[3] = as_float(v.w);
+    }
+    // acc + sum of the squares of the vector's elements, in element order
+    static __device__ __forceinline__ float sumsq(const u32x4 &v, float acc) {
+        float f[4];
+        unpack(v, f);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(f[k], f[k], acc);
+        return acc;
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&f)[4]) {
+        u32x4 v;
+        v.x = as_u32(f[0]);
+        v.y = as_u32(f[1]);
+        v.z = as_u32(f[2]);
+        v.w = as_u32(f[3]);
+        return v;
+    }
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return as_float(d & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <>
+struct Elem<bf16_t> {
+    static constexpr int kPerVec = 8;
+    static __device__ __forceinline__ float load(const bf16_t *p) {
+        return __builtin_bit_cast(float, (uint32_t)p->bits << 16);
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, float v) {
+        p->bits = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+    static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[8]) {
+        f[0] = bf16_lo(v.x);
+        f[1] = bf16_hi(v.x);
+        f[2] = bf16_lo(v.y);
+        f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z);
+        f[5] = bf16_hi(v.z);
+        f[6] = bf16_lo(v.w);
+        f[7] = bf16_hi(v.w);
+    }
+    // acc + sum of squares with v_dot2_f32_bf16: each bf16 product is exact in
+    // fp32; pairs are added in element order.
+    static __device__ __forceinline__ float sumsq(const u32x4 &v, float acc) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), as_bf16x2(v.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), as_bf16x2(v.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), as_bf16x2(v.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), as_bf16x2(v.w), acc, false);
+        return acc;
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&f)[8]) {
+        u32x4 v;
+        v.x = pack_bf16x2(f[0], f[1]);
+        v.y = pack_bf16x2(f[2], f[3]);
+        v.z = pack_bf16x2(f[4], f[5]);
+        v.w = pack_bf16x2(f[6], f[7]);
+        return v;
+    }
+};
+
+// Raw buffer resource (stride 0): `bytes` is the record count. Word 3 of the
+// descriptor selects 32-bit data format, the value used for raw (untyped)
+// buffer access on CDNA. The base pointer must be wave-uniform.
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kOff = 0x80000000u;  // an offset past every record count used here
+
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Buf(const void *base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3)) {}
+    __device__ __forceinline__ u32x4 load16(uint32_t off) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    __device__ __forceinline__ void store16(uint32_t off, const u32x4 &v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(g32x4, v), r, off, 0, 0);
+    }
+    __device__ __forceinline__ float load4(uint32_t off) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+    __device__ __forceinline__ void store4(uint32_t off, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    }
+};
+
+// Hide a packed vector's value from the optimiser. Used so the compiler keeps
+// rows and weights packed in registers (4 VGPRs per 16 bytes) and unpacks
+// them where they are used, instead of hoisting or keeping the unpacked fp32
+// copies alive (twice the registers for bf16), which would cut occupancy.
+__device__ __forceinline__ void keep_packed(u32x4 &v) { asm volatile("" : "+v"(v)); }
+
+// ---- lane-group sums ------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// DPP controls (GCN/CDNA encoding).
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within each 16 lanes
+
+// ds_swizzle bit-mask mode: and 0x1F, or 0, xor 0x10 -> partner lane ^ 16 (within 32).
+constexpr int kSwizzleXor16 = 0x401F;
+
+// Sum over aligned groups of G lanes (G a power of two, 1..64); every lane of
+// a group receives the group's sum. After each step all lanes of the merged
+// group hold the same value (a + b == b + a in IEEE arithmetic), so the
+// result is uniform and its rounding does not depend on the lane.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group must be a power of two <= 64");
+    if constexpr (G >= 2) v += dpp<kQuadXor1>(v);
+    if constexpr (G >= 4) v += dpp<kQuadXor2>(v);
+    // After the quad steps every lane of a quad holds the quad sum, so the
+    // mirror permutations pair each lane with a lane of the neighbouring quad
+    // (half-row) or half-row (row).
+    if constexpr (G >= 8) v += dpp<kRowHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp<kRowMirror>(v);
+    if constexpr (G >= 32)
+        v += __builtin_bit_cast(float,
+                                __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16));
+    if constexpr (G >= 64) {
+        float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+        float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        v = lo + hi;
+    }
+    return v;
+}
+
+// Sum over a row group of LPR lanes. For LPR <= 64 the group lives inside one
+// wavefront. For LPR > 64 the group is LPR/64 whole wavefronts: each wave
+// reduces itself, writes one value to LDS, and after a barrier every lane adds
+// the wave partials in wave order. `slots` must hold 2 * (WG / 64) floats;
+// `parity` alternates between consecutive calls so one barrier per call
+// suffices (a slot is rewritten only after every wave has passed the barrier
+// of the following call, which comes after its reads of this one).
+template <int LPR, int WG>
+__device__ __forceinline__ float row_sum(float v, float *slots, int parity) {
+    if constexpr (LPR <= 64) {
+        return group_sum<LPR>(v);
+    } else {
+        constexpr int kWaves = WG / 64;
+        constexpr int kWavesPerRow = LPR / 64;
+        v = group_sum<64>(v);
+        const int wave = threadIdx.x >> 6;
+        float *buf = slots + parity * kWaves;
+        if ((threadIdx.x & 63) == 0) buf[wave] = v;
+        __syncthreads();
+        const int first = wave - (wave % kWavesPerRow);
+        float s = buf[first];
+#pragma unroll
+        for (int k = 1; k < kWavesPerRow; ++k) s += buf[first + k];
+        return s;
+    }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,49 @@
+// rmsn_tables.h -- kernel lookup shared by the kernel files and the host API.
+#pragma once
+
+#include <stdint.h>
+
+namespace rmsn {
+
+// Lanes of the scalar (any-N, any-alignment) row kernels and the combine kernel.
+constexpr int kScalarWG = 256;
+constexpr int kCombineWG = 1024;
+constexpr int kCombineCols = 64;     // dW columns per combine workgroup (16 lanes x 4)
+constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
+constexpr int kCombineSlices = kCombineWG / kCombineLanes;  // partial rows summed side by side
+constexpr int kPartialAlign = 64;    // partial rows are padded to a multiple of 64 floats
+
+// Workgroup size for a row group of `lpr` lanes: at least four wavefronts.
+constexpr int wg_for_lpr(int lpr) { return lpr > 256 ? lpr : 256; }
+
+// Waves per SIMD the compiler is asked to fit (512 VGPRs per SIMD lane), from
+// the registers a lane needs with rows and weights kept packed: `packed`
+// 16-byte vectors (4 VGPRs each), `floats` fp32 accumulators, one offset per
+// vector and ~24 temporaries. The scheduler then trades ILP for occupancy
+// instead of unpacking every operand ahead of use.
+// A workgroup of `wg` lanes occupies wg/256 waves on each of the 4 SIMDs, so
+// never ask for fewer than that.
+constexpr int waves_for(int packed, int floats, int vpt, int wg) {
+    const int regs = 4 * packed + floats + vpt + 24;
+    int w = 512 / regs;
+    const int need = wg / 256 > 1 ? wg / 256 : 1;
+    w = w < need ? need : w;
+    return w > 8 ? 8 : w;
+}
+
+struct KernelEntry {
+    int lpr;         // lanes per row
+    int vpt;         // 16-byte vectors per lane
+    int wg;          // workgroup size
+    const void *fn;  // __global__ function
+};
+
+// dtype: 0 fp32, 1 bf16. nullptr when (lpr, vpt) is not instantiated.
+const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt);
+const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt);
+const void *fwd_scalar_kernel(int dtype);
+const void *bwd_scalar_kernel(int dtype);
+const void *dw_combine_kernel();
+const void *fill_zero_kernel();
+
+}  // namespace rmsn

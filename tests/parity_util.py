@@ -1,0 +1,154 @@
+"""Helpers for the GPU parity tests: device upload/download of storage arrays,
+calls through the C ABI (Python binding), and the tolerance gates.
+
+Tolerance gates (fp64 oracle value o, GPU value g):
+  fp32 y, dx:  |g - o| <= 1e-5 * max(|o|, rms of the row of o, t)
+               where t (dx only) is the rms over the row of the term r*dy*w:
+               dx = r*V - x*c is a difference of terms of that size, and
+               when they cancel (N = 1, or rows dominated by one column)
+               fp32 keeps only an absolute accuracy of ~1e-7 * t
+  fp32 dW:     |g - o| <= 1e-5 * max(|o|, rms(o))
+  bf16 y, dx:  |g - o| <= 2^-7 * |o| + 1e-3            (the stated bf16 bound)
+               and, stricter, |g - o| <= 2^-7 * (|o| + 0.01 * rms of the row)
+  bf16 dW:     |g - o| <= 1e-3 * max(|o|, 1e-2 * rms(o))
+  rstd:        |g - o| <= 1e-5 * o                     (both dtypes)
+The row-rms floor is needed because dx = r*V - x*c can cancel to ~0, where a
+purely relative bound is meaningless. The bf16 bound covers one rounding to
+bf16 (at most 2^-8 relative) with a factor-2 margin.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import memory_bound_normalization_rmsnorm_amd as rn
+
+DT = {"f32": rn.F32, "bf16": rn.BF16}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def to_device(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Storage-format numpy array -> device tensor of the matching torch dtype."""
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.to("cuda")
+
+
+def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Device tensor -> storage-format numpy array (bf16 as uint16 bits)."""
+    t = t.detach().to("cpu").contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def empty_like_storage(shape, dtype: str, fill=float("nan")) -> torch.Tensor:
+    """Device tensor filled with `fill` (NaN by default) so unwritten outputs show up."""
+    return torch.full(shape, fill, dtype=TORCH_DT[dtype], device="cuda")
+
+
+def gpu_fwd(x, w, eps, dtype, cfg=None, x_dev=None, w_dev=None):
+    """Run the forward through the C ABI. Returns (y storage array, rstd fp32 array)."""
+    M, N = x.shape
+    xd = to_device(x, dtype) if x_dev is None else x_dev
+    wd = to_device(w, dtype) if w_dev is None else w_dev
+    y = empty_like_storage((M, N), dtype)
+    rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    if cfg is None:
+        rn.rmsnorm_fwd(xd, wd, eps, M, N, DT[dtype], y, rstd)
+    else:
+        rn.rmsnorm_fwd_with_config(xd, wd, eps, M, N, DT[dtype], y, rstd, cfg)
+    torch.cuda.synchronize()
+    return to_host(y, dtype), rstd.cpu().numpy()
+
+
+def workspace(M, N, dtype, cfg=None):
+    if cfg is None:
+        nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, DT[dtype])
+    else:
+        nbytes = int(cfg.grid) * ((N + 63) // 64 * 64) * 4
+    # 256-byte aligned (the caching allocator aligns to 512); poisoned with NaN
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    return ws, nbytes
+
+
+def gpu_bwd(x, w, dy, rstd, dtype, cfg=None):
+    """Run the backward through the C ABI. rstd: fp32 numpy array (as the forward wrote it).
+    Returns (dx storage array, dW fp32 array)."""
+    M, N = x.shape
+    xd, wd, gd = to_device(x, dtype), to_device(w, dtype), to_device(dy, dtype)
+    rd = torch.from_numpy(np.ascontiguousarray(rstd, dtype=np.float32)).to("cuda")
+    dx = empty_like_storage((M, N), dtype)
+    dw = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    ws, nbytes = workspace(M, N, dtype, cfg)
+    if cfg is None:
+        rn.rmsnorm_bwd(xd, wd, gd, rd, M, N, DT[dtype], dx, dw, ws, nbytes)
+    else:
+        rn.rmsnorm_bwd_with_config(xd, wd, gd, rd, M, N, DT[dtype], dx, dw, ws, nbytes, cfg)
+    torch.cuda.synchronize()
+    return to_host(dx, dtype), dw.cpu().numpy()
+
+
+def _fail(what, err, bound, g, o):
+    k = int(np.argmax(err - bound))
+    idx = np.unravel_index(k, err.shape)
+    return (f"{what}: {int(np.sum(err > bound))} elements out of tolerance; worst at {idx}: "
+            f"gpu={g[idx]!r} oracle={o[idx]!r} err={err[idx]:.3e} bound={bound[idx]:.3e}")
+
+
+def term_rms(x, w, dy, r, dtype, rows=None) -> np.ndarray:
+    """Per-row rms of r_i * dy_ij * w_j (fp64, from the inputs and the oracle's r)."""
+    gs = dy if rows is None else dy[rows]
+    t = r[:, None] * widen(gs, dtype) * widen(w, dtype)[None, :]
+    return np.sqrt(np.mean(t * t, axis=-1, keepdims=True))
+
+
+def check_rows(g_storage: np.ndarray, o: np.ndarray, dtype: str, what: str, floor=None) -> dict:
+    """Gate for y or dx rows. g_storage: GPU rows in storage format; o: fp64 oracle rows;
+    floor: optional per-row magnitude of cancelled terms (dx)."""
+    g = widen(g_storage, dtype)
+    assert g.shape == o.shape, f"{what}: shape {g.shape} vs {o.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    err = np.abs(g - o)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+    if floor is not None:
+        rms = np.maximum(rms, floor)
+    if dtype == "f32":
+        bound = 1e-5 * np.maximum(np.abs(o), rms)
+        assert np.all(err <= bound), _fail(what, err, bound, g, o)
+    else:
+        bound = 2.0 ** -7 * np.abs(o) + 1e-3
+        assert np.all(err <= bound), _fail(what, err, bound, g, o)
+        strict = 2.0 ** -7 * (np.abs(o) + 0.01 * rms)
+        assert np.all(err <= strict), _fail(what + " (strict)", err, strict, g, o)
+    return {"max_abs_err": float(err.max()) if err.size else 0.0,
+            "max_rel_err": float(np.max(err / np.maximum(np.abs(o), 1e-30))) if err.size else 0.0}
+
+
+def check_rstd(g: np.ndarray, o: np.ndarray, what: str = "rstd") -> None:
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    err = np.abs(g.astype(np.float64) - o)
+    bound = 1e-5 * np.abs(o)
+    assert np.all(err <= bound), _fail(what, err, bound, g, o)
+
+
+def check_dw(g: np.ndarray, o: np.ndarray, dtype: str, what: str = "dW") -> None:
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    g = g.astype(np.float64)
+    err = np.abs(g - o)
+    rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
+    if dtype == "f32":
+        bound = 1e-5 * np.maximum(np.abs(o), rms)
+    else:
+        bound = 1e-3 * np.maximum(np.abs(o), 1e-2 * rms)
+    assert np.all(err <= bound), _fail(what, err, bound, g, o)

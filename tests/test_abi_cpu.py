@@ -1,0 +1,145 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol the headers declare, and rejects bad arguments before any HIP call.
+The ladder (a pure host function) picks the documented shapes."""
+
+import os
+import re
+
+import pytest
+
+import memory_bound_normalization_rmsnorm_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(rmsn\w*)\s*\(", src))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "rmsnorm_fwd" in names and "rmsnorm_bwd" in names
+    for n in names:
+        assert hasattr(rn.lib, n), f"{n} declared but not exported"
+    assert set(names) == set(rn.EXPORTED)
+
+
+def test_build_info_and_status_strings():
+    assert "gfx950" in rn.rmsnorm_build_info()
+    assert rn.rmsnorm_status_str(rn.OK) == "ok"
+    for s in (rn.EINVAL, rn.EDTYPE, rn.EWORKSPACE, rn.EHIP, rn.ECONFIG):
+        assert rn.rmsnorm_status_str(s) not in ("ok", "unknown status")
+    assert rn.rmsnorm_status_str(12345) == "unknown status"
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails its checks first
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=7), rn.EDTYPE),
+    (dict(M=-1), rn.EINVAL),
+    (dict(N=0), rn.EINVAL),
+    (dict(eps=-1.0), rn.EINVAL),
+    (dict(eps=float("nan")), rn.EINVAL),
+    (dict(eps=float("inf")), rn.EINVAL),
+    (dict(x=None), rn.EINVAL),
+    (dict(w=None), rn.EINVAL),
+    (dict(y=None), rn.EINVAL),
+    (dict(M=1 << 40, N=1 << 30), rn.EINVAL),
+])
+def test_fwd_argument_errors(args, status):
+    a = dict(x=FAKE, w=FAKE, eps=1e-5, M=4, N=8, dtype=rn.F32, y=FAKE, rstd=None)
+    a.update(args)
+    rc = rn.lib.rmsnorm_fwd(a["x"], a["w"], a["eps"], a["M"], a["N"], a["dtype"], a["y"], a["rstd"], None)
+    assert rc == status
+
+
+def test_fwd_empty_is_noop():
+    assert rn.lib.rmsnorm_fwd(None, None, 1e-5, 0, 8, rn.F32, None, None, None) == rn.OK
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=3), rn.EDTYPE),
+    (dict(M=-5), rn.EINVAL),
+    (dict(dy=None), rn.EINVAL),
+    (dict(rstd=None), rn.EINVAL),
+    (dict(dx=None), rn.EINVAL),
+    (dict(dw=None), rn.EINVAL),
+    (dict(ws=None), rn.EWORKSPACE),
+    (dict(ws=FAKE + 16), rn.EWORKSPACE),
+])
+def test_bwd_argument_errors(args, status):
+    a = dict(x=FAKE, w=FAKE, dy=FAKE, rstd=FAKE, M=4, N=8, dtype=rn.BF16, dx=FAKE, dw=FAKE, ws=FAKE)
+    a.update(args)
+    rc = rn.lib.rmsnorm_bwd(a["x"], a["w"], a["dy"], a["rstd"], a["M"], a["N"], a["dtype"], a["dx"], a["dw"],
+                            a["ws"], 1 << 20, None)
+    assert rc == status
+
+
+def test_workspace_query_argument_errors():
+    assert rn.lib.rmsnorm_bwd_workspace_bytes(4, 8, 9) == rn.EDTYPE
+    assert rn.lib.rmsnorm_bwd_workspace_bytes(-1, 8, rn.F32) == rn.EINVAL
+    assert rn.lib.rmsnorm_bwd_workspace_bytes(0, 8, rn.F32) == 0
+
+
+def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
+    return rn.rmsnorm_select_config(M, N, dtype, is_bwd, aligned, cus, blocks).as_dict()
+
+
+@pytest.mark.parametrize("N,dtype,is_bwd,lpr,vpt", [
+    (128, rn.BF16, 0, 16, 1),      # QK-norm: 16 vectors -> 16 lanes, 4 rows per wavefront
+    (128, rn.BF16, 1, 16, 1),
+    (1024, rn.F32, 0, 64, 4),
+    (1024, rn.F32, 1, 64, 4),
+    (4096, rn.BF16, 0, 64, 8),
+    (4096, rn.BF16, 1, 128, 4),
+    (5120, rn.BF16, 0, 128, 5),
+    (7168, rn.BF16, 0, 128, 7),
+    (7168, rn.BF16, 1, 256, 4),
+    (8192, rn.BF16, 0, 128, 8),
+    (32768, rn.BF16, 0, 512, 8),
+    (32768, rn.BF16, 1, 1024, 4),
+    (8, rn.BF16, 0, 1, 1),
+    (24, rn.BF16, 0, 4, 1),        # 3 vectors -> 4 lanes, one masked
+])
+def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
+    c = cfg(4096, N, dtype, is_bwd)
+    assert c["vector_path"] == 1
+    assert (c["lanes_per_row"], c["vecs_per_lane"]) == (lpr, vpt)
+    assert c["wg_threads"] == max(lpr, 256)
+    assert c["rows_per_wg"] == c["wg_threads"] // lpr
+    nvec = N * (4 if dtype == rn.F32 else 2) // 16
+    assert (vpt - 1) * lpr < nvec <= vpt * lpr
+
+
+@pytest.mark.parametrize("N,dtype,aligned", [(13, rn.F32, 1), (257, rn.BF16, 1), (4096, rn.BF16, 0),
+                                             (65536 + 8, rn.BF16, 1), (3, rn.BF16, 1)])
+def test_ladder_scalar_cases(N, dtype, aligned):
+    c = cfg(100, N, dtype, 0, aligned=aligned)
+    assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
+
+
+def test_ladder_grid_and_workspace_shape():
+    c = cfg(16384, 4096, rn.BF16, 1, cus=256, blocks=2)
+    assert c["grid"] == 512 and c["partial_rows"] == 512 and c["partial_stride"] == 4096
+    c = cfg(10, 4096, rn.BF16, 1, cus=256, blocks=2)      # fewer row blocks than resident slots
+    assert c["grid"] == (10 + c["rows_per_wg"] - 1) // c["rows_per_wg"]
+    c = cfg(7, 13, rn.F32, 1)
+    assert c["partial_stride"] == 64
+    # the ladder depends only on its arguments
+    assert cfg(16384, 4096, rn.BF16, 1) == cfg(16384, 4096, rn.BF16, 1)
+
+
+def test_select_config_argument_errors():
+    with pytest.raises(rn.RmsnormError):
+        rn.rmsnorm_select_config(4, 8, rn.F32, 0, 1, 0, 1)
+    with pytest.raises(rn.RmsnormError):
+        rn.rmsnorm_select_config(4, 8, 5, 0, 1, 256, 1)
+    with pytest.raises(rn.RmsnormError):
+        rn.rmsnorm_select_config(4, 8, rn.F32, 2, 1, 256, 1)

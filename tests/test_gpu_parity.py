@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and ragged shapes compare every element; the full-size synthetic
+workloads compare sampled rows of y and dx, every rstd, and every dW column
+(the oracle computes those exactly one by one), in the launch configuration
+the library chooses by default -- the one the benchmark times.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import memory_bound_normalization_rmsnorm_amd as rn  # noqa: E402
+import oracle  # noqa: E402
+import synthetic_inputs as si  # noqa: E402
+from parity_util import (DT, check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd,  # noqa: E402
+                         term_rms, to_device, to_host, widen)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hello_gpu_ch13_worked_examples.json")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def full_check(x, w, dy, eps, dtype, cfg_f=None, cfg_b=None):
+    y, rstd = gpu_fwd(x, w, eps, dtype, cfg=cfg_f)
+    oy, orr = oracle.fwd(x, w, eps, dtype)
+    check_rows(y, oy, dtype, "y")
+    check_rstd(rstd, orr)
+    dx, dw = gpu_bwd(x, w, dy, rstd, dtype, cfg=cfg_b)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, dtype)
+    check_rows(dx, odx, dtype, "dx", floor=term_rms(x, w, dy, orr, dtype))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, dtype), dtype)
+    return y, rstd, dx, dw
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_worked_examples(dtype):
+    """hello-gpu ch. 13, section 13.1 and Figure 13.1, on the GPU."""
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = si.to_storage(np.array([c["x"]], np.float32), dtype)
+        w = si.to_storage(np.array(c["w"], np.float32), dtype)
+        eps = si.eps_f32(c["eps"])
+        y, rstd = gpu_fwd(x, w, eps, dtype)
+        assert abs(rstd[0] - c["r"]) <= c["tol"]
+        yw = widen(y, dtype)
+        for j, v in c["y"].items():
+            # printed to 4 decimals; bf16 adds at most 2^-8 relative
+            tol = c["tol"] + (2.0 ** -8 * abs(v) if dtype == "bf16" else 0.0)
+            assert abs(yw[0, int(j)] - v) <= tol
+        oy, orr = oracle.fwd(x, w, eps, dtype)
+        check_rows(y, oy, dtype, "y")
+        check_rstd(rstd, orr)
+
+
+SMALL_SHAPES = [
+    (1, 1), (3, 13), (33, 257), (7, 8), (5, 64), (17, 128), (129, 1000), (64, 1024), (31, 4096),
+    (19, 5120), (9, 7168), (3, 8192), (2, 32768), (2, 65536), (300, 96), (1000, 16), (257, 40),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N", SMALL_SHAPES, ids=lambda v: str(v))
+def test_parity_small(M, N, dtype):
+    _say(f"parity_small M={M} N={N} {dtype}")
+    x, w, dy = si.random_case(M, N, dtype, seed=1000 + M * 7 + N, dy_scale=1.0 if dtype == "f32" else 1e-2)
+    full_check(x, w, dy, si.eps_f32(1e-5), dtype)
+
+
+def _instantiated_shapes():
+    # every (lanes_per_row, vecs_per_lane) kernel the library builds
+    out = [(l, 1) for l in (1, 2, 4, 8, 16, 32)]
+    out += [(l, v) for l in (64, 128, 256, 512, 1024) for v in range(1, 9)]
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_vector_kernel(dtype):
+    """Each instantiated (lanes, vectors) kernel, forced through *_with_config,
+    on a ragged row (last vector slot partly empty), a ragged row count and a
+    grid smaller than the row blocks (so workgroups loop)."""
+    epv = 4 if dtype == "f32" else 8
+    for lpr, vpt in _instantiated_shapes():
+        nvec = max(1, lpr * (vpt - 1) + max(1, lpr // 2 + 1))  # the last slot is partial
+        nvec = min(nvec, lpr * vpt)
+        N = nvec * epv
+        wg = max(lpr, 256)
+        rpw = wg // lpr
+        M = 3 * rpw + 1
+        for grid in (1, 2):
+            cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, grid=grid)
+            x, w, dy = si.random_case(M, N, dtype, seed=lpr * 100 + vpt, dy_scale=1e-2)
+            _say(f"kernel lpr={lpr} vpt={vpt} N={N} M={M} grid={grid} {dtype}")
+            full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_f=cfg, cfg_b=cfg)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scalar_path_forced_and_unaligned(dtype):
+    """The scalar kernel (forced, and chosen for unaligned pointers)."""
+    M, N = 37, 4096
+    x, w, dy = si.random_case(M, N, dtype, seed=77, dy_scale=1e-2)
+    cfg = rn.rmsnorm_config(vector_path=0, grid=5)
+    full_check(x, w, dy, si.eps_f32(1e-5), dtype, cfg_f=cfg, cfg_b=cfg)
+    # unaligned: views one element into larger buffers
+    xd = to_device(np.concatenate([x.reshape(-1)[:1], x.reshape(-1)]), dtype)[1:]
+    wd = to_device(np.concatenate([w[:1], w]), dtype)[1:]
+    y = torch.full((M * N + 1,), float("nan"), dtype=xd.dtype, device="cuda")[1:]
+    rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd(xd, wd, si.eps_f32(1e-5), M, N, DT[dtype], y, rstd)
+    torch.cuda.synchronize()
+    oy, orr = oracle.fwd(x, w, si.eps_f32(1e-5), dtype)
+    check_rows(to_host(y, dtype).reshape(M, N), oy, dtype, "y (unaligned)")
+    check_rstd(rstd.cpu().numpy(), orr)
+
+
+def test_backward_with_oracle_rstd():
+    """Feeding the backward the oracle's rstd (rounded to fp32) separates
+    backward error from forward error."""
+    M, N, dtype = 64, 4096, "bf16"
+    x, w, dy = si.random_case(M, N, dtype, seed=91, dy_scale=1e-2)
+    eps = si.eps_f32(1e-6)
+    _, orr = oracle.fwd(x, w, eps, dtype, want_y=False)
+    dx, dw = gpu_bwd(x, w, dy, orr.astype(np.float32), dtype)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, dtype)
+    check_rows(dx, odx, dtype, "dx", floor=term_rms(x, w, dy, orr, dtype))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, dtype), dtype)
+
+
+def test_invariants_on_gpu():
+    """hello-gpu ch. 13, section 13.4: zero input -> zero output, zero weight ->
+    zero output; and zero dy -> zero dx and dW."""
+    for dtype in ("f32", "bf16"):
+        M, N = 8, 1024
+        x, w, dy = si.random_case(M, N, dtype, seed=5)
+        x[2] = 0
+        y, rstd = gpu_fwd(x, w, si.eps_f32(1e-5), dtype)
+        assert np.all(widen(y[2], dtype) == 0.0)
+        assert rstd[2] == pytest.approx(1.0 / np.sqrt(si.eps_f32(1e-5)), rel=1e-6)
+        y0, _ = gpu_fwd(x, np.zeros_like(w), si.eps_f32(1e-5), dtype)
+        assert np.all(widen(y0, dtype) == 0.0)
+        dx, dw = gpu_bwd(x, w, np.zeros_like(dy), rstd, dtype)
+        assert np.all(widen(dx, dtype) == 0.0) and np.all(dw == 0.0)
+
+
+def test_large_magnitudes_fp32():
+    """Rows near 1e15 (squares ~1e30, still finite in fp32 sums) and tiny rows."""
+    M, N, dtype = 6, 4096, "f32"
+    x, w, dy = si.random_case(M, N, dtype, seed=8)
+    scale = np.array([1e15, 1e-15, 1.0, 1e10, 1e-10, 3.0], np.float32)[:, None]
+    x = (x * scale).astype(np.float32)
+    full_check(x, w, dy, si.eps_f32(1e-5), dtype)
+
+
+def test_empty_and_degenerate():
+    for dtype in ("f32", "bf16"):
+        N = 64
+        x = torch.empty((0, N), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
+        w = torch.ones(N, dtype=x.dtype, device="cuda")
+        rn.rmsnorm_fwd(x, w, 1e-5, 0, N, DT[dtype], x, None)
+        dw = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+        assert rn.rmsnorm_bwd_workspace_bytes(0, N, DT[dtype]) == 0
+        rn.rmsnorm_bwd(x, w, x, None, 0, N, DT[dtype], x, dw, None, 0)
+        torch.cuda.synchronize()
+        assert torch.all(dw == 0)
+
+
+def test_error_codes_on_device():
+    M, N = 16, 256
+    x = torch.randn(M, N, device="cuda")
+    w = torch.ones(N, device="cuda")
+    dx = torch.empty_like(x)
+    dw = torch.empty(N, device="cuda")
+    rstd = torch.ones(M, device="cuda")
+    need = rn.rmsnorm_bwd_workspace_bytes(M, N, rn.F32)
+    ws = torch.empty(need // 4 + 64, device="cuda")
+    with pytest.raises(rn.RmsnormError) as e:
+        rn.rmsnorm_bwd(x, w, x, rstd, M, N, rn.F32, dx, dw, ws, need - 4)
+    assert e.value.status == rn.EWORKSPACE
+    with pytest.raises(rn.RmsnormError) as e:
+        rn.rmsnorm_bwd(x, w, x, rstd, M, N, rn.F32, dx, dw, ws.data_ptr() + 4, need)
+    assert e.value.status == rn.EWORKSPACE
+    with pytest.raises(rn.RmsnormError) as e:  # 8 lanes x 1 vector cannot cover 64 fp32 vectors
+        rn.rmsnorm_fwd_with_config(x, w, 1e-5, M, N, rn.F32, dx, rstd, rn.rmsnorm_config(
+            vector_path=1, lanes_per_row=8, vecs_per_lane=1, grid=1))
+    assert e.value.status == rn.ECONFIG
+
+
+def test_dw_bit_identical_across_reruns():
+    """Same input -> same dW bits, 10 reruns, and again on fresh buffers at
+    other addresses ("RMSNorm backward (almost) without the column
+    reduction", section "The problem: summing across rows")."""
+    wl = si.WORKLOADS["bf16_16384x4096"]
+    M, N = 4096, wl.N
+    x, w, dy = si.random_case(M, N, "bf16", seed=123, dy_scale=1e-2)
+    y, rstd = gpu_fwd(x, w, si.eps_f32(wl.eps), "bf16")
+    ref_dx, ref = gpu_bwd(x, w, dy, rstd, "bf16")
+    for i in range(10):
+        _pad = torch.empty(1 + i * 4096, device="cuda")  # shift the allocator's addresses
+        dx, dw = gpu_bwd(x, w, dy, rstd, "bf16")
+        assert np.array_equal(dw.view(np.uint32), ref.view(np.uint32)), f"dW bits differ on rerun {i}"
+        assert np.array_equal(dx, ref_dx), f"dx bits differ on rerun {i}"
+        del _pad
+
+
+def _sample_rows(M, k=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(k, M), replace=False).tolist())
+    rows |= {0, 1, M - 2, M - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < M), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", list(si.WORKLOADS))
+def test_full_size_workload(name):
+    """Full-size synthetic workload in the default launch configuration:
+    sampled rows of y and dx, every rstd and every dW column."""
+    wl = si.WORKLOADS[name]
+    _say(f"workload {name}: generating inputs")
+    x, w, dy = si.make_inputs(wl)
+    eps = si.eps_f32(wl.eps)
+    _say(f"workload {name}: gpu")
+    y, rstd = gpu_fwd(x, w, eps, wl.dtype)
+    dx, dw = gpu_bwd(x, w, dy, rstd, wl.dtype)
+    rows = _sample_rows(wl.M, seed=wl.seed)
+    if wl.outlier_rows:
+        rows = np.union1d(rows, si.outlier_picks(wl)[0])
+    _say(f"workload {name}: oracle")
+    oy, _ = oracle.fwd(x, w, eps, wl.dtype, rows=rows)
+    check_rows(y[rows], oy, wl.dtype, "y")
+    _, orr = oracle.fwd(x, w, eps, wl.dtype, want_y=False)
+    check_rstd(rstd, orr)
+    odx, orows = oracle.bwd_dx(x, w, dy, eps, wl.dtype, rows=rows)
+    check_rows(dx[rows], odx, wl.dtype, "dx", floor=term_rms(x, w, dy, orows, wl.dtype, rows=rows))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, wl.dtype), wl.dtype)
+    assert np.all(np.isfinite(widen(y, wl.dtype))) and np.all(np.isfinite(widen(dx, wl.dtype)))
