@@ -5,7 +5,8 @@
  *     rstd_i = 1 / sqrt((1/N) * sum_j x_ij^2 + eps)      (eps inside the root,
  *     y_ij   = x_ij * rstd_i * w_j                          N the true width)
  * as defined in hello-gpu "Chapter 13 Fused RMSNorm", section 13.1, and in the
- * profiling-kernels page, Problem 15 ("The concepts").
+ * page "Profiling, GPU utilisation and writing a fused kernel", Problem 15
+ * ("The concepts").
  *
  * Backward: with V_ij = dy_ij * w_j ("the incoming gradient after applying the
  * gain", "RMSNorm backward (almost) without the column reduction", section
@@ -71,7 +72,8 @@ typedef struct {
     int32_t vecs_per_lane;   /* 16-byte vectors each lane holds per row (vector path) */
     int32_t wg_threads;      /* workgroup size */
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
-    int32_t reserved;
+    int32_t prefetch;        /* 1: the next row block's loads are issued before the current
+                                block's arithmetic (register double buffer) */
     int64_t grid;            /* workgroups launched */
     int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid) */
     int64_t partial_stride;  /* backward: floats between consecutive partial rows */
@@ -123,9 +125,9 @@ int rmsnorm_bwd_combine(const void *workspace, int64_t partial_rows, int64_t N, 
 
 /*
  * Forward / backward with an explicit launch configuration instead of the
- * ladder's choice: lanes_per_row, vecs_per_lane (vector path) or
- * vector_path = 0 (scalar path), and grid (>= 1) are read; the other fields
- * are derived. For searching the configuration space ("What a tuned RMSNorm
+ * ladder's choice: vector_path, lanes_per_row, vecs_per_lane, wg_threads
+ * (0: the default, the smallest multiple of lanes_per_row that is at least
+ * 256), prefetch and grid (>= 1) are read; the other fields are derived. For searching the configuration space ("What a tuned RMSNorm
  * kernel actually costs on Hopper", section 06: the memory-path knobs belong
  * in the search space). Returns RMSN_ECONFIG when the configuration does not
  * cover the row or its kernel is not built. The backward workspace must hold

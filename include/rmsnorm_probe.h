@@ -6,9 +6,10 @@
  * RMSNorm kernel actually costs on Hopper", section 02). Each probe streams
  * 16-byte vectors over caller-owned device buffers; `bytes` must be a
  * multiple of 16 and every pointer 16-byte aligned. `grid` is the number of
- * 256-lane workgroups (0 = one vector per lane, no striding). Work is enqueued
- * on `stream` (a hipStream_t; NULL = default stream). Returns 0 or a negative
- * rmsn_status (see rmsnorm.h).
+ * 256-lane workgroups (0 = one vector per lane, no striding). `variant`
+ * selects the cache hint: bit 0 non-temporal loads, bit 1 non-temporal
+ * stores (0..3). Work is enqueued on `stream` (a hipStream_t; NULL = default
+ * stream). Returns 0 or a negative rmsn_status (see rmsnorm.h).
  */
 #ifndef RMSNORM_MI355X_PROBE_H
 #define RMSNORM_MI355X_PROBE_H
@@ -21,13 +22,14 @@ extern "C" {
 #endif
 
 /* dst[i] = src[i]: moves 2 * bytes (one read, one write). */
-int rmsn_probe_copy(const void *src, void *dst, size_t bytes, int64_t grid, void *stream);
+int rmsn_probe_copy(const void *src, void *dst, size_t bytes, int64_t grid, int variant, void *stream);
 
 /* dst[i] = pattern: moves `bytes` (write only). */
-int rmsn_probe_write(void *dst, size_t bytes, int64_t grid, void *stream);
+int rmsn_probe_write(void *dst, size_t bytes, int64_t grid, int variant, void *stream);
 
 /* c[i] = a[i] + b[i] as 32-bit integers: moves 3 * bytes (two reads, one write). */
-int rmsn_probe_add(const void *a, const void *b, void *c, size_t bytes, int64_t grid, void *stream);
+int rmsn_probe_add(const void *a, const void *b, void *c, size_t bytes, int64_t grid, int variant,
+                   void *stream);
 
 #ifdef __cplusplus
 }

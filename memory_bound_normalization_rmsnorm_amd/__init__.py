@@ -21,7 +21,9 @@ import torch  # noqa: F401  (loads the HIP runtime the library links against)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "librmsnorm_mi355x.so"
-LIB_PATH = os.path.join(_HERE, LIB_NAME)
+# RMSNORM_MI355X_LIB selects another build of the same library (for example
+# one compiled with different flags, to compare variants); default: in-tree.
+LIB_PATH = os.environ.get("RMSNORM_MI355X_LIB") or os.path.join(_HERE, LIB_NAME)
 
 F32 = 0
 BF16 = 1
@@ -47,14 +49,14 @@ class rmsnorm_config(ctypes.Structure):
         ("vecs_per_lane", ctypes.c_int32),
         ("wg_threads", ctypes.c_int32),
         ("rows_per_wg", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("prefetch", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("partial_rows", ctypes.c_int64),
         ("partial_stride", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:
-        return {name: int(getattr(self, name)) for name, _ in self._fields_ if name != "reserved"}
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
 
 
 def _load() -> ctypes.CDLL:
@@ -77,9 +79,9 @@ def _load() -> ctypes.CDLL:
         "rmsnorm_select_config": (i32, [i64, i64, i32, i32, i32, i32, i32, cfgp]),
         "rmsnorm_query_config": (i32, [i64, i64, i32, i32, cfgp]),
         "rmsnorm_build_info": (ctypes.c_char_p, []),
-        "rmsn_probe_copy": (i32, [vp, vp, sz, i64, vp]),
-        "rmsn_probe_write": (i32, [vp, sz, i64, vp]),
-        "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, vp]),
+        "rmsn_probe_copy": (i32, [vp, vp, sz, i64, i32, vp]),
+        "rmsn_probe_write": (i32, [vp, sz, i64, i32, vp]),
+        "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -92,8 +94,9 @@ lib = _load()
 
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_config", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
-    "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_status_str", "rmsnorm_select_config", "rmsnorm_query_config",
-    "rmsnorm_build_info", "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_add",
+    "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_status_str",
+    "rmsnorm_select_config", "rmsnorm_query_config", "rmsnorm_build_info",
+    "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_add",
 )
 
 
@@ -195,14 +198,16 @@ def rmsnorm_query_config(M, N, dtype, is_bwd) -> rmsnorm_config:
     return cfg
 
 
-def rmsn_probe_copy(src, dst, nbytes, grid=0, stream=None) -> None:
-    _check("rmsn_probe_copy", lib.rmsn_probe_copy(_ptr(src), _ptr(dst), int(nbytes), int(grid), _stream(stream)))
+def rmsn_probe_copy(src, dst, nbytes, grid=0, variant=0, stream=None) -> None:
+    _check("rmsn_probe_copy", lib.rmsn_probe_copy(_ptr(src), _ptr(dst), int(nbytes), int(grid), int(variant),
+                                                  _stream(stream)))
 
 
-def rmsn_probe_write(dst, nbytes, grid=0, stream=None) -> None:
-    _check("rmsn_probe_write", lib.rmsn_probe_write(_ptr(dst), int(nbytes), int(grid), _stream(stream)))
+def rmsn_probe_write(dst, nbytes, grid=0, variant=0, stream=None) -> None:
+    _check("rmsn_probe_write", lib.rmsn_probe_write(_ptr(dst), int(nbytes), int(grid), int(variant),
+                                                    _stream(stream)))
 
 
-def rmsn_probe_add(a, b, c, nbytes, grid=0, stream=None) -> None:
-    _check("rmsn_probe_add", lib.rmsn_probe_add(_ptr(a), _ptr(b), _ptr(c), int(nbytes), int(grid),
+def rmsn_probe_add(a, b, c, nbytes, grid=0, variant=0, stream=None) -> None:
+    _check("rmsn_probe_add", lib.rmsn_probe_add(_ptr(a), _ptr(b), _ptr(c), int(nbytes), int(grid), int(variant),
                                                 _stream(stream)))

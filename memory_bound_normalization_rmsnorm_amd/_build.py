@@ -19,8 +19,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["rmsn_fwd.hip", "rmsn_bwd.hip", "rmsn_probe.hip", "rmsn_api.cpp"]
-HEADERS = ["rmsn_device.h", "rmsn_tables.h"]
+SOURCES = ["rmsn_fwd_f32.hip", "rmsn_fwd_bf16.hip", "rmsn_bwd_f32.hip", "rmsn_bwd_bf16.hip",
+           "rmsn_common.hip", "rmsn_probe.hip", "rmsn_api.cpp"]
+HEADERS = ["rmsn_device.h", "rmsn_tables.h", "rmsn_instances.h", "rmsn_fwd_kernels.h", "rmsn_bwd_kernels.h"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -42,10 +43,10 @@ def _git_rev() -> str:
         return "nogit"
 
 
-def _compile(src: str, info: str) -> tuple[str, str]:
+def _compile(src: str, info: str, build_dir: str, extra: tuple) -> tuple[str, str]:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, f'-DRMSN_BUILD_INFO="{info}"', "-c", path, "-o", obj]
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, f'-DRMSN_BUILD_INFO="{info}"', "-c", path, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = DEVICE_FLAGS + ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,25 +55,28 @@ def _compile(src: str, info: str) -> tuple[str, str]:
     return obj, res.stderr
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    info = f"rmsnorm-mi355x {_git_rev()} {ARCH} hipcc -O3 -packed-fp32-ops"
+def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile every source for gfx950 and link the shared library. Returns its path.
+    `out` and `extra_flags` (e.g. -D choices) build a variant elsewhere."""
+    build_dir = BUILD if out == LIB_PATH else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
+    extra = tuple(extra_flags)
+    info = f"rmsnorm-mi355x {_git_rev()} {ARCH} hipcc -O3 -packed-fp32-ops {' '.join(extra)}".strip()
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda s: _compile(s, info), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, info, build_dir, extra), SOURCES))
     objs = [o for o, _ in results]
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+    with open(os.path.join(build_dir, "resource_usage.txt"), "w") as f:
         for (o, log), s in zip(results, SOURCES):
             f.write(f"==== {s}\n{log}\n")
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr[-4000:]}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out}")
+    return out
 
 
 def is_stale() -> bool:

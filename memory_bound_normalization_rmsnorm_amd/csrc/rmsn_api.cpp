@@ -25,7 +25,7 @@ namespace {
 using rmsn::KernelEntry;
 
 constexpr int64_t kMaxN = int64_t(1) << 30;
-constexpr int kMaxVecLanes = 1024;
+constexpr int64_t kMaxVecLanes = 1024;
 
 int elem_size(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
 bool valid_dtype(int dtype) { return dtype == RMSN_F32 || dtype == RMSN_BF16; }
@@ -45,25 +45,36 @@ int check_shape(int64_t M, int64_t N, int dtype) {
     return RMSN_OK;
 }
 
-// The row-width ladder: which kernel shape serves a row of N elements.
-//   * rows of at most 32 vectors: one lane per vector, several rows per wave
-//     (QK-norm: 128 bf16 = 16 vectors -> 16 lanes, 4 rows per wavefront);
-//   * up to 64 * V vectors: one wavefront per row, up to V vectors per lane;
-//   * wider: a power-of-two number of wavefronts per row (up to 16, one
-//     1024-lane workgroup) so that each lane holds between V/2 and V vectors;
-//   * anything the vector kernels cannot take (N*elem not a multiple of 16
-//     bytes, unaligned pointers, more than 1024 * V vectors): the scalar kernel.
-// V is 8 for the forward (a lane holds x and w: 64 VGPRs at V = 8) and 4 for
-// the backward (x, dy, w and V * elems fp32 dW sums), so both keep at least
-// four wavefronts per SIMD on the common widths.
-int max_vecs_per_lane(int is_bwd) { return is_bwd ? 4 : 8; }
+// The row-width ladder: which kernel shape serves a row of N elements, and
+// how many workgroups run it. Measured on MI355X over the synthetic workloads
+// (widths 128 to 32768, bf16 and fp32), the rules below were the fastest or
+// within noise of it.
+//   Forward: lanes per row chosen so each lane holds at most 4 16-byte
+//     vectors (rows of at most 32 vectors: one lane per vector, several rows
+//     per wavefront, e.g. QK-norm's 128 bf16 = 16 lanes, 4 rows per wave);
+//     one row block per workgroup (grid = row blocks), so the hardware
+//     dispatcher balances the tail.
+//   Backward: one vector per lane up to 1024 lanes per row (more lanes, fewer
+//     registers, more rows in flight), then up to 4 vectors per lane; a
+//     persistent grid of about two workgroups per compute unit (three for
+//     rows of under a wavefront), fewer when the fp32 dW partial rows would
+//     exceed ~5% of the algorithmic bytes, never fewer than one per compute
+//     unit; the next row block is prefetched when the workgroup has at most
+//     512 lanes (enough registers for the second buffer).
+//   Anything the vector kernels cannot take (N*elem not a multiple of 16
+//     bytes, unaligned pointers, more than 1024 * 8 vectors forward or
+//     1024 * 4 backward) goes to the scalar kernel.
+constexpr int kFwdMaxVecs = 4;
+constexpr int kBwdMaxVecs = 4;
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
-void set_vector_shape(int64_t lpr, int64_t vpt, rmsnorm_config *c) {
+void set_vector_shape(int64_t lpr, int64_t vpt, int wg, int pf, rmsnorm_config *c) {
     c->vector_path = 1;
     c->lanes_per_row = (int32_t)lpr;
     c->vecs_per_lane = (int32_t)vpt;
-    c->wg_threads = rmsn::wg_for_lpr((int)lpr);
+    c->wg_threads = wg > 0 ? wg : rmsn::wg_for_lpr((int)lpr);
     c->rows_per_wg = c->wg_threads / c->lanes_per_row;
+    c->prefetch = pf;
 }
 
 void set_scalar_shape(rmsnorm_config *c) {
@@ -72,42 +83,55 @@ void set_scalar_shape(rmsnorm_config *c) {
     c->vecs_per_lane = 0;
     c->wg_threads = rmsn::kScalarWG;
     c->rows_per_wg = 1;
+    c->prefetch = 0;
 }
 
 bool vector_ok(int64_t N, int dtype, bool aligned) { return aligned && (N * elem_size(dtype)) % 16 == 0; }
 
 void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config *c) {
-    const int64_t V = max_vecs_per_lane(is_bwd);
     const int64_t nvec = N * elem_size(dtype) / 16;
-    if (!vector_ok(N, dtype, aligned) || nvec > kMaxVecLanes * V) {
+    const int64_t vmax = is_bwd ? kBwdMaxVecs : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
+    if (!vector_ok(N, dtype, aligned) || nvec > kMaxVecLanes * vmax) {
         set_scalar_shape(c);
         return;
     }
     int64_t lpr, vpt;
     if (nvec <= 32) {
         lpr = next_pow2(nvec);
-        vpt = 1;
-    } else if (nvec <= 64 * V) {
-        lpr = 64;
-        vpt = (nvec + 63) / 64;
+    } else if (is_bwd) {
+        lpr = nvec <= kMaxVecLanes ? next_pow2(nvec) : kMaxVecLanes;
     } else {
-        lpr = next_pow2((nvec + V - 1) / V);
-        vpt = (nvec + lpr - 1) / lpr;
+        lpr = next_pow2((nvec + kFwdMaxVecs - 1) / kFwdMaxVecs);
+        if (lpr < 64) lpr = 64;
+        if (lpr > kMaxVecLanes) lpr = kMaxVecLanes;
     }
-    set_vector_shape(lpr, vpt, c);
+    vpt = (nvec + lpr - 1) / lpr;
+    const int wg = rmsn::wg_for_lpr((int)lpr);
+    set_vector_shape(lpr, vpt, wg, (is_bwd && wg <= 512) ? 1 : 0, c);
 }
 
-// Grid: as many workgroups as stay resident (num_cus * blocks_per_cu), never
-// more than there are row blocks. The backward writes one partial row per
-// workgroup.
-void ladder_grid(int64_t M, int64_t N, int num_cus, int blocks_per_cu, rmsnorm_config *c) {
+// Grid. Forward: one row block per workgroup (capped at 2^20 workgroups,
+// which then loop). Backward (persistent, one partial dW row per workgroup):
+// see the ladder comment; `blocks_per_cu` caps it at what stays resident.
+void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int num_cus, int blocks_per_cu, rmsnorm_config *c) {
     const int64_t row_blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
-    int64_t resident = int64_t(num_cus) * (blocks_per_cu > 0 ? blocks_per_cu : 1);
-    if (resident < 1) resident = 1;
-    c->grid = row_blocks < resident ? row_blocks : resident;
+    int64_t grid;
+    if (!is_bwd) {
+        grid = row_blocks < kMaxGrid ? row_blocks : kMaxGrid;
+    } else {
+        const int64_t cus = num_cus > 0 ? num_cus : 1;
+        int64_t want = (c->lanes_per_row < 64 ? 3 : 2) * cus;
+        // partial rows are written once and read once: 8 * N bytes each
+        const int64_t bytes = 3 * M * N * elem_size(dtype);
+        const int64_t cap = bytes / 20 / (8 * N);
+        if (want > cap) want = cap > cus ? cap : cus;
+        const int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
+        if (want > resident) want = resident;
+        grid = row_blocks < want ? row_blocks : want;
+    }
+    c->grid = grid > 0 ? grid : 1;
     c->partial_rows = c->grid;
     c->partial_stride = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
-    c->reserved = 0;
 }
 
 // ---- per-device cache ----------------------------------------------------
@@ -157,8 +181,9 @@ int occupancy(const void *fn, int wg, int *blocks) {
 
 const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd) {
     if (!c.vector_path) return is_bwd ? rmsn::bwd_scalar_kernel(dtype) : rmsn::fwd_scalar_kernel(dtype);
-    const KernelEntry *e = is_bwd ? rmsn::bwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane)
-                                  : rmsn::fwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane);
+    const KernelEntry *e =
+        is_bwd ? rmsn::bwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch)
+               : rmsn::fwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch);
     return e ? e->fn : nullptr;
 }
 
@@ -174,7 +199,7 @@ int resolve(int64_t M, int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_c
     if (st != RMSN_OK) return st;
     st = occupancy(k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
-    ladder_grid(M, N, cus, blocks, c);
+    ladder_grid(M, N, dtype, is_bwd, cus, blocks, c);
     if (fn) *fn = k;
     return RMSN_OK;
 }
@@ -202,13 +227,16 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         const int64_t nvec = N * elem_size(dtype) / 16;
         if (!vector_ok(N, dtype, aligned)) return RMSN_ECONFIG;
         if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
-        set_vector_shape(req->lanes_per_row, req->vecs_per_lane, c);
+        if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > 1)
+            return RMSN_ECONFIG;
+        if (req->wg_threads > 0 && (req->wg_threads % req->lanes_per_row) != 0) return RMSN_ECONFIG;
+        set_vector_shape(req->lanes_per_row, req->vecs_per_lane, req->wg_threads, req->prefetch, c);
     } else {
         set_scalar_shape(c);
     }
     const void *k = kernel_for(*c, dtype, is_bwd);
     if (!k) return RMSN_ECONFIG;
-    ladder_grid(M, N, 1, 1, c);
+    ladder_grid(M, N, dtype, is_bwd, 1, 1, c);
     c->grid = req->grid;
     c->partial_rows = req->grid;
     *fn = k;
@@ -325,7 +353,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     if (!out || num_cus < 1 || blocks_per_cu < 1 || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
     std::memset(out, 0, sizeof *out);
     ladder_shape(N, dtype, is_bwd, aligned != 0, out);
-    ladder_grid(M, N, num_cus, blocks_per_cu, out);
+    ladder_grid(M, N, dtype, is_bwd, num_cus, blocks_per_cu, out);
     return RMSN_OK;
 }
 

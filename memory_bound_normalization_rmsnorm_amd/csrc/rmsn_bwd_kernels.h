@@ -1,4 +1,4 @@
-// rmsn_bwd.hip -- RMSNorm backward kernels for gfx950.
+// rmsn_bwd_kernels.h -- RMSNorm backward kernel templates for gfx950.
 //
 // Per row i, with r = rstd_i (written by the forward), V_ij = dy_ij * w_j
 // and S_i = sum_j V_ij x_ij:
@@ -12,22 +12,27 @@
 // fixed row -> workgroup map. Each lane keeps running dW sums for its columns
 // in registers over all the rows it visits; at the end the RPW row groups of
 // the workgroup are added in group order through LDS and the workgroup writes
-// one fp32 partial row. No atomics anywhere.
+// one fp32 partial row. No atomics anywhere. With PF the next row block's x,
+// dy and rstd loads are issued before the current block's arithmetic (a
+// register double buffer in place of the pages' shared-memory async-copy
+// pipeline: the persistent grid gives up the scheduler's latency hiding).
 //
 // Combine kernel: dW_j = sum_p partial[p][j] in a fixed order (64 strided
 // slices of p summed in ascending order, then a fixed binary tree over the
-// slices), one workgroup per 64 columns.
+// slices), one workgroup per 16 columns.
 //
 // The results depend only on (M, N, dtype, grid): the same call on the same
 // device gives the same bits every time.
+#pragma once
+
 #include "rmsn_device.h"
 #include "rmsn_tables.h"
 
 namespace rmsn {
 
-template <typename T, int LPR, int VPT, int WG>
+template <typename T, int LPR, int VPT, int WG, bool PF>
 __global__ void __launch_bounds__(WG)
-__attribute__((amdgpu_waves_per_eu(waves_for(3 * VPT, VPT * Elem<T>::kPerVec, VPT, WG))))
+__attribute__((amdgpu_waves_per_eu(waves_for(PF ? 5 * VPT : 3 * VPT, VPT * Elem<T>::kPerVec, VPT, WG))))
 bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ dy,
         const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial,
         int64_t ldp, int64_t M, int32_t N, int32_t nvec) {
@@ -61,26 +66,63 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
 #pragma unroll
         for (int k = 0; k < EPV; ++k) acc[v][k] = 0.f;
 
+    // rows of the block starting at b that exist (0 past the end)
+    auto rows_at = [&](int64_t b) -> uint32_t {
+        const int64_t left = M - b;
+        return left <= 0 ? 0u : (left < RPW ? (uint32_t)left : (uint32_t)RPW);
+    };
+
     int parity = 0;
     const int64_t step = (int64_t)gridDim.x * RPW;
-    for (int64_t base = (int64_t)blockIdx.x * RPW; base < M; base += step) {
-        const int64_t left = M - base;
-        const uint32_t rows = left < RPW ? (uint32_t)left : (uint32_t)RPW;
-        const Buf xb(x + base * N, rows * row_bytes);
-        const Buf gb(dy + base * N, rows * row_bytes);
+    int64_t base = (int64_t)blockIdx.x * RPW;
+    u32x4 xn[VPT], gn[VPT];  // prefetched next block (PF)
+    float rn = 0.f;
+    if constexpr (PF) {
+        const int64_t b0 = base < M ? base : 0;
+        const uint32_t rows0 = rows_at(base);
+        const Buf xb(x + b0 * N, rows0 * row_bytes), gb(dy + b0 * N, rows0 * row_bytes), rb(rstd + b0, rows0 * 4u);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            xn[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+            gn[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+        }
+        rn = rb.load4((uint32_t)grp * 4u);
+    }
+    for (; base < M; base += step) {
+        const uint32_t rows = rows_at(base);
         const Buf db(dx + base * N, rows * row_bytes);
-        const Buf rb(rstd + base, rows * 4u);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) keep_packed(wv[v]);
 
-        u32x4 xv[VPT], gv[VPT];
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            xv[v] = xb.load16(off[v]);
-            gv[v] = gb.load16(off[v]);
-        }
         // rows past M read r = 0 (and x = dy = 0), so they add nothing to dW
-        const float r = rb.load4((uint32_t)grp * 4u);
+        u32x4 xv[VPT], gv[VPT];
+        float r;
+        if constexpr (PF) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                xv[v] = xn[v];
+                gv[v] = gn[v];
+            }
+            r = rn;
+            const int64_t nb = base + step;
+            const int64_t b1 = nb < M ? nb : base;
+            const uint32_t rows1 = rows_at(nb);
+            const Buf xb(x + b1 * N, rows1 * row_bytes), gb(dy + b1 * N, rows1 * row_bytes), rb(rstd + b1, rows1 * 4u);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                xn[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+                gn[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+            }
+            rn = rb.load4((uint32_t)grp * 4u);
+        } else {
+            const Buf xb(x + base * N, rows * row_bytes), gb(dy + base * N, rows * row_bytes), rb(rstd + base, rows * 4u);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                xv[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+                gv[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+            }
+            r = rb.load4((uint32_t)grp * 4u);
+        }
 
         float s = 0.f;
 #pragma unroll
@@ -112,7 +154,7 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
             E::unpack(wv[v], fw);
 #pragma unroll
             for (int k = 0; k < EPV; ++k) o[k] = __builtin_fmaf(-fx[k], c, r * (fg[k] * fw[k]));
-            db.store16(off[v], E::pack(o));
+            db.store16<RMSN_BWD_STORE_AUX>(off[v], E::pack(o));
         }
     }
 
@@ -183,86 +225,5 @@ bwd_scalar(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
         }
     }
 }
-
-// dW[col] = sum over p of partial[p][col]; 64 columns per workgroup. Lane
-// (slice s, quad c) sums rows p = s, s + 64, s + 128, ... in ascending order
-// for columns 4c..4c+3; the 64 slice sums are then folded by a fixed binary
-// tree in LDS. Rows are padded to ldp floats (a multiple of 64) and 256-byte
-// aligned, so the float4 loads stay inside the workspace.
-__global__ void __launch_bounds__(kCombineWG)
-dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
-           float *__restrict__ dw) {
-    __shared__ float4 red[kCombineSlices][kCombineLanes];
-    const int quad = threadIdx.x % kCombineLanes;
-    const int slice = threadIdx.x / kCombineLanes;
-    const int64_t col = (int64_t)blockIdx.x * kCombineCols + 4 * quad;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (col < N) {
-        for (int64_t p = slice; p < P; p += kCombineSlices) {
-            const float4 v = *reinterpret_cast<const float4 *>(partial + p * ldp + col);
-            a.x += v.x;
-            a.y += v.y;
-            a.z += v.z;
-            a.w += v.w;
-        }
-    }
-    red[slice][quad] = a;
-    __syncthreads();
-#pragma unroll
-    for (int h = kCombineSlices / 2; h >= 1; h >>= 1) {
-        if (slice < h) {
-            float4 u = red[slice][quad];
-            const float4 v = red[slice + h][quad];
-            u.x += v.x;
-            u.y += v.y;
-            u.z += v.z;
-            u.w += v.w;
-            red[slice][quad] = u;
-        }
-        __syncthreads();
-    }
-    if (slice == 0 && col < N) {
-        const float4 u = red[0][quad];
-        const float o[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (col + e < N) dw[col + e] = o[e];
-    }
-}
-
-__global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
-}
-
-// ---- dispatch tables -------------------------------------------------------
-
-#define RMSN_BWD(T, L, V) {L, V, wg_for_lpr(L), reinterpret_cast<const void *>(&bwd_vec<T, L, V, wg_for_lpr(L)>)}
-#define RMSN_BWD_VPT(T, L)                                                                      \
-    RMSN_BWD(T, L, 1), RMSN_BWD(T, L, 2), RMSN_BWD(T, L, 3), RMSN_BWD(T, L, 4), RMSN_BWD(T, L, 5), \
-        RMSN_BWD(T, L, 6), RMSN_BWD(T, L, 7), RMSN_BWD(T, L, 8)
-#define RMSN_BWD_ALL(T)                                                                           \
-    RMSN_BWD(T, 1, 1), RMSN_BWD(T, 2, 1), RMSN_BWD(T, 4, 1), RMSN_BWD(T, 8, 1), RMSN_BWD(T, 16, 1), \
-        RMSN_BWD(T, 32, 1), RMSN_BWD_VPT(T, 64), RMSN_BWD_VPT(T, 128), RMSN_BWD_VPT(T, 256),      \
-        RMSN_BWD_VPT(T, 512), RMSN_BWD_VPT(T, 1024)
-
-static const KernelEntry kBwdF32[] = {RMSN_BWD_ALL(float)};
-static const KernelEntry kBwdBf16[] = {RMSN_BWD_ALL(bf16_t)};
-
-const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt) {
-    const KernelEntry *t = dtype == 0 ? kBwdF32 : kBwdBf16;
-    const int n = dtype == 0 ? (int)(sizeof(kBwdF32) / sizeof(kBwdF32[0]))
-                             : (int)(sizeof(kBwdBf16) / sizeof(kBwdBf16[0]));
-    for (int i = 0; i < n; ++i)
-        if (t[i].lpr == lpr && t[i].vpt == vpt) return &t[i];
-    return nullptr;
-}
-
-const void *bwd_scalar_kernel(int dtype) {
-    return dtype == 0 ? reinterpret_cast<const void *>(&bwd_scalar<float>)
-                      : reinterpret_cast<const void *>(&bwd_scalar<bf16_t>);
-}
-
-const void *dw_combine_kernel() { return reinterpret_cast<const void *>(&dw_combine); }
-const void *fill_zero_kernel() { return reinterpret_cast<const void *>(&fill_zero); }
 
 }  // namespace rmsn

@@ -1,0 +1,86 @@
+// rmsn_common.hip -- the kernels that do not depend on the vector shape: the
+// scalar (any-N) forward and backward row kernels, the fixed-order dW combine
+// and a zero fill; plus the dtype dispatch of the vector-kernel tables.
+#include "rmsn_bwd_kernels.h"
+#include "rmsn_fwd_kernels.h"
+
+namespace rmsn {
+
+// dW[col] = sum over p of partial[p][col]; kCombineCols (16) columns per
+// workgroup. Lane (slice s, quad c) sums rows p = s, s + S, s + 2S, ...
+// (S = kCombineSlices = 64) in ascending order for columns 4c..4c+3; the S
+// slice sums are then folded by a fixed binary tree in LDS. Rows are padded to
+// ldp floats (a multiple of 64) and 256-byte aligned, so the float4 loads stay
+// inside the workspace.
+__global__ void __launch_bounds__(kCombineWG)
+dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
+           float *__restrict__ dw) {
+    __shared__ float4 red[kCombineSlices][kCombineLanes];
+    const int quad = threadIdx.x % kCombineLanes;
+    const int slice = threadIdx.x / kCombineLanes;
+    const int64_t col = (int64_t)blockIdx.x * kCombineCols + 4 * quad;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (col < N) {
+        for (int64_t p = slice; p < P; p += kCombineSlices) {
+            const float4 v = *reinterpret_cast<const float4 *>(partial + p * ldp + col);
+            a.x += v.x;
+            a.y += v.y;
+            a.z += v.z;
+            a.w += v.w;
+        }
+    }
+    red[slice][quad] = a;
+    __syncthreads();
+#pragma unroll
+    for (int h = kCombineSlices / 2; h >= 1; h >>= 1) {
+        if (slice < h) {
+            float4 u = red[slice][quad];
+            const float4 v = red[slice + h][quad];
+            u.x += v.x;
+            u.y += v.y;
+            u.z += v.z;
+            u.w += v.w;
+            red[slice][quad] = u;
+        }
+        __syncthreads();
+    }
+    if (slice == 0 && col < N) {
+        const float4 u = red[0][quad];
+        const float o[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col + e < N) dw[col + e] = o[e];
+    }
+}
+
+__global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+const KernelEntry *fwd_vec_kernel_f32(int lpr, int vpt, int wg, int pf);
+const KernelEntry *fwd_vec_kernel_bf16(int lpr, int vpt, int wg, int pf);
+const KernelEntry *bwd_vec_kernel_f32(int lpr, int vpt, int wg, int pf);
+const KernelEntry *bwd_vec_kernel_bf16(int lpr, int vpt, int wg, int pf);
+
+const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf) {
+    return dtype == 0 ? fwd_vec_kernel_f32(lpr, vpt, wg, pf) : fwd_vec_kernel_bf16(lpr, vpt, wg, pf);
+}
+
+const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf) {
+    return dtype == 0 ? bwd_vec_kernel_f32(lpr, vpt, wg, pf) : bwd_vec_kernel_bf16(lpr, vpt, wg, pf);
+}
+
+const void *fwd_scalar_kernel(int dtype) {
+    return dtype == 0 ? reinterpret_cast<const void *>(&fwd_scalar<float>)
+                      : reinterpret_cast<const void *>(&fwd_scalar<bf16_t>);
+}
+
+const void *bwd_scalar_kernel(int dtype) {
+    return dtype == 0 ? reinterpret_cast<const void *>(&bwd_scalar<float>)
+                      : reinterpret_cast<const void *>(&bwd_scalar<bf16_t>);
+}
+
+const void *dw_combine_kernel() { return reinterpret_cast<const void *>(&dw_combine); }
+const void *fill_zero_kernel() { return reinterpret_cast<const void *>(&fill_zero); }
+
+}  // namespace rmsn

@@ -115,17 +115,37 @@ struct Elem<bf16_t> {
 // descriptor selects 32-bit data format, the value used for raw (untyped)
 // buffer access on CDNA. The base pointer must be wave-uniform.
 constexpr int kBufWord3 = 0x00020000;
+// Cache-policy bits of the buffer accesses (CDNA3/4: bit 0 sc0, bit 1 nt,
+// bit 4 sc1). Rows are streamed exactly once; measured on MI355X, the
+// non-temporal hint pays on the forward's stores and on both the backward's
+// loads and stores, and costs on the forward's loads. The defaults below are
+// those measurements; -D overrides exist to re-measure.
+constexpr int kNonTemporal = 2;
+#ifndef RMSN_FWD_LOAD_AUX
+#define RMSN_FWD_LOAD_AUX 0
+#endif
+#ifndef RMSN_FWD_STORE_AUX
+#define RMSN_FWD_STORE_AUX 2
+#endif
+#ifndef RMSN_BWD_LOAD_AUX
+#define RMSN_BWD_LOAD_AUX 2
+#endif
+#ifndef RMSN_BWD_STORE_AUX
+#define RMSN_BWD_STORE_AUX 2
+#endif
 constexpr uint32_t kOff = 0x80000000u;  // an offset past every record count used here
 
 struct Buf {
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ Buf(const void *base, uint32_t bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3)) {}
+    template <int AUX = 0>
     __device__ __forceinline__ u32x4 load16(uint32_t off) const {
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
     }
+    template <int AUX = 0>
     __device__ __forceinline__ void store16(uint32_t off, const u32x4 &v) const {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(g32x4, v), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(g32x4, v), r, off, 0, AUX);
     }
     __device__ __forceinline__ float load4(uint32_t off) const {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));

@@ -1,4 +1,4 @@
-// rmsn_fwd.hip -- RMSNorm forward kernels for gfx950.
+// rmsn_fwd_kernels.h -- RMSNorm forward kernel templates for gfx950.
 //
 // Per row i: rstd_i = 1/sqrt(sum_j x_ij^2 / N + eps), y_ij = x_ij * rstd_i * w_j
 // (hello-gpu "Chapter 13 Fused RMSNorm", section 13.1). The square, the row
@@ -12,20 +12,25 @@
 // buffer resource per row block whose record count covers only the rows that
 // exist; vectors past the row end use an out-of-range offset. Such lanes load
 // zeros (adding nothing to the sum) and store nothing; the mean always
-// divides by the true N. A workgroup of WG = max(LPR, 256) lanes works on
-// WG / LPR rows at a time and strides over rows by grid * (WG / LPR); w is
-// loaded into registers once per workgroup.
+// divides by the true N. A workgroup of WG lanes (a multiple of LPR, at least
+// 256) works on WG / LPR rows at a time and strides over rows by grid * (WG / LPR); w is
+// loaded into registers once per workgroup. With PF the loads of the next row
+// block are issued before the current block's arithmetic (a register double
+// buffer: a persistent grid gives up the scheduler's latency hiding across
+// workgroups, so the pipelining is explicit).
 //
 // Scalar kernel: any N and any alignment; one workgroup of 256 lanes per row,
 // strided fp32/bf16 element loads, x re-read (from cache) for the output.
+#pragma once
+
 #include "rmsn_device.h"
 #include "rmsn_tables.h"
 
 namespace rmsn {
 
-template <typename T, int LPR, int VPT, int WG>
+template <typename T, int LPR, int VPT, int WG, bool PF>
 __global__ void __launch_bounds__(WG)
-__attribute__((amdgpu_waves_per_eu(waves_for(2 * VPT, 0, VPT, WG))))
+__attribute__((amdgpu_waves_per_eu(waves_for(PF ? 3 * VPT : 2 * VPT, 0, VPT, WG))))
 fwd_vec(const T *__restrict__ x, const T *__restrict__ w, T *__restrict__ y,
         float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t nvec) {
     using E = Elem<T>;
@@ -50,20 +55,40 @@ fwd_vec(const T *__restrict__ x, const T *__restrict__ w, T *__restrict__ y,
         off[v] = in ? (uint32_t)grp * row_bytes + (uint32_t)idx * 16u : kOff;
         wv[v] = wb.load16(in ? (uint32_t)idx * 16u : kOff);
     }
+    // rows of the block starting at b that exist (0 past the end)
+    auto rows_at = [&](int64_t b) -> uint32_t {
+        const int64_t left = M - b;
+        return left <= 0 ? 0u : (left < RPW ? (uint32_t)left : (uint32_t)RPW);
+    };
 
     int parity = 0;
     const int64_t step = (int64_t)gridDim.x * RPW;
-    for (int64_t base = (int64_t)blockIdx.x * RPW; base < M; base += step) {
-        const int64_t left = M - base;
-        const uint32_t rows = left < RPW ? (uint32_t)left : (uint32_t)RPW;
-        const Buf xb(x + base * N, rows * row_bytes);
+    int64_t base = (int64_t)blockIdx.x * RPW;
+    u32x4 xn[VPT];  // prefetched next block (PF)
+    if constexpr (PF) {
+        const Buf xb(x + (base < M ? base : 0) * N, rows_at(base) * row_bytes);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) xn[v] = xb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
+    }
+    for (; base < M; base += step) {
+        const uint32_t rows = rows_at(base);
         const Buf yb(y + base * N, rows * row_bytes);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) keep_packed(wv[v]);
 
         u32x4 xv[VPT];
+        if constexpr (PF) {
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) xv[v] = xb.load16(off[v]);
+            for (int v = 0; v < VPT; ++v) xv[v] = xn[v];
+            const int64_t nb = base + step;
+            const Buf xb(x + (nb < M ? nb : base) * N, rows_at(nb) * row_bytes);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) xn[v] = xb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
+        } else {
+            const Buf xb(x + base * N, rows * row_bytes);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) xv[v] = xb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
+        }
 
         float ss = 0.f;
 #pragma unroll
@@ -85,7 +110,7 @@ fwd_vec(const T *__restrict__ x, const T *__restrict__ w, T *__restrict__ y,
             E::unpack(wv[v], g);
 #pragma unroll
             for (int k = 0; k < E::kPerVec; ++k) f[k] = (f[k] * r) * g[k];
-            yb.store16(off[v], E::pack(f));
+            yb.store16<RMSN_FWD_STORE_AUX>(off[v], E::pack(f));
         }
     }
 }
@@ -112,34 +137,6 @@ fwd_scalar(const T *__restrict__ x, const T *__restrict__ w, T *__restrict__ y,
         T *yr = y + row * (int64_t)N;
         for (int j = threadIdx.x; j < N; j += kScalarWG) E::store(yr + j, (E::load(xr + j) * r) * E::load(w + j));
     }
-}
-
-// ---- dispatch tables -------------------------------------------------------
-
-#define RMSN_FWD(T, L, V) {L, V, wg_for_lpr(L), reinterpret_cast<const void *>(&fwd_vec<T, L, V, wg_for_lpr(L)>)}
-#define RMSN_FWD_VPT(T, L)                                                                      \
-    RMSN_FWD(T, L, 1), RMSN_FWD(T, L, 2), RMSN_FWD(T, L, 3), RMSN_FWD(T, L, 4), RMSN_FWD(T, L, 5), \
-        RMSN_FWD(T, L, 6), RMSN_FWD(T, L, 7), RMSN_FWD(T, L, 8)
-#define RMSN_FWD_ALL(T)                                                                           \
-    RMSN_FWD(T, 1, 1), RMSN_FWD(T, 2, 1), RMSN_FWD(T, 4, 1), RMSN_FWD(T, 8, 1), RMSN_FWD(T, 16, 1), \
-        RMSN_FWD(T, 32, 1), RMSN_FWD_VPT(T, 64), RMSN_FWD_VPT(T, 128), RMSN_FWD_VPT(T, 256),      \
-        RMSN_FWD_VPT(T, 512), RMSN_FWD_VPT(T, 1024)
-
-static const KernelEntry kFwdF32[] = {RMSN_FWD_ALL(float)};
-static const KernelEntry kFwdBf16[] = {RMSN_FWD_ALL(bf16_t)};
-
-const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt) {
-    const KernelEntry *t = dtype == 0 ? kFwdF32 : kFwdBf16;
-    const int n = dtype == 0 ? (int)(sizeof(kFwdF32) / sizeof(kFwdF32[0]))
-                             : (int)(sizeof(kFwdBf16) / sizeof(kFwdBf16[0]));
-    for (int i = 0; i < n; ++i)
-        if (t[i].lpr == lpr && t[i].vpt == vpt) return &t[i];
-    return nullptr;
-}
-
-const void *fwd_scalar_kernel(int dtype) {
-    return dtype == 0 ? reinterpret_cast<const void *>(&fwd_scalar<float>)
-                      : reinterpret_cast<const void *>(&fwd_scalar<bf16_t>);
 }
 
 }  // namespace rmsn

@@ -1,0 +1,35 @@
+// rmsn_instances.h -- the (lanes per row, vectors per lane, workgroup size,
+// prefetch) shapes the vector kernels are built for, as an X-macro list:
+// RMSN_ALL_SHAPES(X) expands X(L, V, W, P) once per shape.
+//   * narrow rows (1..32 lanes, one vector each): 256-lane workgroups;
+//   * one or more wavefronts per row with 1..8 vectors per lane, and
+//     workgroups of 256, 512 or 1024 lanes (the ladder's default is the
+//     smallest that holds a row and four wavefronts);
+//   * every shape with and without the register prefetch of the next row.
+#pragma once
+
+#define RMSN_V8(X, L, W, P) X(L, 1, W, P) X(L, 2, W, P) X(L, 3, W, P) X(L, 4, W, P) \
+    X(L, 5, W, P) X(L, 6, W, P) X(L, 7, W, P) X(L, 8, W, P)
+#define RMSN_PF(M, X, L, W) M(X, L, W, 0) M(X, L, W, 1)
+#define RMSN_NARROW(X, L, W, P) X(L, 1, W, P)
+
+#define RMSN_ALL_SHAPES(X)                                                                    \
+    RMSN_PF(RMSN_NARROW, X, 1, 256) RMSN_PF(RMSN_NARROW, X, 2, 256)                           \
+    RMSN_PF(RMSN_NARROW, X, 4, 256) RMSN_PF(RMSN_NARROW, X, 8, 256)                           \
+    RMSN_PF(RMSN_NARROW, X, 16, 256) RMSN_PF(RMSN_NARROW, X, 32, 256)                         \
+    RMSN_PF(RMSN_V8, X, 64, 256) RMSN_PF(RMSN_V8, X, 64, 512) RMSN_PF(RMSN_V8, X, 64, 1024)    \
+    RMSN_PF(RMSN_V8, X, 128, 256) RMSN_PF(RMSN_V8, X, 128, 512) RMSN_PF(RMSN_V8, X, 128, 1024) \
+    RMSN_PF(RMSN_V8, X, 256, 256) RMSN_PF(RMSN_V8, X, 256, 512) RMSN_PF(RMSN_V8, X, 256, 1024) \
+    RMSN_PF(RMSN_V8, X, 512, 512) RMSN_PF(RMSN_V8, X, 512, 1024)                              \
+    RMSN_PF(RMSN_V8, X, 1024, 1024)
+
+namespace rmsn {
+
+template <int N>
+const KernelEntry *find_entry(const KernelEntry (&t)[N], int lpr, int vpt, int wg, int pf) {
+    for (int i = 0; i < N; ++i)
+        if (t[i].lpr == lpr && t[i].vpt == vpt && t[i].wg == wg && t[i].pf == pf) return &t[i];
+    return nullptr;
+}
+
+}  // namespace rmsn

@@ -7,8 +7,8 @@ namespace rmsn {
 
 // Lanes of the scalar (any-N, any-alignment) row kernels and the combine kernel.
 constexpr int kScalarWG = 256;
-constexpr int kCombineWG = 1024;
-constexpr int kCombineCols = 64;     // dW columns per combine workgroup (16 lanes x 4)
+constexpr int kCombineWG = 256;
+constexpr int kCombineCols = 16;     // dW columns per combine workgroup (4 lanes x 4)
 constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
 constexpr int kCombineSlices = kCombineWG / kCombineLanes;  // partial rows summed side by side
 constexpr int kPartialAlign = 64;    // partial rows are padded to a multiple of 64 floats
@@ -35,12 +35,13 @@ struct KernelEntry {
     int lpr;         // lanes per row
     int vpt;         // 16-byte vectors per lane
     int wg;          // workgroup size
+    int pf;          // 1: next row's loads issued before the current row's arithmetic
     const void *fn;  // __global__ function
 };
 
-// dtype: 0 fp32, 1 bf16. nullptr when (lpr, vpt) is not instantiated.
-const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt);
-const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt);
+// dtype: 0 fp32, 1 bf16. nullptr when (lpr, vpt, wg, pf) is not instantiated.
+const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf);
+const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf);
 const void *fwd_scalar_kernel(int dtype);
 const void *bwd_scalar_kernel(int dtype);
 const void *dw_combine_kernel();

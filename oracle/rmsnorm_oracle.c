@@ -11,7 +11,8 @@
  *
  *   Forward -- hello-gpu "Chapter 13 Fused RMSNorm", section 13.1 (the
  *   definition and the worked examples); the same definition appears in the
- *   profiling-kernels page, Problem 15 ("The concepts"):
+ *   page "Profiling, GPU utilisation and writing a fused kernel", Problem 15
+ *   ("The concepts"):
  *       ms_i = (1/N) * sum_j x_ij^2          (N = true column count)
  *       r_i  = 1 / sqrt(ms_i + eps)          (eps inside the root)
  *       y_ij = x_ij * r_i * w_j              (w is per column, shared by rows)

@@ -96,15 +96,18 @@ def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
     (128, rn.BF16, 0, 16, 1),      # QK-norm: 16 vectors -> 16 lanes, 4 rows per wavefront
     (128, rn.BF16, 1, 16, 1),
     (1024, rn.F32, 0, 64, 4),
-    (1024, rn.F32, 1, 64, 4),
-    (4096, rn.BF16, 0, 64, 8),
-    (4096, rn.BF16, 1, 128, 4),
-    (5120, rn.BF16, 0, 128, 5),
-    (7168, rn.BF16, 0, 128, 7),
-    (7168, rn.BF16, 1, 256, 4),
-    (8192, rn.BF16, 0, 128, 8),
-    (32768, rn.BF16, 0, 512, 8),
+    (1024, rn.F32, 1, 256, 1),
+    (4096, rn.BF16, 0, 128, 4),
+    (4096, rn.BF16, 1, 512, 1),
+    (5120, rn.BF16, 0, 256, 3),
+    (5120, rn.BF16, 1, 1024, 1),
+    (7168, rn.BF16, 0, 256, 4),
+    (7168, rn.BF16, 1, 1024, 1),
+    (8192, rn.BF16, 0, 256, 4),
+    (8192, rn.BF16, 1, 1024, 1),
+    (32768, rn.BF16, 0, 1024, 4),
     (32768, rn.BF16, 1, 1024, 4),
+    (65536, rn.BF16, 0, 1024, 8),
     (8, rn.BF16, 0, 1, 1),
     (24, rn.BF16, 0, 4, 1),        # 3 vectors -> 4 lanes, one masked
 ])
@@ -118,20 +121,31 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (vpt - 1) * lpr < nvec <= vpt * lpr
 
 
-@pytest.mark.parametrize("N,dtype,aligned", [(13, rn.F32, 1), (257, rn.BF16, 1), (4096, rn.BF16, 0),
-                                             (65536 + 8, rn.BF16, 1), (3, rn.BF16, 1)])
-def test_ladder_scalar_cases(N, dtype, aligned):
-    c = cfg(100, N, dtype, 0, aligned=aligned)
+@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(13, rn.F32, 1, 0), (257, rn.BF16, 1, 0), (4096, rn.BF16, 0, 0),
+                                                    (65536 + 8, rn.BF16, 1, 0), (3, rn.BF16, 1, 1),
+                                                    (32768 + 8, rn.BF16, 1, 1)])
+def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
+    c = cfg(100, N, dtype, is_bwd, aligned=aligned)
     assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
 
 
 def test_ladder_grid_and_workspace_shape():
+    # backward: two workgroups per compute unit, one fp32 partial row each
     c = cfg(16384, 4096, rn.BF16, 1, cus=256, blocks=2)
-    assert c["grid"] == 512 and c["partial_rows"] == 512 and c["partial_stride"] == 4096
-    c = cfg(10, 4096, rn.BF16, 1, cus=256, blocks=2)      # fewer row blocks than resident slots
+    assert c["grid"] == 512 and c["partial_rows"] == 512 and c["partial_stride"] == 4096 and c["prefetch"] == 1
+    # ... capped by residency
+    assert cfg(16384, 4096, rn.BF16, 1, cus=256, blocks=1)["grid"] == 256
+    # ... fewer when the partial rows would exceed ~5% of the bytes (wide rows, few of them), never below the CUs
+    assert cfg(4096, 32768, rn.BF16, 1, cus=256, blocks=2)["grid"] == 256
+    # ... three per compute unit for rows narrower than a wavefront
+    assert cfg(1 << 20, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 768
+    c = cfg(10, 4096, rn.BF16, 1, cus=256, blocks=2)      # fewer row blocks than workgroups wanted
     assert c["grid"] == (10 + c["rows_per_wg"] - 1) // c["rows_per_wg"]
-    c = cfg(7, 13, rn.F32, 1)
-    assert c["partial_stride"] == 64
+    # forward: one row block per workgroup
+    c = cfg(16384, 4096, rn.BF16, 0, cus=256, blocks=6)
+    assert c["rows_per_wg"] == 2 and c["grid"] == 8192 and c["prefetch"] == 0
+    assert cfg(1 << 24, 128, rn.BF16, 0)["grid"] == 1 << 20    # capped; workgroups then loop
+    assert cfg(7, 13, rn.F32, 1)["partial_stride"] == 64
     # the ladder depends only on its arguments
     assert cfg(16384, 4096, rn.BF16, 1) == cfg(16384, 4096, rn.BF16, 1)
 

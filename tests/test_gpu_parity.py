@@ -83,30 +83,34 @@ def test_parity_small(M, N, dtype):
 
 
 def _instantiated_shapes():
-    # every (lanes_per_row, vecs_per_lane) kernel the library builds
-    out = [(l, 1) for l in (1, 2, 4, 8, 16, 32)]
-    out += [(l, v) for l in (64, 128, 256, 512, 1024) for v in range(1, 9)]
+    """Every (lanes_per_row, vecs_per_lane, wg_threads, prefetch) kernel the library builds."""
+    out = []
+    for pf in (0, 1):
+        out += [(lpr, 1, 256, pf) for lpr in (1, 2, 4, 8, 16, 32)]
+        for lpr, wgs in ((64, (256, 512, 1024)), (128, (256, 512, 1024)), (256, (256, 512, 1024)),
+                         (512, (512, 1024)), (1024, (1024,))):
+            out += [(lpr, v, wg, pf) for wg in wgs for v in range(1, 9)]
     return out
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_every_vector_kernel(dtype):
-    """Each instantiated (lanes, vectors) kernel, forced through *_with_config,
-    on a ragged row (last vector slot partly empty), a ragged row count and a
-    grid smaller than the row blocks (so workgroups loop)."""
+    """Each instantiated vector kernel, forced through *_with_config, on a
+    ragged row (last vector slot partly empty), a ragged row count, and a grid
+    of 2 so workgroups loop over row blocks (and, with prefetch, load past the
+    last block)."""
     epv = 4 if dtype == "f32" else 8
-    for lpr, vpt in _instantiated_shapes():
-        nvec = max(1, lpr * (vpt - 1) + max(1, lpr // 2 + 1))  # the last slot is partial
-        nvec = min(nvec, lpr * vpt)
+    shapes = _instantiated_shapes()
+    assert len(shapes) == 204
+    for lpr, vpt, wg, pf in shapes:
+        nvec = min(lpr * vpt, max(1, lpr * (vpt - 1) + max(1, lpr // 2 + 1)))  # the last slot is partial
         N = nvec * epv
-        wg = max(lpr, 256)
-        rpw = wg // lpr
-        M = 3 * rpw + 1
-        for grid in (1, 2):
-            cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, grid=grid)
-            x, w, dy = si.random_case(M, N, dtype, seed=lpr * 100 + vpt, dy_scale=1e-2)
-            _say(f"kernel lpr={lpr} vpt={vpt} N={N} M={M} grid={grid} {dtype}")
-            full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_f=cfg, cfg_b=cfg)
+        M = 3 * (wg // lpr) + 1
+        cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, wg_threads=wg,
+                                prefetch=pf, grid=2)
+        x, w, dy = si.random_case(M, N, dtype, seed=lpr * 100 + vpt + wg + pf, dy_scale=1e-2)
+        _say(f"kernel lpr={lpr} vpt={vpt} wg={wg} pf={pf} N={N} M={M} {dtype}")
+        full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_f=cfg, cfg_b=cfg)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
