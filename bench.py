@@ -20,7 +20,7 @@ actually costs on Hopper", section 02):
     the backward), never the dW partial traffic the kernels add.
 Per-kernel times come from HIP events recorded around each launch inside the
 timed region. A second, isolated measurement times single calls with a
-1 GiB cache-flushing copy before each (median of 50).
+1 GiB cache-flushing read before each (median of 50).
 
 `python bench.py` prints one JSON line. `--gpus N` with N > 1 exits: this
 build runs on one GPU.
@@ -146,7 +146,8 @@ class Timer:
 
 def probe_roofline(torch, rn, timer, gib):
     """Best of copy, pure write and 2-read-1-write over several grid sizes and
-    cache hints (non-temporal loads and/or stores) (GB/s)."""
+    cache hints (non-temporal loads and/or stores) (GB/s). A pure-read probe is
+    reported beside them."""
     nbytes = int(gib * GIB) // 256 * 256
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -171,10 +172,21 @@ def probe_roofline(torch, rn, timer, gib):
                 if best is None or gbps > best[0]:
                     best = (gbps, g, v, med)
         out[name] = {"GBps": round(best[0], 1), "grid": best[1], "nt_variant": best[2], "median_ms": round(best[3], 4)}
+    # a pure read, reported for information (the roofline is the best of the three above)
+    sink = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    best = None
+    for v in (0, 1):
+        for g in grids:
+            med, _ = timer.median_ms(lambda: rn.rmsn_probe_read(a, nbytes, sink, g, v), reps=11, warmup=2)
+            gbps = nbytes / (med * 1e-3) / 1e9
+            if best is None or gbps > best[0]:
+                best = (gbps, g, v, med)
+    read = {"GBps": round(best[0], 1), "grid": best[1], "nt_variant": best[2], "median_ms": round(best[3], 4)}
     del a, b, c
     torch.cuda.empty_cache()
     best_name = max(out, key=lambda k: out[k]["GBps"])
-    return {"best_GBps": out[best_name]["GBps"], "best_probe": best_name, "probes": out, "buffer_GiB": gib}
+    return {"best_GBps": out[best_name]["GBps"], "best_probe": best_name, "probes": out, "read_GBps": read,
+            "buffer_GiB": gib}
 
 
 def main(argv=None):
@@ -346,13 +358,16 @@ def main(argv=None):
         return 0
 
     # ---- isolated calls with a cache flush before each ------------------------
+    # the flush reads 1 GiB (more than L2 + the 256 MB MALL) and writes nothing,
+    # so no dirty lines are left to be written back during the timed call
     flush_n = GIB
     fa = torch.empty(flush_n, dtype=torch.uint8, device="cuda")
-    fb = torch.empty(flush_n, dtype=torch.uint8, device="cuda")
+    fb = torch.zeros(64, dtype=torch.uint8, device="cuda")
     fa.fill_(3)
+    torch.cuda.synchronize()
 
     def flush():
-        rn.rmsn_probe_copy(fa, fb, flush_n, 0)
+        rn.rmsn_probe_read(fa, flush_n, fb, 0)
 
     iso_f, _ = timer.median_ms(lambda: fwd(sets[0]), args.isolated_reps, between=flush)
     iso_b, _ = timer.median_ms(lambda: combine(bwd_rows(sets[0])), args.isolated_reps, between=flush)

@@ -27,6 +27,10 @@ int rmsn_probe_copy(const void *src, void *dst, size_t bytes, int64_t grid, int 
 /* dst[i] = pattern: moves `bytes` (write only). */
 int rmsn_probe_write(void *dst, size_t bytes, int64_t grid, int variant, void *stream);
 
+/* Reads src (moves `bytes`); writes at most 16 bytes to sink (device memory,
+ * 16-byte aligned). Used as a cache flush that leaves no dirty lines behind. */
+int rmsn_probe_read(const void *src, size_t bytes, int64_t grid, int variant, void *sink, void *stream);
+
 /* c[i] = a[i] + b[i] as 32-bit integers: moves 3 * bytes (two reads, one write). */
 int rmsn_probe_add(const void *a, const void *b, void *c, size_t bytes, int64_t grid, int variant,
                    void *stream);

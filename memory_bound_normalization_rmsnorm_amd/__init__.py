@@ -81,6 +81,7 @@ def _load() -> ctypes.CDLL:
         "rmsnorm_build_info": (ctypes.c_char_p, []),
         "rmsn_probe_copy": (i32, [vp, vp, sz, i64, i32, vp]),
         "rmsn_probe_write": (i32, [vp, sz, i64, i32, vp]),
+        "rmsn_probe_read": (i32, [vp, sz, i64, i32, vp, vp]),
         "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -96,7 +97,7 @@ EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_config", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
     "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_status_str",
     "rmsnorm_select_config", "rmsnorm_query_config", "rmsnorm_build_info",
-    "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_add",
+    "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_read", "rmsn_probe_add",
 )
 
 
@@ -206,6 +207,11 @@ def rmsn_probe_copy(src, dst, nbytes, grid=0, variant=0, stream=None) -> None:
 def rmsn_probe_write(dst, nbytes, grid=0, variant=0, stream=None) -> None:
     _check("rmsn_probe_write", lib.rmsn_probe_write(_ptr(dst), int(nbytes), int(grid), int(variant),
                                                     _stream(stream)))
+
+
+def rmsn_probe_read(src, nbytes, sink, grid=0, variant=0, stream=None) -> None:
+    _check("rmsn_probe_read", lib.rmsn_probe_read(_ptr(src), int(nbytes), int(grid), int(variant), _ptr(sink),
+                                                  _stream(stream)))
 
 
 def rmsn_probe_add(a, b, c, nbytes, grid=0, variant=0, stream=None) -> None:

@@ -6,12 +6,14 @@
 
 namespace rmsn {
 
-// dW[col] = sum over p of partial[p][col]; kCombineCols (16) columns per
-// workgroup. Lane (slice s, quad c) sums rows p = s, s + S, s + 2S, ...
-// (S = kCombineSlices = 64) in ascending order for columns 4c..4c+3; the S
-// slice sums are then folded by a fixed binary tree in LDS. Rows are padded to
-// ldp floats (a multiple of 64) and 256-byte aligned, so the float4 loads stay
-// inside the workspace.
+// dW[col] = sum over p of partial[p][col]; kCombineCols (32) columns per
+// workgroup, so each partial row contributes one whole 128-byte cache line to
+// one workgroup (narrower strips made two workgroups, usually on different
+// XCDs, fetch the same line). Lane (slice s, quad c) sums rows p = s, s + S,
+// s + 2S, ... (S = kCombineSlices = 64) in ascending order for columns
+// 4c..4c+3; the S slice sums are then folded by a fixed binary tree in LDS.
+// Rows are padded to ldp floats (a multiple of 64) and 256-byte aligned, so
+// the float4 loads stay inside the workspace.
 __global__ void __launch_bounds__(kCombineWG)
 dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
            float *__restrict__ dw) {

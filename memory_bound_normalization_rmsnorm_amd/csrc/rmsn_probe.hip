@@ -1,4 +1,5 @@
-// rmsn_probe.hip -- HBM roofline probes: copy, pure write, 2-read-1-write.
+// rmsn_probe.hip -- HBM roofline probes: copy, pure write, 2-read-1-write,
+// and a pure read (used as a cache flush that leaves no dirty lines).
 // Each lane streams 16-byte vectors; with a grid smaller than the vector
 // count, lanes stride by the whole grid so every access of one instruction
 // is contiguous across the wavefront. Each probe is built with and without
@@ -46,6 +47,15 @@ probe_add(const u32x4 *__restrict__ a, const u32x4 *__restrict__ b, u32x4 *__res
         st<NTS>(c + i, ld<NTL>(a + i) + ld<NTL>(b + i));
 }
 
+// Reads every vector; the (practically never taken) data-dependent store keeps
+// the loads alive without writing back anything.
+template <bool NTL, bool NTS>
+__global__ void __launch_bounds__(kWG) probe_read(const u32x4 *__restrict__ src, u32x4 *__restrict__ sink, int64_t n) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)blockIdx.x * kWG + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWG) acc ^= ld<NTL>(src + i);
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x94d049bbu && acc.w == 0x2545f491u) st<NTS>(sink, acc);
+}
+
 bool bad(const void *p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15u); }
 
 int grid_for(size_t bytes, int64_t grid, int variant, int64_t *n, unsigned *g) {
@@ -89,6 +99,16 @@ int rmsn_probe_write(void *dst, size_t bytes, int64_t grid, int variant, void *s
     if (st != RMSN_OK || n == 0) return st;
     RMSN_PROBE_DISPATCH(probe_write, variant, dim3(g), dim3(kWG), 0, static_cast<hipStream_t>(stream),
                         static_cast<u32x4 *>(dst), n)
+    return done(hipGetLastError());
+}
+
+int rmsn_probe_read(const void *src, size_t bytes, int64_t grid, int variant, void *sink, void *stream) {
+    if (bad(src) || bad(sink)) return RMSN_EINVAL;
+    int64_t n; unsigned g;
+    int st = grid_for(bytes, grid, variant, &n, &g);
+    if (st != RMSN_OK || n == 0) return st;
+    RMSN_PROBE_DISPATCH(probe_read, variant, dim3(g), dim3(kWG), 0, static_cast<hipStream_t>(stream),
+                        static_cast<const u32x4 *>(src), static_cast<u32x4 *>(sink), n)
     return done(hipGetLastError());
 }
 

@@ -7,8 +7,8 @@ namespace rmsn {
 
 // Lanes of the scalar (any-N, any-alignment) row kernels and the combine kernel.
 constexpr int kScalarWG = 256;
-constexpr int kCombineWG = 256;
-constexpr int kCombineCols = 16;     // dW columns per combine workgroup (4 lanes x 4)
+constexpr int kCombineWG = 512;
+constexpr int kCombineCols = 32;     // dW columns per combine workgroup: one 128-byte line per partial row
 constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
 constexpr int kCombineSlices = kCombineWG / kCombineLanes;  // partial rows summed side by side
 constexpr int kPartialAlign = 64;    // partial rows are padded to a multiple of 64 floats

@@ -1,0 +1,202 @@
+"""Launch-configuration search for the RMSNorm kernels, with an on-disk cache.
+
+The library's default configuration comes from an analytical ladder on the
+row width (``rmsnorm_select_config``). This module searches the space the
+ladder chooses from -- lanes per row, workgroup size, register prefetch and
+grid -- by timing each candidate through ``rmsnorm_{fwd,bwd}_with_config``.
+It keeps the winner per (device, compute units, M, N, dtype, direction,
+library build).
+
+Scoring follows the benchmark's regime, not an L2-cold one: inputs rotate
+through cloned buffer sets that together exceed the last-level caches, and
+each candidate runs K back-to-back launches between one pair of HIP events.
+The Quack study ("What a tuned RMSNorm kernel actually costs on Hopper",
+section 06) warns that a search scored in a different regime than the one
+that runs regresses cells. The ladder's own choice is always a candidate, so
+a tuned configuration is never slower than the default in the scoring regime,
+up to timing noise. It also keeps the memory-path knobs (prefetch depth,
+workgroup shape) in the search space, which that section asks for.
+
+Note: the backward's dW bits depend on the configuration (the number of
+partial rows sets the summation order). A tuned configuration is
+deterministic run to run, but its dW bits differ from the default's.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import time
+
+import torch
+
+from . import (BF16, F32, LIB_PATH, RmsnormError, lib, rmsnorm_bwd_with_config, rmsnorm_build_info,
+               rmsnorm_config, rmsnorm_fwd_with_config, rmsnorm_query_config)
+
+ELEM = {F32: 4, BF16: 2}
+TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+# (lanes per row, workgroup sizes) built into the library; see csrc/rmsn_instances.h
+BUILT = {1: (256,), 2: (256,), 4: (256,), 8: (256,), 16: (256,), 32: (256,), 64: (256, 512, 1024),
+         128: (256, 512, 1024), 256: (256, 512, 1024), 512: (512, 1024), 1024: (1024,)}
+MAX_VPT = 8
+DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
+
+
+def cache_key(M: int, N: int, dtype: int, is_bwd: int, device_name: str, num_cus: int) -> str:
+    build = rmsnorm_build_info()
+    return f"{device_name}|{num_cus}|{build}|{'bwd' if is_bwd else 'fwd'}|{dtype}|{M}|{N}"
+
+
+def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: rmsnorm_config | None = None):
+    """Every built vector shape that covers a row of N elements with one
+    partially used slot at most, crossed with grids: the row-block count,
+    its halves, and 1-4 workgroups per compute unit. Pure host logic."""
+    es = ELEM[dtype]
+    if (N * es) % 16:
+        return [default] if default is not None else []
+    nvec = N * es // 16
+    out = []
+    for lpr, wgs in BUILT.items():
+        vpt = -(-nvec // lpr)
+        if vpt > MAX_VPT:
+            continue
+        if vpt == 1 and lpr > 1 and nvec <= lpr // 2:
+            continue  # half the lanes would hold the row as well
+        if lpr < 64 and vpt > 1:
+            continue  # narrow shapes are built with one vector per lane
+        for wg in wgs:
+            rpw = wg // lpr
+            row_blocks = -(-M // rpw)
+            grids = {row_blocks, -(-row_blocks // 2)} | {k * num_cus for k in (1, 2, 3, 4)}
+            for pf in (0, 1):
+                for g in sorted(x for x in grids if 1 <= x <= min(row_blocks, 1 << 20)):
+                    out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt,
+                                              wg_threads=wg, prefetch=pf, grid=g))
+    if default is not None:
+        out.insert(0, default)
+    return out
+
+
+def _key(c: rmsnorm_config):
+    return (c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch, c.grid)
+
+
+class _Bench:
+    """Rotating device buffers for one (M, N, dtype) and a timer."""
+
+    def __init__(self, M, N, dtype, sets_bytes=3 << 30, seed=0):
+        self.M, self.N, self.dtype = M, N, dtype
+        t = TORCH[dtype]
+        per_set = 4 * M * N * ELEM[dtype] + 4 * M
+        self.R = max(2, min(8, sets_bytes // max(per_set, 1)))
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        self.sets = []
+        for _ in range(self.R):
+            self.sets.append(dict(
+                x=torch.randn(M, N, device="cuda", generator=g).to(t),
+                dy=(torch.randn(M, N, device="cuda", generator=g) * 1e-2).to(t),
+                y=torch.empty(M, N, dtype=t, device="cuda"), dx=torch.empty(M, N, dtype=t, device="cuda"),
+                rstd=torch.empty(M, device="cuda")))
+        self.w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).to(t)
+        self.dw = torch.empty(N, device="cuda")
+        self.ws = None
+        self.ws_bytes = 0
+
+    def _ensure_ws(self, nbytes):
+        if nbytes > self.ws_bytes:
+            self.ws = torch.empty(nbytes // 4 + 64, device="cuda")
+            self.ws_bytes = nbytes
+
+    def run(self, cfg, is_bwd, k):
+        s = self.sets[k % self.R]
+        if is_bwd:
+            rmsnorm_bwd_with_config(s["x"], self.w, s["dy"], s["rstd"], self.M, self.N, self.dtype, s["dx"], self.dw,
+                                    self.ws, self.ws_bytes, cfg)
+        else:
+            rmsnorm_fwd_with_config(s["x"], self.w, 1e-6, self.M, self.N, self.dtype, s["y"], s["rstd"], cfg)
+
+    def time_us(self, cfg, is_bwd, K=30, W=3):
+        if is_bwd:
+            ldp = -(-self.N // 64) * 64
+            self._ensure_ws(int(cfg.grid) * ldp * 4)
+        for k in range(W):
+            self.run(cfg, is_bwd, k)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(K):
+            self.run(cfg, is_bwd, k)
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / K
+
+
+def tune(M: int, N: int, dtype: int, is_bwd: int, budget_s: float = 60.0, K: int = 30, verbose: bool = False):
+    """Time the candidates (ladder default first) and return (best config, results).
+    Stops early when the time budget is spent; the default is always timed."""
+    if not torch.cuda.is_available():
+        raise RuntimeError("tuning needs the GPU")
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    default = rmsnorm_query_config(M, N, dtype, is_bwd)
+    bench = _Bench(M, N, dtype)
+    fwd_default = rmsnorm_query_config(M, N, dtype, 0)
+    for s in bench.sets:  # the backward reads the forward's rstd
+        rmsnorm_fwd_with_config(s["x"], bench.w, 1e-6, M, N, dtype, s["y"], s["rstd"], fwd_default)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    results, seen = [], set()
+    for cfg in candidates(M, N, dtype, is_bwd, props.multi_processor_count, default):
+        if _key(cfg) in seen:
+            continue
+        seen.add(_key(cfg))
+        if results and time.time() - t0 > budget_s:
+            break
+        try:
+            us = bench.time_us(cfg, is_bwd, K=K)
+        except RmsnormError:
+            continue
+        results.append((us, cfg))
+        if verbose:
+            print(f"  {cfg.as_dict()} -> {us:.2f} us", flush=True)
+    results.sort(key=lambda r: r[0])
+    return results[0][1], results
+
+
+def best_config(M: int, N: int, dtype: int, is_bwd: int, cache_path: str = DEFAULT_CACHE, budget_s: float = 60.0,
+                retune: bool = False) -> rmsnorm_config:
+    """The cached winner for this shape on this device and library build; tunes
+    (and stores) on a miss."""
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    key = cache_key(M, N, dtype, is_bwd, props.name, props.multi_processor_count)
+    cache = load_cache(cache_path)
+    if not retune and key in cache:
+        return config_from_dict(cache[key]["config"])
+    cfg, results = tune(M, N, dtype, is_bwd, budget_s=budget_s)
+    default_us = next(us for us, c in results if _key(c) == _key(rmsnorm_query_config(M, N, dtype, is_bwd)))
+    cache[key] = {"config": cfg.as_dict(), "us": results[0][0], "default_us": default_us,
+                  "candidates_timed": len(results), "library": LIB_PATH}
+    save_cache(cache_path, cache)
+    return cfg
+
+
+def config_from_dict(d: dict) -> rmsnorm_config:
+    return rmsnorm_config(**{k: int(v) for k, v in d.items() if k in dict(rmsnorm_config._fields_)})
+
+
+def load_cache(path: str) -> dict:
+    try:
+        with open(path) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
+def save_cache(path: str, cache: dict) -> None:
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(cache, f, indent=1, sort_keys=True)
+    os.replace(tmp, path)
+
+
+__all__ = ["best_config", "tune", "candidates", "cache_key", "config_from_dict", "load_cache", "save_cache", "lib"]

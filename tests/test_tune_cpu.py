@@ -1,0 +1,36 @@
+"""Host logic of the configuration search: candidate enumeration and the cache."""
+
+import memory_bound_normalization_rmsnorm_amd as rn
+from memory_bound_normalization_rmsnorm_amd import tune
+
+
+def test_candidates_cover_the_row_and_include_the_default():
+    default = rn.rmsnorm_select_config(16384, 4096, rn.BF16, 1, 1, 256, 2)
+    cands = tune.candidates(16384, 4096, rn.BF16, 1, 256, default)
+    assert tune._key(cands[0]) == tune._key(default)
+    nvec = 4096 * 2 // 16
+    shapes = set()
+    for c in cands:
+        assert c.lanes_per_row * c.vecs_per_lane >= nvec
+        assert (c.vecs_per_lane - 1) * c.lanes_per_row < nvec      # at most one partial slot
+        assert c.wg_threads % c.lanes_per_row == 0
+        assert 1 <= c.grid <= -(-16384 // (c.wg_threads // c.lanes_per_row))
+        shapes.add((c.lanes_per_row, c.vecs_per_lane))
+    assert {(64, 8), (128, 4), (256, 2), (512, 1)} <= shapes
+    assert (1024, 1) not in shapes                                 # half of its lanes would be idle
+
+
+def test_candidates_for_widths_the_vector_path_cannot_take():
+    default = rn.rmsnorm_select_config(10, 13, rn.F32, 0, 1, 256, 2)
+    assert [tune._key(c) for c in tune.candidates(10, 13, rn.F32, 0, 256, default)] == [tune._key(default)]
+
+
+def test_cache_round_trip(tmp_path):
+    cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=128, vecs_per_lane=4, wg_threads=512, prefetch=1, grid=77)
+    path = str(tmp_path / "sub" / "tuned.json")
+    key = tune.cache_key(16384, 4096, rn.BF16, 0, "dev", 256)
+    assert "fwd" in key and "16384" in key and rn.rmsnorm_build_info() in key
+    tune.save_cache(path, {key: {"config": cfg.as_dict()}})
+    back = tune.config_from_dict(tune.load_cache(path)[key]["config"])
+    assert tune._key(back) == tune._key(cfg)
+    assert tune.load_cache(str(tmp_path / "missing.json")) == {}
