@@ -26,8 +26,8 @@ SOURCE = os.path.join(HERE, "rmsnorm_oracle.c")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "librmsnorm_oracle.so")
 
-_DTYPE_CODE = {"f32": 0, "bf16": 1, "f64": 2}
-_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}
+_DTYPE_CODE = {"f32": 0, "bf16": 1, "f64": 2, "f16": 3}
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64, "f16": np.float16}
 
 
 def build(source: str = SOURCE, out: str = LIB_PATH, extra_flags=()) -> str:
@@ -41,22 +41,29 @@ def build(source: str = SOURCE, out: str = LIB_PATH, extra_flags=()) -> str:
     return out
 
 
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
 class Oracle:
     """Handle on one compiled copy of the oracle library."""
 
     def __init__(self, lib_path: str):
         self.path = lib_path
         lib = ctypes.CDLL(lib_path)
-        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
-        lib.rmsn_oracle_fwd.argtypes = [vp, vp, ctypes.c_int, i64, i64, dp, vp, i64, vp, vp]
-        lib.rmsn_oracle_bwd_dx.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, dp, vp, i64, vp, vp]
-        lib.rmsn_oracle_bwd_dw.argtypes = [vp, vp, ctypes.c_int, i64, i64, dp, vp]
-        for f in (lib.rmsn_oracle_fwd, lib.rmsn_oracle_bwd_dx, lib.rmsn_oracle_bwd_dw):
+        i64, vp, dp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
+        lib.rmsn_oracle_fwd.argtypes = [vp, vp, vp, ci, ci, i64, i64, dp, vp, i64, vp, vp, vp]
+        lib.rmsn_oracle_bwd_dx.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, dp, vp, i64, vp, vp]
+        lib.rmsn_oracle_bwd_dw.argtypes = [vp, vp, vp, ci, i64, i64, dp, vp]
+        lib.rmsn_oracle_round.argtypes = [vp, i64, ci, vp]
+        for f in (lib.rmsn_oracle_fwd, lib.rmsn_oracle_bwd_dx, lib.rmsn_oracle_bwd_dw, lib.rmsn_oracle_round):
             f.restype = ctypes.c_int
         self._lib = lib
 
     @staticmethod
     def _check(a, dtype, shape):
+        if a is None:
+            return None
         a = np.ascontiguousarray(a)
         if a.dtype != _STORAGE[dtype]:
             raise TypeError(f"expected {_STORAGE[dtype]} storage for {dtype}, got {a.dtype}")
@@ -71,50 +78,72 @@ class Oracle:
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         return rows, rows.size
 
-    def fwd(self, x, w, eps, dtype, rows=None, want_y=True):
-        """Return (y, r) in float64 for the listed rows (all rows by default)."""
+    def _fwd(self, x, res, w, eps, dtype, wdtype, rows, want_y):
         M, N = np.shape(x)
+        wdtype = wdtype or dtype
         x = self._check(x, dtype, (M, N))
-        w = self._check(w, dtype, (N,))
+        res = self._check(res, dtype, (M, N))
+        w = self._check(w, wdtype, (N,))
         rows_a, n = self._rows(rows, M)
         y = np.empty((n, N), dtype=np.float64) if want_y else None
+        h = np.empty((n, N), dtype=np.float64) if res is not None else None
         r = np.empty(n, dtype=np.float64)
-        rc = self._lib.rmsn_oracle_fwd(
-            x.ctypes.data, w.ctypes.data, _DTYPE_CODE[dtype], M, N, float(eps),
-            None if rows_a is None else rows_a.ctypes.data, n,
-            None if y is None else y.ctypes.data, r.ctypes.data)
+        rc = self._lib.rmsn_oracle_fwd(_ptr(x), _ptr(res), _ptr(w), _DTYPE_CODE[dtype], _DTYPE_CODE[wdtype],
+                                       M, N, float(eps), _ptr(rows_a), n, _ptr(h), _ptr(y), r.ctypes.data)
         if rc != 0:
             raise ValueError("oracle forward rejected its arguments")
+        return h, y, r
+
+    def fwd(self, x, w, eps, dtype, rows=None, want_y=True, wdtype=None):
+        """Return (y, r) in float64 for the listed rows (all rows by default)."""
+        _, y, r = self._fwd(x, None, w, eps, dtype, wdtype, rows, want_y)
         return y, r
 
-    def bwd_dx(self, x, w, dy, eps, dtype, rows=None):
-        """Return (dx, r) in float64 for the listed rows (all rows by default)."""
+    def fwd_residual(self, x, res, w, eps, dtype, rows=None, want_y=True, wdtype=None):
+        """Fused residual add: return (h, y, r), h = round(x + res) in `dtype`
+        (as float64), y the forward of h."""
+        return self._fwd(x, res, w, eps, dtype, wdtype, rows, want_y)
+
+    def bwd_dx(self, x, w, dy, eps, dtype, rows=None, res=None, dh=None, wdtype=None):
+        """Return (dx, r) in float64 for the listed rows (all rows by default).
+        With res, the input is the stored sum round(x + res); dh is added to dx."""
         M, N = np.shape(x)
+        wdtype = wdtype or dtype
         x = self._check(x, dtype, (M, N))
-        w = self._check(w, dtype, (N,))
+        res = self._check(res, dtype, (M, N))
+        w = self._check(w, wdtype, (N,))
         dy = self._check(dy, dtype, (M, N))
+        dh = self._check(dh, dtype, (M, N))
         rows_a, n = self._rows(rows, M)
         dx = np.empty((n, N), dtype=np.float64)
         r = np.empty(n, dtype=np.float64)
-        rc = self._lib.rmsn_oracle_bwd_dx(
-            x.ctypes.data, w.ctypes.data, dy.ctypes.data, _DTYPE_CODE[dtype], M, N,
-            float(eps), None if rows_a is None else rows_a.ctypes.data, n,
-            dx.ctypes.data, r.ctypes.data)
+        rc = self._lib.rmsn_oracle_bwd_dx(_ptr(x), _ptr(res), _ptr(w), _ptr(dy), _ptr(dh), _DTYPE_CODE[dtype],
+                                          _DTYPE_CODE[wdtype], M, N, float(eps), _ptr(rows_a), n,
+                                          dx.ctypes.data, r.ctypes.data)
         if rc != 0:
             raise ValueError("oracle backward (dx) rejected its arguments")
         return dx, r
 
-    def bwd_dw(self, x, dy, eps, dtype):
+    def bwd_dw(self, x, dy, eps, dtype, res=None):
         """Return dW (float64, length N) summed over every row."""
         M, N = np.shape(x)
         x = self._check(x, dtype, (M, N))
+        res = self._check(res, dtype, (M, N))
         dy = self._check(dy, dtype, (M, N))
         dw = np.empty(N, dtype=np.float64)
-        rc = self._lib.rmsn_oracle_bwd_dw(x.ctypes.data, dy.ctypes.data, _DTYPE_CODE[dtype],
-                                          M, N, float(eps), dw.ctypes.data)
+        rc = self._lib.rmsn_oracle_bwd_dw(_ptr(x), _ptr(res), _ptr(dy), _DTYPE_CODE[dtype], M, N, float(eps),
+                                          dw.ctypes.data)
         if rc != 0:
             raise ValueError("oracle backward (dW) rejected its arguments")
         return dw
+
+    def round(self, values, dtype):
+        """Round float64 values to the storage format `dtype` (nearest, ties to even), as float64."""
+        v = np.ascontiguousarray(values, dtype=np.float64)
+        out = np.empty_like(v)
+        if self._lib.rmsn_oracle_round(v.ctypes.data, v.size, _DTYPE_CODE[dtype], out.ctypes.data) != 0:
+            raise ValueError("oracle rounding rejected its arguments")
+        return out
 
 
 _default = None
@@ -130,13 +159,21 @@ def get() -> Oracle:
     return _default
 
 
-def fwd(x, w, eps, dtype, rows=None, want_y=True):
-    return get().fwd(x, w, eps, dtype, rows=rows, want_y=want_y)
+def fwd(x, w, eps, dtype, rows=None, want_y=True, wdtype=None):
+    return get().fwd(x, w, eps, dtype, rows=rows, want_y=want_y, wdtype=wdtype)
 
 
-def bwd_dx(x, w, dy, eps, dtype, rows=None):
-    return get().bwd_dx(x, w, dy, eps, dtype, rows=rows)
+def fwd_residual(x, res, w, eps, dtype, rows=None, want_y=True, wdtype=None):
+    return get().fwd_residual(x, res, w, eps, dtype, rows=rows, want_y=want_y, wdtype=wdtype)
 
 
-def bwd_dw(x, dy, eps, dtype):
-    return get().bwd_dw(x, dy, eps, dtype)
+def bwd_dx(x, w, dy, eps, dtype, rows=None, res=None, dh=None, wdtype=None):
+    return get().bwd_dx(x, w, dy, eps, dtype, rows=rows, res=res, dh=dh, wdtype=wdtype)
+
+
+def bwd_dw(x, dy, eps, dtype, res=None):
+    return get().bwd_dw(x, dy, eps, dtype, res=res)
+
+
+def round_to(values, dtype):
+    return get().round(values, dtype)

@@ -13,7 +13,13 @@ Each ``pin_*`` function takes an ``oracle.Oracle`` handle and raises
   * central finite differences of the forward (pins dx and dW, whose formulas
     are lost on the persistent-backward page),
   * PyTorch's own fp64 ``rms_norm`` and autograd on the CPU, an independent
-    implementation of the same definition.
+    implementation of the same definition,
+  * library conversions for the storage formats: numpy's float16 decode of
+    every bit pattern, numpy's float64 -> float16/float32 casts and torch's
+    float32 -> bfloat16 cast for round-to-nearest-even, plus hand-derived ties,
+  * for the fused residual add (the profiling page, Problem 15): the worked
+    example reached as x + res, exact rounding cases of the stored sum, and
+    central finite differences of L = sum(dy * y(x + res)) + sum(dh * (x + res)).
 
 The functions are shared by ``test_oracle.py`` (the real oracle must pass all
 of them) and ``test_oracle_mutants.py`` (every planted mistake must fail at
@@ -295,6 +301,138 @@ def pin_row_selection(orc):
     assert np.array_equal(dxs, dx[rows])
 
 
+def pin_fp16_decode(orc):
+    """Every finite fp16 bit pattern decodes to numpy's float16 value. (The
+    residual forward with res = 0 returns the stored sum x + 0 = x.)"""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    vals = bits.view(np.float16)
+    keep = np.isfinite(vals)
+    x = vals[keep].reshape(1, -1)
+    h, _, _ = orc.fwd_residual(x, np.zeros_like(x), np.ones(x.shape[1], np.float16), 1.0, "f16", want_y=False)
+    assert np.array_equal(h[0], x[0].astype(np.float64)), "fp16 decode differs from numpy"
+
+
+def pin_rounding(orc):
+    """Round to nearest, ties to even, against library conversions: numpy's
+    float64 -> float16 and float64 -> float32 casts, torch's float32 -> bfloat16
+    cast (on float32-exact inputs); plus hand-derived ties and overflow."""
+    import torch
+
+    rng = np.random.default_rng(37)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 6, 4000),
+                        rng.standard_normal(500) * 1e-6, [0.0, -0.0, 65504.0, 65519.9, -70000.0, 6e-8, 3e-8]])
+    got16 = orc.round(v, "f16")
+    with np.errstate(over="ignore"):
+        want16 = v.astype(np.float16).astype(np.float64)
+    assert np.array_equal(got16, want16), "fp16 rounding differs from numpy"
+    got32 = orc.round(v, "f32")
+    assert np.array_equal(got32, v.astype(np.float32).astype(np.float64)), "fp32 rounding differs"
+    v32 = v.astype(np.float32).astype(np.float64)
+    gotb = orc.round(v32, "bf16")
+    wantb = torch.tensor(v32, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(gotb, wantb), "bf16 rounding differs from torch"
+    # ties: bf16 keeps 8 significant bits, so 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -9 + 2 ** -17])
+    assert np.array_equal(orc.round(ties, "bf16"), [1.0, 1 + 2 ** -6, -1.0, 2 ** -9])
+    assert np.array_equal(orc.round(np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 65520.0]), "f16"),
+                          [1.0, 1 + 2 ** -9, np.inf])
+
+
+def pin_residual_worked_example(orc):
+    """hello-gpu ch. 13, Figure 13.1, reached through the residual form:
+    x + res = [3, 4, -3, -4] (exact) must give the printed r and y."""
+    with open(GOLDEN) as f:
+        c = json.load(f)["cases"][1]
+    x = _f32([[1.0, 2.0, -1.0, -2.0]])
+    res = _f32([[2.0, 2.0, -2.0, -2.0]])
+    h, y, r = orc.fwd_residual(x, res, _f32(c["w"]), _eps32(c["eps"]), "f32")
+    assert np.array_equal(h[0], c["x"]), "residual sum"
+    assert abs(r[0] - c["r"]) <= c["tol"]
+    for j, v in c["y"].items():
+        assert abs(y[0, int(j)] - v) <= c["tol"]
+
+
+def pin_residual_rounding(orc):
+    """The stored sum is rounded to the activation format before it is
+    normalised: bf16 1 + 2^-8 is a tie and stays 1; 1 + 3*2^-8 goes to 1 + 2^-6.
+    With res = 0 the forward and backward equal the plain ones exactly."""
+    bf = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    x = bf([[1.0, 1.0, 2.0, -3.0]])
+    res = bf([[2 ** -8, 3 * 2 ** -8, 0.0, 0.0]])
+    w = bf([1.0, 1.0, 1.0, 1.0])
+    h, y, r = orc.fwd_residual(x, res, w, 0.0, "bf16")
+    assert np.array_equal(h[0], [1.0, 1 + 2 ** -6, 2.0, -3.0]), h
+    ms = np.mean(h[0] ** 2)
+    _close(r[0], 1 / np.sqrt(ms), 1e-15, what="r of the stored sum")
+    rng = np.random.default_rng(41)
+    xb = bf(rng.standard_normal((3, 16)))
+    wb = bf(rng.uniform(0.5, 1.5, 16))
+    dyb = bf(rng.standard_normal((3, 16)))
+    zero = np.zeros_like(xb)
+    h0, y0, r0 = orc.fwd_residual(xb, zero, wb, 1e-5, "bf16")
+    y1, r1 = orc.fwd(xb, wb, 1e-5, "bf16")
+    assert np.array_equal(y0, y1) and np.array_equal(r0, r1)
+    dx0, _ = orc.bwd_dx(xb, wb, dyb, 1e-5, "bf16", res=zero, dh=zero)
+    dx1, _ = orc.bwd_dx(xb, wb, dyb, 1e-5, "bf16")
+    assert np.array_equal(dx0, dx1)
+    assert np.array_equal(orc.bwd_dw(xb, dyb, 1e-5, "bf16", res=zero), orc.bwd_dw(xb, dyb, 1e-5, "bf16"))
+
+
+def pin_residual_finite_differences(orc):
+    """L = sum(dy * y(x + res)) + sum(dh * (x + res)): central differences in x
+    and in res both equal the residual backward's dx (fp64 storage, where the
+    stored sum is exact); its dW equals the plain dW at h = x + res."""
+    rng = np.random.default_rng(43)
+    M, N, eps = 3, 6, 1e-3
+    x = rng.standard_normal((M, N))
+    res = rng.standard_normal((M, N))
+    w = rng.uniform(0.5, 1.5, N)
+    dy = rng.standard_normal((M, N))
+    dh = rng.standard_normal((M, N))
+
+    def loss(xx, rr):
+        h, y, _ = orc.fwd_residual(xx, rr, w, eps, "f64")
+        return float(np.sum(dy * y) + np.sum(dh * h))
+
+    dx, _ = orc.bwd_dx(x, w, dy, eps, "f64", res=res, dh=dh)
+    for which in ("x", "res"):
+        fd = np.empty_like(x)
+        for i in range(M):
+            for j in range(N):
+                hstep = 1e-6 * max(1.0, abs(x[i, j]))
+                a, b = x.copy(), x.copy()
+                ra, rb = res.copy(), res.copy()
+                if which == "x":
+                    a[i, j] += hstep
+                    b[i, j] -= hstep
+                else:
+                    ra[i, j] += hstep
+                    rb[i, j] -= hstep
+                fd[i, j] = (loss(a, ra) - loss(b, rb)) / (2 * hstep)
+        _close(dx, fd, 0.0, atol=1e-7 * max(1.0, np.max(np.abs(fd))), what=f"residual dx vs d/d{which}")
+    _close(orc.bwd_dw(x, dy, eps, "f64", res=res), orc.bwd_dw(x + res, dy, eps, "f64"), 1e-13, atol=1e-15,
+           what="residual dW")
+
+
+def pin_weight_dtype(orc):
+    """Weights in their own format widen exactly: bf16 or fp16 activations with
+    fp32 weights equal the same numbers given as fp64 weights."""
+    rng = np.random.default_rng(47)
+    for dt, mk in (("bf16", lambda a: (np.asarray(a, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)),
+                   ("f16", lambda a: np.asarray(a, np.float16))):
+        x = mk(rng.standard_normal((3, 20)))
+        dy = mk(rng.standard_normal((3, 20)))
+        w32 = rng.uniform(0.5, 1.5, 20).astype(np.float32)
+        y_a, r_a = orc.fwd(x, w32, 1e-5, dt, wdtype="f32")
+        y_b, r_b = orc.fwd(x, w32.astype(np.float64), 1e-5, dt, wdtype="f64")
+        assert np.array_equal(y_a, y_b) and np.array_equal(r_a, r_b)
+        d_a, _ = orc.bwd_dx(x, w32, dy, 1e-5, dt, wdtype="f32")
+        d_b, _ = orc.bwd_dx(x, w32.astype(np.float64), dy, 1e-5, dt, wdtype="f64")
+        assert np.array_equal(d_a, d_b)
+        y_c, _ = orc.fwd(x, w32, 1e-5, dt, wdtype="f32")
+        assert not np.array_equal(y_c, orc.fwd(x, np.ones(20, np.float32), 1e-5, dt, wdtype="f32")[0])
+
+
 ALL_PINS = [
     pin_worked_examples,
     pin_one_column,
@@ -307,4 +445,10 @@ ALL_PINS = [
     pin_torch_reference,
     pin_storage_widening,
     pin_row_selection,
+    pin_fp16_decode,
+    pin_rounding,
+    pin_residual_worked_example,
+    pin_residual_rounding,
+    pin_residual_finite_differences,
+    pin_weight_dtype,
 ]
