@@ -21,8 +21,9 @@
  * ("What a tuned RMSNorm kernel actually costs on Hopper", section 05).
  *
  * Conventions for every entry point:
- *   - x, w, y, dy, dx share one storage dtype (RMSN_F32 or RMSN_BF16); rstd,
- *     dW and the workspace are always fp32.
+ *   - `dtype` is an rmsn_dtype: the activation format of x, y, dy, dx (and
+ *     res, h, dh) and the weight format of w; rstd, dW and the workspace are
+ *     always fp32.
  *   - All tensor pointers are DEVICE pointers, allocated and owned by the
  *     caller. Matrices are row-major and contiguous (row stride = N
  *     elements); w and dW have N elements; rstd has M elements.
@@ -47,9 +48,19 @@
 extern "C" {
 #endif
 
+/*
+ * Storage formats: activations (x, y, dy, dx, and the residual tensors) and
+ * weights w. 16-bit outputs are rounded to nearest even. rstd, dW and the
+ * workspace are fp32 in every format. The *_WF32 formats keep fp32 (master)
+ * weights with 16-bit activations ("What a tuned RMSNorm kernel actually costs
+ * on Hopper", section 07: weight format as a separate dimension).
+ */
 typedef enum {
-    RMSN_F32 = 0,  /* IEEE fp32 storage */
-    RMSN_BF16 = 1  /* bfloat16 storage; outputs are rounded to nearest even */
+    RMSN_F32 = 0,       /* fp32 activations, fp32 weights */
+    RMSN_BF16 = 1,      /* bf16 activations, bf16 weights */
+    RMSN_F16 = 2,       /* fp16 activations, fp16 weights */
+    RMSN_BF16_WF32 = 3, /* bf16 activations, fp32 weights */
+    RMSN_F16_WF32 = 4   /* fp16 activations, fp32 weights */
 } rmsn_dtype;
 
 typedef enum {
@@ -108,6 +119,33 @@ int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype);
 int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
                 int64_t N, int dtype, void *dx, float *dw, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * Fused residual add + RMSNorm (page "Profiling, GPU utilisation and writing
+ * a fused kernel", Problem 15: read x and the residual, write their sum and
+ * the normalised sum, in one pass).
+ *
+ * rmsnorm_fwd_residual: h = x + res rounded to the activation format and
+ * stored ([M][N], the residual stream for the next layer); y and rstd are the
+ * forward of h as stored, i.e. exactly the unfused add followed by
+ * rmsnorm_fwd(h). h must not alias x or res.
+ *
+ * rmsnorm_bwd_residual: the backward of that pair. h: the stored sum the
+ * forward wrote (in place of x); dy: gradient of y; dh: gradient flowing into
+ * h from the residual branch. dx = dh + (the rmsnorm input gradient at h),
+ * rounded once: the gradient of both x and res. dW as in rmsnorm_bwd. The
+ * workspace contract is rmsnorm_bwd's (rmsnorm_bwd_workspace_bytes covers
+ * both).
+ *
+ * cfg: NULL for the ladder's choice, or an explicit configuration as for the
+ * *_with_config calls. Same errors as rmsnorm_fwd / rmsnorm_bwd; res / dh must
+ * not be NULL when M > 0.
+ */
+int rmsnorm_fwd_residual(const void *x, const void *res, const void *w, float eps, int64_t M, int64_t N,
+                         int dtype, void *h, void *y, float *rstd, const rmsnorm_config *cfg, void *stream);
+int rmsnorm_bwd_residual(const void *h, const void *w, const void *dy, const void *dh, const float *rstd,
+                         int64_t M, int64_t N, int dtype, void *dx, float *dw, void *workspace,
+                         size_t workspace_bytes, const rmsnorm_config *cfg, void *stream);
 
 /*
  * The two kernels of rmsnorm_bwd as separate calls, for callers that time or

@@ -27,6 +27,9 @@ LIB_PATH = os.environ.get("RMSNORM_MI355X_LIB") or os.path.join(_HERE, LIB_NAME)
 
 F32 = 0
 BF16 = 1
+F16 = 2
+BF16_WF32 = 3
+F16_WF32 = 4
 
 OK = 0
 EINVAL = -1
@@ -74,6 +77,8 @@ def _load() -> ctypes.CDLL:
         "rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]),
         "rmsnorm_bwd_with_config": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, cfgp, vp]),
         "rmsnorm_bwd_rows": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, ctypes.POINTER(i64), vp]),
+        "rmsnorm_fwd_residual": (i32, [vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, cfgp, vp]),
+        "rmsnorm_bwd_residual": (i32, [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, cfgp, vp]),
         "rmsnorm_bwd_combine": (i32, [vp, i64, i64, vp, vp]),
         "rmsnorm_status_str": (ctypes.c_char_p, [i32]),
         "rmsnorm_select_config": (i32, [i64, i64, i32, i32, i32, i32, i32, cfgp]),
@@ -95,7 +100,8 @@ lib = _load()
 
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_config", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
-    "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_status_str",
+    "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_fwd_residual",
+    "rmsnorm_bwd_residual", "rmsnorm_status_str",
     "rmsnorm_select_config", "rmsnorm_query_config", "rmsnorm_build_info",
     "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_read", "rmsn_probe_add",
 )
@@ -122,13 +128,16 @@ def _check(name: str, rc: int) -> None:
         raise RmsnormError(name, rc, rmsnorm_status_str(rc))
 
 
-def dtype_code(torch_dtype) -> int:
-    """rmsn_dtype code of a torch dtype (float32 or bfloat16)."""
-    if torch_dtype == torch.float32:
-        return F32
-    if torch_dtype == torch.bfloat16:
-        return BF16
-    raise ValueError(f"unsupported dtype {torch_dtype}")
+def dtype_code(torch_dtype, weight_dtype=None) -> int:
+    """rmsn_dtype code of an activation torch dtype and (optionally) a weight dtype."""
+    weight_dtype = weight_dtype or torch_dtype
+    codes = {(torch.float32, torch.float32): F32, (torch.bfloat16, torch.bfloat16): BF16,
+             (torch.float16, torch.float16): F16, (torch.bfloat16, torch.float32): BF16_WF32,
+             (torch.float16, torch.float32): F16_WF32}
+    try:
+        return codes[(torch_dtype, weight_dtype)]
+    except KeyError:
+        raise ValueError(f"unsupported formats {torch_dtype} / {weight_dtype}") from None
 
 
 def rmsnorm_status_str(status: int) -> str:
@@ -168,6 +177,21 @@ def rmsnorm_bwd_with_config(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, work
            lib.rmsnorm_bwd_with_config(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N), int(dtype),
                                        _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
                                        ctypes.byref(cfg), _stream(stream)))
+
+
+def rmsnorm_fwd_residual(x, res, w, eps, M, N, dtype, h, y, rstd, cfg=None, stream=None) -> None:
+    _check("rmsnorm_fwd_residual",
+           lib.rmsnorm_fwd_residual(_ptr(x), _ptr(res), _ptr(w), float(eps), int(M), int(N), int(dtype), _ptr(h),
+                                    _ptr(y), _ptr(rstd), None if cfg is None else ctypes.byref(cfg),
+                                    _stream(stream)))
+
+
+def rmsnorm_bwd_residual(h, w, dy, dh, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, cfg=None,
+                         stream=None) -> None:
+    _check("rmsnorm_bwd_residual",
+           lib.rmsnorm_bwd_residual(_ptr(h), _ptr(w), _ptr(dy), _ptr(dh), _ptr(rstd), int(M), int(N), int(dtype),
+                                    _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
+                                    None if cfg is None else ctypes.byref(cfg), _stream(stream)))
 
 
 def rmsnorm_bwd_rows(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, stream=None) -> int:

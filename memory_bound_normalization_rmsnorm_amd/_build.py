@@ -19,8 +19,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["rmsn_fwd_f32.hip", "rmsn_fwd_bf16.hip", "rmsn_bwd_f32.hip", "rmsn_bwd_bf16.hip",
-           "rmsn_common.hip", "rmsn_probe.hip", "rmsn_api.cpp"]
+FORMATS = ["f32", "bf16", "f16", "bf16w32", "f16w32"]
+SOURCES = ([f"rmsn_fwd_{f}.hip" for f in FORMATS] + [f"rmsn_bwd_{f}.hip" for f in FORMATS]
+           + ["rmsn_common.hip", "rmsn_probe.hip", "rmsn_api.cpp"])
 HEADERS = ["rmsn_device.h", "rmsn_tables.h", "rmsn_instances.h", "rmsn_fwd_kernels.h", "rmsn_bwd_kernels.h"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
@@ -62,7 +63,8 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
     os.makedirs(build_dir, exist_ok=True)
     extra = tuple(extra_flags)
     info = f"rmsnorm-mi355x {_git_rev()} {ARCH} hipcc -O3 -packed-fp32-ops {' '.join(extra)}".strip()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 4, 16))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
         results = list(ex.map(lambda s: _compile(s, info, build_dir, extra), SOURCES))
     objs = [o for o, _ in results]
     with open(os.path.join(build_dir, "resource_usage.txt"), "w") as f:

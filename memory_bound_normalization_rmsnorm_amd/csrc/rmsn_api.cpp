@@ -27,8 +27,10 @@ using rmsn::KernelEntry;
 constexpr int64_t kMaxN = int64_t(1) << 30;
 constexpr int64_t kMaxVecLanes = 1024;
 
+// bytes per activation element (x, y, dy, dx, res, h, dh); weights are fp32
+// for RMSN_F32 and the *_WF32 formats, 16-bit otherwise
 int elem_size(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
-bool valid_dtype(int dtype) { return dtype == RMSN_F32 || dtype == RMSN_BF16; }
+bool valid_dtype(int dtype) { return dtype >= RMSN_F32 && dtype <= RMSN_F16_WF32; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -179,20 +181,20 @@ int occupancy(const void *fn, int wg, int *blocks) {
     return RMSN_OK;
 }
 
-const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd) {
-    if (!c.vector_path) return is_bwd ? rmsn::bwd_scalar_kernel(dtype) : rmsn::fwd_scalar_kernel(dtype);
+const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd, int res) {
+    if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res);
     const KernelEntry *e =
-        is_bwd ? rmsn::bwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch)
-               : rmsn::fwd_vec_kernel(dtype, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch);
+        is_bwd ? rmsn::bwd_vec_kernel(dtype, res, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch)
+               : rmsn::fwd_vec_kernel(dtype, res, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch);
     return e ? e->fn : nullptr;
 }
 
-// Full configuration on the current device.
-int resolve(int64_t M, int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config *c,
+// Full configuration on the current device (res: the residual-fused kernel).
+int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, bool aligned, rmsnorm_config *c,
             const void **fn) {
     std::memset(c, 0, sizeof *c);
     ladder_shape(N, dtype, is_bwd, aligned, c);
-    const void *k = kernel_for(*c, dtype, is_bwd);
+    const void *k = kernel_for(*c, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     int cus = 0, blocks = 0;
     int st = device_info(&cus);
@@ -219,8 +221,8 @@ int launch(const void *fn, int64_t grid, int wg, void **args, hipStream_t stream
 // An explicit configuration (config search, benchmarks) is checked against
 // the shape: the kernel must exist, cover the row, and the grid must be
 // positive. Shape fields derived from lanes_per_row are recomputed.
-int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, int is_bwd, bool aligned,
-                    rmsnorm_config *c, const void **fn) {
+int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, int is_bwd, int res,
+                    bool aligned, rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
     if (req->vector_path) {
@@ -234,7 +236,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     } else {
         set_scalar_shape(c);
     }
-    const void *k = kernel_for(*c, dtype, is_bwd);
+    const void *k = kernel_for(*c, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     ladder_grid(M, N, dtype, is_bwd, 1, 1, c);
     c->grid = req->grid;
@@ -243,22 +245,24 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     return RMSN_OK;
 }
 
-int fwd_impl(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype, void *y, float *rstd,
-             void *stream, const rmsnorm_config *req) {
+int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M, int64_t N, int dtype, void *h,
+             void *y, float *rstd, void *stream, const rmsnorm_config *req) {
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!std::isfinite(eps) || eps < 0.f) return RMSN_EINVAL;
     if (M == 0) return RMSN_OK;
-    if (!x || !w || !y) return RMSN_EINVAL;
-    const bool aligned = aligned16(x) && aligned16(w) && aligned16(y);
+    if (!x || !w || !y || (res && !h)) return RMSN_EINVAL;
+    const int fused = res ? 1 : 0;
+    const bool aligned = aligned16(x) && aligned16(w) && aligned16(y) && (!fused || (aligned16(res) && aligned16(h)));
     rmsnorm_config c;
     const void *fn = nullptr;
-    st = req ? explicit_config(req, M, N, dtype, 0, aligned, &c, &fn) : resolve(M, N, dtype, 0, aligned, &c, &fn);
+    st = req ? explicit_config(req, M, N, dtype, 0, fused, aligned, &c, &fn)
+             : resolve(M, N, dtype, 0, fused, aligned, &c, &fn);
     if (st != RMSN_OK) return st;
     int32_t n32 = (int32_t)N;
     int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
-    void *args[] = {(void *)&x, (void *)&w, (void *)&y, (void *)&rstd, (void *)&eps,
-                    (void *)&M, (void *)&n32, (void *)&nvec};
+    void *args[] = {(void *)&x, (void *)&res, (void *)&w, (void *)&h, (void *)&y, (void *)&rstd,
+                    (void *)&eps, (void *)&M, (void *)&n32, (void *)&nvec};
     return launch(fn, c.grid, c.wg_threads, args, static_cast<hipStream_t>(stream));
 }
 
@@ -274,9 +278,9 @@ int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStre
                   rmsn::kCombineWG, cargs, s);
 }
 
-int rows_impl(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N, int dtype,
-              void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows, hipStream_t s,
-              const rmsnorm_config *req) {
+int rows_impl(const void *x, const void *w, const void *dy, const void *dh, const float *rstd, int64_t M,
+              int64_t N, int dtype, void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows,
+              hipStream_t s, const rmsnorm_config *req) {
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!partial_rows) return RMSN_EINVAL;
@@ -284,10 +288,12 @@ int rows_impl(const void *x, const void *w, const void *dy, const float *rstd, i
     if (M == 0) return RMSN_OK;
     if (!x || !w || !dy || !rstd || !dx) return RMSN_EINVAL;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RMSN_EWORKSPACE;
-    const bool aligned = aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx);
+    const int fused = dh ? 1 : 0;
+    const bool aligned = aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx) && (!fused || aligned16(dh));
     rmsnorm_config c;
     const void *fn = nullptr;
-    st = req ? explicit_config(req, M, N, dtype, 1, aligned, &c, &fn) : resolve(M, N, dtype, 1, aligned, &c, &fn);
+    st = req ? explicit_config(req, M, N, dtype, 1, fused, aligned, &c, &fn)
+             : resolve(M, N, dtype, 1, fused, aligned, &c, &fn);
     if (st != RMSN_OK) return st;
     if (req) {
         if (workspace_bytes < (size_t)workspace_for(c)) return RMSN_EWORKSPACE;
@@ -301,15 +307,15 @@ int rows_impl(const void *x, const void *w, const void *dy, const float *rstd, i
     int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
     float *partial = static_cast<float *>(workspace);
     int64_t ldp = c.partial_stride;
-    void *args[] = {(void *)&x, (void *)&w, (void *)&dy, (void *)&rstd, (void *)&dx,
+    void *args[] = {(void *)&x, (void *)&w, (void *)&dy, (void *)&dh, (void *)&rstd, (void *)&dx,
                     (void *)&partial, (void *)&ldp, (void *)&M, (void *)&n32, (void *)&nvec};
     st = launch(fn, c.grid, c.wg_threads, args, s);
     if (st == RMSN_OK) *partial_rows = c.partial_rows;
     return st;
 }
 
-int bwd_impl(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N, int dtype,
-             void *dx, float *dw, void *workspace, size_t workspace_bytes, void *stream,
+int bwd_impl(const void *x, const void *w, const void *dy, const void *dh, const float *rstd, int64_t M,
+             int64_t N, int dtype, void *dx, float *dw, void *workspace, size_t workspace_bytes, void *stream,
              const rmsnorm_config *req) {
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
@@ -323,7 +329,7 @@ int bwd_impl(const void *x, const void *w, const void *dy, const float *rstd, in
     }
     if (!dw) return RMSN_EINVAL;
     int64_t P = 0;
-    st = rows_impl(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req);
+    st = rows_impl(x, w, dy, dh, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req);
     if (st != RMSN_OK) return st;
     return combine_impl(workspace, P, N, dw, s);
 }
@@ -361,50 +367,70 @@ int rmsnorm_query_config(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_co
     const int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!out || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
-    return resolve(M, N, dtype, is_bwd, true, out, nullptr);
+    return resolve(M, N, dtype, is_bwd, 0, true, out, nullptr);
 }
 
 int rmsnorm_fwd(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype, void *y,
                 float *rstd, void *stream) {
-    return fwd_impl(x, w, eps, M, N, dtype, y, rstd, stream, nullptr);
+    return fwd_impl(x, nullptr, w, eps, M, N, dtype, nullptr, y, rstd, stream, nullptr);
 }
 
 int rmsnorm_fwd_with_config(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype,
                             void *y, float *rstd, const rmsnorm_config *cfg, void *stream) {
     if (!cfg) return RMSN_EINVAL;
-    return fwd_impl(x, w, eps, M, N, dtype, y, rstd, stream, cfg);
+    return fwd_impl(x, nullptr, w, eps, M, N, dtype, nullptr, y, rstd, stream, cfg);
+}
+
+int rmsnorm_fwd_residual(const void *x, const void *res, const void *w, float eps, int64_t M, int64_t N,
+                         int dtype, void *h, void *y, float *rstd, const rmsnorm_config *cfg, void *stream) {
+    if (M > 0 && !res) return RMSN_EINVAL;
+    if (M == 0) return check_shape(M, N, dtype);
+    return fwd_impl(x, res, w, eps, M, N, dtype, h, y, rstd, stream, cfg);
 }
 
 int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype) {
     const int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (M == 0) return 0;
-    // Enough for either row kernel, so a caller's alignment never changes the answer.
-    rmsnorm_config cv, cs;
-    int s1 = resolve(M, N, dtype, 1, true, &cv, nullptr);
-    if (s1 != RMSN_OK) return s1;
-    int s2 = resolve(M, N, dtype, 1, false, &cs, nullptr);
-    if (s2 != RMSN_OK) return s2;
-    const int64_t a = workspace_for(cv), b = workspace_for(cs);
-    return a > b ? a : b;
+    // Enough for every row kernel the call may pick (plain or residual-fused,
+    // vector or scalar), so neither the caller's alignment nor the residual
+    // variant changes the answer.
+    int64_t need = 0;
+    for (int fused = 0; fused <= 1; ++fused) {
+        for (int aligned = 0; aligned <= 1; ++aligned) {
+            rmsnorm_config c;
+            const int s = resolve(M, N, dtype, 1, fused, aligned != 0, &c, nullptr);
+            if (s != RMSN_OK) return s;
+            const int64_t b = workspace_for(c);
+            if (b > need) need = b;
+        }
+    }
+    return need;
 }
 
 int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,
                 int dtype, void *dx, float *dw, void *workspace, size_t workspace_bytes, void *stream) {
-    return bwd_impl(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, nullptr);
+    return bwd_impl(x, w, dy, nullptr, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, nullptr);
 }
 
 int rmsnorm_bwd_with_config(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
                             int64_t N, int dtype, void *dx, float *dw, void *workspace,
                             size_t workspace_bytes, const rmsnorm_config *cfg, void *stream) {
     if (!cfg) return RMSN_EINVAL;
-    return bwd_impl(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, cfg);
+    return bwd_impl(x, w, dy, nullptr, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, cfg);
+}
+
+int rmsnorm_bwd_residual(const void *h, const void *w, const void *dy, const void *dh, const float *rstd,
+                         int64_t M, int64_t N, int dtype, void *dx, float *dw, void *workspace,
+                         size_t workspace_bytes, const rmsnorm_config *cfg, void *stream) {
+    if (M > 0 && !dh) return RMSN_EINVAL;
+    return bwd_impl(h, w, dy, dh, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, cfg);
 }
 
 int rmsnorm_bwd_rows(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,
                      int dtype, void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows,
                      void *stream) {
-    return rows_impl(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, partial_rows,
+    return rows_impl(x, w, dy, nullptr, rstd, M, N, dtype, dx, workspace, workspace_bytes, partial_rows,
                      static_cast<hipStream_t>(stream), nullptr);
 }
 

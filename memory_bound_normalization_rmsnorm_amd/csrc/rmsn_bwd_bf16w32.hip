@@ -1,0 +1,20 @@
+// rmsn_bwd_bf16w32.hip -- backward vector kernels for bf16 activations, fp32 weights:
+// the plain kernels on RMSN_LADDER_SHAPES and the residual-fused ones on
+// RMSN_LADDER_SHAPES (rmsn_instances.h), and the lookup the host dispatch uses.
+#include "rmsn_bwd_kernels.h"
+#include "rmsn_instances.h"
+
+namespace rmsn {
+
+#define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&bwd_vec<bf16_t, float, false, L, V, W, (P != 0)>)},
+static const KernelEntry kPlain[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY)};
+#undef RMSN_ENTRY
+#define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&bwd_vec<bf16_t, float, true, L, V, W, (P != 0)>)},
+static const KernelEntry kResidual[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY)};
+#undef RMSN_ENTRY
+
+const KernelEntry *bwd_vec_kernel_bf16w32(int res, int lpr, int vpt, int wg, int pf) {
+    return res ? find_entry(kResidual, lpr, vpt, wg, pf) : find_entry(kPlain, lpr, vpt, wg, pf);
+}
+
+}  // namespace rmsn

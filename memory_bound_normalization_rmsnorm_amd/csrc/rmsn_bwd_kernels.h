@@ -5,21 +5,20 @@
 //     dx_ij = r V_ij - x_ij r^3 S_i / N,    dW_j = sum_i dy_ij x_ij r_i
 // ("RMSNorm backward (almost) without the column reduction": the formulas of
 // section "The backward pass", the persistent design of section "The
-// persistent kernel").
+// persistent kernel"). With the fused residual add (RES), x is the stored sum
+// h the forward wrote and the gradient dh flowing into h from the residual
+// branch is added before the single rounding: dx = dh + (the dx above), the
+// gradient of both inputs of the sum.
 //
 // Persistent row kernel: the grid is sized to what the chip keeps resident.
 // Workgroup b works on rows b*RPW .. b*RPW+RPW-1, then strides by grid*RPW, a
 // fixed row -> workgroup map. Each lane keeps running dW sums for its columns
 // in registers over all the rows it visits; at the end the RPW row groups of
 // the workgroup are added in group order through LDS and the workgroup writes
-// one fp32 partial row. No atomics anywhere. With PF the next row block's x,
-// dy and rstd loads are issued before the current block's arithmetic (a
-// register double buffer in place of the pages' shared-memory async-copy
-// pipeline: the persistent grid gives up the scheduler's latency hiding).
-//
-// Combine kernel: dW_j = sum_p partial[p][j] in a fixed order (64 strided
-// slices of p summed in ascending order, then a fixed binary tree over the
-// slices), one workgroup per 16 columns.
+// one fp32 partial row. No atomics anywhere. With PF the next row block's
+// loads are issued before the current block's arithmetic (a register double
+// buffer in place of the pages' shared-memory async-copy pipeline: the
+// persistent grid gives up the scheduler's latency hiding).
 //
 // The results depend only on (M, N, dtype, grid): the same call on the same
 // device gives the same bits every time.
@@ -30,13 +29,23 @@
 
 namespace rmsn {
 
-template <typename T, int LPR, int VPT, int WG, bool PF>
+// 16-byte vectors a lane keeps per row slot: x, dy (and dh), the weights, and
+// the prefetched copies.
+template <typename T, typename TW, bool RES, bool PF>
+constexpr int bwd_packed_per_slot() {
+    constexpr int in = RES ? 3 : 2;
+    return in + WeightVec<T, TW>::kVecs + (PF ? in : 0);
+}
+
+template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, bool PF>
 __global__ void __launch_bounds__(WG)
-__attribute__((amdgpu_waves_per_eu(waves_for(PF ? 5 * VPT : 3 * VPT, VPT * Elem<T>::kPerVec, VPT, WG))))
-bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ dy,
-        const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial,
-        int64_t ldp, int64_t M, int32_t N, int32_t nvec) {
+__attribute__((amdgpu_waves_per_eu(waves_for(VPT * bwd_packed_per_slot<T, TW, RES, PF>(),
+                                             VPT * Elem<T>::kPerVec, VPT, WG))))
+bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
+        const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
+        int32_t N, int32_t nvec) {
     using E = Elem<T>;
+    using WV = WeightVec<T, TW>;
     constexpr int EPV = E::kPerVec;
     constexpr int RPW = WG / LPR;
     static_assert(WG % LPR == 0, "workgroup must hold whole row groups");
@@ -51,14 +60,14 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
     // Byte offset of each of this lane's vectors inside a row block; vectors
     // past the row end get an out-of-range offset (load 0, store nothing).
     uint32_t off[VPT];
-    const Buf wb(w, row_bytes);
-    u32x4 wv[VPT];
+    const Buf wb(w, row_bytes * WV::kVecs);
+    WV wv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int idx = v * LPR + lane;
         const bool in = idx < nvec;
         off[v] = in ? (uint32_t)grp * row_bytes + (uint32_t)idx * 16u : kOff;
-        wv[v] = wb.load16(in ? (uint32_t)idx * 16u : kOff);
+        wv[v].load(wb, idx, in);
     }
     float acc[VPT][EPV];
 #pragma unroll
@@ -71,57 +80,50 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
         const int64_t left = M - b;
         return left <= 0 ? 0u : (left < RPW ? (uint32_t)left : (uint32_t)RPW);
     };
+    // the block's x, dy (and dh) vectors and its rows' rstd; rows past M read
+    // r = 0 and zeros, so they add nothing to dW
+    auto load_block = [&](int64_t b, u32x4 (&xo)[VPT], u32x4 (&go)[VPT], u32x4 (&ho)[VPT], float &ro) {
+        const int64_t bb = b < M ? b : 0;
+        const uint32_t rows = rows_at(b);
+        const Buf xb(x + bb * N, rows * row_bytes), gb(dy + bb * N, rows * row_bytes), rb(rstd + bb, rows * 4u);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            xo[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+            go[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+        }
+        if constexpr (RES) {
+            const Buf hb(dh + bb * N, rows * row_bytes);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) ho[v] = hb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+        }
+        ro = rb.load4((uint32_t)grp * 4u);
+    };
 
     int parity = 0;
     const int64_t step = (int64_t)gridDim.x * RPW;
     int64_t base = (int64_t)blockIdx.x * RPW;
-    u32x4 xn[VPT], gn[VPT];  // prefetched next block (PF)
+    u32x4 xn[VPT], gn[VPT], hn[VPT];  // prefetched next block (PF)
     float rn = 0.f;
-    if constexpr (PF) {
-        const int64_t b0 = base < M ? base : 0;
-        const uint32_t rows0 = rows_at(base);
-        const Buf xb(x + b0 * N, rows0 * row_bytes), gb(dy + b0 * N, rows0 * row_bytes), rb(rstd + b0, rows0 * 4u);
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            xn[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
-            gn[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
-        }
-        rn = rb.load4((uint32_t)grp * 4u);
-    }
+    if constexpr (PF) load_block(base, xn, gn, hn, rn);
     for (; base < M; base += step) {
         const uint32_t rows = rows_at(base);
         const Buf db(dx + base * N, rows * row_bytes);
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) keep_packed(wv[v]);
+        for (int v = 0; v < VPT; ++v) wv[v].keep();
 
-        // rows past M read r = 0 (and x = dy = 0), so they add nothing to dW
-        u32x4 xv[VPT], gv[VPT];
+        u32x4 xv[VPT], gv[VPT], hv[VPT];
         float r;
         if constexpr (PF) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) {
                 xv[v] = xn[v];
                 gv[v] = gn[v];
+                if constexpr (RES) hv[v] = hn[v];
             }
             r = rn;
-            const int64_t nb = base + step;
-            const int64_t b1 = nb < M ? nb : base;
-            const uint32_t rows1 = rows_at(nb);
-            const Buf xb(x + b1 * N, rows1 * row_bytes), gb(dy + b1 * N, rows1 * row_bytes), rb(rstd + b1, rows1 * 4u);
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                xn[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
-                gn[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
-            }
-            rn = rb.load4((uint32_t)grp * 4u);
+            load_block(base + step, xn, gn, hn, rn);
         } else {
-            const Buf xb(x + base * N, rows * row_bytes), gb(dy + base * N, rows * row_bytes), rb(rstd + base, rows * 4u);
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                xv[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
-                gv[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
-            }
-            r = rb.load4((uint32_t)grp * 4u);
+            load_block(base, xv, gv, hv, r);
         }
 
         float s = 0.f;
@@ -130,7 +132,7 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
             float fx[EPV], fg[EPV], fw[EPV];
             E::unpack(xv[v], fx);
             E::unpack(gv[v], fg);
-            E::unpack(wv[v], fw);
+            wv[v].unpack(fw);
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
                 s = __builtin_fmaf(fg[k] * fw[k], fx[k], s);
@@ -144,16 +146,22 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
         for (int v = 0; v < VPT; ++v) {
             keep_packed(xv[v]);
             keep_packed(gv[v]);
-            keep_packed(wv[v]);
+            wv[v].keep();
         }
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             float fx[EPV], fg[EPV], fw[EPV], o[EPV];
             E::unpack(xv[v], fx);
             E::unpack(gv[v], fg);
-            E::unpack(wv[v], fw);
+            wv[v].unpack(fw);
 #pragma unroll
             for (int k = 0; k < EPV; ++k) o[k] = __builtin_fmaf(-fx[k], c, r * (fg[k] * fw[k]));
+            if constexpr (RES) {
+                float fh[EPV];
+                E::unpack(hv[v], fh);
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) o[k] += fh[k];
+            }
             db.store16<RMSN_BWD_STORE_AUX>(off[v], E::pack(o));
         }
     }
@@ -194,11 +202,11 @@ bwd_vec(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ 
     }
 }
 
-template <typename T>
+template <typename T, typename TW, bool RES>
 __global__ void __launch_bounds__(kScalarWG)
-bwd_scalar(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ dy,
-           const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial,
-           int64_t ldp, int64_t M, int32_t N, int32_t /*nvec*/) {
+bwd_scalar(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
+           const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
+           int32_t N, int32_t /*nvec*/) {
     using E = Elem<T>;
     __shared__ float slots[2 * (kScalarWG / 64)];
     const float n = (float)N;
@@ -208,19 +216,19 @@ bwd_scalar(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     for (int j = threadIdx.x; j < N; j += kScalarWG) prow[j] = 0.f;
     int parity = 0;
     for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-        const T *xr = x + row * (int64_t)N;
-        const T *gr = dy + row * (int64_t)N;
+        const int64_t o = row * (int64_t)N;
         const float r = rstd[row];
         float s = 0.f;
         for (int j = threadIdx.x; j < N; j += kScalarWG)
-            s = __builtin_fmaf(E::load(gr + j) * E::load(w + j), E::load(xr + j), s);
+            s = __builtin_fmaf(E::load(dy + o + j) * Elem<TW>::load(w + j), E::load(x + o + j), s);
         s = row_sum<kScalarWG, kScalarWG>(s, slots, parity);
         parity ^= 1;
-        const float c = r * (r * (r * (s / n)));  // r^3 S/N without forming r^3 (underflows for rows near 1e15)
-        T *dr = dx + row * (int64_t)N;
+        const float c = r * (r * (r * (s / n)));
         for (int j = threadIdx.x; j < N; j += kScalarWG) {
-            const float fx = E::load(xr + j), fg = E::load(gr + j), fw = E::load(w + j);
-            E::store(dr + j, __builtin_fmaf(-fx, c, r * (fg * fw)));
+            const float fx = E::load(x + o + j), fg = E::load(dy + o + j), fw = Elem<TW>::load(w + j);
+            float g = __builtin_fmaf(-fx, c, r * (fg * fw));
+            if constexpr (RES) g += E::load(dh + o + j);
+            E::store(dx + o + j, g);
             prow[j] = __builtin_fmaf(fg * fx, r, prow[j]);
         }
     }

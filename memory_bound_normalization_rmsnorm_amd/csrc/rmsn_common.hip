@@ -59,27 +59,55 @@ __global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t 
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-const KernelEntry *fwd_vec_kernel_f32(int lpr, int vpt, int wg, int pf);
-const KernelEntry *fwd_vec_kernel_bf16(int lpr, int vpt, int wg, int pf);
-const KernelEntry *bwd_vec_kernel_f32(int lpr, int vpt, int wg, int pf);
-const KernelEntry *bwd_vec_kernel_bf16(int lpr, int vpt, int wg, int pf);
+#define RMSN_FORMATS(X) X(f32) X(bf16) X(f16) X(bf16w32) X(f16w32)
+#define RMSN_DECL(tag)                                                                 \
+    const KernelEntry *fwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf); \
+    const KernelEntry *bwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf);
+RMSN_FORMATS(RMSN_DECL)
+#undef RMSN_DECL
 
-const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf) {
-    return dtype == 0 ? fwd_vec_kernel_f32(lpr, vpt, wg, pf) : fwd_vec_kernel_bf16(lpr, vpt, wg, pf);
+// Format codes (rmsn_dtype): 0 fp32, 1 bf16, 2 fp16, 3 bf16 with fp32 weights,
+// 4 fp16 with fp32 weights.
+const KernelEntry *fwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf) {
+    switch (dtype) {
+    case 0: return fwd_vec_kernel_f32(res, lpr, vpt, wg, pf);
+    case 1: return fwd_vec_kernel_bf16(res, lpr, vpt, wg, pf);
+    case 2: return fwd_vec_kernel_f16(res, lpr, vpt, wg, pf);
+    case 3: return fwd_vec_kernel_bf16w32(res, lpr, vpt, wg, pf);
+    case 4: return fwd_vec_kernel_f16w32(res, lpr, vpt, wg, pf);
+    default: return nullptr;
+    }
 }
 
-const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf) {
-    return dtype == 0 ? bwd_vec_kernel_f32(lpr, vpt, wg, pf) : bwd_vec_kernel_bf16(lpr, vpt, wg, pf);
+const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf) {
+    switch (dtype) {
+    case 0: return bwd_vec_kernel_f32(res, lpr, vpt, wg, pf);
+    case 1: return bwd_vec_kernel_bf16(res, lpr, vpt, wg, pf);
+    case 2: return bwd_vec_kernel_f16(res, lpr, vpt, wg, pf);
+    case 3: return bwd_vec_kernel_bf16w32(res, lpr, vpt, wg, pf);
+    case 4: return bwd_vec_kernel_f16w32(res, lpr, vpt, wg, pf);
+    default: return nullptr;
+    }
 }
 
-const void *fwd_scalar_kernel(int dtype) {
-    return dtype == 0 ? reinterpret_cast<const void *>(&fwd_scalar<float>)
-                      : reinterpret_cast<const void *>(&fwd_scalar<bf16_t>);
+template <typename T, typename TW>
+const void *scalar_kernel(int is_bwd, int res) {
+    if (is_bwd)
+        return res ? reinterpret_cast<const void *>(&bwd_scalar<T, TW, true>)
+                   : reinterpret_cast<const void *>(&bwd_scalar<T, TW, false>);
+    return res ? reinterpret_cast<const void *>(&fwd_scalar<T, TW, true>)
+               : reinterpret_cast<const void *>(&fwd_scalar<T, TW, false>);
 }
 
-const void *bwd_scalar_kernel(int dtype) {
-    return dtype == 0 ? reinterpret_cast<const void *>(&bwd_scalar<float>)
-                      : reinterpret_cast<const void *>(&bwd_scalar<bf16_t>);
+const void *scalar_kernel(int dtype, int is_bwd, int res) {
+    switch (dtype) {
+    case 0: return scalar_kernel<float, float>(is_bwd, res);
+    case 1: return scalar_kernel<bf16_t, bf16_t>(is_bwd, res);
+    case 2: return scalar_kernel<f16_t, f16_t>(is_bwd, res);
+    case 3: return scalar_kernel<bf16_t, float>(is_bwd, res);
+    case 4: return scalar_kernel<f16_t, float>(is_bwd, res);
+    default: return nullptr;
+    }
 }
 
 const void *dw_combine_kernel() { return reinterpret_cast<const void *>(&dw_combine); }

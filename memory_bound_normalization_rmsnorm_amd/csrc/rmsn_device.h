@@ -20,6 +20,7 @@ namespace rmsn {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t g32x4 __attribute__((vector_size(16)));  // the buffer builtins' vector type
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Bit reinterpretation goes through these by-value helpers. Applied directly
 // to an ext_vector element (`__builtin_bit_cast(float, v.y)`), clang reads
@@ -28,9 +29,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
-// Storage types: fp32 is `float`; bf16 is carried as its 16-bit pattern.
+// Storage types: fp32 is `float`; bf16 and fp16 are carried as their 16-bit
+// patterns.
 struct bf16_t {
+    uint16_t bits;
+};
+struct f16_t {
     uint16_t bits;
 };
 
@@ -111,6 +117,49 @@ struct Elem<bf16_t> {
     }
 };
 
+__device__ __forceinline__ float f16_lo(uint32_t d) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(d & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t d) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> 16)); }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};  // round to nearest even (v_cvt_f16_f32)
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <>
+struct Elem<f16_t> {
+    static constexpr int kPerVec = 8;
+    static __device__ __forceinline__ float load(const f16_t *p) { return (float)__builtin_bit_cast(_Float16, p->bits); }
+    static __device__ __forceinline__ void store(f16_t *p, float v) {
+        p->bits = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+    static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[8]) {
+        f[0] = f16_lo(v.x);
+        f[1] = f16_hi(v.x);
+        f[2] = f16_lo(v.y);
+        f[3] = f16_hi(v.y);
+        f[4] = f16_lo(v.z);
+        f[5] = f16_hi(v.z);
+        f[6] = f16_lo(v.w);
+        f[7] = f16_hi(v.w);
+    }
+    // acc + sum of squares with v_dot2_f32_f16: each fp16 product is exact in
+    // fp32; pairs are added in element order.
+    static __device__ __forceinline__ float sumsq(const u32x4 &v, float acc) {
+        acc = __builtin_amdgcn_fdot2(as_f16x2(v.x), as_f16x2(v.x), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(v.y), as_f16x2(v.y), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(v.z), as_f16x2(v.z), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(v.w), as_f16x2(v.w), acc, false);
+        return acc;
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&f)[8]) {
+        u32x4 v;
+        v.x = pack_f16x2(f[0], f[1]);
+        v.y = pack_f16x2(f[2], f[3]);
+        v.z = pack_f16x2(f[4], f[5]);
+        v.w = pack_f16x2(f[6], f[7]);
+        return v;
+    }
+};
+
 // Raw buffer resource (stride 0): `bytes` is the record count. Word 3 of the
 // descriptor selects 32-bit data format, the value used for raw (untyped)
 // buffer access on CDNA. The base pointer must be wave-uniform.
@@ -160,6 +209,42 @@ struct Buf {
 // them where they are used, instead of hoisting or keeping the unpacked fp32
 // copies alive (twice the registers for bf16), which would cut occupancy.
 __device__ __forceinline__ void keep_packed(u32x4 &v) { asm volatile("" : "+v"(v)); }
+
+// The weights that pair with one 16-byte activation vector of format T, in
+// format TW: one 16-byte vector when TW is T, two when 16-bit activations
+// meet fp32 (master) weights. Weight element e of the group belongs to the
+// same column as activation element e.
+template <typename T, typename TW>
+struct WeightVec {
+    static constexpr int kPerVec = Elem<T>::kPerVec;
+    static constexpr int kVecs = kPerVec * (int)sizeof(TW) / 16;
+    static_assert(kVecs == 1 || kVecs == 2, "weights pair with one activation vector");
+    u32x4 v[kVecs];
+
+    // idx: the activation vector's index in its row (kOff-style masking by `in`)
+    __device__ __forceinline__ void load(const Buf &wb, int idx, bool in) {
+#pragma unroll
+        for (int q = 0; q < kVecs; ++q) v[q] = wb.load16(in ? (uint32_t)(idx * kVecs + q) * 16u : kOff);
+    }
+    __device__ __forceinline__ void keep() {
+#pragma unroll
+        for (int q = 0; q < kVecs; ++q) keep_packed(v[q]);
+    }
+    __device__ __forceinline__ void unpack(float (&f)[kPerVec]) const {
+        if constexpr (kVecs == 1) {
+            Elem<TW>::unpack(v[0], f);
+        } else {
+            float a[4], b[4];
+            Elem<float>::unpack(v[0], a);
+            Elem<float>::unpack(v[1], b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = a[e];
+                f[4 + e] = b[e];
+            }
+        }
+    }
+};
 
 // ---- lane-group sums ------------------------------------------------------
 

@@ -1,14 +1,20 @@
-// rmsn_fwd_bf16.hip -- forward vector kernels, bf16 storage: every
-// shape of rmsn_instances.h, and the lookup the host dispatch uses.
+// rmsn_fwd_bf16.hip -- forward vector kernels for bf16 activations and weights:
+// the plain kernels on RMSN_ALL_SHAPES and the residual-fused ones on
+// RMSN_LADDER_SHAPES (rmsn_instances.h), and the lookup the host dispatch uses.
 #include "rmsn_fwd_kernels.h"
 #include "rmsn_instances.h"
 
 namespace rmsn {
 
-#define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&fwd_vec<bf16_t, L, V, W, (P != 0)>)},
-static const KernelEntry kTable[] = {RMSN_ALL_SHAPES(RMSN_ENTRY)};
+#define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&fwd_vec<bf16_t, bf16_t, false, L, V, W, (P != 0)>)},
+static const KernelEntry kPlain[] = {RMSN_ALL_SHAPES(RMSN_ENTRY)};
+#undef RMSN_ENTRY
+#define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&fwd_vec<bf16_t, bf16_t, true, L, V, W, (P != 0)>)},
+static const KernelEntry kResidual[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY)};
 #undef RMSN_ENTRY
 
-const KernelEntry *fwd_vec_kernel_bf16(int lpr, int vpt, int wg, int pf) { return find_entry(kTable, lpr, vpt, wg, pf); }
+const KernelEntry *fwd_vec_kernel_bf16(int res, int lpr, int vpt, int wg, int pf) {
+    return res ? find_entry(kResidual, lpr, vpt, wg, pf) : find_entry(kPlain, lpr, vpt, wg, pf);
+}
 
 }  // namespace rmsn

@@ -1,11 +1,15 @@
 // rmsn_instances.h -- the (lanes per row, vectors per lane, workgroup size,
-// prefetch) shapes the vector kernels are built for, as an X-macro list:
-// RMSN_ALL_SHAPES(X) expands X(L, V, W, P) once per shape.
+// prefetch) shapes the vector kernels are built for, as X-macro lists that
+// expand X(L, V, W, P) once per shape.
+// RMSN_ALL_SHAPES (204 shapes; the fp32 and bf16 kernels, the configuration
+// search space):
 //   * narrow rows (1..32 lanes, one vector each): 256-lane workgroups;
 //   * one or more wavefronts per row with 1..8 vectors per lane, and
 //     workgroups of 256, 512 or 1024 lanes (the ladder's default is the
 //     smallest that holds a row and four wavefronts);
 //   * every shape with and without the register prefetch of the next row.
+// RMSN_LADDER_SHAPES (92 shapes; fp16, fp32-weight and residual-fused
+// kernels): the same, with only the ladder's default workgroup per width.
 #pragma once
 
 #define RMSN_V8(X, L, W, P) X(L, 1, W, P) X(L, 2, W, P) X(L, 3, W, P) X(L, 4, W, P) \
@@ -22,6 +26,13 @@
     RMSN_PF(RMSN_V8, X, 256, 256) RMSN_PF(RMSN_V8, X, 256, 512) RMSN_PF(RMSN_V8, X, 256, 1024) \
     RMSN_PF(RMSN_V8, X, 512, 512) RMSN_PF(RMSN_V8, X, 512, 1024)                              \
     RMSN_PF(RMSN_V8, X, 1024, 1024)
+
+#define RMSN_LADDER_SHAPES(X)                                                                 \
+    RMSN_PF(RMSN_NARROW, X, 1, 256) RMSN_PF(RMSN_NARROW, X, 2, 256)                           \
+    RMSN_PF(RMSN_NARROW, X, 4, 256) RMSN_PF(RMSN_NARROW, X, 8, 256)                           \
+    RMSN_PF(RMSN_NARROW, X, 16, 256) RMSN_PF(RMSN_NARROW, X, 32, 256)                         \
+    RMSN_PF(RMSN_V8, X, 64, 256) RMSN_PF(RMSN_V8, X, 128, 256) RMSN_PF(RMSN_V8, X, 256, 256)  \
+    RMSN_PF(RMSN_V8, X, 512, 512) RMSN_PF(RMSN_V8, X, 1024, 1024)
 
 namespace rmsn {
 

@@ -39,11 +39,11 @@ struct KernelEntry {
     const void *fn;  // __global__ function
 };
 
-// dtype: 0 fp32, 1 bf16. nullptr when (lpr, vpt, wg, pf) is not instantiated.
-const KernelEntry *fwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf);
-const KernelEntry *bwd_vec_kernel(int dtype, int lpr, int vpt, int wg, int pf);
-const void *fwd_scalar_kernel(int dtype);
-const void *bwd_scalar_kernel(int dtype);
+// dtype: an rmsn_dtype code (activation and weight formats); res: 1 for the
+// residual-fused kernels. nullptr when (lpr, vpt, wg, pf) is not instantiated.
+const KernelEntry *fwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf);
+const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf);
+const void *scalar_kernel(int dtype, int is_bwd, int res);
 const void *dw_combine_kernel();
 const void *fill_zero_kernel();
 

@@ -8,7 +8,8 @@ bit-identical inputs.
 
 Storage conventions:
   * fp32 tensors are ``np.float32`` arrays;
-  * bf16 tensors are ``np.uint16`` arrays holding the bf16 bit patterns.
+  * bf16 tensors are ``np.uint16`` arrays holding the bf16 bit patterns;
+  * fp16 tensors are ``np.float16`` arrays (numpy rounds to nearest even).
 
 The workloads mirror the synthetic shapes measured on the pages: the Quack
 Hopper study's widest row (32768 x 8192, "What a tuned RMSNorm kernel actually
@@ -23,7 +24,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-DTYPES = ("f32", "bf16")
+DTYPES = ("f32", "bf16", "f16")
 
 
 def f32_to_bf16_bits(a: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
@@ -53,6 +54,8 @@ def to_storage(a32: np.ndarray, dtype: str) -> np.ndarray:
         return np.ascontiguousarray(a32, dtype=np.float32)
     if dtype == "bf16":
         return f32_to_bf16_bits(a32)
+    if dtype == "f16":
+        return np.ascontiguousarray(np.asarray(a32, dtype=np.float32).astype(np.float16))
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -61,6 +64,8 @@ def storage_to_f32(a: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(a, dtype=np.float32)
     if dtype == "bf16":
         return bf16_bits_to_f32(a)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float16).astype(np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -169,8 +174,9 @@ def make_inputs(wl: Workload):
 
 
 def random_case(M: int, N: int, dtype: str, seed: int, x_scale: float = 1.0,
-                dy_scale: float = 1.0, w_dist: str = "normal"):
-    """Small seeded case for parity tests: (x, w, dy) in storage format."""
+                dy_scale: float = 1.0, w_dist: str = "normal", wdtype: str | None = None):
+    """Small seeded case for parity tests: (x, w, dy) in storage format (w in
+    `wdtype`, default the activation format)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     x = rng.standard_normal((M, N), dtype=np.float32) * np.float32(x_scale)
     if w_dist == "normal":
@@ -178,4 +184,10 @@ def random_case(M: int, N: int, dtype: str, seed: int, x_scale: float = 1.0,
     else:
         w = rng.uniform(0.5, 1.5, N).astype(np.float32)
     dy = rng.standard_normal((M, N), dtype=np.float32) * np.float32(dy_scale)
-    return to_storage(x, dtype), to_storage(w, dtype), to_storage(dy, dtype)
+    return to_storage(x, dtype), to_storage(w, wdtype or dtype), to_storage(dy, dtype)
+
+
+def random_tensor(shape, dtype: str, seed: int, scale: float = 1.0) -> np.ndarray:
+    """A seeded N(0, scale^2) tensor in storage format (residuals, gradients)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return to_storage(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale), dtype)

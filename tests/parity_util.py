@@ -10,7 +10,10 @@ Tolerance gates (fp64 oracle value o, GPU value g):
   fp32 dW:     |g - o| <= 1e-5 * max(|o|, rms(o))
   bf16 y, dx:  |g - o| <= 2^-7 * |o| + 1e-3            (the stated bf16 bound)
                and, stricter, |g - o| <= 2^-7 * (|o| + 0.01 * rms of the row)
-  bf16 dW:     |g - o| <= 1e-3 * max(|o|, 1e-2 * rms(o))
+  fp16 y, dx:  |g - o| <= 2^-10 * (|o| + 0.01 * rms of the row) + 2^-24
+               (one rounding to fp16 is at most 2^-11 relative, doubled; the
+               constant covers fp16's subnormal quantum)
+  bf16, fp16 dW: |g - o| <= 1e-3 * max(|o|, 1e-2 * rms(o))
   rstd:        |g - o| <= 1e-5 * o                     (both dtypes)
 The row-rms floor is needed because dx = r*V - x*c can cancel to ~0, where a
 purely relative bound is meaningless. The bf16 bound covers one rounding to
@@ -24,13 +27,21 @@ import torch
 
 import memory_bound_normalization_rmsnorm_amd as rn
 
-DT = {"f32": rn.F32, "bf16": rn.BF16}
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": rn.F32, "bf16": rn.BF16, "f16": rn.F16}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+# format name -> (activation storage, weight storage, rmsn_dtype code)
+FORMATS = {"f32": ("f32", "f32", rn.F32), "bf16": ("bf16", "bf16", rn.BF16), "f16": ("f16", "f16", rn.F16),
+           "bf16w32": ("bf16", "f32", rn.BF16_WF32), "f16w32": ("f16", "f32", rn.F16_WF32)}
 
 
-def to_device(a: np.ndarray, dtype: str) -> torch.Tensor:
+def _storage_of(a: np.ndarray) -> str:
+    return {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16", np.dtype(np.float16): "f16"}[a.dtype]
+
+
+def to_device(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
     """Storage-format numpy array -> device tensor of the matching torch dtype."""
     a = np.ascontiguousarray(a)
+    dtype = dtype or _storage_of(a)
     if dtype == "bf16":
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
     else:
@@ -46,7 +57,8 @@ def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
     return t.numpy()
 
 
-def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+def widen(a: np.ndarray, dtype: str | None = None) -> np.ndarray:
+    dtype = dtype or _storage_of(np.asarray(a))
     if dtype == "bf16":
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
@@ -57,24 +69,45 @@ def empty_like_storage(shape, dtype: str, fill=float("nan")) -> torch.Tensor:
     return torch.full(shape, fill, dtype=TORCH_DT[dtype], device="cuda")
 
 
+def _code(dtype, w):
+    """rmsn_dtype code from the activation storage name and the weight array."""
+    wd = _storage_of(np.asarray(w))
+    if wd == dtype:
+        return DT[dtype]
+    return {("bf16", "f32"): rn.BF16_WF32, ("f16", "f32"): rn.F16_WF32}[(dtype, wd)]
+
+
 def gpu_fwd(x, w, eps, dtype, cfg=None, x_dev=None, w_dev=None):
-    """Run the forward through the C ABI. Returns (y storage array, rstd fp32 array)."""
+    """Run the forward through the C ABI. Returns (y storage array, rstd fp32 array).
+    dtype names the activation storage; the weight format is w's own."""
     M, N = x.shape
     xd = to_device(x, dtype) if x_dev is None else x_dev
-    wd = to_device(w, dtype) if w_dev is None else w_dev
+    wd = to_device(w) if w_dev is None else w_dev
     y = empty_like_storage((M, N), dtype)
     rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
     if cfg is None:
-        rn.rmsnorm_fwd(xd, wd, eps, M, N, DT[dtype], y, rstd)
+        rn.rmsnorm_fwd(xd, wd, eps, M, N, _code(dtype, w), y, rstd)
     else:
-        rn.rmsnorm_fwd_with_config(xd, wd, eps, M, N, DT[dtype], y, rstd, cfg)
+        rn.rmsnorm_fwd_with_config(xd, wd, eps, M, N, _code(dtype, w), y, rstd, cfg)
     torch.cuda.synchronize()
     return to_host(y, dtype), rstd.cpu().numpy()
 
 
-def workspace(M, N, dtype, cfg=None):
+def gpu_fwd_residual(x, res, w, eps, dtype, cfg=None):
+    """Fused residual forward. Returns (h, y storage arrays, rstd fp32 array)."""
+    M, N = x.shape
+    h = empty_like_storage((M, N), dtype)
+    y = empty_like_storage((M, N), dtype)
+    rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd_residual(to_device(x, dtype), to_device(res, dtype), to_device(w), eps, M, N, _code(dtype, w),
+                            h, y, rstd, cfg)
+    torch.cuda.synchronize()
+    return to_host(h, dtype), to_host(y, dtype), rstd.cpu().numpy()
+
+
+def workspace(M, N, code, cfg=None):
     if cfg is None:
-        nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, DT[dtype])
+        nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, code)
     else:
         nbytes = int(cfg.grid) * ((N + 63) // 64 * 64) * 4
     # 256-byte aligned (the caching allocator aligns to 512); poisoned with NaN
@@ -82,19 +115,23 @@ def workspace(M, N, dtype, cfg=None):
     return ws, nbytes
 
 
-def gpu_bwd(x, w, dy, rstd, dtype, cfg=None):
+def gpu_bwd(x, w, dy, rstd, dtype, cfg=None, dh=None):
     """Run the backward through the C ABI. rstd: fp32 numpy array (as the forward wrote it).
+    With dh, the residual-fused backward (x is then the stored sum h).
     Returns (dx storage array, dW fp32 array)."""
     M, N = x.shape
-    xd, wd, gd = to_device(x, dtype), to_device(w, dtype), to_device(dy, dtype)
+    code = _code(dtype, w)
+    xd, wd, gd = to_device(x, dtype), to_device(w), to_device(dy, dtype)
     rd = torch.from_numpy(np.ascontiguousarray(rstd, dtype=np.float32)).to("cuda")
     dx = empty_like_storage((M, N), dtype)
     dw = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
-    ws, nbytes = workspace(M, N, dtype, cfg)
-    if cfg is None:
-        rn.rmsnorm_bwd(xd, wd, gd, rd, M, N, DT[dtype], dx, dw, ws, nbytes)
+    ws, nbytes = workspace(M, N, code, cfg)
+    if dh is not None:
+        rn.rmsnorm_bwd_residual(xd, wd, gd, to_device(dh, dtype), rd, M, N, code, dx, dw, ws, nbytes, cfg)
+    elif cfg is None:
+        rn.rmsnorm_bwd(xd, wd, gd, rd, M, N, code, dx, dw, ws, nbytes)
     else:
-        rn.rmsnorm_bwd_with_config(xd, wd, gd, rd, M, N, DT[dtype], dx, dw, ws, nbytes, cfg)
+        rn.rmsnorm_bwd_with_config(xd, wd, gd, rd, M, N, code, dx, dw, ws, nbytes, cfg)
     torch.cuda.synchronize()
     return to_host(dx, dtype), dw.cpu().numpy()
 
@@ -106,11 +143,16 @@ def _fail(what, err, bound, g, o):
             f"gpu={g[idx]!r} oracle={o[idx]!r} err={err[idx]:.3e} bound={bound[idx]:.3e}")
 
 
-def term_rms(x, w, dy, r, dtype, rows=None) -> np.ndarray:
-    """Per-row rms of r_i * dy_ij * w_j (fp64, from the inputs and the oracle's r)."""
+def term_rms(x, w, dy, r, dtype, rows=None, dh=None) -> np.ndarray:
+    """Per-row rms of the terms dx adds up: r_i * dy_ij * w_j, and dh when the
+    residual gradient is added (fp64, from the inputs and the oracle's r)."""
     gs = dy if rows is None else dy[rows]
-    t = r[:, None] * widen(gs, dtype) * widen(w, dtype)[None, :]
-    return np.sqrt(np.mean(t * t, axis=-1, keepdims=True))
+    t = r[:, None] * widen(gs, dtype) * widen(w)[None, :]
+    out = np.sqrt(np.mean(t * t, axis=-1, keepdims=True))
+    if dh is not None:
+        hs = widen(dh if rows is None else dh[rows], dtype)
+        out = np.maximum(out, np.sqrt(np.mean(hs * hs, axis=-1, keepdims=True)))
+    return out
 
 
 def check_rows(g_storage: np.ndarray, o: np.ndarray, dtype: str, what: str, floor=None) -> dict:
@@ -125,6 +167,9 @@ def check_rows(g_storage: np.ndarray, o: np.ndarray, dtype: str, what: str, floo
         rms = np.maximum(rms, floor)
     if dtype == "f32":
         bound = 1e-5 * np.maximum(np.abs(o), rms)
+        assert np.all(err <= bound), _fail(what, err, bound, g, o)
+    elif dtype == "f16":
+        bound = 2.0 ** -10 * (np.abs(o) + 0.01 * rms) + 2.0 ** -24
         assert np.all(err <= bound), _fail(what, err, bound, g, o)
     else:
         bound = 2.0 ** -7 * np.abs(o) + 1e-3

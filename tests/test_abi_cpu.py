@@ -60,12 +60,43 @@ def test_fwd_argument_errors(args, status):
     assert rc == status
 
 
+def test_residual_argument_errors():
+    # missing residual / dh with rows present; bad format; M = 0 is a no-op
+    assert rn.lib.rmsnorm_fwd_residual(FAKE, None, FAKE, 1e-5, 4, 8, rn.BF16, FAKE, FAKE, None, None, None) == rn.EINVAL
+    assert rn.lib.rmsnorm_fwd_residual(FAKE, FAKE, FAKE, 1e-5, 4, 8, rn.BF16, None, FAKE, None, None, None) == rn.EINVAL
+    assert rn.lib.rmsnorm_fwd_residual(FAKE, FAKE, FAKE, 1e-5, 4, 8, 11, FAKE, FAKE, None, None, None) == rn.EDTYPE
+    assert rn.lib.rmsnorm_fwd_residual(None, None, None, 1e-5, 0, 8, rn.F16, None, None, None, None, None) == rn.OK
+    assert rn.lib.rmsnorm_bwd_residual(FAKE, FAKE, FAKE, None, FAKE, 4, 8, rn.F16, FAKE, FAKE, FAKE, 1 << 20,
+                                       None, None) == rn.EINVAL
+    assert rn.lib.rmsnorm_bwd_residual(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, rn.F16, FAKE, FAKE, None, 1 << 20,
+                                       None, None) == rn.EWORKSPACE
+
+
+def test_dtype_codes():
+    import torch
+    assert rn.dtype_code(torch.float32) == rn.F32 and rn.dtype_code(torch.bfloat16) == rn.BF16
+    assert rn.dtype_code(torch.float16) == rn.F16
+    assert rn.dtype_code(torch.bfloat16, torch.float32) == rn.BF16_WF32
+    assert rn.dtype_code(torch.float16, torch.float32) == rn.F16_WF32
+    with pytest.raises(ValueError):
+        rn.dtype_code(torch.float32, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", [rn.F16, rn.BF16_WF32, rn.F16_WF32])
+def test_ladder_covers_new_formats(dtype):
+    # 16-bit activations: the same shapes as bf16
+    for N, is_bwd in ((4096, 0), (4096, 1), (128, 0), (32768, 1)):
+        a = cfg(16384, N, dtype, is_bwd)
+        b = cfg(16384, N, rn.BF16, is_bwd)
+        assert a == b
+
+
 def test_fwd_empty_is_noop():
     assert rn.lib.rmsnorm_fwd(None, None, 1e-5, 0, 8, rn.F32, None, None, None) == rn.OK
 
 
 @pytest.mark.parametrize("args,status", [
-    (dict(dtype=3), rn.EDTYPE),
+    (dict(dtype=9), rn.EDTYPE),
     (dict(M=-5), rn.EINVAL),
     (dict(dy=None), rn.EINVAL),
     (dict(rstd=None), rn.EINVAL),

@@ -1,0 +1,281 @@
+"""GPU parity for the other storage formats and the fused residual add.
+
+Formats: fp16 activations and weights, and fp32 (master) weights with bf16 or
+fp16 activations ("What a tuned RMSNorm kernel actually costs on Hopper",
+section 07: the weight format is a dimension of its own). Fused residual add
+(page "Profiling, GPU utilisation and writing a fused kernel", Problem 15):
+the stored sum h must equal the oracle's round(x + res) bit for bit, since both
+sides round the exact sum once; y, rstd, dx and dW take the gates of the plain
+path, with the residual gradient dh counted in dx's cancellation floor.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import memory_bound_normalization_rmsnorm_amd as rn  # noqa: E402
+import oracle  # noqa: E402
+import synthetic_inputs as si  # noqa: E402
+from parity_util import (FORMATS, check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd,  # noqa: E402
+                         gpu_fwd_residual, term_rms, to_device, to_host, widen, workspace)
+
+NEW_FORMATS = ("f16", "bf16w32", "f16w32")
+ALL_FORMATS = tuple(FORMATS)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _case(M, N, fmt, seed, dy_scale=1e-2):
+    act, wst, _ = FORMATS[fmt]
+    x, w, dy = si.random_case(M, N, act, seed=seed, dy_scale=dy_scale, wdtype=wst)
+    return act, wst, x, w, dy
+
+
+def plain_check(x, w, dy, eps, act, wst, cfg=None):
+    y, rstd = gpu_fwd(x, w, eps, act, cfg=cfg)
+    oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
+    check_rows(y, oy, act, "y")
+    check_rstd(rstd, orr)
+    dx, dw = gpu_bwd(x, w, dy, rstd, act, cfg=cfg)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
+    check_rows(dx, odx, act, "dx", floor=term_rms(x, w, dy, orr, act))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act)
+
+
+def residual_check(x, res, w, dy, dh, eps, act, wst, cfg=None, rows=None):
+    """Fused residual forward and backward against the oracle's unfused
+    composition. rows: compare only these rows of y and dx (full-size runs)."""
+    h, y, rstd = gpu_fwd_residual(x, res, w, eps, act, cfg=cfg)
+    oh, oy, orr = oracle.fwd_residual(x, res, w, eps, act, rows=rows, wdtype=wst)
+    sel = slice(None) if rows is None else rows
+    assert np.array_equal(widen(h[sel], act), oh), "h differs from round(x + res)"
+    check_rows(y[sel], oy, act, "y (residual)")
+    if rows is None:
+        check_rstd(rstd, orr)
+    else:
+        check_rstd(rstd[rows], orr)
+    dx, dw = gpu_bwd(h, w, dy, rstd, act, cfg=cfg, dh=dh)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, act, rows=rows, res=res, dh=dh, wdtype=wst)
+    hs = h if rows is None else h[rows]
+    check_rows(dx[sel], odx, act, "dx (residual)",
+               floor=term_rms(hs, w, dy, orr, act, rows=rows, dh=dh))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, act, res=res), act, "dW (residual)")
+    return h, y, rstd, dx, dw
+
+
+SHAPES = [(1, 1), (3, 13), (33, 257), (7, 8), (17, 128), (129, 1000), (64, 1024), (31, 4096),
+          (19, 5120), (9, 7168), (3, 8192), (2, 32768), (300, 96), (1000, 16)]
+
+
+@pytest.mark.parametrize("fmt", NEW_FORMATS)
+@pytest.mark.parametrize("M,N", SHAPES, ids=lambda v: str(v))
+def test_formats_small(M, N, fmt):
+    _say(f"formats_small M={M} N={N} {fmt}")
+    act, wst, x, w, dy = _case(M, N, fmt, seed=2000 + M * 7 + N)
+    plain_check(x, w, dy, si.eps_f32(1e-5), act, wst)
+
+
+def _ladder_shapes():
+    """The (lanes_per_row, vecs_per_lane, wg_threads, prefetch) kernels built for
+    every format: the ladder's default workgroup per width."""
+    out = []
+    for pf in (0, 1):
+        out += [(lpr, 1, 256, pf) for lpr in (1, 2, 4, 8, 16, 32)]
+        for lpr in (64, 128, 256, 512, 1024):
+            out += [(lpr, v, max(256, lpr), pf) for v in range(1, 9)]
+    return out
+
+
+def _ragged(lpr, vpt, wg, epv):
+    nvec = min(lpr * vpt, max(1, lpr * (vpt - 1) + max(1, lpr // 2 + 1)))  # the last slot is partial
+    return 3 * (wg // lpr) + 1, nvec * epv
+
+
+@pytest.mark.parametrize("fmt", NEW_FORMATS)
+def test_every_ladder_kernel(fmt):
+    """Each kernel built for the format, forced through *_with_config on a ragged
+    row, a ragged row count and a grid of 2 (workgroups loop over row blocks)."""
+    shapes = _ladder_shapes()
+    assert len(shapes) == 92
+    for lpr, vpt, wg, pf in shapes:
+        M, N = _ragged(lpr, vpt, wg, 8)
+        cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, wg_threads=wg,
+                                prefetch=pf, grid=2)
+        _say(f"kernel lpr={lpr} vpt={vpt} wg={wg} pf={pf} N={N} M={M} {fmt}")
+        act, wst, x, w, dy = _case(M, N, fmt, seed=lpr * 100 + vpt + wg + pf)
+        plain_check(x, w, dy, si.eps_f32(1e-6), act, wst, cfg=cfg)
+
+
+@pytest.mark.parametrize("fmt", NEW_FORMATS)
+def test_formats_scalar_and_unaligned(fmt):
+    M, N = 37, 4096
+    act, wst, x, w, dy = _case(M, N, fmt, seed=78)
+    plain_check(x, w, dy, si.eps_f32(1e-5), act, wst, cfg=rn.rmsnorm_config(vector_path=0, grid=5))
+    xd = to_device(np.concatenate([x.reshape(-1)[:1], x.reshape(-1)]))[1:]
+    wd = to_device(np.concatenate([w[:1], w]))[1:]
+    y = torch.full((M * N + 1,), float("nan"), dtype=xd.dtype, device="cuda")[1:]
+    rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    rn.rmsnorm_fwd(xd, wd, si.eps_f32(1e-5), M, N, FORMATS[fmt][2], y, rstd)
+    torch.cuda.synchronize()
+    oy, orr = oracle.fwd(x, w, si.eps_f32(1e-5), act, wdtype=wst)
+    check_rows(to_host(y, act).reshape(M, N), oy, act, "y (unaligned)")
+    check_rstd(rstd.cpu().numpy(), orr)
+
+
+def test_fp16_range():
+    """fp16 rows near the top of its range (squares overflow fp16, not fp32) and
+    rows of subnormals: the sums are fp32, the outputs rounded once."""
+    M, N = 4, 2048
+    _, _, x, w, dy = _case(M, N, "f16", seed=9, dy_scale=1.0)
+    xs = x.astype(np.float32)
+    xs[0] *= 8000.0     # |x| up to ~4e4, x^2 ~ 1e9
+    xs[1] *= 1e-6       # mostly subnormal fp16
+    xs[2] = 0.0
+    x = si.to_storage(xs, "f16")
+    assert np.all(np.isfinite(x))
+    plain_check(x, w, dy, si.eps_f32(1e-6), "f16", "f16")
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 13), (33, 257), (64, 1024), (31, 4096), (9, 7168), (2, 32768),
+                                 (1000, 16)], ids=lambda v: str(v))
+def test_residual_small(M, N, fmt):
+    _say(f"residual_small M={M} N={N} {fmt}")
+    act, wst, x, w, dy = _case(M, N, fmt, seed=3000 + M * 7 + N, dy_scale=1.0 if fmt == "f32" else 1e-2)
+    res = si.random_tensor((M, N), act, seed=4000 + M + N)
+    dh = si.random_tensor((M, N), act, seed=5000 + M + N, scale=1e-2)
+    residual_check(x, res, w, dy, dh, si.eps_f32(1e-5), act, wst)
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_residual_every_ladder_kernel(fmt):
+    """Each residual-fused kernel, forced, on ragged shapes with a grid of 2."""
+    act = FORMATS[fmt][0]
+    epv = 4 if act == "f32" else 8
+    for lpr, vpt, wg, pf in _ladder_shapes():
+        M, N = _ragged(lpr, vpt, wg, epv)
+        cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, wg_threads=wg,
+                                prefetch=pf, grid=2)
+        _say(f"residual kernel lpr={lpr} vpt={vpt} wg={wg} pf={pf} N={N} M={M} {fmt}")
+        act, wst, x, w, dy = _case(M, N, fmt, seed=lpr * 10 + vpt + wg + pf)
+        res = si.random_tensor((M, N), act, seed=lpr + vpt + 17 * pf)
+        dh = si.random_tensor((M, N), act, seed=lpr + vpt + 31 * pf, scale=1e-2)
+        residual_check(x, res, w, dy, dh, si.eps_f32(1e-6), act, wst, cfg=cfg)
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_residual_scalar_path(fmt):
+    M, N = 37, 1000
+    act, wst, x, w, dy = _case(M, N, fmt, seed=79)
+    res = si.random_tensor((M, N), act, seed=80)
+    dh = si.random_tensor((M, N), act, seed=81, scale=1e-2)
+    residual_check(x, res, w, dy, dh, si.eps_f32(1e-5), act, wst, cfg=rn.rmsnorm_config(vector_path=0, grid=5))
+
+
+def test_residual_equals_unfused():
+    """The fused pair equals the unfused composition run on the GPU: y and rstd
+    of rmsnorm_fwd(h) bit for bit, and the fused dx equals dh plus the plain
+    backward's dx up to that one extra rounding."""
+    M, N, act = 256, 4096, "bf16"
+    _, _, x, w, dy = _case(M, N, "bf16", seed=82)
+    res = si.random_tensor((M, N), act, seed=83)
+    dh = si.random_tensor((M, N), act, seed=84, scale=1e-2)
+    eps = si.eps_f32(1e-6)
+    # one explicit configuration for both paths: the row-sum order and the
+    # dW partial-row count are then the same
+    cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=256, vecs_per_lane=2, wg_threads=256, prefetch=1,
+                            grid=64)
+    h, y, rstd = gpu_fwd_residual(x, res, w, eps, act, cfg=cfg)
+    y2, rstd2 = gpu_fwd(h, w, eps, act, cfg=cfg)
+    assert np.array_equal(y, y2) and np.array_equal(rstd.view(np.uint32), rstd2.view(np.uint32))
+    dx, dw = gpu_bwd(h, w, dy, rstd, act, cfg=cfg, dh=dh)
+    dx2, dw2 = gpu_bwd(h, w, dy, rstd, act, cfg=cfg)
+    assert np.array_equal(dw.view(np.uint32), dw2.view(np.uint32)), "dh must not change dW"
+    # fused: round(dh + g); unfused: round(dh + round(g)); they differ by at
+    # most one bf16 rounding of the result
+    a, b = widen(dx, act), widen(dh, act) + widen(dx2, act)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 2.0 ** -7 * np.abs(widen(dx2, act)) + 1e-30)
+
+
+def test_residual_null_rstd_and_empty():
+    M, N, act = 5, 512, "bf16"
+    _, _, x, w, _ = _case(M, N, "bf16", seed=85)
+    res = si.random_tensor((M, N), act, seed=86)
+    h = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(h)
+    rn.rmsnorm_fwd_residual(to_device(x), to_device(res), to_device(w), 1e-5, M, N, rn.BF16, h, y, None)
+    torch.cuda.synchronize()
+    oh, oy, _ = oracle.fwd_residual(x, res, w, si.eps_f32(1e-5), act)
+    assert np.array_equal(widen(to_host(h, act), act), oh)
+    check_rows(to_host(y, act), oy, act, "y (no rstd)")
+    e = torch.empty((0, N), dtype=torch.bfloat16, device="cuda")
+    wd = to_device(w)
+    rn.rmsnorm_fwd_residual(e, e, wd, 1e-5, 0, N, rn.BF16, e, e, None)
+    dw = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    rn.rmsnorm_bwd_residual(e, wd, e, e, None, 0, N, rn.BF16, e, dw, None, 0)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+
+
+def test_residual_dw_bit_identical_across_reruns():
+    M, N, act = 2048, 4096, "bf16"
+    _, _, x, w, dy = _case(M, N, "bf16", seed=87)
+    res = si.random_tensor((M, N), act, seed=88)
+    dh = si.random_tensor((M, N), act, seed=89, scale=1e-2)
+    h, _, rstd = gpu_fwd_residual(x, res, w, si.eps_f32(1e-6), act)
+    ref_dx, ref = gpu_bwd(h, w, dy, rstd, act, dh=dh)
+    for i in range(5):
+        _pad = torch.empty(1 + i * 4096, device="cuda")
+        dx, dw = gpu_bwd(h, w, dy, rstd, act, dh=dh)
+        assert np.array_equal(dw.view(np.uint32), ref.view(np.uint32)), f"dW bits differ on rerun {i}"
+        assert np.array_equal(dx, ref_dx), f"dx bits differ on rerun {i}"
+        del _pad
+
+
+def _sample_rows(M, k=32, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(k, M), replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("fmt,M,N", [("bf16", 16384, 4096), ("f16", 16384, 4096), ("bf16w32", 4096, 8192),
+                                     ("f16w32", 8192, 5120), ("bf16", 1048576, 128)],
+                         ids=lambda v: str(v))
+def test_residual_full_size(fmt, M, N):
+    """Full-size residual runs in the default launch configuration: sampled rows
+    of h, y, dx; sampled rstd; every dW column."""
+    _say(f"residual full size {fmt} {M}x{N}: inputs")
+    act, wst, x, w, dy = _case(M, N, fmt, seed=6000 + N)
+    res = si.random_tensor((M, N), act, seed=6001 + N)
+    dh = si.random_tensor((M, N), act, seed=6002 + N, scale=1e-2)
+    _say(f"residual full size {fmt} {M}x{N}: gpu + oracle")
+    residual_check(x, res, w, dy, dh, si.eps_f32(1e-6), act, wst, rows=_sample_rows(M, seed=N))
+
+
+@pytest.mark.parametrize("fmt,M,N", [("f16", 16384, 4096), ("bf16w32", 16384, 4096), ("f16w32", 4096, 32768)],
+                         ids=lambda v: str(v))
+def test_formats_full_size(fmt, M, N):
+    _say(f"format full size {fmt} {M}x{N}")
+    act, wst, x, w, dy = _case(M, N, fmt, seed=7000 + N)
+    eps = si.eps_f32(1e-6)
+    y, rstd = gpu_fwd(x, w, eps, act)
+    dx, dw = gpu_bwd(x, w, dy, rstd, act)
+    rows = _sample_rows(M, seed=N + 1)
+    oy, orr = oracle.fwd(x, w, eps, act, rows=rows, wdtype=wst)
+    check_rows(y[rows], oy, act, "y")
+    check_rstd(rstd[rows], orr)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, act, rows=rows, wdtype=wst)
+    check_rows(dx[rows], odx, act, "dx", floor=term_rms(x, w, dy, orr, act, rows=rows))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act)
