@@ -57,7 +57,11 @@ def parse_args(argv=None):
     ap.add_argument("--isolated-reps", type=int, default=50)
     ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="time budget of the CPU-baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (profiling runs)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "kernels", "copy"],
+    ap.add_argument("--eager-only", action="store_true",
+                    help="per-kernel times from eager batches only, no HIP graphs (counter-collection runs)")
+    ap.add_argument("--cells", default="all", help="cells mode: comma-separated groups (configs, formats, "
+                    "residual, latency, pages) or all")
+    ap.add_argument("--mode", default="bench", choices=["bench", "kernels", "copy", "cells"],
                     help="bench: full run; kernels: only the timed steps (for profilers); "
                          "copy: one probe copy of --probe-gib (counter calibration)")
     ap.add_argument("--out-dir", default=os.environ.get("RMSN_BENCH_OUT", os.path.join(ROOT, "bench_out")))
@@ -217,6 +221,9 @@ def main(argv=None):
         print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes}))
         return 0
 
+    if args.mode == "cells":
+        return run_cells(args, torch, rn, timer)
+
     wl = si.WORKLOADS[args.workload]
     dt = rn.F32 if wl.dtype == "f32" else rn.BF16
     tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
@@ -266,6 +273,7 @@ def main(argv=None):
             "rstd": torch.empty(M, dtype=torch.float32, device="cuda"),
         })
     ws_bytes = rn.rmsnorm_bwd_workspace_bytes(M, N, dt)
+    ldp_floats = -(-N // 64) * 64  # partial-row stride of the workspace
     ws = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device="cuda")
     dw = torch.empty(N, dtype=torch.float32, device="cuda")
     cfg_f = rn.rmsnorm_query_config(M, N, dt, 0).as_dict()
@@ -308,11 +316,14 @@ def main(argv=None):
 
     # ---- timed steps ----------------------------------------------------------
     # K whole steps back to back (the JSON value), then, in the same warm
-    # state, K back-to-back launches of each kernel with the same rotation,
-    # one HIP event pair around each batch: a kernel's average launch duration
-    # is batch time / K. (An event pair around every single launch adds ~2 us
-    # of event processing per launch; the batched average agrees with
-    # rocprofv3's kernel-trace durations.)
+    # state, each kernel's average launch duration: K launches of it with the
+    # same rotation captured in a HIP graph and replayed between one HIP event
+    # pair on the launch stream (replay time / K). Graph replay removes the
+    # host's launch rate (~7 us per launch from Python), which otherwise
+    # bounds any kernel shorter than that; every replay's outputs are compared
+    # bit for bit with the eager launches'. The eager batch (K launches
+    # between one event pair) is reported beside it. (An event pair around
+    # every single launch would add ~2 us of event processing per launch.)
     K, W = args.steps, args.warmup
     parts = [0] * R
 
@@ -343,18 +354,57 @@ def main(argv=None):
         b.synchronize()
         return a.elapsed_time(b) * 1e3 / K
 
+    def graph_batch(fn, outputs, replays=3):
+        """Per-launch us of K launches of fn captured in a HIP graph; outputs()
+        lists the tensors the last launch writes, checked against eager."""
+        for k in range(K):
+            fn(k)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outputs()]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(K):
+                fn(k)
+        times = []
+        for _ in range(replays):
+            for t in outputs():
+                t.fill_(float("nan"))
+            torch.cuda.synchronize()
+            a, b = timer.event(), timer.event()
+            a.record()
+            graph.replay()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / K)
+            for t, r in zip(outputs(), ref):
+                if not torch.equal(t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16),
+                                   r.view(torch.int32) if r.dtype == torch.float32 else r.view(torch.int16)):
+                    raise RuntimeError("graph replay output differs from the eager launches")
+        del graph
+        return statistics.median(times)
+
     def rows_k(k):
         parts[k % R] = bwd_rows(sets[(k + R // 2) % R])
 
-    f_us = batch(lambda k: fwd(sets[k % R]))
-    r_us = batch(rows_k)
-    c_us = batch(lambda k: combine(parts[k % R]))
+    last = (K - 1) % R
+    f_eager = batch(lambda k: fwd(sets[k % R]))
+    r_eager = batch(rows_k)
+    c_eager = batch(lambda k: combine(parts[k % R]))
+    if args.eager_only:
+        f_us, r_us, c_us = f_eager, r_eager, c_eager
+    else:
+        f_us = graph_batch(lambda k: fwd(sets[k % R]), lambda: (sets[last]["y"], sets[last]["rstd"]))
+        r_us = graph_batch(rows_k, lambda: (sets[(last + R // 2) % R]["dx"],
+                                            ws[:parts[last] * ldp_floats].view(parts[last], ldp_floats)[:, :N]))
+        c_us = graph_batch(lambda k: combine(parts[k % R]), lambda: (dw,))
     log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step wall ({step_event_ms * 1e3:.1f} us by events); "
-        f"per launch: fwd {f_us:.1f} us, bwd rows {r_us:.1f} us, combine {c_us:.1f} us")
+        f"per launch (graph / eager): fwd {f_us:.1f} / {f_eager:.1f} us, bwd rows {r_us:.1f} / {r_eager:.1f} us, "
+        f"combine {c_us:.1f} / {c_eager:.1f} us")
+    eager = {"fwd_us": round(f_eager, 2), "bwd_rows_us": round(r_eager, 2), "combine_us": round(c_eager, 2)}
 
     if args.mode == "kernels":
         print(json.dumps({"mode": "kernels", "steps": K, "ms_per_step": ms_per_step, "fwd_us": f_us,
-                          "bwd_rows_us": r_us, "combine_us": c_us}))
+                          "bwd_rows_us": r_us, "combine_us": c_us, "eager": eager}))
         return 0
 
     # ---- isolated calls with a cache flush before each ------------------------
@@ -424,8 +474,11 @@ def main(argv=None):
                 "algorithmic_bytes": bwd_bytes, "isolated_median_us": round(iso_b * 1e3, 2),
                 "isolated_GBps": round(bwd_bytes / (iso_b * 1e-3) / 1e9, 1)},
         "step_event_us": round(step_event_ms * 1e3, 2),
-        "timing": "value: wall clock over K whole steps (synchronised at both ends); per-kernel avg_us: "
-                  "K back-to-back rotated launches of that kernel between one HIP event pair",
+        "timing": "value: wall clock over K whole eager steps (synchronised at both ends); per-kernel avg_us: "
+                  "K rotated launches of that kernel captured in a HIP graph, replayed between one HIP event "
+                  "pair on the launch stream (outputs checked against eager); eager_batch_us: the same K "
+                  "launches issued eagerly between one event pair",
+        "eager_batch_us": eager,
         "pct_measured_roofline": round(100 * value / measured, 1),
         "validation": validation,
         "cpu_baseline": cpu_baseline,
@@ -440,6 +493,203 @@ def main(argv=None):
         json.dump(result, f, indent=1)
     print(json.dumps(result))
     return 0
+
+
+# ---- the measurement cells ---------------------------------------------------
+# Each cell is one shape and format, timed for one or more variants of the
+# forward and the backward call:
+#   fused     rmsnorm_fwd / rmsnorm_bwd (the library's path)
+#   unfused   rmsn_unfused_fwd / rmsn_unfused_bwd (one kernel per step: the
+#             row crosses HBM once per kernel)
+#   residual  rmsnorm_fwd_residual / rmsnorm_bwd_residual (fused residual add)
+#   residual_unfused  rmsn_add then rmsnorm_fwd; rmsnorm_bwd then rmsn_add
+# GB/s is always the operation's algorithmic bytes over the call time, so a
+# variant that moves more bytes shows up as a lower rate for the same work.
+# Groups: the synthetic configurations; other storage formats ("What a tuned
+# RMSNorm kernel actually costs on Hopper", section 07); the fused residual
+# add ("Profiling, GPU utilisation and writing a fused kernel", Problem 15);
+# the latency regime at d = 4096 (same page, the benchmark of Problem 15);
+# the shapes the other pages test (hello-gpu ch. 13 section 13.4 and 13.5;
+# "RMSNorm backward (almost) without the column reduction", its benchmark).
+CELL_GROUPS = {
+    "configs": [("fp32_256x1024", "f32", 256, 1024), ("bf16_16384x4096", "bf16", 16384, 4096),
+                ("bf16_32768x8192", "bf16", 32768, 8192), ("bf16_qknorm_1048576x128", "bf16", 1048576, 128),
+                ("bf16_4096x32768", "bf16", 4096, 32768), ("bf16_16384x5120", "bf16", 16384, 5120),
+                ("bf16_16384x7168", "bf16", 16384, 7168)],
+    "formats": [("f16_16384x4096", "f16", 16384, 4096), ("bf16w32_16384x4096", "bf16w32", 16384, 4096),
+                ("f16w32_16384x4096", "f16w32", 16384, 4096), ("bf16w32_32768x8192", "bf16w32", 32768, 8192),
+                ("fp32_16384x4096", "f32", 16384, 4096), ("fp32_4096x32768", "f32", 4096, 32768)],
+    "residual": [("bf16_16384x4096", "bf16", 16384, 4096), ("bf16_32768x8192", "bf16", 32768, 8192),
+                 ("f16w32_16384x4096", "f16w32", 16384, 4096), ("bf16_1024x4096", "bf16", 1024, 4096)],
+    "latency": [(f"bf16_{m}x4096", "bf16", m, 4096) for m in (1, 16, 256, 4096, 32768)],
+    "pages": [("fp32_3x13", "f32", 3, 13), ("fp32_33x257", "f32", 33, 257), ("fp32_1024x4096", "f32", 1024, 4096),
+              ("bf16_16384x8192", "bf16", 16384, 8192)],
+}
+CELL_VARIANTS = {"configs": ("fused", "unfused"), "formats": ("fused",), "residual": ("residual", "residual_unfused"),
+                 "latency": ("fused", "unfused"), "pages": ("fused", "unfused")}
+FMT = {"f32": ("f32", 4, 4), "bf16": ("bf16", 2, 2), "f16": ("f16", 2, 2), "bf16w32": ("bf16", 2, 4),
+       "f16w32": ("f16", 2, 4)}  # activation storage, activation bytes, weight bytes
+
+
+def cell_bytes(variant, M, N, es, wsz):
+    """Algorithmic bytes of one forward and one backward call of the operation."""
+    if variant.startswith("residual"):
+        # fwd: read x, res, w; write h, y, rstd. bwd: read h, dy, dh, w, rstd; write dx, dW
+        return 4 * M * N * es + N * wsz + 4 * M, 4 * M * N * es + N * wsz + 4 * M + 4 * N
+    return 2 * M * N * es + N * wsz + 4 * M, 3 * M * N * es + N * wsz + 4 * M + 4 * N
+
+
+def run_cells(args, torch, rn, timer):
+    """Time every cell's variants as K calls captured in a HIP graph and
+    replayed (the per-call time without host launch gaps), and as K eager
+    launches between two events. Every graph replay's outputs are compared with
+    the eager call's, bit for bit."""
+    import numpy as np
+
+    groups = list(CELL_GROUPS) if args.cells == "all" else args.cells.split(",")
+    roof = probe_roofline(torch, rn, timer, args.probe_gib)
+    measured = roof["best_GBps"]
+    log(f"roofline {measured} GB/s ({roof['best_probe']})")
+    codes = {"f32": rn.F32, "bf16": rn.BF16, "f16": rn.F16, "bf16w32": rn.BF16_WF32, "f16w32": rn.F16_WF32}
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    rows = []
+    for group in groups:
+        for name, fmt, M, N in CELL_GROUPS[group]:
+            act, es, wsz = FMT[fmt]
+            code = codes[fmt]
+            eps = float(np.float32(1e-6))
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(M * 7919 + N)
+            variants = CELL_VARIANTS[group]
+            resid = any(v.startswith("residual") for v in variants)
+            per_set = M * N * es * (7 if resid else 4) + 4 * M
+            R = max(2, min(64, -(-int(1.5 * GIB) // per_set)))
+
+            def randn(scale=1.0):
+                return (torch.randn((M, N), generator=gen, device="cuda") * scale).to(tdt[act])
+
+            base = {"x": randn(), "dy": randn(1e-2)}
+            if resid:
+                base["res"] = randn()
+                base["dh"] = randn(1e-2)
+            w = (1.0 + 0.1 * torch.randn(N, generator=gen, device="cuda")).to(torch.float32 if wsz == 4 else tdt[act])
+            sets = []
+            for k in range(R):
+                s = {key: (v if k == 0 else v.clone()) for key, v in base.items()}
+                for key in ("y", "dx") + (("h",) if resid else ()):
+                    s[key] = torch.empty((M, N), dtype=tdt[act], device="cuda")
+                s["rstd"] = torch.empty(M, dtype=torch.float32, device="cuda")
+                sets.append(s)
+            ws_n = max(rn.rmsnorm_bwd_workspace_bytes(M, N, code),
+                       rn.rmsn_unfused_bwd_workspace_bytes(M, N, code) if (N * es) % 16 == 0 else 0, 256)
+            ws = torch.empty(ws_n // 4, dtype=torch.float32, device="cuda")
+            dw = torch.empty(N, dtype=torch.float32, device="cuda")
+            fb, bb = None, None
+            for variant in variants:
+                if variant.startswith("unfused") and (N * es) % 16 != 0:
+                    continue  # the unfused kernels take the vector layout only
+                fb, bb = cell_bytes(variant, M, N, es, wsz)
+                ops = cell_ops(rn, variant, sets, w, dw, ws, ws_n, eps, M, N, code)
+                # every set's rstd (and h) for the backward
+                for k in range(R):
+                    ops["fwd"](k)
+                torch.cuda.synchronize()
+                rec = {"group": group, "cell": name, "format": fmt, "M": M, "N": N, "variant": variant,
+                       "rotation_sets": R}
+                for which, nbytes in (("fwd", fb), ("bwd", bb)):
+                    g_us, e_us = time_cell(torch, timer, ops[which], ops["outputs_" + which], R)
+                    best = min(g_us, e_us)
+                    rec[which + "_graph_us"] = round(g_us, 2)
+                    rec[which + "_eager_us"] = round(e_us, 2)
+                    rec[which + "_GBps"] = round(nbytes / (best * 1e-6) / 1e9, 1)
+                    rec[which + "_pct_roofline"] = round(100 * nbytes / (best * 1e-6) / 1e9 / measured, 1)
+                    rec[which + "_bytes"] = nbytes
+                rows.append(rec)
+                log(json.dumps(rec))
+            del sets, base, ws, dw
+            torch.cuda.empty_cache()
+    out = {"mode": "cells", "roofline": roof, "cells": rows}
+    os.makedirs(args.out_dir, exist_ok=True)
+    with open(os.path.join(args.out_dir, "cells.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
+def cell_ops(rn, variant, sets, w, dw, ws, ws_n, eps, M, N, code):
+    """Forward and backward calls of a variant on rotation set k, and the
+    outputs each writes (for the replay check)."""
+    if variant == "fused":
+        return {
+            "fwd": lambda k: rn.rmsnorm_fwd(sets[k]["x"], w, eps, M, N, code, sets[k]["y"], sets[k]["rstd"]),
+            "bwd": lambda k: rn.rmsnorm_bwd(sets[k]["x"], w, sets[k]["dy"], sets[k]["rstd"], M, N, code,
+                                            sets[k]["dx"], dw, ws, ws_n),
+            "outputs_fwd": lambda k: (sets[k]["y"], sets[k]["rstd"]), "outputs_bwd": lambda k: (sets[k]["dx"], dw)}
+    if variant == "unfused":
+        return {
+            "fwd": lambda k: rn.rmsn_unfused_fwd(sets[k]["x"], w, eps, M, N, code, sets[k]["y"], sets[k]["rstd"]),
+            "bwd": lambda k: rn.rmsn_unfused_bwd(sets[k]["x"], w, sets[k]["dy"], sets[k]["rstd"], M, N, code,
+                                                 sets[k]["dx"], dw, ws, ws_n),
+            "outputs_fwd": lambda k: (sets[k]["y"], sets[k]["rstd"]), "outputs_bwd": lambda k: (sets[k]["dx"], dw)}
+    if variant == "residual":
+        return {
+            "fwd": lambda k: rn.rmsnorm_fwd_residual(sets[k]["x"], sets[k]["res"], w, eps, M, N, code, sets[k]["h"],
+                                                     sets[k]["y"], sets[k]["rstd"]),
+            "bwd": lambda k: rn.rmsnorm_bwd_residual(sets[k]["h"], w, sets[k]["dy"], sets[k]["dh"], sets[k]["rstd"],
+                                                     M, N, code, sets[k]["dx"], dw, ws, ws_n),
+            "outputs_fwd": lambda k: (sets[k]["h"], sets[k]["y"], sets[k]["rstd"]),
+            "outputs_bwd": lambda k: (sets[k]["dx"], dw)}
+    if variant == "residual_unfused":
+        def fwd(k):
+            s = sets[k]
+            rn.rmsn_add(s["x"], s["res"], s["h"], M * N, code)
+            rn.rmsnorm_fwd(s["h"], w, eps, M, N, code, s["y"], s["rstd"])
+
+        def bwd(k):
+            s = sets[k]
+            rn.rmsnorm_bwd(s["h"], w, s["dy"], s["rstd"], M, N, code, s["dx"], dw, ws, ws_n)
+            rn.rmsn_add(s["dx"], s["dh"], s["dx"], M * N, code)
+        return {"fwd": fwd, "bwd": bwd, "outputs_fwd": lambda k: (sets[k]["h"], sets[k]["y"], sets[k]["rstd"]),
+                "outputs_bwd": lambda k: (sets[k]["dx"], dw)}
+    raise ValueError(variant)
+
+
+def time_cell(torch, timer, op, outputs, R, replays=5):
+    """(graph per-call us, eager per-call us) for op over the rotation sets."""
+    K = R * max(1, -(-16 // R))
+    # eager reference of the last call, then K eager launches between events
+    for k in range(K):
+        op(k % R)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs((K - 1) % R)]
+    e0, e1 = timer.event(), timer.event()
+    e0.record()
+    for k in range(K):
+        op(k % R)
+    e1.record()
+    e1.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / K
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(K):
+            op(k % R)
+    times = []
+    for _ in range(replays):
+        for t in outputs((K - 1) % R):
+            t.fill_(float("nan"))  # a replay must rewrite every output
+        torch.cuda.synchronize()
+        a, b = timer.event(), timer.event()
+        a.record()
+        graph.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3 / K)
+        for t, r in zip(outputs((K - 1) % R), ref):
+            if not torch.equal(t.view(torch.uint8) if t.dtype != torch.float32 else t.view(torch.int32),
+                               r.view(torch.uint8) if r.dtype != torch.float32 else r.view(torch.int32)):
+                raise RuntimeError("graph replay output differs from the eager call")
+    del graph
+    return statistics.median(times), eager_us
 
 
 def load_traffic(src_hash, kernel, workload):

@@ -1,8 +1,9 @@
 """Python binding of the gfx950 RMSNorm library (``librmsnorm_mi355x.so``).
 
 Argument marshalling only: every function forwards to the C entry point of
-the same name declared in ``include/rmsnorm.h`` (and ``include/rmsnorm_probe.h``
-for the roofline probes). Pointers may be given as integers (device
+the same name declared in ``include/rmsnorm.h`` (``include/rmsnorm_probe.h``
+for the roofline probes, ``include/rmsnorm_baseline.h`` for the unfused
+reference kernels). Pointers may be given as integers (device
 addresses) or as torch tensors (their ``data_ptr()``); ``stream`` may be an
 integer hipStream_t, a ``torch.cuda.Stream``, or None for torch's current
 stream. A non-zero status raises ``RmsnormError``.
@@ -88,6 +89,10 @@ def _load() -> ctypes.CDLL:
         "rmsn_probe_write": (i32, [vp, sz, i64, i32, vp]),
         "rmsn_probe_read": (i32, [vp, sz, i64, i32, vp, vp]),
         "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, i32, vp]),
+        "rmsn_unfused_fwd": (i32, [vp, vp, f32, i64, i64, i32, vp, vp, vp]),
+        "rmsn_unfused_bwd_workspace_bytes": (i64, [i64, i64, i32]),
+        "rmsn_unfused_bwd": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]),
+        "rmsn_add": (i32, [vp, vp, vp, i64, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -104,6 +109,7 @@ EXPORTED = (
     "rmsnorm_bwd_residual", "rmsnorm_status_str",
     "rmsnorm_select_config", "rmsnorm_query_config", "rmsnorm_build_info",
     "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_read", "rmsn_probe_add",
+    "rmsn_unfused_fwd", "rmsn_unfused_bwd_workspace_bytes", "rmsn_unfused_bwd", "rmsn_add",
 )
 
 
@@ -241,3 +247,25 @@ def rmsn_probe_read(src, nbytes, sink, grid=0, variant=0, stream=None) -> None:
 def rmsn_probe_add(a, b, c, nbytes, grid=0, variant=0, stream=None) -> None:
     _check("rmsn_probe_add", lib.rmsn_probe_add(_ptr(a), _ptr(b), _ptr(c), int(nbytes), int(grid), int(variant),
                                                 _stream(stream)))
+
+
+def rmsn_unfused_fwd(x, w, eps, M, N, dtype, y, rstd, stream=None) -> None:
+    _check("rmsn_unfused_fwd", lib.rmsn_unfused_fwd(_ptr(x), _ptr(w), float(eps), int(M), int(N), int(dtype),
+                                                    _ptr(y), _ptr(rstd), _stream(stream)))
+
+
+def rmsn_unfused_bwd_workspace_bytes(M, N, dtype) -> int:
+    n = int(lib.rmsn_unfused_bwd_workspace_bytes(int(M), int(N), int(dtype)))
+    if n < 0:
+        raise RmsnormError("rmsn_unfused_bwd_workspace_bytes", n, rmsnorm_status_str(n))
+    return n
+
+
+def rmsn_unfused_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream=None) -> None:
+    _check("rmsn_unfused_bwd", lib.rmsn_unfused_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N),
+                                                    int(dtype), _ptr(dx), _ptr(dw), _ptr(workspace),
+                                                    int(workspace_bytes), _stream(stream)))
+
+
+def rmsn_add(a, b, c, n, dtype, stream=None) -> None:
+    _check("rmsn_add", lib.rmsn_add(_ptr(a), _ptr(b), _ptr(c), int(n), int(dtype), _stream(stream)))

@@ -57,15 +57,23 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     one row block per workgroup (grid = row blocks), so the hardware
 //     dispatcher balances the tail.
 //   Backward: one vector per lane up to 1024 lanes per row (more lanes, fewer
-//     registers, more rows in flight), then up to 4 vectors per lane; a
-//     persistent grid of about two workgroups per compute unit (three for
-//     rows of under a wavefront), fewer when the fp32 dW partial rows would
-//     exceed ~5% of the algorithmic bytes, never fewer than one per compute
-//     unit; the next row block is prefetched when the workgroup has at most
-//     512 lanes (enough registers for the second buffer).
+//     registers, more rows in flight); a persistent grid of about two
+//     workgroups per compute unit (three for rows of under a wavefront),
+//     fewer when the fp32 dW partial rows would exceed ~5% of the algorithmic
+//     bytes, never fewer than one per compute unit; the next row block is
+//     prefetched when the workgroup has at most 512 lanes (enough registers
+//     for the second buffer). Rows of more than 1024 vectors: 16-bit
+//     activations take the wide-row kernel (dW sums in LDS, 2 to 4 vectors
+//     per lane, prefetching when the weights are 16-bit too: 5-16% faster
+//     than keeping the sums in registers at 16384 to 32768 columns); fp32
+//     rows keep the register kernel up to 4 vectors per lane (as fast) and
+//     take the wide kernel from 5 to 8 (the register kernel spills there). One
+//     wide workgroup per compute unit (its LDS allows no more at 4 vectors).
 //   Anything the vector kernels cannot take (N*elem not a multiple of 16
-//     bytes, unaligned pointers, more than 1024 * 8 vectors forward or
-//     1024 * 4 backward) goes to the scalar kernel.
+//     bytes, unaligned pointers, more than 1024 * 8 vectors forward, or
+//     backward more than 1024 * 4 16-bit or 1024 * 8 fp32 vectors) goes to
+//     the scalar kernel.
+constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
 constexpr int kFwdMaxVecs = 4;
 constexpr int kBwdMaxVecs = 4;
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
@@ -90,11 +98,22 @@ void set_scalar_shape(rmsnorm_config *c) {
 
 bool vector_ok(int64_t N, int dtype, bool aligned) { return aligned && (N * elem_size(dtype)) % 16 == 0; }
 
+// Largest vectors per lane of the wide-row backward kernels: their dW sums
+// (vectors x 1024 lanes x elements per vector, fp32) fill at most 128 KiB.
+int64_t wide_max_vecs(int dtype) { return dtype == RMSN_F32 ? 8 : 4; }
+
 void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config *c) {
     const int64_t nvec = N * elem_size(dtype) / 16;
-    const int64_t vmax = is_bwd ? kBwdMaxVecs : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
+    const int64_t vmax = is_bwd ? wide_max_vecs(dtype) : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
     if (!vector_ok(N, dtype, aligned) || nvec > kMaxVecLanes * vmax) {
         set_scalar_shape(c);
+        return;
+    }
+    if (is_bwd && nvec > kMaxVecLanes && (dtype != RMSN_F32 || nvec > kMaxVecLanes * kBwdMaxVecs)) {
+        const int64_t vpt = (nvec + kMaxVecLanes - 1) / kMaxVecLanes;
+        const int pf = (dtype == RMSN_BF16 || dtype == RMSN_F16) ? 1 : 0;
+        set_vector_shape(kMaxVecLanes, vpt, rmsn::kWideLanes, pf, c);
+        c->vector_path = kWidePath;
         return;
     }
     int64_t lpr, vpt;
@@ -122,7 +141,7 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int num_cus, int b
         grid = row_blocks < kMaxGrid ? row_blocks : kMaxGrid;
     } else {
         const int64_t cus = num_cus > 0 ? num_cus : 1;
-        int64_t want = (c->lanes_per_row < 64 ? 3 : 2) * cus;
+        int64_t want = (c->vector_path == kWidePath ? 1 : c->lanes_per_row < 64 ? 3 : 2) * cus;
         // partial rows are written once and read once: 8 * N bytes each
         const int64_t bytes = 3 * M * N * elem_size(dtype);
         const int64_t cap = bytes / 20 / (8 * N);
@@ -183,6 +202,10 @@ int occupancy(const void *fn, int wg, int *blocks) {
 
 const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd, int res) {
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res);
+    if (c.vector_path == kWidePath) {
+        const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
+        return e ? e->fn : nullptr;
+    }
     const KernelEntry *e =
         is_bwd ? rmsn::bwd_vec_kernel(dtype, res, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch)
                : rmsn::fwd_vec_kernel(dtype, res, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch);
@@ -225,6 +248,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
                     bool aligned, rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
+    if (req->vector_path < 0 || req->vector_path > kWidePath) return RMSN_ECONFIG;
     if (req->vector_path) {
         const int64_t nvec = N * elem_size(dtype) / 16;
         if (!vector_ok(N, dtype, aligned)) return RMSN_ECONFIG;
@@ -232,7 +256,11 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > 1)
             return RMSN_ECONFIG;
         if (req->wg_threads > 0 && (req->wg_threads % req->lanes_per_row) != 0) return RMSN_ECONFIG;
+        if (req->vector_path == kWidePath &&
+            (req->lanes_per_row != rmsn::kWideLanes || (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes)))
+            return RMSN_ECONFIG;
         set_vector_shape(req->lanes_per_row, req->vecs_per_lane, req->wg_threads, req->prefetch, c);
+        c->vector_path = req->vector_path;
     } else {
         set_scalar_shape(c);
     }

@@ -1,6 +1,7 @@
 // rmsn_bwd_f32.hip -- backward vector kernels for fp32 activations and weights:
 // the plain kernels on RMSN_ALL_SHAPES and the residual-fused ones on
-// RMSN_LADDER_SHAPES (rmsn_instances.h), and the lookup the host dispatch uses.
+// RMSN_LADDER_SHAPES, the wide-row kernels on RMSN_WIDE_SHAPES_32 (rmsn_instances.h),
+// and the lookups the host dispatch uses.
 #include "rmsn_bwd_kernels.h"
 #include "rmsn_instances.h"
 
@@ -13,8 +14,18 @@ static const KernelEntry kPlain[] = {RMSN_ALL_SHAPES(RMSN_ENTRY)};
 static const KernelEntry kResidual[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY)};
 #undef RMSN_ENTRY
 
+#define RMSN_WIDE_ENTRY(V, P) {kWideLanes, V, kWideLanes, P, reinterpret_cast<const void *>(&bwd_wide<float, float, false, V, (P != 0)>)},
+static const KernelEntry kWide[] = {RMSN_WIDE_SHAPES_32(RMSN_WIDE_ENTRY)};
+#undef RMSN_WIDE_ENTRY
+#define RMSN_WIDE_ENTRY(V, P) {kWideLanes, V, kWideLanes, P, reinterpret_cast<const void *>(&bwd_wide<float, float, true, V, (P != 0)>)},
+static const KernelEntry kWideResidual[] = {RMSN_WIDE_SHAPES_32(RMSN_WIDE_ENTRY)};
+#undef RMSN_WIDE_ENTRY
+
 const KernelEntry *bwd_vec_kernel_f32(int res, int lpr, int vpt, int wg, int pf) {
     return res ? find_entry(kResidual, lpr, vpt, wg, pf) : find_entry(kPlain, lpr, vpt, wg, pf);
 }
 
+const KernelEntry *bwd_wide_kernel_f32(int res, int vpt, int pf) {
+    return find_entry(res ? kWideResidual : kWide, kWideLanes, vpt, kWideLanes, pf);
+}
 }  // namespace rmsn

@@ -40,7 +40,7 @@ constexpr int bwd_packed_per_slot() {
 template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, bool PF>
 __global__ void __launch_bounds__(WG)
 __attribute__((amdgpu_waves_per_eu(waves_for(VPT * bwd_packed_per_slot<T, TW, RES, PF>(),
-                                             VPT * Elem<T>::kPerVec, VPT, WG))))
+                                             VPT * Elem<T>::kPerVec, VPT, WG, RES ? 2 * Elem<T>::kPerVec : 0))))
 bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
         const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
         int32_t N, int32_t nvec) {
@@ -198,6 +198,156 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
                 }
             }
             __syncthreads();
+        }
+    }
+}
+
+// Wide rows (more than 1024 16-byte vectors): 1024 lanes per row, VPT vectors
+// per lane, and each lane's running dW sums kept in LDS instead of registers.
+// The sums are per lane (a lane touches only its own slots, laid out so the
+// lanes of a wavefront hit consecutive 16-byte words), so they need no
+// barrier; moving them out of the register file leaves room for the
+// prefetched next row, or, for fp32 rows of up to 32768, for eight vectors
+// per lane. Weights stay in registers when they take at most 4 vectors per
+// lane counting the prefetch buffers' share, and are re-read (from cache) at
+// each use otherwise. With RES the residual gradient dh is loaded in the
+// second pass, one vector at a time, where it is needed.
+template <typename T, typename TW, int VPT, bool PF>
+constexpr bool wide_keeps_w() {
+    return VPT * WeightVec<T, TW>::kVecs * (PF ? 2 : 1) <= 4;
+}
+
+template <typename T, typename TW, bool RES, int VPT, bool PF>
+__global__ void __launch_bounds__(kWideLanes) __attribute__((amdgpu_waves_per_eu(kWideLanes / 256)))
+bwd_wide(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
+         const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
+         int32_t N, int32_t nvec) {
+    using E = Elem<T>;
+    using WV = WeightVec<T, TW>;
+    constexpr int LPR = kWideLanes;
+    constexpr int EPV = E::kPerVec;
+    constexpr int Q = EPV / 4;  // float4 words of dW sums per vector
+    constexpr bool kKeepW = wide_keeps_w<T, TW, VPT, PF>();
+    static_assert(VPT * EPV * LPR * 4 <= kWideLdsBytes, "dW sums must fit in LDS");
+    __shared__ float slots[2 * (LPR / 64)];
+    __shared__ float4 acc[VPT * Q * LPR];
+
+    const int lane = threadIdx.x;
+    const float n = (float)N;
+    const uint32_t row_bytes = (uint32_t)nvec * 16u;
+    const Buf wb(w, row_bytes * WV::kVecs);
+
+    uint32_t off[VPT];
+    WV wv[kKeepW ? VPT : 1];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int idx = v * LPR + lane;
+        off[v] = idx < nvec ? (uint32_t)idx * 16u : kOff;
+        if constexpr (kKeepW) wv[v].load(wb, idx, idx < nvec);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) acc[(v * Q + q) * LPR + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // weights of vector slot v: the kept registers, or a (cached) reload
+    auto weights = [&](int v, float (&fw)[EPV]) {
+        if constexpr (kKeepW) {
+            wv[v].unpack(fw);
+        } else {
+            WV t;
+            t.load(wb, v * LPR + lane, off[v] != kOff);
+            t.unpack(fw);
+        }
+    };
+    auto load_block = [&](int64_t b, u32x4 (&xo)[VPT], u32x4 (&go)[VPT], float &ro) {
+        const int64_t bb = b < M ? b : 0;
+        const uint32_t bytes = b < M ? row_bytes : 0u;
+        const Buf xb(x + bb * N, bytes), gb(dy + bb * N, bytes), rb(rstd + bb, b < M ? 4u : 0u);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            xo[v] = xb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+            go[v] = gb.load16<RMSN_BWD_LOAD_AUX>(off[v]);
+        }
+        ro = rb.load4(0u);
+    };
+
+    int parity = 0;
+    const int64_t step = (int64_t)gridDim.x;
+    int64_t row = (int64_t)blockIdx.x;
+    u32x4 xn[VPT], gn[VPT];
+    float rn = 0.f;
+    if constexpr (PF) load_block(row, xn, gn, rn);
+    for (; row < M; row += step) {
+        if constexpr (kKeepW) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) wv[v].keep();
+        }
+        u32x4 xv[VPT], gv[VPT];
+        float r;
+        if constexpr (PF) {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                xv[v] = xn[v];
+                gv[v] = gn[v];
+            }
+            r = rn;
+            load_block(row + step, xn, gn, rn);
+        } else {
+            load_block(row, xv, gv, r);
+        }
+
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float fx[EPV], fg[EPV], fw[EPV];
+            E::unpack(xv[v], fx);
+            E::unpack(gv[v], fg);
+            weights(v, fw);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) s = __builtin_fmaf(fg[k] * fw[k], fx[k], s);
+        }
+        s = row_sum<LPR, LPR>(s, slots, parity);
+        parity ^= 1;
+        const float c = r * (r * (r * (s / n)));
+        const Buf db(dx + row * N, row_bytes);
+        const Buf hb(RES ? dh + row * N : dx, RES ? row_bytes : 0u);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            keep_packed(xv[v]);
+            keep_packed(gv[v]);
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float fx[EPV], fg[EPV], fw[EPV], o[EPV];
+            E::unpack(xv[v], fx);
+            E::unpack(gv[v], fg);
+            weights(v, fw);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) o[k] = __builtin_fmaf(-fx[k], c, r * (fg[k] * fw[k]));
+            if constexpr (RES) {
+                float fh[EPV];
+                E::unpack(hb.load16<RMSN_BWD_LOAD_AUX>(off[v]), fh);
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) o[k] += fh[k];
+            }
+            db.store16<RMSN_BWD_STORE_AUX>(off[v], E::pack(o));
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                float4 &a = acc[(v * Q + q) * LPR + lane];
+                a.x = __builtin_fmaf(fg[4 * q] * fx[4 * q], r, a.x);
+                a.y = __builtin_fmaf(fg[4 * q + 1] * fx[4 * q + 1], r, a.y);
+                a.z = __builtin_fmaf(fg[4 * q + 2] * fx[4 * q + 2], r, a.z);
+                a.w = __builtin_fmaf(fg[4 * q + 3] * fx[4 * q + 3], r, a.w);
+            }
+        }
+    }
+
+    float *prow = partial + (int64_t)blockIdx.x * ldp;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int idx = v * LPR + lane;
+        if (idx < nvec) {
+            float4 *dst = reinterpret_cast<float4 *>(prow + (int64_t)idx * EPV);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) dst[q] = acc[(v * Q + q) * LPR + lane];
         }
     }
 }

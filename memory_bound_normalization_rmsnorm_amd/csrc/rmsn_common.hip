@@ -12,6 +12,9 @@ namespace rmsn {
 // XCDs, fetch the same line). Lane (slice s, quad c) sums rows p = s, s + S,
 // s + 2S, ... (S = kCombineSlices = 64) in ascending order for columns
 // 4c..4c+3; the S slice sums are then folded by a fixed binary tree in LDS.
+// A lane issues the loads of kCombineUnroll of its rows before adding them
+// (still in ascending order), so the partial rows stream in with that many
+// loads in flight per lane instead of one memory latency per row.
 // Rows are padded to ldp floats (a multiple of 64) and 256-byte aligned, so
 // the float4 loads stay inside the workspace.
 __global__ void __launch_bounds__(kCombineWG)
@@ -23,7 +26,22 @@ dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
     const int64_t col = (int64_t)blockIdx.x * kCombineCols + 4 * quad;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     if (col < N) {
-        for (int64_t p = slice; p < P; p += kCombineSlices) {
+        constexpr int U = kCombineUnroll;
+        constexpr int S = kCombineSlices;
+        int64_t p = slice;
+        for (; p + (U - 1) * S < P; p += U * S) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float4 *>(partial + (p + u * S) * ldp + col);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                a.x += v[u].x;
+                a.y += v[u].y;
+                a.z += v[u].z;
+                a.w += v[u].w;
+            }
+        }
+        for (; p < P; p += S) {
             const float4 v = *reinterpret_cast<const float4 *>(partial + p * ldp + col);
             a.x += v.x;
             a.y += v.y;
@@ -62,7 +80,8 @@ __global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t 
 #define RMSN_FORMATS(X) X(f32) X(bf16) X(f16) X(bf16w32) X(f16w32)
 #define RMSN_DECL(tag)                                                                 \
     const KernelEntry *fwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf); \
-    const KernelEntry *bwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf);
+    const KernelEntry *bwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf); \
+    const KernelEntry *bwd_wide_kernel_##tag(int res, int vpt, int pf);
 RMSN_FORMATS(RMSN_DECL)
 #undef RMSN_DECL
 
@@ -86,6 +105,17 @@ const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, 
     case 2: return bwd_vec_kernel_f16(res, lpr, vpt, wg, pf);
     case 3: return bwd_vec_kernel_bf16w32(res, lpr, vpt, wg, pf);
     case 4: return bwd_vec_kernel_f16w32(res, lpr, vpt, wg, pf);
+    default: return nullptr;
+    }
+}
+
+const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf) {
+    switch (dtype) {
+    case 0: return bwd_wide_kernel_f32(res, vpt, pf);
+    case 1: return bwd_wide_kernel_bf16(res, vpt, pf);
+    case 2: return bwd_wide_kernel_f16(res, vpt, pf);
+    case 3: return bwd_wide_kernel_bf16w32(res, vpt, pf);
+    case 4: return bwd_wide_kernel_f16w32(res, vpt, pf);
     default: return nullptr;
     }
 }

@@ -46,7 +46,8 @@ constexpr int fwd_packed_per_slot() {
 
 template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, bool PF>
 __global__ void __launch_bounds__(WG)
-__attribute__((amdgpu_waves_per_eu(waves_for(VPT * fwd_packed_per_slot<T, TW, RES, PF>(), 0, VPT, WG))))
+__attribute__((amdgpu_waves_per_eu(waves_for(VPT * fwd_packed_per_slot<T, TW, RES, PF>(), 0, VPT, WG,
+                                             (RES || WeightVec<T, TW>::kVecs > 1) ? Elem<T>::kPerVec : 0))))
 fwd_vec(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict__ w, T *__restrict__ h,
         T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t nvec) {
     using E = Elem<T>;

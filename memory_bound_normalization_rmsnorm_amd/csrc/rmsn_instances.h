@@ -34,6 +34,14 @@
     RMSN_PF(RMSN_V8, X, 64, 256) RMSN_PF(RMSN_V8, X, 128, 256) RMSN_PF(RMSN_V8, X, 256, 256)  \
     RMSN_PF(RMSN_V8, X, 512, 512) RMSN_PF(RMSN_V8, X, 1024, 1024)
 
+// Wide-row backward kernels (1024 lanes, dW sums in LDS), as (vectors per
+// lane, prefetch): at most 128 KiB of sums, i.e. 4 vectors of 8 16-bit
+// elements or 8 vectors of 4 fp32 elements per lane. fp32 rows of 6 or more
+// vectors per lane have no prefetching variant (it does not fit in 128 VGPRs).
+#define RMSN_WIDE_SHAPES_16(X) X(2, 0) X(2, 1) X(3, 0) X(3, 1) X(4, 0) X(4, 1)
+#define RMSN_WIDE_SHAPES_32(X) X(2, 0) X(2, 1) X(3, 0) X(3, 1) X(4, 0) X(4, 1) X(5, 0) X(5, 1) \
+    X(6, 0) X(7, 0) X(8, 0)
+
 namespace rmsn {
 
 template <int N>

@@ -11,6 +11,7 @@ constexpr int kCombineWG = 512;
 constexpr int kCombineCols = 32;     // dW columns per combine workgroup: one 128-byte line per partial row
 constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
 constexpr int kCombineSlices = kCombineWG / kCombineLanes;  // partial rows summed side by side
+constexpr int kCombineUnroll = 8;    // partial-row loads a combine lane has in flight
 constexpr int kPartialAlign = 64;    // partial rows are padded to a multiple of 64 floats
 
 // Workgroup size for a row group of `lpr` lanes: at least four wavefronts.
@@ -19,17 +20,23 @@ constexpr int wg_for_lpr(int lpr) { return lpr > 256 ? lpr : 256; }
 // Waves per SIMD the compiler is asked to fit (512 VGPRs per SIMD lane), from
 // the registers a lane needs with rows and weights kept packed: `packed`
 // 16-byte vectors (4 VGPRs each), `floats` fp32 accumulators, one offset per
-// vector and ~24 temporaries. The scheduler then trades ILP for occupancy
-// instead of unpacking every operand ahead of use.
+// vector and 24 + `extra` temporaries (the unpacked operands of one vector:
+// kernels that combine more inputs per element pass more). The scheduler then
+// trades ILP for occupancy instead of unpacking every operand ahead of use.
 // A workgroup of `wg` lanes occupies wg/256 waves on each of the 4 SIMDs, so
 // never ask for fewer than that.
-constexpr int waves_for(int packed, int floats, int vpt, int wg) {
-    const int regs = 4 * packed + floats + vpt + 24;
+constexpr int waves_for(int packed, int floats, int vpt, int wg, int extra = 0) {
+    const int regs = 4 * packed + floats + vpt + 24 + extra;
     int w = 512 / regs;
     const int need = wg / 256 > 1 ? wg / 256 : 1;
     w = w < need ? need : w;
     return w > 8 ? 8 : w;
 }
+
+// Wide-row backward kernels: 1024 lanes per row, dW sums in LDS (at most
+// 128 KiB of the CU's 160 KiB).
+constexpr int kWideLanes = 1024;
+constexpr int kWideLdsBytes = 128 * 1024;
 
 struct KernelEntry {
     int lpr;         // lanes per row
@@ -43,6 +50,8 @@ struct KernelEntry {
 // residual-fused kernels. nullptr when (lpr, vpt, wg, pf) is not instantiated.
 const KernelEntry *fwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf);
 const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf);
+// wide-row backward kernels (lanes per row and workgroup kWideLanes)
+const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf);
 const void *scalar_kernel(int dtype, int is_bwd, int res);
 const void *dw_combine_kernel();
 const void *fill_zero_kernel();

@@ -30,15 +30,20 @@ import time
 
 import torch
 
-from . import (BF16, F32, LIB_PATH, RmsnormError, lib, rmsnorm_bwd_with_config, rmsnorm_build_info,
-               rmsnorm_config, rmsnorm_fwd_with_config, rmsnorm_query_config)
+from . import (BF16, BF16_WF32, F16, F16_WF32, F32, LIB_PATH, RmsnormError, lib, rmsnorm_bwd_with_config,
+               rmsnorm_build_info, rmsnorm_config, rmsnorm_fwd_with_config, rmsnorm_query_config)
 
-ELEM = {F32: 4, BF16: 2}
-TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+# activation element bytes, activation torch dtype and weight torch dtype of each format
+ELEM = {F32: 4, BF16: 2, F16: 2, BF16_WF32: 2, F16_WF32: 2}
+TORCH = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16, BF16_WF32: torch.bfloat16,
+         F16_WF32: torch.float16}
+WEIGHT = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16, BF16_WF32: torch.float32,
+          F16_WF32: torch.float32}
 # (lanes per row, workgroup sizes) built into the library; see csrc/rmsn_instances.h
 BUILT = {1: (256,), 2: (256,), 4: (256,), 8: (256,), 16: (256,), 32: (256,), 64: (256, 512, 1024),
          128: (256, 512, 1024), 256: (256, 512, 1024), 512: (512, 1024), 1024: (1024,)}
 MAX_VPT = 8
+WIDE_LANES = 1024  # wide-row backward kernels (vector_path 2): 1024 lanes, dW sums in LDS
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
 
@@ -50,7 +55,10 @@ def cache_key(M: int, N: int, dtype: int, is_bwd: int, device_name: str, num_cus
 def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: rmsnorm_config | None = None):
     """Every built vector shape that covers a row of N elements with one
     partially used slot at most, crossed with grids: the row-block count,
-    its halves, and 1-4 workgroups per compute unit. Pure host logic."""
+    its halves, and 1-4 workgroups per compute unit; for backward rows of more
+    than 1024 vectors also the wide-row kernels at one and two workgroups per
+    compute unit. Shapes that are not built fail at launch and are skipped.
+    Pure host logic."""
     es = ELEM[dtype]
     if (N * es) % 16:
         return [default] if default is not None else []
@@ -72,6 +80,13 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
                 for g in sorted(x for x in grids if 1 <= x <= min(row_blocks, 1 << 20)):
                     out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt,
                                               wg_threads=wg, prefetch=pf, grid=g))
+    wide_max = 8 if dtype == F32 else 4
+    if is_bwd and WIDE_LANES < nvec <= WIDE_LANES * wide_max:
+        vpt = -(-nvec // WIDE_LANES)
+        for pf in (0, 1):
+            for g in sorted({num_cus, 2 * num_cus} & set(range(1, M + 1))):
+                out.append(rmsnorm_config(vector_path=2, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
+                                          wg_threads=WIDE_LANES, prefetch=pf, grid=g))
     if default is not None:
         out.insert(0, default)
     return out
@@ -97,7 +112,7 @@ class _Bench:
                 dy=(torch.randn(M, N, device="cuda", generator=g) * 1e-2).to(t),
                 y=torch.empty(M, N, dtype=t, device="cuda"), dx=torch.empty(M, N, dtype=t, device="cuda"),
                 rstd=torch.empty(M, device="cuda")))
-        self.w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).to(t)
+        self.w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).to(WEIGHT[dtype])
         self.dw = torch.empty(N, device="cuda")
         self.ws = None
         self.ws_bytes = 0

@@ -72,6 +72,31 @@ def test_residual_argument_errors():
                                        None, None) == rn.EWORKSPACE
 
 
+def test_unfused_baseline_argument_errors():
+    # the unfused reference calls take the 16-byte vector layout only; all of
+    # these are rejected before any HIP call
+    L = rn.lib
+    assert L.rmsn_unfused_fwd(FAKE, FAKE, 1e-5, 4, 12, rn.BF16, FAKE, FAKE, None) == rn.EINVAL   # 24 B rows
+    assert L.rmsn_unfused_fwd(FAKE + 2, FAKE, 1e-5, 4, 16, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsn_unfused_fwd(FAKE, FAKE, 1e-5, 4, 16, rn.BF16, FAKE, None, None) == rn.EINVAL    # rstd required
+    assert L.rmsn_unfused_fwd(FAKE, FAKE, -1.0, 4, 16, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsn_unfused_fwd(FAKE, FAKE, 1e-5, 4, 16, 7, FAKE, FAKE, None) == rn.EDTYPE
+    assert L.rmsn_unfused_fwd(None, None, 1e-5, 0, 16, rn.F32, None, None, None) == rn.OK
+    assert L.rmsn_unfused_bwd_workspace_bytes(0, 64, rn.F32) == 0
+    assert L.rmsn_unfused_bwd_workspace_bytes(4, 6, rn.F32) == rn.EINVAL
+    need = L.rmsn_unfused_bwd_workspace_bytes(1000, 4096, rn.BF16)
+    assert need == 256 * 4096 * 4 + 4096  # 256 row chunks of partial dW, then S (1000 floats, padded)
+    assert L.rmsn_unfused_bwd(FAKE, FAKE, FAKE, FAKE, 1000, 4096, rn.BF16, FAKE, FAKE, FAKE, need - 1,
+                              None) == rn.EWORKSPACE
+    assert L.rmsn_unfused_bwd(FAKE, FAKE, FAKE, FAKE, 1000, 4096, rn.BF16, FAKE, FAKE, FAKE + 16, need,
+                              None) == rn.EWORKSPACE
+    assert L.rmsn_unfused_bwd(FAKE, FAKE, FAKE, None, 1000, 4096, rn.BF16, FAKE, FAKE, FAKE, need,
+                              None) == rn.EINVAL
+    assert L.rmsn_add(FAKE, FAKE, FAKE, 12, rn.BF16, None) == rn.EINVAL
+    assert L.rmsn_add(FAKE, FAKE, FAKE, 16, 9, None) == rn.EDTYPE
+    assert L.rmsn_add(None, None, None, 0, rn.F16, None) == rn.OK
+
+
 def test_dtype_codes():
     import torch
     assert rn.dtype_code(torch.float32) == rn.F32 and rn.dtype_code(torch.bfloat16) == rn.BF16
@@ -84,11 +109,34 @@ def test_dtype_codes():
 
 @pytest.mark.parametrize("dtype", [rn.F16, rn.BF16_WF32, rn.F16_WF32])
 def test_ladder_covers_new_formats(dtype):
-    # 16-bit activations: the same shapes as bf16
+    # 16-bit activations: the same shapes as bf16, except that the wide-row
+    # backward prefetches only when the weights are 16-bit too
     for N, is_bwd in ((4096, 0), (4096, 1), (128, 0), (32768, 1)):
         a = cfg(16384, N, dtype, is_bwd)
         b = cfg(16384, N, rn.BF16, is_bwd)
+        if a["vector_path"] == 2 and dtype != rn.F16:
+            assert a["prefetch"] == 0 and b["prefetch"] == 1
+            a["prefetch"] = b["prefetch"]
         assert a == b
+
+
+@pytest.mark.parametrize("N,dtype,vpt,pf", [
+    (16384, rn.BF16, 2, 1), (24576, rn.BF16, 3, 1), (32768, rn.BF16, 4, 1), (32768, rn.BF16_WF32, 4, 0),
+    (32768, rn.F16, 4, 1), (20480, rn.F32, 5, 0), (32768, rn.F32, 8, 0),
+])
+def test_ladder_wide_rows(N, dtype, vpt, pf):
+    """Backward rows of more than 1024 vectors: the wide-row kernel (1024 lanes,
+    dW sums in LDS), one workgroup per compute unit."""
+    c = cfg(4096, N, dtype, 1)
+    assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"]) == \
+        (2, 1024, vpt, 1024, pf)
+    assert c["grid"] == 256
+    # fp32 up to 4 vectors per lane keeps the register kernel
+    r = cfg(4096, 16384, rn.F32, 1)
+    assert (r["vector_path"], r["vecs_per_lane"]) == (1, 4)
+    # beyond what the LDS sums hold: the scalar kernel
+    assert cfg(4096, 65536, rn.BF16, 1)["vector_path"] == 0
+    assert cfg(4096, 36864, rn.F32, 1)["vector_path"] == 0
 
 
 def test_fwd_empty_is_noop():
@@ -137,8 +185,8 @@ def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
     (8192, rn.BF16, 0, 256, 4),
     (8192, rn.BF16, 1, 1024, 1),
     (32768, rn.BF16, 0, 1024, 4),
-    (32768, rn.BF16, 1, 1024, 4),
     (65536, rn.BF16, 0, 1024, 8),
+    (16384, rn.F32, 1, 1024, 4),
     (8, rn.BF16, 0, 1, 1),
     (24, rn.BF16, 0, 4, 1),        # 3 vectors -> 4 lanes, one masked
 ])

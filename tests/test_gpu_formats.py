@@ -279,3 +279,47 @@ def test_formats_full_size(fmt, M, N):
     odx, orr = oracle.bwd_dx(x, w, dy, eps, act, rows=rows, wdtype=wst)
     check_rows(dx[rows], odx, act, "dx", floor=term_rms(x, w, dy, orr, act, rows=rows))
     check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act)
+
+
+def _wide_shapes(fmt):
+    """(vectors per lane, prefetch) of the wide-row backward kernels built for a format."""
+    vpts = range(2, 9) if fmt == "f32" else range(2, 5)
+    return [(v, pf) for v in vpts for pf in (0, 1) if not (fmt == "f32" and v >= 6 and pf)]
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("residual", [False, True])
+def test_every_wide_kernel(fmt, residual):
+    """Each wide-row backward kernel (1024 lanes per row, dW sums in LDS), forced
+    on a ragged row (the last vector slot partly empty), 7 rows and a grid of 3
+    so workgroups loop over rows and the last one runs short."""
+    act, wst, code = FORMATS[fmt]
+    epv = 4 if act == "f32" else 8
+    for vpt, pf in _wide_shapes(fmt):
+        nvec = 1024 * (vpt - 1) + 517
+        M, N = 7, nvec * epv
+        cfg = rn.rmsnorm_config(vector_path=2, lanes_per_row=1024, vecs_per_lane=vpt, wg_threads=1024,
+                                prefetch=pf, grid=3)
+        _say(f"wide kernel vpt={vpt} pf={pf} N={N} M={M} {fmt} residual={residual}")
+        _, _, x, w, dy = _case(M, N, fmt, seed=9000 + vpt * 10 + pf)
+        eps = si.eps_f32(1e-6)
+        if residual:
+            res = si.random_tensor((M, N), act, seed=9100 + vpt)
+            dh = si.random_tensor((M, N), act, seed=9200 + vpt, scale=1e-2)
+            h, _, rstd = gpu_fwd_residual(x, res, w, eps, act)
+            dx, dw = gpu_bwd(h, w, dy, rstd, act, cfg=cfg, dh=dh)
+            odx, orr = oracle.bwd_dx(x, w, dy, eps, act, res=res, dh=dh, wdtype=wst)
+            check_rows(dx, odx, act, "dx (wide, residual)", floor=term_rms(h, w, dy, orr, act, dh=dh))
+            check_dw(dw, oracle.bwd_dw(x, dy, eps, act, res=res), act, "dW (wide, residual)")
+        else:
+            _, rstd = gpu_fwd(x, w, eps, act)
+            dx, dw = gpu_bwd(x, w, dy, rstd, act, cfg=cfg)
+            odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
+            check_rows(dx, odx, act, "dx (wide)", floor=term_rms(x, w, dy, orr, act))
+            check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act, "dW (wide)")
+            # same row-sum order and per-lane dW order as the register kernel of
+            # the same shape and grid: identical bits
+            reg = rn.rmsnorm_config(vector_path=1, lanes_per_row=1024, vecs_per_lane=vpt, wg_threads=1024,
+                                    prefetch=0, grid=3)
+            dx2, dw2 = gpu_bwd(x, w, dy, rstd, act, cfg=reg)
+            assert np.array_equal(dx, dx2) and np.array_equal(dw.view(np.uint32), dw2.view(np.uint32))
