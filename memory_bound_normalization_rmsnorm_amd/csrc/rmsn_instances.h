@@ -8,8 +8,9 @@
 //     workgroups of 256, 512 or 1024 lanes (the ladder's default is the
 //     smallest that holds a row and four wavefronts);
 //   * every shape with and without the register prefetch of the next row.
-// RMSN_LADDER_SHAPES (92 shapes; fp16, fp32-weight and residual-fused
-// kernels): the same, with only the ladder's default workgroup per width.
+// RMSN_LADDER_SHAPES (98 shapes; fp16, fp32-weight and residual-fused
+// kernels): the same, with only the workgroups the ladder picks per width
+// (the row's own, and 1024 lanes for backward rows of 64 to 256 lanes).
 #pragma once
 
 #define RMSN_V8(X, L, W, P) X(L, 1, W, P) X(L, 2, W, P) X(L, 3, W, P) X(L, 4, W, P) \
@@ -32,6 +33,8 @@
     RMSN_PF(RMSN_NARROW, X, 4, 256) RMSN_PF(RMSN_NARROW, X, 8, 256)                           \
     RMSN_PF(RMSN_NARROW, X, 16, 256) RMSN_PF(RMSN_NARROW, X, 32, 256)                         \
     RMSN_PF(RMSN_V8, X, 64, 256) RMSN_PF(RMSN_V8, X, 128, 256) RMSN_PF(RMSN_V8, X, 256, 256)  \
+    RMSN_PF(RMSN_NARROW, X, 64, 1024) RMSN_PF(RMSN_NARROW, X, 128, 1024)                      \
+    RMSN_PF(RMSN_NARROW, X, 256, 1024)                                                        \
     RMSN_PF(RMSN_V8, X, 512, 512) RMSN_PF(RMSN_V8, X, 1024, 1024)
 
 // Wide-row backward kernels (1024 lanes, dW sums in LDS), as (vectors per

@@ -120,6 +120,31 @@ def test_ladder_covers_new_formats(dtype):
         assert a == b
 
 
+def test_ladder_backward_grid_and_prefetch():
+    """Partial rows (written and read once, 8 N bytes each) stay within 1/6 of
+    the algorithmic bytes, never below one workgroup per CU; 1024-lane rows
+    prefetch only when each workgroup walks at most 16 rows."""
+    # bf16 4096 x 4096: cap = 6*4096*4096 / 6 / (8*4096) = 512 -> 2 per CU
+    assert cfg(4096, 4096, rn.BF16, 1)["grid"] == 512
+    # bf16 1024 x 4096: cap 128 -> one per CU
+    assert cfg(1024, 4096, rn.BF16, 1)["grid"] == 256
+    # below one row block per CU: the row blocks
+    assert cfg(100, 4096, rn.BF16, 1)["grid"] == 100
+    # 1024 lanes: 4096 rows over 512 workgroups (8 each) prefetch, 16384 over 512 (32) do not
+    a, b = cfg(4096, 8192, rn.BF16, 1), cfg(16384, 8192, rn.BF16, 1)
+    assert (a["lanes_per_row"], a["grid"], a["prefetch"]) == (1024, 512, 1)
+    assert (b["lanes_per_row"], b["grid"], b["prefetch"]) == (1024, 512, 0)
+    # fp32, two vectors per lane: the same rule; 3 or more never prefetch
+    assert cfg(4096, 8192, rn.F32, 1)["prefetch"] == 1
+    assert cfg(4096, 12288, rn.F32, 1)["prefetch"] == 0
+    # rows of 64..256 lanes: 1024-lane workgroups, prefetching; 512 lanes: their own, prefetching
+    for N, lpr in ((512, 64), (1024, 128), (2048, 256)):
+        c = cfg(16384, N, rn.BF16, 1)
+        assert (c["lanes_per_row"], c["wg_threads"], c["rows_per_wg"], c["prefetch"]) == (lpr, 1024, 1024 // lpr, 1)
+    c = cfg(16384, 4096, rn.BF16, 1)
+    assert (c["lanes_per_row"], c["wg_threads"], c["prefetch"], c["grid"]) == (512, 512, 1, 512)
+
+
 @pytest.mark.parametrize("N,dtype,vpt,pf", [
     (16384, rn.BF16, 2, 1), (24576, rn.BF16, 3, 1), (32768, rn.BF16, 4, 1), (32768, rn.BF16_WF32, 4, 0),
     (32768, rn.F16, 4, 1), (20480, rn.F32, 5, 0), (32768, rn.F32, 8, 0),
@@ -194,7 +219,8 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     c = cfg(4096, N, dtype, is_bwd)
     assert c["vector_path"] == 1
     assert (c["lanes_per_row"], c["vecs_per_lane"]) == (lpr, vpt)
-    assert c["wg_threads"] == max(lpr, 256)
+    # backward rows of 64 to 256 lanes share 1024-lane workgroups
+    assert c["wg_threads"] == (1024 if is_bwd and 64 <= lpr <= 256 else max(lpr, 256))
     assert c["rows_per_wg"] == c["wg_threads"] // lpr
     nvec = N * (4 if dtype == rn.F32 else 2) // 16
     assert (vpt - 1) * lpr < nvec <= vpt * lpr

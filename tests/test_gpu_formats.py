@@ -89,10 +89,11 @@ def test_formats_small(M, N, fmt):
 
 def _ladder_shapes():
     """The (lanes_per_row, vecs_per_lane, wg_threads, prefetch) kernels built for
-    every format: the ladder's default workgroup per width."""
+    every format: the workgroups the ladder picks per width."""
     out = []
     for pf in (0, 1):
         out += [(lpr, 1, 256, pf) for lpr in (1, 2, 4, 8, 16, 32)]
+        out += [(lpr, 1, 1024, pf) for lpr in (64, 128, 256)]
         for lpr in (64, 128, 256, 512, 1024):
             out += [(lpr, v, max(256, lpr), pf) for v in range(1, 9)]
     return out
@@ -108,7 +109,7 @@ def test_every_ladder_kernel(fmt):
     """Each kernel built for the format, forced through *_with_config on a ragged
     row, a ragged row count and a grid of 2 (workgroups loop over row blocks)."""
     shapes = _ladder_shapes()
-    assert len(shapes) == 92
+    assert len(shapes) == 98
     for lpr, vpt, wg, pf in shapes:
         M, N = _ragged(lpr, vpt, wg, 8)
         cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, wg_threads=wg,
