@@ -251,3 +251,50 @@ def test_full_size_workload(name):
     check_rows(dx[rows], odx, wl.dtype, "dx", floor=term_rms(x, w, dy, orows, wl.dtype, rows=rows))
     check_dw(dw, oracle.bwd_dw(x, dy, eps, wl.dtype), wl.dtype)
     assert np.all(np.isfinite(widen(y, wl.dtype))) and np.all(np.isfinite(widen(dx, wl.dtype)))
+
+
+def test_beyond_4gib_tensors():
+    """bf16 1048576 x 2560: 2.7e9 elements, 5.4 GB per tensor, so element
+    indices pass 2^31 and byte offsets pass 2^32. Inputs are drawn on the
+    device (seeded); sampled rows, including the last ones, go to the host for
+    the oracle. dW is checked column by column against the fp64 sum of
+    dy * x * rstd over all rows (plain PyTorch, in row chunks)."""
+    M, N, dtype = 1 << 20, 2560, "bf16"
+    eps = si.eps_f32(1e-6)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    _say("4 GiB+: generating on the device")
+    x = torch.randn((M, N), generator=g, device="cuda").to(torch.bfloat16)
+    dy = (torch.randn((M, N), generator=g, device="cuda") * 1e-2).to(torch.bfloat16)
+    w = (1 + 0.1 * torch.randn(N, generator=g, device="cuda")).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    rstd = torch.empty(M, device="cuda")
+    _say("4 GiB+: forward")
+    rn.rmsnorm_fwd(x, w, eps, M, N, rn.BF16, y, rstd)
+    dx = torch.empty_like(x)
+    dw = torch.empty(N, device="cuda")
+    nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, rn.BF16)
+    ws = torch.empty(nbytes // 4 + 64, device="cuda")
+    _say("4 GiB+: backward")
+    rn.rmsnorm_bwd(x, w, dy, rstd, M, N, rn.BF16, dx, dw, ws, nbytes)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([_sample_rows(M, k=24, seed=7), np.arange(M - 8, M)])).astype(np.int64)
+    ri = torch.from_numpy(rows).cuda()
+    xs, dys = to_host(x[ri], dtype), to_host(dy[ri], dtype)
+    wh = to_host(w, dtype)
+    oy, orr = oracle.fwd(xs, wh, eps, dtype)
+    check_rows(to_host(y[ri], dtype), oy, dtype, "y (rows past 4 GiB)")
+    check_rstd(rstd[ri].cpu().numpy(), orr)
+    odx, orr = oracle.bwd_dx(xs, wh, dys, eps, dtype)
+    check_rows(to_host(dx[ri], dtype), odx, dtype, "dx (rows past 4 GiB)", floor=term_rms(xs, wh, dys, orr, dtype))
+    _say("4 GiB+: dW reference")
+    ref = torch.zeros(N, dtype=torch.float64, device="cuda")
+    for s in range(0, M, 1 << 16):
+        e = min(M, s + (1 << 16))
+        ref += (dy[s:e].double() * x[s:e].double() * rstd[s:e].double()[:, None]).sum(0)
+    ref = ref.cpu().numpy()
+    err = np.abs(dw.cpu().numpy().astype(np.float64) - ref)
+    bound = 1e-3 * np.maximum(np.abs(ref), 1e-2 * np.sqrt(np.mean(ref * ref)))
+    assert np.all(err <= bound), f"dW: max err {err.max()}"
+    del x, dy, y, dx, ws
+    torch.cuda.empty_cache()
