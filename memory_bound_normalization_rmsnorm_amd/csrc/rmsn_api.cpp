@@ -164,9 +164,10 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int num_cus, int b
     } else {
         const int64_t cus = num_cus > 0 ? num_cus : 1;
         int64_t want = (c->vector_path == kWidePath ? 1 : c->lanes_per_row < 64 ? 3 : 2) * cus;
-        // partial rows are written once and read once: 8 * N bytes each
-        const int64_t bytes = 3 * M * N * elem_size(dtype);
-        const int64_t cap = bytes / kPartialShare / (8 * N);
+        // partial rows are written once and read once (8 * N bytes each); at
+        // most 1/kPartialShare of the 3 * M * N * elem algorithmic bytes, so
+        // at most 3 * M * elem / (8 * kPartialShare) rows (N cancels)
+        const int64_t cap = 3 * M * elem_size(dtype) / (8 * kPartialShare);
         if (want > cap) want = cap > cus ? cap : cus;
         const int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
         if (want > resident) want = resident;
