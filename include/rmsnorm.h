@@ -78,13 +78,17 @@ typedef enum {
  * actually costs on Hopper", section 03). Reported for logs and tests.
  */
 typedef struct {
-    int32_t vector_path;     /* 1: 16-byte vector row kernel; 0: scalar row kernel */
+    int32_t vector_path;     /* 1: 16-byte vector row kernel; 2: the backward's wide-row vector
+                                kernel (1024 lanes, dW sums in LDS); 0: scalar row kernel */
     int32_t lanes_per_row;   /* lanes that share one row (1..1024) */
     int32_t vecs_per_lane;   /* 16-byte vectors each lane holds per row (vector path) */
     int32_t wg_threads;      /* workgroup size */
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
     int32_t prefetch;        /* 1: the next row block's loads are issued before the current
                                 block's arithmetic (register double buffer) */
+    int32_t stream_loads;    /* forward, rows of 64 lanes or more: 1 when the row loads carry the
+                                non-temporal hint (the ladder sets it; an explicit 0 suits inputs
+                                that are still cache-resident); ignored by the backward */
     int64_t grid;            /* workgroups launched */
     int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid) */
     int64_t partial_stride;  /* backward: floats between consecutive partial rows */

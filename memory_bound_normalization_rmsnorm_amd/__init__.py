@@ -54,6 +54,7 @@ class rmsnorm_config(ctypes.Structure):
         ("wg_threads", ctypes.c_int32),
         ("rows_per_wg", ctypes.c_int32),
         ("prefetch", ctypes.c_int32),
+        ("stream_loads", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("partial_rows", ctypes.c_int64),
         ("partial_stride", ctypes.c_int64),

@@ -165,13 +165,20 @@ struct Elem<f16_t> {
 // buffer access on CDNA. The base pointer must be wave-uniform.
 constexpr int kBufWord3 = 0x00020000;
 // Cache-policy bits of the buffer accesses (CDNA3/4: bit 0 sc0, bit 1 nt,
-// bit 4 sc1). Rows are streamed exactly once; measured on MI355X, the
-// non-temporal hint pays on the forward's stores and on both the backward's
-// loads and stores, and costs on the forward's loads. The defaults below are
-// those measurements; -D overrides exist to re-measure.
+// bit 4 sc1). Rows are streamed exactly once; measured on MI355X (HIP-graph
+// timed, inputs rotating past the 256 MB MALL), the non-temporal hint pays on
+// the forward's stores, on the forward's loads of wavefront-wide rows (0-18%
+// from 1024 x 1024 to 65536 x 4096; the host passes that choice as
+// `stream_ld`, so a caller whose input is still cache-resident can turn it
+// off: there it cost 7% at 4096 x 4096), and on both the backward's loads and
+// stores. It costs 1.6% on the loads of narrow rows (QK-norm's 128). The
+// defaults below are those measurements; -D overrides exist to re-measure.
 constexpr int kNonTemporal = 2;
 #ifndef RMSN_FWD_LOAD_AUX
-#define RMSN_FWD_LOAD_AUX 0
+#define RMSN_FWD_LOAD_AUX 2         // streaming forward loads
+#endif
+#ifndef RMSN_FWD_NARROW_LOAD_AUX
+#define RMSN_FWD_NARROW_LOAD_AUX 0  // the other forward loads
 #endif
 #ifndef RMSN_FWD_STORE_AUX
 #define RMSN_FWD_STORE_AUX 2

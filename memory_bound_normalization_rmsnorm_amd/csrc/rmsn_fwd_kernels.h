@@ -49,12 +49,23 @@ __global__ void __launch_bounds__(WG)
 __attribute__((amdgpu_waves_per_eu(waves_for(VPT * fwd_packed_per_slot<T, TW, RES, PF>(), 0, VPT, WG,
                                              (RES || WeightVec<T, TW>::kVecs > 1) ? Elem<T>::kPerVec : 0))))
 fwd_vec(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict__ w, T *__restrict__ h,
-        T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t nvec) {
+        T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t nvec,
+        int32_t stream_ld) {
     using E = Elem<T>;
     using WV = WeightVec<T, TW>;
     constexpr int RPW = WG / LPR;
+    // Row loads carry the non-temporal hint when the host asks for it (long
+    // grids of wavefront-wide rows); narrow rows never do.
+    const bool nt_loads = LPR >= 64 && stream_ld != 0;
     static_assert(WG % LPR == 0, "workgroup must hold whole row groups");
     __shared__ float slots[LPR > 64 ? 2 * (WG / 64) : 1];
+    // Narrow rows (several per wavefront): the workgroup's rstd values are
+    // gathered in LDS and written by its first RPW lanes in one coalesced
+    // store, instead of one partial store per wavefront (a second store
+    // instruction per wavefront that cost 3% at 128 columns).
+    constexpr bool kGatherRstd = LPR < 64;
+    __shared__ float rsh[kGatherRstd ? 2 * RPW : 1];
+    int rpar = 0;
 
     const int lane = threadIdx.x % LPR;
     const int grp = threadIdx.x / LPR;
@@ -83,12 +94,21 @@ fwd_vec(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict
         const int64_t bb = b < M ? b : 0;
         const uint32_t bytes = rows_at(b) * row_bytes;
         const Buf xb(x + bb * N, bytes);
+        const Buf rb(RES ? res + bb * N : x, RES ? bytes : 0u);
+        if (nt_loads) {
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) xo[v] = xb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
-        if constexpr (RES) {
-            const Buf rb(res + bb * N, bytes);
+            for (int v = 0; v < VPT; ++v) xo[v] = xb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
+            if constexpr (RES) {
 #pragma unroll
-            for (int v = 0; v < VPT; ++v) ro[v] = rb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
+                for (int v = 0; v < VPT; ++v) ro[v] = rb.load16<RMSN_FWD_LOAD_AUX>(off[v]);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) xo[v] = xb.load16<RMSN_FWD_NARROW_LOAD_AUX>(off[v]);
+            if constexpr (RES) {
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) ro[v] = rb.load16<RMSN_FWD_NARROW_LOAD_AUX>(off[v]);
+            }
         }
     };
 
@@ -139,7 +159,17 @@ fwd_vec(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict
 
         if (rstd) {
             const Buf rb(rstd + base, rows * 4u);
-            rb.store4(lane == 0 ? (uint32_t)grp * 4u : kOff, r);
+            if constexpr (kGatherRstd) {
+                // double-buffered: a buffer is rewritten two blocks later, after
+                // every lane has passed the next block's barrier
+                float *buf = rsh + rpar * RPW;
+                if (lane == 0) buf[grp] = r;
+                __syncthreads();
+                if (threadIdx.x < RPW) rb.store4((uint32_t)threadIdx.x * 4u, buf[threadIdx.x]);
+                rpar ^= 1;
+            } else {
+                rb.store4(lane == 0 ? (uint32_t)grp * 4u : kOff, r);
+            }
         }
 #pragma unroll
         for (int v = 0; v < VPT; ++v) keep_packed(xv[v]);
@@ -158,7 +188,8 @@ fwd_vec(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict
 template <typename T, typename TW, bool RES>
 __global__ void __launch_bounds__(kScalarWG)
 fwd_scalar(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict__ w, T *__restrict__ h,
-           T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t /*nvec*/) {
+           T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t /*nvec*/,
+           int32_t /*stream_ld*/) {
     using E = Elem<T>;
     __shared__ float slots[2 * (kScalarWG / 64)];
     const float n = (float)N;

@@ -2,8 +2,8 @@
 
 The library's default configuration comes from an analytical ladder on the
 row width (``rmsnorm_select_config``). This module searches the space the
-ladder chooses from -- lanes per row, workgroup size, register prefetch and
-grid -- by timing each candidate through ``rmsnorm_{fwd,bwd}_with_config``.
+ladder chooses from -- lanes per row, workgroup size, register prefetch,
+grid and (forward) non-temporal row loads -- by timing each candidate through ``rmsnorm_{fwd,bwd}_with_config``.
 It keeps the winner per (device, compute units, M, N, dtype, direction,
 library build).
 
@@ -77,10 +77,12 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             rpw = wg // lpr
             row_blocks = -(-M // rpw)
             grids = {row_blocks, -(-row_blocks // 2)} | {k * num_cus for k in (1, 2, 3, 4)}
+            streams = (0, 1) if (not is_bwd and lpr >= 64) else (0,)
             for pf in (0, 1):
                 for g in sorted(x for x in grids if 1 <= x <= min(row_blocks, 1 << 20)):
-                    out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt,
-                                              wg_threads=wg, prefetch=pf, grid=g))
+                    for sl in streams:
+                        out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt,
+                                                  wg_threads=wg, prefetch=pf, stream_loads=sl, grid=g))
     wide_max = 8 if dtype == F32 else 4
     if is_bwd and WIDE_LANES < nvec <= WIDE_LANES * wide_max:
         vpt = -(-nvec // WIDE_LANES)
@@ -94,7 +96,7 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
 
 
 def _key(c: rmsnorm_config):
-    return (c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch, c.grid)
+    return (c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch, c.grid, c.stream_loads)
 
 
 class _Bench:

@@ -221,6 +221,12 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (c["lanes_per_row"], c["vecs_per_lane"]) == (lpr, vpt)
     # backward rows of 64 to 256 lanes share 1024-lane workgroups
     assert c["wg_threads"] == (1024 if is_bwd and 64 <= lpr <= 256 else max(lpr, 256))
+    # the forward streams rows of a wavefront or more with non-temporal loads
+    # (4096 rows: every input here exceeds the 4 MiB threshold but N = 8, 24)
+    big = 4096 * N * (4 if dtype == rn.F32 else 2) >= 4 << 20
+    assert c["stream_loads"] == (1 if not is_bwd and lpr >= 64 and big else 0)
+    # a decode step's few rows stay on plain loads
+    assert cfg(16, N, dtype, 0)["stream_loads"] == 0
     assert c["rows_per_wg"] == c["wg_threads"] // lpr
     nvec = N * (4 if dtype == rn.F32 else 2) // 16
     assert (vpt - 1) * lpr < nvec <= vpt * lpr

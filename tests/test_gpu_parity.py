@@ -106,8 +106,9 @@ def test_every_vector_kernel(dtype):
         nvec = min(lpr * vpt, max(1, lpr * (vpt - 1) + max(1, lpr // 2 + 1)))  # the last slot is partial
         N = nvec * epv
         M = 3 * (wg // lpr) + 1
+        # the non-temporal forward loads on every other kernel (a cache hint only)
         cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt, wg_threads=wg,
-                                prefetch=pf, grid=2)
+                                prefetch=pf, stream_loads=(vpt + pf) % 2, grid=2)
         x, w, dy = si.random_case(M, N, dtype, seed=lpr * 100 + vpt + wg + pf, dy_scale=1e-2)
         _say(f"kernel lpr={lpr} vpt={vpt} wg={wg} pf={pf} N={N} M={M} {dtype}")
         full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_f=cfg, cfg_b=cfg)
