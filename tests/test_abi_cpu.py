@@ -164,6 +164,26 @@ def test_ladder_wide_rows(N, dtype, vpt, pf):
     assert cfg(4096, 36864, rn.F32, 1)["vector_path"] == 0
 
 
+def test_explicit_config_errors():
+    """Explicit configurations are checked against the shape before any HIP call."""
+    L, C = rn.lib, rn.rmsnorm_config
+
+    def fwd(**kw):
+        c = C(vector_path=1, lanes_per_row=128, vecs_per_lane=4, wg_threads=256, grid=8)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, 64, 4096, rn.BF16, FAKE, FAKE, c, None)
+
+    assert fwd(stream_loads=2) == rn.ECONFIG
+    assert fwd(grid=0) == rn.ECONFIG
+    assert fwd(lanes_per_row=64) == rn.ECONFIG           # 64 x 4 vectors do not cover 512
+    assert fwd(wg_threads=320) == rn.ECONFIG             # not whole rows
+    assert fwd(vecs_per_lane=9, lanes_per_row=64) == rn.ECONFIG  # not built
+    assert fwd(vector_path=2, lanes_per_row=1024, vecs_per_lane=1, wg_threads=1024) == rn.ECONFIG  # backward only
+    assert fwd(vector_path=3) == rn.ECONFIG
+    assert fwd(prefetch=2) == rn.ECONFIG
+
+
 def test_fwd_empty_is_noop():
     assert rn.lib.rmsnorm_fwd(None, None, 1e-5, 0, 8, rn.F32, None, None, None) == rn.OK
 
@@ -246,7 +266,9 @@ def test_ladder_grid_and_workspace_shape():
     assert c["grid"] == 512 and c["partial_rows"] == 512 and c["partial_stride"] == 4096 and c["prefetch"] == 1
     # ... capped by residency
     assert cfg(16384, 4096, rn.BF16, 1, cus=256, blocks=1)["grid"] == 256
-    # ... fewer when the partial rows would exceed ~5% of the bytes (wide rows, few of them), never below the CUs
+    # ... fewer when the partial rows would exceed 1/6 of the bytes, never below the CUs
+    assert cfg(2048, 4096, rn.BF16, 1, cus=256, blocks=2)["grid"] == 256
+    # ... the wide-row kernel: one per compute unit
     assert cfg(4096, 32768, rn.BF16, 1, cus=256, blocks=2)["grid"] == 256
     # ... three per compute unit for rows narrower than a wavefront
     assert cfg(1 << 20, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 768
