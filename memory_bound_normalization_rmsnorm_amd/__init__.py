@@ -122,6 +122,42 @@ def _ptr(p):
     return p.data_ptr()
 
 
+# activation and weight torch dtypes of each format code
+_ACT = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16, BF16_WF32: torch.bfloat16,
+        F16_WF32: torch.float16}
+_WEIGHT = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16, BF16_WF32: torch.float32,
+           F16_WF32: torch.float32}
+
+
+def _arg(p, what: str, kind: str = "raw", code=None, count=None, nbytes=None):
+    """Pointer of an argument. Integers (device addresses) and None pass
+    through. A tensor must be a contiguous GPU tensor of the format's dtype
+    (kind "act", "weight" or "f32") holding at least `count` elements (or
+    `nbytes` bytes): the C entry points take raw pointers and cannot check
+    what they point to, and a short buffer would be read or written out of
+    bounds."""
+    if p is None or isinstance(p, int):
+        return p
+    if not isinstance(p, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor, a device address or None, got {type(p).__name__}")
+    if not p.is_cuda:
+        raise ValueError(f"{what}: tensor is on {p.device}, not on the GPU")
+    if not p.is_contiguous():
+        raise ValueError(f"{what}: tensor is not contiguous (row-major [M][N] is required)")
+    want = {"act": _ACT.get(code), "weight": _WEIGHT.get(code), "f32": torch.float32}.get(kind)
+    if want is not None and p.dtype != want:
+        raise TypeError(f"{what}: dtype {p.dtype}, format {code} needs {want}")
+    if count is not None and count >= 0 and p.numel() < count:
+        raise ValueError(f"{what}: {p.numel()} elements, the call needs {count}")
+    if nbytes is not None and nbytes >= 0 and p.numel() * p.element_size() < nbytes:
+        raise ValueError(f"{what}: {p.numel() * p.element_size()} bytes, the call needs {nbytes}")
+    return p.data_ptr()
+
+
+def _mn(M, N):
+    return int(M) * int(N) if int(M) >= 0 and int(N) >= 0 else -1
+
+
 def _stream(s):
     if s is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -156,14 +192,18 @@ def rmsnorm_build_info() -> str:
 
 
 def rmsnorm_fwd(x, w, eps, M, N, dtype, y, rstd, stream=None) -> None:
-    _check("rmsnorm_fwd", lib.rmsnorm_fwd(_ptr(x), _ptr(w), float(eps), int(M), int(N), int(dtype),
-                                          _ptr(y), _ptr(rstd), _stream(stream)))
+    mn = _mn(M, N)
+    _check("rmsnorm_fwd", lib.rmsnorm_fwd(_arg(x, "x", "act", dtype, mn), _arg(w, "w", "weight", dtype, int(N)),
+                                          float(eps), int(M), int(N), int(dtype), _arg(y, "y", "act", dtype, mn),
+                                          _arg(rstd, "rstd", "f32", count=int(M)), _stream(stream)))
 
 
 def rmsnorm_fwd_with_config(x, w, eps, M, N, dtype, y, rstd, cfg: rmsnorm_config, stream=None) -> None:
+    mn = _mn(M, N)
     _check("rmsnorm_fwd_with_config",
-           lib.rmsnorm_fwd_with_config(_ptr(x), _ptr(w), float(eps), int(M), int(N), int(dtype), _ptr(y),
-                                       _ptr(rstd), ctypes.byref(cfg), _stream(stream)))
+           lib.rmsnorm_fwd_with_config(_arg(x, "x", "act", dtype, mn), _arg(w, "w", "weight", dtype, int(N)),
+                                       float(eps), int(M), int(N), int(dtype), _arg(y, "y", "act", dtype, mn),
+                                       _arg(rstd, "rstd", "f32", count=int(M)), ctypes.byref(cfg), _stream(stream)))
 
 
 def rmsnorm_bwd_workspace_bytes(M, N, dtype) -> int:
@@ -173,46 +213,69 @@ def rmsnorm_bwd_workspace_bytes(M, N, dtype) -> int:
 
 
 def rmsnorm_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream=None) -> None:
-    _check("rmsnorm_bwd", lib.rmsnorm_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N), int(dtype),
-                                          _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
-                                          _stream(stream)))
+    mn = _mn(M, N)
+    _check("rmsnorm_bwd", lib.rmsnorm_bwd(_arg(x, "x", "act", dtype, mn), _arg(w, "w", "weight", dtype, int(N)),
+                                          _arg(dy, "dy", "act", dtype, mn), _arg(rstd, "rstd", "f32", count=int(M)),
+                                          int(M), int(N), int(dtype), _arg(dx, "dx", "act", dtype, mn),
+                                          _arg(dw, "dw", "f32", count=int(N)),
+                                          _arg(workspace, "workspace", nbytes=int(workspace_bytes)),
+                                          int(workspace_bytes), _stream(stream)))
 
 
 def rmsnorm_bwd_with_config(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes,
                             cfg: rmsnorm_config, stream=None) -> None:
+    mn = _mn(M, N)
     _check("rmsnorm_bwd_with_config",
-           lib.rmsnorm_bwd_with_config(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N), int(dtype),
-                                       _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
-                                       ctypes.byref(cfg), _stream(stream)))
+           lib.rmsnorm_bwd_with_config(_arg(x, "x", "act", dtype, mn), _arg(w, "w", "weight", dtype, int(N)),
+                                       _arg(dy, "dy", "act", dtype, mn), _arg(rstd, "rstd", "f32", count=int(M)),
+                                       int(M), int(N), int(dtype), _arg(dx, "dx", "act", dtype, mn),
+                                       _arg(dw, "dw", "f32", count=int(N)),
+                                       _arg(workspace, "workspace", nbytes=int(workspace_bytes)),
+                                       int(workspace_bytes), ctypes.byref(cfg), _stream(stream)))
 
 
 def rmsnorm_fwd_residual(x, res, w, eps, M, N, dtype, h, y, rstd, cfg=None, stream=None) -> None:
+    mn = _mn(M, N)
     _check("rmsnorm_fwd_residual",
-           lib.rmsnorm_fwd_residual(_ptr(x), _ptr(res), _ptr(w), float(eps), int(M), int(N), int(dtype), _ptr(h),
-                                    _ptr(y), _ptr(rstd), None if cfg is None else ctypes.byref(cfg),
-                                    _stream(stream)))
+           lib.rmsnorm_fwd_residual(_arg(x, "x", "act", dtype, mn), _arg(res, "res", "act", dtype, mn),
+                                    _arg(w, "w", "weight", dtype, int(N)), float(eps), int(M), int(N), int(dtype),
+                                    _arg(h, "h", "act", dtype, mn), _arg(y, "y", "act", dtype, mn),
+                                    _arg(rstd, "rstd", "f32", count=int(M)),
+                                    None if cfg is None else ctypes.byref(cfg), _stream(stream)))
 
 
 def rmsnorm_bwd_residual(h, w, dy, dh, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, cfg=None,
                          stream=None) -> None:
+    mn = _mn(M, N)
     _check("rmsnorm_bwd_residual",
-           lib.rmsnorm_bwd_residual(_ptr(h), _ptr(w), _ptr(dy), _ptr(dh), _ptr(rstd), int(M), int(N), int(dtype),
-                                    _ptr(dx), _ptr(dw), _ptr(workspace), int(workspace_bytes),
-                                    None if cfg is None else ctypes.byref(cfg), _stream(stream)))
+           lib.rmsnorm_bwd_residual(_arg(h, "h", "act", dtype, mn), _arg(w, "w", "weight", dtype, int(N)),
+                                    _arg(dy, "dy", "act", dtype, mn), _arg(dh, "dh", "act", dtype, mn),
+                                    _arg(rstd, "rstd", "f32", count=int(M)), int(M), int(N), int(dtype),
+                                    _arg(dx, "dx", "act", dtype, mn), _arg(dw, "dw", "f32", count=int(N)),
+                                    _arg(workspace, "workspace", nbytes=int(workspace_bytes)),
+                                    int(workspace_bytes), None if cfg is None else ctypes.byref(cfg),
+                                    _stream(stream)))
 
 
 def rmsnorm_bwd_rows(x, w, dy, rstd, M, N, dtype, dx, workspace, workspace_bytes, stream=None) -> int:
     """Backward row kernel only; returns the number of partial dW rows written."""
     p = ctypes.c_int64(0)
-    _check("rmsnorm_bwd_rows", lib.rmsnorm_bwd_rows(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N),
-                                                    int(dtype), _ptr(dx), _ptr(workspace), int(workspace_bytes),
-                                                    ctypes.byref(p), _stream(stream)))
+    mn = _mn(M, N)
+    _check("rmsnorm_bwd_rows", lib.rmsnorm_bwd_rows(_arg(x, "x", "act", dtype, mn),
+                                                    _arg(w, "w", "weight", dtype, int(N)),
+                                                    _arg(dy, "dy", "act", dtype, mn),
+                                                    _arg(rstd, "rstd", "f32", count=int(M)), int(M), int(N),
+                                                    int(dtype), _arg(dx, "dx", "act", dtype, mn),
+                                                    _arg(workspace, "workspace", nbytes=int(workspace_bytes)),
+                                                    int(workspace_bytes), ctypes.byref(p), _stream(stream)))
     return int(p.value)
 
 
 def rmsnorm_bwd_combine(workspace, partial_rows, N, dw, stream=None) -> None:
-    _check("rmsnorm_bwd_combine", lib.rmsnorm_bwd_combine(_ptr(workspace), int(partial_rows), int(N), _ptr(dw),
-                                                          _stream(stream)))
+    ldp = (int(N) + 63) // 64 * 64
+    _check("rmsnorm_bwd_combine",
+           lib.rmsnorm_bwd_combine(_arg(workspace, "workspace", nbytes=int(partial_rows) * ldp * 4),
+                                   int(partial_rows), int(N), _arg(dw, "dw", "f32", count=int(N)), _stream(stream)))
 
 
 def rmsnorm_select_config(M, N, dtype, is_bwd, aligned, num_cus, blocks_per_cu) -> rmsnorm_config:
@@ -231,28 +294,33 @@ def rmsnorm_query_config(M, N, dtype, is_bwd) -> rmsnorm_config:
 
 
 def rmsn_probe_copy(src, dst, nbytes, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_copy", lib.rmsn_probe_copy(_ptr(src), _ptr(dst), int(nbytes), int(grid), int(variant),
-                                                  _stream(stream)))
+    _check("rmsn_probe_copy", lib.rmsn_probe_copy(_arg(src, "src", nbytes=int(nbytes)),
+                                                  _arg(dst, "dst", nbytes=int(nbytes)), int(nbytes), int(grid),
+                                                  int(variant), _stream(stream)))
 
 
 def rmsn_probe_write(dst, nbytes, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_write", lib.rmsn_probe_write(_ptr(dst), int(nbytes), int(grid), int(variant),
-                                                    _stream(stream)))
+    _check("rmsn_probe_write", lib.rmsn_probe_write(_arg(dst, "dst", nbytes=int(nbytes)), int(nbytes), int(grid),
+                                                    int(variant), _stream(stream)))
 
 
 def rmsn_probe_read(src, nbytes, sink, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_read", lib.rmsn_probe_read(_ptr(src), int(nbytes), int(grid), int(variant), _ptr(sink),
-                                                  _stream(stream)))
+    _check("rmsn_probe_read", lib.rmsn_probe_read(_arg(src, "src", nbytes=int(nbytes)), int(nbytes), int(grid),
+                                                  int(variant), _arg(sink, "sink", nbytes=16), _stream(stream)))
 
 
 def rmsn_probe_add(a, b, c, nbytes, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_add", lib.rmsn_probe_add(_ptr(a), _ptr(b), _ptr(c), int(nbytes), int(grid), int(variant),
-                                                _stream(stream)))
+    _check("rmsn_probe_add", lib.rmsn_probe_add(_arg(a, "a", nbytes=int(nbytes)), _arg(b, "b", nbytes=int(nbytes)),
+                                                _arg(c, "c", nbytes=int(nbytes)), int(nbytes), int(grid),
+                                                int(variant), _stream(stream)))
 
 
 def rmsn_unfused_fwd(x, w, eps, M, N, dtype, y, rstd, stream=None) -> None:
-    _check("rmsn_unfused_fwd", lib.rmsn_unfused_fwd(_ptr(x), _ptr(w), float(eps), int(M), int(N), int(dtype),
-                                                    _ptr(y), _ptr(rstd), _stream(stream)))
+    mn = _mn(M, N)
+    _check("rmsn_unfused_fwd", lib.rmsn_unfused_fwd(_arg(x, "x", "act", dtype, mn),
+                                                    _arg(w, "w", "weight", dtype, int(N)), float(eps), int(M),
+                                                    int(N), int(dtype), _arg(y, "y", "act", dtype, mn),
+                                                    _arg(rstd, "rstd", "f32", count=int(M)), _stream(stream)))
 
 
 def rmsn_unfused_bwd_workspace_bytes(M, N, dtype) -> int:
@@ -263,10 +331,17 @@ def rmsn_unfused_bwd_workspace_bytes(M, N, dtype) -> int:
 
 
 def rmsn_unfused_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream=None) -> None:
-    _check("rmsn_unfused_bwd", lib.rmsn_unfused_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(rstd), int(M), int(N),
-                                                    int(dtype), _ptr(dx), _ptr(dw), _ptr(workspace),
+    mn = _mn(M, N)
+    _check("rmsn_unfused_bwd", lib.rmsn_unfused_bwd(_arg(x, "x", "act", dtype, mn),
+                                                    _arg(w, "w", "weight", dtype, int(N)),
+                                                    _arg(dy, "dy", "act", dtype, mn),
+                                                    _arg(rstd, "rstd", "f32", count=int(M)), int(M), int(N),
+                                                    int(dtype), _arg(dx, "dx", "act", dtype, mn),
+                                                    _arg(dw, "dw", "f32", count=int(N)),
+                                                    _arg(workspace, "workspace", nbytes=int(workspace_bytes)),
                                                     int(workspace_bytes), _stream(stream)))
 
 
 def rmsn_add(a, b, c, n, dtype, stream=None) -> None:
-    _check("rmsn_add", lib.rmsn_add(_ptr(a), _ptr(b), _ptr(c), int(n), int(dtype), _stream(stream)))
+    _check("rmsn_add", lib.rmsn_add(_arg(a, "a", "act", dtype, int(n)), _arg(b, "b", "act", dtype, int(n)),
+                                    _arg(c, "c", "act", dtype, int(n)), int(n), int(dtype), _stream(stream)))

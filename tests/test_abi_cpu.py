@@ -290,3 +290,45 @@ def test_select_config_argument_errors():
         rn.rmsnorm_select_config(4, 8, 5, 0, 1, 256, 1)
     with pytest.raises(rn.RmsnormError):
         rn.rmsnorm_select_config(4, 8, rn.F32, 2, 1, 256, 1)
+
+
+def test_binding_refuses_bad_tensors():
+    """The binding passes tensors as raw pointers, so it checks them first: on
+    the GPU, contiguous, of the format's dtype, large enough. These all fail
+    before any call into the library (no GPU needed for the first ones)."""
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    w = torch.zeros(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="not on the GPU"):
+        rn.rmsnorm_fwd(x, w, 1e-5, 4, 8, rn.BF16, x, None)
+    with pytest.raises(TypeError, match="expected a torch tensor"):
+        rn.rmsnorm_fwd([1, 2], FAKE, 1e-5, 4, 8, rn.BF16, FAKE, None)
+    # integers (device addresses) and None pass through unchecked
+    assert rn._arg(FAKE, "x", "act", rn.BF16, 32) == FAKE and rn._arg(None, "rstd", "f32", count=4) is None
+
+
+def test_binding_tensor_checks_logic():
+    """The checks themselves, on CPU tensors made to look like GPU ones."""
+    import torch
+
+    class FakeCuda(torch.Tensor):
+        @property
+        def is_cuda(self):
+            return True
+
+    def t(*shape, dtype=torch.bfloat16):
+        return torch.zeros(*shape, dtype=dtype).as_subclass(FakeCuda)
+
+    with pytest.raises(TypeError, match="dtype"):
+        rn._arg(t(4, 8, dtype=torch.float32), "x", "act", rn.BF16, 32)
+    with pytest.raises(TypeError, match="dtype"):
+        rn._arg(t(8), "w", "weight", rn.BF16_WF32, 8)          # fp32 weights expected
+    with pytest.raises(ValueError, match="elements"):
+        rn._arg(t(3, 8), "y", "act", rn.BF16, 32)               # short output
+    with pytest.raises(ValueError, match="not contiguous"):
+        rn._arg(t(8, 4).t(), "x", "act", rn.BF16, 32)
+    with pytest.raises(ValueError, match="bytes"):
+        rn._arg(t(10, dtype=torch.float32), "workspace", nbytes=64)
+    ok = t(4, 8)
+    assert rn._arg(ok, "x", "act", rn.BF16, 32) == ok.data_ptr()
+    assert rn._arg(ok, "x", "act", 9, 32) == ok.data_ptr()   # unknown format: the library reports it

@@ -1,0 +1,28 @@
+"""The library through its C ABI alone: tests/c_abi/rmsn_c_check, a C++
+program with no Python or torch in its process, runs the forward and the
+backward on hipMalloc buffers for bf16 and fp32 shapes (vector, wide-row,
+narrow-row and scalar kernels) and checks every output element against the
+fp64 oracle it links. Built by the repository's build step."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+BINARY = os.path.join(os.path.dirname(__file__), "c_abi", "rmsn_c_check")
+
+
+def test_c_abi_program_matches_oracle():
+    assert os.path.exists(BINARY), f"{BINARY} is not built: run __graft_entry__.build()"
+    res = subprocess.run([BINARY], capture_output=True, text=True, timeout=120)
+    print(res.stdout[-3000:], flush=True)
+    assert res.returncode == 0, f"rmsn_c_check failed ({res.returncode}):\n{res.stdout[-3000:]}\n{res.stderr[-2000:]}"
+    assert res.stdout.strip().endswith("ok")
