@@ -119,8 +119,15 @@ struct Elem<bf16_t> {
 
 __device__ __forceinline__ float f16_lo(uint32_t d) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(d & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t d) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> 16)); }
+// The fp32 values are rounded once, to nearest even, to fp16. The empty asm
+// makes them opaque fp32 registers first: otherwise the compiler may fold the
+// conversion into the fma that produced them (v_fma_mixlo/mixhi_f16, which
+// rounds the exact fma result to fp16), and whether it does depends on the
+// code around the call, so two kernels computing the same fp32 value could
+// store different fp16 bits.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    f16x2 v = {(_Float16)lo, (_Float16)hi};  // round to nearest even (v_cvt_f16_f32)
+    asm("" : "+v"(lo), "+v"(hi));
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -129,6 +136,7 @@ struct Elem<f16_t> {
     static constexpr int kPerVec = 8;
     static __device__ __forceinline__ float load(const f16_t *p) { return (float)__builtin_bit_cast(_Float16, p->bits); }
     static __device__ __forceinline__ void store(f16_t *p, float v) {
+        asm("" : "+v"(v));  // one rounding of the fp32 value, as in pack_f16x2
         p->bits = __builtin_bit_cast(uint16_t, (_Float16)v);
     }
     static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[8]) {
