@@ -84,8 +84,9 @@ typedef struct {
     int32_t vecs_per_lane;   /* 16-byte vectors each lane holds per row (vector path) */
     int32_t wg_threads;      /* workgroup size */
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
-    int32_t prefetch;        /* 1: the next row block's loads are issued before the current
-                                block's arithmetic (register double buffer) */
+    int32_t prefetch;        /* row blocks whose loads are issued before the current block's
+                                arithmetic (a register ring): 0 or 1; the backward also 2 for
+                                one vector per lane */
     int32_t stream_loads;    /* forward, rows of 64 lanes or more: 1 when the row loads carry the
                                 non-temporal hint (the ladder sets it; an explicit 0 suits inputs
                                 that are still cache-resident); ignored by the backward */

@@ -66,7 +66,8 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     block is prefetched below 1024 lanes per row; at 1024 lanes (one or
 //     two vectors per lane) only when each workgroup walks at most 16 rows:
 //     over longer walks the second buffer costs more occupancy than it
-//     hides. Measured over 39 shapes (M 1024..1M, N 128..32768) against the
+//     hides. Rows of 512 or 1024 well-filled lanes instead prefetch two
+//     blocks with one workgroup per compute unit (see deep_prefetch). Measured over 39 shapes (M 1024..1M, N 128..32768) against the
 //     earlier rules (workgroup = row, 5% partial cap, no prefetch at 1024
 //     lanes): 5% faster by geometric mean, up to 21% at mid-size M, within
 //     1% at 16384 x 4096. Rows of more than 1024 vectors: 16-bit
@@ -146,11 +147,26 @@ void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config
     set_vector_shape(lpr, vpt, wg, lpr < kMaxVecLanes ? 1 : 0, c);
 }
 
-// Backward prefetch at 1024 lanes per row (one or two vectors per lane; the
-// prefetching kernels with more vectors spill): on when each workgroup walks
-// at most kShortWalk rows. Needs the grid, so it runs after ladder_grid.
-void ladder_prefetch(int64_t M, int is_bwd, rmsnorm_config *c) {
-    if (is_bwd && c->vector_path == 1 && c->lanes_per_row == kMaxVecLanes && c->vecs_per_lane <= 2)
+// Backward rows of 512 or 1024 lanes with one vector per lane and at least
+// 3/4 of the lanes busy: two row blocks prefetched and one workgroup per
+// compute unit (half the partial rows). Measured against two workgroups per
+// CU with one block prefetched: 1.3-7.6% faster at 4096..65536 rows of
+// 4096..8192 columns (16384 x 4096: 71.2 -> 69.3 us); at 5120 columns (5/8
+// of 1024 lanes busy) 6.5% slower, hence the lane condition.
+bool deep_prefetch(int is_bwd, int64_t N, int dtype, const rmsnorm_config *c) {
+    const int64_t nvec = N * elem_size(dtype) / 16;
+    return is_bwd && c->vector_path == 1 && c->vecs_per_lane == 1 && c->lanes_per_row >= 512 &&
+           4 * nvec >= 3 * (int64_t)c->lanes_per_row;
+}
+
+// Backward prefetch depth. The deep shapes above: 2. Otherwise at 1024 lanes
+// per row (one or two vectors per lane; the prefetching kernels with more
+// vectors spill): 1 when each workgroup walks at most kShortWalk rows, else 0.
+// Needs the grid, so it runs after ladder_grid.
+void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config *c) {
+    if (deep_prefetch(is_bwd, N, dtype, c))
+        c->prefetch = 2;
+    else if (is_bwd && c->vector_path == 1 && c->lanes_per_row == kMaxVecLanes && c->vecs_per_lane <= 2)
         c->prefetch = M <= kShortWalk * c->grid ? 1 : 0;
 }
 
@@ -172,7 +188,10 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int num_cus, int b
         c->stream_loads = (c->vector_path == 1 && c->lanes_per_row >= 64 && in_bytes >= kStreamMinBytes) ? 1 : 0;
     } else {
         const int64_t cus = num_cus > 0 ? num_cus : 1;
-        int64_t want = (c->vector_path == kWidePath ? 1 : c->lanes_per_row < 64 ? 3 : 2) * cus;
+        int64_t want = (c->vector_path == kWidePath || deep_prefetch(is_bwd, N, dtype, c) ? 1
+                        : c->lanes_per_row < 64                                     ? 3
+                                                                                    : 2) *
+                       cus;
         // partial rows are written once and read once (8 * N bytes each); at
         // most 1/kPartialShare of the 3 * M * N * elem algorithmic bytes, so
         // at most 3 * M * elem / (8 * kPartialShare) rows (N cancels)
@@ -257,7 +276,7 @@ int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, bool aligned, 
     st = occupancy(k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, cus, blocks, c);
-    ladder_prefetch(M, is_bwd, c);
+    ladder_prefetch(M, N, dtype, is_bwd, c);
     k = kernel_for(*c, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     if (fn) *fn = k;
@@ -288,7 +307,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         const int64_t nvec = N * elem_size(dtype) / 16;
         if (!vector_ok(N, dtype, aligned)) return RMSN_ECONFIG;
         if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
-        if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > 1)
+        if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > 2)
             return RMSN_ECONFIG;
         if (req->wg_threads > 0 && (req->wg_threads % req->lanes_per_row) != 0) return RMSN_ECONFIG;
         if (req->vector_path == kWidePath &&
@@ -426,7 +445,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     std::memset(out, 0, sizeof *out);
     ladder_shape(N, dtype, is_bwd, aligned != 0, out);
     ladder_grid(M, N, dtype, is_bwd, num_cus, blocks_per_cu, out);
-    ladder_prefetch(M, is_bwd, out);
+    ladder_prefetch(M, N, dtype, is_bwd, out);
     return RMSN_OK;
 }
 

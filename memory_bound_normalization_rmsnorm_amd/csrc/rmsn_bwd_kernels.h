@@ -30,17 +30,20 @@
 namespace rmsn {
 
 // 16-byte vectors a lane keeps per row slot: x, dy (and dh), the weights, and
-// the prefetched copies.
-template <typename T, typename TW, bool RES, bool PF>
+// the PF prefetched copies.
+template <typename T, typename TW, bool RES, int PF>
 constexpr int bwd_packed_per_slot() {
     constexpr int in = RES ? 3 : 2;
-    return in + WeightVec<T, TW>::kVecs + (PF ? in : 0);
+    return in * (1 + PF) + WeightVec<T, TW>::kVecs;
 }
 
-template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, bool PF>
+// PF: row blocks loaded ahead of the one being computed (0, 1 or 2; a
+// register ring, the loop unrolled so every slot index is static).
+template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, int PF>
 __global__ void __launch_bounds__(WG)
 __attribute__((amdgpu_waves_per_eu(waves_for(VPT * bwd_packed_per_slot<T, TW, RES, PF>(),
-                                             VPT * Elem<T>::kPerVec, VPT, WG, RES ? 2 * Elem<T>::kPerVec : 0))))
+                                             VPT * Elem<T>::kPerVec, VPT, WG,
+                                             (RES ? 2 * Elem<T>::kPerVec : 0) + (PF == 2 ? 2 * Elem<T>::kPerVec : 0)))))
 bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
         const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
         int32_t N, int32_t nvec) {
@@ -102,30 +105,11 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
     int parity = 0;
     const int64_t step = (int64_t)gridDim.x * RPW;
     int64_t base = (int64_t)blockIdx.x * RPW;
-    u32x4 xn[VPT], gn[VPT], hn[VPT];  // prefetched next block (PF)
-    float rn = 0.f;
-    if constexpr (PF) load_block(base, xn, gn, hn, rn);
-    for (; base < M; base += step) {
+
+    // dx and the dW sums of the block at `base`, from its loaded vectors
+    auto compute = [&](int64_t base, u32x4 (&xv)[VPT], u32x4 (&gv)[VPT], u32x4 (&hv)[VPT], float r) {
         const uint32_t rows = rows_at(base);
         const Buf db(dx + base * N, rows * row_bytes);
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) wv[v].keep();
-
-        u32x4 xv[VPT], gv[VPT], hv[VPT];
-        float r;
-        if constexpr (PF) {
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) {
-                xv[v] = xn[v];
-                gv[v] = gn[v];
-                if constexpr (RES) hv[v] = hn[v];
-            }
-            r = rn;
-            load_block(base + step, xn, gn, hn, rn);
-        } else {
-            load_block(base, xv, gv, hv, r);
-        }
-
         float s = 0.f;
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
@@ -163,6 +147,59 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
                 for (int k = 0; k < EPV; ++k) o[k] += fh[k];
             }
             db.store16<RMSN_BWD_STORE_AUX>(off[v], E::pack(o));
+        }
+    };
+    auto copy = [&](u32x4 (&xo)[VPT], u32x4 (&go)[VPT], u32x4 (&ho)[VPT], const u32x4 (&xi)[VPT],
+                    const u32x4 (&gi)[VPT], const u32x4 (&hi)[VPT]) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            xo[v] = xi[v];
+            go[v] = gi[v];
+            if constexpr (RES) ho[v] = hi[v];
+        }
+    };
+    auto pin_w = [&]() {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) wv[v].keep();
+    };
+
+    u32x4 xv[VPT], gv[VPT], hv[VPT];  // the block being computed
+    float r;
+    if constexpr (PF == 0) {
+        for (; base < M; base += step) {
+            pin_w();
+            load_block(base, xv, gv, hv, r);
+            compute(base, xv, gv, hv, r);
+        }
+    } else if constexpr (PF == 1) {
+        u32x4 xa[VPT], ga[VPT], ha[VPT];  // the next block
+        float ra;
+        load_block(base, xa, ga, ha, ra);
+        for (; base < M; base += step) {
+            pin_w();
+            copy(xv, gv, hv, xa, ga, ha);
+            r = ra;
+            load_block(base + step, xa, ga, ha, ra);
+            compute(base, xv, gv, hv, r);
+        }
+    } else {
+        static_assert(PF == 2, "prefetch depth 0, 1 or 2");
+        u32x4 xa[VPT], ga[VPT], ha[VPT], xb[VPT], gb[VPT], hb[VPT];  // the next two blocks
+        float ra, rb;
+        load_block(base, xa, ga, ha, ra);
+        load_block(base + step, xb, gb, hb, rb);
+        for (; base < M; base += 2 * step) {
+            pin_w();
+            copy(xv, gv, hv, xa, ga, ha);
+            r = ra;
+            load_block(base + 2 * step, xa, ga, ha, ra);
+            compute(base, xv, gv, hv, r);
+            if (base + step >= M) break;
+            pin_w();
+            copy(xv, gv, hv, xb, gb, hb);
+            r = rb;
+            load_block(base + 3 * step, xb, gb, hb, rb);
+            compute(base + step, xv, gv, hv, r);
         }
     }
 

@@ -45,6 +45,12 @@
 #define RMSN_WIDE_SHAPES_32(X) X(2, 0) X(2, 1) X(3, 0) X(3, 1) X(4, 0) X(4, 1) X(5, 0) X(5, 1) \
     X(6, 0) X(7, 0) X(8, 0)
 
+// Backward kernels with two row blocks prefetched (depth 2), for the shapes the
+// backward ladder uses with one vector per lane.
+#define RMSN_BWD_DEEP_SHAPES(X) X(1, 1, 256, 2) X(2, 1, 256, 2) X(4, 1, 256, 2) X(8, 1, 256, 2) \
+    X(16, 1, 256, 2) X(32, 1, 256, 2) X(64, 1, 1024, 2) X(128, 1, 1024, 2) X(256, 1, 1024, 2)   \
+    X(512, 1, 512, 2) X(1024, 1, 1024, 2)
+
 namespace rmsn {
 
 template <int N>

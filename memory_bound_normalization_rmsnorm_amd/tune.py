@@ -78,7 +78,8 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             row_blocks = -(-M // rpw)
             grids = {row_blocks, -(-row_blocks // 2)} | {k * num_cus for k in (1, 2, 3, 4)}
             streams = (0, 1) if (not is_bwd and lpr >= 64) else (0,)
-            for pf in (0, 1):
+            depths = (0, 1, 2) if (is_bwd and vpt == 1) else (0, 1)  # depth 2: backward, one vector per lane
+            for pf in depths:
                 for g in sorted(x for x in grids if 1 <= x <= min(row_blocks, 1 << 20)):
                     for sl in streams:
                         out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt,

@@ -122,27 +122,34 @@ def test_ladder_covers_new_formats(dtype):
 
 def test_ladder_backward_grid_and_prefetch():
     """Partial rows (written and read once, 8 N bytes each) stay within 1/6 of
-    the algorithmic bytes, never below one workgroup per CU; 1024-lane rows
-    prefetch only when each workgroup walks at most 16 rows."""
-    # bf16 4096 x 4096: cap = 6*4096*4096 / 6 / (8*4096) = 512 -> 2 per CU
-    assert cfg(4096, 4096, rn.BF16, 1)["grid"] == 512
-    # bf16 1024 x 4096: cap 128 -> one per CU
-    assert cfg(1024, 4096, rn.BF16, 1)["grid"] == 256
+    the algorithmic bytes, never below one workgroup per CU. Rows of 512 or
+    1024 lanes with 3/4 of them busy prefetch two row blocks with one
+    workgroup per CU; other 1024-lane rows prefetch one block only when each
+    workgroup walks at most 16 rows."""
+    # bf16 4096 x 2048 (256 lanes): cap = 6*4096*2048 / 6 / (8*2048) = 512 -> 2 per CU
+    assert cfg(4096, 2048, rn.BF16, 1)["grid"] == 512
+    # bf16 1024 x 2048: cap 128 -> one per CU
+    assert cfg(1024, 2048, rn.BF16, 1)["grid"] == 256
     # below one row block per CU: the row blocks
     assert cfg(100, 4096, rn.BF16, 1)["grid"] == 100
-    # 1024 lanes: 4096 rows over 512 workgroups (8 each) prefetch, 16384 over 512 (32) do not
-    a, b = cfg(4096, 8192, rn.BF16, 1), cfg(16384, 8192, rn.BF16, 1)
+    # deep prefetch: 512 lanes (4096 columns), 1024 lanes (8192, 7168 columns), fp32 4096
+    for M, N, dt, lpr in ((4096, 4096, rn.BF16, 512), (16384, 4096, rn.BF16, 512), (16384, 8192, rn.BF16, 1024),
+                          (4096, 7168, rn.BF16, 1024), (16384, 4096, rn.F32, 1024)):
+        c = cfg(M, N, dt, 1)
+        assert (c["lanes_per_row"], c["vecs_per_lane"], c["prefetch"], c["grid"]) == (lpr, 1, 2, 256), (M, N)
+    # 5120 columns fill 5/8 of 1024 lanes: the short-walk rule (4096 rows over 512 prefetch, 16384 do not)
+    a, b = cfg(4096, 5120, rn.BF16, 1), cfg(16384, 5120, rn.BF16, 1)
     assert (a["lanes_per_row"], a["grid"], a["prefetch"]) == (1024, 512, 1)
     assert (b["lanes_per_row"], b["grid"], b["prefetch"]) == (1024, 512, 0)
-    # fp32, two vectors per lane: the same rule; 3 or more never prefetch
+    # fp32, two vectors per lane: the short-walk rule; 3 or more never prefetch
     assert cfg(4096, 8192, rn.F32, 1)["prefetch"] == 1
     assert cfg(4096, 12288, rn.F32, 1)["prefetch"] == 0
-    # rows of 64..256 lanes: 1024-lane workgroups, prefetching; 512 lanes: their own, prefetching
+    # rows of 64..256 lanes: 1024-lane workgroups, prefetching one block
     for N, lpr in ((512, 64), (1024, 128), (2048, 256)):
         c = cfg(16384, N, rn.BF16, 1)
         assert (c["lanes_per_row"], c["wg_threads"], c["rows_per_wg"], c["prefetch"]) == (lpr, 1024, 1024 // lpr, 1)
     c = cfg(16384, 4096, rn.BF16, 1)
-    assert (c["lanes_per_row"], c["wg_threads"], c["prefetch"], c["grid"]) == (512, 512, 1, 512)
+    assert (c["lanes_per_row"], c["wg_threads"], c["prefetch"], c["grid"]) == (512, 512, 2, 256)
 
 
 @pytest.mark.parametrize("N,dtype,vpt,pf", [
@@ -262,10 +269,10 @@ def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
 
 def test_ladder_grid_and_workspace_shape():
     # backward: two workgroups per compute unit, one fp32 partial row each
-    c = cfg(16384, 4096, rn.BF16, 1, cus=256, blocks=2)
-    assert c["grid"] == 512 and c["partial_rows"] == 512 and c["partial_stride"] == 4096 and c["prefetch"] == 1
+    c = cfg(16384, 2048, rn.BF16, 1, cus=256, blocks=2)
+    assert c["grid"] == 512 and c["partial_rows"] == 512 and c["partial_stride"] == 2048 and c["prefetch"] == 1
     # ... capped by residency
-    assert cfg(16384, 4096, rn.BF16, 1, cus=256, blocks=1)["grid"] == 256
+    assert cfg(16384, 2048, rn.BF16, 1, cus=256, blocks=1)["grid"] == 256
     # ... fewer when the partial rows would exceed 1/6 of the bytes, never below the CUs
     assert cfg(2048, 4096, rn.BF16, 1, cus=256, blocks=2)["grid"] == 256
     # ... the wide-row kernel: one per compute unit

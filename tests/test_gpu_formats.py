@@ -324,3 +324,33 @@ def test_every_wide_kernel(fmt, residual):
                                     prefetch=0, grid=3)
             dx2, dw2 = gpu_bwd(x, w, dy, rstd, act, cfg=reg)
             assert np.array_equal(dx, dx2) and np.array_equal(dw.view(np.uint32), dw2.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("residual", [False, True])
+def test_every_deep_prefetch_kernel_formats(fmt, residual):
+    """Depth-2 prefetch backward kernels of every format, plain and residual."""
+    act, wst, code = FORMATS[fmt]
+    epv = 4 if act == "f32" else 8
+    for lpr, wg in ((1, 256), (16, 256), (64, 1024), (256, 1024), (512, 512), (1024, 1024)):
+        nvec = max(1, lpr // 2 + 1) if lpr > 1 else 1
+        M, N = 5 * (wg // lpr) + 1, nvec * epv
+        cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=1, wg_threads=wg, prefetch=2,
+                                grid=2)
+        _say(f"deep prefetch lpr={lpr} wg={wg} N={N} M={M} {fmt} residual={residual}")
+        _, _, x, w, dy = _case(M, N, fmt, seed=9500 + lpr)
+        eps = si.eps_f32(1e-6)
+        if residual:
+            res = si.random_tensor((M, N), act, seed=9600 + lpr)
+            dh = si.random_tensor((M, N), act, seed=9700 + lpr, scale=1e-2)
+            h, _, rstd = gpu_fwd_residual(x, res, w, eps, act)
+            dx, dw = gpu_bwd(h, w, dy, rstd, act, cfg=cfg, dh=dh)
+            odx, orr = oracle.bwd_dx(x, w, dy, eps, act, res=res, dh=dh, wdtype=wst)
+            check_rows(dx, odx, act, "dx (deep, residual)", floor=term_rms(h, w, dy, orr, act, dh=dh))
+            check_dw(dw, oracle.bwd_dw(x, dy, eps, act, res=res), act, "dW (deep, residual)")
+        else:
+            _, rstd = gpu_fwd(x, w, eps, act)
+            dx, dw = gpu_bwd(x, w, dy, rstd, act, cfg=cfg)
+            odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
+            check_rows(dx, odx, act, "dx (deep)", floor=term_rms(x, w, dy, orr, act))
+            check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act, "dW (deep)")

@@ -299,3 +299,24 @@ def test_beyond_4gib_tensors():
     assert np.all(err <= bound), f"dW: max err {err.max()}"
     del x, dy, y, dx, ws
     torch.cuda.empty_cache()
+
+
+DEEP_SHAPES = [(1, 256), (2, 256), (4, 256), (8, 256), (16, 256), (32, 256), (64, 1024), (128, 1024),
+               (256, 1024), (512, 512), (1024, 1024)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_deep_prefetch_kernel(dtype):
+    """The backward kernels with two row blocks prefetched, forced through
+    *_with_config: a ragged row, 6 row blocks over a grid of 2, so each
+    workgroup walks 3 blocks (both ring slots, and the exit after the first)."""
+    epv = 4 if dtype == "f32" else 8
+    for lpr, wg in DEEP_SHAPES:
+        nvec = max(1, lpr // 2 + 1) if lpr > 1 else 1
+        N = nvec * epv
+        M = 5 * (wg // lpr) + 1
+        cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=1, wg_threads=wg, prefetch=2,
+                                grid=2)
+        x, w, dy = si.random_case(M, N, dtype, seed=lpr * 31 + wg, dy_scale=1e-2)
+        _say(f"deep prefetch lpr={lpr} wg={wg} N={N} M={M} {dtype}")
+        full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_b=cfg)
