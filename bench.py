@@ -62,7 +62,8 @@ def parse_args(argv=None):
     ap.add_argument("--cells", default="all", help="cells mode: comma-separated groups (configs, formats, "
                     "residual, latency, pages) or all")
     ap.add_argument("--mode", default="bench", choices=["bench", "kernels", "copy", "cells"],
-                    help="bench: full run; kernels: only the timed steps (for profilers); "
+                    help="bench: full run; kernels: the warmup steps, then each kernel's graph replays "
+                         "(eager batches with --eager-only), for profilers; "
                          "copy: one probe copy of --probe-gib (counter calibration)")
     ap.add_argument("--out-dir", default=os.environ.get("RMSN_BENCH_OUT", os.path.join(ROOT, "bench_out")))
     return ap.parse_args(argv)
@@ -370,6 +371,10 @@ def main(argv=None):
     # every single launch would add ~2 us of event processing per launch.)
     K, W = args.steps, args.warmup
     parts = [0] * R
+    # --mode kernels launches only what the per-kernel figures time (the
+    # warmup steps, then the graph replays; eager batches with --eager-only),
+    # so a profiler's per-kernel averages cover the same launches
+    kernels_only = args.mode == "kernels"
 
     def step(k):
         fwd(sets[k % R])
@@ -378,16 +383,18 @@ def main(argv=None):
     for k in range(W):
         step(k)
     torch.cuda.synchronize()
-    e0, e1 = timer.event(), timer.event()
-    t_start = time.perf_counter()
-    e0.record()
-    for k in range(K):
-        step(k)
-    e1.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    step_event_ms = e0.elapsed_time(e1) / K
-    ms_per_step = elapsed * 1e3 / K
+    ms_per_step = step_event_ms = None
+    if not kernels_only:
+        e0, e1 = timer.event(), timer.event()
+        t_start = time.perf_counter()
+        e0.record()
+        for k in range(K):
+            step(k)
+        e1.record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        step_event_ms = e0.elapsed_time(e1) / K
+        ms_per_step = elapsed * 1e3 / K
 
     def batch(fn):
         a, b = timer.event(), timer.event()
@@ -399,9 +406,11 @@ def main(argv=None):
         return a.elapsed_time(b) * 1e3 / K
 
     def graph_batch(fn, outputs, replays=3):
-        """Per-launch us of K launches of fn captured in a HIP graph; outputs()
-        lists the tensors the last launch writes, checked against eager."""
-        for k in range(K):
+        """Per-launch us of K launches of fn captured in a HIP graph: the median
+        of `replays` timed replays after one untimed one. outputs() lists the
+        tensors the last launch writes; every replay's are checked against the
+        eager launches' (the last R launches of the sequence, which write them)."""
+        for k in range(max(0, K - R), K):
             fn(k)
         torch.cuda.synchronize()
         ref = [t.clone() for t in outputs()]
@@ -409,6 +418,8 @@ def main(argv=None):
         with torch.cuda.graph(graph):
             for k in range(K):
                 fn(k)
+        graph.replay()
+        torch.cuda.synchronize()
         times = []
         for _ in range(replays):
             for t in outputs():
@@ -431,9 +442,11 @@ def main(argv=None):
         parts[k % R] = bwd_rows(sets[(k + R // 2) % R])
 
     last = (K - 1) % R
-    f_eager = batch(lambda k: fwd(sets[k % R]))
-    r_eager = batch(rows_k)
-    c_eager = batch(lambda k: combine(parts[k % R]))
+    f_eager = r_eager = c_eager = None
+    if args.eager_only or not kernels_only:
+        f_eager = batch(lambda k: fwd(sets[k % R]))
+        r_eager = batch(rows_k)
+        c_eager = batch(lambda k: combine(parts[k % R]))
     if args.eager_only:
         f_us, r_us, c_us = f_eager, r_eager, c_eager
     else:
@@ -441,10 +454,15 @@ def main(argv=None):
         r_us = graph_batch(rows_k, lambda: (sets[(last + R // 2) % R]["dx"],
                                             ws[:parts[last] * ldp_floats].view(parts[last], ldp_floats)[:, :N]))
         c_us = graph_batch(lambda k: combine(parts[k % R]), lambda: (dw,))
-    log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step wall ({step_event_ms * 1e3:.1f} us by events); "
-        f"per launch (graph / eager): fwd {f_us:.1f} / {f_eager:.1f} us, bwd rows {r_us:.1f} / {r_eager:.1f} us, "
-        f"combine {c_us:.1f} / {c_eager:.1f} us")
-    eager = {"fwd_us": round(f_eager, 2), "bwd_rows_us": round(r_eager, 2), "combine_us": round(c_eager, 2)}
+    def us(v):
+        return "-" if v is None else f"{v:.1f}"
+
+    if ms_per_step is not None:
+        log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step wall ({step_event_ms * 1e3:.1f} us by events)")
+    log(f"per launch (graph / eager): fwd {us(f_us)} / {us(f_eager)} us, bwd rows {us(r_us)} / {us(r_eager)} us, "
+        f"combine {us(c_us)} / {us(c_eager)} us")
+    eager = None if f_eager is None else {"fwd_us": round(f_eager, 2), "bwd_rows_us": round(r_eager, 2),
+                                          "combine_us": round(c_eager, 2)}
 
     if args.mode == "kernels":
         print(json.dumps({"mode": "kernels", "steps": K, "ms_per_step": ms_per_step, "fwd_us": f_us,
