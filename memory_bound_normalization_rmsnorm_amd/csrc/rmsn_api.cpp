@@ -67,7 +67,9 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     two vectors per lane) only when each workgroup walks at most 16 rows:
 //     over longer walks the second buffer costs more occupancy than it
 //     hides. Rows of 512 or 1024 well-filled lanes instead prefetch two
-//     blocks with one workgroup per compute unit (see deep_prefetch). Measured over 39 shapes (M 1024..1M, N 128..32768) against the
+//     blocks with one workgroup per compute unit (see deep_prefetch). Some
+//     16-bit rows of 257 to 1023 vectors run on whole wavefronts rather than
+//     the next power of two (see rowwg_lanes). Measured over 39 shapes (M 1024..1M, N 128..32768) against the
 //     earlier rules (workgroup = row, 5% partial cap, no prefetch at 1024
 //     lanes): 5% faster by geometric mean, up to 21% at mid-size M, within
 //     1% at 16384 x 4096. Rows of more than 1024 vectors: 16-bit
@@ -88,6 +90,7 @@ constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialS
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
 constexpr int64_t kStreamMinBytes = int64_t(4) << 20;  // forward inputs from this size stream (one XCD's L2)
 constexpr int kBwdMaxVecs = 4;
+constexpr int64_t kRowWGMinVecs = 256;  // backward rows wider than this may run on whole wavefronts (rowwg_lanes)
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 void set_vector_shape(int64_t lpr, int64_t vpt, int wg, int pf, rmsnorm_config *c) {
@@ -110,11 +113,40 @@ void set_scalar_shape(rmsnorm_config *c) {
 
 bool vector_ok(int64_t N, int dtype, bool aligned) { return aligned && (N * elem_size(dtype)) % 16 == 0; }
 
+// A backward row on whole wavefronts whose count is not a power of two runs
+// on the kernels whose row is the whole workgroup (its size set at launch).
+bool row_is_wg(const rmsnorm_config &c) {
+    const int64_t l = c.lanes_per_row;
+    return c.vector_path == 1 && c.vecs_per_lane == 1 && l > 64 && l <= kMaxVecLanes && l % 64 == 0 &&
+           (l & (l - 1)) != 0 && c.wg_threads == l;
+}
+
 // Largest vectors per lane of the wide-row backward kernels: their dW sums
 // (vectors x 1024 lanes x elements per vector, fp32) fill at most 128 KiB.
 int64_t wide_max_vecs(int dtype) { return dtype == RMSN_F32 ? 8 : 4; }
 
-void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config *c) {
+// Lanes of a backward row on whole wavefronts (not a power of two), or 0
+// where the power-of-two row is kept. Measured on MI355X (bf16, M 4096 to
+// 65536, graph-timed, inputs not cache-resident) against the power-of-two
+// rows at their best prefetch depth and grid:
+//   320-384 lanes (2560-3072 columns): depth 2, two per CU, 4-12% faster;
+//   448 lanes: the 512-lane row is as fast or faster (kept);
+//   576-640 lanes: depth 2, one per CU, 7-8% faster when each workgroup walks
+//     at most kShortWalk rows; over longer walks the 1024-lane row without
+//     prefetch is within 2% either way (kept);
+//   704-768 lanes (6144 columns): depth 2, one per CU, 2-8% faster;
+//   832-960 lanes: the 1024-lane row is 1-4% faster (kept).
+// fp32 activations or weights measured as ties and keep the power-of-two row.
+int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
+    if ((dtype != RMSN_BF16 && dtype != RMSN_F16) || nvec <= kRowWGMinVecs || nvec >= kMaxVecLanes) return 0;
+    const int64_t lanes = (nvec + 63) / 64 * 64;
+    if ((lanes & (lanes - 1)) == 0) return 0;
+    if (lanes <= 384) return lanes;
+    if (lanes > 512 && lanes <= 768 && (lanes > 640 || M <= kShortWalk * cus)) return lanes;
+    return 0;
+}
+
+void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, bool aligned, int64_t cus, rmsnorm_config *c) {
     const int64_t nvec = N * elem_size(dtype) / 16;
     const int64_t vmax = is_bwd ? wide_max_vecs(dtype) : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
     if (!vector_ok(N, dtype, aligned) || nvec > kMaxVecLanes * vmax) {
@@ -133,6 +165,7 @@ void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config
         lpr = next_pow2(nvec);
     } else if (is_bwd) {
         lpr = nvec <= kMaxVecLanes ? next_pow2(nvec) : kMaxVecLanes;
+        if (const int64_t l = rowwg_lanes(M, nvec, dtype, cus)) lpr = l;
     } else {
         lpr = next_pow2((nvec + kFwdMaxVecs - 1) / kFwdMaxVecs);
         if (lpr < 64) lpr = 64;
@@ -153,10 +186,14 @@ void ladder_shape(int64_t N, int dtype, int is_bwd, bool aligned, rmsnorm_config
 // CU with one block prefetched: 1.3-7.6% faster at 4096..65536 rows of
 // 4096..8192 columns (16384 x 4096: 71.2 -> 69.3 us); at 5120 columns (5/8
 // of 1024 lanes busy) 6.5% slower, hence the lane condition.
-bool deep_prefetch(int is_bwd, int64_t N, int dtype, const rmsnorm_config *c) {
+// Rows on whole wavefronts (row_is_wg) always prefetch two blocks: two
+// workgroups per CU up to 384 lanes, one above (see rowwg_lanes).
+// Returns the workgroups per compute unit of a depth-2 shape, 0 otherwise.
+int deep_prefetch(int is_bwd, int64_t N, int dtype, const rmsnorm_config *c) {
+    if (!is_bwd || c->vector_path != 1 || c->vecs_per_lane != 1) return 0;
+    if (row_is_wg(*c)) return c->lanes_per_row <= 384 ? 2 : 1;
     const int64_t nvec = N * elem_size(dtype) / 16;
-    return is_bwd && c->vector_path == 1 && c->vecs_per_lane == 1 && c->lanes_per_row >= 512 &&
-           4 * nvec >= 3 * (int64_t)c->lanes_per_row;
+    return c->lanes_per_row >= 512 && 4 * nvec >= 3 * (int64_t)c->lanes_per_row ? 1 : 0;
 }
 
 // Backward prefetch depth. The deep shapes above: 2. Otherwise at 1024 lanes
@@ -188,10 +225,8 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int num_cus, int b
         c->stream_loads = (c->vector_path == 1 && c->lanes_per_row >= 64 && in_bytes >= kStreamMinBytes) ? 1 : 0;
     } else {
         const int64_t cus = num_cus > 0 ? num_cus : 1;
-        int64_t want = (c->vector_path == kWidePath || deep_prefetch(is_bwd, N, dtype, c) ? 1
-                        : c->lanes_per_row < 64                                     ? 3
-                                                                                    : 2) *
-                       cus;
+        const int deep = deep_prefetch(is_bwd, N, dtype, c);
+        int64_t want = (c->vector_path == kWidePath ? 1 : deep ? deep : c->lanes_per_row < 64 ? 3 : 2) * cus;
         // partial rows are written once and read once (8 * N bytes each); at
         // most 1/kPartialShare of the 3 * M * N * elem algorithmic bytes, so
         // at most 3 * M * elem / (8 * kPartialShare) rows (N cancels)
@@ -257,6 +292,10 @@ const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd, int res) 
         const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
         return e ? e->fn : nullptr;
     }
+    if (is_bwd && row_is_wg(c)) {
+        const KernelEntry *e = rmsn::bwd_vec_kernel(dtype, res, 0, 1, (int)kMaxVecLanes, c.prefetch);
+        return e ? e->fn : nullptr;
+    }
     const KernelEntry *e =
         is_bwd ? rmsn::bwd_vec_kernel(dtype, res, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch)
                : rmsn::fwd_vec_kernel(dtype, res, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch);
@@ -267,12 +306,12 @@ const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd, int res) 
 int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, bool aligned, rmsnorm_config *c,
             const void **fn) {
     std::memset(c, 0, sizeof *c);
-    ladder_shape(N, dtype, is_bwd, aligned, c);
-    const void *k = kernel_for(*c, dtype, is_bwd, res);
-    if (!k) return RMSN_ECONFIG;
     int cus = 0, blocks = 0;
     int st = device_info(&cus);
     if (st != RMSN_OK) return st;
+    ladder_shape(M, N, dtype, is_bwd, aligned, cus, c);
+    const void *k = kernel_for(*c, dtype, is_bwd, res);
+    if (!k) return RMSN_ECONFIG;
     st = occupancy(k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, cus, blocks, c);
@@ -443,7 +482,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     if (st != RMSN_OK) return st;
     if (!out || num_cus < 1 || blocks_per_cu < 1 || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
     std::memset(out, 0, sizeof *out);
-    ladder_shape(N, dtype, is_bwd, aligned != 0, out);
+    ladder_shape(M, N, dtype, is_bwd, aligned != 0, num_cus, out);
     ladder_grid(M, N, dtype, is_bwd, num_cus, blocks_per_cu, out);
     ladder_prefetch(M, N, dtype, is_bwd, out);
     return RMSN_OK;

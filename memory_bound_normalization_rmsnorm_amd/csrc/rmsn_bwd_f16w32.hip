@@ -8,10 +8,10 @@
 namespace rmsn {
 
 #define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&bwd_vec<f16_t, float, false, L, V, W, P>)},
-static const KernelEntry kPlain[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY) RMSN_BWD_DEEP_SHAPES(RMSN_ENTRY)};
+static const KernelEntry kPlain[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY) RMSN_BWD_DEEP_SHAPES(RMSN_ENTRY) RMSN_BWD_ROWWG_SHAPES(RMSN_ENTRY)};
 #undef RMSN_ENTRY
 #define RMSN_ENTRY(L, V, W, P) {L, V, W, P, reinterpret_cast<const void *>(&bwd_vec<f16_t, float, true, L, V, W, P>)},
-static const KernelEntry kResidual[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY) RMSN_BWD_DEEP_SHAPES(RMSN_ENTRY)};
+static const KernelEntry kResidual[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY) RMSN_BWD_DEEP_SHAPES(RMSN_ENTRY) RMSN_BWD_ROWWG_SHAPES(RMSN_ENTRY)};
 #undef RMSN_ENTRY
 
 #define RMSN_WIDE_ENTRY(V, P) {kWideLanes, V, kWideLanes, P, reinterpret_cast<const void *>(&bwd_wide<f16_t, float, false, V, (P != 0)>)},

@@ -39,6 +39,9 @@ constexpr int bwd_packed_per_slot() {
 
 // PF: row blocks loaded ahead of the one being computed (0, 1 or 2; a
 // register ring, the loop unrolled so every slot index is static).
+// LPR = 0: the row is the whole workgroup, whose size (a multiple of 64 up to
+// WG) is chosen at launch, so a row of 640 or 896 vectors runs on 10 or 14
+// wavefronts with every lane holding a vector (one vector per lane).
 template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, int PF>
 __global__ void __launch_bounds__(WG)
 __attribute__((amdgpu_waves_per_eu(waves_for(VPT * bwd_packed_per_slot<T, TW, RES, PF>(),
@@ -50,13 +53,16 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
     using E = Elem<T>;
     using WV = WeightVec<T, TW>;
     constexpr int EPV = E::kPerVec;
-    constexpr int RPW = WG / LPR;
-    static_assert(WG % LPR == 0, "workgroup must hold whole row groups");
-    __shared__ float slots[LPR > 64 ? 2 * (WG / 64) : 1];
+    constexpr bool kRowIsWG = LPR == 0;
+    constexpr int RPW = kRowIsWG ? 1 : WG / LPR;
+    static_assert(kRowIsWG || WG % LPR == 0, "workgroup must hold whole row groups");
+    static_assert(!kRowIsWG || VPT == 1, "a workgroup-sized row holds one vector per lane");
+    __shared__ float slots[LPR > 64 || kRowIsWG ? 2 * (WG / 64) : 1];
     __shared__ float comb[RPW > 1 ? WG * EPV : 1];
 
-    const int lane = threadIdx.x % LPR;
-    const int grp = threadIdx.x / LPR;
+    const int lpr = kRowIsWG ? (int)blockDim.x : LPR;
+    const int lane = kRowIsWG ? (int)threadIdx.x : (int)threadIdx.x % LPR;
+    const int grp = kRowIsWG ? 0 : (int)threadIdx.x / LPR;
     const float n = (float)N;
     const uint32_t row_bytes = (uint32_t)nvec * 16u;
 
@@ -67,7 +73,7 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
     WV wv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        const int idx = v * LPR + lane;
+        const int idx = v * lpr + lane;
         const bool in = idx < nvec;
         off[v] = in ? (uint32_t)grp * row_bytes + (uint32_t)idx * 16u : kOff;
         wv[v].load(wb, idx, in);
@@ -123,7 +129,10 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
                 acc[v][k] = __builtin_fmaf(fg[k] * fx[k], r, acc[v][k]);
             }
         }
-        s = row_sum<LPR, WG>(s, slots, parity);
+        if constexpr (kRowIsWG)
+            s = wg_sum<WG>(s, slots, parity);
+        else
+            s = row_sum<LPR, WG>(s, slots, parity);
         parity ^= 1;
         const float c = r * (r * (r * (s / n)));  // r^3 S/N without forming r^3 (underflows for rows near 1e15)
 #pragma unroll
@@ -207,7 +216,7 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
     if constexpr (RPW == 1) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const int idx = v * LPR + lane;
+            const int idx = v * lpr + lane;
             if (idx < nvec) {
                 float4 *dst = reinterpret_cast<float4 *>(prow + (int64_t)idx * EPV);
 #pragma unroll

@@ -330,4 +330,20 @@ __device__ __forceinline__ float row_sum(float v, float *slots, int parity) {
     }
 }
 
+// Sum over the whole workgroup, whose size (a multiple of 64, at most WG) is
+// set at launch: as row_sum with one row per workgroup, the wave partials
+// added in wave order. `slots` must hold 2 * (WG / 64) floats; `parity` as in
+// row_sum.
+template <int WG>
+__device__ __forceinline__ float wg_sum(float v, float *slots, int parity) {
+    v = group_sum<64>(v);
+    const int waves = (int)(blockDim.x >> 6);
+    float *buf = slots + parity * (WG / 64);
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float s = buf[0];
+    for (int k = 1; k < waves; ++k) s += buf[k];
+    return s;
+}
+
 }  // namespace rmsn

@@ -51,6 +51,13 @@
     X(16, 1, 256, 2) X(32, 1, 256, 2) X(64, 1, 1024, 2) X(128, 1, 1024, 2) X(256, 1, 1024, 2)   \
     X(512, 1, 512, 2) X(1024, 1, 1024, 2)
 
+// Backward kernels whose row is the whole workgroup, sized at launch to the
+// row's vectors rounded up to whole wavefronts (one vector per lane), for
+// rows of 256 to 1024 vectors that are not a power of two (640 lanes at 5120
+// 16-bit columns instead of 1024 with 3/8 idle), as (0, 1, launch bound,
+// prefetch depth).
+#define RMSN_BWD_ROWWG_SHAPES(X) X(0, 1, 1024, 1) X(0, 1, 1024, 2)
+
 namespace rmsn {
 
 template <int N>

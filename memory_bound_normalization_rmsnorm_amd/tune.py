@@ -45,6 +45,7 @@ BUILT = {1: (256,), 2: (256,), 4: (256,), 8: (256,), 16: (256,), 32: (256,), 64:
          128: (256, 512, 1024), 256: (256, 512, 1024), 512: (512, 1024), 1024: (1024,)}
 MAX_VPT = 8
 WIDE_LANES = 1024  # wide-row backward kernels (vector_path 2): 1024 lanes, dW sums in LDS
+ROWWG_MIN_VECS = 256  # backward rows wider than this may run on any whole number of wavefronts
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
 
@@ -58,7 +59,8 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
     partially used slot at most, crossed with grids: the row-block count,
     its halves, and 1-4 workgroups per compute unit; for backward rows of more
     than 1024 vectors also the wide-row kernels at one and two workgroups per
-    compute unit. Shapes that are not built fail at launch and are skipped.
+    compute unit, and for backward rows of 257 to 1024 vectors whose whole
+    wavefronts are not a power of two the workgroup-sized row kernels. Shapes that are not built fail at launch and are skipped.
     Pure host logic."""
     es = ELEM[dtype]
     if (N * es) % 16:
@@ -84,6 +86,14 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
                     for sl in streams:
                         out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=vpt,
                                                   wg_threads=wg, prefetch=pf, stream_loads=sl, grid=g))
+    # backward rows of 257 to 1024 vectors on whole wavefronts (not a power of
+    # two): the kernels whose row is the whole workgroup, one vector per lane
+    rowwg = -(-nvec // 64) * 64
+    if is_bwd and ROWWG_MIN_VECS < nvec <= WIDE_LANES and rowwg & (rowwg - 1):
+        for pf in (1, 2):
+            for g in sorted({k * num_cus for k in (1, 2, 3)} & set(range(1, M + 1))):
+                out.append(rmsnorm_config(vector_path=1, lanes_per_row=rowwg, vecs_per_lane=1, wg_threads=rowwg,
+                                          prefetch=pf, grid=g))
     wide_max = 8 if dtype == F32 else 4
     if is_bwd and WIDE_LANES < nvec <= WIDE_LANES * wide_max:
         vpt = -(-nvec // WIDE_LANES)

@@ -137,10 +137,14 @@ def test_ladder_backward_grid_and_prefetch():
                           (4096, 7168, rn.BF16, 1024), (16384, 4096, rn.F32, 1024)):
         c = cfg(M, N, dt, 1)
         assert (c["lanes_per_row"], c["vecs_per_lane"], c["prefetch"], c["grid"]) == (lpr, 1, 2, 256), (M, N)
-    # 5120 columns fill 5/8 of 1024 lanes: the short-walk rule (4096 rows over 512 prefetch, 16384 do not)
+    # 5120 columns: 640 whole-wavefront lanes over short walks (4096 rows), else
+    # 1024 lanes (5/8 busy) under the short-walk rule (16384 rows: no prefetch)
     a, b = cfg(4096, 5120, rn.BF16, 1), cfg(16384, 5120, rn.BF16, 1)
-    assert (a["lanes_per_row"], a["grid"], a["prefetch"]) == (1024, 512, 1)
+    assert (a["lanes_per_row"], a["wg_threads"], a["grid"], a["prefetch"]) == (640, 640, 256, 2)
     assert (b["lanes_per_row"], b["grid"], b["prefetch"]) == (1024, 512, 0)
+    # fp32 weights keep the power-of-two row: 4096 rows over 512 prefetch one block
+    c = cfg(4096, 5120, rn.BF16_WF32, 1)
+    assert (c["lanes_per_row"], c["grid"], c["prefetch"]) == (1024, 512, 1)
     # fp32, two vectors per lane: the short-walk rule; 3 or more never prefetch
     assert cfg(4096, 8192, rn.F32, 1)["prefetch"] == 1
     assert cfg(4096, 12288, rn.F32, 1)["prefetch"] == 0
@@ -231,7 +235,7 @@ def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
     (4096, rn.BF16, 0, 128, 4),
     (4096, rn.BF16, 1, 512, 1),
     (5120, rn.BF16, 0, 256, 3),
-    (5120, rn.BF16, 1, 1024, 1),
+    (5120, rn.BF16, 1, 640, 1),    # whole wavefronts (4096 rows: a short walk)
     (7168, rn.BF16, 0, 256, 4),
     (7168, rn.BF16, 1, 1024, 1),
     (8192, rn.BF16, 0, 256, 4),
@@ -339,3 +343,43 @@ def test_binding_tensor_checks_logic():
     ok = t(4, 8)
     assert rn._arg(ok, "x", "act", rn.BF16, 32) == ok.data_ptr()
     assert rn._arg(ok, "x", "act", 9, 32) == ok.data_ptr()   # unknown format: the library reports it
+
+
+@pytest.mark.parametrize("N,M,dtype,lanes,grid", [
+    (2560, 16384, rn.BF16, 320, 512),     # 320 vectors: whole wavefronts, two per CU
+    (3072, 16384, rn.F16, 384, 512),
+    (3584, 16384, rn.BF16, 512, 256),     # 448: the 512-lane row (deep prefetch) is kept
+    (4608, 4096, rn.BF16, 576, 256),      # 576-640: whole wavefronts on short walks only
+    (4608, 16384, rn.BF16, 1024, 512),
+    (6144, 65536, rn.BF16, 768, 256),     # 704-768: whole wavefronts, one per CU
+    (5632, 65536, rn.F16, 704, 256),
+    (7168, 16384, rn.BF16, 1024, 256),    # 832-960: the 1024-lane row is kept
+    (2560, 16384, rn.F32, 1024, 512),     # fp32 keeps the power-of-two row
+    (2560, 16384, rn.F16_WF32, 512, 512),
+])
+def test_ladder_whole_wavefront_rows(N, M, dtype, lanes, grid):
+    """Backward rows of 257 to 1023 16-bit vectors run on whole wavefronts
+    (a workgroup-sized row, depth-2 prefetch) where that measured faster than
+    the next power of two; elsewhere the power-of-two row is kept."""
+    c = cfg(M, N, dtype, 1)
+    assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["grid"]) == (1, lanes, 1, grid)
+    if lanes & (lanes - 1):
+        assert (c["wg_threads"], c["rows_per_wg"], c["prefetch"]) == (lanes, 1, 2)
+
+
+def test_explicit_whole_wavefront_config_checks():
+    """Workgroup-sized rows through *_with_config are checked before any HIP
+    call: the row must fit the lanes, hold one vector per lane, and the
+    workgroup must be the row."""
+    L, C = rn.lib, rn.rmsnorm_config
+
+    def bwd(**kw):
+        c = C(vector_path=1, lanes_per_row=640, vecs_per_lane=1, wg_threads=640, prefetch=2, grid=4)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return L.rmsnorm_bwd_with_config(FAKE, FAKE, FAKE, FAKE, 8, 5120, rn.BF16, FAKE, FAKE, FAKE, 1 << 30, c, None)
+
+    assert bwd(wg_threads=1280) == rn.ECONFIG               # two rows per workgroup: not built
+    assert bwd(vecs_per_lane=2) == rn.ECONFIG               # one vector per lane only
+    assert bwd(lanes_per_row=576, wg_threads=576) == rn.ECONFIG  # 576 lanes do not cover 640 vectors
+    assert bwd(prefetch=0) == rn.ECONFIG                    # depths 1 and 2 are built

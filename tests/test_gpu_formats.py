@@ -354,3 +354,36 @@ def test_every_deep_prefetch_kernel_formats(fmt, residual):
             odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
             check_rows(dx, odx, act, "dx (deep)", floor=term_rms(x, w, dy, orr, act))
             check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act, "dW (deep)")
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("residual", [False, True])
+def test_every_workgroup_row_kernel_formats(fmt, residual):
+    """Backward kernels whose row is the whole workgroup (sized at launch to
+    the row's whole wavefronts), every format, plain and residual, both
+    prefetch depths; a ragged last wavefront and 7 rows over a grid of 3."""
+    act, wst, code = FORMATS[fmt]
+    epv = 4 if act == "f32" else 8
+    for lanes in (384, 640, 896):
+        nvec = lanes - 21
+        M, N = 7, nvec * epv
+        _, _, x, w, dy = _case(M, N, fmt, seed=9800 + lanes)
+        eps = si.eps_f32(1e-6)
+        res = si.random_tensor((M, N), act, seed=9900 + lanes)
+        dh = si.random_tensor((M, N), act, seed=9950 + lanes, scale=1e-2)
+        for pf in (1, 2):
+            cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lanes, vecs_per_lane=1, wg_threads=lanes,
+                                    prefetch=pf, grid=3)
+            _say(f"workgroup row lanes={lanes} pf={pf} N={N} M={M} {fmt} residual={residual}")
+            if residual:
+                h, _, rstd = gpu_fwd_residual(x, res, w, eps, act)
+                dx, dw = gpu_bwd(h, w, dy, rstd, act, cfg=cfg, dh=dh)
+                odx, orr = oracle.bwd_dx(x, w, dy, eps, act, res=res, dh=dh, wdtype=wst)
+                check_rows(dx, odx, act, "dx (workgroup row, residual)", floor=term_rms(h, w, dy, orr, act, dh=dh))
+                check_dw(dw, oracle.bwd_dw(x, dy, eps, act, res=res), act, "dW (workgroup row, residual)")
+            else:
+                _, rstd = gpu_fwd(x, w, eps, act)
+                dx, dw = gpu_bwd(x, w, dy, rstd, act, cfg=cfg)
+                odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
+                check_rows(dx, odx, act, "dx (workgroup row)", floor=term_rms(x, w, dy, orr, act))
+                check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act, "dW (workgroup row)")

@@ -320,3 +320,29 @@ def test_every_deep_prefetch_kernel(dtype):
         x, w, dy = si.random_case(M, N, dtype, seed=lpr * 31 + wg, dy_scale=1e-2)
         _say(f"deep prefetch lpr={lpr} wg={wg} N={N} M={M} {dtype}")
         full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_b=cfg)
+
+
+# Backward rows of 257..1024 vectors on whole wavefronts that are not a power
+# of two: the kernels whose row is the whole workgroup, sized at launch.
+ROWWG_LANES = (320, 384, 448, 576, 640, 704, 832, 896, 960)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_workgroup_row_kernel(dtype):
+    """Workgroup-sized backward rows at every prefetch depth, forced through
+    *_with_config: the last wavefront partly empty, 7 rows over grids of 2 and
+    3 (workgroups walk 2 to 4 rows: both ring slots and the early exit); the
+    ladder's own choice at the same width as well."""
+    epv = 4 if dtype == "f32" else 8
+    for lanes in ROWWG_LANES:
+        nvec = lanes - 37
+        N, M = nvec * epv, 7
+        x, w, dy = si.random_case(M, N, dtype, seed=lanes * 3 + 1, dy_scale=1e-2)
+        for pf in (1, 2):
+            for grid in (2, 3):
+                cfg = rn.rmsnorm_config(vector_path=1, lanes_per_row=lanes, vecs_per_lane=1, wg_threads=lanes,
+                                        prefetch=pf, grid=grid)
+                _say(f"workgroup row lanes={lanes} pf={pf} grid={grid} N={N} M={M} {dtype}")
+                full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_b=cfg)
+        _say(f"workgroup row width, the ladder's own choice: N={N} {dtype}")
+        full_check(x, w, dy, si.eps_f32(1e-6), dtype)
