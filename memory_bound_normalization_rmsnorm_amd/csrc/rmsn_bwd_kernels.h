@@ -214,14 +214,20 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
 
     float *prow = partial + (int64_t)blockIdx.x * ldp;
     if constexpr (RPW == 1) {
+        const Buf pb(prow, (uint32_t)nvec * (uint32_t)(EPV * 4));
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int idx = v * lpr + lane;
             if (idx < nvec) {
-                float4 *dst = reinterpret_cast<float4 *>(prow + (int64_t)idx * EPV);
 #pragma unroll
-                for (int q = 0; q < EPV / 4; ++q)
-                    dst[q] = make_float4(acc[v][4 * q], acc[v][4 * q + 1], acc[v][4 * q + 2], acc[v][4 * q + 3]);
+                for (int q = 0; q < EPV / 4; ++q) {
+                    u32x4 o;
+                    o.x = as_u32(acc[v][4 * q]);
+                    o.y = as_u32(acc[v][4 * q + 1]);
+                    o.z = as_u32(acc[v][4 * q + 2]);
+                    o.w = as_u32(acc[v][4 * q + 3]);
+                    pb.store16<RMSN_BWD_PARTIAL_AUX>((uint32_t)(idx * EPV + 4 * q) * 4u, o);
+                }
             }
         }
     } else {
@@ -386,14 +392,21 @@ bwd_wide(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
         }
     }
 
-    float *prow = partial + (int64_t)blockIdx.x * ldp;
+    const Buf pb(partial + (int64_t)blockIdx.x * ldp, (uint32_t)nvec * (uint32_t)(EPV * 4));
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int idx = v * LPR + lane;
         if (idx < nvec) {
-            float4 *dst = reinterpret_cast<float4 *>(prow + (int64_t)idx * EPV);
 #pragma unroll
-            for (int q = 0; q < Q; ++q) dst[q] = acc[(v * Q + q) * LPR + lane];
+            for (int q = 0; q < Q; ++q) {
+                const float4 a = acc[(v * Q + q) * LPR + lane];
+                u32x4 o;
+                o.x = as_u32(a.x);
+                o.y = as_u32(a.y);
+                o.z = as_u32(a.z);
+                o.w = as_u32(a.w);
+                pb.store16<RMSN_BWD_PARTIAL_AUX>((uint32_t)(idx * EPV + 4 * q) * 4u, o);
+            }
         }
     }
 }

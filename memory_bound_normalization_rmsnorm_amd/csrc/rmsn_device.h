@@ -197,6 +197,9 @@ constexpr int kNonTemporal = 2;
 #ifndef RMSN_BWD_STORE_AUX
 #define RMSN_BWD_STORE_AUX 2
 #endif
+#ifndef RMSN_BWD_PARTIAL_AUX
+#define RMSN_BWD_PARTIAL_AUX 0  // the backward's partial dW rows (read back by the combine)
+#endif
 constexpr uint32_t kOff = 0x80000000u;  // an offset past every record count used here
 
 struct Buf {
