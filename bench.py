@@ -45,6 +45,7 @@ METRIC = "RMSNorm fwd/bwd achieved GB/s and % of measured HBM roofline, 1 MI355X
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 GIB = 1 << 30
 SETTLE_S = 0.25  # untimed steps before the warmup steps (clock settle after the CPU leg)
+CELL_SETTLE_S = 0.05  # untimed graph replays before each cell's timed replays
 
 
 def parse_args(argv=None):
@@ -738,13 +739,42 @@ def cell_ops(rn, variant, sets, w, dw, ws, ws_n, eps, M, N, code):
 
 
 def time_cell(torch, timer, op, outputs, R, replays=5):
-    """(graph per-call us, eager per-call us) for op over the rotation sets."""
+    """(graph per-call us, eager per-call us) for op over the rotation sets.
+    Two graph replays are checked first: every output is filled with NaN
+    before each and must come back equal to the eager call's. Then replays run
+    untimed for CELL_SETTLE_S (clock settle, as before the timed steps), then
+    `replays` back to back between HIP events (the median per call), then the
+    eager batch (K launches between one event pair)."""
     K = R * max(1, -(-16 // R))
-    # eager reference of the last call, then K eager launches between events
     for k in range(K):
         op(k % R)
     torch.cuda.synchronize()
     ref = [t.clone() for t in outputs((K - 1) % R)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(K):
+            op(k % R)
+    for _ in range(2):
+        for t in outputs((K - 1) % R):
+            t.fill_(float("nan"))  # a replay must rewrite every output
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outputs((K - 1) % R), ref):
+            if not torch.equal(t.view(torch.uint8) if t.dtype != torch.float32 else t.view(torch.int32),
+                               r.view(torch.uint8) if r.dtype != torch.float32 else r.view(torch.int32)):
+                raise RuntimeError("graph replay output differs from the eager call")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CELL_SETTLE_S:
+        graph.replay()
+        torch.cuda.synchronize()
+    ev = [timer.event() for _ in range(replays + 1)]
+    ev[0].record()
+    for i in range(replays):
+        graph.replay()
+        ev[i + 1].record()
+    ev[-1].synchronize()
+    times = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / K for i in range(replays)]
+    del graph
     e0, e1 = timer.event(), timer.event()
     e0.record()
     for k in range(K):
@@ -752,26 +782,6 @@ def time_cell(torch, timer, op, outputs, R, replays=5):
     e1.record()
     e1.synchronize()
     eager_us = e0.elapsed_time(e1) * 1e3 / K
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for k in range(K):
-            op(k % R)
-    times = []
-    for _ in range(replays):
-        for t in outputs((K - 1) % R):
-            t.fill_(float("nan"))  # a replay must rewrite every output
-        torch.cuda.synchronize()
-        a, b = timer.event(), timer.event()
-        a.record()
-        graph.replay()
-        b.record()
-        b.synchronize()
-        times.append(a.elapsed_time(b) * 1e3 / K)
-        for t, r in zip(outputs((K - 1) % R), ref):
-            if not torch.equal(t.view(torch.uint8) if t.dtype != torch.float32 else t.view(torch.int32),
-                               r.view(torch.uint8) if r.dtype != torch.float32 else r.view(torch.int32)):
-                raise RuntimeError("graph replay output differs from the eager call")
-    del graph
     return statistics.median(times), eager_us
 
 
