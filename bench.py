@@ -243,8 +243,9 @@ def size_matched_probes(torch, rn, nbytes, gib_total=1.5):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(json.dumps({"error": f"--gpus {args.gpus}: this RMSNorm build runs on one GPU only; "
-                                   "multi-GPU sharding is described in DESIGN.md and not run"}))
+        print(json.dumps({"error": f"--gpus {args.gpus}: the benchmark runs on one GPU only; "
+                                   "RMSNorm rows shard across GPUs with no communication except one "
+                                   "exchange of the N dW partial sums per GPU, which is not run here"}))
         return 2
     import numpy as np
     import torch
@@ -497,9 +498,16 @@ def main(argv=None):
     def flush():
         rn.rmsn_probe_read(fa, flush_n, fb, 0)
 
-    iso_f, _ = timer.median_ms(lambda: fwd(sets[0]), args.isolated_reps, between=flush)
-    iso_b, _ = timer.median_ms(lambda: combine(bwd_rows(sets[0])), args.isolated_reps, between=flush)
+    iso_f, iso_f_all = timer.median_ms(lambda: fwd(sets[0]), args.isolated_reps, between=flush)
+    iso_b, iso_b_all = timer.median_ms(lambda: combine(bwd_rows(sets[0])), args.isolated_reps, between=flush)
     del fa, fb
+
+    def spread(ms):
+        # latency distribution of the isolated calls, us: min, p10, median, p90, max
+        q = sorted(ms)
+        at = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))] * 1e3
+        return {"min": round(q[0] * 1e3, 2), "p10": round(at(0.1), 2), "median": round(statistics.median(q) * 1e3, 2),
+                "p90": round(at(0.9), 2), "max": round(q[-1] * 1e3, 2), "n": len(q)}
 
     if do_full and not args.no_cpu_baseline:
         validation["after_timing"] = validate(wl, snapshot(), oracle_ref, (x_h, w_h, dy_h))
@@ -550,11 +558,11 @@ def main(argv=None):
                                       bwd_rows_pct_of_2r1w=round(100 * rows_gbps / sized["2r1w_GBps"], 1)),
         "fwd": {"avg_us": round(f_us, 2), "GBps": round(fwd_gbps, 1), "pct_measured_roofline": round(100 * fwd_gbps / measured, 1),
                 "algorithmic_bytes": fwd_bytes, "isolated_median_us": round(iso_f * 1e3, 2),
-                "isolated_GBps": round(fwd_bytes / (iso_f * 1e-3) / 1e9, 1)},
+                "isolated_GBps": round(fwd_bytes / (iso_f * 1e-3) / 1e9, 1), "isolated_us": spread(iso_f_all)},
         "bwd": {"avg_us": round(bwd_call_us, 2), "rows_kernel_us": round(r_us, 2), "combine_us": round(c_us, 2),
                 "GBps": round(bwd_gbps, 1), "pct_measured_roofline": round(100 * bwd_gbps / measured, 1),
                 "algorithmic_bytes": bwd_bytes, "isolated_median_us": round(iso_b * 1e3, 2),
-                "isolated_GBps": round(bwd_bytes / (iso_b * 1e-3) / 1e9, 1)},
+                "isolated_GBps": round(bwd_bytes / (iso_b * 1e-3) / 1e9, 1), "isolated_us": spread(iso_b_all)},
         "step_event_us": round(step_event_ms * 1e3, 2),
         "settle_steps": settle_steps,
         "timing": "value: wall clock over K whole eager steps (synchronised at both ends), after untimed steps "

@@ -259,7 +259,9 @@ def test_beyond_4gib_tensors():
     indices pass 2^31 and byte offsets pass 2^32. Inputs are drawn on the
     device (seeded); sampled rows, including the last ones, go to the host for
     the oracle. dW is checked column by column against the fp64 sum of
-    dy * x * rstd over all rows (plain PyTorch, in row chunks)."""
+    dy * x * r over all rows, with r = 1/sqrt(mean(x^2) + eps) also in fp64
+    (plain PyTorch, in row chunks): no part of that reference comes from the
+    kernels' outputs."""
     M, N, dtype = 1 << 20, 2560, "bf16"
     eps = si.eps_f32(1e-6)
     g = torch.Generator(device="cuda")
@@ -292,7 +294,10 @@ def test_beyond_4gib_tensors():
     ref = torch.zeros(N, dtype=torch.float64, device="cuda")
     for s in range(0, M, 1 << 16):
         e = min(M, s + (1 << 16))
-        ref += (dy[s:e].double() * x[s:e].double() * rstd[s:e].double()[:, None]).sum(0)
+        xd = x[s:e].double()
+        r = 1.0 / torch.sqrt((xd * xd).mean(dim=1) + float(eps))
+        ref += (dy[s:e].double() * xd * r[:, None]).sum(0)
+        del xd
     ref = ref.cpu().numpy()
     err = np.abs(dw.cpu().numpy().astype(np.float64) - ref)
     bound = 1e-3 * np.maximum(np.abs(ref), 1e-2 * np.sqrt(np.mean(ref * ref)))
