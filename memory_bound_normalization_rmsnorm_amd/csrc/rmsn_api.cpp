@@ -55,8 +55,7 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     vectors (rows of at most 32 vectors: one lane per vector, several rows
 //     per wavefront, e.g. QK-norm's 128 bf16 = 16 lanes, 4 rows per wave);
 //     one row block per workgroup (grid = row blocks), so the hardware
-//     dispatcher balances the tail; with fp32 weights a persistent grid of
-//     two workgroups per compute unit instead (see ladder_grid).
+//     dispatcher balances the tail.
 //   Backward: one vector per lane up to 1024 lanes per row (more lanes, fewer
 //     registers, more rows in flight); workgroups of 1024 lanes for rows of
 //     64 to 256 lanes (4 to 16 rows per pass), of the row itself otherwise
@@ -86,7 +85,6 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     the scalar kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
 constexpr int kFwdMaxVecs = 4;
-constexpr int64_t kFwdW32PerCU = 2;  // persistent forward workgroups per CU with fp32 weights
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
@@ -210,31 +208,13 @@ void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config
 }
 
 // Grid. Forward: one row block per workgroup (capped at 2^20 workgroups,
-// which then loop), or persistent for the plain call with fp32 weights (res:
-// the residual-fused kernel). Backward (persistent, one partial dW row per
-// workgroup): see the ladder comment; `blocks_per_cu` caps it at what stays
-// resident.
-void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_cus, int blocks_per_cu,
-                 rmsnorm_config *c) {
+// which then loop). Backward (persistent, one partial dW row per workgroup):
+// see the ladder comment; `blocks_per_cu` caps it at what stays resident.
+void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int num_cus, int blocks_per_cu, rmsnorm_config *c) {
     const int64_t row_blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
     int64_t grid;
     if (!is_bwd) {
         grid = row_blocks < kMaxGrid ? row_blocks : kMaxGrid;
-        // fp32 (master) weights with 16-bit rows: every workgroup reads all of
-        // w (twice the bytes of 16-bit weights) from L2 before its row. For
-        // the plain forward on rows of a wavefront or more at 4 vectors per
-        // lane, a persistent grid of two workgroups per compute unit keeps w
-        // in registers across its row blocks: measured 2-3% faster at
-        // 16384 x 4096 and 4096 x 32768, 7-8% at 32768 x 8192, than one row
-        // block per workgroup. It lost elsewhere (38% on QK-norm rows, 2.5% at
-        // 3 vectors per lane, 1-4% with the residual add), and with 16-bit
-        // weights the two are within 2%.
-        if ((dtype == RMSN_BF16_WF32 || dtype == RMSN_F16_WF32) && !res && c->vector_path == 1 &&
-            c->lanes_per_row >= 64 && c->vecs_per_lane == kFwdMaxVecs) {
-            const int64_t per_cu = blocks_per_cu > 0 && blocks_per_cu < kFwdW32PerCU ? blocks_per_cu : kFwdW32PerCU;
-            const int64_t cap = (num_cus > 0 ? num_cus : 1) * per_cu;
-            if (grid > cap) grid = cap;
-        }
         // non-temporal row loads for rows of a wavefront or more: measured with
         // inputs that are not cache-resident (the benchmark's regime), they are
         // 0-18% faster at every such shape; narrow rows lose 1.6% with them.
@@ -334,7 +314,7 @@ int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, bool aligned, 
     if (!k) return RMSN_ECONFIG;
     st = occupancy(k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
-    ladder_grid(M, N, dtype, is_bwd, res, cus, blocks, c);
+    ladder_grid(M, N, dtype, is_bwd, cus, blocks, c);
     ladder_prefetch(M, N, dtype, is_bwd, c);
     k = kernel_for(*c, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
@@ -380,7 +360,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     }
     const void *k = kernel_for(*c, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
-    ladder_grid(M, N, dtype, is_bwd, res, 1, 1, c);
+    ladder_grid(M, N, dtype, is_bwd, 1, 1, c);
     c->grid = req->grid;
     c->partial_rows = req->grid;
     c->stream_loads = req->vector_path ? req->stream_loads : 0;
@@ -503,7 +483,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     if (!out || num_cus < 1 || blocks_per_cu < 1 || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
     std::memset(out, 0, sizeof *out);
     ladder_shape(M, N, dtype, is_bwd, aligned != 0, num_cus, out);
-    ladder_grid(M, N, dtype, is_bwd, 0, num_cus, blocks_per_cu, out);
+    ladder_grid(M, N, dtype, is_bwd, num_cus, blocks_per_cu, out);
     ladder_prefetch(M, N, dtype, is_bwd, out);
     return RMSN_OK;
 }
