@@ -80,7 +80,9 @@ typedef enum {
 typedef struct {
     int32_t vector_path;     /* 1: 16-byte vector row kernel; 2: the backward's wide-row vector
                                 kernel (1024 lanes, dW sums in LDS); 0: scalar row kernel */
-    int32_t lanes_per_row;   /* lanes that share one row (1..1024) */
+    int32_t lanes_per_row;   /* lanes that share one row (1..1024): a power of two, or for the
+                                backward with one vector per lane any multiple of 64 up to 1024
+                                with wg_threads equal to it (the row is the whole workgroup) */
     int32_t vecs_per_lane;   /* 16-byte vectors each lane holds per row (vector path) */
     int32_t wg_threads;      /* workgroup size */
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
