@@ -189,9 +189,10 @@ int rmsnorm_bwd_with_config(const void *x, const void *w, const void *dy, const 
 const char *rmsnorm_status_str(int status);
 
 /*
- * The ladder as a pure host function (no HIP call): the configuration for
- * (M, N, dtype, direction) on a device with `num_cus` compute units when the
- * chosen kernel fits `blocks_per_cu` workgroups per compute unit. `aligned`
+ * The ladder as a pure host function (no HIP call): the configuration of the
+ * plain (not residual-fused) call for (M, N, dtype, direction) on a device
+ * with `num_cus` compute units when the chosen kernel fits `blocks_per_cu`
+ * workgroups per compute unit. `aligned`
  * says whether the caller's pointers are 16-byte aligned. is_bwd: 0 forward,
  * 1 backward. Returns RMSN_OK or RMSN_EINVAL / RMSN_EDTYPE.
  */

@@ -387,3 +387,29 @@ def test_every_workgroup_row_kernel_formats(fmt, residual):
                 odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
                 check_rows(dx, odx, act, "dx (workgroup row)", floor=term_rms(x, w, dy, orr, act))
                 check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act, "dW (workgroup row)")
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_forward_mid_size_grid(fmt):
+    """Mid-size inputs (4 to 8 row blocks per compute unit): the ladder's
+    forward runs a prefetching grid of three workgroups per CU, so most
+    workgroups loop over two or three row blocks; every row of y and every
+    rstd against the oracle. The residual-fused call at the same sizes keeps
+    one block per workgroup."""
+    act, wst, code = FORMATS[fmt]
+    for M, N in ((2048, 4096), (4096, 2048)):
+        c = rn.rmsnorm_query_config(M, N, code, 0)
+        assert (c.grid, c.prefetch) == (3 * torch.cuda.get_device_properties(0).multi_processor_count, 1), c.as_dict()
+        _say(f"mid-size forward {fmt} {M}x{N} grid={c.grid}")
+        _, _, x, w, dy = _case(M, N, fmt, seed=9990 + M)
+        eps = si.eps_f32(1e-6)
+        y, rstd = gpu_fwd(x, w, eps, act)
+        oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
+        check_rows(y, oy, act, "y (mid-size grid)")
+        check_rstd(rstd, orr)
+        res = si.random_tensor((M, N), act, seed=9991 + M)
+        h, y2, rstd2 = gpu_fwd_residual(x, res, w, eps, act)
+        oh, oy2, orr2 = oracle.fwd_residual(x, res, w, eps, act, wdtype=wst)
+        assert np.array_equal(widen(h, act), oh)
+        check_rows(y2, oy2, act, "y (residual, mid-size)")
+        check_rstd(rstd2, orr2)
