@@ -75,14 +75,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+HOST_SOURCES = ("rmsn_api.cpp",)  # host code only: the ladder and the launches, no kernel
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources: counter-derived traffic is only reused for this exact code."""
+    """Hash of the kernel sources (every file of csrc/ but the host-only
+    HOST_SOURCES). Counter-derived traffic is reused only for this exact
+    kernel code and, separately checked, the same launch configuration."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "memory_bound_normalization_rmsnorm_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name in HOST_SOURCES:
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def launch_key(cfg: dict) -> list:
+    """The fields of a launch configuration that decide a kernel's traffic."""
+    return [int(cfg[k]) for k in ("vector_path", "lanes_per_row", "vecs_per_lane", "wg_threads", "prefetch",
+                                  "stream_loads", "grid")]
 
 
 def git_rev() -> str:
@@ -483,7 +496,8 @@ def main(argv=None):
 
     if args.mode == "kernels":
         print(json.dumps({"mode": "kernels", "steps": K, "ms_per_step": ms_per_step, "fwd_us": f_us,
-                          "bwd_rows_us": r_us, "combine_us": c_us, "eager": eager}))
+                          "bwd_rows_us": r_us, "combine_us": c_us, "eager": eager, "source_hash": env["source_hash"],
+                          "fwd_launch": launch_key(cfg_f), "bwd_launch": launch_key(cfg_b)}))
         return 0
 
     # ---- isolated calls with a cache flush before each ------------------------
@@ -525,7 +539,7 @@ def main(argv=None):
     rows_gbps = rows_bytes / (r_us * 1e-6) / 1e9
     value = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9
 
-    traffic = load_traffic(env["source_hash"], "bwd_rows", args.workload)
+    traffic = load_traffic(env["source_hash"], "bwd_rows", args.workload, launch_key(cfg_b))
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -793,9 +807,10 @@ def time_cell(torch, timer, op, outputs, R, replays=5):
     return statistics.median(times), eager_us
 
 
-def load_traffic(src_hash, kernel, workload):
+def load_traffic(src_hash, kernel, workload, launch):
     """HBM traffic per launch from committed rocprofv3 counter runs, only when
-    they were taken on the current kernel sources; else None."""
+    they were taken on the current kernel sources and the same launch
+    configuration; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -803,7 +818,7 @@ def load_traffic(src_hash, kernel, workload):
     except (OSError, ValueError):
         return None
     entry = data.get(f"{kernel}:{workload}")
-    if not entry or entry.get("source_hash") != src_hash:
+    if not entry or entry.get("source_hash") != src_hash or entry.get("launch") != launch:
         return None
     return entry.get("traffic_bytes_per_launch")
 
