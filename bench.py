@@ -106,18 +106,46 @@ def git_rev() -> str:
         return "unknown"
 
 
+def _find(obj, key):
+    """First value stored under `key` anywhere in a parsed JSON document."""
+    if isinstance(obj, dict):
+        if key in obj:
+            return obj[key]
+        obj = list(obj.values())
+    if isinstance(obj, list):
+        for v in obj:
+            r = _find(v, key)
+            if r is not None:
+                return r
+    return None
+
+
 def smi_snapshot() -> dict:
     """GPU utilisation / VRAM as reported by the management tool (the run
-    records it; a busy device makes every ratio suspect)."""
+    records it; a busy device makes every ratio suspect): graphics and memory
+    controller activity (%) and VRAM in use, plus the tool's raw output."""
     for cmd in (["amd-smi", "metric", "--usage", "--mem-usage", "--json"],
                 ["rocm-smi", "--showuse", "--showmemuse", "--json"]):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
             if r.returncode == 0 and r.stdout.strip():
-                return {"tool": cmd[0], "raw": r.stdout.strip()[:4000]}
+                out = {"tool": cmd[0], "raw": r.stdout.strip()}
+                try:
+                    doc = json.loads(r.stdout)
+                    for key in ("gfx_activity", "umc_activity", "used_vram", "total_vram"):
+                        v = _find(doc, key)
+                        out[key] = v.get("value") if isinstance(v, dict) else v
+                except ValueError:
+                    pass
+                return out
         except Exception:
             continue
     return {"tool": None, "raw": "unavailable"}
+
+
+def smi_brief(snap) -> dict | None:
+    return None if snap is None else {k: snap.get(k) for k in ("tool", "gfx_activity", "umc_activity", "used_vram",
+                                                                 "total_vram")}
 
 
 def cpu_info() -> dict:
@@ -403,6 +431,8 @@ def main(argv=None):
     # 1000). So untimed steps run for SETTLE_S of wall time before the W
     # warmup steps, whatever W is: the timed region measures the loaded
     # steady state a training loop runs in.
+    # idle check just before the timed region (the device should be ours alone)
+    env["smi_before_timing"] = smi_snapshot() if args.mode == "bench" else None
     settle_steps, t_settle = 0, time.perf_counter()
     if not kernels_only:
         while time.perf_counter() - t_settle < SETTLE_S:
@@ -579,6 +609,8 @@ def main(argv=None):
                 "isolated_GBps": round(bwd_bytes / (iso_b * 1e-3) / 1e9, 1), "isolated_us": spread(iso_b_all)},
         "step_event_us": round(step_event_ms * 1e3, 2),
         "settle_steps": settle_steps,
+        "idle_check": {"at_start": smi_brief(env["smi_at_start"]),
+                       "before_timing": smi_brief(env["smi_before_timing"])},
         "timing": "value: wall clock over K whole eager steps (synchronised at both ends), after untimed steps "
                   f"for {SETTLE_S} s (clock settle after the CPU leg) and W warmup steps; per-kernel avg_us: "
                   "K rotated launches of that kernel captured in a HIP graph, replayed between one HIP event "
