@@ -120,8 +120,10 @@ int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype);
  * contents on entry do not matter. Enqueues two kernels on `stream`: the
  * persistent row kernel (dx and per-workgroup dW partials) and a fixed-order
  * combine of the partials ("RMSNorm backward (almost) without the column
- * reduction", section "The persistent kernel"). With M == 0, dW is still
- * written (zeros) when N >= 1 and dW is not NULL.
+ * reduction", section "The persistent kernel"). When the row kernel runs as a
+ * single workgroup (a few rows) and dW is 16-byte aligned, that workgroup's
+ * partial row is dW and only the row kernel is enqueued. With M == 0, dW is
+ * still written (zeros) when N >= 1 and dW is not NULL.
  */
 int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
                 int64_t N, int dtype, void *dx, float *dw, void *workspace,

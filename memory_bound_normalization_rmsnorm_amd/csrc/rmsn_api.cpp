@@ -423,9 +423,12 @@ int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStre
                   rmsn::kCombineWG, cargs, s);
 }
 
+// dw_direct: when not NULL and the grid is a single workgroup, its partial row
+// is dW itself, written straight to dw_direct (16-byte aligned) instead of
+// the workspace; *partial_rows is then 0 and there is nothing to combine.
 int rows_impl(const void *x, const void *w, const void *dy, const void *dh, const float *rstd, int64_t M,
               int64_t N, int dtype, void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows,
-              hipStream_t s, const rmsnorm_config *req) {
+              hipStream_t s, const rmsnorm_config *req, float *dw_direct = nullptr) {
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!partial_rows) return RMSN_EINVAL;
@@ -450,12 +453,13 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
     }
     int32_t n32 = (int32_t)N;
     int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
-    float *partial = static_cast<float *>(workspace);
+    const bool direct = dw_direct && c.partial_rows == 1 && aligned16(dw_direct);
+    float *partial = direct ? dw_direct : static_cast<float *>(workspace);
     int64_t ldp = c.partial_stride;
     void *args[] = {(void *)&x, (void *)&w, (void *)&dy, (void *)&dh, (void *)&rstd, (void *)&dx,
                     (void *)&partial, (void *)&ldp, (void *)&M, (void *)&n32, (void *)&nvec};
     st = launch(fn, c.grid, c.wg_threads, args, s);
-    if (st == RMSN_OK) *partial_rows = c.partial_rows;
+    if (st == RMSN_OK) *partial_rows = direct ? 0 : c.partial_rows;
     return st;
 }
 
@@ -474,9 +478,11 @@ int bwd_impl(const void *x, const void *w, const void *dy, const void *dh, const
     }
     if (!dw) return RMSN_EINVAL;
     int64_t P = 0;
-    st = rows_impl(x, w, dy, dh, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req);
+    // A single workgroup (a few rows, e.g. one decode step's) writes dW
+    // itself: no combine launch, about half of such a call's time.
+    st = rows_impl(x, w, dy, dh, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req, dw);
     if (st != RMSN_OK) return st;
-    return combine_impl(workspace, P, N, dw, s);
+    return P == 0 ? RMSN_OK : combine_impl(workspace, P, N, dw, s);
 }
 
 }  // namespace

@@ -366,3 +366,40 @@ def test_every_workgroup_row_kernel(dtype):
                 full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_b=cfg)
         _say(f"workgroup row width, the ladder's own choice: N={N} {dtype}")
         full_check(x, w, dy, si.eps_f32(1e-6), dtype)
+
+
+@pytest.mark.parametrize("dtype,M,N", [("bf16", 1, 4096), ("bf16", 16, 128), ("f32", 1, 1024), ("bf16", 1, 32768),
+                                       ("f32", 1, 257), ("bf16", 8, 1024)], ids=lambda v: str(v))
+def test_single_workgroup_backward_writes_dw(dtype, M, N):
+    """A backward whose row kernel runs as one workgroup writes dW itself (no
+    combine launch): dW and dx against the oracle, equal to the two-call path
+    (rows, then combine, through the workspace), and, with dW not 16-byte
+    aligned, the combine path again."""
+    x, w, dy = si.random_case(M, N, dtype, seed=M * 31 + N, dy_scale=1e-2)
+    eps = si.eps_f32(1e-6)
+    code = DT[dtype]
+    assert rn.rmsnorm_query_config(M, N, code, 1).grid == 1
+    _say(f"single-workgroup backward {dtype} {M}x{N}")
+    _, rstd = gpu_fwd(x, w, eps, dtype)
+    dx, dw = gpu_bwd(x, w, dy, rstd, dtype)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, dtype)
+    check_rows(dx, odx, dtype, "dx", floor=term_rms(x, w, dy, orr, dtype))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, dtype), dtype)
+    # the two-call path through the workspace
+    xd, wd, gd = to_device(x, dtype), to_device(w), to_device(dy, dtype)
+    rd = torch.from_numpy(rstd).cuda()
+    dxd = torch.empty_like(xd)
+    nb = rn.rmsnorm_bwd_workspace_bytes(M, N, code)
+    ws = torch.empty(nb // 4 + 64, device="cuda")
+    P = rn.rmsnorm_bwd_rows(xd, wd, gd, rd, M, N, code, dxd, ws, nb)
+    dw2 = torch.full((N,), float("nan"), device="cuda")
+    rn.rmsnorm_bwd_combine(ws, P, N, dw2)
+    torch.cuda.synchronize()
+    assert P == 1 and np.array_equal(dw2.cpu().numpy(), dw), "two-call dW differs"
+    # dW one float past a 16-byte boundary: the combine path
+    big = torch.full((N + 4,), float("nan"), device="cuda")
+    dw3 = big[1:N + 1]
+    rn.rmsnorm_bwd(xd, wd, gd, rd, M, N, code, dxd, dw3, ws, nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(dw3.cpu().numpy(), dw), "dW through the combine differs"
+    assert torch.isnan(big[0]) and torch.isnan(big[N + 1:]).all(), "wrote outside dW"
