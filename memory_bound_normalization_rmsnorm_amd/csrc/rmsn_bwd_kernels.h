@@ -260,13 +260,18 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
 // lanes of a wavefront hit consecutive 16-byte words), so they need no
 // barrier; moving them out of the register file leaves room for the
 // prefetched next row, or, for fp32 rows of up to 32768, for eight vectors
-// per lane. Weights stay in registers when they take at most 4 vectors per
-// lane counting the prefetch buffers' share, and are re-read (from cache) at
-// each use otherwise. With RES the residual gradient dh is loaded in the
+// per lane. Weights stay in registers when they take at most 6 vectors per
+// lane counting the prefetch buffers' share (no kernel spills at 6; keeping
+// them measured 1.5-2.8% faster than at 4 for bf16 24576 and fp32 20480-24576
+// columns; 16-bit rows of 4 vectors with prefetch would spill), and are
+// re-read (from cache) at each use otherwise. With RES the residual gradient dh is loaded in the
 // second pass, one vector at a time, where it is needed.
+#ifndef RMSN_WIDE_KEEP_W_SHARE
+#define RMSN_WIDE_KEEP_W_SHARE 6  // weight vectors per lane, counting the prefetch buffers' share
+#endif
 template <typename T, typename TW, int VPT, bool PF>
 constexpr bool wide_keeps_w() {
-    return VPT * WeightVec<T, TW>::kVecs * (PF ? 2 : 1) <= 4;
+    return VPT * WeightVec<T, TW>::kVecs * (PF ? 2 : 1) <= RMSN_WIDE_KEEP_W_SHARE;
 }
 
 template <typename T, typename TW, bool RES, int VPT, bool PF>
