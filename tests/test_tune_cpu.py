@@ -34,3 +34,14 @@ def test_cache_round_trip(tmp_path):
     back = tune.config_from_dict(tune.load_cache(path)[key]["config"])
     assert tune._key(back) == tune._key(cfg)
     assert tune.load_cache(str(tmp_path / "missing.json")) == {}
+
+
+def test_candidates_include_whole_wavefront_backward_rows():
+    """Backward rows of 257-1023 vectors whose whole wavefronts are not a power
+    of two: the workgroup-sized row kernels, at both prefetch depths."""
+    cands = tune.candidates(16384, 5120, rn.BF16, 1, 256)
+    rowwg = {(c.lanes_per_row, c.wg_threads, c.prefetch) for c in cands if c.lanes_per_row == 640}
+    assert rowwg == {(640, 640, 1), (640, 640, 2)}
+    assert not [c for c in tune.candidates(16384, 5120, rn.BF16, 0, 256) if c.lanes_per_row == 640]  # forward
+    assert not [c for c in tune.candidates(16384, 4096, rn.BF16, 1, 256) if c.lanes_per_row % 64 == 0 and
+                c.lanes_per_row & (c.lanes_per_row - 1)]                                           # 512: a power of two
