@@ -133,11 +133,13 @@ fwd_vec(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict
         const uint32_t rows = rows_at(base);
         const Buf yb(y + base * N, rows * row_bytes);
 
-        // Up to 128 lanes per row the row loads go out before the weights are
-        // pinned: pinning waits for the weight loads, and issued first, the row
-        // loads overlap them (5% at 128 columns, 1.6% at 4096). Wider rows pin
-        // first (0.6-2.5% faster there, measured on the same device).
-        constexpr bool kRowsFirst = LPR <= 128;
+        // The row loads go out before the weights are pinned (pinning waits
+        // for the weight loads; issued first, the row loads overlap them) up
+        // to 128 lanes per row (5% at 128 columns, 1.6% at 4096), and at any
+        // width in the plain forward with 16-bit weights (2-6% at 12288-16384
+        // columns, neutral elsewhere). fp32 weights on wider rows pin first:
+        // rows first measured 4% slower there (32768 x 8192, 16384 x 16384).
+        constexpr bool kRowsFirst = LPR <= 128 || (sizeof(TW) == 2 && !RES);
         if constexpr (kKeepW && !kRowsFirst) {
 #pragma unroll
             for (int v = 0; v < VPT; ++v) wv[v].keep();
