@@ -306,8 +306,8 @@ int occupancy(const void *fn, int wg, int *blocks) {
     return RMSN_OK;
 }
 
-const void *kernel_for(const rmsnorm_config &c, int dtype, int is_bwd, int res) {
-    if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res);
+const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd, int res) {
+    if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
     if (c.vector_path == kWidePath) {
         const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
         return e ? e->fn : nullptr;
@@ -330,13 +330,13 @@ int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, bool aligned, 
     int st = device_info(&cus);
     if (st != RMSN_OK) return st;
     ladder_shape(M, N, dtype, is_bwd, aligned, cus, c);
-    const void *k = kernel_for(*c, dtype, is_bwd, res);
+    const void *k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     st = occupancy(k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, res, cus, blocks, c);
     ladder_prefetch(M, N, dtype, is_bwd, c);
-    k = kernel_for(*c, dtype, is_bwd, res);
+    k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     if (fn) *fn = k;
     return RMSN_OK;
@@ -378,7 +378,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     } else {
         set_scalar_shape(c);
     }
-    const void *k = kernel_for(*c, dtype, is_bwd, res);
+    const void *k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     ladder_grid(M, N, dtype, is_bwd, res, 1, 1, c);
     c->grid = req->grid;

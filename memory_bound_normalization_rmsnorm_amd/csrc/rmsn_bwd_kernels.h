@@ -416,18 +416,25 @@ bwd_wide(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
     }
 }
 
-template <typename T, typename TW, bool RES>
+// Scalar backward (any N, any alignment): one workgroup per row at a time,
+// element loads. Each lane owns columns threadIdx.x + k*kScalarWG of the
+// workgroup's dW running sums for the whole kernel (no lane touches another's,
+// so no barrier), kept in LDS when the row has at most kScalarLdsCols columns
+// (LDS) and in the workgroup's partial row in memory otherwise; the partial
+// row is written once at the end in the LDS case. The sums see the same fma
+// sequence either way, so dW has the same bits.
+template <typename T, typename TW, bool RES, bool LDS>
 __global__ void __launch_bounds__(kScalarWG)
 bwd_scalar(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
            const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
            int32_t N, int32_t /*nvec*/) {
     using E = Elem<T>;
     __shared__ float slots[2 * (kScalarWG / 64)];
+    __shared__ float sums[LDS ? kScalarLdsCols : 1];
     const float n = (float)N;
-    // Each lane owns columns threadIdx.x + k*kScalarWG of this workgroup's
-    // partial row for the whole kernel, so its read-modify-writes never race.
     float *prow = partial + (int64_t)blockIdx.x * ldp;
-    for (int j = threadIdx.x; j < N; j += kScalarWG) prow[j] = 0.f;
+    float *acc = LDS ? sums : prow;
+    for (int j = threadIdx.x; j < N; j += kScalarWG) acc[j] = 0.f;
     int parity = 0;
     for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
         const int64_t o = row * (int64_t)N;
@@ -443,8 +450,11 @@ bwd_scalar(const T *__restrict__ x, const TW *__restrict__ w, const T *__restric
             float g = __builtin_fmaf(-fx, c, r * (fg * fw));
             if constexpr (RES) g += E::load(dh + o + j);
             E::store(dx + o + j, g);
-            prow[j] = __builtin_fmaf(fg * fx, r, prow[j]);
+            acc[j] = __builtin_fmaf(fg * fx, r, acc[j]);
         }
+    }
+    if constexpr (LDS) {
+        for (int j = threadIdx.x; j < N; j += kScalarWG) prow[j] = acc[j];
     }
 }
 

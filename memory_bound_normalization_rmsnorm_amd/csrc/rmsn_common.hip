@@ -121,21 +121,25 @@ const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf) {
 }
 
 template <typename T, typename TW>
-const void *scalar_kernel(int is_bwd, int res) {
-    if (is_bwd)
-        return res ? reinterpret_cast<const void *>(&bwd_scalar<T, TW, true>)
-                   : reinterpret_cast<const void *>(&bwd_scalar<T, TW, false>);
+const void *scalar_kernel(int is_bwd, int res, int lds) {
+    if (is_bwd) {
+        if (lds)
+            return res ? reinterpret_cast<const void *>(&bwd_scalar<T, TW, true, true>)
+                       : reinterpret_cast<const void *>(&bwd_scalar<T, TW, false, true>);
+        return res ? reinterpret_cast<const void *>(&bwd_scalar<T, TW, true, false>)
+                   : reinterpret_cast<const void *>(&bwd_scalar<T, TW, false, false>);
+    }
     return res ? reinterpret_cast<const void *>(&fwd_scalar<T, TW, true>)
                : reinterpret_cast<const void *>(&fwd_scalar<T, TW, false>);
 }
 
-const void *scalar_kernel(int dtype, int is_bwd, int res) {
+const void *scalar_kernel(int dtype, int is_bwd, int res, int lds) {
     switch (dtype) {
-    case 0: return scalar_kernel<float, float>(is_bwd, res);
-    case 1: return scalar_kernel<bf16_t, bf16_t>(is_bwd, res);
-    case 2: return scalar_kernel<f16_t, f16_t>(is_bwd, res);
-    case 3: return scalar_kernel<bf16_t, float>(is_bwd, res);
-    case 4: return scalar_kernel<f16_t, float>(is_bwd, res);
+    case 0: return scalar_kernel<float, float>(is_bwd, res, lds);
+    case 1: return scalar_kernel<bf16_t, bf16_t>(is_bwd, res, lds);
+    case 2: return scalar_kernel<f16_t, f16_t>(is_bwd, res, lds);
+    case 3: return scalar_kernel<bf16_t, float>(is_bwd, res, lds);
+    case 4: return scalar_kernel<f16_t, float>(is_bwd, res, lds);
     default: return nullptr;
     }
 }

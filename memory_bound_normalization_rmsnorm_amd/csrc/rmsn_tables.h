@@ -7,6 +7,7 @@ namespace rmsn {
 
 // Lanes of the scalar (any-N, any-alignment) row kernels and the combine kernel.
 constexpr int kScalarWG = 256;
+constexpr int kScalarLdsCols = 16384;  // scalar backward rows up to this width keep their dW sums in LDS (64 KiB)
 constexpr int kCombineWG = 512;
 constexpr int kCombineCols = 32;     // dW columns per combine workgroup: one 128-byte line per partial row
 constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
@@ -52,7 +53,8 @@ const KernelEntry *fwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, 
 const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf);
 // wide-row backward kernels (lanes per row and workgroup kWideLanes)
 const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf);
-const void *scalar_kernel(int dtype, int is_bwd, int res);
+// lds: the backward kernel that keeps its dW sums in LDS (rows of at most kScalarLdsCols columns)
+const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
 const void *dw_combine_kernel();
 const void *fill_zero_kernel();
 

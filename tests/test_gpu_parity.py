@@ -403,3 +403,17 @@ def test_single_workgroup_backward_writes_dw(dtype, M, N):
     torch.cuda.synchronize()
     assert np.array_equal(dw3.cpu().numpy(), dw), "dW through the combine differs"
     assert torch.isnan(big[0]) and torch.isnan(big[N + 1:]).all(), "wrote outside dW"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scalar_backward_sums_in_lds_and_in_memory(dtype):
+    """The scalar backward keeps its dW running sums in LDS up to 16384
+    columns and in its partial row in memory beyond: both sides of that limit,
+    forced through the scalar path with a grid that makes workgroups walk
+    several rows, against the oracle."""
+    for N in (16384, 16385):
+        M = 37
+        x, w, dy = si.random_case(M, N, dtype, seed=N + 5, dy_scale=1e-2)
+        cfg = rn.rmsnorm_config(vector_path=0, grid=5)
+        _say(f"scalar backward N={N} {dtype}")
+        full_check(x, w, dy, si.eps_f32(1e-6), dtype, cfg_f=cfg, cfg_b=cfg)
