@@ -79,7 +79,12 @@ typedef enum {
  */
 typedef struct {
     int32_t vector_path;     /* 1: 16-byte vector row kernel; 2: the backward's wide-row vector
-                                kernel (1024 lanes, dW sums in LDS); 0: scalar row kernel */
+                                kernel (1024 lanes, dW sums in LDS); 3: element kernel (rows
+                                that are not a multiple of 16 bytes or not 16-byte aligned,
+                                257..16384 columns: 1024 lanes, vecs_per_lane = elements per
+                                lane, a power of two up to 16; the ladder's choice for the
+                                backward and for fp32 forward rows, an explicit choice for
+                                the others); 0: scalar row kernel */
     int32_t lanes_per_row;   /* lanes that share one row (1..1024): a power of two, or for the
                                 backward with one vector per lane any multiple of 64 up to 1024
                                 with wg_threads equal to it (the row is the whole workgroup) */

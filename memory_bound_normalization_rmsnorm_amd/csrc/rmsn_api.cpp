@@ -85,6 +85,8 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     backward more than 1024 * 4 16-bit or 1024 * 8 fp32 vectors) goes to
 //     the scalar kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
+constexpr int kElemPath = 3;  // rmsnorm_config::vector_path of the element kernels
+constexpr int64_t kElemMinN = 257;  // narrower unvectorisable rows keep the scalar kernel
 constexpr int kFwdMaxVecs = 4;
 // forward row blocks per CU (inclusive range) taking a prefetching grid of kFwdMidPerCU workgroups per CU
 constexpr int64_t kFwdMidLo = 4, kFwdMidHi = 8, kFwdMidPerCU = 3;
@@ -104,6 +106,21 @@ void set_vector_shape(int64_t lpr, int64_t vpt, int wg, int pf, rmsnorm_config *
     c->rows_per_wg = c->wg_threads / c->lanes_per_row;
     c->prefetch = pf;
 }
+
+// Element kernels: one row per kElemWG-lane workgroup, k elements per lane
+// (the smallest power of two with kElemWG * k >= N).
+void set_elem_shape(int64_t N, rmsnorm_config *c) {
+    int64_t k = 1;
+    while (rmsn::kElemWG * k < N) k <<= 1;
+    c->vector_path = kElemPath;
+    c->lanes_per_row = rmsn::kElemWG;
+    c->vecs_per_lane = (int32_t)k;
+    c->wg_threads = rmsn::kElemWG;
+    c->rows_per_wg = 1;
+    c->prefetch = 0;
+}
+
+bool elem_ok(int64_t N) { return N >= kElemMinN && N <= int64_t(rmsn::kElemWG) * rmsn::kElemMaxK; }
 
 void set_scalar_shape(rmsnorm_config *c) {
     c->vector_path = 0;
@@ -152,7 +169,21 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
 void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, bool aligned, int64_t cus, rmsnorm_config *c) {
     const int64_t nvec = N * elem_size(dtype) / 16;
     const int64_t vmax = is_bwd ? wide_max_vecs(dtype) : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
-    if (!vector_ok(N, dtype, aligned) || nvec > kMaxVecLanes * vmax) {
+    if (!vector_ok(N, dtype, aligned)) {
+        // rows that are not a multiple of 16 bytes or not 16-byte aligned:
+        // element kernels (the row read once into registers) for the
+        // backward and for fp32 forward rows, else the scalar kernel. With
+        // 2-byte elements the element forward's 1024-lane rows keep too few
+        // rows in flight: bf16 16384 x 4100 took 172 us against the scalar
+        // kernel's 131 (fp32 16384 x 4098: 99 against 177; backward 1.4-3x
+        // faster in every format).
+        if (elem_ok(N) && (is_bwd || elem_size(dtype) == 4))
+            set_elem_shape(N, c);
+        else
+            set_scalar_shape(c);
+        return;
+    }
+    if (nvec > kMaxVecLanes * vmax) {
         set_scalar_shape(c);
         return;
     }
@@ -308,6 +339,7 @@ int occupancy(const void *fn, int wg, int *blocks) {
 
 const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd, int res) {
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
+    if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane);
     if (c.vector_path == kWidePath) {
         const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
         return e ? e->fn : nullptr;
@@ -361,8 +393,16 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
                     bool aligned, rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
-    if (req->vector_path < 0 || req->vector_path > kWidePath) return RMSN_ECONFIG;
-    if (req->vector_path) {
+    if (req->vector_path < 0 || req->vector_path > kElemPath) return RMSN_ECONFIG;
+    if (req->vector_path == kElemPath) {
+        const int64_t k = req->vecs_per_lane;
+        if (req->lanes_per_row != rmsn::kElemWG || (req->wg_threads != 0 && req->wg_threads != rmsn::kElemWG) ||
+            k < 1 || k > rmsn::kElemMaxK || (k & (k - 1)) != 0 || int64_t(rmsn::kElemWG) * k < N ||
+            req->prefetch != 0 || req->stream_loads != 0)
+            return RMSN_ECONFIG;
+        set_elem_shape(N, c);
+        c->vecs_per_lane = (int32_t)k;
+    } else if (req->vector_path) {
         const int64_t nvec = N * elem_size(dtype) / 16;
         if (!vector_ok(N, dtype, aligned)) return RMSN_ECONFIG;
         if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
@@ -404,7 +444,7 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
              : resolve(M, N, dtype, 0, fused, aligned, &c, &fn);
     if (st != RMSN_OK) return st;
     int32_t n32 = (int32_t)N;
-    int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
+    int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
     int32_t stream_ld = c.stream_loads;
     void *args[] = {(void *)&x, (void *)&res, (void *)&w, (void *)&h, (void *)&y, (void *)&rstd,
                     (void *)&eps, (void *)&M, (void *)&n32, (void *)&nvec, (void *)&stream_ld};
@@ -452,7 +492,7 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
         if (workspace_bytes < (size_t)need) return RMSN_EWORKSPACE;
     }
     int32_t n32 = (int32_t)N;
-    int32_t nvec = c.vector_path ? (int32_t)(N * elem_size(dtype) / 16) : 0;
+    int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
     const bool direct = dw_direct && c.partial_rows == 1 && aligned16(dw_direct);
     float *partial = direct ? dw_direct : static_cast<float *>(workspace);
     int64_t ldp = c.partial_stride;

@@ -48,6 +48,8 @@ struct Elem<float> {
     static constexpr int kPerVec = 4;  // elements per 16-byte vector
     static __device__ __forceinline__ float load(const float *p) { return *p; }
     static __device__ __forceinline__ void store(float *p, float v) { *p = v; }
+    // the value store() writes, read back (the storage rounding, in registers)
+    static __device__ __forceinline__ float rounded(float v) { return v; }
     static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[4]) {
         f[0] = as_float(v.x);
         f[1] = as_float(v.y);
@@ -87,6 +89,9 @@ struct Elem<bf16_t> {
     }
     static __device__ __forceinline__ void store(bf16_t *p, float v) {
         p->bits = __builtin_bit_cast(uint16_t, (__bf16)v);
+    }
+    static __device__ __forceinline__ float rounded(float v) {
+        return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v) << 16);
     }
     static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[8]) {
         f[0] = bf16_lo(v.x);
@@ -138,6 +143,10 @@ struct Elem<f16_t> {
     static __device__ __forceinline__ void store(f16_t *p, float v) {
         asm("" : "+v"(v));  // one rounding of the fp32 value, as in pack_f16x2
         p->bits = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+    static __device__ __forceinline__ float rounded(float v) {
+        asm("" : "+v"(v));
+        return (float)(_Float16)v;
     }
     static __device__ __forceinline__ void unpack(const u32x4 &v, float (&f)[8]) {
         f[0] = f16_lo(v.x);

@@ -8,6 +8,11 @@ namespace rmsn {
 // Lanes of the scalar (any-N, any-alignment) row kernels and the combine kernel.
 constexpr int kScalarWG = 256;
 constexpr int kScalarLdsCols = 16384;  // scalar backward rows up to this width keep their dW sums in LDS (64 KiB)
+// Element kernels (rows that are not a multiple of 16 bytes or not 16-byte
+// aligned): kElemWG lanes per row, K elements per lane, K a power of two up to
+// kElemMaxK.
+constexpr int kElemWG = 1024;
+constexpr int kElemMaxK = 16;
 constexpr int kCombineWG = 512;
 constexpr int kCombineCols = 32;     // dW columns per combine workgroup: one 128-byte line per partial row
 constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
@@ -55,6 +60,8 @@ const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, 
 const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf);
 // lds: the backward kernel that keeps its dW sums in LDS (rows of at most kScalarLdsCols columns)
 const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
+// element kernels: k elements per lane (1, 2, 4, 8 or 16), nullptr otherwise
+const void *elem_kernel(int dtype, int is_bwd, int res, int k);
 const void *dw_combine_kernel();
 const void *fill_zero_kernel();
 

@@ -263,12 +263,37 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (vpt - 1) * lpr < nvec <= vpt * lpr
 
 
-@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(13, rn.F32, 1, 0), (257, rn.BF16, 1, 0), (4096, rn.BF16, 0, 0),
+@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(13, rn.F32, 1, 0), (255, rn.BF16, 1, 0), (256, rn.BF16, 0, 1),
                                                     (65536 + 8, rn.BF16, 1, 0), (3, rn.BF16, 1, 1),
-                                                    (32768 + 8, rn.BF16, 1, 1)])
+                                                    (32768 + 8, rn.BF16, 1, 1), (16385, rn.BF16, 1, 0),
+                                                    (20000, rn.F32, 0, 1)])
 def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
+    """The scalar kernel: rows the vector kernels cannot take that are too
+    narrow (256 columns or fewer) or too wide (more than 16384) for the
+    element kernels, and rows wider than the vector kernels hold."""
     c = cfg(100, N, dtype, is_bwd, aligned=aligned)
     assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
+
+
+@pytest.mark.parametrize("N,dtype,aligned,k", [(257, rn.BF16, 1, 1), (1024, rn.BF16, 0, 1), (1025, rn.F16, 1, 2),
+                                               (4095, rn.BF16, 1, 4), (4100, rn.BF16_WF32, 1, 8),
+                                               (4096, rn.BF16, 0, 4), (5001, rn.F32, 1, 8), (16383, rn.F16, 1, 16),
+                                               (16384, rn.F32, 0, 16)])
+def test_ladder_element_cases(N, dtype, aligned, k):
+    """Rows that are not a multiple of 16 bytes, or not 16-byte aligned, of
+    257 to 16384 columns: the backward, and the forward of fp32 activations,
+    take the element kernels, 1024 lanes, the smallest power-of-two number of
+    elements per lane that covers the row, the backward persistent over the
+    grid of the other row kernels; the forward of 2-byte activations stays on
+    the scalar kernel."""
+    for is_bwd in (0, 1):
+        c = cfg(4096, N, dtype, is_bwd, aligned=aligned)
+        if not is_bwd and dtype != rn.F32:
+            assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
+            continue
+        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["rows_per_wg"],
+                c["prefetch"], c["stream_loads"]) == (3, 1024, k, 1024, 1, 0, 0)
+        assert c["grid"] == (512 if is_bwd else 4096)
 
 
 def test_ladder_grid_and_workspace_shape():
@@ -403,3 +428,25 @@ def test_ladder_forward_mid_size_grid(dtype):
         assert (c["grid"], c["prefetch"]) == (-(-M // c["rows_per_wg"]), 0), (M, N, c)
     # the residual-fused call keeps one block per workgroup (queried on the device, not here);
     # an explicit configuration keeps its own prefetch (checked with the other explicit tests)
+
+
+def test_explicit_element_config_checks():
+    """Element-kernel configurations through *_with_config are checked before
+    any HIP call: 1024 lanes, a power-of-two count of elements per lane up to
+    16 that covers the row, no prefetch, no streaming loads."""
+    L, C = rn.lib, rn.rmsnorm_config
+
+    def fwd(**kw):
+        c = C(vector_path=3, lanes_per_row=1024, vecs_per_lane=8, wg_threads=1024, grid=8)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, 64, 4100, rn.BF16, FAKE, FAKE, c, None)
+
+    assert fwd(vecs_per_lane=4) == rn.ECONFIG       # 4096 elements do not cover 4100
+    assert fwd(vecs_per_lane=6) == rn.ECONFIG       # not a power of two
+    assert fwd(vecs_per_lane=32) == rn.ECONFIG      # beyond 16
+    assert fwd(lanes_per_row=512) == rn.ECONFIG
+    assert fwd(wg_threads=512) == rn.ECONFIG
+    assert fwd(prefetch=1) == rn.ECONFIG
+    assert fwd(stream_loads=1) == rn.ECONFIG
+    assert fwd(vector_path=4) == rn.ECONFIG

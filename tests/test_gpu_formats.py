@@ -413,3 +413,64 @@ def test_forward_mid_size_grid(fmt):
         assert np.array_equal(widen(h, act), oh)
         check_rows(y2, oy2, act, "y (residual, mid-size)")
         check_rstd(rstd2, orr2)
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("residual", [False, True])
+def test_every_element_kernel(fmt, residual):
+    """The element kernels (rows that are not a multiple of 16 bytes), every
+    elements-per-lane count, every format, plain and residual: the ladder's
+    own configuration, and the backward forced to a grid of 3 so workgroups
+    walk several rows; 7 rows, the row length 5 short of 1024 * K."""
+    act, wst, code = FORMATS[fmt]
+    eps = si.eps_f32(1e-6)
+    for k in (1, 2, 4, 8, 16):
+        M, N = 7, 1024 * k - 5
+        _, _, x, w, dy = _case(M, N, fmt, seed=7000 + k)
+        c = rn.rmsnorm_query_config(M, N, code, 1)
+        assert (c.vector_path, c.vecs_per_lane) == (3, k), c.as_dict()
+        forced = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, wg_threads=1024, grid=3)
+        for cfg in (None, forced):
+            _say(f"element kernel k={k} N={N} {fmt} residual={residual} cfg={None if cfg is None else cfg.as_dict()}")
+            if residual:
+                res = si.random_tensor((M, N), act, seed=7100 + k)
+                dh = si.random_tensor((M, N), act, seed=7200 + k, scale=1e-2)
+                residual_check(x, res, w, dy, dh, eps, act, wst, cfg=cfg)
+            else:
+                plain_check(x, w, dy, eps, act, wst, cfg=cfg)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32", "f16w32"])
+def test_element_kernels_on_unaligned_pointers(fmt):
+    """16-byte-multiple rows whose pointers are not 16-byte aligned (views one
+    element into larger buffers) take the element kernels; outputs against the
+    oracle, and nothing written outside the views."""
+    act, wst, code = FORMATS[fmt]
+    M, N = 37, 4096
+    _, _, x, w, dy = _case(M, N, fmt, seed=7300)
+    eps = si.eps_f32(1e-6)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[act]
+
+    def view_of(a, dtype):
+        d = to_device(np.concatenate([a.reshape(-1)[:1], a.reshape(-1)]), dtype)
+        return d[1:]
+
+    xd, dyd = view_of(x, act), view_of(dy, act)
+    wd = view_of(w, wst)
+    ybuf = torch.full((M * N + 2,), float("nan"), dtype=tdt, device="cuda")
+    dxbuf = torch.full((M * N + 2,), float("nan"), dtype=tdt, device="cuda")
+    y, dx = ybuf[1:M * N + 1], dxbuf[1:M * N + 1]
+    rstd = torch.full((M,), float("nan"), device="cuda")
+    dw = torch.full((N,), float("nan"), device="cuda")
+    rn.rmsnorm_fwd(xd, wd, eps, M, N, code, y, rstd)
+    nb = rn.rmsnorm_bwd_workspace_bytes(M, N, code)
+    ws = torch.empty(nb // 4 + 64, device="cuda")
+    rn.rmsnorm_bwd(xd, wd, dyd, rstd, M, N, code, dx, dw, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.isnan(ybuf[0]) and torch.isnan(ybuf[-1]) and torch.isnan(dxbuf[0]) and torch.isnan(dxbuf[-1])
+    oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
+    check_rows(to_host(y, act).reshape(M, N), oy, act, "y (unaligned)")
+    check_rstd(rstd.cpu().numpy(), orr)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wst)
+    check_rows(to_host(dx, act).reshape(M, N), odx, act, "dx (unaligned)", floor=term_rms(x, w, dy, orr, act))
+    check_dw(dw.cpu().numpy(), oracle.bwd_dw(x, dy, eps, act), act)
