@@ -32,9 +32,13 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream). Nothing synchronises the host.
  *   - Argument checks run before any HIP call. M == 0 is a valid no-op.
- *   - Any N >= 1 is accepted. 16-byte vector loads are used when
- *     N * sizeof(elem) is a multiple of 16 and every matrix/vector pointer is
- *     16-byte aligned; otherwise a scalar path of the same arithmetic runs.
+ *   - Any N >= 1 is accepted. Every pointer must be aligned to its element
+ *     type (2 or 4 bytes; RMSN_EINVAL otherwise). 16-byte vector loads are
+ *     used when N * sizeof(elem) is a multiple of 16 and every matrix/vector
+ *     pointer is 16-byte aligned; otherwise kernels of the same arithmetic
+ *     with narrower accesses run (rows of 257 to 16384 columns: groups of
+ *     consecutive elements as wide as N and the pointers' alignment allow;
+ *     other widths: one element per access).
  *   - y must not alias x; dx must not alias x or dy (undefined behaviour).
  *   - Return value: RMSN_OK (0) or a negative rmsn_status.
  */
@@ -81,10 +85,8 @@ typedef struct {
     int32_t vector_path;     /* 1: 16-byte vector row kernel; 2: the backward's wide-row vector
                                 kernel (1024 lanes, dW sums in LDS); 3: element kernel (rows
                                 that are not a multiple of 16 bytes or not 16-byte aligned,
-                                257..16384 columns: 1024 lanes, vecs_per_lane = elements per
-                                lane, a power of two up to 16; the ladder's choice for the
-                                backward and for fp32 forward rows, an explicit choice for
-                                the others); 0: scalar row kernel */
+                                257..16384 columns: 1024 lanes, vecs_per_lane accesses of
+                                elems_per_access elements per lane); 0: scalar row kernel */
     int32_t lanes_per_row;   /* lanes that share one row (1..1024): a power of two, or for the
                                 backward with one vector per lane any multiple of 64 up to 1024
                                 with wg_threads equal to it (the row is the whole workgroup) */
@@ -93,10 +95,16 @@ typedef struct {
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
     int32_t prefetch;        /* row blocks whose loads are issued before the current block's
                                 arithmetic (a register ring): 0 or 1; the backward also 2 for
-                                one vector per lane */
+                                one vector per lane (vector path) */
     int32_t stream_loads;    /* forward, rows of 64 lanes or more: 1 when the row loads carry the
                                 non-temporal hint (the ladder sets it; an explicit 0 suits inputs
                                 that are still cache-resident); ignored by the backward */
+    int32_t elems_per_access; /* element kernels: consecutive elements each access moves (1, 2,
+                                4 or 8; at most 16 bytes of activations or weights), dividing N,
+                                every pointer aligned to its access; vecs_per_lane *
+                                elems_per_access is at most 16 and covers N / 1024. The ladder
+                                takes the largest; 0 in an explicit element configuration asks
+                                for that one. 0 on the other paths */
     int64_t grid;            /* workgroups launched */
     int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid) */
     int64_t partial_stride;  /* backward: floats between consecutive partial rows */
@@ -199,9 +207,10 @@ const char *rmsnorm_status_str(int status);
  * The ladder as a pure host function (no HIP call): the configuration of the
  * plain (not residual-fused) call for (M, N, dtype, direction) on a device
  * with `num_cus` compute units when the chosen kernel fits `blocks_per_cu`
- * workgroups per compute unit. `aligned`
- * says whether the caller's pointers are 16-byte aligned. is_bwd: 0 forward,
- * 1 backward. Returns RMSN_OK or RMSN_EINVAL / RMSN_EDTYPE.
+ * workgroups per compute unit. `aligned`: the alignment of the caller's
+ * pointers, 1 for 16-byte aligned, 0 for only aligned to their element type,
+ * or 2, 4, 8 or 16 for that many bytes. is_bwd: 0 forward, 1 backward.
+ * Returns RMSN_OK or RMSN_EINVAL / RMSN_EDTYPE.
  */
 int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int aligned, int num_cus,
                           int blocks_per_cu, rmsnorm_config *out);

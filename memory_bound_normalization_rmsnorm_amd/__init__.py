@@ -55,6 +55,7 @@ class rmsnorm_config(ctypes.Structure):
         ("rows_per_wg", ctypes.c_int32),
         ("prefetch", ctypes.c_int32),
         ("stream_loads", ctypes.c_int32),
+        ("elems_per_access", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("partial_rows", ctypes.c_int64),
         ("partial_stride", ctypes.c_int64),

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <unordered_map>
 
@@ -33,6 +34,49 @@ int elem_size(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
 bool valid_dtype(int dtype) { return dtype >= RMSN_F32 && dtype <= RMSN_F16_WF32; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// bytes per weight element
+int w_size(int dtype) { return (dtype == RMSN_BF16 || dtype == RMSN_F16) ? 2 : 4; }
+
+// Common alignment in bytes (a power of two, capped at 16) of the activation
+// pointers and of the weight pointer.
+struct Align {
+    int act;
+    int w;
+};
+
+int low_align(uintptr_t bits) {
+    int a = 1;
+    while (a < 16 && (bits & uintptr_t(a)) == 0) a <<= 1;
+    return a;
+}
+
+Align align_of(std::initializer_list<const void *> acts, const void *w) {
+    uintptr_t bits = 0;
+    for (const void *p : acts) bits |= reinterpret_cast<uintptr_t>(p);
+    return {low_align(bits), low_align(reinterpret_cast<uintptr_t>(w))};
+}
+
+bool all16(const Align &a) { return a.act >= 16 && a.w >= 16; }
+
+// Every element access is naturally aligned (required of every pointer).
+bool natural(const Align &a, int dtype) { return a.act >= elem_size(dtype) && a.w >= w_size(dtype); }
+
+// Elements per access of the element kernels: the largest power of two G with
+// at most 16 bytes per access of activations and weights, N % G == 0 (no row
+// ends inside a group) and every pointer aligned to its G-element access.
+int elem_group(int64_t N, int dtype, const Align &a) {
+    const int s = elem_size(dtype), sw = w_size(dtype), big = s > sw ? s : sw;
+    int g = 1;
+    while (2 * g * big <= 16 && N % (2 * g) == 0 && a.act % (2 * g * s) == 0 && a.w % (2 * g * sw) == 0) g *= 2;
+    return g;
+}
+
+bool elem_group_ok(int64_t N, int dtype, const Align &a, int64_t g) {
+    const int s = elem_size(dtype), sw = w_size(dtype), big = s > sw ? s : sw;
+    return (g == 1 || g == 2 || g == 4 || g == 8) && g * big <= 16 && N % g == 0 && a.act % (g * s) == 0 &&
+           a.w % (g * sw) == 0;
+}
 
 int64_t next_pow2(int64_t v) {
     int64_t p = 1;
@@ -107,14 +151,16 @@ void set_vector_shape(int64_t lpr, int64_t vpt, int wg, int pf, rmsnorm_config *
     c->prefetch = pf;
 }
 
-// Element kernels: one row per kElemWG-lane workgroup, k elements per lane
-// (the smallest power of two with kElemWG * k >= N).
-void set_elem_shape(int64_t N, rmsnorm_config *c) {
-    int64_t k = 1;
-    while (rmsn::kElemWG * k < N) k <<= 1;
+// Element kernels: one row per kElemWG-lane workgroup, g elements per access,
+// k = ceil(N / (g * kElemWG)) accesses per lane. A one-row register prefetch
+// measured no faster (bf16 and fp32, 1500 to 15000 columns, one element per
+// access) and, in the backward, costs the second workgroup per CU from 5
+// elements per lane, so there is none.
+void set_elem_shape(int64_t N, int g, rmsnorm_config *c) {
     c->vector_path = kElemPath;
     c->lanes_per_row = rmsn::kElemWG;
-    c->vecs_per_lane = (int32_t)k;
+    c->vecs_per_lane = (int32_t)((N + int64_t(g) * rmsn::kElemWG - 1) / (int64_t(g) * rmsn::kElemWG));
+    c->elems_per_access = g;
     c->wg_threads = rmsn::kElemWG;
     c->rows_per_wg = 1;
     c->prefetch = 0;
@@ -131,7 +177,7 @@ void set_scalar_shape(rmsnorm_config *c) {
     c->prefetch = 0;
 }
 
-bool vector_ok(int64_t N, int dtype, bool aligned) { return aligned && (N * elem_size(dtype)) % 16 == 0; }
+bool vector_ok(int64_t N, int dtype, const Align &a) { return all16(a) && (N * elem_size(dtype)) % 16 == 0; }
 
 // A backward row on whole wavefronts whose count is not a power of two runs
 // on the kernels whose row is the whole workgroup (its size set at launch).
@@ -166,19 +212,19 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
     return 0;
 }
 
-void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, bool aligned, int64_t cus, rmsnorm_config *c) {
+void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, const Align &a, int64_t cus, rmsnorm_config *c) {
     const int64_t nvec = N * elem_size(dtype) / 16;
     const int64_t vmax = is_bwd ? wide_max_vecs(dtype) : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
-    if (!vector_ok(N, dtype, aligned)) {
+    if (!vector_ok(N, dtype, a)) {
         // rows that are not a multiple of 16 bytes or not 16-byte aligned:
-        // element kernels (the row read once into registers) for the
-        // backward and for fp32 forward rows, else the scalar kernel. With
-        // 2-byte elements the element forward's 1024-lane rows keep too few
-        // rows in flight: bf16 16384 x 4100 took 172 us against the scalar
-        // kernel's 131 (fp32 16384 x 4098: 99 against 177; backward 1.4-3x
-        // faster in every format).
-        if (elem_ok(N) && (is_bwd || elem_size(dtype) == 4))
-            set_elem_shape(N, c);
+        // the element kernels (the row read once into registers) from 257
+        // to 16384 columns, else the scalar kernel. At 16384 rows, against
+        // the scalar kernel: bf16 4100 columns (4 elements per access) 130
+        // -> 60 us forward and 459 -> 83 backward; bf16 4095 (one per
+        // access) 129 -> 62 and 463 -> 79; fp32 4098 (two per access) 177
+        // -> 102 and 491 -> 156 (see ladder_grid for the forward's grid).
+        if (elem_ok(N))
+            set_elem_shape(N, elem_group(N, dtype, a), c);
         else
             set_scalar_shape(c);
         return;
@@ -272,6 +318,14 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         // Inputs smaller than one XCD's L2 are likely still cache-resident (a
         // decode step's few rows): there they add latency (2.2 -> 2.5 us at
         // 1 x 4096), so they stay off.
+        // Element kernels with 2-byte activations: a resident grid whose
+        // workgroups walk the rows (bf16 16384 x 4100: 111 us against 164
+        // with a workgroup per row; 16384 x 1500: 53 against 79). With fp32
+        // activations a workgroup per row was 2-4% faster.
+        if (c->vector_path == kElemPath && elem_size(dtype) == 2) {
+            const int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
+            if (grid > resident) grid = resident;
+        }
         const int64_t in_bytes = M * N * elem_size(dtype);
         c->stream_loads = (c->vector_path == 1 && c->lanes_per_row >= 64 && in_bytes >= kStreamMinBytes) ? 1 : 0;
     } else {
@@ -339,7 +393,7 @@ int occupancy(const void *fn, int wg, int *blocks) {
 
 const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd, int res) {
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
-    if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane);
+    if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access);
     if (c.vector_path == kWidePath) {
         const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
         return e ? e->fn : nullptr;
@@ -355,13 +409,13 @@ const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd
 }
 
 // Full configuration on the current device (res: the residual-fused kernel).
-int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, bool aligned, rmsnorm_config *c,
+int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Align &a, rmsnorm_config *c,
             const void **fn) {
     std::memset(c, 0, sizeof *c);
     int cus = 0, blocks = 0;
     int st = device_info(&cus);
     if (st != RMSN_OK) return st;
-    ladder_shape(M, N, dtype, is_bwd, aligned, cus, c);
+    ladder_shape(M, N, dtype, is_bwd, a, cus, c);
     const void *k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     st = occupancy(k, c->wg_threads, &blocks);
@@ -390,21 +444,24 @@ int launch(const void *fn, int64_t grid, int wg, void **args, hipStream_t stream
 // the shape: the kernel must exist, cover the row, and the grid must be
 // positive. Shape fields derived from lanes_per_row are recomputed.
 int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, int is_bwd, int res,
-                    bool aligned, rmsnorm_config *c, const void **fn) {
+                    const Align &a, rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
     if (req->vector_path < 0 || req->vector_path > kElemPath) return RMSN_ECONFIG;
     if (req->vector_path == kElemPath) {
         const int64_t k = req->vecs_per_lane;
+        const int64_t g = req->elems_per_access ? req->elems_per_access : elem_group(N, dtype, a);
         if (req->lanes_per_row != rmsn::kElemWG || (req->wg_threads != 0 && req->wg_threads != rmsn::kElemWG) ||
-            k < 1 || k > rmsn::kElemMaxK || (k & (k - 1)) != 0 || int64_t(rmsn::kElemWG) * k < N ||
-            req->prefetch != 0 || req->stream_loads != 0)
+            !elem_group_ok(N, dtype, a, g) || k < 1 || k * g > rmsn::kElemMaxK ||
+            int64_t(rmsn::kElemWG) * k * g < N || req->prefetch != 0 || req->stream_loads != 0)
             return RMSN_ECONFIG;
-        set_elem_shape(N, c);
+        set_elem_shape(N, (int)g, c);
         c->vecs_per_lane = (int32_t)k;
+    } else if (req->elems_per_access != 0) {
+        return RMSN_ECONFIG;
     } else if (req->vector_path) {
         const int64_t nvec = N * elem_size(dtype) / 16;
-        if (!vector_ok(N, dtype, aligned)) return RMSN_ECONFIG;
+        if (!vector_ok(N, dtype, a)) return RMSN_ECONFIG;
         if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
         if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > 2)
             return RMSN_ECONFIG;
@@ -437,11 +494,11 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
     if (M == 0) return RMSN_OK;
     if (!x || !w || !y || (res && !h)) return RMSN_EINVAL;
     const int fused = res ? 1 : 0;
-    const bool aligned = aligned16(x) && aligned16(w) && aligned16(y) && (!fused || (aligned16(res) && aligned16(h)));
+    const Align a = fused ? align_of({x, y, res, h}, w) : align_of({x, y}, w);
+    if (!natural(a, dtype)) return RMSN_EINVAL;
     rmsnorm_config c;
     const void *fn = nullptr;
-    st = req ? explicit_config(req, M, N, dtype, 0, fused, aligned, &c, &fn)
-             : resolve(M, N, dtype, 0, fused, aligned, &c, &fn);
+    st = req ? explicit_config(req, M, N, dtype, 0, fused, a, &c, &fn) : resolve(M, N, dtype, 0, fused, a, &c, &fn);
     if (st != RMSN_OK) return st;
     int32_t n32 = (int32_t)N;
     int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
@@ -477,11 +534,11 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
     if (!x || !w || !dy || !rstd || !dx) return RMSN_EINVAL;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RMSN_EWORKSPACE;
     const int fused = dh ? 1 : 0;
-    const bool aligned = aligned16(x) && aligned16(w) && aligned16(dy) && aligned16(dx) && (!fused || aligned16(dh));
+    const Align a = fused ? align_of({x, dy, dx, dh}, w) : align_of({x, dy, dx}, w);
+    if (!natural(a, dtype)) return RMSN_EINVAL;
     rmsnorm_config c;
     const void *fn = nullptr;
-    st = req ? explicit_config(req, M, N, dtype, 1, fused, aligned, &c, &fn)
-             : resolve(M, N, dtype, 1, fused, aligned, &c, &fn);
+    st = req ? explicit_config(req, M, N, dtype, 1, fused, a, &c, &fn) : resolve(M, N, dtype, 1, fused, a, &c, &fn);
     if (st != RMSN_OK) return st;
     if (req) {
         if (workspace_bytes < (size_t)workspace_for(c)) return RMSN_EWORKSPACE;
@@ -548,8 +605,12 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     const int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!out || num_cus < 1 || blocks_per_cu < 1 || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
+    if (aligned < 0 || aligned > 16 || (aligned > 1 && (aligned & (aligned - 1)) != 0)) return RMSN_EINVAL;
+    // 0: every pointer only naturally aligned; 1: all 16-byte aligned; 2..16: that many bytes
+    const int v = aligned == 1 ? 16 : aligned;
+    const Align a{v > elem_size(dtype) ? v : elem_size(dtype), v > w_size(dtype) ? v : w_size(dtype)};
     std::memset(out, 0, sizeof *out);
-    ladder_shape(M, N, dtype, is_bwd, aligned != 0, num_cus, out);
+    ladder_shape(M, N, dtype, is_bwd, a, num_cus, out);
     ladder_grid(M, N, dtype, is_bwd, 0, num_cus, blocks_per_cu, out);
     ladder_prefetch(M, N, dtype, is_bwd, out);
     return RMSN_OK;
@@ -559,7 +620,7 @@ int rmsnorm_query_config(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_co
     const int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!out || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
-    return resolve(M, N, dtype, is_bwd, 0, true, out, nullptr);
+    return resolve(M, N, dtype, is_bwd, 0, Align{16, 16}, out, nullptr);
 }
 
 int rmsnorm_fwd(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype, void *y,
@@ -589,9 +650,10 @@ int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype) {
     // variant changes the answer.
     int64_t need = 0;
     for (int fused = 0; fused <= 1; ++fused) {
-        for (int aligned = 0; aligned <= 1; ++aligned) {
+        for (int v : {1, 4, 8, 16}) {  // every pointer alignment that selects a different kernel
+            const Align a{v > elem_size(dtype) ? v : elem_size(dtype), v > w_size(dtype) ? v : w_size(dtype)};
             rmsnorm_config c;
-            const int s = resolve(M, N, dtype, 1, fused, aligned != 0, &c, nullptr);
+            const int s = resolve(M, N, dtype, 1, fused, a, &c, nullptr);
             if (s != RMSN_OK) return s;
             const int64_t b = workspace_for(c);
             if (b > need) need = b;

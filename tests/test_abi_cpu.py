@@ -275,25 +275,32 @@ def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
     assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
 
 
-@pytest.mark.parametrize("N,dtype,aligned,k", [(257, rn.BF16, 1, 1), (1024, rn.BF16, 0, 1), (1025, rn.F16, 1, 2),
-                                               (4095, rn.BF16, 1, 4), (4100, rn.BF16_WF32, 1, 8),
-                                               (4096, rn.BF16, 0, 4), (5001, rn.F32, 1, 8), (16383, rn.F16, 1, 16),
-                                               (16384, rn.F32, 0, 16)])
-def test_ladder_element_cases(N, dtype, aligned, k):
+@pytest.mark.parametrize("N,dtype,aligned,k,g", [
+    (257, rn.BF16, 1, 1, 1), (1024, rn.BF16, 0, 1, 1), (1025, rn.F16, 1, 2, 1), (4095, rn.BF16, 1, 4, 1),
+    (4100, rn.BF16, 1, 2, 4),        # 8200-byte rows: 8-byte accesses
+    (4100, rn.BF16, 4, 3, 2),        # ... pointers only 4-byte aligned: 4-byte accesses
+    (4100, rn.BF16_WF32, 1, 2, 4),   # fp32 weights: 16-byte weight accesses
+    (4100, rn.F16_WF32, 2, 5, 1),
+    (4098, rn.F32, 1, 3, 2), (4096, rn.BF16, 0, 4, 1), (4104, rn.BF16, 8, 2, 4),
+    (8192, rn.BF16, 8, 2, 4), (16384, rn.F16, 8, 4, 4), (16384, rn.F32, 8, 8, 2), (16376, rn.BF16, 8, 4, 4),
+    (5001, rn.F32, 1, 5, 1), (10239, rn.F32, 1, 10, 1), (10241, rn.BF16, 1, 11, 1), (16383, rn.F16, 1, 16, 1),
+    (16384, rn.F32, 0, 16, 1)])
+def test_ladder_element_cases(N, dtype, aligned, k, g):
     """Rows that are not a multiple of 16 bytes, or not 16-byte aligned, of
-    257 to 16384 columns: the backward, and the forward of fp32 activations,
-    take the element kernels, 1024 lanes, the smallest power-of-two number of
-    elements per lane that covers the row, the backward persistent over the
-    grid of the other row kernels; the forward of 2-byte activations stays on
-    the scalar kernel."""
+    257 to 16384 columns: the element kernels, 1024 lanes, g elements per
+    access (the largest power of two, up to 16 bytes of activations or
+    weights, that divides N and the pointers' alignment), ceil(N / (1024 g))
+    accesses per lane, no prefetch; the backward persistent over the grid of
+    the other row kernels, the forward a workgroup per row for fp32
+    activations and a resident grid for 2-byte ones."""
     for is_bwd in (0, 1):
         c = cfg(4096, N, dtype, is_bwd, aligned=aligned)
-        if not is_bwd and dtype != rn.F32:
-            assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
-            continue
-        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["rows_per_wg"],
-                c["prefetch"], c["stream_loads"]) == (3, 1024, k, 1024, 1, 0, 0)
-        assert c["grid"] == (512 if is_bwd else 4096)
+        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["elems_per_access"], c["wg_threads"],
+                c["rows_per_wg"], c["prefetch"], c["stream_loads"]) == (3, 1024, k, g, 1024, 1, 0, 0)
+        assert c["grid"] == (512 if is_bwd or dtype != rn.F32 else 4096)
+        assert cfg(300, N, dtype, is_bwd, aligned=aligned)["grid"] == (256 if is_bwd else 300)
+        assert cfg(4096, N, dtype, is_bwd, aligned=aligned, blocks=1)["grid"] == (
+            256 if is_bwd or dtype != rn.F32 else 4096)
 
 
 def test_ladder_grid_and_workspace_shape():
@@ -432,21 +439,54 @@ def test_ladder_forward_mid_size_grid(dtype):
 
 def test_explicit_element_config_checks():
     """Element-kernel configurations through *_with_config are checked before
-    any HIP call: 1024 lanes, a power-of-two count of elements per lane up to
-    16 that covers the row, no prefetch, no streaming loads."""
+    any HIP call: 1024 lanes, 1 to 16 elements per lane covering the row, 1, 2,
+    4 or 8 elements per access dividing N and the pointers' alignment, no
+    prefetch, no streaming loads; elems_per_access is 0 on the other paths;
+    a pointer not aligned to its element type is refused."""
     L, C = rn.lib, rn.rmsnorm_config
 
-    def fwd(**kw):
-        c = C(vector_path=3, lanes_per_row=1024, vecs_per_lane=8, wg_threads=1024, grid=8)
+    def conf(kw):
+        c = C(vector_path=3, lanes_per_row=1024, vecs_per_lane=8, elems_per_access=1, wg_threads=1024, grid=8)
         for k, v in kw.items():
             setattr(c, k, v)
-        return L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, 64, 4100, rn.BF16, FAKE, FAKE, c, None)
+        return c
+
+    def fwd(**kw):
+        return L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, 64, 4100, rn.BF16, FAKE, FAKE, conf(kw), None)
+
+    def bwd(N, **kw):
+        return L.rmsnorm_bwd_with_config(FAKE, FAKE, FAKE, FAKE, 64, N, rn.BF16, FAKE, FAKE, FAKE, 1 << 30,
+                                         conf(kw), None)
+
+    def bwd_res(N, **kw):
+        return L.rmsnorm_bwd_residual(FAKE, FAKE, FAKE, FAKE, FAKE, 64, N, rn.BF16, FAKE, FAKE, FAKE, 1 << 30,
+                                      conf(kw), None)
 
     assert fwd(vecs_per_lane=4) == rn.ECONFIG       # 4096 elements do not cover 4100
-    assert fwd(vecs_per_lane=6) == rn.ECONFIG       # not a power of two
-    assert fwd(vecs_per_lane=32) == rn.ECONFIG      # beyond 16
+    assert fwd(vecs_per_lane=17) == rn.ECONFIG      # beyond 16
+    assert fwd(vecs_per_lane=0) == rn.ECONFIG
     assert fwd(lanes_per_row=512) == rn.ECONFIG
     assert fwd(wg_threads=512) == rn.ECONFIG
     assert fwd(prefetch=1) == rn.ECONFIG
+    assert fwd(prefetch=-1) == rn.ECONFIG
     assert fwd(stream_loads=1) == rn.ECONFIG
     assert fwd(vector_path=4) == rn.ECONFIG
+    assert fwd(elems_per_access=3) == rn.ECONFIG
+    assert fwd(elems_per_access=8, vecs_per_lane=1) == rn.ECONFIG     # 8 does not divide 4100
+    assert fwd(elems_per_access=4, vecs_per_lane=8) == rn.ECONFIG     # 32 elements per lane
+    assert fwd(elems_per_access=4, vecs_per_lane=1) == rn.ECONFIG     # 4096 elements do not cover 4100
+    assert L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, 64, 4100, rn.BF16, FAKE + 4, FAKE,
+                                     conf(dict(elems_per_access=4, vecs_per_lane=2)), None) == rn.ECONFIG
+    assert L.rmsnorm_fwd_with_config(FAKE, FAKE + 8, 1e-5, 64, 4100, rn.BF16_WF32, FAKE, FAKE,
+                                     conf(dict(elems_per_access=4, vecs_per_lane=2)), None) == rn.ECONFIG
+    assert L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, 64, 4096, rn.BF16, FAKE, FAKE,
+                                     C(vector_path=1, lanes_per_row=512, vecs_per_lane=1, elems_per_access=2,
+                                       grid=8), None) == rn.ECONFIG
+    # pointers not aligned to their element type
+    assert L.rmsnorm_fwd(FAKE + 1, FAKE, 1e-5, 64, 4100, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_fwd(FAKE, FAKE + 2, 1e-5, 64, 4100, rn.BF16_WF32, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_fwd(FAKE, FAKE, 1e-5, 64, 4100, rn.F32, FAKE + 2, FAKE, None) == rn.EINVAL
+    assert bwd(4100, vecs_per_lane=5, prefetch=1) == rn.ECONFIG
+    assert bwd(14000, vecs_per_lane=13) == rn.ECONFIG                # 13312 elements do not cover 14000
+    assert bwd_res(4100, vecs_per_lane=5, stream_loads=1) == rn.ECONFIG
+    assert bwd_res(4100, vecs_per_lane=5, lanes_per_row=256) == rn.ECONFIG

@@ -419,16 +419,19 @@ def test_forward_mid_size_grid(fmt):
 @pytest.mark.parametrize("residual", [False, True])
 def test_every_element_kernel(fmt, residual):
     """The element kernels (rows that are not a multiple of 16 bytes), every
-    elements-per-lane count, every format, plain and residual: the ladder's
-    own configuration, and the backward forced to a grid of 3 so workgroups
-    walk several rows; 7 rows, the row length 5 short of 1024 * K."""
+    format, plain and residual, every elements-per-lane count (K = 1..16): the
+    ladder's own configuration, and the kernels forced to a grid of 3 so that
+    workgroups walk several rows; 7 rows, of 5 elements short of 1024 * K
+    and of one element past 1024 * (K - 1) (only lane 0 holds an element at
+    k = K - 1)."""
     act, wst, code = FORMATS[fmt]
     eps = si.eps_f32(1e-6)
-    for k in (1, 2, 4, 8, 16):
-        M, N = 7, 1024 * k - 5
-        _, _, x, w, dy = _case(M, N, fmt, seed=7000 + k)
-        c = rn.rmsnorm_query_config(M, N, code, 1)
-        assert (c.vector_path, c.vecs_per_lane) == (3, k), c.as_dict()
+    for k, N in [(k, n) for k in range(1, 17) for n in (1024 * k - 5, 1024 * (k - 1) + 1) if n >= 257]:
+        M = 7
+        _, _, x, w, dy = _case(M, N, fmt, seed=7000 + N)
+        for d in (0, 1):
+            c = rn.rmsnorm_query_config(M, N, code, d)
+            assert (c.vector_path, c.vecs_per_lane, c.prefetch) == (3, k, 0), c.as_dict()
         forced = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, wg_threads=1024, grid=3)
         for cfg in (None, forced):
             _say(f"element kernel k={k} N={N} {fmt} residual={residual} cfg={None if cfg is None else cfg.as_dict()}")
@@ -440,34 +443,84 @@ def test_every_element_kernel(fmt, residual):
                 plain_check(x, w, dy, eps, act, wst, cfg=cfg)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "f32", "f16w32"])
-def test_element_kernels_on_unaligned_pointers(fmt):
-    """16-byte-multiple rows whose pointers are not 16-byte aligned (views one
-    element into larger buffers) take the element kernels; outputs against the
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("residual", [False, True])
+def test_element_kernels_grouped(fmt, residual):
+    """Element kernels moving G > 1 consecutive elements per access: rows of
+    N = G * (1024 K - 1) columns (G the largest power of two dividing N, so
+    the ladder picks G) for the smallest, a middle and the largest K that G
+    allows; where G accesses are 16 bytes wide the row is vectorisable and the
+    element kernel is forced (elems_per_access = G). The ladder's
+    configuration, and the same kernel on a grid of 3 so that workgroups walk
+    several rows; 7 rows."""
+    act, wst, code = FORMATS[fmt]
+    s = 4 if act == "f32" else 2
+    big = max(s, 4 if wst == "f32" else 2)
+    eps = si.eps_f32(1e-6)
+    for g in (2, 4, 8):
+        if g * big > 16:
+            continue
+        kmax = 16 // g
+        for k in sorted({1, max(1, kmax // 2), kmax}):
+            M, N = 7, g * (1024 * k - 1)
+            if N < 257:
+                continue
+            _, _, x, w, dy = _case(M, N, fmt, seed=7400 + N)
+            forced = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, elems_per_access=g,
+                                       wg_threads=1024, grid=3)
+            if g * s < 16:
+                for d in (0, 1):
+                    c = rn.rmsnorm_query_config(M, N, code, d)
+                    assert (c.vector_path, c.vecs_per_lane, c.elems_per_access) == (3, k, g), c.as_dict()
+                cfgs = (None, forced)
+            else:
+                ladder = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, elems_per_access=g,
+                                           wg_threads=1024, grid=M)
+                cfgs = (ladder, forced)
+            for cfg in cfgs:
+                _say(f"grouped element kernel g={g} k={k} N={N} {fmt} residual={residual} "
+                     f"cfg={None if cfg is None else cfg.as_dict()}")
+                if residual:
+                    res = si.random_tensor((M, N), act, seed=7500 + N)
+                    dh = si.random_tensor((M, N), act, seed=7600 + N, scale=1e-2)
+                    residual_check(x, res, w, dy, dh, eps, act, wst, cfg=cfg)
+                else:
+                    plain_check(x, w, dy, eps, act, wst, cfg=cfg)
+
+
+@pytest.mark.parametrize("fmt,off", [("bf16", 1), ("bf16", 2), ("bf16", 4), ("f32", 1), ("f32", 2),
+                                     ("f16w32", 1), ("f16w32", 2)])
+def test_element_kernels_on_unaligned_pointers(fmt, off):
+    """16-byte-multiple rows whose pointers are not 16-byte aligned (views
+    `off` elements into larger buffers: 2- to 8-byte alignment, so one to four
+    elements per access) take the element kernels; outputs against the
     oracle, and nothing written outside the views."""
     act, wst, code = FORMATS[fmt]
     M, N = 37, 4096
-    _, _, x, w, dy = _case(M, N, fmt, seed=7300)
+    _, _, x, w, dy = _case(M, N, fmt, seed=7300 + off)
     eps = si.eps_f32(1e-6)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[act]
 
     def view_of(a, dtype):
-        d = to_device(np.concatenate([a.reshape(-1)[:1], a.reshape(-1)]), dtype)
-        return d[1:]
+        d = to_device(np.concatenate([a.reshape(-1)[:off], a.reshape(-1)]), dtype)
+        return d[off:]
 
     xd, dyd = view_of(x, act), view_of(dy, act)
     wd = view_of(w, wst)
-    ybuf = torch.full((M * N + 2,), float("nan"), dtype=tdt, device="cuda")
-    dxbuf = torch.full((M * N + 2,), float("nan"), dtype=tdt, device="cuda")
-    y, dx = ybuf[1:M * N + 1], dxbuf[1:M * N + 1]
+    ybuf = torch.full((M * N + 2 * off,), float("nan"), dtype=tdt, device="cuda")
+    dxbuf = torch.full((M * N + 2 * off,), float("nan"), dtype=tdt, device="cuda")
+    y, dx = ybuf[off:M * N + off], dxbuf[off:M * N + off]
+    assert y.data_ptr() % 16 != 0 and xd.data_ptr() % 16 != 0
     rstd = torch.full((M,), float("nan"), device="cuda")
     dw = torch.full((N,), float("nan"), device="cuda")
+    _say(f"unaligned element kernels {fmt} off={off}")
     rn.rmsnorm_fwd(xd, wd, eps, M, N, code, y, rstd)
     nb = rn.rmsnorm_bwd_workspace_bytes(M, N, code)
     ws = torch.empty(nb // 4 + 64, device="cuda")
     rn.rmsnorm_bwd(xd, wd, dyd, rstd, M, N, code, dx, dw, ws, nb)
     torch.cuda.synchronize()
-    assert torch.isnan(ybuf[0]) and torch.isnan(ybuf[-1]) and torch.isnan(dxbuf[0]) and torch.isnan(dxbuf[-1])
+    assert torch.isnan(ybuf[:off]).all() and torch.isnan(ybuf[M * N + off:]).all()
+    assert torch.isnan(dxbuf[:off]).all() and torch.isnan(dxbuf[M * N + off:]).all()
     oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
     check_rows(to_host(y, act).reshape(M, N), oy, act, "y (unaligned)")
     check_rstd(rstd.cpu().numpy(), orr)
