@@ -134,6 +134,8 @@ constexpr int64_t kElemMinN = 257;  // narrower unvectorisable rows keep the sca
 constexpr int kFwdMaxVecs = 4;
 // forward row blocks per CU (inclusive range) taking a prefetching grid of kFwdMidPerCU workgroups per CU
 constexpr int64_t kFwdMidLo = 4, kFwdMidHi = 8, kFwdMidPerCU = 3;
+constexpr int64_t kFwdWidePerCU = 2;     // resident forward workgroups per CU with fp32 weights
+constexpr int64_t kFwdWideMinLanes = 128;  // ... for rows of at least this many lanes
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
@@ -318,6 +320,22 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         // Inputs smaller than one XCD's L2 are likely still cache-resident (a
         // decode step's few rows): there they add latency (2.2 -> 2.5 us at
         // 1 x 4096), so they stay off.
+        // 16-bit activations with fp32 weights: each one-block workgroup
+        // re-reads the weights (twice the bytes of a 16-bit row) from cache.
+        // A resident grid of two workgroups per CU keeps them in registers
+        // over its rows (plain call, rows of 128 lanes or more, beyond the
+        // mid-size range). bf16 weights fp32: 32768 x 8192 184 -> 175 us,
+        // 8192 x 16384 92.9 -> 89.1, 4096 x 32768 93.6 -> 92.2, 16384 x 4096
+        // 45.6 -> 44.6 (fp16 likewise). Narrower rows lose: 65536 x 2048
+        // (64 lanes) 88.3 -> 89.5, 1M x 128 88 -> 129. With 16-bit weights
+        // the same grid was 0-4% slower.
+        if (!res && c->vector_path == 1 && elem_size(dtype) == 2 && w_size(dtype) == 4 &&
+            c->lanes_per_row >= kFwdWideMinLanes && row_blocks > kFwdMidHi * cus) {
+            int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
+            if (resident > kFwdWidePerCU * cus) resident = kFwdWidePerCU * cus;
+            grid = row_blocks < resident ? row_blocks : resident;
+            c->prefetch = 0;
+        }
         // Element kernels with 2-byte activations: a resident grid whose
         // workgroups walk the rows (bf16 16384 x 4100: 111 us against 164
         // with a workgroup per row; 16384 x 1500: 53 against 79). With fp32

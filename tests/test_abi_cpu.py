@@ -110,14 +110,27 @@ def test_dtype_codes():
 @pytest.mark.parametrize("dtype", [rn.F16, rn.BF16_WF32, rn.F16_WF32])
 def test_ladder_covers_new_formats(dtype):
     # 16-bit activations: the same shapes as bf16, except that the wide-row
-    # backward prefetches only when the weights are 16-bit too
-    for N, is_bwd in ((4096, 0), (4096, 1), (128, 0), (32768, 1)):
+    # backward prefetches only when the weights are 16-bit too, and that the
+    # forward with fp32 weights runs a resident grid of two workgroups per CU
+    # beyond 8 row blocks per CU (so that the weights stay in registers)
+    for N, is_bwd in ((4096, 0), (4096, 1), (128, 0), (32768, 1), (32768, 0)):
         a = cfg(16384, N, dtype, is_bwd)
         b = cfg(16384, N, rn.BF16, is_bwd)
         if a["vector_path"] == 2 and dtype != rn.F16:
             assert a["prefetch"] == 0 and b["prefetch"] == 1
             a["prefetch"] = b["prefetch"]
+        if not is_bwd and dtype != rn.F16 and N != 128:   # 128 columns: 1024 row blocks, 4 per CU
+            assert a["grid"] == a["partial_rows"] == 512 and a["prefetch"] == 0 and b["grid"] > 512
+            a["grid"], a["partial_rows"] = b["grid"], b["partial_rows"]
         assert a == b
+    # fp32 weights: at most the resident workgroups; mid-size inputs keep the mid-size grid;
+    # rows of under 128 lanes keep one block per workgroup
+    if dtype != rn.F16:
+        assert cfg(65536, 2048, dtype, 0)["grid"] == 65536 // cfg(65536, 2048, dtype, 0)["rows_per_wg"]
+        assert cfg(1 << 20, 128, dtype, 0)["grid"] == cfg(1 << 20, 128, rn.BF16, 0)["grid"]
+        assert cfg(16384, 4096, dtype, 0, blocks=1)["grid"] == 256
+        c, d = cfg(2048, 4096, dtype, 0), cfg(2048, 4096, rn.BF16, 0)
+        assert (c["grid"], c["prefetch"]) == (d["grid"], d["prefetch"]) == (768, 1)
 
 
 def test_ladder_backward_grid_and_prefetch():
@@ -420,9 +433,12 @@ def test_explicit_whole_wavefront_config_checks():
 @pytest.mark.parametrize("dtype", [rn.F32, rn.BF16, rn.F16, rn.BF16_WF32, rn.F16_WF32])
 def test_ladder_forward_mid_size_grid(dtype):
     """Forward inputs of 4 to 8 row blocks per compute unit on 256-lane
-    workgroups: a grid of three per CU prefetching the next block; fewer or
-    more row blocks keep one block per workgroup without prefetch."""
+    workgroups: a grid of three per CU prefetching the next block; fewer row
+    blocks keep one block per workgroup without prefetch, and so do more,
+    except rows of 128 lanes or more with fp32 weights and 16-bit
+    activations (two per CU)."""
     es = 4 if dtype == rn.F32 else 2
+    w32 = dtype in (rn.BF16_WF32, rn.F16_WF32)
     for M, N in ((2048, 4096), (4096, 2048), (8192, 2048), (1024, 8192)):
         c = cfg(M, N, dtype, 0)
         rb = -(-M // c["rows_per_wg"])
@@ -432,7 +448,9 @@ def test_ladder_forward_mid_size_grid(dtype):
             assert mid
     for M, N in ((512, 4096), (16384, 4096), (16384, 2048)):
         c = cfg(M, N, dtype, 0)
-        assert (c["grid"], c["prefetch"]) == (-(-M // c["rows_per_wg"]), 0), (M, N, c)
+        rb = -(-M // c["rows_per_wg"])
+        wide = w32 and rb > 8 * 256 and c["lanes_per_row"] >= 128
+        assert (c["grid"], c["prefetch"]) == ((512, 0) if wide else (rb, 0)), (M, N, c)
     # the residual-fused call keeps one block per workgroup (queried on the device, not here);
     # an explicit configuration keeps its own prefetch (checked with the other explicit tests)
 
