@@ -18,8 +18,10 @@ from parity_util import check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd, term
 
 
 @pytest.mark.parametrize("is_bwd", [0, 1])
-def test_tuned_config_is_correct_and_cached(is_bwd, tmp_path):
-    M, N, dtype = 2048, 1024, "bf16"
+@pytest.mark.parametrize("M,N", [(2048, 1024), (1000, 4100)])   # 4100: the element kernels
+def test_tuned_config_is_correct_and_cached(is_bwd, M, N, tmp_path):
+    dtype = "bf16"
+    print(f"tune M={M} N={N} is_bwd={is_bwd}", flush=True)
     path = str(tmp_path / "tuned.json")
     cfg = tune.best_config(M, N, rn.BF16, is_bwd, cache_path=path, budget_s=5.0)
     entry = next(iter(tune.load_cache(path).values()))
