@@ -33,7 +33,7 @@
  *     default stream). Nothing synchronises the host.
  *   - Argument checks run before any HIP call. M == 0 is a valid no-op.
  *   - Any N >= 1 is accepted. Every pointer must be aligned to its element
- *     type (2 or 4 bytes; RMSN_EINVAL otherwise). 16-byte vector loads are
+ *     type (2 or 4 bytes; rstd and dW 4; RMSN_EINVAL otherwise). 16-byte vector loads are
  *     used when N * sizeof(elem) is a multiple of 16 and every matrix/vector
  *     pointer is 16-byte aligned; otherwise kernels of the same arithmetic
  *     with narrower accesses run (rows of 257 to 16384 columns: groups of

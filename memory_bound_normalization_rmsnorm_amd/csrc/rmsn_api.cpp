@@ -34,6 +34,7 @@ int elem_size(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
 bool valid_dtype(int dtype) { return dtype >= RMSN_F32 && dtype <= RMSN_F16_WF32; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // bytes per weight element
 int w_size(int dtype) { return (dtype == RMSN_BF16 || dtype == RMSN_F16) ? 2 : 4; }
@@ -513,7 +514,7 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
     if (!x || !w || !y || (res && !h)) return RMSN_EINVAL;
     const int fused = res ? 1 : 0;
     const Align a = fused ? align_of({x, y, res, h}, w) : align_of({x, y}, w);
-    if (!natural(a, dtype)) return RMSN_EINVAL;
+    if (!natural(a, dtype) || !aligned4(rstd)) return RMSN_EINVAL;
     rmsnorm_config c;
     const void *fn = nullptr;
     st = req ? explicit_config(req, M, N, dtype, 0, fused, a, &c, &fn) : resolve(M, N, dtype, 0, fused, a, &c, &fn);
@@ -528,7 +529,7 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
 
 int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStream_t s) {
     if (N < 1 || N > kMaxN || P < 0) return RMSN_EINVAL;
-    if (!dw) return RMSN_EINVAL;
+    if (!dw || !aligned4(dw)) return RMSN_EINVAL;
     if (P > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)) return RMSN_EWORKSPACE;
     const float *cpartial = static_cast<const float *>(workspace);
     int64_t ldp = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
@@ -553,7 +554,7 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RMSN_EWORKSPACE;
     const int fused = dh ? 1 : 0;
     const Align a = fused ? align_of({x, dy, dx, dh}, w) : align_of({x, dy, dx}, w);
-    if (!natural(a, dtype)) return RMSN_EINVAL;
+    if (!natural(a, dtype) || !aligned4(rstd)) return RMSN_EINVAL;
     rmsnorm_config c;
     const void *fn = nullptr;
     st = req ? explicit_config(req, M, N, dtype, 1, fused, a, &c, &fn) : resolve(M, N, dtype, 1, fused, a, &c, &fn);
@@ -584,6 +585,7 @@ int bwd_impl(const void *x, const void *w, const void *dy, const void *dh, const
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!aligned4(dw)) return RMSN_EINVAL;
     if (M == 0) {
         if (!dw) return RMSN_OK;
         int64_t n = N;

@@ -504,6 +504,13 @@ def test_explicit_element_config_checks():
     assert L.rmsnorm_fwd(FAKE + 1, FAKE, 1e-5, 64, 4100, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
     assert L.rmsnorm_fwd(FAKE, FAKE + 2, 1e-5, 64, 4100, rn.BF16_WF32, FAKE, FAKE, None) == rn.EINVAL
     assert L.rmsnorm_fwd(FAKE, FAKE, 1e-5, 64, 4100, rn.F32, FAKE + 2, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_fwd(FAKE, FAKE, 1e-5, 64, 4096, rn.BF16, FAKE, FAKE + 2, None) == rn.EINVAL     # rstd
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, FAKE + 2, 64, 4096, rn.BF16, FAKE, FAKE, FAKE, 1 << 30,
+                         None) == rn.EINVAL                                                         # rstd
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, FAKE, 64, 4096, rn.BF16, FAKE, FAKE + 2, FAKE, 1 << 30,
+                         None) == rn.EINVAL                                                         # dW
+    assert L.rmsnorm_bwd(FAKE, FAKE, FAKE, FAKE, 0, 4096, rn.BF16, FAKE, FAKE + 2, FAKE, 1 << 30,
+                         None) == rn.EINVAL                                                         # dW, M = 0
     assert bwd(4100, vecs_per_lane=5, prefetch=1) == rn.ECONFIG
     assert bwd(14000, vecs_per_lane=13) == rn.ECONFIG                # 13312 elements do not cover 14000
     assert bwd_res(4100, vecs_per_lane=5, stream_loads=1) == rn.ECONFIG
