@@ -125,10 +125,12 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     rows keep the register kernel up to 4 vectors per lane (as fast) and
 //     take the wide kernel from 5 to 8 (the register kernel spills there). One
 //     wide workgroup per compute unit (its LDS allows no more at 4 vectors).
-//   Anything the vector kernels cannot take (N*elem not a multiple of 16
-//     bytes, unaligned pointers, more than 1024 * 8 vectors forward, or
-//     backward more than 1024 * 4 16-bit or 1024 * 8 fp32 vectors) goes to
-//     the scalar kernel.
+//   Rows the vector kernels cannot take because N*elem is not a multiple of
+//     16 bytes or a pointer is not 16-byte aligned go to the element kernels
+//     from 257 to 16384 columns (see ladder_shape); those and anything else
+//     they cannot take (more than 1024 * 8 vectors forward, or backward more
+//     than 1024 * 4 16-bit or 1024 * 8 fp32 vectors) go to the scalar
+//     kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
 constexpr int kElemPath = 3;  // rmsnorm_config::vector_path of the element kernels
 constexpr int64_t kElemMinN = 257;  // narrower unvectorisable rows keep the scalar kernel

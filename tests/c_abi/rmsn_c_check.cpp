@@ -212,7 +212,9 @@ int main() {
     ok &= run_case<uint16_t>(257, 4096, true, 1);    // vector path, ragged row count
     ok &= run_case<uint16_t>(64, 32768, true, 2);    // wide-row backward
     ok &= run_case<uint16_t>(1000, 128, true, 3);    // several rows per wavefront
-    ok &= run_case<float>(33, 257, false, 4);        // scalar path (row not a multiple of 16 bytes)
+    ok &= run_case<float>(33, 257, false, 4);        // element kernels (row not a multiple of 16 bytes)
+    ok &= run_case<uint16_t>(9, 4100, true, 6);      // element kernels, 4 elements per access
+    ok &= run_case<float>(7, 13, false, 7);          // scalar path (13 columns)
     ok &= run_case<float>(96, 1024, false, 5);
     std::printf("%s\n", ok ? "ok" : "FAILED");
     return ok ? 0 : 1;

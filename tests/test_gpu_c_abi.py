@@ -1,7 +1,7 @@
 """The library through its C ABI alone: tests/c_abi/rmsn_c_check, a C++
 program with no Python or torch in its process, runs the forward and the
 backward on hipMalloc buffers for bf16 and fp32 shapes (vector, wide-row,
-narrow-row and scalar kernels) and checks every output element against the
+narrow-row, element and scalar kernels) and checks every output element against the
 fp64 oracle it links. Built by the repository's build step."""
 
 from __future__ import annotations

@@ -126,13 +126,17 @@ def test_formats_scalar_and_unaligned(fmt):
     plain_check(x, w, dy, si.eps_f32(1e-5), act, wst, cfg=rn.rmsnorm_config(vector_path=0, grid=5))
     xd = to_device(np.concatenate([x.reshape(-1)[:1], x.reshape(-1)]))[1:]
     wd = to_device(np.concatenate([w[:1], w]))[1:]
-    y = torch.full((M * N + 1,), float("nan"), dtype=xd.dtype, device="cuda")[1:]
-    rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
-    rn.rmsnorm_fwd(xd, wd, si.eps_f32(1e-5), M, N, FORMATS[fmt][2], y, rstd)
-    torch.cuda.synchronize()
     oy, orr = oracle.fwd(x, w, si.eps_f32(1e-5), act, wdtype=wst)
-    check_rows(to_host(y, act).reshape(M, N), oy, act, "y (unaligned)")
-    check_rstd(rstd.cpu().numpy(), orr)
+    for forced in (None, rn.rmsnorm_config(vector_path=0, grid=5)):   # the ladder (element kernels), the scalar
+        y = torch.full((M * N + 1,), float("nan"), dtype=xd.dtype, device="cuda")[1:]
+        rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        if forced is None:
+            rn.rmsnorm_fwd(xd, wd, si.eps_f32(1e-5), M, N, FORMATS[fmt][2], y, rstd)
+        else:
+            rn.rmsnorm_fwd_with_config(xd, wd, si.eps_f32(1e-5), M, N, FORMATS[fmt][2], y, rstd, forced)
+        torch.cuda.synchronize()
+        check_rows(to_host(y, act).reshape(M, N), oy, act, "y (unaligned)")
+        check_rstd(rstd.cpu().numpy(), orr)
 
 
 def test_fp16_range():

@@ -116,21 +116,26 @@ def test_every_vector_kernel(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_scalar_path_forced_and_unaligned(dtype):
-    """The scalar kernel (forced, and chosen for unaligned pointers)."""
+    """The scalar kernel forced, on aligned buffers and on unaligned views
+    (one element into larger buffers; the ladder gives those the element
+    kernels, checked here too)."""
     M, N = 37, 4096
     x, w, dy = si.random_case(M, N, dtype, seed=77, dy_scale=1e-2)
     cfg = rn.rmsnorm_config(vector_path=0, grid=5)
     full_check(x, w, dy, si.eps_f32(1e-5), dtype, cfg_f=cfg, cfg_b=cfg)
-    # unaligned: views one element into larger buffers
     xd = to_device(np.concatenate([x.reshape(-1)[:1], x.reshape(-1)]), dtype)[1:]
     wd = to_device(np.concatenate([w[:1], w]), dtype)[1:]
-    y = torch.full((M * N + 1,), float("nan"), dtype=xd.dtype, device="cuda")[1:]
-    rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
-    rn.rmsnorm_fwd(xd, wd, si.eps_f32(1e-5), M, N, DT[dtype], y, rstd)
-    torch.cuda.synchronize()
     oy, orr = oracle.fwd(x, w, si.eps_f32(1e-5), dtype)
-    check_rows(to_host(y, dtype).reshape(M, N), oy, dtype, "y (unaligned)")
-    check_rstd(rstd.cpu().numpy(), orr)
+    for forced in (None, cfg):
+        y = torch.full((M * N + 1,), float("nan"), dtype=xd.dtype, device="cuda")[1:]
+        rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        if forced is None:
+            rn.rmsnorm_fwd(xd, wd, si.eps_f32(1e-5), M, N, DT[dtype], y, rstd)
+        else:
+            rn.rmsnorm_fwd_with_config(xd, wd, si.eps_f32(1e-5), M, N, DT[dtype], y, rstd, forced)
+        torch.cuda.synchronize()
+        check_rows(to_host(y, dtype).reshape(M, N), oy, dtype, f"y (unaligned, {'scalar' if forced else 'ladder'})")
+        check_rstd(rstd.cpu().numpy(), orr)
 
 
 def test_backward_with_oracle_rstd():
