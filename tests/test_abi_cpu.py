@@ -247,7 +247,10 @@ def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
     (1024, rn.F32, 1, 256, 1),
     (4096, rn.BF16, 0, 128, 4),
     (4096, rn.BF16, 1, 512, 1),
-    (5120, rn.BF16, 0, 256, 3),
+    (5120, rn.BF16, 0, 128, 5),    # 640 vectors: exactly 5 per lane on 128 lanes
+    (10240, rn.BF16, 0, 256, 5),
+    (2560, rn.F32, 0, 128, 5),
+    (2560, rn.BF16, 0, 128, 3),    # 320 vectors: 64 lanes x 5 measured a tie; kept
     (5120, rn.BF16, 1, 640, 1),    # whole wavefronts (4096 rows: a short walk)
     (7168, rn.BF16, 0, 256, 4),
     (7168, rn.BF16, 1, 1024, 1),
