@@ -256,12 +256,13 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, const Align &a, i
         lpr = next_pow2((nvec + kFwdMaxVecs - 1) / kFwdMaxVecs);
         if (lpr < 64) lpr = 64;
         if (lpr > kMaxVecLanes) lpr = kMaxVecLanes;
-        // Rows of exactly 5 vectors on each of 128 or 256 lanes
-        // fill every slot at 5 per lane, where the rule above leaves a fifth
-        // of them idle at 3 per lane: bf16 16384 x 5120 56.0 -> 54.7 us,
-        // 32768 x 5120 111.3 -> 108.2, 8192 x 10240 57.4 -> 56.7; fp32 16384
-        // x 2560 56.0 -> 54.3. Exact rows at 7 per lane (896, 1792 vectors)
-        // measured -0.7..+0.5%, so only 5.
+        // Rows of exactly 5 vectors on each of 128 or 256 lanes fill every
+        // slot at 5 per lane, where the rule above leaves a fifth of them
+        // idle at 3 per lane: bf16 16384 x 5120 56.0 -> 54.7 us, 32768 x 5120
+        // 111.3 -> 108.2, 16384 x 10240 112.2 -> 110.8; fp32 16384 x 2560
+        // 56.0 -> 54.3. At 512 lanes (20480 columns), at 64 (2560 bf16) and
+        // at 7 per lane (896, 1792 vectors) it measured a tie (-0.7..+0.5%),
+        // so only these.
         const int64_t l5 = nvec / kFwdExactVecs;
         if (nvec % kFwdExactVecs == 0 && l5 >= 128 && l5 <= 256 && (l5 & (l5 - 1)) == 0) lpr = l5;
     }
