@@ -62,7 +62,7 @@ def parse_args(argv=None):
     ap.add_argument("--eager-only", action="store_true",
                     help="per-kernel times from eager batches only, no HIP graphs (counter-collection runs)")
     ap.add_argument("--cells", default="all", help="cells mode: comma-separated groups (configs, formats, "
-                    "residual, latency, pages) or all")
+                    "residual, latency, element, pages) or all")
     ap.add_argument("--mode", default="bench", choices=["bench", "kernels", "copy", "cells"],
                     help="bench: full run; kernels: the warmup steps, then each kernel's graph replays "
                          "(eager batches with --eager-only), for profilers; "
@@ -647,6 +647,7 @@ def main(argv=None):
 # RMSNorm kernel actually costs on Hopper", section 07); the fused residual
 # add ("Profiling, GPU utilisation and writing a fused kernel", Problem 15);
 # the latency regime at d = 4096 (same page, the benchmark of Problem 15);
+# rows that are not a multiple of 16 bytes (the element kernels);
 # the shapes the other pages test (hello-gpu ch. 13 section 13.4 and 13.5;
 # "RMSNorm backward (almost) without the column reduction", its benchmark).
 CELL_GROUPS = {
@@ -660,11 +661,13 @@ CELL_GROUPS = {
     "residual": [("bf16_16384x4096", "bf16", 16384, 4096), ("bf16_32768x8192", "bf16", 32768, 8192),
                  ("f16w32_16384x4096", "f16w32", 16384, 4096), ("bf16_1024x4096", "bf16", 1024, 4096)],
     "latency": [(f"bf16_{m}x4096", "bf16", m, 4096) for m in (1, 16, 256, 4096, 32768)],
+    "element": [("bf16_16384x4100", "bf16", 16384, 4100), ("bf16_16384x4095", "bf16", 16384, 4095),
+                ("fp32_16384x4098", "f32", 16384, 4098)],
     "pages": [("fp32_3x13", "f32", 3, 13), ("fp32_33x257", "f32", 33, 257), ("fp32_1024x4096", "f32", 1024, 4096),
               ("bf16_16384x8192", "bf16", 16384, 8192)],
 }
 CELL_VARIANTS = {"configs": ("fused", "unfused"), "formats": ("fused",), "residual": ("residual", "residual_unfused"),
-                 "latency": ("fused", "unfused"), "pages": ("fused", "unfused")}
+                 "latency": ("fused", "unfused"), "element": ("fused",), "pages": ("fused", "unfused")}
 FMT = {"f32": ("f32", 4, 4), "bf16": ("bf16", 2, 2), "f16": ("f16", 2, 2), "bf16w32": ("bf16", 2, 4),
        "f16w32": ("f16", 2, 4)}  # activation storage, activation bytes, weight bytes
 

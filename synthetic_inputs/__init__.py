@@ -122,6 +122,9 @@ WORKLOADS = {
                  description="bf16 16384x5120, eps 1e-5; x~N(0,1), w~U(0.5,1.5), dy~1e-2 N(0,1)"),
         Workload("bf16_16384x7168", "bf16", 16384, 7168, 1e-5, "uniform", 1e-2, 520,
                  description="bf16 16384x7168, eps 1e-5; x~N(0,1), w~U(0.5,1.5), dy~1e-2 N(0,1)"),
+        Workload("bf16_16384x4100", "bf16", 16384, 4100, 1e-5, "uniform", 1e-2, 530,
+                 description="bf16 16384x4100 (8200-byte rows, not a multiple of 16 bytes), eps 1e-5; "
+                             "x~N(0,1), w~U(0.5,1.5), dy~1e-2 N(0,1)"),
     ]
 }
 
