@@ -341,7 +341,7 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         // 8192 x 16384 92.9 -> 89.1, 4096 x 32768 93.6 -> 92.2, 16384 x 4096
         // 45.6 -> 44.6 (fp16 likewise). Narrower rows lose: 65536 x 2048
         // (64 lanes) 88.3 -> 89.5, 1M x 128 88 -> 129. With 16-bit weights
-        // the same grid was 0-4% slower.
+        // the same grid was 0-4% slower, and with the residual add 1-2%.
         if (!res && c->vector_path == 1 && elem_size(dtype) == 2 && w_size(dtype) == 4 &&
             c->lanes_per_row >= kFwdWideMinLanes && row_blocks > kFwdMidHi * cus) {
             int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
