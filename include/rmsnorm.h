@@ -36,9 +36,9 @@
  *     type (2 or 4 bytes; rstd and dW 4; RMSN_EINVAL otherwise). 16-byte vector loads are
  *     used when N * sizeof(elem) is a multiple of 16 and every matrix/vector
  *     pointer is 16-byte aligned; otherwise kernels of the same arithmetic
- *     with narrower accesses run (rows of 257 to 16384 columns: groups of
+ *     with narrower accesses run (rows of up to 16384 columns: groups of
  *     consecutive elements as wide as N and the pointers' alignment allow;
- *     other widths: one element per access).
+ *     wider rows: one element per access).
  *   - y must not alias x; dx must not alias x or dy (undefined behaviour).
  *   - Return value: RMSN_OK (0) or a negative rmsn_status.
  */
@@ -85,8 +85,9 @@ typedef struct {
     int32_t vector_path;     /* 1: 16-byte vector row kernel; 2: the backward's wide-row vector
                                 kernel (1024 lanes, dW sums in LDS); 3: element kernel (rows
                                 that are not a multiple of 16 bytes or not 16-byte aligned,
-                                257..16384 columns: 1024 lanes, vecs_per_lane accesses of
-                                elems_per_access elements per lane); 0: scalar row kernel */
+                                up to 16384 columns: lanes_per_row = wg_threads = 64, 128, 256,
+                                512 or 1024, vecs_per_lane accesses of elems_per_access
+                                elements per lane); 0: scalar row kernel */
     int32_t lanes_per_row;   /* lanes that share one row (1..1024): a power of two, or for the
                                 backward with one vector per lane any multiple of 64 up to 1024
                                 with wg_threads equal to it (the row is the whole workgroup) */

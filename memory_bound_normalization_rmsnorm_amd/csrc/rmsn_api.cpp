@@ -5,6 +5,7 @@
 // reported without touching the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -133,7 +134,8 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
 constexpr int kElemPath = 3;  // rmsnorm_config::vector_path of the element kernels
-constexpr int64_t kElemMinN = 257;  // narrower unvectorisable rows keep the scalar kernel
+constexpr int64_t kElemFwdMaxBytes = 32;  // forward element rows: bytes of row per lane (elem_lanes)
+constexpr int64_t kElemBwdMaxElems = 12, kElemBwdMaxBytes = 40;  // backward: elements and bytes per lane
 constexpr int kFwdMaxVecs = 4;
 constexpr int64_t kFwdExactVecs = 5;  // forward rows that split exactly into this many vectors per lane take it
 // forward row blocks per CU (inclusive range) taking a prefetching grid of kFwdMidPerCU workgroups per CU
@@ -157,22 +159,48 @@ void set_vector_shape(int64_t lpr, int64_t vpt, int wg, int pf, rmsnorm_config *
     c->prefetch = pf;
 }
 
-// Element kernels: one row per kElemWG-lane workgroup, g elements per access,
-// k = ceil(N / (g * kElemWG)) accesses per lane. A one-row register prefetch
-// measured no faster (bf16 and fp32, 1500 to 15000 columns, one element per
-// access) and, in the backward, costs the second workgroup per CU from 5
-// elements per lane, so there is none.
-void set_elem_shape(int64_t N, int g, rmsnorm_config *c) {
+// Element kernels: one row per workgroup of `lanes` lanes, g elements per
+// access, k = ceil(N / (g * lanes)) accesses per lane. A one-row register
+// prefetch measured no faster (bf16 and fp32, 1500 to 15000 columns, one
+// element per access) and, in the backward, costs the second workgroup per CU
+// from 5 elements per lane, so there is none.
+void set_elem_shape(int64_t N, int g, int lanes, rmsnorm_config *c) {
     c->vector_path = kElemPath;
-    c->lanes_per_row = rmsn::kElemWG;
-    c->vecs_per_lane = (int32_t)((N + int64_t(g) * rmsn::kElemWG - 1) / (int64_t(g) * rmsn::kElemWG));
+    c->lanes_per_row = lanes;
+    c->vecs_per_lane = (int32_t)((N + int64_t(g) * lanes - 1) / (int64_t(g) * lanes));
     c->elems_per_access = g;
-    c->wg_threads = rmsn::kElemWG;
+    c->wg_threads = lanes;
     c->rows_per_wg = 1;
     c->prefetch = 0;
 }
 
-bool elem_ok(int64_t N) { return N >= kElemMinN && N <= int64_t(rmsn::kElemWG) * rmsn::kElemMaxK; }
+bool elem_lanes_ok(int64_t lanes) {
+    return lanes >= rmsn::kElemMinLanes && lanes <= rmsn::kElemMaxLanes && (lanes & (lanes - 1)) == 0;
+}
+
+// Lanes of an element row: the fewest (a power of two from 64) that keep each
+// lane's share of the row within a budget, so that short rows do not leave
+// most of a 1024-lane workgroup idle and a compute unit holds more rows. The
+// forward budget is 32 bytes of row per lane; the backward's, which also holds
+// dy and the dW sums, 12 elements and 40 bytes. Measured at 16384 rows against
+// every lane count, graph-timed: the forward rule picked the fastest at every
+// row (bf16 300 columns 29.4 -> 7.9 us with 64 lanes, 1500 43.5 -> 21.2 with
+// 128, 2050 45.9 -> 26.9 with 256, 4100 58.4 -> 52.5 with 512); the backward
+// rule the fastest or within 1-3% everywhere but bf16 1500 (128 lanes 40.0
+// us, 256 lanes 37.5): 300 38.2 -> 16.7 us, 700 45.0 -> 22.1, 4100 82.4 ->
+// 77.6, fp32 4098 158.4 -> 155.1.
+int elem_lanes(int64_t N, int g, int dtype, int is_bwd) {
+    const int64_t es = elem_size(dtype);
+    const int64_t max_elems = is_bwd ? kElemBwdMaxElems : rmsn::kElemMaxK;
+    const int64_t max_bytes = is_bwd ? kElemBwdMaxBytes : kElemFwdMaxBytes;
+    for (int64_t lanes = rmsn::kElemMinLanes; lanes < rmsn::kElemMaxLanes; lanes *= 2) {
+        const int64_t per_lane = (N + g * lanes - 1) / (g * lanes) * g;
+        if (per_lane <= max_elems && per_lane * es <= max_bytes) return (int)lanes;
+    }
+    return rmsn::kElemMaxLanes;
+}
+
+bool elem_ok(int64_t N) { return N <= int64_t(rmsn::kElemMaxLanes) * rmsn::kElemMaxK; }
 
 void set_scalar_shape(rmsnorm_config *c) {
     c->vector_path = 0;
@@ -229,10 +257,12 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, const Align &a, i
         // -> 60 us forward and 459 -> 83 backward; bf16 4095 (one per
         // access) 129 -> 62 and 463 -> 79; fp32 4098 (two per access) 177
         // -> 102 and 491 -> 156 (see ladder_grid for the forward's grid).
-        if (elem_ok(N))
-            set_elem_shape(N, elem_group(N, dtype, a), c);
-        else
+        if (elem_ok(N)) {
+            const int g = elem_group(N, dtype, a);
+            set_elem_shape(N, g, elem_lanes(N, g, dtype, is_bwd), c);
+        } else {
             set_scalar_shape(c);
+        }
         return;
     }
     if (nvec > kMaxVecLanes * vmax) {
@@ -349,20 +379,20 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             grid = row_blocks < resident ? row_blocks : resident;
             c->prefetch = 0;
         }
-        // Element kernels with 2-byte activations: a resident grid whose
-        // workgroups walk the rows (bf16 16384 x 4100: 111 us against 164
-        // with a workgroup per row; 16384 x 1500: 53 against 79). With fp32
-        // activations a workgroup per row was 2-4% faster.
-        if (c->vector_path == kElemPath && elem_size(dtype) == 2) {
-            const int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
-            if (grid > resident) grid = resident;
-        }
+        // Element kernels keep a workgroup per row. On rows sized by
+        // elem_lanes a resident grid walking the rows was as fast or slower
+        // (bf16 16384 x 12002: 138 us against 148; 16384 x 4100: 52.5 against
+        // 55.1); it had helped only with every row on 1024 lanes.
         const int64_t in_bytes = M * N * elem_size(dtype);
         c->stream_loads = (c->vector_path == 1 && c->lanes_per_row >= 64 && in_bytes >= kStreamMinBytes) ? 1 : 0;
     } else {
         const int64_t cus = num_cus > 0 ? num_cus : 1;
         const int deep = deep_prefetch(is_bwd, N, dtype, c);
         int64_t want = (c->vector_path == kWidePath ? 1 : deep ? deep : c->lanes_per_row < 64 ? 3 : 2) * cus;
+        // element rows: about 1024 lanes per CU, 2 to 8 workgroups (bf16 16384
+        // x 300 on 64 lanes: 16.7 us at 8 per CU, 19.0 at 2)
+        if (c->vector_path == kElemPath)
+            want = std::min<int64_t>(8, std::max<int64_t>(2, 1024 / c->lanes_per_row)) * cus;
         // partial rows are written once and read once (8 * N bytes each); at
         // most 1/kPartialShare of the 3 * M * N * elem algorithmic bytes, so
         // at most 3 * M * elem / (8 * kPartialShare) rows (N cancels)
@@ -424,7 +454,7 @@ int occupancy(const void *fn, int wg, int *blocks) {
 
 const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd, int res) {
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
-    if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access);
+    if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access, c.lanes_per_row);
     if (c.vector_path == kWidePath) {
         const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
         return e ? e->fn : nullptr;
@@ -482,11 +512,12 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     if (req->vector_path == kElemPath) {
         const int64_t k = req->vecs_per_lane;
         const int64_t g = req->elems_per_access ? req->elems_per_access : elem_group(N, dtype, a);
-        if (req->lanes_per_row != rmsn::kElemWG || (req->wg_threads != 0 && req->wg_threads != rmsn::kElemWG) ||
-            !elem_group_ok(N, dtype, a, g) || k < 1 || k * g > rmsn::kElemMaxK ||
-            int64_t(rmsn::kElemWG) * k * g < N || req->prefetch != 0 || req->stream_loads != 0)
+        const int64_t lanes = req->lanes_per_row;
+        if (!elem_lanes_ok(lanes) || (req->wg_threads != 0 && req->wg_threads != lanes) ||
+            !elem_group_ok(N, dtype, a, g) || k < 1 || k * g > rmsn::kElemMaxK || lanes * k * g < N ||
+            req->prefetch != 0 || req->stream_loads != 0)
             return RMSN_ECONFIG;
-        set_elem_shape(N, (int)g, c);
+        set_elem_shape(N, (int)g, (int)lanes, c);
         c->vecs_per_lane = (int32_t)k;
     } else if (req->elems_per_access != 0) {
         return RMSN_ECONFIG;

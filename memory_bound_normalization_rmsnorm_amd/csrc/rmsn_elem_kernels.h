@@ -1,4 +1,4 @@
-// rmsn_elem.hip -- RMSNorm forward and backward for rows the 16-byte vector
+// rmsn_elem_kernels.h -- RMSNorm forward and backward for rows the 16-byte vector
 // kernels cannot take: a row whose byte size is not a multiple of 16 (e.g.
 // 4100 bf16 columns) or a pointer that is not 16-byte aligned. The arithmetic
 // is that of the vector kernels (hello-gpu "Chapter 13 Fused RMSNorm",
@@ -11,7 +11,7 @@
 // largest power of two that divides N and whose bytes divide the alignment of
 // every pointer, so that every access is naturally aligned and no row has a
 // partial group (4100 bf16 columns: G = 4, 8-byte accesses; 4095: G = 1). A
-// row is one workgroup of kElemWG lanes; lane l holds groups l + k * kElemWG
+// row is one workgroup of L lanes (64 to 1024); lane l holds groups l + k * L
 // (k < K) in registers, read once; each wavefront access covers 64
 // consecutive groups. Groups past the row end are masked. Workgroups walk
 // rows cyclically (row = workgroup + t * grid); the backward keeps its dW
@@ -19,6 +19,8 @@
 // workgroup for the fixed-order combine. No atomics. K * G (elements per
 // lane) is the smallest multiple of G that covers the row: registers, and
 // with them the workgroups a compute unit holds, grow with it.
+#pragma once
+
 #include <type_traits>
 
 #include "rmsn_device.h"
@@ -101,11 +103,11 @@ struct Packed {
 };
 
 // The lane's groups of one row (zeros past the row end).
-template <typename T, int K, int G>
+template <typename T, int L, int K, int G>
 __device__ __forceinline__ void load_row(const T *__restrict__ p, int32_t N, Packed<T, G> (&v)[K]) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int j = G * ((int)threadIdx.x + k * kElemWG);
+        const int j = G * ((int)threadIdx.x + k * L);
         if (j < N)
             v[k].load(p + j);
         else
@@ -113,31 +115,31 @@ __device__ __forceinline__ void load_row(const T *__restrict__ p, int32_t N, Pac
     }
 }
 
-template <typename T, typename TW, bool RES, int K, int G>
-__global__ void __launch_bounds__(kElemWG)
+template <typename T, typename TW, bool RES, int L, int K, int G>
+__global__ void __launch_bounds__(L)
 fwd_elem(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict__ w, T *__restrict__ h,
          T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t /*nvec*/,
          int32_t /*stream_ld*/) {
-    __shared__ float slots[2 * (kElemWG / 64)];
+    __shared__ float slots[2 * (L / 64)];
     const float n = (float)N;
     Packed<TW, G> gw[K];
-    load_row<TW, K, G>(w, N, gw);
+    load_row<TW, L, K, G>(w, N, gw);
     int parity = 0;
     for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
         const int64_t o = row * (int64_t)N;
         Packed<T, G> v[K];
-        load_row<T, K, G>(x + o, N, v);
+        load_row<T, L, K, G>(x + o, N, v);
         if constexpr (RES) {
             // h = x + res rounded once to the activation format and stored; the row is h as stored
             Packed<T, G> q[K];
-            load_row<T, K, G>(res + o, N, q);
+            load_row<T, L, K, G>(res + o, N, q);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 float a[G];
 #pragma unroll
                 for (int i = 0; i < G; ++i) a[i] = v[k].get(i) + q[k].get(i);
                 v[k].set(a);
-                const int j = G * ((int)threadIdx.x + k * kElemWG);
+                const int j = G * ((int)threadIdx.x + k * L);
                 if (j < N) v[k].store(h + o + j);
             }
         }
@@ -146,7 +148,7 @@ fwd_elem(const T *__restrict__ x, const T *__restrict__ res, const TW *__restric
         for (int k = 0; k < K; ++k)
 #pragma unroll
             for (int i = 0; i < G; ++i) ss = __builtin_fmaf(v[k].get(i), v[k].get(i), ss);
-        ss = row_sum<kElemWG, kElemWG>(ss, slots, parity);
+        ss = row_sum<L, L>(ss, slots, parity);
         parity ^= 1;
         const float r = __frsqrt_rn(ss / n + eps);
         if (threadIdx.x == 0 && rstd) rstd[row] = r;
@@ -154,7 +156,7 @@ fwd_elem(const T *__restrict__ x, const T *__restrict__ res, const TW *__restric
         for (int k = 0; k < K; ++k) {
             v[k].rewiden();
             gw[k].rewiden();
-            const int j = G * ((int)threadIdx.x + k * kElemWG);
+            const int j = G * ((int)threadIdx.x + k * L);
             if (j < N) {
                 float out[G];
 #pragma unroll
@@ -167,24 +169,24 @@ fwd_elem(const T *__restrict__ x, const T *__restrict__ res, const TW *__restric
     }
 }
 
-template <typename T, typename TW, bool RES, int K, int G>
-__global__ void __launch_bounds__(kElemWG)
+template <typename T, typename TW, bool RES, int L, int K, int G>
+__global__ void __launch_bounds__(L)
 bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
          const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
          int32_t N, int32_t /*nvec*/) {
-    __shared__ float slots[2 * (kElemWG / 64)];
+    __shared__ float slots[2 * (L / 64)];
     const float n = (float)N;
     Packed<TW, G> gw[K];
     float acc[K * G];
-    load_row<TW, K, G>(w, N, gw);
+    load_row<TW, L, K, G>(w, N, gw);
 #pragma unroll
     for (int e = 0; e < K * G; ++e) acc[e] = 0.f;
     int parity = 0;
     Packed<T, G> gx[K], gg[K];  // the row's x and dy
     float r = 0.f;              // and rstd
     if (blockIdx.x < M) {
-        load_row<T, K, G>(x + blockIdx.x * (int64_t)N, N, gx);
-        load_row<T, K, G>(dy + blockIdx.x * (int64_t)N, N, gg);
+        load_row<T, L, K, G>(x + blockIdx.x * (int64_t)N, N, gx);
+        load_row<T, L, K, G>(dy + blockIdx.x * (int64_t)N, N, gg);
         r = rstd[blockIdx.x];
     }
     for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
@@ -196,7 +198,7 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
 #pragma unroll
             for (int i = 0; i < G; ++i) s = __builtin_fmaf(gg[k].get(i) * gw[k].get(i), gx[k].get(i), s);
         }
-        s = row_sum<kElemWG, kElemWG>(s, slots, parity);
+        s = row_sum<L, L>(s, slots, parity);
         parity ^= 1;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -207,7 +209,7 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
         const float c = r * (r * (r * (s / n)));  // r^3 S/N without forming r^3
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int j = G * ((int)threadIdx.x + k * kElemWG);
+            const int j = G * ((int)threadIdx.x + k * L);
             if (j < N) {
                 float g[G];
                 Packed<T, G> d;
@@ -226,8 +228,8 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
         }
         const int64_t next = row + gridDim.x;
         if (next < M) {
-            load_row<T, K, G>(x + next * (int64_t)N, N, gx);
-            load_row<T, K, G>(dy + next * (int64_t)N, N, gg);
+            load_row<T, L, K, G>(x + next * (int64_t)N, N, gx);
+            load_row<T, L, K, G>(dy + next * (int64_t)N, N, gg);
             r = rstd[next];
         }
     }
@@ -237,7 +239,7 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
     float *prow = partial + (int64_t)blockIdx.x * ldp;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int j = G * ((int)threadIdx.x + k * kElemWG);
+        const int j = G * ((int)threadIdx.x + k * L);
         if (j < N) {
 #pragma unroll
             for (int i = 0; i < G; i += PG) {
@@ -249,68 +251,74 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
     }
 }
 
-namespace {
-
-template <typename T, typename TW, int K, int G>
-const void *pick(int is_bwd, int res) {
+// The kernel of (format, direction, residual, k accesses, g elements per
+// access) at L lanes per row; nullptr where none is built. Explicitly
+// instantiated once per L, each in its own translation unit.
+template <typename T, typename TW, int L, int K, int G>
+const void *elem_pick_fn(int is_bwd, int res) {
     if constexpr (K * G > kElemMaxK || G * sizeof(T) > 16 || G * sizeof(TW) > 16) {
         return nullptr;
     } else {
         if (is_bwd)
-            return res ? reinterpret_cast<const void *>(&bwd_elem<T, TW, true, K, G>)
-                       : reinterpret_cast<const void *>(&bwd_elem<T, TW, false, K, G>);
-        return res ? reinterpret_cast<const void *>(&fwd_elem<T, TW, true, K, G>)
-                   : reinterpret_cast<const void *>(&fwd_elem<T, TW, false, K, G>);
+            return res ? reinterpret_cast<const void *>(&bwd_elem<T, TW, true, L, K, G>)
+                       : reinterpret_cast<const void *>(&bwd_elem<T, TW, false, L, K, G>);
+        return res ? reinterpret_cast<const void *>(&fwd_elem<T, TW, true, L, K, G>)
+                   : reinterpret_cast<const void *>(&fwd_elem<T, TW, false, L, K, G>);
     }
 }
 
-template <typename T, typename TW, int G>
-const void *pick_k(int is_bwd, int res, int k) {
+template <typename T, typename TW, int L, int G>
+const void *elem_pick_k(int is_bwd, int res, int k) {
     switch (k) {
-    case 1: return pick<T, TW, 1, G>(is_bwd, res);
-    case 2: return pick<T, TW, 2, G>(is_bwd, res);
-    case 3: return pick<T, TW, 3, G>(is_bwd, res);
-    case 4: return pick<T, TW, 4, G>(is_bwd, res);
-    case 5: return pick<T, TW, 5, G>(is_bwd, res);
-    case 6: return pick<T, TW, 6, G>(is_bwd, res);
-    case 7: return pick<T, TW, 7, G>(is_bwd, res);
-    case 8: return pick<T, TW, 8, G>(is_bwd, res);
-    case 9: return pick<T, TW, 9, G>(is_bwd, res);
-    case 10: return pick<T, TW, 10, G>(is_bwd, res);
-    case 11: return pick<T, TW, 11, G>(is_bwd, res);
-    case 12: return pick<T, TW, 12, G>(is_bwd, res);
-    case 13: return pick<T, TW, 13, G>(is_bwd, res);
-    case 14: return pick<T, TW, 14, G>(is_bwd, res);
-    case 15: return pick<T, TW, 15, G>(is_bwd, res);
-    case 16: return pick<T, TW, 16, G>(is_bwd, res);
+    case 1: return elem_pick_fn<T, TW, L, 1, G>(is_bwd, res);
+    case 2: return elem_pick_fn<T, TW, L, 2, G>(is_bwd, res);
+    case 3: return elem_pick_fn<T, TW, L, 3, G>(is_bwd, res);
+    case 4: return elem_pick_fn<T, TW, L, 4, G>(is_bwd, res);
+    case 5: return elem_pick_fn<T, TW, L, 5, G>(is_bwd, res);
+    case 6: return elem_pick_fn<T, TW, L, 6, G>(is_bwd, res);
+    case 7: return elem_pick_fn<T, TW, L, 7, G>(is_bwd, res);
+    case 8: return elem_pick_fn<T, TW, L, 8, G>(is_bwd, res);
+    case 9: return elem_pick_fn<T, TW, L, 9, G>(is_bwd, res);
+    case 10: return elem_pick_fn<T, TW, L, 10, G>(is_bwd, res);
+    case 11: return elem_pick_fn<T, TW, L, 11, G>(is_bwd, res);
+    case 12: return elem_pick_fn<T, TW, L, 12, G>(is_bwd, res);
+    case 13: return elem_pick_fn<T, TW, L, 13, G>(is_bwd, res);
+    case 14: return elem_pick_fn<T, TW, L, 14, G>(is_bwd, res);
+    case 15: return elem_pick_fn<T, TW, L, 15, G>(is_bwd, res);
+    case 16: return elem_pick_fn<T, TW, L, 16, G>(is_bwd, res);
     default: return nullptr;
     }
 }
 
-template <typename T, typename TW>
-const void *pick_g(int is_bwd, int res, int k, int g) {
+template <typename T, typename TW, int L>
+const void *elem_pick_g(int is_bwd, int res, int k, int g) {
     switch (g) {
-    case 1: return pick_k<T, TW, 1>(is_bwd, res, k);
-    case 2: return pick_k<T, TW, 2>(is_bwd, res, k);
-    case 4: return pick_k<T, TW, 4>(is_bwd, res, k);
-    case 8: return pick_k<T, TW, 8>(is_bwd, res, k);
+    case 1: return elem_pick_k<T, TW, L, 1>(is_bwd, res, k);
+    case 2: return elem_pick_k<T, TW, L, 2>(is_bwd, res, k);
+    case 4: return elem_pick_k<T, TW, L, 4>(is_bwd, res, k);
+    case 8: return elem_pick_k<T, TW, L, 8>(is_bwd, res, k);
     default: return nullptr;
     }
 }
-
-}  // namespace
 
 // Format codes (rmsn_dtype): 0 fp32, 1 bf16, 2 fp16, 3 bf16 with fp32 weights,
 // 4 fp16 with fp32 weights.
-const void *elem_kernel(int dtype, int is_bwd, int res, int k, int g) {
+template <int L>
+const void *elem_pick(int dtype, int is_bwd, int res, int k, int g) {
     switch (dtype) {
-    case 0: return pick_g<float, float>(is_bwd, res, k, g);
-    case 1: return pick_g<bf16_t, bf16_t>(is_bwd, res, k, g);
-    case 2: return pick_g<f16_t, f16_t>(is_bwd, res, k, g);
-    case 3: return pick_g<bf16_t, float>(is_bwd, res, k, g);
-    case 4: return pick_g<f16_t, float>(is_bwd, res, k, g);
+    case 0: return elem_pick_g<float, float, L>(is_bwd, res, k, g);
+    case 1: return elem_pick_g<bf16_t, bf16_t, L>(is_bwd, res, k, g);
+    case 2: return elem_pick_g<f16_t, f16_t, L>(is_bwd, res, k, g);
+    case 3: return elem_pick_g<bf16_t, float, L>(is_bwd, res, k, g);
+    case 4: return elem_pick_g<f16_t, float, L>(is_bwd, res, k, g);
     default: return nullptr;
     }
 }
+
+extern template const void *elem_pick<64>(int, int, int, int, int);
+extern template const void *elem_pick<128>(int, int, int, int, int);
+extern template const void *elem_pick<256>(int, int, int, int, int);
+extern template const void *elem_pick<512>(int, int, int, int, int);
+extern template const void *elem_pick<1024>(int, int, int, int, int);
 
 }  // namespace rmsn

@@ -1,0 +1,9 @@
+// rmsn_elem_l512.hip -- the element kernels with 512 lanes per row (each lane
+// count in its own translation unit, so that they compile in parallel).
+#include "rmsn_elem_kernels.h"
+
+namespace rmsn {
+
+template const void *elem_pick<512>(int, int, int, int, int);
+
+}  // namespace rmsn

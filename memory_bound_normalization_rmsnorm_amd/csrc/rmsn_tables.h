@@ -9,8 +9,10 @@ namespace rmsn {
 constexpr int kScalarWG = 256;
 constexpr int kScalarLdsCols = 16384;  // scalar backward rows up to this width keep their dW sums in LDS (64 KiB)
 // Element kernels (rows that are not a multiple of 16 bytes or not 16-byte
-// aligned): kElemWG lanes per row, at most kElemMaxK elements per lane.
-constexpr int kElemWG = 1024;
+// aligned): kElemMinLanes to kElemMaxLanes lanes per row (a power of two), at
+// most kElemMaxK elements per lane.
+constexpr int kElemMinLanes = 64;
+constexpr int kElemMaxLanes = 1024;
 constexpr int kElemMaxK = 16;
 constexpr int kCombineWG = 512;
 constexpr int kCombineCols = 32;     // dW columns per combine workgroup: one 128-byte line per partial row
@@ -59,9 +61,10 @@ const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, 
 const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf);
 // lds: the backward kernel that keeps its dW sums in LDS (rows of at most kScalarLdsCols columns)
 const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
-// element kernels: k accesses of g elements per lane (g 1, 2, 4 or 8, at most
-// 16 bytes per access; k * g at most kElemMaxK), nullptr otherwise
-const void *elem_kernel(int dtype, int is_bwd, int res, int k, int g);
+// element kernels: rows of `lanes` lanes (64, 128, 256, 512 or 1024), k
+// accesses of g elements per lane (g 1, 2, 4 or 8, at most 16 bytes per
+// access; k * g at most kElemMaxK), nullptr otherwise
+const void *elem_kernel(int dtype, int is_bwd, int res, int k, int g, int lanes);
 const void *dw_combine_kernel();
 const void *fill_zero_kernel();
 

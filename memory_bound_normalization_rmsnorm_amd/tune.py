@@ -45,7 +45,7 @@ BUILT = {1: (256,), 2: (256,), 4: (256,), 8: (256,), 16: (256,), 32: (256,), 64:
          128: (256, 512, 1024), 256: (256, 512, 1024), 512: (512, 1024), 1024: (1024,)}
 MAX_VPT = 8
 WIDE_LANES = 1024  # wide-row backward kernels (vector_path 2): 1024 lanes, dW sums in LDS
-ELEM_LANES, ELEM_MAX, ELEM_MIN_N = 1024, 16, 257  # element kernels (vector_path 3): lanes, elements per lane, row
+ELEM_LANES, ELEM_MAX = (64, 128, 256, 512, 1024), 16  # element kernels (vector_path 3): lanes, elements per lane
 ROWWG_MIN_VECS = 256  # backward rows wider than this may run on any whole number of wavefronts
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
@@ -62,25 +62,30 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
     than 1024 vectors also the wide-row kernels at one and two workgroups per
     compute unit, and for backward rows of 257 to 1024 vectors whose whole
     wavefronts are not a power of two the workgroup-sized row kernels. Shapes that are not built fail at launch and are skipped.
-    Rows that are not a multiple of 16 bytes (257 to 16384 columns) get the
+    Rows that are not a multiple of 16 bytes (up to 16384 columns) get the
     element kernels instead: the widest group of consecutive elements per
     access that N allows (pointers 16-byte aligned, as in the search's own
-    buffers) and one element per access, each at the fewest accesses per lane
-    that cover the row, crossed with the same grids. Pure host logic."""
+    buffers) and one element per access, on every row size from 64 to 1024
+    lanes that holds the row in at most 16 elements per lane, each at the
+    fewest accesses per lane, crossed with the row count, its half and 1, 2, 4
+    and 8 workgroups per compute unit. Pure host logic."""
     es = ELEM[dtype]
     if (N * es) % 16:
         out = [default] if default is not None else []
-        if ELEM_MIN_N <= N <= ELEM_LANES * ELEM_MAX:
+        if N <= ELEM_LANES[-1] * ELEM_MAX:
             big = max(es, 4 if WEIGHT[dtype] == torch.float32 else 2)
             g = 1
             while 2 * g * big <= 16 and N % (2 * g) == 0:
                 g *= 2
-            grids = sorted(x for x in {M, -(-M // 2)} | {k * num_cus for k in (1, 2, 3, 4)} if 1 <= x <= M)
+            grids = sorted(x for x in {M, -(-M // 2)} | {k * num_cus for k in (1, 2, 4, 8)} if 1 <= x <= M)
             for gg in sorted({g, 1}, reverse=True):
-                k = -(-N // (ELEM_LANES * gg))
-                for grid in grids:
-                    out.append(rmsnorm_config(vector_path=3, lanes_per_row=ELEM_LANES, vecs_per_lane=k,
-                                              elems_per_access=gg, wg_threads=ELEM_LANES, grid=grid))
+                for lanes in ELEM_LANES:
+                    k = -(-N // (lanes * gg))
+                    if k * gg > ELEM_MAX:
+                        continue
+                    for grid in grids:
+                        out.append(rmsnorm_config(vector_path=3, lanes_per_row=lanes, vecs_per_lane=k,
+                                                  elems_per_access=gg, wg_threads=lanes, grid=grid))
         return out
     nvec = N * es // 16
     out = []

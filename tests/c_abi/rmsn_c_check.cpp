@@ -214,7 +214,8 @@ int main() {
     ok &= run_case<uint16_t>(1000, 128, true, 3);    // several rows per wavefront
     ok &= run_case<float>(33, 257, false, 4);        // element kernels (row not a multiple of 16 bytes)
     ok &= run_case<uint16_t>(9, 4100, true, 6);      // element kernels, 4 elements per access
-    ok &= run_case<float>(7, 13, false, 7);          // scalar path (13 columns)
+    ok &= run_case<float>(7, 13, false, 7);          // element kernels, 64-lane rows
+    ok &= run_case<float>(3, 16385, false, 8);       // scalar path (wider than the element kernels hold)
     ok &= run_case<float>(96, 1024, false, 5);
     std::printf("%s\n", ok ? "ok" : "FAILED");
     return ok ? 0 : 1;

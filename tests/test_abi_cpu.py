@@ -279,44 +279,56 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (vpt - 1) * lpr < nvec <= vpt * lpr
 
 
-@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(13, rn.F32, 1, 0), (255, rn.BF16, 1, 0), (256, rn.BF16, 0, 1),
-                                                    (65536 + 8, rn.BF16, 1, 0), (3, rn.BF16, 1, 1),
-                                                    (32768 + 8, rn.BF16, 1, 1), (16385, rn.BF16, 1, 0),
-                                                    (20000, rn.F32, 0, 1)])
+@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(65536 + 8, rn.BF16, 1, 0), (32768 + 8, rn.BF16, 1, 1),
+                                                    (16385, rn.BF16, 1, 0), (20000, rn.F32, 0, 1)])
 def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
-    """The scalar kernel: rows the vector kernels cannot take that are too
-    narrow (256 columns or fewer) or too wide (more than 16384) for the
-    element kernels, and rows wider than the vector kernels hold."""
+    """The scalar kernel: rows the vector kernels cannot take that are wider
+    than the element kernels hold (16384 columns), and rows wider than the
+    vector kernels hold."""
     c = cfg(100, N, dtype, is_bwd, aligned=aligned)
     assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
 
 
-@pytest.mark.parametrize("N,dtype,aligned,k,g", [
-    (257, rn.BF16, 1, 1, 1), (1024, rn.BF16, 0, 1, 1), (1025, rn.F16, 1, 2, 1), (4095, rn.BF16, 1, 4, 1),
-    (4100, rn.BF16, 1, 2, 4),        # 8200-byte rows: 8-byte accesses
-    (4100, rn.BF16, 4, 3, 2),        # ... pointers only 4-byte aligned: 4-byte accesses
-    (4100, rn.BF16_WF32, 1, 2, 4),   # fp32 weights: 16-byte weight accesses
-    (4100, rn.F16_WF32, 2, 5, 1),
-    (4098, rn.F32, 1, 3, 2), (4096, rn.BF16, 0, 4, 1), (4104, rn.BF16, 8, 2, 4),
-    (8192, rn.BF16, 8, 2, 4), (16384, rn.F16, 8, 4, 4), (16384, rn.F32, 8, 8, 2), (16376, rn.BF16, 8, 4, 4),
-    (5001, rn.F32, 1, 5, 1), (10239, rn.F32, 1, 10, 1), (10241, rn.BF16, 1, 11, 1), (16383, rn.F16, 1, 16, 1),
-    (16384, rn.F32, 0, 16, 1)])
-def test_ladder_element_cases(N, dtype, aligned, k, g):
-    """Rows that are not a multiple of 16 bytes, or not 16-byte aligned, of
-    257 to 16384 columns: the element kernels, 1024 lanes, g elements per
-    access (the largest power of two, up to 16 bytes of activations or
-    weights, that divides N and the pointers' alignment), ceil(N / (1024 g))
-    accesses per lane, no prefetch; the backward persistent over the grid of
-    the other row kernels, the forward a workgroup per row for fp32
-    activations and a resident grid for 2-byte ones."""
-    for is_bwd in (0, 1):
-        c = cfg(4096, N, dtype, is_bwd, aligned=aligned)
+ELEMENT_CASES = [
+    # N, format, pointer alignment (1: 16 bytes), elements per access, forward (lanes, accesses), backward (...)
+    (3, rn.BF16, 1, 1, (64, 1), (64, 1)), (13, rn.F32, 1, 1, (64, 1), (64, 1)), (255, rn.BF16, 1, 1, (64, 4), (64, 4)),
+    (256, rn.BF16, 0, 1, (64, 4), (64, 4)), (257, rn.BF16, 1, 1, (64, 5), (64, 5)), (300, rn.BF16, 1, 4, (64, 2), (64, 2)),
+    (1024, rn.BF16, 0, 1, (64, 16), (128, 8)), (1025, rn.F16, 1, 1, (128, 9), (128, 9)),
+    (1500, rn.BF16, 1, 4, (128, 3), (128, 3)), (2050, rn.BF16, 1, 2, (256, 5), (256, 5)),
+    (4095, rn.BF16, 1, 1, (256, 16), (512, 8)), (4096, rn.BF16, 0, 1, (256, 16), (512, 8)),
+    (4100, rn.BF16, 1, 4, (512, 3), (512, 3)),        # 8200-byte rows: 8-byte accesses
+    (4100, rn.BF16, 4, 2, (512, 5), (512, 5)),        # ... pointers only 4-byte aligned: 4-byte accesses
+    (4100, rn.BF16_WF32, 1, 4, (512, 3), (512, 3)),   # fp32 weights: 16-byte weight accesses
+    (4100, rn.F16_WF32, 2, 1, (512, 9), (512, 9)),
+    (4098, rn.F32, 1, 2, (1024, 3), (512, 5)), (4104, rn.BF16, 8, 4, (512, 3), (512, 3)),
+    (5001, rn.F32, 1, 1, (1024, 5), (512, 10)), (8192, rn.BF16, 8, 4, (512, 4), (1024, 2)),
+    (10241, rn.BF16, 1, 1, (1024, 11), (1024, 11)), (16383, rn.F16, 1, 1, (1024, 16), (1024, 16)),
+    (16384, rn.F16, 8, 4, (1024, 4), (1024, 4)), (16384, rn.F32, 8, 2, (1024, 8), (1024, 8)),
+    (16384, rn.F32, 0, 1, (1024, 16), (1024, 16)),
+]
+
+
+@pytest.mark.parametrize("N,dtype,aligned,g,fwd,bwd", ELEMENT_CASES)
+def test_ladder_element_cases(N, dtype, aligned, g, fwd, bwd):
+    """Rows that are not a multiple of 16 bytes, or not 16-byte aligned, of up
+    to 16384 columns: the element kernels. g elements per access (the largest
+    power of two, up to 16 bytes of activations or weights, that divides N
+    and the pointers' alignment); the fewest lanes, from 64, that keep a
+    lane's share of the row within 16 elements and 32 bytes (forward) or 12
+    elements and 40 bytes (backward), else 1024; ceil(N / (lanes g)) accesses
+    per lane; no prefetch. The forward runs a workgroup per row; the backward
+    is persistent on about 1024 lanes per CU (2 to 8 workgroups), within the
+    partial-row and residency caps of the other row kernels."""
+    es = 4 if dtype == rn.F32 else 2
+    for is_bwd, (lanes, k) in ((0, fwd), (1, bwd)):
+        c = cfg(16384, N, dtype, is_bwd, aligned=aligned, blocks=8)
         assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["elems_per_access"], c["wg_threads"],
-                c["rows_per_wg"], c["prefetch"], c["stream_loads"]) == (3, 1024, k, g, 1024, 1, 0, 0)
-        assert c["grid"] == (512 if is_bwd or dtype != rn.F32 else 4096)
+                c["rows_per_wg"], c["prefetch"], c["stream_loads"]) == (3, lanes, k, g, lanes, 1, 0, 0), c
+        assert lanes * k * g >= N and k * g <= 16
+        cap = max(256, 3 * 16384 * es // 48)
+        assert c["grid"] == (min(max(2, min(8, 1024 // lanes)) * 256, cap, 8 * 256) if is_bwd else 16384)
         assert cfg(300, N, dtype, is_bwd, aligned=aligned)["grid"] == (256 if is_bwd else 300)
-        assert cfg(4096, N, dtype, is_bwd, aligned=aligned, blocks=1)["grid"] == (
-            256 if is_bwd or dtype != rn.F32 else 4096)
+        assert cfg(16384, N, dtype, is_bwd, aligned=aligned, blocks=1)["grid"] == (256 if is_bwd else 16384)
 
 
 def test_ladder_grid_and_workspace_shape():

@@ -423,11 +423,12 @@ def test_forward_mid_size_grid(fmt):
 @pytest.mark.parametrize("residual", [False, True])
 def test_every_element_kernel(fmt, residual):
     """The element kernels (rows that are not a multiple of 16 bytes), every
-    format, plain and residual, every elements-per-lane count (K = 1..16): the
-    ladder's own configuration, and the kernels forced to a grid of 3 so that
-    workgroups walk several rows; 7 rows, of 5 elements short of 1024 * K
-    and of one element past 1024 * (K - 1) (only lane 0 holds an element at
-    k = K - 1)."""
+    format, plain and residual, every elements-per-lane count (K = 1..16) on
+    1024-lane rows: the ladder's own configuration (its row size is the
+    ladder's; it must cover the row), and the 1024-lane kernel forced to a
+    grid of 3 so that workgroups walk several rows; 7 rows, of 5 elements
+    short of 1024 * K and of one element past 1024 * (K - 1) (only lane 0
+    holds an element at k = K - 1)."""
     act, wst, code = FORMATS[fmt]
     eps = si.eps_f32(1e-6)
     for k, N in [(k, n) for k in range(1, 17) for n in (1024 * k - 5, 1024 * (k - 1) + 1) if n >= 257]:
@@ -435,8 +436,10 @@ def test_every_element_kernel(fmt, residual):
         _, _, x, w, dy = _case(M, N, fmt, seed=7000 + N)
         for d in (0, 1):
             c = rn.rmsnorm_query_config(M, N, code, d)
-            assert (c.vector_path, c.vecs_per_lane, c.prefetch) == (3, k, 0), c.as_dict()
-        forced = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, wg_threads=1024, grid=3)
+            assert (c.vector_path, c.elems_per_access, c.prefetch) == (3, 1, 0), c.as_dict()
+            assert c.lanes_per_row * c.vecs_per_lane >= N and c.vecs_per_lane <= 16, c.as_dict()
+        forced = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, elems_per_access=1,
+                                   wg_threads=1024, grid=3)
         for cfg in (None, forced):
             _say(f"element kernel k={k} N={N} {fmt} residual={residual} cfg={None if cfg is None else cfg.as_dict()}")
             if residual:
@@ -475,7 +478,8 @@ def test_element_kernels_grouped(fmt, residual):
             if g * s < 16:
                 for d in (0, 1):
                     c = rn.rmsnorm_query_config(M, N, code, d)
-                    assert (c.vector_path, c.vecs_per_lane, c.elems_per_access) == (3, k, g), c.as_dict()
+                    assert (c.vector_path, c.elems_per_access) == (3, g), c.as_dict()
+                    assert c.lanes_per_row * c.vecs_per_lane * g >= N, c.as_dict()
                 cfgs = (None, forced)
             else:
                 ladder = rn.rmsnorm_config(vector_path=3, lanes_per_row=1024, vecs_per_lane=k, elems_per_access=g,
@@ -487,6 +491,35 @@ def test_element_kernels_grouped(fmt, residual):
                 if residual:
                     res = si.random_tensor((M, N), act, seed=7500 + N)
                     dh = si.random_tensor((M, N), act, seed=7600 + N, scale=1e-2)
+                    residual_check(x, res, w, dy, dh, eps, act, wst, cfg=cfg)
+                else:
+                    plain_check(x, w, dy, eps, act, wst, cfg=cfg)
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("residual", [False, True])
+def test_element_kernels_every_row_size(fmt, residual):
+    """Element rows of 64, 128, 256 and 512 lanes (1024 above), one and G > 1
+    elements per access, the fewest and the most accesses per lane: rows of
+    N = G * (lanes * K - 1) columns forced onto that kernel with a grid of 3
+    (workgroups walk several rows); 7 rows, plain and residual, against the
+    oracle."""
+    act, wst, code = FORMATS[fmt]
+    big = max(4 if act == "f32" else 2, 4 if wst == "f32" else 2)
+    eps = si.eps_f32(1e-6)
+    for lanes in (64, 128, 256, 512):
+        for g in (1, 2, 4):
+            if g * big > 16:
+                continue
+            for k in (1, 16 // g):
+                M, N = 7, g * (lanes * k - 1)
+                _, _, x, w, dy = _case(M, N, fmt, seed=7700 + N + lanes)
+                cfg = rn.rmsnorm_config(vector_path=3, lanes_per_row=lanes, vecs_per_lane=k, elems_per_access=g,
+                                        wg_threads=lanes, grid=3)
+                _say(f"element rows lanes={lanes} g={g} k={k} N={N} {fmt} residual={residual}")
+                if residual:
+                    res = si.random_tensor((M, N), act, seed=7800 + N)
+                    dh = si.random_tensor((M, N), act, seed=7900 + N, scale=1e-2)
                     residual_check(x, res, w, dy, dh, eps, act, wst, cfg=cfg)
                 else:
                     plain_check(x, w, dy, eps, act, wst, cfg=cfg)

@@ -21,23 +21,24 @@ def test_candidates_cover_the_row_and_include_the_default():
 
 
 def test_candidates_for_widths_the_vector_path_cannot_take():
-    default = rn.rmsnorm_select_config(10, 13, rn.F32, 0, 1, 256, 2)
-    assert [tune._key(c) for c in tune.candidates(10, 13, rn.F32, 0, 256, default)] == [tune._key(default)]
-    # 257..16384 columns: element kernels, the widest group N allows and single elements
-    for M, N, dt, g, kg, k1 in ((4096, 4100, rn.BF16, 4, 2, 5), (4096, 4098, rn.F32, 2, 3, 5),
-                                (4096, 4100, rn.BF16_WF32, 4, 2, 5), (100, 4095, rn.F16, 1, 4, 4)):
+    default = rn.rmsnorm_select_config(10, 70001, rn.F32, 0, 1, 256, 2)     # wider than the element kernels
+    assert [tune._key(c) for c in tune.candidates(10, 70001, rn.F32, 0, 256, default)] == [tune._key(default)]
+    # up to 16384 columns: element kernels, the widest group N allows and single elements, every row size
+    # that holds the row in 16 elements per lane
+    for M, N, dt, g in ((4096, 4100, rn.BF16, 4), (4096, 4098, rn.F32, 2), (4096, 4100, rn.BF16_WF32, 4),
+                        (100, 4095, rn.F16, 1), (3000, 13, rn.F32, 1)):
         for d in (0, 1):
             default = rn.rmsnorm_select_config(M, N, dt, d, 1, 256, 2)
             cands = tune.candidates(M, N, dt, d, 256, default)
             assert tune._key(cands[0]) == tune._key(default)
-            assert (default.vector_path, default.elems_per_access, default.vecs_per_lane) == (3, g, kg)
-            elem = {(c.elems_per_access, c.vecs_per_lane) for c in cands[1:]}
-            assert elem == {(g, kg), (1, k1)}
+            assert (default.vector_path, default.elems_per_access) == (3, g)
+            want = {(gg, lanes, -(-N // (lanes * gg))) for gg in {g, 1} for lanes in (64, 128, 256, 512, 1024)
+                    if -(-N // (lanes * gg)) * gg <= 16}
+            assert {(c.elems_per_access, c.lanes_per_row, c.vecs_per_lane) for c in cands[1:]} == want
             grids = {c.grid for c in cands[1:]}
             assert max(grids) == M and (256 in grids or M < 256) and all(1 <= x <= M for x in grids)
             for c in cands[1:]:
-                assert (c.vector_path, c.lanes_per_row, c.wg_threads, c.prefetch) == (3, 1024, 1024, 0)
-                assert c.elems_per_access * c.vecs_per_lane * 1024 >= N
+                assert (c.vector_path, c.wg_threads, c.prefetch) == (3, c.lanes_per_row, 0)
 
 
 def test_cache_round_trip(tmp_path):
