@@ -210,12 +210,15 @@ def test_error_codes_on_device():
     assert e.value.status == rn.ECONFIG
 
 
-# One shape per backward kernel family the ladder picks (and, with fp32
-# weights, the persistent forward): 512-lane rows with two blocks prefetched,
-# whole-wavefront rows (640 and 320 lanes), the wide-row kernel, narrow rows
-# several to a wavefront, fp32 rows of 1024 lanes.
+# One shape per backward kernel family the ladder picks (and the forward's
+# grids): 512-lane rows with two blocks prefetched, whole-wavefront rows (640
+# and 320 lanes), the wide-row kernel, narrow rows several to a wavefront, fp32
+# rows of 1024 lanes, fp32 weights (the mid-size and the resident forward
+# grids), and the element kernels on 64-lane rows 8 to a CU, 512-lane rows
+# with 8-byte accesses and fp32 rows with 2 elements per access.
 DETERMINISM_CASES = [("bf16", 4096, 4096), ("bf16", 4096, 5120), ("bf16", 8192, 2560), ("bf16", 256, 32768),
-                     ("bf16", 65536, 128), ("f32", 1024, 4096), ("bf16w32", 2048, 8192)]
+                     ("bf16", 65536, 128), ("f32", 1024, 4096), ("bf16w32", 2048, 8192), ("bf16w32", 8192, 4096),
+                     ("bf16", 16384, 300), ("bf16", 4096, 4100), ("f32", 2048, 4098)]
 
 
 @pytest.mark.parametrize("fmt,M,N", DETERMINISM_CASES, ids=lambda v: str(v))
