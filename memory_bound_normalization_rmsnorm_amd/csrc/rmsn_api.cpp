@@ -145,6 +145,7 @@ constexpr int64_t kFwdWideMinLanes = 128;  // ... for rows of at least this many
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
+constexpr int64_t kBwdSingleElems = 16384, kBwdSinglePasses = 4;  // backward inputs one workgroup walks
 constexpr int64_t kStreamMinBytes = int64_t(4) << 20;  // forward inputs from this size stream (one XCD's L2)
 constexpr int kBwdMaxVecs = 4;
 constexpr int64_t kRowWGMinVecs = 256;  // backward rows wider than this may run on whole wavefronts (rowwg_lanes)
@@ -401,6 +402,15 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         const int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
         if (want > resident) want = resident;
         grid = row_blocks < want ? row_blocks : want;
+        // A few rows (a decode step's): one workgroup walks them all and
+        // writes dW itself, with no combine launch. Faster while M * N is at
+        // most kBwdSingleElems and the walk at most kBwdSinglePasses row
+        // blocks (each pass costs a load latency): bf16 4096 columns 5.1 ->
+        // 3.2 us at M = 2 and
+        // 5.2 -> 4.6 at M = 4 (6 rows: 5.3 against 6.0), 8192 columns 6.0 ->
+        // 4.8 at M = 2, 2048 columns 5.5 -> 4.3 at M = 8, fp32 4096 5.5 -> 3.3
+        // at M = 2 (graph-timed rows + combine against the one kernel).
+        if (row_blocks <= kBwdSinglePasses && M * N <= kBwdSingleElems) grid = 1;
     }
     c->grid = grid > 0 ? grid : 1;
     c->partial_rows = c->grid;

@@ -331,6 +331,19 @@ def test_ladder_element_cases(N, dtype, aligned, g, fwd, bwd):
         assert cfg(16384, N, dtype, is_bwd, aligned=aligned, blocks=1)["grid"] == (256 if is_bwd else 16384)
 
 
+def test_ladder_backward_single_workgroup_for_a_few_rows():
+    """A few rows: one workgroup walks them and writes dW itself (no combine)
+    while M * N <= 16384 and the walk is at most 4 row blocks."""
+    for M, N, dt in ((1, 4096, rn.BF16), (2, 4096, rn.BF16), (4, 4096, rn.BF16), (2, 8192, rn.BF16),
+                     (8, 2048, rn.BF16), (4, 4096, rn.F32), (3, 5001, rn.BF16)):
+        c = cfg(M, N, dt, 1)
+        assert c["grid"] == c["partial_rows"] == 1, (M, N, c)
+    for M, N, dt in ((5, 4096, rn.BF16), (3, 8192, rn.BF16), (12, 2048, rn.BF16), (300, 3, rn.BF16),
+                     (17, 1024, rn.F32)):
+        c = cfg(M, N, dt, 1)
+        assert c["grid"] > 1, (M, N, c)
+
+
 def test_ladder_grid_and_workspace_shape():
     # backward: two workgroups per compute unit, one fp32 partial row each
     c = cfg(16384, 2048, rn.BF16, 1, cus=256, blocks=2)
