@@ -20,8 +20,6 @@
 #define RMSN_BUILD_INFO "unknown build"
 #endif
 
-extern "C" int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype);
-
 namespace {
 
 using rmsn::KernelEntry;
@@ -417,19 +415,57 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
     c->partial_stride = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
 }
 
-// ---- per-device cache ----------------------------------------------------
+// ---- per-device caches -----------------------------------------------------
+//
+// Device properties (compute units), kernel occupancy, and the resolved
+// launch configuration of each (device, M, N, format, direction, residual,
+// alignment class), so that a call does one device query and one locked
+// lookup instead of re-running the ladder: a decode-sized backward kernel
+// takes 2.5 us, and the host path must stay well below that. The
+// configuration cache is cleared when it reaches kCacheMax entries (a caller
+// cycling through many shapes still gets the same configurations, recomputed).
 
 struct DeviceInfo {
     int num_cus = 0;
     std::unordered_map<const void *, int> occupancy;
 };
 
+struct CfgKey {
+    int64_t M, N;
+    int dev, dtype, is_bwd, res, act, w;
+    bool operator==(const CfgKey &o) const {
+        return M == o.M && N == o.N && dev == o.dev && dtype == o.dtype && is_bwd == o.is_bwd && res == o.res &&
+               act == o.act && w == o.w;
+    }
+};
+
+struct CfgKeyHash {
+    size_t operator()(const CfgKey &k) const {
+        uint64_t h = 1469598103934665603ull;  // FNV-1a over the fields
+        for (int64_t v : {k.M, k.N, (int64_t)k.dev, (int64_t)k.dtype, (int64_t)k.is_bwd, (int64_t)k.res,
+                          (int64_t)k.act, (int64_t)k.w}) {
+            h ^= (uint64_t)v;
+            h *= 1099511628211ull;
+        }
+        return (size_t)h;
+    }
+};
+
+struct Resolved {
+    rmsnorm_config c;
+    const void *fn;
+};
+
+constexpr size_t kCacheMax = 4096;
+
 std::mutex g_mu;
 std::unordered_map<int, DeviceInfo> g_devices;
+std::unordered_map<CfgKey, Resolved, CfgKeyHash> g_resolved;
+std::unordered_map<CfgKey, int64_t, CfgKeyHash> g_workspace;  // key fields is_bwd..w unused (0)
 
-int device_info(int *num_cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return RMSN_EHIP;
+int current_device(int *dev) { return hipGetDevice(dev) == hipSuccess ? RMSN_OK : RMSN_EHIP; }
+
+int device_info(int dev, int *num_cus) {
     std::lock_guard<std::mutex> lk(g_mu);
     DeviceInfo &d = g_devices[dev];
     if (d.num_cus == 0) {
@@ -442,9 +478,7 @@ int device_info(int *num_cus) {
     return RMSN_OK;
 }
 
-int occupancy(const void *fn, int wg, int *blocks) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return RMSN_EHIP;
+int occupancy(int dev, const void *fn, int wg, int *blocks) {
     {
         std::lock_guard<std::mutex> lk(g_mu);
         auto &occ = g_devices[dev].occupancy;
@@ -479,28 +513,83 @@ const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd
     return e ? e->fn : nullptr;
 }
 
-// Full configuration on the current device (res: the residual-fused kernel).
-int resolve(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Align &a, rmsnorm_config *c,
-            const void **fn) {
+// The ladder's full configuration on device `dev`, uncached.
+int resolve_uncached(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int res, const Align &a,
+                     rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     int cus = 0, blocks = 0;
-    int st = device_info(&cus);
+    int st = device_info(dev, &cus);
     if (st != RMSN_OK) return st;
     ladder_shape(M, N, dtype, is_bwd, a, cus, c);
     const void *k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
-    st = occupancy(k, c->wg_threads, &blocks);
+    st = occupancy(dev, k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, res, cus, blocks, c);
     ladder_prefetch(M, N, dtype, is_bwd, c);
     k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
+    *fn = k;
+    return RMSN_OK;
+}
+
+// Full configuration on device `dev` (res: the residual-fused kernel), cached.
+int resolve(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int res, const Align &a, rmsnorm_config *c,
+            const void **fn) {
+    const CfgKey key{M, N, dev, dtype, is_bwd, res, a.act, a.w};
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_resolved.find(key);
+        if (it != g_resolved.end()) {
+            *c = it->second.c;
+            if (fn) *fn = it->second.fn;
+            return RMSN_OK;
+        }
+    }
+    const void *k = nullptr;
+    const int st = resolve_uncached(dev, M, N, dtype, is_bwd, res, a, c, &k);
+    if (st != RMSN_OK) return st;
     if (fn) *fn = k;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_resolved.size() >= kCacheMax) g_resolved.clear();
+    g_resolved.emplace(key, Resolved{*c, k});
     return RMSN_OK;
 }
 
 int64_t workspace_for(const rmsnorm_config &c) {
     return c.partial_rows * c.partial_stride * int64_t(sizeof(float));
+}
+
+// The documented workspace requirement of rmsnorm_bwd on device `dev`: enough
+// for every row kernel the call may pick (plain or residual-fused, vector or
+// scalar), so neither the caller's alignment nor the residual variant changes
+// the answer. Cached per (device, M, N, format); *need receives the bytes.
+int workspace_need(int dev, int64_t M, int64_t N, int dtype, int64_t *need) {
+    const CfgKey key{M, N, dev, dtype, 0, 0, 0, 0};
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_workspace.find(key);
+        if (it != g_workspace.end()) {
+            *need = it->second;
+            return RMSN_OK;
+        }
+    }
+    int64_t most = 0;
+    for (int fused = 0; fused <= 1; ++fused) {
+        for (int v : {1, 4, 8, 16}) {  // every pointer alignment that selects a different kernel
+            const Align a{v > elem_size(dtype) ? v : elem_size(dtype), v > w_size(dtype) ? v : w_size(dtype)};
+            rmsnorm_config c;
+            const int s = resolve(dev, M, N, dtype, 1, fused, a, &c, nullptr);
+            if (s != RMSN_OK) return s;
+            const int64_t b = workspace_for(c);
+            if (b > most) most = b;
+        }
+    }
+    *need = most;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_workspace.size() >= kCacheMax) g_workspace.clear();
+    g_workspace.emplace(key, most);
+    return RMSN_OK;
 }
 
 int launch(const void *fn, int64_t grid, int wg, void **args, hipStream_t stream) {
@@ -570,7 +659,13 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
     if (!natural(a, dtype) || !aligned4(rstd)) return RMSN_EINVAL;
     rmsnorm_config c;
     const void *fn = nullptr;
-    st = req ? explicit_config(req, M, N, dtype, 0, fused, a, &c, &fn) : resolve(M, N, dtype, 0, fused, a, &c, &fn);
+    if (req) {
+        st = explicit_config(req, M, N, dtype, 0, fused, a, &c, &fn);
+    } else {
+        int dev = 0;
+        st = current_device(&dev);
+        if (st == RMSN_OK) st = resolve(dev, M, N, dtype, 0, fused, a, &c, &fn);
+    }
     if (st != RMSN_OK) return st;
     int32_t n32 = (int32_t)N;
     int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
@@ -610,14 +705,19 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
     if (!natural(a, dtype) || !aligned4(rstd)) return RMSN_EINVAL;
     rmsnorm_config c;
     const void *fn = nullptr;
-    st = req ? explicit_config(req, M, N, dtype, 1, fused, a, &c, &fn) : resolve(M, N, dtype, 1, fused, a, &c, &fn);
-    if (st != RMSN_OK) return st;
     if (req) {
+        st = explicit_config(req, M, N, dtype, 1, fused, a, &c, &fn);
+        if (st != RMSN_OK) return st;
         if (workspace_bytes < (size_t)workspace_for(c)) return RMSN_EWORKSPACE;
     } else {
+        int dev = 0;
+        st = current_device(&dev);
+        if (st == RMSN_OK) st = resolve(dev, M, N, dtype, 1, fused, a, &c, &fn);
+        if (st != RMSN_OK) return st;
         // the documented contract: at least what rmsnorm_bwd_workspace_bytes reports
-        const int64_t need = rmsnorm_bwd_workspace_bytes(M, N, dtype);
-        if (need < 0) return (int)need;
+        int64_t need = 0;
+        st = workspace_need(dev, M, N, dtype, &need);
+        if (st != RMSN_OK) return st;
         if (workspace_bytes < (size_t)need) return RMSN_EWORKSPACE;
     }
     int32_t n32 = (int32_t)N;
@@ -693,7 +793,10 @@ int rmsnorm_query_config(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_co
     const int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!out || (is_bwd != 0 && is_bwd != 1)) return RMSN_EINVAL;
-    return resolve(M, N, dtype, is_bwd, 0, Align{16, 16}, out, nullptr);
+    int dev = 0;
+    const int s = current_device(&dev);
+    if (s != RMSN_OK) return s;
+    return resolve(dev, M, N, dtype, is_bwd, 0, Align{16, 16}, out, nullptr);
 }
 
 int rmsnorm_fwd(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype, void *y,
@@ -715,24 +818,15 @@ int rmsnorm_fwd_residual(const void *x, const void *res, const void *w, float ep
 }
 
 int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype) {
-    const int st = check_shape(M, N, dtype);
+    int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (M == 0) return 0;
-    // Enough for every row kernel the call may pick (plain or residual-fused,
-    // vector or scalar), so neither the caller's alignment nor the residual
-    // variant changes the answer.
+    int dev = 0;
+    st = current_device(&dev);
+    if (st != RMSN_OK) return st;
     int64_t need = 0;
-    for (int fused = 0; fused <= 1; ++fused) {
-        for (int v : {1, 4, 8, 16}) {  // every pointer alignment that selects a different kernel
-            const Align a{v > elem_size(dtype) ? v : elem_size(dtype), v > w_size(dtype) ? v : w_size(dtype)};
-            rmsnorm_config c;
-            const int s = resolve(M, N, dtype, 1, fused, a, &c, nullptr);
-            if (s != RMSN_OK) return s;
-            const int64_t b = workspace_for(c);
-            if (b > need) need = b;
-        }
-    }
-    return need;
+    st = workspace_need(dev, M, N, dtype, &need);
+    return st != RMSN_OK ? st : need;
 }
 
 int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,
