@@ -73,7 +73,8 @@ typedef enum {
     RMSN_EDTYPE = -2,      /* dtype is not an rmsn_dtype */
     RMSN_EWORKSPACE = -3,  /* workspace null or smaller than rmsnorm_bwd_workspace_bytes() */
     RMSN_EHIP = -4,        /* a HIP runtime call or kernel launch failed */
-    RMSN_ECONFIG = -5      /* an explicit launch configuration does not fit the shape */
+    RMSN_ECONFIG = -5,     /* an explicit launch configuration does not fit the shape */
+    RMSN_ESCRATCH = -6     /* rmsnorm_bwd_noalloc: the shape needs more than the static workspace */
 } rmsn_status;
 
 /*
@@ -200,6 +201,30 @@ int rmsnorm_fwd_with_config(const void *x, const void *w, float eps, int64_t M, 
 int rmsnorm_bwd_with_config(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
                             int64_t N, int dtype, void *dx, float *dw, void *workspace,
                             size_t workspace_bytes, const rmsnorm_config *cfg, void *stream);
+
+/*
+ * Backward without allocation, for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. Same arguments, results and errors as
+ * rmsnorm_bwd, minus the workspace: the fp32 dW partial rows go to a static
+ * device array of RMSN_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on
+ * each GPU it runs on until the process ends. The same kernels with the same
+ * grid run, so dx and dW equal rmsnorm_bwd's bit for bit. The call allocates
+ * nothing and launches what rmsnorm_bwd launches; its first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress).
+ *
+ * Limit: the shape's row kernel must need at most RMSN_NOALLOC_SCRATCH_BYTES
+ * of partial rows (grid * round_up(N, 64) * 4 bytes; bf16 4096 x 32768 needs
+ * exactly 32 MiB), else RMSN_ESCRATCH is returned before anything is
+ * launched. Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (two streams, two host threads) race on it and their dW
+ * is undefined; calls on one stream are ordered and safe. Nothing in the
+ * array needs to start at zero: each call's row kernel writes every partial
+ * row its combine reads.
+ */
+#define RMSN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int rmsnorm_bwd_noalloc(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
+                        int64_t N, int dtype, void *dx, float *dw, void *stream);
 
 /* Static text for a status code ("ok", "invalid argument", ...). Never NULL. */
 const char *rmsnorm_status_str(int status);

@@ -38,6 +38,8 @@ EDTYPE = -2
 EWORKSPACE = -3
 EHIP = -4
 ECONFIG = -5
+ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20  # RMSN_NOALLOC_SCRATCH_BYTES
 
 
 class RmsnormError(RuntimeError):
@@ -80,6 +82,7 @@ def _load() -> ctypes.CDLL:
         "rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]),
         "rmsnorm_bwd_with_config": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, cfgp, vp]),
         "rmsnorm_bwd_rows": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, sz, ctypes.POINTER(i64), vp]),
+        "rmsnorm_bwd_noalloc": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp]),
         "rmsnorm_fwd_residual": (i32, [vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, cfgp, vp]),
         "rmsnorm_bwd_residual": (i32, [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, cfgp, vp]),
         "rmsnorm_bwd_combine": (i32, [vp, i64, i64, vp, vp]),
@@ -108,7 +111,7 @@ lib = _load()
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_config", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
     "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_fwd_residual",
-    "rmsnorm_bwd_residual", "rmsnorm_status_str",
+    "rmsnorm_bwd_residual", "rmsnorm_bwd_noalloc", "rmsnorm_status_str",
     "rmsnorm_select_config", "rmsnorm_query_config", "rmsnorm_build_info",
     "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_read", "rmsn_probe_add",
     "rmsn_unfused_fwd", "rmsn_unfused_bwd_workspace_bytes", "rmsn_unfused_bwd", "rmsn_add",
@@ -221,6 +224,18 @@ def rmsnorm_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes,
                                           _arg(dw, "dw", "f32", count=int(N)),
                                           _arg(workspace, "workspace", nbytes=int(workspace_bytes)),
                                           int(workspace_bytes), _stream(stream)))
+
+
+def rmsnorm_bwd_noalloc(x, w, dy, rstd, M, N, dtype, dx, dw, stream=None) -> None:
+    """rmsnorm_bwd with its dW partial rows in the library's static device
+    array instead of a caller's workspace (no allocation; RMSN_ESCRATCH when
+    the shape needs more than NOALLOC_SCRATCH_BYTES)."""
+    mn = _mn(M, N)
+    _check("rmsnorm_bwd_noalloc",
+           lib.rmsnorm_bwd_noalloc(_arg(x, "x", "act", dtype, mn), _arg(w, "w", "weight", dtype, int(N)),
+                                   _arg(dy, "dy", "act", dtype, mn), _arg(rstd, "rstd", "f32", count=int(M)),
+                                   int(M), int(N), int(dtype), _arg(dx, "dx", "act", dtype, mn),
+                                   _arg(dw, "dw", "f32", count=int(N)), _stream(stream)))
 
 
 def rmsnorm_bwd_with_config(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes,

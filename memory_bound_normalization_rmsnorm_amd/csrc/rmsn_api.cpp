@@ -690,16 +690,21 @@ int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStre
 // dw_direct: when not NULL and the grid is a single workgroup, its partial row
 // is dW itself, written straight to dw_direct (16-byte aligned) instead of
 // the workspace; *partial_rows is then 0 and there is nothing to combine.
+// scratch: the workspace is the static device array of rmsnorm_bwd_noalloc
+// (the ladder's configuration only); `workspace` is then set to its address
+// on the current device, after every argument check, and the shape is refused
+// (RMSN_ESCRATCH) when its partial rows do not fit.
 int rows_impl(const void *x, const void *w, const void *dy, const void *dh, const float *rstd, int64_t M,
-              int64_t N, int dtype, void *dx, void *workspace, size_t workspace_bytes, int64_t *partial_rows,
-              hipStream_t s, const rmsnorm_config *req, float *dw_direct = nullptr) {
+              int64_t N, int dtype, void *dx, void *&workspace, size_t workspace_bytes, int64_t *partial_rows,
+              hipStream_t s, const rmsnorm_config *req, float *dw_direct = nullptr, bool scratch = false) {
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     if (!partial_rows) return RMSN_EINVAL;
     *partial_rows = 0;
     if (M == 0) return RMSN_OK;
     if (!x || !w || !dy || !rstd || !dx) return RMSN_EINVAL;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return RMSN_EWORKSPACE;
+    if (scratch && req) return RMSN_EINVAL;
+    if (!scratch && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)) return RMSN_EWORKSPACE;
     const int fused = dh ? 1 : 0;
     const Align a = fused ? align_of({x, dy, dx, dh}, w) : align_of({x, dy, dx}, w);
     if (!natural(a, dtype) || !aligned4(rstd)) return RMSN_EINVAL;
@@ -714,11 +719,18 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
         st = current_device(&dev);
         if (st == RMSN_OK) st = resolve(dev, M, N, dtype, 1, fused, a, &c, &fn);
         if (st != RMSN_OK) return st;
-        // the documented contract: at least what rmsnorm_bwd_workspace_bytes reports
-        int64_t need = 0;
-        st = workspace_need(dev, M, N, dtype, &need);
-        if (st != RMSN_OK) return st;
-        if (workspace_bytes < (size_t)need) return RMSN_EWORKSPACE;
+        if (scratch) {
+            // the static array: what this configuration writes must fit
+            if ((uint64_t)workspace_for(c) > (uint64_t)RMSN_NOALLOC_SCRATCH_BYTES) return RMSN_ESCRATCH;
+            st = rmsn::scratch_region(dev, &workspace);
+            if (st != RMSN_OK) return st;
+        } else {
+            // the documented contract: at least what rmsnorm_bwd_workspace_bytes reports
+            int64_t need = 0;
+            st = workspace_need(dev, M, N, dtype, &need);
+            if (st != RMSN_OK) return st;
+            if (workspace_bytes < (size_t)need) return RMSN_EWORKSPACE;
+        }
     }
     int32_t n32 = (int32_t)N;
     int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
@@ -734,7 +746,7 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
 
 int bwd_impl(const void *x, const void *w, const void *dy, const void *dh, const float *rstd, int64_t M,
              int64_t N, int dtype, void *dx, float *dw, void *workspace, size_t workspace_bytes, void *stream,
-             const rmsnorm_config *req) {
+             const rmsnorm_config *req, bool scratch = false) {
     int st = check_shape(M, N, dtype);
     if (st != RMSN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -750,7 +762,7 @@ int bwd_impl(const void *x, const void *w, const void *dy, const void *dh, const
     int64_t P = 0;
     // A single workgroup (a few rows, e.g. one decode step's) writes dW
     // itself: no combine launch, about half of such a call's time.
-    st = rows_impl(x, w, dy, dh, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req, dw);
+    st = rows_impl(x, w, dy, dh, rstd, M, N, dtype, dx, workspace, workspace_bytes, &P, s, req, dw, scratch);
     if (st != RMSN_OK) return st;
     return P == 0 ? RMSN_OK : combine_impl(workspace, P, N, dw, s);
 }
@@ -767,6 +779,7 @@ const char *rmsnorm_status_str(int status) {
     case RMSN_EWORKSPACE: return "workspace missing, misaligned or too small";
     case RMSN_EHIP: return "HIP runtime error";
     case RMSN_ECONFIG: return "launch configuration does not fit the shape";
+    case RMSN_ESCRATCH: return "shape needs more workspace than the static no-allocation scratch holds";
     default: return "unknown status";
     }
 }
@@ -846,6 +859,11 @@ int rmsnorm_bwd_residual(const void *h, const void *w, const void *dy, const voi
                          size_t workspace_bytes, const rmsnorm_config *cfg, void *stream) {
     if (M > 0 && !dh) return RMSN_EINVAL;
     return bwd_impl(h, w, dy, dh, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream, cfg);
+}
+
+int rmsnorm_bwd_noalloc(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,
+                        int dtype, void *dx, float *dw, void *stream) {
+    return bwd_impl(x, w, dy, nullptr, rstd, M, N, dtype, dx, dw, nullptr, 0, stream, nullptr, true);
 }
 
 int rmsnorm_bwd_rows(const void *x, const void *w, const void *dy, const float *rstd, int64_t M, int64_t N,

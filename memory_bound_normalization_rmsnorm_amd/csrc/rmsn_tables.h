@@ -68,4 +68,9 @@ const void *elem_kernel(int dtype, int is_bwd, int res, int k, int g, int lanes)
 const void *dw_combine_kernel();
 const void *fill_zero_kernel();
 
+// Device address of the current device `dev`'s copy of the static workspace
+// of rmsnorm_bwd_noalloc (RMSN_NOALLOC_SCRATCH_BYTES, 256-byte aligned),
+// looked up on the first call per device and cached. RMSN_OK or RMSN_EHIP.
+int scratch_region(int dev, void **ptr);
+
 }  // namespace rmsn

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 def test_build_info_and_status_strings():
     assert "gfx950" in rn.rmsnorm_build_info()
     assert rn.rmsnorm_status_str(rn.OK) == "ok"
-    for s in (rn.EINVAL, rn.EDTYPE, rn.EWORKSPACE, rn.EHIP, rn.ECONFIG):
+    for s in (rn.EINVAL, rn.EDTYPE, rn.EWORKSPACE, rn.EHIP, rn.ECONFIG, rn.ESCRATCH):
         assert rn.rmsnorm_status_str(s) not in ("ok", "unknown status")
     assert rn.rmsnorm_status_str(12345) == "unknown status"
 
@@ -70,6 +70,24 @@ def test_residual_argument_errors():
                                        None, None) == rn.EINVAL
     assert rn.lib.rmsnorm_bwd_residual(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, rn.F16, FAKE, FAKE, None, 1 << 20,
                                        None, None) == rn.EWORKSPACE
+
+
+def test_noalloc_argument_errors():
+    # rmsnorm_bwd_noalloc checks its arguments before any HIP call (and before
+    # looking up the static workspace)
+    L = rn.lib
+    assert L.rmsnorm_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 4, 8, 9, FAKE, FAKE, None) == rn.EDTYPE
+    assert L.rmsnorm_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, -1, 8, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 4, 0, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 4, 8, rn.BF16, FAKE, None, None) == rn.EINVAL
+    for k in range(4):  # x, w, dy, rstd missing
+        a = [FAKE] * 4
+        a[k] = None
+        assert L.rmsnorm_bwd_noalloc(*a, 4, 8, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 4, 8, rn.BF16, None, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_bwd_noalloc(FAKE + 1, FAKE, FAKE, FAKE, 4, 8, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
+    assert L.rmsnorm_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, 4, 8, rn.BF16, FAKE, FAKE + 2, None) == rn.EINVAL
+    assert rn.rmsnorm_status_str(rn.ESCRATCH) not in ("ok", "unknown status")
 
 
 def test_unfused_baseline_argument_errors():
