@@ -46,6 +46,16 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 GIB = 1 << 30
 SETTLE_S = 0.25  # untimed steps before the warmup steps (clock settle after the CPU leg)
 CELL_SETTLE_S = 0.05  # untimed graph replays before each cell's timed replays
+# Per-kernel graph length: launches per HIP graph, sized from the kernel's
+# bytes so that one replay lasts about GRAPH_TARGET_MS (at least
+# GRAPH_MIN_LAUNCHES launches), whatever --steps is. Short graphs made the
+# average launch slower than the kernel's steady state (20 launches: 69.0 us
+# against 65.0 us for the backward row kernel at bf16 16384 x 4096).
+GRAPH_MIN_LAUNCHES, GRAPH_MAX_LAUNCHES, GRAPH_TARGET_MS = 200, 4000, 50.0
+GRAPH_EST_GBPS = 6000.0   # for sizing only: a launch is estimated at its bytes / this rate, at least 5 us
+SMALL_CELL_BYTES = 4 << 20  # cells with less than this per rotation set are timed call by call after a flush
+CELL_ROTATION_BYTES = 2 * GIB  # larger cells rotate through at least this many bytes of sets
+CELL_PARITY_ROWS = 64       # rows of y and dx each cell compares with the oracle (every rstd and dW column too)
 
 
 def parse_args(argv=None):
@@ -96,6 +106,25 @@ def launch_key(cfg: dict) -> list:
     """The fields of a launch configuration that decide a kernel's traffic."""
     return [int(cfg[k]) for k in ("vector_path", "lanes_per_row", "vecs_per_lane", "wg_threads", "prefetch",
                                   "stream_loads", "grid")]
+
+
+def graph_launches(nbytes: int) -> int:
+    """Launches per timing graph for a kernel moving `nbytes` per launch."""
+    est_us = max(5.0, nbytes / (GRAPH_EST_GBPS * 1e3))
+    return int(min(GRAPH_MAX_LAUNCHES, max(GRAPH_MIN_LAUNCHES, -(-GRAPH_TARGET_MS * 1e3 // est_us))))
+
+
+def oracle_threads() -> int:
+    """Threads of the all-cores oracle leg: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when that is set (the host's share for this GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def git_rev() -> str:
@@ -456,33 +485,35 @@ def main(argv=None):
         step_event_ms = e0.elapsed_time(e1) / K
         ms_per_step = elapsed * 1e3 / K
 
-    def batch(fn):
+    def batch(fn, n):
         a, b = timer.event(), timer.event()
         a.record()
-        for k in range(K):
+        for k in range(n):
             fn(k)
         b.record()
         b.synchronize()
-        return a.elapsed_time(b) * 1e3 / K
+        return a.elapsed_time(b) * 1e3 / n
 
-    def graph_batch(fn, outputs, replays=3):
-        """Per-launch us of K launches of fn captured in a HIP graph: the median
-        of `replays` timed replays after one untimed one. outputs() lists the
-        tensors the last launch writes; every replay's are checked against the
-        eager launches' (the last R launches of the sequence, which write them)."""
-        for k in range(max(0, K - R), K):
+    def graph_batch(fn, outputs, KG, replays=3):
+        """Per-launch us of KG launches of fn captured in a HIP graph: the median
+        of `replays` timed replays after one untimed one. outputs(last) lists the
+        tensors launch `last` writes (the last of the sequence); every replay's
+        are checked against the eager launches' (the last R launches of the
+        sequence, which write them)."""
+        last = (KG - 1) % R
+        for k in range(max(0, KG - R), KG):
             fn(k)
         torch.cuda.synchronize()
-        ref = [t.clone() for t in outputs()]
+        ref = [t.clone() for t in outputs(last)]
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for k in range(K):
+            for k in range(KG):
                 fn(k)
         graph.replay()
         torch.cuda.synchronize()
         times = []
         for _ in range(replays):
-            for t in outputs():
+            for t in outputs(last):
                 t.fill_(float("nan"))
             torch.cuda.synchronize()
             a, b = timer.event(), timer.event()
@@ -490,8 +521,8 @@ def main(argv=None):
             graph.replay()
             b.record()
             b.synchronize()
-            times.append(a.elapsed_time(b) * 1e3 / K)
-            for t, r in zip(outputs(), ref):
+            times.append(a.elapsed_time(b) * 1e3 / KG)
+            for t, r in zip(outputs(last), ref):
                 if not torch.equal(t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16),
                                    r.view(torch.int32) if r.dtype == torch.float32 else r.view(torch.int16)):
                     raise RuntimeError("graph replay output differs from the eager launches")
@@ -501,19 +532,23 @@ def main(argv=None):
     def rows_k(k):
         parts[k % R] = bwd_rows(sets[(k + R // 2) % R])
 
-    last = (K - 1) % R
+    P_rows = cfg_b["partial_rows"]
+    KG = {"fwd": graph_launches(fwd_bytes), "bwd_rows": graph_launches(rows_bytes),
+          "combine": graph_launches(P_rows * ldp_floats * 4 + combine_bytes)}
     f_eager = r_eager = c_eager = None
     if args.eager_only or not kernels_only:
-        f_eager = batch(lambda k: fwd(sets[k % R]))
-        r_eager = batch(rows_k)
-        c_eager = batch(lambda k: combine(parts[k % R]))
+        # --eager-only (counter runs) launches K of each; otherwise as many as the graphs hold
+        f_eager = batch(lambda k: fwd(sets[k % R]), K if args.eager_only else KG["fwd"])
+        r_eager = batch(rows_k, K if args.eager_only else KG["bwd_rows"])
+        c_eager = batch(lambda k: combine(parts[k % R]), K if args.eager_only else KG["combine"])
     if args.eager_only:
         f_us, r_us, c_us = f_eager, r_eager, c_eager
     else:
-        f_us = graph_batch(lambda k: fwd(sets[k % R]), lambda: (sets[last]["y"], sets[last]["rstd"]))
-        r_us = graph_batch(rows_k, lambda: (sets[(last + R // 2) % R]["dx"],
-                                            ws[:parts[last] * ldp_floats].view(parts[last], ldp_floats)[:, :N]))
-        c_us = graph_batch(lambda k: combine(parts[k % R]), lambda: (dw,))
+        f_us = graph_batch(lambda k: fwd(sets[k % R]), lambda last: (sets[last]["y"], sets[last]["rstd"]), KG["fwd"])
+        r_us = graph_batch(rows_k, lambda last: (sets[(last + R // 2) % R]["dx"],
+                                                 ws[:parts[last] * ldp_floats].view(parts[last], ldp_floats)[:, :N]),
+                           KG["bwd_rows"])
+        c_us = graph_batch(lambda k: combine(parts[k % R]), lambda last: (dw,), KG["combine"])
     def us(v):
         return "-" if v is None else f"{v:.1f}"
 
@@ -527,6 +562,7 @@ def main(argv=None):
     if args.mode == "kernels":
         print(json.dumps({"mode": "kernels", "steps": K, "ms_per_step": ms_per_step, "fwd_us": f_us,
                           "bwd_rows_us": r_us, "combine_us": c_us, "eager": eager, "source_hash": env["source_hash"],
+                          "graph_launches": None if args.eager_only else KG, "graph_replays": 3,
                           "fwd_launch": launch_key(cfg_f), "bwd_launch": launch_key(cfg_b)}))
         return 0
 
@@ -613,9 +649,11 @@ def main(argv=None):
                        "before_timing": smi_brief(env["smi_before_timing"])},
         "timing": "value: wall clock over K whole eager steps (synchronised at both ends), after untimed steps "
                   f"for {SETTLE_S} s (clock settle after the CPU leg) and W warmup steps; per-kernel avg_us: "
-                  "K rotated launches of that kernel captured in a HIP graph, replayed between one HIP event "
-                  "pair on the launch stream (outputs checked against eager); eager_batch_us: the same K "
-                  "launches issued eagerly between one event pair",
+                  "graph_launches rotated launches of that kernel (about 50 ms of work, at least 200, whatever "
+                  "K is) captured in a HIP graph, the median of 3 replays each between one HIP event pair on "
+                  "the launch stream (outputs checked against eager); eager_batch_us: the same launches "
+                  "issued eagerly between one event pair",
+        "graph_launches": KG,
         "eager_batch_us": eager,
         "pct_measured_roofline": round(100 * value / measured, 1),
         "validation": validation,
@@ -681,11 +719,21 @@ def cell_bytes(variant, M, N, es, wsz):
 
 
 def run_cells(args, torch, rn, timer):
-    """Time every cell's variants as K calls captured in a HIP graph and
-    replayed (the per-call time without host launch gaps), and as K eager
-    launches between two events. Every graph replay's outputs are compared with
-    the eager call's, bit for bit."""
+    """Time every cell's variants. Each variant is first checked against the
+    fp64 oracle on the cell's own inputs (CELL_PARITY_ROWS rows of y and dx,
+    every rstd, every dW column; the residual sum h bit for bit); a cell that
+    fails gets no time. Cells of at least SMALL_CELL_BYTES per rotation set
+    rotate through at least CELL_ROTATION_BYTES of sets and are timed as K
+    calls captured in a HIP graph and replayed (the per-call time without
+    host launch gaps), and as K eager launches between two events; every
+    graph replay's outputs are compared with the eager call's, bit for bit.
+    Smaller cells would sit in the 256 MB MALL however they rotate, so each
+    of their calls is timed on its own between two events, after a 1 GiB
+    cache-flushing read (the median of args.isolated_reps calls)."""
     import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_util import to_host
 
     groups = list(CELL_GROUPS) if args.cells == "all" else args.cells.split(",")
     roof = probe_roofline(torch, rn, timer, args.probe_gib)
@@ -693,7 +741,14 @@ def run_cells(args, torch, rn, timer):
     log(f"roofline {measured} GB/s ({roof['best_probe']})")
     codes = {"f32": rn.F32, "bf16": rn.BF16, "f16": rn.F16, "bf16w32": rn.BF16_WF32, "f16w32": rn.F16_WF32}
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-    rows = []
+    # the cache-flushing read of the small cells' isolated calls
+    flush_a = torch.full((GIB,), 3, dtype=torch.uint8, device="cuda")
+    flush_sink = torch.zeros(64, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        rn.rmsn_probe_read(flush_a, GIB, flush_sink, 0)
+
+    rows, failures = [], []
     for group in groups:
         for name, fmt, M, N in CELL_GROUPS[group]:
             act, es, wsz = FMT[fmt]
@@ -704,7 +759,8 @@ def run_cells(args, torch, rn, timer):
             variants = CELL_VARIANTS[group]
             resid = any(v.startswith("residual") for v in variants)
             per_set = M * N * es * (7 if resid else 4) + 4 * M
-            R = max(2, min(64, -(-int(1.5 * GIB) // per_set)))
+            small = per_set < SMALL_CELL_BYTES
+            R = 2 if small else max(4, -(-CELL_ROTATION_BYTES // per_set))
 
             def randn(scale=1.0):
                 return (torch.randn((M, N), generator=gen, device="cuda") * scale).to(tdt[act])
@@ -714,6 +770,7 @@ def run_cells(args, torch, rn, timer):
                 base["res"] = randn()
                 base["dh"] = randn(1e-2)
             w = (1.0 + 0.1 * torch.randn(N, generator=gen, device="cuda")).to(torch.float32 if wsz == 4 else tdt[act])
+            ref = cell_reference(base, w, eps, act, "f32" if wsz == 4 else act, M, N, to_host)
             sets = []
             for k in range(R):
                 s = {key: (v if k == 0 else v.clone()) for key, v in base.items()}
@@ -731,30 +788,112 @@ def run_cells(args, torch, rn, timer):
                     continue  # the unfused kernels take the vector layout only
                 fb, bb = cell_bytes(variant, M, N, es, wsz)
                 ops = cell_ops(rn, variant, sets, w, dw, ws, ws_n, eps, M, N, code)
-                # every set's rstd (and h) for the backward
+                rec = {"group": group, "cell": name, "format": fmt, "M": M, "N": N, "variant": variant,
+                       "rotation_sets": R, "timing": "isolated" if small else "graph"}
+                # every set's rstd (and h) for the backward; set 0's outputs checked against the oracle
                 for k in range(R):
                     ops["fwd"](k)
+                for t in ops["outputs_bwd"](0):
+                    t.fill_(float("nan"))
+                ops["bwd"](0)
                 torch.cuda.synchronize()
-                rec = {"group": group, "cell": name, "format": fmt, "M": M, "N": N, "variant": variant,
-                       "rotation_sets": R}
+                try:
+                    rec["parity"] = cell_check(sets[0], dw, ref, act, variant, resid, to_host)
+                except AssertionError as e:
+                    rec["parity"] = {"passed": False, "error": str(e)[:500]}
+                    failures.append(f"{name}/{variant}")
+                    rows.append(rec)
+                    log(json.dumps(rec))
+                    continue
                 for which, nbytes in (("fwd", fb), ("bwd", bb)):
-                    g_us, e_us = time_cell(torch, timer, ops[which], ops["outputs_" + which], R)
-                    best = min(g_us, e_us)
-                    rec[which + "_graph_us"] = round(g_us, 2)
-                    rec[which + "_eager_us"] = round(e_us, 2)
+                    if small:
+                        med, times = timer.median_ms(lambda: ops[which](0), args.isolated_reps, between=flush)
+                        best = med * 1e3
+                        rec[which + "_isolated_us"] = round(best, 2)
+                        rec[which + "_isolated_p10_p90_us"] = [round(sorted(times)[int(0.1 * (len(times) - 1))] * 1e3, 2),
+                                                                round(sorted(times)[int(0.9 * (len(times) - 1))] * 1e3, 2)]
+                        g_us, e_us = time_cell(torch, timer, ops[which], ops["outputs_" + which], R)
+                        rec[which + "_warm_graph_us"] = round(g_us, 2)
+                    else:
+                        g_us, e_us = time_cell(torch, timer, ops[which], ops["outputs_" + which], R)
+                        best = min(g_us, e_us)
+                        rec[which + "_graph_us"] = round(g_us, 2)
+                        rec[which + "_eager_us"] = round(e_us, 2)
                     rec[which + "_GBps"] = round(nbytes / (best * 1e-6) / 1e9, 1)
                     rec[which + "_pct_roofline"] = round(100 * nbytes / (best * 1e-6) / 1e9 / measured, 1)
                     rec[which + "_bytes"] = nbytes
                 rows.append(rec)
                 log(json.dumps(rec))
-            del sets, base, ws, dw
+            del sets, base, ws, dw, ref
             torch.cuda.empty_cache()
-    out = {"mode": "cells", "roofline": roof, "cells": rows}
+    del flush_a, flush_sink
+    out = {"mode": "cells", "roofline": roof, "cells": rows, "parity_failures": failures,
+           "timing": f"cells under {SMALL_CELL_BYTES >> 20} MiB per rotation set: the median of "
+                     f"{args.isolated_reps} single calls, each between two HIP events after a 1 GiB "
+                     "cache-flushing read (warm graph-replay times beside them); larger cells: rotation "
+                     f"through at least {CELL_ROTATION_BYTES >> 30} GiB of input sets, the lower of the "
+                     "graph-replay and eager per-call times"}
     os.makedirs(args.out_dir, exist_ok=True)
     with open(os.path.join(args.out_dir, "cells.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
-    return 0
+    return 1 if failures else 0
+
+
+def cell_reference(base, w, eps, act, wdt, M, N, to_host):
+    """The oracle's values for a cell, from host copies of its device inputs:
+    y and dx on CELL_PARITY_ROWS rows spread over the cell (first and last
+    included), r on every row and dW over every row (threads over row blocks,
+    as the CPU-baseline leg), and the stored residual sum h on the sampled
+    rows."""
+    import numpy as np
+
+    import oracle
+
+    x = to_host(base["x"], act)
+    dy = to_host(base["dy"], act)
+    res = to_host(base["res"], act) if "res" in base else None
+    dh = to_host(base["dh"], act) if "dh" in base else None
+    wh = to_host(w, wdt)
+    rows = np.unique(np.linspace(0, M - 1, min(M, CELL_PARITY_ROWS)).astype(np.int64))
+    if res is None:
+        oy, _ = oracle.fwd(x, wh, eps, act, rows=rows, wdtype=wdt)
+        oh = None
+    else:
+        oh, oy, _ = oracle.fwd_residual(x, res, wh, eps, act, rows=rows, wdtype=wdt)
+    odx, orr_rows = oracle.bwd_dx(x, wh, dy, eps, act, rows=rows, res=res, dh=dh, wdtype=wdt)
+    _, r, _, dw = oracle_pass(x, wh, dy, eps, act, oracle_threads(), keep=False, wdtype=wdt, res=res, dh=dh,
+                              rows_outputs=False)
+    return {"rows": rows, "y": oy, "h": oh, "dx": odx, "r_rows": orr_rows, "rstd": r, "dw": dw,
+            "x": x, "w": wh, "dy": dy, "dh": dh}
+
+
+def cell_check(s, dw, ref, act, variant, resid, to_host):
+    """Gates of one variant's outputs (rotation set 0) against the cell's
+    oracle values; returns the statistics, raises AssertionError on a miss."""
+    import numpy as np
+
+    from parity_util import check_dw, check_rows, check_rstd, term_rms, widen
+
+    rows = ref["rows"]
+    out = {"rows_checked": int(rows.size)}
+    y = to_host(s["y"], act)[rows]
+    out["y_max_gate_ratio"] = check_rows(y, ref["y"], act, "y")["max_gate_ratio"]
+    if resid:
+        assert np.array_equal(widen(to_host(s["h"], act)[rows], act), ref["h"]), "stored residual sum h"
+    extra = None
+    if variant == "residual_unfused":
+        # the normalisation's dx is rounded to storage before dh is added
+        u = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -24}[act]
+        extra = 2 * u * np.abs(ref["dx"] - widen(ref["dh"][rows], act))
+    floor = term_rms(None, ref["w"], ref["dy"], ref["r_rows"], act, rows=rows, dh=ref["dh"])
+    out["dx_max_gate_ratio"] = check_rows(to_host(s["dx"], act)[rows], ref["dx"], act, "dx", floor=floor,
+                                          extra=extra)["max_gate_ratio"]
+    out["rstd_max_rel_err"] = check_rstd(s["rstd"].cpu().numpy(), ref["rstd"])["max_rel_err"]
+    d = check_dw(dw.cpu().numpy(), ref["dw"], act)
+    out.update({"dw_max_rel_err": d["max_rel_err"], "dw_max_gate_ratio": d["max_gate_ratio"],
+                "dw_cols_above_plain_rel_tol": d["cols_above_plain_rel_tol"], "passed": True})
+    return out
 
 
 def cell_ops(rn, variant, sets, w, dw, ws, ws_n, eps, M, N, code):
@@ -858,69 +997,123 @@ def load_traffic(src_hash, kernel, workload, launch):
     return entry.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline_leg(wl, x, w, dy, eps, budget_s):
-    """The fp64 oracle, as it stands, on this host: forward (y, rstd) and
-    backward dx for consecutive blocks of rows until the time budget is spent
-    (single thread), plus dW over all rows. Its results also serve as the
-    reference the GPU outputs are validated against. Returns (baseline
-    record, reference)."""
+def oracle_pass(x, w, dy, eps, dtype, threads, keep=False, wdtype=None, res=None, dh=None, rows_outputs=True):
+    """One whole pass of the fp64 oracle over a workload: forward (y, r) and
+    backward dx for every row, and dW over every row (rows_outputs False: only
+    r and dW; y and dx are not computed). The rows are split into
+    `threads` contiguous blocks (a static schedule), one thread per block (the
+    oracle's C code releases the GIL while it runs); each block's dW is summed
+    over its own rows in fp64 and the block sums are added in block order, so
+    the result does not depend on thread timing. Returns (y, r, dx, dw); y
+    and dx only when `keep`, else None (each block's are dropped)."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
 
-    block = 256
-    done = 0
-    t_rows = 0.0
-    ref_rows = {}
-    while done < wl.M and t_rows < budget_s:
-        rows = np.arange(done, min(done + block, wl.M), dtype=np.int64)
-        t0 = time.perf_counter()
-        oy, orr = oracle.fwd(x, w, eps, wl.dtype, rows=rows)
-        odx, _ = oracle.bwd_dx(x, w, dy, eps, wl.dtype, rows=rows)
-        t_rows += time.perf_counter() - t0
-        if len(ref_rows) < 4:  # keep a few blocks for validation
-            ref_rows[int(rows[0])] = (rows, oy, orr, odx)
-        done = int(rows[-1]) + 1
-    t0 = time.perf_counter()
-    _, r_all = oracle.fwd(x, w, eps, wl.dtype, want_y=False)
-    odw = oracle.bwd_dw(x, dy, eps, wl.dtype)
-    t_all = time.perf_counter() - t0
-    es = 4 if wl.dtype == "f32" else 2
-    per_row = (2 * wl.N * es + 4) + (3 * wl.N * es + 4)   # fwd + bwd algorithmic bytes of one row
-    gbps = done * per_row / t_rows / 1e9
+    M, N = x.shape
+    T = max(1, min(int(threads), M)) if M else 1
+    bounds = [(M * t // T, M * (t + 1) // T) for t in range(T)]
+    y_all = np.empty((M, N)) if keep and rows_outputs else None
+    dx_all = np.empty((M, N)) if keep and rows_outputs else None
+    r_all = np.empty(M)
+
+    def block(t):
+        lo, hi = bounds[t]
+        rows = np.arange(lo, hi, dtype=np.int64)
+        sl = slice(lo, hi)
+        if res is None:
+            oy, orr = oracle.fwd(x, w, eps, dtype, rows=rows, wdtype=wdtype, want_y=rows_outputs)
+        else:
+            _, oy, orr = oracle.fwd_residual(x, res, w, eps, dtype, rows=rows, wdtype=wdtype, want_y=rows_outputs)
+        if rows_outputs:
+            odx, _ = oracle.bwd_dx(x, w, dy, eps, dtype, rows=rows, res=res, dh=dh, wdtype=wdtype)
+        odw = oracle.bwd_dw(x[sl], dy[sl], eps, dtype, res=None if res is None else res[sl])
+        r_all[sl] = orr
+        if keep and rows_outputs:
+            y_all[sl] = oy
+            dx_all[sl] = odx
+        return odw
+
+    if T == 1:
+        parts = [block(0)]
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=T) as ex:
+            parts = list(ex.map(block, range(T)))
+    dw = np.zeros(N)
+    for p in parts:  # block order
+        dw += p
+    return y_all, r_all, dx_all, dw
+
+
+def cpu_baseline_leg(wl, x, w, dy, eps, budget_s):
+    """The fp64 oracle, as it stands, timed on this host over the whole
+    workload (forward y and rstd, backward dx and dW, every row): single
+    threaded, and on all the host CPUs this process may use (rows in static
+    contiguous blocks, one per thread, per-thread dW added in thread order).
+    Each variant is the median of up to 3 passes within `budget_s`. The last
+    all-cores pass is kept as the validation reference. Returns (baseline
+    record, reference)."""
+    nbytes = wl.fwd_bytes() + wl.bwd_bytes()
+    T = oracle_threads()
+
+    def timed(threads, keep_last):
+        times, out, t_start = [], None, time.perf_counter()
+        for k in range(3):
+            t0 = time.perf_counter()
+            out = oracle_pass(x, w, dy, eps, wl.dtype, threads, keep=keep_last and k == 2)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s and k < 2:
+                if keep_last:  # the reference needs the kept outputs
+                    out = oracle_pass(x, w, dy, eps, wl.dtype, threads, keep=True)
+                break
+        return statistics.median(times), len(times), out
+
+    t1, n1, _ = timed(1, False)
+    tn, nn, ref = timed(T, True)
+    info = cpu_info()
     record = {
-        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"fp64 oracle forward (y, rstd) and backward dx on the first {done} of {wl.M} rows "
-                  f"(bounded to ~{budget_s:.0f}s, single thread); x and w and the row bytes of fwd+bwd counted",
-        "seconds": round(t_rows, 2), "rows": done,
-        "dw_all_rows_seconds": round(t_all, 2),
+        "value": round(nbytes / tn / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+        "sample": f"the whole workload ({wl.M} x {wl.N} {wl.dtype}): fp64 oracle forward (y, rstd) and backward "
+                  f"(dx, dW) over every row, median of {nn} passes; rows split into {T} contiguous blocks, one "
+                  "thread each, per-thread dW added in thread order; GB/s = the algorithmic bytes of one forward "
+                  "and one backward call over the pass time",
+        "seconds": round(tn, 3),
+        "single_thread": {"value": round(nbytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1, "seconds": round(t1, 3),
+                          "passes": n1},
+        "cpu_model": info["model"], "logical_cpus_available": info["logical_cpus_available"],
     }
     log(f"cpu baseline: {record}")
-    return record, {"rows": ref_rows, "rstd": r_all, "dw": odw}
+    y, r, dx, dw = ref
+    return record, {"y": y, "rstd": r, "dx": dx, "dw": dw}
 
 
-def validate(wl, gpu, ref, inputs):
-    """Tolerance gates against the oracle: y and dx on the reference row blocks,
-    every rstd, every dW column. A failed gate raises: a wrong kernel gets no
-    number."""
-    import numpy as np
-
+def validate(wl, gpu, ref, inputs, block=2048):
+    """Tolerance gates against the oracle on every row of y and dx (in blocks
+    of rows), every rstd and every dW column. A failed gate raises: a wrong
+    kernel gets no number."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from parity_util import check_dw, check_rows, check_rstd, term_rms
 
     x, w, dy = inputs
     y, rstd, dx, dw = gpu
-    stats = {"y_max_abs_err": 0.0, "dx_max_abs_err": 0.0}
-    for rows, oy, orr, odx in ref["rows"].values():
-        sy = check_rows(y[rows], oy, wl.dtype, "y")
-        sdx = check_rows(dx[rows], odx, wl.dtype, "dx", floor=term_rms(x, w, dy, orr, wl.dtype, rows=rows))
-        stats["y_max_abs_err"] = max(stats["y_max_abs_err"], sy["max_abs_err"])
-        stats["dx_max_abs_err"] = max(stats["dx_max_abs_err"], sdx["max_abs_err"])
-    check_rstd(rstd, ref["rstd"])
-    check_dw(dw, ref["dw"], wl.dtype)
-    stats["rstd_max_rel_err"] = float(np.max(np.abs(rstd - ref["rstd"]) / ref["rstd"]))
-    stats["dw_max_rel_err"] = float(np.max(np.abs(dw - ref["dw"]) / np.maximum(np.abs(ref["dw"]), 1e-30)))
-    stats["rows_checked"] = int(sum(len(v[0]) for v in ref["rows"].values()))
+    stats = {"y_max_abs_err": 0.0, "dx_max_abs_err": 0.0, "y_max_gate_ratio": 0.0, "dx_max_gate_ratio": 0.0}
+    M = wl.M
+    for lo in range(0, M, block):
+        rows = slice(lo, min(M, lo + block))
+        idx = list(range(rows.start, rows.stop))
+        sy = check_rows(y[rows], ref["y"][rows], wl.dtype, "y")
+        sdx = check_rows(dx[rows], ref["dx"][rows], wl.dtype, "dx",
+                         floor=term_rms(x, w, dy, ref["rstd"][rows], wl.dtype, rows=idx))
+        for k, st in (("y", sy), ("dx", sdx)):
+            stats[k + "_max_abs_err"] = max(stats[k + "_max_abs_err"], st["max_abs_err"])
+            stats[k + "_max_gate_ratio"] = max(stats[k + "_max_gate_ratio"], st["max_gate_ratio"])
+    stats["rstd_max_rel_err"] = check_rstd(rstd, ref["rstd"])["max_rel_err"]
+    dws = check_dw(dw, ref["dw"], wl.dtype)
+    stats.update({"dw_max_rel_err": dws["max_rel_err"], "dw_max_gate_ratio": dws["max_gate_ratio"],
+                  "dw_cols_above_plain_rel_tol": dws["cols_above_plain_rel_tol"], "dw_gate": dws["gate"]})
+    stats["rows_checked"] = M
     stats["passed"] = True
     return stats
 

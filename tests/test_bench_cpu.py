@@ -74,3 +74,107 @@ def test_more_than_one_gpu_is_refused(bench, capsys):
     assert bench.main(["--gpus", "2"]) == 2
     out = json.loads(capsys.readouterr().out.strip())
     assert "one GPU only" in out["error"]
+
+
+def test_graph_launches_independent_of_steps(bench):
+    # about 50 ms per replay, at least 200 launches, at most 4000
+    assert bench.graph_launches(402_743_296) == 745        # backward rows at bf16 16384 x 4096 (~67 us)
+    assert bench.graph_launches(268_509_184) == 1118
+    assert bench.graph_launches(16_384) == bench.GRAPH_MAX_LAUNCHES   # a few-us kernel
+    assert bench.graph_launches(10 << 30) == bench.GRAPH_MIN_LAUNCHES
+
+
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_threaded_oracle_pass_matches_the_plain_oracle(bench, threads):
+    """The all-cores CPU baseline runs the oracle on row blocks in threads and
+    adds the per-block dW in block order: the same y, r and dx as one call,
+    and dW equal to the sequential sum up to fp64 rounding."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    x, w, dy = si.random_case(37, 96, "bf16", seed=11, dy_scale=1e-2)
+    eps = si.eps_f32(1e-6)
+    y, r, dx, dw = bench.oracle_pass(x, w, dy, eps, "bf16", threads, keep=True)
+    oy, orr = oracle.fwd(x, w, eps, "bf16")
+    odx, _ = oracle.bwd_dx(x, w, dy, eps, "bf16")
+    odw = oracle.bwd_dw(x, dy, eps, "bf16")
+    assert np.array_equal(y, oy) and np.array_equal(r, orr) and np.array_equal(dx, odx)
+    assert np.allclose(dw, odw, rtol=1e-13, atol=1e-15)
+    _, r2, dx2, dw2 = bench.oracle_pass(x, w, dy, eps, "bf16", threads, keep=False)
+    assert dx2 is None and np.array_equal(r2, orr) and np.array_equal(dw2, dw)
+
+
+def test_validate_checks_every_row(bench):
+    """validate() gates every row of y and dx (in blocks), every rstd and every
+    dW column: the oracle's own values rounded to bf16 pass, and one wrong
+    element in the last row fails."""
+    import types
+
+    import numpy as np
+
+    import synthetic_inputs as si
+
+    M, N = 300, 64
+    x, w, dy = si.random_case(M, N, "bf16", seed=12, dy_scale=1e-2)
+    eps = si.eps_f32(1e-6)
+    y, r, dx, dw = bench.oracle_pass(x, w, dy, eps, "bf16", 4, keep=True)
+    wl = types.SimpleNamespace(M=M, N=N, dtype="bf16")
+    gpu = (si.to_storage(y.astype(np.float32), "bf16"), r.astype(np.float32),
+           si.to_storage(dx.astype(np.float32), "bf16"), dw.astype(np.float32))
+    ref = {"y": y, "rstd": r, "dx": dx, "dw": dw}
+    stats = bench.validate(wl, gpu, ref, (x, w, dy), block=64)
+    assert stats["passed"] and stats["rows_checked"] == M
+    assert stats["dw_cols_above_plain_rel_tol"] == 0 and stats["y_max_gate_ratio"] <= 1.0
+    bad = gpu[2].copy()
+    bad[M - 1, N - 1] ^= np.uint16(0x4000)  # a large change to one dx element of the last row
+    with pytest.raises(AssertionError):
+        bench.validate(wl, (gpu[0], gpu[1], bad, gpu[3]), ref, (x, w, dy), block=64)
+
+
+@pytest.mark.parametrize("variant,fmt", [("fused", "bf16"), ("fused", "bf16w32"), ("residual", "f16"),
+                                         ("residual_unfused", "bf16")])
+def test_cell_check_against_the_oracle(bench, variant, fmt):
+    """The cells-mode gate: outputs equal to the oracle's values rounded once to
+    storage pass; one wrong dx element in a sampled row fails."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from parity_util import to_host
+
+    M, N = 70, 48
+    act, es, wsz = bench.FMT[fmt]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[act]
+    g = torch.Generator().manual_seed(5)
+    base = {"x": torch.randn((M, N), generator=g).to(tdt), "dy": (torch.randn((M, N), generator=g) * 1e-2).to(tdt)}
+    resid = variant.startswith("residual")
+    if resid:
+        base["res"] = torch.randn((M, N), generator=g).to(tdt)
+        base["dh"] = (torch.randn((M, N), generator=g) * 1e-2).to(tdt)
+    wdt = "f32" if wsz == 4 else act
+    w = (1 + 0.1 * torch.randn(N, generator=g)).to(torch.float32 if wsz == 4 else tdt)
+    eps = float(np.float32(1e-6))
+    ref = bench.cell_reference(base, w, eps, act, wdt, M, N, to_host)
+    assert ref["rows"][0] == 0 and ref["rows"][-1] == M - 1
+    xh, dyh = to_host(base["x"], act), to_host(base["dy"], act)
+    res = to_host(base["res"], act) if resid else None
+    dh = to_host(base["dh"], act) if resid else None
+    wh = to_host(w, wdt)
+    if resid:
+        h, y, r = oracle.fwd_residual(xh, res, wh, eps, act, wdtype=wdt)
+    else:
+        (y, r), h = oracle.fwd(xh, wh, eps, act, wdtype=wdt), None
+    dx, _ = oracle.bwd_dx(xh, wh, dyh, eps, act, res=res, dh=dh, wdtype=wdt)
+    s = {"y": torch.from_numpy(y).to(tdt), "dx": torch.from_numpy(dx).to(tdt),
+         "rstd": torch.from_numpy(r.astype(np.float32))}
+    if resid:
+        s["h"] = torch.from_numpy(h).to(tdt)
+    dw = torch.from_numpy(oracle.bwd_dw(xh, dyh, eps, act, res=res).astype(np.float32))
+    out = bench.cell_check(s, dw, ref, act, variant, resid, to_host)
+    assert out["passed"] and out["rows_checked"] == min(M, bench.CELL_PARITY_ROWS)
+    k = int(ref["rows"][3])
+    s["dx"][k, 5] = s["dx"][k, 5] * 3 + 1
+    with pytest.raises(AssertionError):
+        bench.cell_check(s, dw, ref, act, variant, resid, to_host)
