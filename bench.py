@@ -105,7 +105,7 @@ def source_hash() -> str:
 def launch_key(cfg: dict) -> list:
     """The fields of a launch configuration that decide a kernel's traffic."""
     return [int(cfg[k]) for k in ("vector_path", "lanes_per_row", "vecs_per_lane", "wg_threads", "prefetch",
-                                  "stream_loads", "grid")]
+                                  "stream_loads", "grid")] + ([1] if cfg.get("copy_mode") else [])
 
 
 def graph_launches(nbytes: int) -> int:

@@ -96,8 +96,9 @@ typedef struct {
     int32_t wg_threads;      /* workgroup size */
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
     int32_t prefetch;        /* row blocks whose loads are issued before the current block's
-                                arithmetic (a register ring): 0 or 1; the backward also 2 for
-                                one vector per lane (vector path) */
+                                arithmetic. copy_mode 0 (a register ring): 0 or 1; the backward
+                                also 2 for one vector per lane (vector path). copy_mode 1: the
+                                LDS stages, 2 to 8 */
     int32_t stream_loads;    /* forward, rows of 64 lanes or more: 1 when the row loads carry the
                                 non-temporal hint (the ladder sets it; an explicit 0 suits inputs
                                 that are still cache-resident); ignored by the backward */
@@ -107,6 +108,16 @@ typedef struct {
                                 elems_per_access is at most 16 and covers N / 1024. The ladder
                                 takes the largest; 0 in an explicit element configuration asks
                                 for that one. 0 on the other paths */
+    int32_t copy_mode;       /* backward, vector path, one vector per lane: how the row blocks
+                                ahead arrive. 0: loaded into registers (the register ring);
+                                1: copied global->LDS by 16-byte direct-to-LDS loads into a ring
+                                of `prefetch` LDS stages ("What a tuned RMSNorm kernel actually
+                                costs on Hopper", sections 06 and 09: the copy path and the
+                                pipeline depth as search dimensions). Built for rows of 256
+                                lanes on 1024-lane workgroups (2-4 stages), 512 lanes (2, 3, 4,
+                                6, 8), 1024 lanes (2-4) and whole-wavefront rows on the
+                                workgroup (2-4); with the fused residual add 2-3 stages (512
+                                lanes: 2, 3, 4, 6). 0 on every other path */
     int64_t grid;            /* workgroups launched */
     int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid) */
     int64_t partial_stride;  /* backward: floats between consecutive partial rows */
@@ -189,7 +200,8 @@ int rmsnorm_bwd_combine(const void *workspace, int64_t partial_rows, int64_t N, 
  * Forward / backward with an explicit launch configuration instead of the
  * ladder's choice: vector_path, lanes_per_row, vecs_per_lane, wg_threads
  * (0: the default, the smallest multiple of lanes_per_row that is at least
- * 256), prefetch and grid (>= 1) are read; the other fields are derived. For searching the configuration space ("What a tuned RMSNorm
+ * 256), prefetch, copy_mode (backward only) and grid (>= 1) are read; the
+ * other fields are derived. For searching the configuration space ("What a tuned RMSNorm
  * kernel actually costs on Hopper", section 06: the memory-path knobs belong
  * in the search space). Returns RMSN_ECONFIG when the configuration does not
  * cover the row or its kernel is not built. The backward workspace must hold

@@ -131,6 +131,9 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     than 1024 * 4 16-bit or 1024 * 8 fp32 vectors) go to the scalar
 //     kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
+constexpr int kCopyLds = 1;   // rmsnorm_config::copy_mode of the LDS-staged backward kernels
+constexpr int kMaxLdsStages = 8;
+constexpr int kLdsStages = 2;  // LDS stages the ladder picks
 constexpr int kElemPath = 3;  // rmsnorm_config::vector_path of the element kernels
 constexpr int64_t kElemFwdMaxBytes = 32;  // forward element rows: bytes of row per lane (elem_lanes)
 constexpr int64_t kElemBwdMaxElems = 12, kElemBwdMaxBytes = 40;  // backward: elements and bytes per lane
@@ -331,6 +334,36 @@ void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config
         c->prefetch = M <= kShortWalk * c->grid ? 1 : 0;
 }
 
+// Backward memory path. Rows of one vector per lane from 384 to 1024 vectors
+// (at least 3/4 of 512 lanes busy) with each workgroup walking 8 to 64 rows
+// take the LDS-staged kernel: the next two row blocks copied global->LDS
+// (copy_mode 1, two stages), one workgroup per compute unit; rows of up to 512
+// vectors on 512 lanes, wider ones on their whole wavefronts (16-bit
+// activations) or on 1024 lanes (fp32 activations). Measured on MI355X against
+// the register-ring rules above (whole rmsnorm_bwd calls, graph-timed, inputs
+// rotating past the MALL; bf16 unless stated): 4096 x 4096 23.7 -> 22.6 us,
+// 16384 x 4096 69.5 -> 68.6, 16384 x 5120 89.9 -> 83.3 (640 lanes), 8192 x
+// 5120 51.9 -> 45.7, 16384 x 6144 104.8 -> 101.9, 16384 x 7168 121.8 -> 116.9
+// (896 lanes), 4096 x 8192 41.0 -> 39.5, 16384 x 3072 59.0 -> 58.2; bf16 with
+// fp32 weights 4096 x 5120 31.7 -> 27.2; fp32 4096 x 2560 28.0 -> 26.5,
+// 16384 x 4096 133.5 -> 129.7. Deeper rings (3 to 8 stages) were never
+// faster than two. Over longer walks the register ring wins (65536 x 4096:
+// 264.6 against 278.3 us), as it does for walks of 1 to 4 rows (256 x 4096:
+// 8.5 against 8.8 us) and for rows of 320 vectors (2560 bf16 columns); the
+// residual-fused backward measured within noise either way and keeps it.
+constexpr int64_t kLdsMinVecs = 384, kLdsMinWalk = 8, kLdsMaxWalk = 64;
+
+void ladder_copy(int64_t M, int64_t N, int dtype, int is_bwd, int res, int64_t cus, rmsnorm_config *c) {
+    if (!is_bwd || res || c->vector_path != 1 || cus < 1) return;
+    const int64_t nvec = N * elem_size(dtype) / 16;
+    if (nvec < kLdsMinVecs || nvec > kMaxVecLanes || M < kLdsMinWalk * cus || M > kLdsMaxWalk * cus) return;
+    const int64_t lanes = nvec <= 512 ? 512 : dtype == RMSN_F32 ? kMaxVecLanes : (nvec + 63) / 64 * 64;
+    set_vector_shape(lanes, 1, (int)lanes, kLdsStages, c);
+    c->copy_mode = kCopyLds;
+    c->grid = cus;
+    c->partial_rows = c->grid;
+}
+
 // Grid. Forward: one row block per workgroup (capped at 2^20 workgroups,
 // which then loop), except mid-size inputs of the plain call (res: the
 // residual-fused kernel), which get a prefetching grid of three per CU.
@@ -503,6 +536,12 @@ const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd
         const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
         return e ? e->fn : nullptr;
     }
+    if (is_bwd && c.copy_mode == kCopyLds) {
+        if (c.vector_path != 1 || c.vecs_per_lane != 1) return nullptr;
+        const KernelEntry *e = row_is_wg(c) ? rmsn::bwd_lds_kernel(dtype, res, 0, (int)kMaxVecLanes, c.prefetch)
+                                            : rmsn::bwd_lds_kernel(dtype, res, c.lanes_per_row, c.wg_threads, c.prefetch);
+        return e ? e->fn : nullptr;
+    }
     if (is_bwd && row_is_wg(c)) {
         const KernelEntry *e = rmsn::bwd_vec_kernel(dtype, res, 0, 1, (int)kMaxVecLanes, c.prefetch);
         return e ? e->fn : nullptr;
@@ -527,6 +566,7 @@ int resolve_uncached(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int r
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, res, cus, blocks, c);
     ladder_prefetch(M, N, dtype, is_bwd, c);
+    ladder_copy(M, N, dtype, is_bwd, res, cus, c);
     k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     *fn = k;
@@ -614,7 +654,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         const int64_t lanes = req->lanes_per_row;
         if (!elem_lanes_ok(lanes) || (req->wg_threads != 0 && req->wg_threads != lanes) ||
             !elem_group_ok(N, dtype, a, g) || k < 1 || k * g > rmsn::kElemMaxK || lanes * k * g < N ||
-            req->prefetch != 0 || req->stream_loads != 0)
+            req->prefetch != 0 || req->stream_loads != 0 || req->copy_mode != 0)
             return RMSN_ECONFIG;
         set_elem_shape(N, (int)g, (int)lanes, c);
         c->vecs_per_lane = (int32_t)k;
@@ -624,7 +664,10 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         const int64_t nvec = N * elem_size(dtype) / 16;
         if (!vector_ok(N, dtype, a)) return RMSN_ECONFIG;
         if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
-        if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > 2)
+        if (req->copy_mode < 0 || req->copy_mode > kCopyLds) return RMSN_ECONFIG;
+        const int max_pf = req->copy_mode == kCopyLds ? kMaxLdsStages : 2;
+        if (req->copy_mode == kCopyLds && (!is_bwd || req->vector_path != 1 || req->prefetch < 2)) return RMSN_ECONFIG;
+        if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > max_pf)
             return RMSN_ECONFIG;
         if (req->wg_threads > 0 && (req->wg_threads % req->lanes_per_row) != 0) return RMSN_ECONFIG;
         if (req->vector_path == kWidePath &&
@@ -633,6 +676,9 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         if (req->stream_loads < 0 || req->stream_loads > 1) return RMSN_ECONFIG;
         set_vector_shape(req->lanes_per_row, req->vecs_per_lane, req->wg_threads, req->prefetch, c);
         c->vector_path = req->vector_path;
+        c->copy_mode = req->copy_mode;
+    } else if (req->copy_mode != 0) {
+        return RMSN_ECONFIG;
     } else {
         set_scalar_shape(c);
     }
@@ -799,6 +845,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     ladder_shape(M, N, dtype, is_bwd, a, num_cus, out);
     ladder_grid(M, N, dtype, is_bwd, 0, num_cus, blocks_per_cu, out);
     ladder_prefetch(M, N, dtype, is_bwd, out);
+    ladder_copy(M, N, dtype, is_bwd, 0, num_cus, out);
     return RMSN_OK;
 }
 

@@ -1,0 +1,20 @@
+// rmsn_bwd_lds_f16w32.hip -- LDS-staged backward kernels (rmsn_bwd_lds.h) for
+// fp16 activations with fp32 weights: the plain kernels on RMSN_LDS_SHAPES and the residual-fused
+// ones on RMSN_LDS_RES_SHAPES (rmsn_instances.h), and their lookup.
+#include "rmsn_bwd_lds.h"
+#include "rmsn_instances.h"
+
+namespace rmsn {
+
+#define RMSN_ENTRY(L, W, S) {L, 1, W, S, reinterpret_cast<const void *>(&bwd_lds<f16_t, float, false, L, W, S>)},
+static const KernelEntry kLds[] = {RMSN_LDS_SHAPES(RMSN_ENTRY)};
+#undef RMSN_ENTRY
+#define RMSN_ENTRY(L, W, S) {L, 1, W, S, reinterpret_cast<const void *>(&bwd_lds<f16_t, float, true, L, W, S>)},
+static const KernelEntry kLdsResidual[] = {RMSN_LDS_RES_SHAPES(RMSN_ENTRY)};
+#undef RMSN_ENTRY
+
+const KernelEntry *bwd_lds_kernel_f16w32(int res, int lpr, int wg, int st) {
+    return res ? find_entry(kLdsResidual, lpr, 1, wg, st) : find_entry(kLds, lpr, 1, wg, st);
+}
+
+}  // namespace rmsn

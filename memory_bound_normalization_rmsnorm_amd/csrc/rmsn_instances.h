@@ -58,6 +58,17 @@
 // prefetch depth).
 #define RMSN_BWD_ROWWG_SHAPES(X) X(0, 1, 1024, 1) X(0, 1, 1024, 2)
 
+// LDS-staged backward kernels (rmsn_bwd_lds.h), as (lanes per row, workgroup,
+// stages): rows of 256 lanes on 1024-lane workgroups, rows of 512 and 1024
+// lanes, and rows on whole wavefronts sized at launch (0), each with the
+// stage counts that fit in 160 KiB of LDS (three inputs per stage with the
+// fused residual add).
+#define RMSN_LDS_SHAPES(X) X(256, 1024, 2) X(256, 1024, 3) X(256, 1024, 4)                             \
+    X(512, 512, 2) X(512, 512, 3) X(512, 512, 4) X(512, 512, 6) X(512, 512, 8)                          \
+    X(1024, 1024, 2) X(1024, 1024, 3) X(1024, 1024, 4) X(0, 1024, 2) X(0, 1024, 3) X(0, 1024, 4)
+#define RMSN_LDS_RES_SHAPES(X) X(256, 1024, 2) X(256, 1024, 3) X(512, 512, 2) X(512, 512, 3)            \
+    X(512, 512, 4) X(512, 512, 6) X(1024, 1024, 2) X(1024, 1024, 3) X(0, 1024, 2) X(0, 1024, 3)
+
 namespace rmsn {
 
 template <int N>

@@ -59,6 +59,10 @@ const KernelEntry *fwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, 
 const KernelEntry *bwd_vec_kernel(int dtype, int res, int lpr, int vpt, int wg, int pf);
 // wide-row backward kernels (lanes per row and workgroup kWideLanes)
 const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf);
+// LDS-staged backward kernels (one vector per lane): rows of `lpr` lanes (0:
+// the whole workgroup, sized at launch) on `wg`-lane workgroups, `st` row
+// blocks in flight; KernelEntry::pf holds st
+const KernelEntry *bwd_lds_kernel(int dtype, int res, int lpr, int wg, int st);
 // lds: the backward kernel that keeps its dW sums in LDS (rows of at most kScalarLdsCols columns)
 const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
 // element kernels: rows of `lanes` lanes (64, 128, 256, 512 or 1024), k

@@ -2,8 +2,10 @@
 
 The library's default configuration comes from an analytical ladder on the
 row width (``rmsnorm_select_config``). This module searches the space the
-ladder chooses from -- lanes per row, workgroup size, register prefetch,
-grid and (forward) non-temporal row loads -- by timing each candidate through ``rmsnorm_{fwd,bwd}_with_config``.
+ladder chooses from -- lanes per row, workgroup size, grid, (forward)
+non-temporal row loads, and the backward's memory path: register prefetch of
+0-2 row blocks, or global->LDS copies into 2-8 LDS stages (copy_mode) -- by
+timing each candidate through ``rmsnorm_{fwd,bwd}_with_config``.
 It keeps the winner per (device, compute units, M, N, dtype, direction,
 library build).
 
@@ -47,6 +49,9 @@ MAX_VPT = 8
 WIDE_LANES = 1024  # wide-row backward kernels (vector_path 2): 1024 lanes, dW sums in LDS
 ELEM_LANES, ELEM_MAX = (64, 128, 256, 512, 1024), 16  # element kernels (vector_path 3): lanes, elements per lane
 ROWWG_MIN_VECS = 256  # backward rows wider than this may run on any whole number of wavefronts
+# LDS-staged backward kernels (copy_mode 1): (lanes per row, workgroup) -> stage counts built; lanes 0 is
+# the row on the whole workgroup (see csrc/rmsn_instances.h)
+LDS_BUILT = {(256, 1024): (2, 3, 4), (512, 512): (2, 3, 4, 6, 8), (1024, 1024): (2, 3, 4), (0, 1024): (2, 3, 4)}
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
 
@@ -116,6 +121,22 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             for g in sorted({k * num_cus for k in (1, 2, 3)} & set(range(1, M + 1))):
                 out.append(rmsnorm_config(vector_path=1, lanes_per_row=rowwg, vecs_per_lane=1, wg_threads=rowwg,
                                           prefetch=pf, grid=g))
+    # the LDS-staged backward: rows of one vector per lane, every built stage
+    # count, one and two workgroups per compute unit
+    if is_bwd and 256 <= nvec <= WIDE_LANES:
+        lanes = 1 << (nvec - 1).bit_length()
+        shapes = []
+        if (lanes, 1024 if lanes == 256 else lanes) in LDS_BUILT and nvec > lanes // 2:
+            shapes.append((lanes, 1024 if lanes == 256 else lanes, LDS_BUILT[(lanes, 1024 if lanes == 256 else lanes)]))
+        if rowwg & (rowwg - 1):
+            shapes.append((rowwg, rowwg, LDS_BUILT[(0, 1024)]))
+        for lpr, wg, stages in shapes:
+            rpw = wg // lpr
+            row_blocks = -(-M // rpw)
+            for st in stages:
+                for g in sorted({k * num_cus for k in (1, 2)} & set(range(1, row_blocks + 1))) or [row_blocks]:
+                    out.append(rmsnorm_config(vector_path=1, lanes_per_row=lpr, vecs_per_lane=1, wg_threads=wg,
+                                              prefetch=st, copy_mode=1, grid=g))
     wide_max = 8 if dtype == F32 else 4
     if is_bwd and WIDE_LANES < nvec <= WIDE_LANES * wide_max:
         vpt = -(-nvec // WIDE_LANES)
@@ -130,7 +151,7 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
 
 def _key(c: rmsnorm_config):
     return (c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch, c.grid, c.stream_loads,
-            c.elems_per_access)
+            c.elems_per_access, c.copy_mode)
 
 
 class _Bench:

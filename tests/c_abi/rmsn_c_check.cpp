@@ -11,8 +11,12 @@
 //   y, dx bf16: |g-o| <= 2^-7 * (|o| + 0.01 * that row rms)
 //   rstd:       |g-o| <= 1e-5 * o;   dW: |g-o| <= tol * max(|o|, floor * rms(dW))
 // Prints "ok" and exits 0 when every check passes, nonzero otherwise.
+// With --host-timing it instead reports the host time per call of the entry
+// points at decode-sized shapes (M = 1, 2, 4 rows of 4096 bf16 columns).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -199,9 +203,80 @@ bool run_case(int64_t M, int64_t N, bool bf16, uint64_t seed) {
     return g_failures == before;
 }
 
+// Host time per call (no Python in the process): batches of kBatch calls are
+// issued back to back and timed on the host clock around the issuing only;
+// the stream is drained between batches (untimed) so the launch queue never
+// fills and blocks the caller. Reported: the median over batches of the time
+// per call, for rmsnorm_bwd (argument checks, the cached configuration and
+// workspace lookups, one or two launches), rmsnorm_fwd, and, for scale,
+// rmsnorm_bwd_combine (argument checks and a single launch, no lookup).
+bool host_timing() {
+    constexpr int kBatch = 200, kBatches = 25;
+    const int64_t N = 4096;
+    uint16_t *x, *dy, *dx, *w, *y;
+    float *rstd, *dw;
+    void *ws;
+    const size_t elems = 4 * N;
+    HIP_OK(hipMalloc(&x, elems * 2));
+    HIP_OK(hipMalloc(&dy, elems * 2));
+    HIP_OK(hipMalloc(&dx, elems * 2));
+    HIP_OK(hipMalloc(&y, elems * 2));
+    HIP_OK(hipMalloc(&w, N * 2));
+    HIP_OK(hipMalloc(&rstd, 4 * sizeof(float)));
+    HIP_OK(hipMalloc(&dw, N * sizeof(float)));
+    HIP_OK(hipMemset(x, 0x3f, elems * 2));
+    HIP_OK(hipMemset(dy, 0x3c, elems * 2));
+    HIP_OK(hipMemset(w, 0x3f, N * 2));
+    const size_t ws_bytes = 64u << 20;
+    HIP_OK(hipMalloc(&ws, ws_bytes));
+    hipStream_t s;
+    HIP_OK(hipStreamCreate(&s));
+    auto time_calls = [&](const char *what, int64_t M, auto &&call) -> bool {
+        std::vector<double> per;
+        for (int b = 0; b < kBatches + 2; ++b) {
+            const auto t0 = std::chrono::steady_clock::now();
+            for (int i = 0; i < kBatch; ++i)
+                if (call(M) != RMSN_OK) {
+                    std::printf("FAIL %s returned an error\n", what);
+                    return false;
+                }
+            const auto t1 = std::chrono::steady_clock::now();
+            if (hipStreamSynchronize(s) != hipSuccess) return false;
+            if (b >= 2) per.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count() / kBatch);
+        }
+        std::sort(per.begin(), per.end());
+        std::printf("host time per call: %s M=%lld N=%lld bf16: median %.2f us (min %.2f, max %.2f) over %d x %d calls\n",
+                    what, (long long)M, (long long)N, per[per.size() / 2], per.front(), per.back(), kBatches, kBatch);
+        return true;
+    };
+    bool ok = true;
+    for (int64_t M : {1, 2, 4}) {
+        ok &= time_calls("rmsnorm_bwd", M, [&](int64_t m) {
+            return rmsnorm_bwd(x, w, dy, rstd, m, N, RMSN_BF16, dx, dw, ws, ws_bytes, s);
+        });
+        ok &= time_calls("rmsnorm_fwd", M, [&](int64_t m) {
+            return rmsnorm_fwd(x, w, 1e-6f, m, N, RMSN_BF16, y, rstd, s);
+        });
+    }
+    ok &= time_calls("rmsnorm_bwd_combine", 1, [&](int64_t) { return rmsnorm_bwd_combine(ws, 1, N, dw, s); });
+    for (void *p : {(void *)x, (void *)dy, (void *)dx, (void *)y, (void *)w, (void *)rstd, (void *)dw, ws}) (void)hipFree(p);
+    (void)hipStreamDestroy(s);
+    return ok;
+}
+
 }  // namespace
 
-int main() {
+int main(int argc, char **argv) {
+    if (argc > 1 && std::strcmp(argv[1], "--host-timing") == 0) {
+        int dev = 0;
+        if (hipGetDeviceCount(&dev) != hipSuccess || dev < 1) {
+            std::printf("FAIL no HIP device\n");
+            return 2;
+        }
+        const bool ok = host_timing();
+        std::printf("%s\n", ok ? "ok" : "FAILED");
+        return ok ? 0 : 1;
+    }
     int dev = 0;
     if (hipGetDeviceCount(&dev) != hipSuccess || dev < 1) {
         std::printf("FAIL no HIP device\n");

@@ -143,6 +143,35 @@ def _fail(what, err, bound, g, o):
             f"gpu={g[idx]!r} oracle={o[idx]!r} err={err[idx]:.3e} bound={bound[idx]:.3e}")
 
 
+def oracle_row_blocks(x, w, dy, eps, dtype, block=2048, threads=None, wdtype=None):
+    """The oracle's y, r and dx over every row, in consecutive blocks of
+    `block` rows (so an 8192-column workload never holds more than a block of
+    fp64 rows): yields (row slice, y, r, dx) per block. Each block's rows are
+    split over `threads` threads (the oracle's C code releases the GIL); the
+    values are the oracle's, row by row, whatever the split."""
+    import concurrent.futures
+    import os
+
+    import oracle
+
+    M = x.shape[0]
+    T = threads or max(1, min(16, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=T) as ex:
+        for lo in range(0, M, block):
+            hi = min(M, lo + block)
+            cuts = [lo + (hi - lo) * t // T for t in range(T + 1)]
+            parts = [np.arange(cuts[t], cuts[t + 1], dtype=np.int64) for t in range(T) if cuts[t + 1] > cuts[t]]
+
+            def one(rows):
+                oy, orr = oracle.fwd(x, w, eps, dtype, rows=rows, wdtype=wdtype)
+                odx, _ = oracle.bwd_dx(x, w, dy, eps, dtype, rows=rows, wdtype=wdtype)
+                return oy, orr, odx
+
+            res = list(ex.map(one, parts))
+            yield (slice(lo, hi), np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]),
+                   np.concatenate([r[2] for r in res]))
+
+
 def term_rms(x, w, dy, r, dtype, rows=None, dh=None) -> np.ndarray:
     """Per-row rms of the terms dx adds up: r_i * dy_ij * w_j, and dh when the
     residual gradient is added (fp64, from the inputs and the oracle's r)."""

@@ -163,19 +163,22 @@ def test_ladder_backward_grid_and_prefetch():
     assert cfg(1024, 2048, rn.BF16, 1)["grid"] == 256
     # below one row block per CU: the row blocks
     assert cfg(100, 4096, rn.BF16, 1)["grid"] == 100
-    # deep prefetch: 512 lanes (4096 columns), 1024 lanes (8192, 7168 columns), fp32 4096
-    for M, N, dt, lpr in ((4096, 4096, rn.BF16, 512), (16384, 4096, rn.BF16, 512), (16384, 8192, rn.BF16, 1024),
-                          (4096, 7168, rn.BF16, 1024), (16384, 4096, rn.F32, 1024)):
+    # deep prefetch (register ring, walks outside the LDS path's 8 to 64 rows):
+    # 512 lanes (4096 columns), 1024 lanes (8192, 7168 columns), fp32 4096
+    for M, N, dt, lpr in ((1024, 4096, rn.BF16, 512), (65536, 4096, rn.BF16, 512), (65536, 8192, rn.BF16, 1024),
+                          (1024, 7168, rn.BF16, 1024), (65536, 4096, rn.F32, 1024)):
         c = cfg(M, N, dt, 1)
-        assert (c["lanes_per_row"], c["vecs_per_lane"], c["prefetch"], c["grid"]) == (lpr, 1, 2, 256), (M, N)
-    # 5120 columns: 640 whole-wavefront lanes over short walks (4096 rows), else
-    # 1024 lanes (5/8 busy) under the short-walk rule (16384 rows: no prefetch)
-    a, b = cfg(4096, 5120, rn.BF16, 1), cfg(16384, 5120, rn.BF16, 1)
+        assert (c["lanes_per_row"], c["vecs_per_lane"], c["prefetch"], c["grid"], c["copy_mode"]) == \
+            (lpr, 1, 2, 256, 0), (M, N)
+    # 5120 columns: 640 whole-wavefront lanes over short walks (1536 rows), else
+    # 1024 lanes (5/8 busy) under the short-walk rule (65536 rows: no prefetch)
+    a, b = cfg(1536, 5120, rn.BF16, 1), cfg(65536, 5120, rn.BF16, 1)
     assert (a["lanes_per_row"], a["wg_threads"], a["grid"], a["prefetch"]) == (640, 640, 256, 2)
     assert (b["lanes_per_row"], b["grid"], b["prefetch"]) == (1024, 512, 0)
-    # fp32 weights keep the power-of-two row: 4096 rows over 512 prefetch one block
-    c = cfg(4096, 5120, rn.BF16_WF32, 1)
-    assert (c["lanes_per_row"], c["grid"], c["prefetch"]) == (1024, 512, 1)
+    # fp32 weights keep the power-of-two row: 1536 rows over 256 (the partial
+    # cap) prefetch one block
+    c = cfg(1536, 5120, rn.BF16_WF32, 1)
+    assert (c["lanes_per_row"], c["grid"], c["prefetch"]) == (1024, 256, 1)
     # fp32, two vectors per lane: the short-walk rule; 3 or more never prefetch
     assert cfg(4096, 8192, rn.F32, 1)["prefetch"] == 1
     assert cfg(4096, 12288, rn.F32, 1)["prefetch"] == 0
@@ -271,7 +274,7 @@ def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
     (2560, rn.BF16, 0, 128, 3),    # 320 vectors: 64 lanes x 5 measured a tie; kept
     (5120, rn.BF16, 1, 640, 1),    # whole wavefronts (4096 rows: a short walk)
     (7168, rn.BF16, 0, 256, 4),
-    (7168, rn.BF16, 1, 1024, 1),
+    (7168, rn.BF16, 1, 896, 1),    # 896 vectors, 4096 rows: the LDS-staged row on whole wavefronts
     (8192, rn.BF16, 0, 256, 4),
     (8192, rn.BF16, 1, 1024, 1),
     (32768, rn.BF16, 0, 1024, 4),
@@ -286,6 +289,9 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (c["lanes_per_row"], c["vecs_per_lane"]) == (lpr, vpt)
     # backward rows of 64 to 256 lanes share 1024-lane workgroups
     assert c["wg_threads"] == (1024 if is_bwd and 64 <= lpr <= 256 else max(lpr, 256))
+    # the LDS-staged backward for rows of 384 to 1024 vectors (4096 rows: a walk of 16)
+    nv = N * (4 if dtype == rn.F32 else 2) // 16
+    assert c["copy_mode"] == (1 if is_bwd and 384 <= nv <= 1024 else 0)
     # the forward streams rows of a wavefront or more with non-temporal loads
     # (4096 rows: every input here exceeds the 4 MiB threshold but N = 8, 24)
     big = 4096 * N * (4 if dtype == rn.F32 else 2) >= 4 << 20
@@ -438,24 +444,62 @@ def test_binding_tensor_checks_logic():
 
 @pytest.mark.parametrize("N,M,dtype,lanes,grid", [
     (2560, 16384, rn.BF16, 320, 512),     # 320 vectors: whole wavefronts, two per CU
-    (3072, 16384, rn.F16, 384, 512),
-    (3584, 16384, rn.BF16, 512, 256),     # 448: the 512-lane row (deep prefetch) is kept
-    (4608, 4096, rn.BF16, 576, 256),      # 576-640: whole wavefronts on short walks only
-    (4608, 16384, rn.BF16, 1024, 512),
+    (3072, 65536, rn.F16, 384, 512),
+    (3584, 65536, rn.BF16, 512, 256),     # 448: the 512-lane row (deep prefetch) is kept
+    (4608, 1536, rn.BF16, 576, 256),      # 576-640: whole wavefronts on short walks only
+    (4608, 65536, rn.BF16, 1024, 512),
     (6144, 65536, rn.BF16, 768, 256),     # 704-768: whole wavefronts, one per CU
     (5632, 65536, rn.F16, 704, 256),
-    (7168, 16384, rn.BF16, 1024, 256),    # 832-960: the 1024-lane row is kept
-    (2560, 16384, rn.F32, 1024, 512),     # fp32 keeps the power-of-two row
+    (7168, 65536, rn.BF16, 1024, 256),    # 832-960: the 1024-lane row is kept
+    (2560, 65536, rn.F32, 1024, 512),     # fp32 keeps the power-of-two row
     (2560, 16384, rn.F16_WF32, 512, 512),
 ])
 def test_ladder_whole_wavefront_rows(N, M, dtype, lanes, grid):
     """Backward rows of 257 to 1023 16-bit vectors run on whole wavefronts
     (a workgroup-sized row, depth-2 prefetch) where that measured faster than
-    the next power of two; elsewhere the power-of-two row is kept."""
+    the next power of two; elsewhere the power-of-two row is kept. (Register
+    ring; walks of 8 to 64 rows of 384 vectors or more take the LDS path.)"""
     c = cfg(M, N, dtype, 1)
+    assert c["copy_mode"] == 0
     assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["grid"]) == (1, lanes, 1, grid)
     if lanes & (lanes - 1):
         assert (c["wg_threads"], c["rows_per_wg"], c["prefetch"]) == (lanes, 1, 2)
+
+
+@pytest.mark.parametrize("M,N,dtype,lanes", [
+    (16384, 4096, rn.BF16, 512),          # the headline workload: a walk of 64
+    (2048, 4096, rn.BF16, 512),           # a walk of 8
+    (4096, 3072, rn.F16, 512),            # 384 vectors: 3/4 of 512 lanes
+    (16384, 5120, rn.BF16, 640),          # whole wavefronts (16-bit activations)
+    (8192, 6144, rn.F16, 768),
+    (16384, 7168, rn.BF16, 896),
+    (4096, 5120, rn.BF16_WF32, 640),
+    (4096, 8192, rn.BF16, 1024),
+    (4096, 2560, rn.F32, 1024),           # fp32: the power-of-two row
+    (16384, 4096, rn.F32, 1024),
+    (4096, 2048, rn.F32, 512),
+])
+def test_ladder_lds_path(M, N, dtype, lanes):
+    """Backward rows of 384 to 1024 vectors over walks of 8 to 64 rows per
+    workgroup take the LDS-staged kernel: two stages, one workgroup per CU."""
+    c = cfg(M, N, dtype, 1)
+    assert (c["copy_mode"], c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"],
+            c["rows_per_wg"], c["prefetch"], c["grid"], c["partial_rows"]) == (1, 1, lanes, 1, lanes, 1, 2, 256, 256)
+
+
+@pytest.mark.parametrize("M,N,dtype", [
+    (1792, 4096, rn.BF16),                # a walk of 7
+    (16385, 4096, rn.BF16),               # a walk of 65
+    (16384, 2560, rn.BF16),               # 320 vectors
+    (16384, 2048, rn.BF16),               # 256 vectors
+    (4096, 16384, rn.BF16),               # 2048 vectors: the wide-row kernel
+    (16384, 4100, rn.BF16),               # not a multiple of 16 bytes: the element kernels
+])
+def test_ladder_lds_path_boundaries(M, N, dtype):
+    c = cfg(M, N, dtype, 1)
+    assert c["copy_mode"] == 0
+    assert cfg(M, N, dtype, 0)["copy_mode"] == 0   # never the forward
+    assert cfg(16384, 4096, rn.BF16, 1, aligned=0)["copy_mode"] == 0   # unaligned pointers: element kernels
 
 
 def test_explicit_whole_wavefront_config_checks():
@@ -561,3 +605,33 @@ def test_explicit_element_config_checks():
     assert bwd(14000, vecs_per_lane=13) == rn.ECONFIG                # 13312 elements do not cover 14000
     assert bwd_res(4100, vecs_per_lane=5, stream_loads=1) == rn.ECONFIG
     assert bwd_res(4100, vecs_per_lane=5, lanes_per_row=256) == rn.ECONFIG
+
+
+def test_lds_copy_mode_configurations():
+    """Explicit configurations with copy_mode 1 (the LDS-staged backward):
+    built shapes get past every check to the launch (which fails here, with
+    no GPU); unbuilt stage counts, depths outside 2..8, several vectors per
+    lane, other paths and the forward are refused before any HIP call."""
+    import ctypes
+
+    def rc(dt, N, is_bwd=1, **kw):
+        d = dict(vector_path=1, lanes_per_row=256, vecs_per_lane=1, wg_threads=1024, prefetch=2, copy_mode=1,
+                 grid=3)
+        d.update(kw)
+        c = rn.rmsnorm_config(**d)
+        if is_bwd:
+            return rn.lib.rmsnorm_bwd_with_config(FAKE, FAKE, FAKE, FAKE, 63, N, dt, FAKE, FAKE, FAKE, 1 << 30,
+                                                  ctypes.byref(c), None)
+        return rn.lib.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-6, 63, N, dt, FAKE, FAKE, ctypes.byref(c), None)
+
+    for dt, N, kw in ((rn.F32, 524, {}), (rn.BF16, 2128, dict(lanes_per_row=512, wg_threads=512, prefetch=8)),
+                      (rn.BF16_WF32, 5120, dict(lanes_per_row=640, wg_threads=640, prefetch=3)),
+                      (rn.F16, 8192, dict(lanes_per_row=1024, wg_threads=1024, prefetch=4))):
+        assert rc(dt, N, **kw) == rn.EHIP, (dt, N, kw)  # valid: reaches the launch
+    bad = [dict(lanes_per_row=512, wg_threads=512, prefetch=5), dict(lanes_per_row=512, wg_threads=512, prefetch=1),
+           dict(lanes_per_row=512, wg_threads=512, prefetch=9), dict(lanes_per_row=256, vecs_per_lane=2),
+           dict(lanes_per_row=512, wg_threads=1024, prefetch=4), dict(copy_mode=2), dict(copy_mode=-1),
+           dict(vector_path=2, lanes_per_row=1024, wg_threads=1024), dict(vector_path=0)]
+    for kw in bad:
+        assert rc(rn.BF16, 2128, **kw) == rn.ECONFIG, kw
+    assert rc(rn.BF16, 4096, is_bwd=0, lanes_per_row=128, vecs_per_lane=4, wg_threads=256) == rn.ECONFIG

@@ -56,8 +56,24 @@ def test_candidates_include_whole_wavefront_backward_rows():
     """Backward rows of 257-1023 vectors whose whole wavefronts are not a power
     of two: the workgroup-sized row kernels, at both prefetch depths."""
     cands = tune.candidates(16384, 5120, rn.BF16, 1, 256)
-    rowwg = {(c.lanes_per_row, c.wg_threads, c.prefetch) for c in cands if c.lanes_per_row == 640}
+    rowwg = {(c.lanes_per_row, c.wg_threads, c.prefetch) for c in cands if c.lanes_per_row == 640 and not c.copy_mode}
     assert rowwg == {(640, 640, 1), (640, 640, 2)}
+
+
+def test_candidates_include_the_lds_pipeline():
+    """The backward's memory path is a search dimension: LDS-staged
+    configurations (copy_mode 1) at every built stage count, for power-of-two
+    rows and for rows on whole wavefronts, at one and two workgroups per CU;
+    none for the forward or for rows of more than one vector per lane."""
+    def lds(M, N, dt=rn.BF16, is_bwd=1):
+        return {(c.lanes_per_row, c.wg_threads, c.prefetch, c.grid)
+                for c in tune.candidates(M, N, dt, is_bwd, 256) if c.copy_mode == 1}
+    assert lds(16384, 4096) == {(512, 512, s, g) for s in (2, 3, 4, 6, 8) for g in (256, 512)}
+    assert {(l, s) for l, _, s, _ in lds(16384, 5120)} == {(l, s) for l in (640, 1024) for s in (2, 3, 4)}
+    assert {(l, w) for l, w, _, _ in lds(16384, 2048)} == {(256, 1024)}
+    assert lds(16384, 4096, is_bwd=0) == set()
+    assert lds(4096, 32768) == set()           # 4096 vectors: the wide-row kernels
+    assert lds(4096, 1024) == set()            # 128 vectors
     assert not [c for c in tune.candidates(16384, 5120, rn.BF16, 0, 256) if c.lanes_per_row == 640]  # forward
     assert not [c for c in tune.candidates(16384, 4096, rn.BF16, 1, 256) if c.lanes_per_row % 64 == 0 and
                 c.lanes_per_row & (c.lanes_per_row - 1)]                                           # 512: a power of two
