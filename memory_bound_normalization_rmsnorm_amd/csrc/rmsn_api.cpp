@@ -533,7 +533,10 @@ const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
     if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access, c.lanes_per_row);
     if (c.vector_path == kWidePath) {
-        const KernelEntry *e = is_bwd ? rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch) : nullptr;
+        const KernelEntry *e = !is_bwd ? nullptr
+                               : c.copy_mode == kCopyLds
+                                   ? (res ? nullptr : rmsn::bwd_wide_lds_kernel(dtype, c.lanes_per_row, c.vecs_per_lane, c.prefetch))
+                                   : rmsn::bwd_wide_kernel(dtype, res, c.vecs_per_lane, c.prefetch);
         return e ? e->fn : nullptr;
     }
     if (is_bwd && c.copy_mode == kCopyLds) {
@@ -666,12 +669,17 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         if ((int64_t)req->lanes_per_row * req->vecs_per_lane < nvec) return RMSN_ECONFIG;
         if (req->copy_mode < 0 || req->copy_mode > kCopyLds) return RMSN_ECONFIG;
         const int max_pf = req->copy_mode == kCopyLds ? kMaxLdsStages : 2;
-        if (req->copy_mode == kCopyLds && (!is_bwd || req->vector_path != 1 || req->prefetch < 2)) return RMSN_ECONFIG;
+        // the LDS stages: at least two for rows of one vector per lane, one for wide rows
+        if (req->copy_mode == kCopyLds &&
+            (!is_bwd || req->prefetch < (req->vector_path == 1 ? 2 : req->vector_path == kWidePath ? 1 : 99)))
+            return RMSN_ECONFIG;
         if (req->lanes_per_row < 1 || req->wg_threads < 0 || req->prefetch < 0 || req->prefetch > max_pf)
             return RMSN_ECONFIG;
         if (req->wg_threads > 0 && (req->wg_threads % req->lanes_per_row) != 0) return RMSN_ECONFIG;
+        // wide rows: 1024 lanes, or 512 for the LDS-staged kernels; the workgroup is the row
+        const int wide_lanes = req->lanes_per_row == 512 && req->copy_mode == kCopyLds ? 512 : rmsn::kWideLanes;
         if (req->vector_path == kWidePath &&
-            (req->lanes_per_row != rmsn::kWideLanes || (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes)))
+            (req->lanes_per_row != wide_lanes || (req->wg_threads != 0 && req->wg_threads != wide_lanes)))
             return RMSN_ECONFIG;
         if (req->stream_loads < 0 || req->stream_loads > 1) return RMSN_ECONFIG;
         set_vector_shape(req->lanes_per_row, req->vecs_per_lane, req->wg_threads, req->prefetch, c);

@@ -60,17 +60,17 @@ constexpr int kLdsRstdSlots = 64;
 // and kLdsRstdSlots rstd floats per wavefront.
 constexpr int lds_ring_bytes(int st, int nin, int wg) { return st * (nin * wg * 16 + (wg / 64) * kLdsRstdSlots * 4); }
 
-// s_waitcnt vmcnt(BASE + m) for the runtime m in [0, M] (m is wave-uniform).
-template <int BASE, int M>
+// s_waitcnt vmcnt(BASE + m * Q) for the runtime m in [0, M] (m is wave-uniform).
+template <int BASE, int M, int Q = 1>
 __device__ __forceinline__ void wait_vm(int m) {
     if constexpr (M == 0) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(BASE) : "memory");
     } else {
         if (m >= M) {
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(BASE + M) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(BASE + M * Q) : "memory");
             return;
         }
-        wait_vm<BASE, M - 1>(m);
+        wait_vm<BASE, M - 1, Q>(m);
     }
 }
 
@@ -336,6 +336,204 @@ bwd_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
 #pragma unroll
                 for (int g = 1; g < RPW; ++g) t += comb[g * kSlotCols + q];
                 prow[q] = t;
+            }
+        }
+    }
+}
+
+}  // namespace rmsn
+
+namespace rmsn {
+
+// Wide rows (more than 1024 16-byte vectors: VPT per lane on LPR = 512 or
+// 1024 lanes), one row per workgroup at a time, with the next row(s) staged
+// through LDS. bwd_wide keeps each lane's dW sums in LDS and re-reads weights
+// from cache, because the register file holds the row and its prefetched
+// successor. Here the successor lands in LDS instead (ST stages of a whole
+// row of x and dy: 128 KiB at 32768 16-bit columns, so one stage; two at
+// 16384), which leaves the registers for the dW sums (VPT x 8 floats), and
+// for the weights when the lane's register budget allows (512 registers per
+// SIMD lane shared by LPR / 256 wavefronts: 128 each at 1024 lanes, 256 at
+// 512 lanes; re-read from cache otherwise). Ordering as in bwd_lds: each lane
+// reads back only its own slots and waits for its own copies; with Q = VPT dx
+// stores per row the wait before row j is vmcnt((ST - 1) * L + min(j, ST) * Q).
+template <typename T, typename TW, int LPR, int VPT>
+constexpr bool wide_lds_keeps_w() {
+    // weight vectors per lane that fit beside the row and the dW sums without
+    // spilling (the build's resource report): 2 at 1024 lanes, 6 at 512
+    return VPT * WeightVec<T, TW>::kVecs <= (LPR == 1024 ? 2 : 6);
+}
+
+template <typename T, typename TW, int LPR, int VPT, int ST>
+__global__ void __launch_bounds__(LPR) __attribute__((amdgpu_waves_per_eu(LPR / 256)))
+bwd_wide_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy,
+             const T *__restrict__ dh, const float *__restrict__ rstd, T *__restrict__ dx,
+             float *__restrict__ partial, int64_t ldp, int64_t M, int32_t N, int32_t nvec) {
+    using E = Elem<T>;
+    using WV = WeightVec<T, TW>;
+    constexpr int EPV = E::kPerVec;
+    constexpr int kWaves = LPR / 64;
+    constexpr int L = 2 * VPT + 1;  // copies per stage and lane: x and dy vectors, rstd
+    constexpr int Q = VPT;          // dx stores per row and lane
+    constexpr bool kKeepW = wide_lds_keeps_w<T, TW, LPR, VPT>();
+    constexpr int kVecBytes = LPR * 16;  // bytes between consecutive vector slots of a stage
+    static_assert(LPR == 512 || LPR == 1024, "512 or 1024 lanes");
+    static_assert(ST >= 1 && (ST - 1) * L + ST * Q <= 63, "vmcnt range");
+    static_assert(ST * 2 * VPT * kVecBytes + ST * kWaves * kLdsRstdSlots * 4 + 2 * kWaves * 4 <= 160 * 1024, "LDS");
+    // stage s, input t (0 x, 1 dy), vector v: ring[((s * 2 + t) * VPT + v) * LPR + lane]
+    __shared__ __attribute__((aligned(16))) u32x4 ring[ST * 2 * VPT * LPR];
+    // the rstd copy of wavefront w for stage s: rst[(s * kWaves + w) * kLdsRstdSlots + lane] (lane 0: the row's)
+    __shared__ float rst[ST * kWaves * kLdsRstdSlots];
+    __shared__ float slots[2 * kWaves];
+
+    const int lane = threadIdx.x;
+    const int wave = lane >> 6;
+    const float n = (float)N;
+    const uint32_t row_bytes = (uint32_t)nvec * 16u;
+    const Buf wb(w, row_bytes * WV::kVecs);
+    uint32_t off[VPT];
+    bool vin[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int idx = v * LPR + lane;
+        vin[v] = idx < nvec;
+        off[v] = vin[v] ? (uint32_t)idx * 16u : kOff;
+    }
+    // weights of vector slot v: kept registers, or a (cached) reload
+    WV wv[kKeepW ? VPT : 1];
+    if constexpr (kKeepW) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) wv[v].load(wb, v * LPR + lane, vin[v]);
+    }
+    auto weights = [&](int v, float (&fw)[EPV]) {
+        if constexpr (kKeepW) {
+            wv[v].unpack(fw);
+        } else {
+            WV t;
+            t.load(wb, v * LPR + lane, vin[v]);
+            t.unpack(fw);
+        }
+    };
+    float acc[VPT][EPV];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) acc[v][k] = 0.f;
+
+    const int64_t step = (int64_t)gridDim.x;
+    int64_t row = (int64_t)blockIdx.x;
+    // copies of row b into stage s (rows past M: record count 0, read as nothing)
+    auto issue = [&](int64_t b, int s) {
+        const int64_t bb = b < M ? b : 0;
+        const uint32_t bytes = b < M ? row_bytes : 0u;
+        const __amdgpu_buffer_rsrc_t xr = Buf(x + bb * N, bytes).r;
+        const __amdgpu_buffer_rsrc_t gr = Buf(dy + bb * N, bytes).r;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            u32x4 *sx = ring + ((s * 2 + 0) * VPT + v) * LPR + wave * 64;
+            u32x4 *sg = ring + ((s * 2 + 1) * VPT + v) * LPR + wave * 64;
+            // (an array element passed straight to the builtin makes clang drop
+            // the kernel's host-side stub without a diagnostic)
+            const uint32_t ov = off[v];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)sx, 16, ov, 0, 0, RMSN_BWD_LOAD_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void *)sg, 16, ov, 0, 0, RMSN_BWD_LOAD_AUX);
+        }
+        const __amdgpu_buffer_rsrc_t rr = Buf(rstd + bb, b < M ? 4u : 0u).r;
+        // every lane copies (lanes past the first read past the record count)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(rst + (s * kWaves + wave) * kLdsRstdSlots), 4,
+                                                 (uint32_t)(lane & 63) * 4u, 0, 0, 0);
+        asm volatile("" ::: "memory");
+    };
+    // The kept weights are waited for before the prologue (a plain register
+    // load; waited for later, the compiler's wait would drain the ring).
+    if constexpr (kKeepW) {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) wv[v].keep();
+    }
+    for (int s = 0; s < ST; ++s) issue(row + (int64_t)s * step, s);
+
+    int parity = 0, s = 0, m = 0;
+    for (; row < M; row += step) {
+        wait_vm<(ST - 1) * L, ST, Q>(m);
+        u32x4 xv[VPT], gv[VPT];
+        float r;
+        {
+            const uint32_t ax = lds_off(ring + (s * 2 * VPT) * LPR + lane);
+            const uint32_t ag = lds_off(ring + ((s * 2 + 1) * VPT) * LPR + lane);
+            // Each statement waits for its own reads: the compiler takes an asm
+            // output as ready when the statement ends, and may copy it from
+            // then on. (An asm immediate must be a constant expression, and v is
+            // a loop index, so the addresses are computed.)
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(xv[v]), "=&v"(gv[v])
+                             : "v"(ax + (uint32_t)(v * kVecBytes)), "v"(ag + (uint32_t)(v * kVecBytes))
+                             : "memory");
+            }
+            const uint32_t ar = lds_off(rst + (s * kWaves + wave) * kLdsRstdSlots);
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(ar) : "memory");
+        }
+        issue(row + (int64_t)ST * step, s);
+        s = s + 1 == ST ? 0 : s + 1;
+        m = m < ST ? m + 1 : ST;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            if (!vin[v]) {
+                xv[v] = z;
+                gv[v] = z;
+            }
+        }
+
+        float sacc = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float fx[EPV], fg[EPV], fw[EPV];
+            E::unpack(xv[v], fx);
+            E::unpack(gv[v], fg);
+            weights(v, fw);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                sacc = __builtin_fmaf(fg[k] * fw[k], fx[k], sacc);
+                acc[v][k] = __builtin_fmaf(fg[k] * fx[k], r, acc[v][k]);
+            }
+        }
+        sacc = row_sum_nf<LPR, LPR>(sacc, slots, parity);
+        parity ^= 1;
+        const float c = r * (r * (r * (sacc / n)));
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            keep_packed(xv[v]);
+            keep_packed(gv[v]);
+            if constexpr (kKeepW) wv[v].keep();
+        }
+        const Buf db(dx + row * N, row_bytes);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            float fx[EPV], fg[EPV], fw[EPV], o[EPV];
+            E::unpack(xv[v], fx);
+            E::unpack(gv[v], fg);
+            weights(v, fw);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) o[k] = __builtin_fmaf(-fx[k], c, r * (fg[k] * fw[k]));
+            db.store16<RMSN_BWD_STORE_AUX>(off[v], E::pack(o));
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    const Buf pb(partial + (int64_t)blockIdx.x * ldp, (uint32_t)nvec * (uint32_t)(EPV * 4));
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        if (vin[v]) {
+#pragma unroll
+            for (int q = 0; q < EPV / 4; ++q) {
+                u32x4 o;
+                o.x = as_u32(acc[v][4 * q]);
+                o.y = as_u32(acc[v][4 * q + 1]);
+                o.z = as_u32(acc[v][4 * q + 2]);
+                o.w = as_u32(acc[v][4 * q + 3]);
+                pb.store16<RMSN_BWD_PARTIAL_AUX>((uint32_t)((v * LPR + lane) * EPV + 4 * q) * 4u, o);
             }
         }
     }

@@ -1,6 +1,7 @@
 // rmsn_bwd_lds_f32.hip -- LDS-staged backward kernels (rmsn_bwd_lds.h) for
 // fp32 activations and weights: the plain kernels on RMSN_LDS_SHAPES and the residual-fused
-// ones on RMSN_LDS_RES_SHAPES (rmsn_instances.h), and their lookup.
+// ones on RMSN_LDS_RES_SHAPES, the wide-row ones on RMSN_WIDE_LDS_SHAPES
+// (rmsn_instances.h), and their lookups.
 #include "rmsn_bwd_lds.h"
 #include "rmsn_instances.h"
 
@@ -16,5 +17,7 @@ static const KernelEntry kLdsResidual[] = {RMSN_LDS_RES_SHAPES(RMSN_ENTRY)};
 const KernelEntry *bwd_lds_kernel_f32(int res, int lpr, int wg, int st) {
     return res ? find_entry(kLdsResidual, lpr, 1, wg, st) : find_entry(kLds, lpr, 1, wg, st);
 }
+
+const KernelEntry *bwd_wide_lds_kernel_f32(int, int, int) { return nullptr; }  // 16-bit activations only
 
 }  // namespace rmsn

@@ -82,7 +82,8 @@ __global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t 
     const KernelEntry *fwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf); \
     const KernelEntry *bwd_vec_kernel_##tag(int res, int lpr, int vpt, int wg, int pf); \
     const KernelEntry *bwd_wide_kernel_##tag(int res, int vpt, int pf);                  \
-    const KernelEntry *bwd_lds_kernel_##tag(int res, int lpr, int wg, int st);
+    const KernelEntry *bwd_lds_kernel_##tag(int res, int lpr, int wg, int st);           \
+    const KernelEntry *bwd_wide_lds_kernel_##tag(int lpr, int vpt, int st);
 RMSN_FORMATS(RMSN_DECL)
 #undef RMSN_DECL
 
@@ -128,6 +129,17 @@ const KernelEntry *bwd_lds_kernel(int dtype, int res, int lpr, int wg, int st) {
     case 2: return bwd_lds_kernel_f16(res, lpr, wg, st);
     case 3: return bwd_lds_kernel_bf16w32(res, lpr, wg, st);
     case 4: return bwd_lds_kernel_f16w32(res, lpr, wg, st);
+    default: return nullptr;
+    }
+}
+
+const KernelEntry *bwd_wide_lds_kernel(int dtype, int lpr, int vpt, int st) {
+    switch (dtype) {
+    case 0: return bwd_wide_lds_kernel_f32(lpr, vpt, st);
+    case 1: return bwd_wide_lds_kernel_bf16(lpr, vpt, st);
+    case 2: return bwd_wide_lds_kernel_f16(lpr, vpt, st);
+    case 3: return bwd_wide_lds_kernel_bf16w32(lpr, vpt, st);
+    case 4: return bwd_wide_lds_kernel_f16w32(lpr, vpt, st);
     default: return nullptr;
     }
 }

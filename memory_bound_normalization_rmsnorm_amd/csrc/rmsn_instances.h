@@ -69,6 +69,16 @@
 #define RMSN_LDS_RES_SHAPES(X) X(256, 1024, 2) X(256, 1024, 3) X(512, 512, 2) X(512, 512, 3)            \
     X(512, 512, 4) X(512, 512, 6) X(1024, 1024, 2) X(1024, 1024, 3) X(0, 1024, 2) X(0, 1024, 3)
 
+// Wide-row backward kernels with the next row staged through LDS
+// (rmsn_bwd_lds.h bwd_wide_lds; 16-bit activations only), as (lanes per row,
+// vectors per lane, stages): a whole row of x and dy per stage, so one stage
+// at 24576 columns and up to two at 16384; 1024 lanes at 2 and 3 vectors per
+// lane, 512 lanes (256 registers per lane) at 4 and 6. Rows of 32768 columns
+// have none: at 8 vectors per lane on 512 lanes the dW sums and the row spill
+// (bf16: 269 us against 149 for bwd_wide at 4096 x 32768).
+#define RMSN_WIDE_LDS_SHAPES(X) X(1024, 2, 1) X(1024, 2, 2) X(1024, 3, 1) X(512, 4, 1) X(512, 4, 2) \
+    X(512, 6, 1)
+
 namespace rmsn {
 
 template <int N>

@@ -63,6 +63,9 @@ const KernelEntry *bwd_wide_kernel(int dtype, int res, int vpt, int pf);
 // the whole workgroup, sized at launch) on `wg`-lane workgroups, `st` row
 // blocks in flight; KernelEntry::pf holds st
 const KernelEntry *bwd_lds_kernel(int dtype, int res, int lpr, int wg, int st);
+// wide-row backward kernels (`lpr` = 512 or 1024 lanes, `vpt` vectors per lane)
+// with the next `st` rows staged through LDS; plain (not residual) 16-bit activations
+const KernelEntry *bwd_wide_lds_kernel(int dtype, int lpr, int vpt, int st);
 // lds: the backward kernel that keeps its dW sums in LDS (rows of at most kScalarLdsCols columns)
 const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
 // element kernels: rows of `lanes` lanes (64, 128, 256, 512 or 1024), k

@@ -52,6 +52,8 @@ ROWWG_MIN_VECS = 256  # backward rows wider than this may run on any whole numbe
 # LDS-staged backward kernels (copy_mode 1): (lanes per row, workgroup) -> stage counts built; lanes 0 is
 # the row on the whole workgroup (see csrc/rmsn_instances.h)
 LDS_BUILT = {(256, 1024): (2, 3, 4), (512, 512): (2, 3, 4, 6, 8), (1024, 1024): (2, 3, 4), (0, 1024): (2, 3, 4)}
+# wide rows staged through LDS: (lanes per row, vectors per lane, stages)
+WIDE_LDS_BUILT = ((1024, 2, 1), (1024, 2, 2), (1024, 3, 1), (512, 4, 1), (512, 4, 2), (512, 6, 1))
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
 
@@ -144,6 +146,12 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             for g in sorted({num_cus, 2 * num_cus} & set(range(1, M + 1))):
                 out.append(rmsnorm_config(vector_path=2, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
                                           wg_threads=WIDE_LANES, prefetch=pf, grid=g))
+        # the next rows staged through LDS (16-bit activations): one workgroup per CU
+        if dtype != F32:
+            for lpr, v, st in WIDE_LDS_BUILT:
+                if (v - 1) * lpr < nvec <= v * lpr:
+                    out.append(rmsnorm_config(vector_path=2, lanes_per_row=lpr, vecs_per_lane=v, wg_threads=lpr,
+                                              prefetch=st, copy_mode=1, grid=min(num_cus, M)))
     if default is not None:
         out.insert(0, default)
     return out

@@ -148,3 +148,35 @@ def test_lds_configuration_errors():
     with pytest.raises(rn.RmsnormError) as e:
         rn.rmsnorm_fwd_with_config(x, w, 1e-6, M, N, rn.BF16, out, rstd, cfg)
     assert e.value.status == rn.ECONFIG
+
+
+# (lanes per row, vectors per lane, stages) of the wide-row LDS kernels (rmsn_instances.h)
+WIDE_LDS_SHAPES = [(1024, 2, 1), (1024, 2, 2), (1024, 3, 1), (512, 4, 1), (512, 4, 2), (512, 6, 1)]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16", "bf16w32", "f16w32"])
+def test_every_wide_lds_kernel(fmt):
+    """Wide rows (vector_path 2) with the next rows staged through LDS
+    (copy_mode 1): every built shape, a ragged last vector slot, walks longer
+    and shorter than the ring, against the oracle, and dW bit-identical on a
+    second run."""
+    act = "bf16" if fmt.startswith("bf16") else "f16"
+    wdt = "f32" if fmt.endswith("w32") else act
+    for lpr, vpt, st in WIDE_LDS_SHAPES:
+        nvec = (vpt - 1) * lpr + lpr // 2 + 3
+        N = nvec * 8
+        grid = 3
+        for M in ((2 * st + 1) * grid + 1, grid - 1):
+            x, w, dy = si.random_case(M, N, act, seed=lpr + vpt * 7 + st + M, dy_scale=1e-2, w_dist="uniform",
+                                      wdtype=wdt)
+            eps = si.eps_f32(1e-5)
+            cfg = rn.rmsnorm_config(vector_path=2, lanes_per_row=lpr, vecs_per_lane=vpt, wg_threads=lpr,
+                                    prefetch=st, copy_mode=1, grid=grid)
+            _say(f"wide lds {fmt} lanes={lpr} vpt={vpt} stages={st} M={M} N={N}")
+            _, rstd = gpu_fwd(x, w, eps, act)
+            dx, dw = gpu_bwd(x, w, dy, rstd, act, cfg=cfg)
+            odx, orr = oracle.bwd_dx(x, w, dy, eps, act, wdtype=wdt)
+            check_rows(dx, odx, act, "dx", floor=term_rms(x, w, dy, orr, act))
+            check_dw(dw, oracle.bwd_dw(x, dy, eps, act), act)
+            dx2, dw2 = gpu_bwd(x, w, dy, rstd, act, cfg=cfg)
+            assert np.array_equal(dw.view(np.uint32), dw2.view(np.uint32)), "dW differs between two runs"

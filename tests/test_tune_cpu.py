@@ -67,12 +67,19 @@ def test_candidates_include_the_lds_pipeline():
     none for the forward or for rows of more than one vector per lane."""
     def lds(M, N, dt=rn.BF16, is_bwd=1):
         return {(c.lanes_per_row, c.wg_threads, c.prefetch, c.grid)
-                for c in tune.candidates(M, N, dt, is_bwd, 256) if c.copy_mode == 1}
+                for c in tune.candidates(M, N, dt, is_bwd, 256) if c.copy_mode == 1 and c.vector_path == 1}
     assert lds(16384, 4096) == {(512, 512, s, g) for s in (2, 3, 4, 6, 8) for g in (256, 512)}
     assert {(l, s) for l, _, s, _ in lds(16384, 5120)} == {(l, s) for l in (640, 1024) for s in (2, 3, 4)}
     assert {(l, w) for l, w, _, _ in lds(16384, 2048)} == {(256, 1024)}
     assert lds(16384, 4096, is_bwd=0) == set()
-    assert lds(4096, 32768) == set()           # 4096 vectors: the wide-row kernels
+    assert lds(4096, 32768) == set()           # 4096 vectors: the wide-row kernels (below)
+    wide = {(c.lanes_per_row, c.vecs_per_lane, c.prefetch) for c in tune.candidates(4096, 32768, rn.BF16, 1, 256)
+            if c.copy_mode == 1 and c.vector_path == 2}
+    assert wide == set()                       # 32768 columns: none built (they spill)
+    wide = {(c.lanes_per_row, c.vecs_per_lane, c.prefetch) for c in tune.candidates(4096, 16384, rn.F16, 1, 256)
+            if c.copy_mode == 1 and c.vector_path == 2}
+    assert wide == {(1024, 2, 1), (1024, 2, 2), (512, 4, 1), (512, 4, 2)}
+    assert not any(c.copy_mode for c in tune.candidates(4096, 32768, rn.F32, 1, 256))
     assert lds(4096, 1024) == set()            # 128 vectors
     assert not [c for c in tune.candidates(16384, 5120, rn.BF16, 0, 256) if c.lanes_per_row == 640]  # forward
     assert not [c for c in tune.candidates(16384, 4096, rn.BF16, 1, 256) if c.lanes_per_row % 64 == 0 and
