@@ -157,8 +157,8 @@ int rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd,
 
 /*
  * Fused residual add + RMSNorm (page "Profiling, GPU utilisation and writing
- * a fused kernel", Problem 15: read x and the residual, write their sum and
- * the normalised sum, in one pass).
+ * a fused kernel", Problem 15: the residual sum and its normalisation
+ * produced by one kernel, in one pass over the rows).
  *
  * rmsnorm_fwd_residual: h = x + res rounded to the activation format and
  * stored ([M][N], the residual stream for the next layer); y and rstd are the

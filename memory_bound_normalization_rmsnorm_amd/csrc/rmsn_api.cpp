@@ -323,15 +323,33 @@ int deep_prefetch(int is_bwd, int64_t N, int dtype, const rmsnorm_config *c) {
     return c->lanes_per_row >= 512 && 4 * nvec >= 3 * (int64_t)c->lanes_per_row ? 1 : 0;
 }
 
+// Wide rows (the wide-row kernel) with 16-bit activations and weights over
+// walks of at least kWideLongWalk rows per compute unit: two workgroups per CU
+// (past what stays resident at 4 vectors per lane, whose dW sums fill LDS:
+// the second half of the grid then runs as the first drains), no prefetch at
+// 2 or 3 vectors per lane. Measured (whole rmsnorm_bwd calls, graph-timed,
+// rotating inputs; bf16): 16384 x 16384 286.1 -> 273.0 us, 32768 x 16384
+// 577.6 -> 534.6, 32768 x 24576 844.0 -> 819.2, 16384 x 32768 593.2 -> 566.1,
+// 32768 x 32768 1162.1 -> 1105.5; fp16 likewise. Shorter walks keep one
+// prefetching workgroup per CU (1-2% faster there); fp32 activations or
+// weights measured within 1.5% either way and keep it too.
+constexpr int64_t kWideLongWalk = 64;
+
+bool wide_long_walk(int64_t M, int dtype, int64_t cus, const rmsnorm_config *c) {
+    return c->vector_path == kWidePath && (dtype == RMSN_BF16 || dtype == RMSN_F16) && M >= kWideLongWalk * cus;
+}
+
 // Backward prefetch depth. The deep shapes above: 2. Otherwise at 1024 lanes
 // per row (one or two vectors per lane; the prefetching kernels with more
 // vectors spill): 1 when each workgroup walks at most kShortWalk rows, else 0.
 // Needs the grid, so it runs after ladder_grid.
-void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config *c) {
+void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, int64_t cus, rmsnorm_config *c) {
     if (deep_prefetch(is_bwd, N, dtype, c))
         c->prefetch = 2;
     else if (is_bwd && c->vector_path == 1 && c->lanes_per_row == kMaxVecLanes && c->vecs_per_lane <= 2)
         c->prefetch = M <= kShortWalk * c->grid ? 1 : 0;
+    else if (is_bwd && wide_long_walk(M, dtype, cus, c) && c->vecs_per_lane <= 3)
+        c->prefetch = 0;
 }
 
 // Backward memory path. Rows of one vector per lane from 384 to 1024 vectors
@@ -352,6 +370,7 @@ void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, rmsnorm_config
 // 8.5 against 8.8 us) and for rows of 320 vectors (2560 bf16 columns); the
 // residual-fused backward measured within noise either way and keeps it.
 constexpr int64_t kLdsMinVecs = 384, kLdsMinWalk = 8, kLdsMaxWalk = 64;
+
 
 void ladder_copy(int64_t M, int64_t N, int dtype, int is_bwd, int res, int64_t cus, rmsnorm_config *c) {
     if (!is_bwd || res || c->vector_path != 1 || cus < 1) return;
@@ -432,6 +451,7 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         if (want > cap) want = cap > cus ? cap : cus;
         const int64_t resident = cus * (blocks_per_cu > 0 ? blocks_per_cu : 1);
         if (want > resident) want = resident;
+        if (wide_long_walk(M, dtype, cus, c)) want = 2 * cus;
         grid = row_blocks < want ? row_blocks : want;
         // A few rows (a decode step's): one workgroup walks them all and
         // writes dW itself, with no combine launch. Faster while M * N is at
@@ -440,8 +460,9 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         // 3.2 us at M = 2 and
         // 5.2 -> 4.6 at M = 4 (6 rows: 5.3 against 6.0), 8192 columns 6.0 ->
         // 4.8 at M = 2, 2048 columns 5.5 -> 4.3 at M = 8, fp32 4096 5.5 -> 3.3
-        // at M = 2 (graph-timed rows + combine against the one kernel).
-        if (row_blocks <= kBwdSinglePasses && M * N <= kBwdSingleElems) grid = 1;
+        // at M = 2 (graph-timed rows + combine against the one kernel). Vector
+        // rows only: the element and scalar kernels were not timed this way.
+        if (c->vector_path == 1 && row_blocks <= kBwdSinglePasses && M * N <= kBwdSingleElems) grid = 1;
     }
     c->grid = grid > 0 ? grid : 1;
     c->partial_rows = c->grid;
@@ -568,7 +589,7 @@ int resolve_uncached(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int r
     st = occupancy(dev, k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, res, cus, blocks, c);
-    ladder_prefetch(M, N, dtype, is_bwd, c);
+    ladder_prefetch(M, N, dtype, is_bwd, cus, c);
     ladder_copy(M, N, dtype, is_bwd, res, cus, c);
     k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
@@ -852,7 +873,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     std::memset(out, 0, sizeof *out);
     ladder_shape(M, N, dtype, is_bwd, a, num_cus, out);
     ladder_grid(M, N, dtype, is_bwd, 0, num_cus, blocks_per_cu, out);
-    ladder_prefetch(M, N, dtype, is_bwd, out);
+    ladder_prefetch(M, N, dtype, is_bwd, num_cus, out);
     ladder_copy(M, N, dtype, is_bwd, 0, num_cus, out);
     return RMSN_OK;
 }

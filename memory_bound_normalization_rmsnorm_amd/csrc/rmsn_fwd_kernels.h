@@ -3,8 +3,8 @@
 // Per row i: rstd_i = 1/sqrt(sum_j v_ij^2 / N + eps), y_ij = v_ij * rstd_i * w_j
 // (hello-gpu "Chapter 13 Fused RMSNorm", section 13.1), where v = x, or with
 // the fused residual add (RES; page "Profiling, GPU utilisation and writing a
-// fused kernel", Problem 15: read x and the residual, write the sum and the
-// normalised sum) v = h = x + res rounded to the activation format, stored,
+// fused kernel", Problem 15: the residual sum and its normalisation from
+// one kernel) v = h = x + res rounded to the activation format, stored,
 // and normalised as stored, so the result is that of the unfused add followed
 // by the normalisation. The square, the row sum, the scalar and the scaled
 // store happen in one kernel with the row held in registers, so every input

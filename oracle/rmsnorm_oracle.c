@@ -28,8 +28,8 @@
  *       dW_j  = sum_i dy_ij * x_ij * r_i     (rows ascending)
  *
  *   Residual-add fusion -- the profiling page, Problem 15 (last paragraph of
- *   the kernel sketch): read x and a residual, write their sum and the
- *   normalised sum. Read here as the unfused composition it replaces: the
+ *   the kernel sketch): one kernel that produces both the residual sum and
+ *   its normalisation. Read here as the unfused composition it replaces: the
  *   sum is stored in the activation format, h_ij = round(x_ij + res_ij), and
  *   the forward above is applied to h as stored. Its backward receives, next
  *   to dy, the gradient dh flowing into h from the residual branch, and

@@ -137,6 +137,9 @@ def test_ladder_covers_new_formats(dtype):
         if a["vector_path"] == 2 and dtype != rn.F16:
             assert a["prefetch"] == 0 and b["prefetch"] == 1
             a["prefetch"] = b["prefetch"]
+            # 16384 rows of 32768 (a walk of 64): bf16 takes two workgroups per CU, fp32 weights keep one
+            assert (a["grid"], b["grid"]) == (256, 512)
+            a["grid"], a["partial_rows"] = b["grid"], b["partial_rows"]
         if not is_bwd and dtype != rn.F16 and N != 128:   # 128 columns: 1024 row blocks, 4 per CU
             assert a["grid"] == a["partial_rows"] == 512 and a["prefetch"] == 0 and b["grid"] > 512
             a["grid"], a["partial_rows"] = b["grid"], b["partial_rows"]
@@ -356,14 +359,15 @@ def test_ladder_element_cases(N, dtype, aligned, g, fwd, bwd):
 
 
 def test_ladder_backward_single_workgroup_for_a_few_rows():
-    """A few rows: one workgroup walks them and writes dW itself (no combine)
-    while M * N <= 16384 and the walk is at most 4 row blocks."""
+    """A few rows of the vector kernels: one workgroup walks them and writes dW
+    itself (no combine) while M * N <= 16384 and the walk is at most 4 row
+    blocks. The element kernels (not timed this way) keep their grid."""
     for M, N, dt in ((1, 4096, rn.BF16), (2, 4096, rn.BF16), (4, 4096, rn.BF16), (2, 8192, rn.BF16),
-                     (8, 2048, rn.BF16), (4, 4096, rn.F32), (3, 5001, rn.BF16)):
+                     (8, 2048, rn.BF16), (4, 4096, rn.F32), (4, 2560, rn.BF16)):
         c = cfg(M, N, dt, 1)
         assert c["grid"] == c["partial_rows"] == 1, (M, N, c)
     for M, N, dt in ((5, 4096, rn.BF16), (3, 8192, rn.BF16), (12, 2048, rn.BF16), (300, 3, rn.BF16),
-                     (17, 1024, rn.F32)):
+                     (17, 1024, rn.F32), (3, 5001, rn.BF16), (4, 257, rn.F32)):
         c = cfg(M, N, dt, 1)
         assert c["grid"] > 1, (M, N, c)
 
@@ -635,3 +639,19 @@ def test_lds_copy_mode_configurations():
     for kw in bad:
         assert rc(rn.BF16, 2128, **kw) == rn.ECONFIG, kw
     assert rc(rn.BF16, 4096, is_bwd=0, lanes_per_row=128, vecs_per_lane=4, wg_threads=256) == rn.ECONFIG
+
+
+@pytest.mark.parametrize("M,N,dtype,vpt,pf,grid", [
+    (16384, 16384, rn.BF16, 2, 0, 512),   # a walk of 64: two per CU, no prefetch
+    (32768, 24576, rn.F16, 3, 0, 512),
+    (16384, 32768, rn.BF16, 4, 1, 512),   # 4 vectors per lane keep the prefetch
+    (8192, 16384, rn.BF16, 2, 1, 256),    # a walk of 32: one prefetching workgroup per CU
+    (16384, 16384, rn.BF16_WF32, 2, 0, 256),  # fp32 weights: one per CU, no prefetch
+    (16384, 32768, rn.F32, 8, 0, 256),
+])
+def test_ladder_wide_rows_long_walks(M, N, dtype, vpt, pf, grid):
+    """Wide rows with 16-bit activations and weights over walks of 64 rows per
+    CU or more: two workgroups per CU (beyond residency at 4 vectors per
+    lane), prefetch off at 2-3 vectors per lane."""
+    c = cfg(M, N, dtype, 1, blocks=1)
+    assert (c["vector_path"], c["vecs_per_lane"], c["prefetch"], c["grid"]) == (2, vpt, pf, grid)

@@ -24,7 +24,8 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import memory_bound_normalization_rmsnorm_amd as rn  # noqa: E402
 import oracle  # noqa: E402
 import synthetic_inputs as si  # noqa: E402
-from parity_util import (DT, FORMATS, check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd, oracle_row_blocks,  # noqa: E402
+from parity_util import (DT, FORMATS, check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd, gpu_fwd_residual,  # noqa: E402
+                         oracle_row_blocks,
                          term_rms, to_device, to_host, widen)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hello_gpu_ch13_worked_examples.json")
@@ -422,11 +423,15 @@ def test_every_workgroup_row_kernel(dtype):
 
 
 @pytest.mark.parametrize("dtype,M,N", [("bf16", 1, 4096), ("bf16", 16, 128), ("f32", 1, 1024), ("bf16", 1, 32768),
-                                       ("f32", 1, 257), ("bf16", 8, 1024)], ids=lambda v: str(v))
+                                       ("bf16", 8, 1024), ("bf16", 2, 4096), ("bf16", 4, 4096), ("f32", 4, 4096),
+                                       ("bf16", 8, 2048), ("bf16", 4, 2560)], ids=lambda v: str(v))
 def test_single_workgroup_backward_writes_dw(dtype, M, N):
     """A backward whose row kernel runs as one workgroup writes dW itself (no
-    combine launch): dW and dx against the oracle, equal to the two-call path
-    (rows, then combine, through the workspace), and, with dW not 16-byte
+    combine launch), including walks of 2 to 4 row blocks (the depth-2
+    prefetch kernel at 4 x 4096, 256-lane rows at 8 x 2048, whole-wavefront
+    rows at 4 x 2560): dW and dx against the oracle, equal to the two-call
+    path (rows, then combine, through the workspace), nothing written around a
+    16-byte aligned dW inside a larger buffer, and, with dW not 16-byte
     aligned, the combine path again."""
     x, w, dy = si.random_case(M, N, dtype, seed=M * 31 + N, dy_scale=1e-2)
     eps = si.eps_f32(1e-6)
@@ -456,6 +461,47 @@ def test_single_workgroup_backward_writes_dw(dtype, M, N):
     torch.cuda.synchronize()
     assert np.array_equal(dw3.cpu().numpy(), dw), "dW through the combine differs"
     assert torch.isnan(big[0]) and torch.isnan(big[N + 1:]).all(), "wrote outside dW"
+    # dW 16 bytes into a larger buffer: the direct write, and nothing around it
+    big = torch.full((N + 8,), float("nan"), device="cuda")
+    dw4 = big[4:N + 4]
+    rn.rmsnorm_bwd(xd, wd, gd, rd, M, N, code, dxd, dw4, ws, nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(dw4.cpu().numpy(), dw), "direct dW differs"
+    assert torch.isnan(big[:4]).all() and torch.isnan(big[N + 4:]).all(), "the direct write went outside dW"
+
+
+def test_single_workgroup_residual_backward():
+    """The fused residual backward on one workgroup (2 rows of 4096) writes dW
+    itself: dx and dW against the oracle's residual reading."""
+    M, N = 2, 4096
+    code = rn.BF16
+    assert rn.rmsnorm_query_config(M, N, code, 1).grid == 1
+    x, w, dy = si.random_case(M, N, "bf16", seed=77, dy_scale=1e-2)
+    res = si.random_tensor((M, N), "bf16", seed=78)
+    dh = si.random_tensor((M, N), "bf16", seed=79, scale=1e-2)
+    eps = si.eps_f32(1e-6)
+    h, _, rstd = gpu_fwd_residual(x, res, w, eps, "bf16")
+    dx, dw = gpu_bwd(h, w, dy, rstd, "bf16", dh=dh)
+    odx, orr = oracle.bwd_dx(x, w, dy, eps, "bf16", res=res, dh=dh)
+    check_rows(dx, odx, "bf16", "dx", floor=term_rms(h, w, dy, orr, "bf16", dh=dh))
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, "bf16", res=res), "bf16")
+
+
+def test_element_rows_keep_the_combine_for_few_rows():
+    """The single-workgroup rule was measured on the vector kernels only; rows
+    that are not a multiple of 16 bytes (the element kernels) keep their grid
+    and the combine at a few rows, and match the oracle."""
+    for dtype, M, N in (("bf16", 3, 5001), ("f32", 1, 257)):
+        code = DT[dtype]
+        c = rn.rmsnorm_query_config(M, N, code, 1)
+        assert c.vector_path == 3 and c.grid == M, (dtype, M, N, c.as_dict())
+        x, w, dy = si.random_case(M, N, dtype, seed=N, dy_scale=1e-2)
+        eps = si.eps_f32(1e-6)
+        _, rstd = gpu_fwd(x, w, eps, dtype)
+        dx, dw = gpu_bwd(x, w, dy, rstd, dtype)
+        odx, orr = oracle.bwd_dx(x, w, dy, eps, dtype)
+        check_rows(dx, odx, dtype, "dx", floor=term_rms(x, w, dy, orr, dtype))
+        check_dw(dw, oracle.bwd_dw(x, dy, eps, dtype), dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
