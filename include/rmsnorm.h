@@ -84,14 +84,21 @@ typedef enum {
  */
 typedef struct {
     int32_t vector_path;     /* 1: 16-byte vector row kernel; 2: the backward's wide-row vector
-                                kernel (1024 lanes, dW sums in LDS); 3: element kernel (rows
+                                kernel (1024 lanes, dW sums in LDS); 4: the backward's split-row
+                                kernel (each row on K = lanes_per_row / 1024 workgroups of 1024
+                                lanes, K = 2..16, that exchange their parts of the row sum
+                                through the workspace; vecs_per_lane vectors per lane of each
+                                member's slice, 3-4 for 16-bit and 5-8 for fp32 activations;
+                                grid a multiple of K, at most what stays resident on the
+                                device at once); 3: element kernel (rows
                                 that are not a multiple of 16 bytes or not 16-byte aligned,
                                 up to 16384 columns: lanes_per_row = wg_threads = 64, 128, 256,
                                 512 or 1024, vecs_per_lane accesses of elems_per_access
                                 elements per lane); 0: scalar row kernel */
     int32_t lanes_per_row;   /* lanes that share one row (1..1024): a power of two, or for the
                                 backward with one vector per lane any multiple of 64 up to 1024
-                                with wg_threads equal to it (the row is the whole workgroup) */
+                                with wg_threads equal to it (the row is the whole workgroup);
+                                split rows: K * 1024 */
     int32_t vecs_per_lane;   /* 16-byte vectors each lane holds per row (vector path) */
     int32_t wg_threads;      /* workgroup size */
     int32_t rows_per_wg;     /* rows a workgroup works on at once */
@@ -119,7 +126,8 @@ typedef struct {
                                 workgroup (2-4); with the fused residual add 2-3 stages (512
                                 lanes: 2, 3, 4, 6). 0 on every other path */
     int64_t grid;            /* workgroups launched */
-    int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid) */
+    int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid; split
+                                rows: grid / K, one per group of K workgroups) */
     int64_t partial_stride;  /* backward: floats between consecutive partial rows */
 } rmsnorm_config;
 
@@ -185,8 +193,9 @@ int rmsnorm_bwd_residual(const void *h, const void *w, const void *dy, const voi
 /*
  * The two kernels of rmsnorm_bwd as separate calls, for callers that time or
  * schedule them apart. rmsnorm_bwd_rows runs the persistent row kernel: dx,
- * and one fp32 partial dW row per workgroup in the workspace (rows of
- * round_up(N, 64) floats); *partial_rows receives how many (0 when M == 0).
+ * and one fp32 partial dW row per workgroup (per group of K workgroups on
+ * split rows) in the workspace (rows of round_up(N, 64) floats);
+ * *partial_rows receives how many (0 when M == 0).
  * rmsnorm_bwd_combine then writes dW[j] = sum over p < partial_rows of
  * partial[p][j] in a fixed order. Same arguments, checks and workspace
  * contract as rmsnorm_bwd; rmsnorm_bwd(...) equals rows followed by combine.
@@ -205,8 +214,10 @@ int rmsnorm_bwd_combine(const void *workspace, int64_t partial_rows, int64_t N, 
  * kernel actually costs on Hopper", section 06: the memory-path knobs belong
  * in the search space). Returns RMSN_ECONFIG when the configuration does not
  * cover the row or its kernel is not built. The backward workspace must hold
- * grid * partial_stride floats (partial_stride = N rounded up to 64). dW bits
- * depend on the configuration.
+ * grid * partial_stride floats (partial_stride = N rounded up to 64); split
+ * rows (vector_path 4): (grid / K) * partial_stride floats, then 16 bytes per
+ * workgroup rounded up to 256 (the exchange slots, zeroed by the call). dW
+ * bits depend on the configuration.
  */
 int rmsnorm_fwd_with_config(const void *x, const void *w, float eps, int64_t M, int64_t N, int dtype,
                             void *y, float *rstd, const rmsnorm_config *cfg, void *stream);
@@ -226,13 +237,15 @@ int rmsnorm_bwd_with_config(const void *x, const void *w, const void *dy, const 
  * looks up that device's copy of the array (hipGetSymbolAddress).
  *
  * Limit: the shape's row kernel must need at most RMSN_NOALLOC_SCRATCH_BYTES
- * of partial rows (grid * round_up(N, 64) * 4 bytes; bf16 4096 x 32768 needs
- * exactly 32 MiB), else RMSN_ESCRATCH is returned before anything is
- * launched. Every call on one GPU shares that GPU's array: calls that overlap
- * in time on one GPU (two streams, two host threads) race on it and their dW
- * is undefined; calls on one stream are ordered and safe. Nothing in the
- * array needs to start at zero: each call's row kernel writes every partial
- * row its combine reads.
+ * of workspace (partial_rows * round_up(N, 64) * 4 bytes, plus 16 bytes per
+ * workgroup rounded up to 256 on split rows; bf16 4096 x 32768 needs exactly
+ * 32 MiB), else RMSN_ESCRATCH is returned before anything is launched. Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (two streams, two host threads) race on it and their dW is undefined;
+ * calls on one stream are ordered and safe. Nothing in the array needs to
+ * start at zero: each call's row kernel writes every partial row its combine
+ * reads, and on split rows the call zeroes the exchange slots itself (a fill
+ * kernel) before the row kernel.
  */
 #define RMSN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 int rmsnorm_bwd_noalloc(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,

@@ -126,11 +126,18 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     wide workgroup per compute unit (its LDS allows no more at 4 vectors).
 //   Rows the vector kernels cannot take because N*elem is not a multiple of
 //     16 bytes or a pointer is not 16-byte aligned go to the element kernels
-//     from 257 to 16384 columns (see ladder_shape); those and anything else
-//     they cannot take (more than 1024 * 8 vectors forward, or backward more
-//     than 1024 * 4 16-bit or 1024 * 8 fp32 vectors) go to the scalar
-//     kernel.
+//     from 257 to 16384 columns (see ladder_shape).
+//   Wider rows: the plain forward holds up to 16 vectors per lane on 1024
+//     lanes (16384 vectors: 131072 16-bit or 65536 fp32 columns; the fused
+//     residual forward up to 8). The backward splits rows of more than
+//     1024 * 4 16-bit or 1024 * 8 fp32 vectors over K = 2..16 workgroups of
+//     1024 lanes (the split-row kernel: each member's dW sums for its slice
+//     in LDS, the row sum exchanged through the workspace), K the fewest
+//     whose slices fit the wide kernel's LDS. Anything wider goes to the
+//     scalar kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
+constexpr int kSplitPath = 4;  // rmsnorm_config::vector_path of the split-row backward kernels
+constexpr int kFwdXWideVecs = 16;  // vectors per lane of the widest plain forward rows
 constexpr int kCopyLds = 1;   // rmsnorm_config::copy_mode of the LDS-staged backward kernels
 constexpr int kMaxLdsStages = 8;
 constexpr int kLdsStages = 2;  // LDS stages the ladder picks
@@ -248,9 +255,24 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
     return 0;
 }
 
-void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, const Align &a, int64_t cus, rmsnorm_config *c) {
+// Split-row backward: K workgroups of 1024 lanes per row, `vpt` vectors per
+// lane of each member's slice (rmsn_bwd_split.h). The grid is set by
+// ladder_grid (groups of K).
+void set_split_shape(int64_t K, int64_t vpt, int pf, rmsnorm_config *c) {
+    set_vector_shape(K * rmsn::kWideLanes, vpt, rmsn::kWideLanes, pf, c);
+    c->vector_path = kSplitPath;
+    c->rows_per_wg = 1;
+}
+
+int64_t split_members(const rmsnorm_config &c) {
+    return c.vector_path == kSplitPath ? c.lanes_per_row / rmsn::kWideLanes : 1;
+}
+
+void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Align &a, int64_t cus,
+                  rmsnorm_config *c) {
     const int64_t nvec = N * elem_size(dtype) / 16;
-    const int64_t vmax = is_bwd ? wide_max_vecs(dtype) : 2 * kFwdMaxVecs;  // the forward keeps 8 for very wide rows
+    // the forward holds very wide rows at up to 16 vectors per lane (8 with the residual add)
+    const int64_t vmax = is_bwd ? wide_max_vecs(dtype) : res ? 2 * kFwdMaxVecs : kFwdXWideVecs;
     if (!vector_ok(N, dtype, a)) {
         // rows that are not a multiple of 16 bytes or not 16-byte aligned:
         // the element kernels (the row read once into registers) from 257
@@ -268,7 +290,16 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, const Align &a, i
         return;
     }
     if (nvec > kMaxVecLanes * vmax) {
-        set_scalar_shape(c);
+        // backward: the fewest members whose slices fit the wide kernel's
+        // LDS, prefetching with 16-bit weights (as the wide rows do)
+        const int64_t K = (nvec + kMaxVecLanes * vmax - 1) / (kMaxVecLanes * vmax);
+        if (is_bwd && K <= rmsn::kMaxSplit) {
+            const int64_t slice = (nvec + K - 1) / K;
+            set_split_shape(K, (slice + kMaxVecLanes - 1) / kMaxVecLanes,
+                            (dtype == RMSN_BF16 || dtype == RMSN_F16) ? 1 : 0, c);
+        } else {
+            set_scalar_shape(c);
+        }
         return;
     }
     if (is_bwd && nvec > kMaxVecLanes && (dtype != RMSN_F32 || nvec > kMaxVecLanes * kBwdMaxVecs)) {
@@ -463,9 +494,18 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         // at M = 2 (graph-timed rows + combine against the one kernel). Vector
         // rows only: the element and scalar kernels were not timed this way.
         if (c->vector_path == 1 && row_blocks <= kBwdSinglePasses && M * N <= kBwdSingleElems) grid = 1;
+        // Split rows: groups of K members, as many as stay resident together
+        // (every member of a group must run at once: they wait on each
+        // other), at most one per row.
+        if (c->vector_path == kSplitPath) {
+            const int64_t K = split_members(*c);
+            int64_t groups = resident / K;
+            if (groups > M) groups = M;
+            grid = (groups > 0 ? groups : 1) * K;
+        }
     }
     c->grid = grid > 0 ? grid : 1;
-    c->partial_rows = c->grid;
+    c->partial_rows = c->grid / split_members(*c);
     c->partial_stride = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
 }
 
@@ -553,6 +593,14 @@ int occupancy(int dev, const void *fn, int wg, int *blocks) {
 const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd, int res) {
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
     if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access, c.lanes_per_row);
+    if (c.vector_path == kSplitPath) {
+        const int64_t K = split_members(c);
+        if (!is_bwd || c.copy_mode != 0 || c.lanes_per_row != K * rmsn::kWideLanes || K < 2 || K > rmsn::kMaxSplit ||
+            c.wg_threads != rmsn::kWideLanes)
+            return nullptr;
+        const KernelEntry *e = rmsn::bwd_split_kernel(dtype, res, c.vecs_per_lane, c.prefetch);
+        return e ? e->fn : nullptr;
+    }
     if (c.vector_path == kWidePath) {
         const KernelEntry *e = !is_bwd ? nullptr
                                : c.copy_mode == kCopyLds
@@ -583,7 +631,7 @@ int resolve_uncached(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int r
     int cus = 0, blocks = 0;
     int st = device_info(dev, &cus);
     if (st != RMSN_OK) return st;
-    ladder_shape(M, N, dtype, is_bwd, a, cus, c);
+    ladder_shape(M, N, dtype, is_bwd, res, a, cus, c);
     const void *k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
     st = occupancy(dev, k, c->wg_threads, &blocks);
@@ -620,8 +668,15 @@ int resolve(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int res, const
     return RMSN_OK;
 }
 
+// Bytes of the partial rows at the start of the workspace.
+int64_t partial_bytes(const rmsnorm_config &c) { return c.partial_rows * c.partial_stride * int64_t(sizeof(float)); }
+
+// The backward's workspace: the partial rows, then (split rows) one exchange
+// slot per workgroup, 256-byte aligned (partial_stride is a multiple of 64
+// floats).
 int64_t workspace_for(const rmsnorm_config &c) {
-    return c.partial_rows * c.partial_stride * int64_t(sizeof(float));
+    const int64_t slots = c.vector_path == kSplitPath ? c.grid * rmsn::kSplitSlotBytes : 0;
+    return partial_bytes(c) + (slots + 255) / 256 * 256;
 }
 
 // The documented workspace requirement of rmsnorm_bwd on device `dev`: enough
@@ -671,7 +726,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
                     const Align &a, rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
-    if (req->vector_path < 0 || req->vector_path > kElemPath) return RMSN_ECONFIG;
+    if (req->vector_path < 0 || req->vector_path > kSplitPath) return RMSN_ECONFIG;
     if (req->vector_path == kElemPath) {
         const int64_t k = req->vecs_per_lane;
         const int64_t g = req->elems_per_access ? req->elems_per_access : elem_group(N, dtype, a);
@@ -684,6 +739,25 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         c->vecs_per_lane = (int32_t)k;
     } else if (req->elems_per_access != 0) {
         return RMSN_ECONFIG;
+    } else if (req->vector_path == kSplitPath) {
+        // K = lanes_per_row / 1024 members per row; the grid whole groups,
+        // all resident at once on the current device
+        const int64_t nvec = N * elem_size(dtype) / 16;
+        const int64_t K = req->lanes_per_row / rmsn::kWideLanes;
+        if (!is_bwd || !vector_ok(N, dtype, a) || req->lanes_per_row % rmsn::kWideLanes != 0 || K < 2 ||
+            K > rmsn::kMaxSplit || (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes) ||
+            (int64_t)req->lanes_per_row * req->vecs_per_lane < nvec || req->prefetch < 0 || req->prefetch > 1 ||
+            req->copy_mode != 0 || req->stream_loads != 0 || req->grid % K != 0)
+            return RMSN_ECONFIG;
+        set_split_shape(K, req->vecs_per_lane, req->prefetch, c);
+        const void *k = kernel_for(*c, N, dtype, is_bwd, res);
+        if (!k) return RMSN_ECONFIG;
+        int dev = 0, cus = 0, blocks = 0;
+        int st = current_device(&dev);
+        if (st == RMSN_OK) st = device_info(dev, &cus);
+        if (st == RMSN_OK) st = occupancy(dev, k, rmsn::kWideLanes, &blocks);
+        if (st != RMSN_OK) return st;
+        if (req->grid > (int64_t)cus * blocks) return RMSN_ECONFIG;
     } else if (req->vector_path) {
         const int64_t nvec = N * elem_size(dtype) / 16;
         if (!vector_ok(N, dtype, a)) return RMSN_ECONFIG;
@@ -716,7 +790,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     ladder_grid(M, N, dtype, is_bwd, res, 1, 1, c);
     c->grid = req->grid;
     c->prefetch = req->vector_path ? req->prefetch : 0;  // as requested (the kernel above was chosen by it)
-    c->partial_rows = req->grid;
+    c->partial_rows = req->grid / split_members(*c);
     c->stream_loads = req->vector_path ? req->stream_loads : 0;
     *fn = k;
     return RMSN_OK;
@@ -762,8 +836,8 @@ int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStre
                   rmsn::kCombineWG, cargs, s);
 }
 
-// dw_direct: when not NULL and the grid is a single workgroup, its partial row
-// is dW itself, written straight to dw_direct (16-byte aligned) instead of
+// dw_direct: when not NULL and the grid writes a single partial row (one
+// workgroup, or one group of a split row), that row is dW itself, written straight to dw_direct (16-byte aligned) instead of
 // the workspace; *partial_rows is then 0 and there is nothing to combine.
 // scratch: the workspace is the static device array of rmsnorm_bwd_noalloc
 // (the ladder's configuration only); `workspace` is then set to its address
@@ -808,10 +882,28 @@ int rows_impl(const void *x, const void *w, const void *dy, const void *dh, cons
         }
     }
     int32_t n32 = (int32_t)N;
-    int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
+    int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath || c.vector_path == kSplitPath)
+                       ? (int32_t)(N * elem_size(dtype) / 16)
+                       : 0;
     const bool direct = dw_direct && c.partial_rows == 1 && aligned16(dw_direct);
     float *partial = direct ? dw_direct : static_cast<float *>(workspace);
     int64_t ldp = c.partial_stride;
+    if (c.vector_path == kSplitPath) {
+        // the exchange slots after the partial rows, zeroed by a kernel (so
+        // that the call can be captured in a graph)
+        void *xch = static_cast<char *>(workspace) + partial_bytes(c);
+        int64_t words = c.grid * rmsn::kSplitSlotBytes / 4;
+        void *zargs[] = {(void *)&xch, (void *)&words};
+        st = launch(rmsn::fill_zero_kernel(), (words + 255) / 256, 256, zargs, s);
+        if (st != RMSN_OK) return st;
+        int32_t K = (int32_t)split_members(c);
+        void *args[] = {(void *)&x, (void *)&w, (void *)&dy, (void *)&dh, (void *)&rstd, (void *)&dx,
+                        (void *)&partial, (void *)&ldp, (void *)&M, (void *)&n32, (void *)&nvec, (void *)&K,
+                        (void *)&xch};
+        st = launch(fn, c.grid, c.wg_threads, args, s);
+        if (st == RMSN_OK) *partial_rows = direct ? 0 : c.partial_rows;
+        return st;
+    }
     void *args[] = {(void *)&x, (void *)&w, (void *)&dy, (void *)&dh, (void *)&rstd, (void *)&dx,
                     (void *)&partial, (void *)&ldp, (void *)&M, (void *)&n32, (void *)&nvec};
     st = launch(fn, c.grid, c.wg_threads, args, s);
@@ -871,7 +963,7 @@ int rmsnorm_select_config(int64_t M, int64_t N, int dtype, int is_bwd, int align
     const int v = aligned == 1 ? 16 : aligned;
     const Align a{v > elem_size(dtype) ? v : elem_size(dtype), v > w_size(dtype) ? v : w_size(dtype)};
     std::memset(out, 0, sizeof *out);
-    ladder_shape(M, N, dtype, is_bwd, a, num_cus, out);
+    ladder_shape(M, N, dtype, is_bwd, 0, a, num_cus, out);
     ladder_grid(M, N, dtype, is_bwd, 0, num_cus, blocks_per_cu, out);
     ladder_prefetch(M, N, dtype, is_bwd, num_cus, out);
     ladder_copy(M, N, dtype, is_bwd, 0, num_cus, out);

@@ -3,6 +3,7 @@
 // RMSN_LADDER_SHAPES, the wide-row kernels on RMSN_WIDE_SHAPES_16 (rmsn_instances.h),
 // and the lookups the host dispatch uses.
 #include "rmsn_bwd_kernels.h"
+#include "rmsn_bwd_split.h"
 #include "rmsn_instances.h"
 
 namespace rmsn {
@@ -28,4 +29,15 @@ const KernelEntry *bwd_vec_kernel_bf16(int res, int lpr, int vpt, int wg, int pf
 const KernelEntry *bwd_wide_kernel_bf16(int res, int vpt, int pf) {
     return find_entry(res ? kWideResidual : kWide, kWideLanes, vpt, kWideLanes, pf);
 }
+#define RMSN_SPLIT_ENTRY(V, P) {kWideLanes, V, kWideLanes, P, reinterpret_cast<const void *>(&bwd_split<bf16_t, bf16_t, false, V, (P != 0)>)},
+static const KernelEntry kSplit[] = {RMSN_SPLIT_SHAPES_16(RMSN_SPLIT_ENTRY)};
+#undef RMSN_SPLIT_ENTRY
+#define RMSN_SPLIT_ENTRY(V, P) {kWideLanes, V, kWideLanes, P, reinterpret_cast<const void *>(&bwd_split<bf16_t, bf16_t, true, V, (P != 0)>)},
+static const KernelEntry kSplitResidual[] = {RMSN_SPLIT_SHAPES_16(RMSN_SPLIT_ENTRY)};
+#undef RMSN_SPLIT_ENTRY
+
+const KernelEntry *bwd_split_kernel_bf16(int res, int vpt, int pf) {
+    return find_entry(res ? kSplitResidual : kSplit, kWideLanes, vpt, kWideLanes, pf);
+}
+
 }  // namespace rmsn

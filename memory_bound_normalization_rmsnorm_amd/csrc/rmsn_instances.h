@@ -79,6 +79,20 @@
 #define RMSN_WIDE_LDS_SHAPES(X) X(1024, 2, 1) X(1024, 2, 2) X(1024, 3, 1) X(512, 4, 1) X(512, 4, 2) \
     X(512, 6, 1)
 
+// Forward rows of 8193 to 16384 16-byte vectors (131072 16-bit or 65536
+// fp32 columns) on one 1024-lane workgroup, 9 to 16 vectors per lane (the
+// weights re-read from cache), plain forward only.
+#define RMSN_FWD_XWIDE_SHAPES(X) X(1024, 9, 1024, 0) X(1024, 10, 1024, 0) X(1024, 11, 1024, 0) \
+    X(1024, 12, 1024, 0) X(1024, 13, 1024, 0) X(1024, 14, 1024, 0) X(1024, 15, 1024, 0) X(1024, 16, 1024, 0)
+
+// Backward rows split over K workgroups (rmsn_bwd_split.h), as (vectors per
+// lane, prefetch): slices of at most 4096 16-byte vectors hold 2049 to 4096
+// of them, 3 or 4 per lane (16-bit activations); fp32 slices of at most 8192,
+// 5 to 8 per lane. Prefetch with 16-bit weights only, as for wide rows.
+#define RMSN_SPLIT_SHAPES_16(X) X(3, 0) X(3, 1) X(4, 0) X(4, 1)
+#define RMSN_SPLIT_SHAPES_W32(X) X(3, 0) X(4, 0)
+#define RMSN_SPLIT_SHAPES_32(X) X(5, 0) X(6, 0) X(7, 0) X(8, 0)
+
 namespace rmsn {
 
 template <int N>

@@ -66,6 +66,13 @@ const KernelEntry *bwd_lds_kernel(int dtype, int res, int lpr, int wg, int st);
 // wide-row backward kernels (`lpr` = 512 or 1024 lanes, `vpt` vectors per lane)
 // with the next `st` rows staged through LDS; plain (not residual) 16-bit activations
 const KernelEntry *bwd_wide_lds_kernel(int dtype, int lpr, int vpt, int st);
+// backward rows split over several 1024-lane workgroups (rmsn_bwd_split.h),
+// `vpt` vectors per lane of the workgroup's slice
+const KernelEntry *bwd_split_kernel(int dtype, int res, int vpt, int pf);
+// bytes of one workgroup's exchange slot of the split backward
+constexpr int kSplitSlotBytes = 16;
+// most workgroups a split row may take
+constexpr int kMaxSplit = 16;
 // lds: the backward kernel that keeps its dW sums in LDS (rows of at most kScalarLdsCols columns)
 const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
 // element kernels: rows of `lanes` lanes (64, 128, 256, 512 or 1024), k

@@ -54,6 +54,15 @@ ROWWG_MIN_VECS = 256  # backward rows wider than this may run on any whole numbe
 LDS_BUILT = {(256, 1024): (2, 3, 4), (512, 512): (2, 3, 4, 6, 8), (1024, 1024): (2, 3, 4), (0, 1024): (2, 3, 4)}
 # wide rows staged through LDS: (lanes per row, vectors per lane, stages)
 WIDE_LDS_BUILT = ((1024, 2, 1), (1024, 2, 2), (1024, 3, 1), (512, 4, 1), (512, 4, 2), (512, 6, 1))
+# vectors per lane of the plain forward's widest rows (1024 lanes)
+FWD_XWIDE_VPT = 16
+# split-row backward kernels (vector_path 4): per format, vectors per lane -> prefetch variants
+SPLIT_MAX = 16
+SPLIT_BUILT = {
+    BF16: {3: (0, 1), 4: (0, 1)}, F16: {3: (0, 1), 4: (0, 1)},
+    BF16_WF32: {3: (0,), 4: (0,)}, F16_WF32: {3: (0,), 4: (0,)},
+    F32: {5: (0,), 6: (0,), 7: (0,), 8: (0,)},
+}
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
 
@@ -67,8 +76,12 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
     partially used slot at most, crossed with grids: the row-block count,
     its halves, and 1-4 workgroups per compute unit; for backward rows of more
     than 1024 vectors also the wide-row kernels at one and two workgroups per
-    compute unit, and for backward rows of 257 to 1024 vectors whose whole
-    wavefronts are not a power of two the workgroup-sized row kernels. Shapes that are not built fail at launch and are skipped.
+    compute unit, for backward rows of 257 to 1024 vectors whose whole
+    wavefronts are not a power of two the workgroup-sized row kernels, for
+    forward rows of 8193 to 16384 vectors 9 to 16 vectors per lane on 1024
+    lanes, and for backward rows beyond the wide kernels the split-row kernels
+    (K and K + 1 members, every built prefetch, resident groups and half of
+    them). Shapes that are not built fail at launch and are skipped.
     Rows that are not a multiple of 16 bytes (up to 16384 columns) get the
     element kernels instead: the widest group of consecutive elements per
     access that N allows (pointers 16-byte aligned, as in the search's own
@@ -152,6 +165,30 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
                 if (v - 1) * lpr < nvec <= v * lpr:
                     out.append(rmsnorm_config(vector_path=2, lanes_per_row=lpr, vecs_per_lane=v, wg_threads=lpr,
                                               prefetch=st, copy_mode=1, grid=min(num_cus, M)))
+    # the plain forward's rows of 9 to 16 vectors per lane on 1024 lanes
+    if not is_bwd and WIDE_LANES * MAX_VPT < nvec <= WIDE_LANES * FWD_XWIDE_VPT:
+        vpt = -(-nvec // WIDE_LANES)
+        for g in sorted(x for x in {M, num_cus, 2 * num_cus} if 1 <= x <= M):
+            for sl in (0, 1):
+                out.append(rmsnorm_config(vector_path=1, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
+                                          wg_threads=WIDE_LANES, stream_loads=sl, grid=g))
+    # backward rows beyond the wide kernels: split over K workgroups, the
+    # fewest K whose slices fit and one more, every built vectors per lane;
+    # groups of K as many as stay resident (one workgroup per CU) and at most M
+    if is_bwd and nvec > WIDE_LANES * wide_max:
+        k0 = -(-nvec // (WIDE_LANES * wide_max))
+        for K in (k0, k0 + 1):
+            if K > SPLIT_MAX:
+                continue
+            vpt = -(-(-(-nvec // K)) // WIDE_LANES)
+            if vpt not in SPLIT_BUILT[dtype]:
+                continue
+            groups = min(num_cus // K, M)
+            for pf in SPLIT_BUILT[dtype][vpt]:
+                for g in sorted({groups, -(-groups // 2)}):
+                    if g >= 1:
+                        out.append(rmsnorm_config(vector_path=4, lanes_per_row=K * WIDE_LANES, vecs_per_lane=vpt,
+                                                  wg_threads=WIDE_LANES, prefetch=pf, grid=g * K))
     if default is not None:
         out.insert(0, default)
     return out

@@ -108,6 +108,10 @@ def gpu_fwd_residual(x, res, w, eps, dtype, cfg=None):
 def workspace(M, N, code, cfg=None):
     if cfg is None:
         nbytes = rn.rmsnorm_bwd_workspace_bytes(M, N, code)
+    elif cfg.vector_path == 4:
+        # split rows: a partial row per group of K, then 16 bytes per workgroup
+        groups = int(cfg.grid) // (int(cfg.lanes_per_row) // 1024)
+        nbytes = groups * ((N + 63) // 64 * 64) * 4 + (int(cfg.grid) * 16 + 255) // 256 * 256
     else:
         nbytes = int(cfg.grid) * ((N + 63) // 64 * 64) * 4
     # 256-byte aligned (the caching allocator aligns to 512); poisoned with NaN

@@ -207,9 +207,41 @@ def test_ladder_wide_rows(N, dtype, vpt, pf):
     # fp32 up to 4 vectors per lane keeps the register kernel
     r = cfg(4096, 16384, rn.F32, 1)
     assert (r["vector_path"], r["vecs_per_lane"]) == (1, 4)
-    # beyond what the LDS sums hold: the scalar kernel
-    assert cfg(4096, 65536, rn.BF16, 1)["vector_path"] == 0
-    assert cfg(4096, 36864, rn.F32, 1)["vector_path"] == 0
+    # beyond what the LDS sums hold: the split-row kernel
+    assert cfg(4096, 65536, rn.BF16, 1)["vector_path"] == 4
+    assert cfg(4096, 36864, rn.F32, 1)["vector_path"] == 4
+
+
+@pytest.mark.parametrize("M,N,dtype,K,vpt,pf,grid", [
+    (4096, 32768 + 8, rn.BF16, 2, 3, 1, 256),    # 4097 vectors: two slices of 2049
+    (4096, 65536, rn.BF16, 2, 4, 1, 256),
+    (4096, 65536, rn.BF16_WF32, 2, 4, 0, 256),   # fp32 weights: no prefetch
+    (4096, 131072, rn.F16, 4, 4, 1, 256),
+    (4096, 98304, rn.BF16, 3, 4, 1, 255),        # 85 groups of 3
+    (4096, 36864, rn.F32, 2, 5, 0, 256),
+    (4096, 65536, rn.F32, 2, 8, 0, 256),
+    (4096, 524288, rn.BF16, 16, 4, 1, 256),      # the widest split row
+    (100, 65536, rn.BF16, 2, 4, 1, 200),         # a group per row
+    (1, 65536, rn.BF16, 2, 4, 1, 2),
+])
+def test_ladder_split_rows(M, N, dtype, K, vpt, pf, grid):
+    """Backward rows wider than the wide-row kernel's LDS sums hold: K
+    workgroups of 1024 lanes per row, the fewest whose slices fit, groups of K
+    as many as stay resident (one workgroup per CU here) and at most one per
+    row; one partial dW row per group."""
+    c = cfg(M, N, dtype, 1, blocks=1)
+    assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"]) == \
+        (4, K * 1024, vpt, 1024, pf)
+    assert c["rows_per_wg"] == 1 and c["copy_mode"] == 0
+    assert (c["grid"], c["partial_rows"]) == (grid, grid // K)
+    nvec = N * (4 if dtype == rn.F32 else 2) // 16
+    slice_ = -(-nvec // K)
+    assert (vpt - 1) * 1024 < slice_ <= vpt * 1024
+    # the forward holds the same rows on one workgroup up to 16 vectors per lane
+    if nvec <= 16384:
+        f = cfg(M, N, dtype, 0)
+        assert (f["vector_path"], f["lanes_per_row"], f["vecs_per_lane"], f["wg_threads"]) == \
+            (1, 1024, -(-nvec // 1024), 1024)
 
 
 def test_explicit_config_errors():
@@ -230,6 +262,34 @@ def test_explicit_config_errors():
     assert fwd(vector_path=2, lanes_per_row=1024, vecs_per_lane=1, wg_threads=1024) == rn.ECONFIG  # backward only
     assert fwd(vector_path=3) == rn.ECONFIG
     assert fwd(prefetch=2) == rn.ECONFIG
+
+
+def test_explicit_split_config_errors():
+    """Split-row configurations (vector_path 4) that cannot fit are refused
+    before any HIP call: not whole groups, K outside 2..16, lanes not whole
+    1024-lane members, slices wider than the kernel, no such kernel, the
+    forward."""
+    L, C = rn.lib, rn.rmsnorm_config
+    M, N = 64, 65536
+
+    def bwd(**kw):
+        c = C(vector_path=4, lanes_per_row=2048, vecs_per_lane=4, wg_threads=1024, prefetch=1, grid=4)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return L.rmsnorm_bwd_with_config(FAKE, FAKE, FAKE, FAKE, M, N, rn.BF16, FAKE, FAKE, FAKE, 1 << 30, c, None)
+
+    assert bwd(grid=3) == rn.ECONFIG
+    assert bwd(lanes_per_row=1024) == rn.ECONFIG
+    assert bwd(lanes_per_row=17 * 1024, grid=17) == rn.ECONFIG
+    assert bwd(lanes_per_row=1536) == rn.ECONFIG
+    assert bwd(vecs_per_lane=3) == rn.ECONFIG      # 2048 x 3 vectors do not cover 8192
+    assert bwd(vecs_per_lane=5) == rn.ECONFIG      # not built for 16-bit rows
+    assert bwd(prefetch=2) == rn.ECONFIG
+    assert bwd(copy_mode=1) == rn.ECONFIG
+    assert bwd(wg_threads=512) == rn.ECONFIG
+    assert bwd(stream_loads=1) == rn.ECONFIG
+    c = C(vector_path=4, lanes_per_row=2048, vecs_per_lane=4, wg_threads=1024, prefetch=1, grid=4)
+    assert L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, M, N, rn.BF16, FAKE, FAKE, c, None) == rn.ECONFIG
 
 
 def test_fwd_empty_is_noop():
@@ -306,12 +366,14 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (vpt - 1) * lpr < nvec <= vpt * lpr
 
 
-@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(65536 + 8, rn.BF16, 1, 0), (32768 + 8, rn.BF16, 1, 1),
+@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(131072 + 8, rn.BF16, 1, 0), (65536 + 4, rn.F32, 1, 0),
+                                                    (524288 + 8, rn.BF16, 1, 1), (524288 + 4, rn.F32, 1, 1),
                                                     (16385, rn.BF16, 1, 0), (20000, rn.F32, 0, 1)])
 def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
     """The scalar kernel: rows the vector kernels cannot take that are wider
     than the element kernels hold (16384 columns), and rows wider than the
-    vector kernels hold."""
+    vector kernels hold (forward: 16 vectors on each of 1024 lanes; backward:
+    16 split-row members of 4 16-bit or 8 fp32 vectors per lane)."""
     c = cfg(100, N, dtype, is_bwd, aligned=aligned)
     assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
 

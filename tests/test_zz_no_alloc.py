@@ -8,8 +8,9 @@ a smaller input, so the second call finds the array holding the first call's
 partial rows; every output is poisoned with NaN before each call. The first
 outputs are also checked against the fp64 oracle. Shapes cover the vector
 kernels with a combine, the single-workgroup call that writes dW itself, the
-wide-row kernel at the array's exact limit, the element kernels, and M = 0. A
-shape whose partial rows exceed the array is refused before any launch.
+wide-row kernel at the array's exact limit, the element kernels, M = 0, and
+split rows (exchange slots after the partial rows, zeroed by each call). A
+shape whose workspace exceeds the array is refused before any launch.
 """
 
 from __future__ import annotations
@@ -83,6 +84,7 @@ PAIRS = [
     ((1024, 4096), (2, 4096), "f32"),         # combine, then one workgroup writing dW itself
     ((2048, 4100), (33, 257), "bf16"),        # element kernels
     ((777, 2560), (0, 2560), "f16"),          # whole-wavefront rows, then M = 0 (dW = 0)
+    ((100, 65536), (2, 49152), "bf16"),       # split rows: exchange slots after the partial rows
 ]
 
 
@@ -106,11 +108,13 @@ def test_noalloc_matches_workspace_call(first, second, dtype):
 
 
 def test_noalloc_refuses_shapes_beyond_the_array():
-    # bf16 rows of 65536 columns take the scalar kernel with two workgroups per
-    # CU: 512 partial rows of 256 KiB = 128 MiB > 32 MiB. Refused before any launch.
+    # bf16 rows of 65536 columns split over two workgroups, one group per two
+    # CUs: 128 partial rows of 256 KiB (32 MiB) plus the exchange slots > 32
+    # MiB. Refused before any launch.
     M, N = 4096, 65536
     cfg = rn.rmsnorm_query_config(M, N, rn.BF16, 1)
-    assert cfg.grid * cfg.partial_stride * 4 > rn.NOALLOC_SCRATCH_BYTES
+    assert cfg.vector_path == 4
+    assert cfg.partial_rows * cfg.partial_stride * 4 + cfg.grid * 16 > rn.NOALLOC_SCRATCH_BYTES
     x = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
     w = torch.ones(N, dtype=torch.bfloat16, device="cuda")
     rstd = torch.ones(M, dtype=torch.float32, device="cuda")
