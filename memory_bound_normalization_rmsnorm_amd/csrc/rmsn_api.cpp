@@ -132,9 +132,19 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     residual forward up to 8). The backward splits rows of more than
 //     1024 * 4 16-bit or 1024 * 8 fp32 vectors over K = 2..16 workgroups of
 //     1024 lanes (the split-row kernel: each member's dW sums for its slice
-//     in LDS, the row sum exchanged through the workspace), K the fewest
-//     whose slices fit the wide kernel's LDS. Anything wider goes to the
-//     scalar kernel.
+//     in LDS, the row sum exchanged through the workspace). 16-bit rows:
+//     K is the fewest whose slices hold 2 vectors per lane, two members per
+//     CU, while that is at most 16; wider rows, and fp32 rows, take the
+//     fewest of one per CU (up to 4 or 8 vectors per lane). No prefetch: at
+//     two per CU it spills, and at one per CU it measured 2% slower (bf16
+//     4096 x 65536). Measured (graph-timed, rotating inputs) two per CU
+//     against one: bf16 4096 x 65536 311.8 -> 293.9 us, 2048 x 131072 340.8
+//     -> 317.8, 1024 x 262144 373.5 -> 378.4 (the one loss), bf16 with fp32
+//     weights 8192 x 49152 646.7 -> 492.8; fp32 rows lose at two per CU (3
+//     vectors per lane: 4096 x 65536 581.3 -> 641.7 us, 4096 x 36864 308.8
+//     -> 330.0). At 32768 16-bit columns the wide kernel stays (148.3 us
+//     against 155.4 split over two). Anything wider goes to the scalar
+//     kernel.
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
 constexpr int kSplitPath = 4;  // rmsnorm_config::vector_path of the split-row backward kernels
 constexpr int kFwdXWideVecs = 16;  // vectors per lane of the widest plain forward rows
@@ -255,6 +265,11 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
     return 0;
 }
 
+// Split rows of two workgroups per CU: vectors per lane of the slices (their
+// dW sums fill at most 64 KiB of LDS and the kernel 64 VGPRs); 16-bit
+// activations only (fp32 rows measured faster on fewer, wider members).
+constexpr int64_t kSplitTwoVecs = 2;
+
 // Split-row backward: K workgroups of 1024 lanes per row, `vpt` vectors per
 // lane of each member's slice (rmsn_bwd_split.h). The grid is set by
 // ladder_grid (groups of K).
@@ -290,13 +305,15 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Al
         return;
     }
     if (nvec > kMaxVecLanes * vmax) {
-        // backward: the fewest members whose slices fit the wide kernel's
-        // LDS, prefetching with 16-bit weights (as the wide rows do)
-        const int64_t K = (nvec + kMaxVecLanes * vmax - 1) / (kMaxVecLanes * vmax);
+        // backward: 16-bit activations, the fewest members of two per CU
+        // (slices of 2 vectors per lane) up to kMaxSplit of them; else the
+        // fewest of one per CU (up to 4 or 8 per lane, as the wide kernel)
+        const int64_t K2 = (nvec + kMaxVecLanes * kSplitTwoVecs - 1) / (kMaxVecLanes * kSplitTwoVecs);
+        const int64_t K1 = (nvec + kMaxVecLanes * vmax - 1) / (kMaxVecLanes * vmax);
+        const int64_t K = dtype != RMSN_F32 && K2 <= rmsn::kMaxSplit ? K2 : K1;
         if (is_bwd && K <= rmsn::kMaxSplit) {
             const int64_t slice = (nvec + K - 1) / K;
-            set_split_shape(K, (slice + kMaxVecLanes - 1) / kMaxVecLanes,
-                            (dtype == RMSN_BF16 || dtype == RMSN_F16) ? 1 : 0, c);
+            set_split_shape(K, (slice + kMaxVecLanes - 1) / kMaxVecLanes, 0, c);
         } else {
             set_scalar_shape(c);
         }

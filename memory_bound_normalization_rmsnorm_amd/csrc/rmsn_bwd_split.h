@@ -45,8 +45,13 @@ struct SplitSlot {
 // sleep); far beyond any real wait (microseconds), well under a second.
 constexpr uint32_t kSplitSpinLimit = 1u << 20;
 
+// Waves per SIMD a member asks for: two workgroups per CU (64 VGPRs each)
+// when its dW sums take at most 64 KiB of LDS (2 vectors of 8 16-bit
+// elements per lane, or 4 of 4 fp32), one above.
+constexpr int split_waves_per_eu(int vpt, int epv) { return (vpt * epv <= 16 ? 2 : 1) * kWideLanes / 256; }
+
 template <typename T, typename TW, bool RES, int VPT, bool PF>
-__global__ void __launch_bounds__(kWideLanes) __attribute__((amdgpu_waves_per_eu(kWideLanes / 256)))
+__global__ void __launch_bounds__(kWideLanes) __attribute__((amdgpu_waves_per_eu(split_waves_per_eu(VPT, Elem<T>::kPerVec))))
 bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
           const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
           int32_t N, int32_t nvec, int32_t K, SplitSlot *__restrict__ xch) {
@@ -55,7 +60,10 @@ bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict
     constexpr int LPR = kWideLanes;
     constexpr int EPV = E::kPerVec;
     constexpr int Q = EPV / 4;  // float4 words of dW sums per vector
-    constexpr bool kKeepW = wide_keeps_w<T, TW, VPT, PF>();  // as the wide-row kernel
+    // weights kept in registers as by the wide-row kernel; at two workgroups
+    // per CU (64 VGPRs) only up to 2 weight vectors per lane
+    constexpr bool kTwoPerCU = split_waves_per_eu(VPT, EPV) > kWideLanes / 256;
+    constexpr bool kKeepW = wide_keeps_w<T, TW, VPT, PF>() && (!kTwoPerCU || VPT * WV::kVecs <= 2);
     static_assert(VPT * EPV * LPR * 4 <= kWideLdsBytes, "dW sums must fit in LDS");
     __shared__ float slots[2 * (LPR / 64)];
     __shared__ float total[2];
@@ -108,8 +116,7 @@ bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict
     SplitSlot *const group = xch + g * K;
     int parity = 0;
     uint32_t it = 0;
-    uint32_t spins = 0;  // polls so far (lane 0), over the whole walk
-    bool dead = false;   // lane 0 gave up waiting: every later sum is NaN
+    uint32_t spins = 0;  // polls so far (lane 0) over the whole walk; at the limit every later sum is NaN
     int64_t row = g;
     u32x4 xn[VPT], gn[VPT];
     float rn = 0.f;
@@ -155,13 +162,13 @@ bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict
                 float part = s;
                 if (p != k) {
                     uint64_t v = 0;
-                    while (!dead) {
+                    while (spins < kSplitSpinLimit) {
                         v = __hip_atomic_load(&group[p].word[it & 1u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         if ((v & ~uint64_t(0xffffffffu)) == tag) break;
-                        if (++spins >= kSplitSpinLimit) dead = true;
+                        ++spins;
                         __builtin_amdgcn_s_sleep(2);
                     }
-                    part = dead ? __builtin_nanf("") : __uint_as_float((uint32_t)v);
+                    part = spins < kSplitSpinLimit ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
                 }
                 t += part;
             }

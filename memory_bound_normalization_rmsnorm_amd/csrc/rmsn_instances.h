@@ -86,11 +86,12 @@
     X(1024, 12, 1024, 0) X(1024, 13, 1024, 0) X(1024, 14, 1024, 0) X(1024, 15, 1024, 0) X(1024, 16, 1024, 0)
 
 // Backward rows split over K workgroups (rmsn_bwd_split.h), as (vectors per
-// lane, prefetch): slices of at most 4096 16-byte vectors hold 2049 to 4096
-// of them, 3 or 4 per lane (16-bit activations); fp32 slices of at most 8192,
-// 5 to 8 per lane. Prefetch with 16-bit weights only, as for wide rows.
-#define RMSN_SPLIT_SHAPES_16(X) X(3, 0) X(3, 1) X(4, 0) X(4, 1)
-#define RMSN_SPLIT_SHAPES_W32(X) X(3, 0) X(4, 0)
+// lane, prefetch). Two workgroups per CU: 2 vectors per lane of 16-bit
+// activations (the ladder's choice up to 16 members); one per CU: 3-4
+// (16-bit) or 5-8 (fp32) for wider rows, fp32 rows and the configuration
+// search. Prefetch with 16-bit weights at one per CU only (at two it spills).
+#define RMSN_SPLIT_SHAPES_16(X) X(2, 0) X(3, 0) X(3, 1) X(4, 0) X(4, 1)
+#define RMSN_SPLIT_SHAPES_W32(X) X(2, 0) X(3, 0) X(4, 0)
 #define RMSN_SPLIT_SHAPES_32(X) X(5, 0) X(6, 0) X(7, 0) X(8, 0)
 
 namespace rmsn {

@@ -59,10 +59,13 @@ FWD_XWIDE_VPT = 16
 # split-row backward kernels (vector_path 4): per format, vectors per lane -> prefetch variants
 SPLIT_MAX = 16
 SPLIT_BUILT = {
-    BF16: {3: (0, 1), 4: (0, 1)}, F16: {3: (0, 1), 4: (0, 1)},
-    BF16_WF32: {3: (0,), 4: (0,)}, F16_WF32: {3: (0,), 4: (0,)},
+    BF16: {2: (0,), 3: (0, 1), 4: (0, 1)}, F16: {2: (0,), 3: (0, 1), 4: (0, 1)},
+    BF16_WF32: {2: (0,), 3: (0,), 4: (0,)}, F16_WF32: {2: (0,), 3: (0,), 4: (0,)},
     F32: {5: (0,), 6: (0,), 7: (0,), 8: (0,)},
 }
+# split members that run two per CU (dW sums of at most 64 KiB): vectors per
+# lane, 16-bit activations only
+SPLIT_TWO_PER_CU = {BF16: 2, F16: 2, BF16_WF32: 2, F16_WF32: 2}
 DEFAULT_CACHE = os.path.join(os.path.expanduser("~"), ".cache", "rmsnorm_mi355x", "tuned.json")
 
 
@@ -80,8 +83,8 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
     wavefronts are not a power of two the workgroup-sized row kernels, for
     forward rows of 8193 to 16384 vectors 9 to 16 vectors per lane on 1024
     lanes, and for backward rows beyond the wide kernels the split-row kernels
-    (K and K + 1 members, every built prefetch, resident groups and half of
-    them). Shapes that are not built fail at launch and are skipped.
+    (the fewest members at one and at two per CU and one more of each,
+    every built prefetch, resident groups and half of them). Shapes that are not built fail at launch and are skipped.
     Rows that are not a multiple of 16 bytes (up to 16384 columns) get the
     element kernels instead: the widest group of consecutive elements per
     access that N allows (pointers 16-byte aligned, as in the search's own
@@ -173,17 +176,23 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
                 out.append(rmsnorm_config(vector_path=1, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
                                           wg_threads=WIDE_LANES, stream_loads=sl, grid=g))
     # backward rows beyond the wide kernels: split over K workgroups, the
-    # fewest K whose slices fit and one more, every built vectors per lane;
-    # groups of K as many as stay resident (one workgroup per CU) and at most M
+    # fewest K whose slices fit at one and at two members per CU, and one
+    # more of each, every built prefetch; groups of K as many as stay resident
+    # and at most M, and half of them
     if is_bwd and nvec > WIDE_LANES * wide_max:
-        k0 = -(-nvec // (WIDE_LANES * wide_max))
-        for K in (k0, k0 + 1):
+        ks = set()
+        two = SPLIT_TWO_PER_CU.get(dtype, 0)
+        for v in (wide_max, two) if two else (wide_max,):
+            k0 = -(-nvec // (WIDE_LANES * v))
+            ks |= {k0, k0 + 1}
+        for K in sorted(ks):
             if K > SPLIT_MAX:
                 continue
             vpt = -(-(-(-nvec // K)) // WIDE_LANES)
             if vpt not in SPLIT_BUILT[dtype]:
                 continue
-            groups = min(num_cus // K, M)
+            per_cu = 2 if vpt <= two else 1
+            groups = min(per_cu * num_cus // K, M)
             for pf in SPLIT_BUILT[dtype][vpt]:
                 for g in sorted({groups, -(-groups // 2)}):
                     if g >= 1:

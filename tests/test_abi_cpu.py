@@ -212,26 +212,30 @@ def test_ladder_wide_rows(N, dtype, vpt, pf):
     assert cfg(4096, 36864, rn.F32, 1)["vector_path"] == 4
 
 
-@pytest.mark.parametrize("M,N,dtype,K,vpt,pf,grid", [
-    (4096, 32768 + 8, rn.BF16, 2, 3, 1, 256),    # 4097 vectors: two slices of 2049
-    (4096, 65536, rn.BF16, 2, 4, 1, 256),
-    (4096, 65536, rn.BF16_WF32, 2, 4, 0, 256),   # fp32 weights: no prefetch
-    (4096, 131072, rn.F16, 4, 4, 1, 256),
-    (4096, 98304, rn.BF16, 3, 4, 1, 255),        # 85 groups of 3
-    (4096, 36864, rn.F32, 2, 5, 0, 256),
-    (4096, 65536, rn.F32, 2, 8, 0, 256),
-    (4096, 524288, rn.BF16, 16, 4, 1, 256),      # the widest split row
-    (100, 65536, rn.BF16, 2, 4, 1, 200),         # a group per row
-    (1, 65536, rn.BF16, 2, 4, 1, 2),
+@pytest.mark.parametrize("M,N,dtype,blocks,K,vpt,grid", [
+    (4096, 32768 + 8, rn.BF16, 2, 3, 2, 510),      # 4097 vectors: three slices of 1366, two members per CU
+    (4096, 65536, rn.BF16, 2, 4, 2, 512),
+    (4096, 65536, rn.BF16_WF32, 2, 4, 2, 512),
+    (4096, 131072, rn.F16, 2, 8, 2, 512),
+    (4096, 98304, rn.BF16, 2, 6, 2, 510),          # 85 groups of 6
+    (4096, 262144, rn.BF16, 2, 16, 2, 512),        # 16 members of 2 vectors per lane
+    (4096, 262144 + 8, rn.BF16, 1, 9, 4, 252),     # more than 16: one member per CU, 4 per lane
+    (4096, 524288, rn.BF16, 1, 16, 4, 256),        # the widest split row
+    (4096, 36864, rn.F32, 1, 2, 5, 256),           # fp32: the fewest members of one per CU
+    (4096, 65536, rn.F32, 1, 2, 8, 256),
+    (4096, 262144, rn.F32, 1, 8, 8, 256),
+    (100, 65536, rn.BF16, 2, 4, 2, 400),           # a group per row
+    (1, 65536, rn.BF16, 2, 4, 2, 4),
 ])
-def test_ladder_split_rows(M, N, dtype, K, vpt, pf, grid):
+def test_ladder_split_rows(M, N, dtype, blocks, K, vpt, grid):
     """Backward rows wider than the wide-row kernel's LDS sums hold: K
-    workgroups of 1024 lanes per row, the fewest whose slices fit, groups of K
-    as many as stay resident (one workgroup per CU here) and at most one per
-    row; one partial dW row per group."""
-    c = cfg(M, N, dtype, 1, blocks=1)
+    workgroups of 1024 lanes per row: 16-bit rows the fewest whose slices
+    hold 2 vectors per lane while that is at most 16 members, else (and fp32
+    rows) the fewest of up to 4 or 8; groups of K as many as stay resident (`blocks` per CU)
+    and at most one per row; one partial dW row per group; no prefetch."""
+    c = cfg(M, N, dtype, 1, blocks=blocks)
     assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"]) == \
-        (4, K * 1024, vpt, 1024, pf)
+        (4, K * 1024, vpt, 1024, 0)
     assert c["rows_per_wg"] == 1 and c["copy_mode"] == 0
     assert (c["grid"], c["partial_rows"]) == (grid, grid // K)
     nvec = N * (4 if dtype == rn.F32 else 2) // 16

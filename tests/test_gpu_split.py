@@ -33,8 +33,10 @@ from parity_util import (check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd, gpu
                          oracle_row_blocks, term_rms)
 
 # (vectors per lane, prefetch) built per format (rmsn_instances.h)
-SPLIT_SHAPES = {"bf16": [(3, 0), (3, 1), (4, 0), (4, 1)], "f16": [(3, 0), (3, 1), (4, 0), (4, 1)],
-                "bf16w32": [(3, 0), (4, 0)], "f16w32": [(3, 0), (4, 0)], "f32": [(5, 0), (6, 0), (7, 0), (8, 0)]}
+SPLIT_SHAPES = {"bf16": [(2, 0), (3, 0), (3, 1), (4, 0), (4, 1)],
+                "f16": [(2, 0), (3, 0), (3, 1), (4, 0), (4, 1)],
+                "bf16w32": [(2, 0), (3, 0), (4, 0)], "f16w32": [(2, 0), (3, 0), (4, 0)],
+                "f32": [(5, 0), (6, 0), (7, 0), (8, 0)]}
 
 
 def _say(msg):

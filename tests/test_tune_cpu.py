@@ -90,12 +90,13 @@ def test_candidates_include_split_rows_and_the_widest_forward():
     """Backward rows beyond the wide kernels: the split-row kernels at the
     fewest members and one more, every built prefetch, whole resident groups;
     forward rows of 9 to 16 vectors per lane on 1024 lanes."""
-    M, N = 4096, 98304  # bf16: 12288 vectors, 3 members of 4 or 4 of 3 per lane
-    default = rn.rmsnorm_select_config(M, N, rn.BF16, 1, 1, 256, 1)
+    M, N = 4096, 98304  # bf16: 12288 vectors: 3 or 4 members of 4 or 3 per lane, 6 or 7 of 2
+    default = rn.rmsnorm_select_config(M, N, rn.BF16, 1, 1, 256, 2)
     cands = tune.candidates(M, N, rn.BF16, 1, 256, default)
     split = {(c.lanes_per_row // 1024, c.vecs_per_lane, c.prefetch, c.grid) for c in cands if c.vector_path == 4}
     assert split == {(3, 4, 0, 255), (3, 4, 1, 255), (3, 4, 0, 129), (3, 4, 1, 129),
-                     (4, 3, 0, 256), (4, 3, 1, 256), (4, 3, 0, 128), (4, 3, 1, 128)}
+                     (4, 3, 0, 256), (4, 3, 1, 256), (4, 3, 0, 128), (4, 3, 1, 128),
+                     (6, 2, 0, 510), (6, 2, 0, 258), (7, 2, 0, 511), (7, 2, 0, 259)}
     assert tune._key(cands[0]) == tune._key(default) and default.vector_path == 4
     # fp32 weights: no prefetch variant; fp32 activations: 5 to 8 vectors per lane
     assert {c.prefetch for c in tune.candidates(M, N, rn.BF16_WF32, 1, 256) if c.vector_path == 4} == {0}
