@@ -90,7 +90,11 @@ typedef struct {
                                 through the workspace; vecs_per_lane vectors per lane of each
                                 member's slice, 3-4 for 16-bit and 5-8 for fp32 activations;
                                 grid a multiple of K, at most what stays resident on the
-                                device at once); 3: element kernel (rows
+                                device at once); 5: the forward's two-pass kernel (rows
+                                wider than 16 vectors per lane on 1024 lanes, 8 with the
+                                residual add: one row per 1024-lane workgroup, read in chunks
+                                of vecs_per_lane = 4, 8 or 16 (residual: 4 or 8) vectors per
+                                lane, twice); 3: element kernel (rows
                                 that are not a multiple of 16 bytes or not 16-byte aligned,
                                 up to 16384 columns: lanes_per_row = wg_threads = 64, 128, 256,
                                 512 or 1024, vecs_per_lane accesses of elems_per_access

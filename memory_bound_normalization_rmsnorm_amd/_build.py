@@ -24,7 +24,8 @@ SOURCES = ([f"rmsn_fwd_{f}.hip" for f in FORMATS] + [f"rmsn_bwd_{f}.hip" for f i
            + [f"rmsn_bwd_lds_{f}.hip" for f in FORMATS]
            + [f"rmsn_elem_l{lanes}.hip" for lanes in (64, 128, 256, 512, 1024)]
            + ["rmsn_common.hip", "rmsn_scratch.hip", "rmsn_probe.hip", "rmsn_baseline.hip", "rmsn_api.cpp"])
-HEADERS = ["rmsn_device.h", "rmsn_tables.h", "rmsn_instances.h", "rmsn_fwd_kernels.h", "rmsn_bwd_kernels.h", "rmsn_bwd_split.h",
+HEADERS = ["rmsn_device.h", "rmsn_tables.h", "rmsn_instances.h", "rmsn_fwd_kernels.h", "rmsn_fwd_loop.h",
+           "rmsn_bwd_kernels.h", "rmsn_bwd_split.h",
            "rmsn_bwd_lds.h", "rmsn_elem_kernels.h"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.

@@ -129,7 +129,9 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     from 257 to 16384 columns (see ladder_shape).
 //   Wider rows: the plain forward holds up to 16 vectors per lane on 1024
 //     lanes (16384 vectors: 131072 16-bit or 65536 fp32 columns; the fused
-//     residual forward up to 8). The backward splits rows of more than
+//     residual forward up to 8); wider forward rows take the two-pass kernel
+//     (the row read twice, the second time from cache), of any width. The
+//     backward splits rows of more than
 //     1024 * 4 16-bit or 1024 * 8 fp32 vectors over K = 2..16 workgroups of
 //     1024 lanes (the split-row kernel: each member's dW sums for its slice
 //     in LDS, the row sum exchanged through the workspace). 16-bit rows:
@@ -148,6 +150,12 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row backward kernels
 constexpr int kSplitPath = 4;  // rmsnorm_config::vector_path of the split-row backward kernels
 constexpr int kFwdXWideVecs = 16;  // vectors per lane of the widest plain forward rows
+constexpr int kLoopPath = 5;  // rmsnorm_config::vector_path of the forward's two-pass kernels
+// Vectors per lane per chunk the ladder picks for them: 4 (two workgroups per
+// CU) was the fastest or tied against 8 and 16 (graph-timed, rotating inputs;
+// bf16 1024 x 262144 246.6 us against 258.0 and 284.1, with the residual add
+// 534.5 against 600.3; fp32 2048 x 131072 502.7 against 502.5 and 564.7).
+constexpr int kLoopChunk = 4;
 constexpr int kCopyLds = 1;   // rmsnorm_config::copy_mode of the LDS-staged backward kernels
 constexpr int kMaxLdsStages = 8;
 constexpr int kLdsStages = 2;  // LDS stages the ladder picks
@@ -265,6 +273,13 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
     return 0;
 }
 
+// Forward two-pass rows: one row per 1024-lane workgroup, `ch` vectors per
+// lane per chunk (rmsn_fwd_loop.h).
+void set_loop_shape(int ch, rmsnorm_config *c) {
+    set_vector_shape(kMaxVecLanes, ch, rmsn::kWideLanes, 0, c);
+    c->vector_path = kLoopPath;
+}
+
 // Split rows of two workgroups per CU: vectors per lane of the slices (their
 // dW sums fill at most 64 KiB of LDS and the kernel 64 VGPRs); 16-bit
 // activations only (fp32 rows measured faster on fewer, wider members).
@@ -302,6 +317,10 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Al
         } else {
             set_scalar_shape(c);
         }
+        return;
+    }
+    if (!is_bwd && nvec > kMaxVecLanes * vmax) {
+        set_loop_shape(kLoopChunk, c);
         return;
     }
     if (nvec > kMaxVecLanes * vmax) {
@@ -610,6 +629,13 @@ int occupancy(int dev, const void *fn, int wg, int *blocks) {
 const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd, int res) {
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
     if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access, c.lanes_per_row);
+    if (c.vector_path == kLoopPath) {
+        if (is_bwd || c.copy_mode != 0 || c.lanes_per_row != kMaxVecLanes || c.wg_threads != rmsn::kWideLanes ||
+            c.prefetch != 0)
+            return nullptr;
+        const KernelEntry *e = rmsn::fwd_loop_kernel(dtype, res, c.vecs_per_lane);
+        return e ? e->fn : nullptr;
+    }
     if (c.vector_path == kSplitPath) {
         const int64_t K = split_members(c);
         if (!is_bwd || c.copy_mode != 0 || c.lanes_per_row != K * rmsn::kWideLanes || K < 2 || K > rmsn::kMaxSplit ||
@@ -743,7 +769,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
                     const Align &a, rmsnorm_config *c, const void **fn) {
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
-    if (req->vector_path < 0 || req->vector_path > kSplitPath) return RMSN_ECONFIG;
+    if (req->vector_path < 0 || req->vector_path > kLoopPath) return RMSN_ECONFIG;
     if (req->vector_path == kElemPath) {
         const int64_t k = req->vecs_per_lane;
         const int64_t g = req->elems_per_access ? req->elems_per_access : elem_group(N, dtype, a);
@@ -756,6 +782,13 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         c->vecs_per_lane = (int32_t)k;
     } else if (req->elems_per_access != 0) {
         return RMSN_ECONFIG;
+    } else if (req->vector_path == kLoopPath) {
+        // the forward's two-pass kernel: 1024 lanes, vecs_per_lane per chunk
+        if (is_bwd || !vector_ok(N, dtype, a) || req->lanes_per_row != kMaxVecLanes ||
+            (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes) || req->prefetch != 0 ||
+            req->copy_mode != 0 || req->stream_loads < 0 || req->stream_loads > 1)
+            return RMSN_ECONFIG;
+        set_loop_shape(req->vecs_per_lane, c);
     } else if (req->vector_path == kSplitPath) {
         // K = lanes_per_row / 1024 members per row; the grid whole groups,
         // all resident at once on the current device
@@ -834,7 +867,7 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
     }
     if (st != RMSN_OK) return st;
     int32_t n32 = (int32_t)N;
-    int32_t nvec = (c.vector_path == 1 || c.vector_path == kWidePath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
+    int32_t nvec = (c.vector_path == 1 || c.vector_path == kLoopPath) ? (int32_t)(N * elem_size(dtype) / 16) : 0;
     int32_t stream_ld = c.stream_loads;
     void *args[] = {(void *)&x, (void *)&res, (void *)&w, (void *)&h, (void *)&y, (void *)&rstd,
                     (void *)&eps, (void *)&M, (void *)&n32, (void *)&nvec, (void *)&stream_ld};

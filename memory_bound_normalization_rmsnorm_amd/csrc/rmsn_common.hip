@@ -84,7 +84,8 @@ __global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t 
     const KernelEntry *bwd_wide_kernel_##tag(int res, int vpt, int pf);                  \
     const KernelEntry *bwd_lds_kernel_##tag(int res, int lpr, int wg, int st);           \
     const KernelEntry *bwd_wide_lds_kernel_##tag(int lpr, int vpt, int st);            \
-    const KernelEntry *bwd_split_kernel_##tag(int res, int vpt, int pf);
+    const KernelEntry *bwd_split_kernel_##tag(int res, int vpt, int pf);               \
+    const KernelEntry *fwd_loop_kernel_##tag(int res, int ch);
 RMSN_FORMATS(RMSN_DECL)
 #undef RMSN_DECL
 
@@ -130,6 +131,17 @@ const KernelEntry *bwd_lds_kernel(int dtype, int res, int lpr, int wg, int st) {
     case 2: return bwd_lds_kernel_f16(res, lpr, wg, st);
     case 3: return bwd_lds_kernel_bf16w32(res, lpr, wg, st);
     case 4: return bwd_lds_kernel_f16w32(res, lpr, wg, st);
+    default: return nullptr;
+    }
+}
+
+const KernelEntry *fwd_loop_kernel(int dtype, int res, int ch) {
+    switch (dtype) {
+    case 0: return fwd_loop_kernel_f32(res, ch);
+    case 1: return fwd_loop_kernel_bf16(res, ch);
+    case 2: return fwd_loop_kernel_f16(res, ch);
+    case 3: return fwd_loop_kernel_bf16w32(res, ch);
+    case 4: return fwd_loop_kernel_f16w32(res, ch);
     default: return nullptr;
     }
 }

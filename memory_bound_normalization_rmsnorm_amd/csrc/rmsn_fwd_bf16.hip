@@ -1,7 +1,10 @@
-// rmsn_fwd_bf16.hip -- forward vector kernels for bf16 activations and weights:
-// the plain kernels on RMSN_ALL_SHAPES and RMSN_FWD_XWIDE_SHAPES, the residual-fused ones on
-// RMSN_LADDER_SHAPES (rmsn_instances.h), and the lookup the host dispatch uses.
+// rmsn_fwd_bf16.hip -- forward vector kernels for bf16 activations and
+// weights: the plain kernels on RMSN_ALL_SHAPES and RMSN_FWD_XWIDE_SHAPES, the
+// residual-fused ones on RMSN_LADDER_SHAPES (rmsn_instances.h), the two-pass
+// kernels for wider rows on RMSN_FWD_LOOP_SHAPES_16 and
+// RMSN_FWD_LOOP_RES_SHAPES_16, and the lookups the host dispatch uses.
 #include "rmsn_fwd_kernels.h"
+#include "rmsn_fwd_loop.h"
 #include "rmsn_instances.h"
 
 namespace rmsn {
@@ -15,6 +18,22 @@ static const KernelEntry kResidual[] = {RMSN_LADDER_SHAPES(RMSN_ENTRY)};
 
 const KernelEntry *fwd_vec_kernel_bf16(int res, int lpr, int vpt, int wg, int pf) {
     return res ? find_entry(kResidual, lpr, vpt, wg, pf) : find_entry(kPlain, lpr, vpt, wg, pf);
+}
+
+#define RMSN_LOOP_ENTRY(C, W) {kWideLanes, C, kWideLanes, W, reinterpret_cast<const void *>(&fwd_loop<bf16_t, bf16_t, false, C, W>)},
+static const KernelEntry kLoop[] = {RMSN_FWD_LOOP_SHAPES_16(RMSN_LOOP_ENTRY)};
+#undef RMSN_LOOP_ENTRY
+#define RMSN_LOOP_ENTRY(C, W) {kWideLanes, C, kWideLanes, W, reinterpret_cast<const void *>(&fwd_loop<bf16_t, bf16_t, true, C, W>)},
+static const KernelEntry kLoopResidual[] = {RMSN_FWD_LOOP_RES_SHAPES_16(RMSN_LOOP_ENTRY)};
+#undef RMSN_LOOP_ENTRY
+
+// the two-pass kernel of `ch` vectors per lane per chunk (its waves per SIMD in the entry's prefetch field)
+const KernelEntry *fwd_loop_kernel_bf16(int res, int ch) {
+    const KernelEntry *t = res ? kLoopResidual : kLoop;
+    const int n = res ? (int)(sizeof kLoopResidual / sizeof *kLoopResidual) : (int)(sizeof kLoop / sizeof *kLoop);
+    for (int i = 0; i < n; ++i)
+        if (t[i].vpt == ch) return &t[i];
+    return nullptr;
 }
 
 }  // namespace rmsn

@@ -1,0 +1,117 @@
+// rmsn_fwd_loop.h -- forward for rows wider than the vector kernels hold in
+// registers (more than 16 16-byte vectors on each of 1024 lanes, or 8 with
+// the fused residual add).
+//
+// The same arithmetic as the vector kernel (hello-gpu "Chapter 13 Fused
+// RMSNorm", section 13.1; with RES the residual sum of "Profiling, GPU
+// utilisation and writing a fused kernel", Problem 15), in two passes over
+// the row, one row per 1024-lane workgroup, CH vectors per lane at a time:
+// pass 1 loads each chunk of x (with RES also res, and stores h = round(x +
+// res)) and adds its squares; after the row sum, pass 2 loads each chunk
+// again, scales it by rstd and the weights and stores y. A row of 262144
+// 16-bit columns is 512 KiB, more than a workgroup's registers and LDS hold,
+// so the second read is the price of unbounded width; pass 1's loads carry
+// no streaming hint, so pass 2 finds the row in the caches (a CU's row in
+// the MALL) rather than in HBM. With RES, pass 2 recomputes h from x and res
+// (both read-only) instead of reading back the h it stored, so no load
+// depends on the ordering of this workgroup's own stores.
+#pragma once
+
+#include "rmsn_device.h"
+#include "rmsn_tables.h"
+
+namespace rmsn {
+
+// the cache-policy bits of a load, as a type (for a generic lambda)
+template <int A>
+struct LoadAux {
+    static constexpr int value = A;
+};
+
+template <typename T, typename TW, bool RES, int CH, int WPE>
+__global__ void __launch_bounds__(kWideLanes) __attribute__((amdgpu_waves_per_eu(WPE)))
+fwd_loop(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict__ w, T *__restrict__ h,
+         T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t nvec,
+         int32_t /*stream_ld*/) {
+    using E = Elem<T>;
+    using WV = WeightVec<T, TW>;
+    constexpr int LPR = kWideLanes;
+    constexpr int EPV = E::kPerVec;
+    __shared__ float slots[2 * (LPR / 64)];
+
+    const int lane = threadIdx.x;
+    const float n = (float)N;
+    const uint32_t row_bytes = (uint32_t)nvec * 16u;
+    const Buf wb(w, row_bytes * WV::kVecs);
+    int parity = 0;
+
+    // the chunk's inputs at vector c0 + v * LPR + lane: v = x, or round(x + res)
+    auto load_chunk = [&](const Buf &xb, const Buf &rb, int c0, uint32_t (&off)[CH], u32x4 (&v)[CH], auto aux) {
+        constexpr int A = decltype(aux)::value;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int idx = c0 + k * LPR + lane;
+            off[k] = idx < nvec ? (uint32_t)idx * 16u : kOff;
+            v[k] = xb.load16<A>(off[k]);
+        }
+        if constexpr (RES) {
+            u32x4 r[CH];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) r[k] = rb.load16<A>(off[k]);
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                float a[EPV], b[EPV];
+                E::unpack(v[k], a);
+                E::unpack(r[k], b);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) a[e] += b[e];
+                v[k] = E::pack(a);
+            }
+        }
+    };
+
+    for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+        const Buf xb(x + row * N, row_bytes);
+        const Buf rb(RES ? res + row * N : x, RES ? row_bytes : 0u);
+        const Buf hb(RES ? h + row * N : y, RES ? row_bytes : 0u);
+        const Buf yb(y + row * N, row_bytes);
+
+        float ss = 0.f;
+        for (int c0 = 0; c0 < nvec; c0 += CH * LPR) {
+            uint32_t off[CH];
+            u32x4 v[CH];
+            load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_NARROW_LOAD_AUX>{});
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if constexpr (RES) hb.store16<RMSN_FWD_STORE_AUX>(off[k], v[k]);
+                ss = E::sumsq(v[k], ss);
+            }
+        }
+        ss = row_sum<LPR, LPR>(ss, slots, parity);
+        parity ^= 1;
+        const float r = __frsqrt_rn(ss / n + eps);
+        if (rstd) {
+            const Buf sb(rstd + row, 4u);
+            sb.store4(lane == 0 ? 0u : kOff, r);
+        }
+
+        for (int c0 = 0; c0 < nvec; c0 += CH * LPR) {
+            uint32_t off[CH];
+            u32x4 v[CH];
+            load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_LOAD_AUX>{});
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                WV t;
+                t.load(wb, c0 + k * LPR + lane, off[k] != kOff);
+                float f[EPV], g[EPV];
+                E::unpack(v[k], f);
+                t.unpack(g);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) f[e] = (f[e] * r) * g[e];
+                yb.store16<RMSN_FWD_STORE_AUX>(off[k], E::pack(f));
+            }
+        }
+    }
+}
+
+}  // namespace rmsn

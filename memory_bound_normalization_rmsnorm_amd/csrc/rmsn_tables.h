@@ -69,6 +69,9 @@ const KernelEntry *bwd_wide_lds_kernel(int dtype, int lpr, int vpt, int st);
 // backward rows split over several 1024-lane workgroups (rmsn_bwd_split.h),
 // `vpt` vectors per lane of the workgroup's slice
 const KernelEntry *bwd_split_kernel(int dtype, int res, int vpt, int pf);
+// forward rows beyond the vector kernels: the two-pass kernel of `ch` vectors
+// per lane per chunk (rmsn_fwd_loop.h)
+const KernelEntry *fwd_loop_kernel(int dtype, int res, int ch);
 // bytes of one workgroup's exchange slot of the split backward
 constexpr int kSplitSlotBytes = 16;
 // most workgroups a split row may take

@@ -56,6 +56,8 @@ LDS_BUILT = {(256, 1024): (2, 3, 4), (512, 512): (2, 3, 4, 6, 8), (1024, 1024): 
 WIDE_LDS_BUILT = ((1024, 2, 1), (1024, 2, 2), (1024, 3, 1), (512, 4, 1), (512, 4, 2), (512, 6, 1))
 # vectors per lane of the plain forward's widest rows (1024 lanes)
 FWD_XWIDE_VPT = 16
+# chunk sizes (vectors per lane) of the plain forward's two-pass kernels (vector_path 5)
+FWD_LOOP_CHUNKS = {BF16: (4, 8, 16), F16: (4, 8, 16), F32: (4, 8, 16), BF16_WF32: (4, 8), F16_WF32: (4, 8)}
 # split-row backward kernels (vector_path 4): per format, vectors per lane -> prefetch variants
 SPLIT_MAX = 16
 SPLIT_BUILT = {
@@ -82,7 +84,9 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
     compute unit, for backward rows of 257 to 1024 vectors whose whole
     wavefronts are not a power of two the workgroup-sized row kernels, for
     forward rows of 8193 to 16384 vectors 9 to 16 vectors per lane on 1024
-    lanes, and for backward rows beyond the wide kernels the split-row kernels
+    lanes, for forward rows beyond 8192 vectors the two-pass kernels (every
+    chunk size, a workgroup per row or two per CU), and for backward rows
+    beyond the wide kernels the split-row kernels
     (the fewest members at one and at two per CU and one more of each,
     every built prefetch, resident groups and half of them). Shapes that are not built fail at launch and are skipped.
     Rows that are not a multiple of 16 bytes (up to 16384 columns) get the
@@ -175,6 +179,13 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             for sl in (0, 1):
                 out.append(rmsnorm_config(vector_path=1, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
                                           wg_threads=WIDE_LANES, stream_loads=sl, grid=g))
+    # the forward's two-pass kernel, every built chunk size, for rows beyond
+    # 8 vectors per lane (beyond 16 it is the only vector kernel)
+    if not is_bwd and nvec > WIDE_LANES * MAX_VPT:
+        for ch in FWD_LOOP_CHUNKS[dtype]:
+            for g in sorted(x for x in {M, 2 * num_cus} if 1 <= x <= M):
+                out.append(rmsnorm_config(vector_path=5, lanes_per_row=WIDE_LANES, vecs_per_lane=ch,
+                                          wg_threads=WIDE_LANES, grid=g))
     # backward rows beyond the wide kernels: split over K workgroups, the
     # fewest K whose slices fit at one and at two members per CU, and one
     # more of each, every built prefetch; groups of K as many as stay resident

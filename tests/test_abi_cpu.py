@@ -268,6 +268,45 @@ def test_explicit_config_errors():
     assert fwd(prefetch=2) == rn.ECONFIG
 
 
+@pytest.mark.parametrize("N,dtype", [(131072 + 8, rn.BF16), (65536 + 4, rn.F32), (1 << 20, rn.BF16_WF32),
+                                     (1 << 22, rn.F16)])
+def test_ladder_forward_two_pass_rows(N, dtype):
+    """Forward rows wider than 16 vectors on each of 1024 lanes: the two-pass
+    kernel (vector_path 5), one row per 1024-lane workgroup, 4 vectors per
+    lane per chunk, a workgroup per row."""
+    for M in (1, 300, 4096):
+        c = cfg(M, N, dtype, 0)
+        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"]) == \
+            (5, 1024, 4, 1024, 0)
+        assert c["grid"] == M and c["rows_per_wg"] == 1
+    # one vector per lane fewer: the register-held row
+    r = cfg(64, 131072 if dtype != rn.F32 else 65536, dtype, 0)
+    assert (r["vector_path"], r["vecs_per_lane"]) == (1, 16)
+
+
+def test_explicit_loop_config_errors():
+    """Two-pass configurations (vector_path 5) are forward only, on 1024 lanes,
+    without prefetch or LDS copies, and only for built chunk sizes."""
+    L, C = rn.lib, rn.rmsnorm_config
+    M, N = 64, 262144
+
+    def fwd(**kw):
+        c = C(vector_path=5, lanes_per_row=1024, vecs_per_lane=8, wg_threads=1024, grid=64)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return L.rmsnorm_fwd_with_config(FAKE, FAKE, 1e-5, M, N, rn.BF16, FAKE, FAKE, c, None)
+
+    assert fwd(lanes_per_row=512) == rn.ECONFIG
+    assert fwd(wg_threads=512) == rn.ECONFIG
+    assert fwd(prefetch=1) == rn.ECONFIG
+    assert fwd(copy_mode=1) == rn.ECONFIG
+    assert fwd(vecs_per_lane=5) == rn.ECONFIG      # not built
+    assert fwd(grid=0) == rn.ECONFIG
+    c = C(vector_path=5, lanes_per_row=1024, vecs_per_lane=8, wg_threads=1024, grid=4)
+    assert L.rmsnorm_bwd_with_config(FAKE, FAKE, FAKE, FAKE, M, N, rn.BF16, FAKE, FAKE, FAKE, 1 << 30, c,
+                                     None) == rn.ECONFIG
+
+
 def test_explicit_split_config_errors():
     """Split-row configurations (vector_path 4) that cannot fit are refused
     before any HIP call: not whole groups, K outside 2..16, lanes not whole
@@ -370,14 +409,13 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     assert (vpt - 1) * lpr < nvec <= vpt * lpr
 
 
-@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(131072 + 8, rn.BF16, 1, 0), (65536 + 4, rn.F32, 1, 0),
-                                                    (524288 + 8, rn.BF16, 1, 1), (524288 + 4, rn.F32, 1, 1),
-                                                    (16385, rn.BF16, 1, 0), (20000, rn.F32, 0, 1)])
+@pytest.mark.parametrize("N,dtype,aligned,is_bwd", [(524288 + 8, rn.BF16, 1, 1), (524288 + 4, rn.F32, 1, 1),
+                                                    (16385, rn.BF16, 1, 0), (20000, rn.F32, 0, 1),
+                                                    (131072 + 8, rn.BF16, 0, 0)])
 def test_ladder_scalar_cases(N, dtype, aligned, is_bwd):
     """The scalar kernel: rows the vector kernels cannot take that are wider
-    than the element kernels hold (16384 columns), and rows wider than the
-    vector kernels hold (forward: 16 vectors on each of 1024 lanes; backward:
-    16 split-row members of 4 16-bit or 8 fp32 vectors per lane)."""
+    than the element kernels hold (16384 columns), and backward rows wider
+    than 16 split-row members of 4 16-bit or 8 fp32 vectors per lane hold."""
     c = cfg(100, N, dtype, is_bwd, aligned=aligned)
     assert c["vector_path"] == 0 and c["wg_threads"] == 256 and c["rows_per_wg"] == 1
 

@@ -8,6 +8,8 @@ the C ABI:
     ragged last slices, walks of several rows per group (both exchange values
     in use), groups without rows, and K from 2 to 16;
   * the plain forward's rows of 9 to 16 vectors per lane on 1024 lanes;
+  * the forward's two-pass kernels (vector_path 5: rows beyond those, read
+    in chunks, twice), every built chunk size, plain and residual-fused;
   * the ladder's own choice at 65536 and 131072 columns (bf16, fp16 with fp32
     weights, fp32, the residual-fused pair), every row and every dW column,
     and dW bit-identical on reruns.
@@ -30,7 +32,7 @@ import memory_bound_normalization_rmsnorm_amd as rn  # noqa: E402
 import oracle  # noqa: E402
 import synthetic_inputs as si  # noqa: E402
 from parity_util import (check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd, gpu_fwd_residual,  # noqa: E402
-                         oracle_row_blocks, term_rms)
+                         oracle_row_blocks, term_rms, widen)
 
 # (vectors per lane, prefetch) built per format (rmsn_instances.h)
 SPLIT_SHAPES = {"bf16": [(2, 0), (3, 0), (3, 1), (4, 0), (4, 1)],
@@ -160,18 +162,50 @@ def test_forward_rows_of_9_to_16_vectors_per_lane(fmt):
         check_rstd(rstd, orr)
 
 
+# chunk sizes (vectors per lane) of the two-pass forward kernels per format (rmsn_instances.h)
+LOOP_CHUNKS = {"bf16": ([4, 8, 16], [4, 8]), "f16": ([4, 8, 16], [4, 8]), "f32": ([4, 8, 16], [4, 8]),
+               "bf16w32": ([4, 8], [4, 8]), "f16w32": ([4, 8], [4, 8])}
+
+
+@pytest.mark.parametrize("res", [False, True], ids=["plain", "residual"])
+@pytest.mark.parametrize("fmt", list(LOOP_CHUNKS))
+def test_every_forward_two_pass_kernel(fmt, res):
+    """Every built chunk size on a row of two and a half chunks plus a ragged
+    wavefront, 5 rows on 3 workgroups (a workgroup takes a second row): y and
+    rstd against the oracle, and with the residual add h bit-exact."""
+    act, wdt, epv = _fmt(fmt)
+    for ch in LOOP_CHUNKS[fmt][1 if res else 0]:
+        nvec = 2 * ch * 1024 + ch * 512 + 37
+        N, M = nvec * epv, 5
+        x, w, _ = si.random_case(M, N, act, seed=ch + 31 * res, wdtype=wdt)
+        eps = si.eps_f32(1e-6)
+        cfg = rn.rmsnorm_config(vector_path=5, lanes_per_row=1024, vecs_per_lane=ch, wg_threads=1024, grid=3)
+        _say(f"two-pass forward {fmt} res={res} chunk={ch} N={N}")
+        if res:
+            r_in = si.random_tensor((M, N), act, seed=ch + 7)
+            h, y, rstd = gpu_fwd_residual(x, r_in, w, eps, act, cfg=cfg)
+            oh, oy, orr = oracle.fwd_residual(x, r_in, w, eps, act, wdtype=wdt)
+            assert np.array_equal(widen(h, act), oh), "h differs from round(x + res)"
+        else:
+            y, rstd = gpu_fwd(x, w, eps, act, cfg=cfg)
+            oy, orr = oracle.fwd(x, w, eps, act, wdtype=wdt)
+        check_rows(y, oy, act, "y")
+        check_rstd(rstd, orr)
+
+
 # (format, M, N, residual): the ladder's own configuration
 LADDER_CASES = [("bf16", 1024, 65536, False), ("bf16", 512, 131072, False), ("f16w32", 512, 131072, False),
                 ("f32", 512, 65536, False), ("bf16", 512, 65536, True), ("bf16", 300, 131072 + 8, False),
-                ("bf16", 1, 131072, False)]
+                ("bf16", 1, 131072, False), ("bf16", 64, 262144, False), ("f32", 64, 131072, False),
+                ("bf16", 64, 98304, True)]
 
 
 @pytest.mark.parametrize("fmt,M,N,res", LADDER_CASES, ids=lambda v: str(v))
 def test_ladder_wide_rows_against_oracle(fmt, M, N, res):
-    """Forward and backward at 65536 and 131072 columns as the library picks
-    them (the backward on split rows, the forward on 1024 lanes holding 8 to
-    16 vectors each): every row of y and dx, every rstd, every dW column; the
-    backward twice, bit-identical."""
+    """Forward and backward at 65536 to 262144 columns as the library picks
+    them (the backward on split rows; the forward on 1024 lanes holding 8 to
+    16 vectors each, or beyond that the two-pass kernel): every row of y and
+    dx, every rstd, every dW column; the backward twice, bit-identical."""
     act, wdt, _ = _fmt(fmt)
     x, w, dy = si.random_case(M, N, act, seed=N + M, dy_scale=1e-2, wdtype=wdt)
     eps = si.eps_f32(1e-6)

@@ -102,6 +102,10 @@ def test_candidates_include_split_rows_and_the_widest_forward():
     assert {c.prefetch for c in tune.candidates(M, N, rn.BF16_WF32, 1, 256) if c.vector_path == 4} == {0}
     assert {(c.lanes_per_row // 1024, c.vecs_per_lane) for c in tune.candidates(M, 40960, rn.F32, 1, 256)
             if c.vector_path == 4} == {(2, 5)}
-    fwd = [c for c in tune.candidates(M, 131072, rn.BF16, 0, 256) if c.vecs_per_lane > 8]
+    fwd = [c for c in tune.candidates(M, 131072, rn.BF16, 0, 256) if c.vector_path == 1 and c.vecs_per_lane > 8]
     assert fwd and all((c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads) == (1, 1024, 16, 1024)
                        for c in fwd)
+    # the two-pass forward: every built chunk size, a workgroup per row or two per CU
+    loop = {(c.vecs_per_lane, c.grid) for c in tune.candidates(M, 262144, rn.BF16, 0, 256) if c.vector_path == 5}
+    assert loop == {(4, 4096), (8, 4096), (16, 4096), (4, 512), (8, 512), (16, 512)}
+    assert {c.vecs_per_lane for c in tune.candidates(M, 262144, rn.BF16_WF32, 0, 256) if c.vector_path == 5} == {4, 8}
