@@ -1,9 +1,11 @@
 """Python binding of the gfx950 RMSNorm library (``librmsnorm_mi355x.so``).
 
 Argument marshalling only: every function forwards to the C entry point of
-the same name declared in ``include/rmsnorm.h`` (``include/rmsnorm_probe.h``
-for the roofline probes, ``include/rmsnorm_baseline.h`` for the unfused
-reference kernels). Pointers may be given as integers (device
+the same name declared in ``include/rmsnorm.h``; the roofline probes
+(``include/rmsnorm_probe.h``) and the unfused reference kernels
+(``include/rmsnorm_baseline.h``) live in a separate measurement library,
+``librmsnorm_mi355x_bench.so``, loaded on their first use, so the product
+library carries no measurement code. Pointers may be given as integers (device
 addresses) or as torch tensors (their ``data_ptr()``); ``stream`` may be an
 integer hipStream_t, a ``torch.cuda.Stream``, or None for torch's current
 stream. A non-zero status raises ``RmsnormError``.
@@ -25,6 +27,8 @@ LIB_NAME = "librmsnorm_mi355x.so"
 # RMSNORM_MI355X_LIB selects another build of the same library (for example
 # one compiled with different flags, to compare variants); default: in-tree.
 LIB_PATH = os.environ.get("RMSNORM_MI355X_LIB") or os.path.join(_HERE, LIB_NAME)
+BENCH_LIB_NAME = "librmsnorm_mi355x_bench.so"
+BENCH_LIB_PATH = os.path.join(_HERE, BENCH_LIB_NAME)
 
 F32 = 0
 BF16 = 1
@@ -91,29 +95,55 @@ def _load() -> ctypes.CDLL:
         "rmsnorm_select_config": (i32, [i64, i64, i32, i32, i32, i32, i32, cfgp]),
         "rmsnorm_query_config": (i32, [i64, i64, i32, i32, cfgp]),
         "rmsnorm_build_info": (ctypes.c_char_p, []),
-        "rmsn_probe_copy": (i32, [vp, vp, sz, i64, i32, vp]),
-        "rmsn_probe_write": (i32, [vp, sz, i64, i32, vp]),
-        "rmsn_probe_read": (i32, [vp, sz, i64, i32, vp, vp]),
-        "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, i32, vp]),
-        "rmsn_unfused_fwd": (i32, [vp, vp, f32, i64, i64, i32, vp, vp, vp]),
-        "rmsn_unfused_bwd_workspace_bytes": (i64, [i64, i64, i32]),
-        "rmsn_unfused_bwd": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]),
-        "rmsn_add": (i32, [vp, vp, vp, i64, i32, vp]),
     }
+    _bind(lib, sig)
+    return lib
+
+
+def _bind(lib, sig):
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    return lib
 
 
 lib = _load()
+_bench = None
 
+
+def bench_lib() -> ctypes.CDLL:
+    """The measurement library (roofline probes, unfused reference kernels),
+    loaded on first use. Raises ImportError when it has not been built."""
+    global _bench
+    if _bench is None:
+        if not os.path.exists(BENCH_LIB_PATH):
+            raise ImportError(f"{BENCH_LIB_PATH} is not built; `python -c 'import __graft_entry__ as g; g.build()'` "
+                              "builds it beside the product library.")
+        b = ctypes.CDLL(BENCH_LIB_PATH)
+        vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        _bind(b, {
+            "rmsn_probe_copy": (i32, [vp, vp, sz, i64, i32, vp]),
+            "rmsn_probe_write": (i32, [vp, sz, i64, i32, vp]),
+            "rmsn_probe_read": (i32, [vp, sz, i64, i32, vp, vp]),
+            "rmsn_probe_add": (i32, [vp, vp, vp, sz, i64, i32, vp]),
+            "rmsn_unfused_fwd": (i32, [vp, vp, f32, i64, i64, i32, vp, vp, vp]),
+            "rmsn_unfused_bwd_workspace_bytes": (i64, [i64, i64, i32]),
+            "rmsn_unfused_bwd": (i32, [vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]),
+            "rmsn_add": (i32, [vp, vp, vp, i64, i32, vp]),
+        })
+        _bench = b
+    return _bench
+
+
+# entry points of the product library (include/rmsnorm.h)
 EXPORTED = (
     "rmsnorm_fwd", "rmsnorm_fwd_with_config", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
     "rmsnorm_bwd_with_config", "rmsnorm_bwd_rows", "rmsnorm_bwd_combine", "rmsnorm_fwd_residual",
     "rmsnorm_bwd_residual", "rmsnorm_bwd_noalloc", "rmsnorm_status_str",
     "rmsnorm_select_config", "rmsnorm_query_config", "rmsnorm_build_info",
+)
+# entry points of the measurement library (include/rmsnorm_probe.h, include/rmsnorm_baseline.h)
+BENCH_EXPORTED = (
     "rmsn_probe_copy", "rmsn_probe_write", "rmsn_probe_read", "rmsn_probe_add",
     "rmsn_unfused_fwd", "rmsn_unfused_bwd_workspace_bytes", "rmsn_unfused_bwd", "rmsn_add",
 )
@@ -311,37 +341,37 @@ def rmsnorm_query_config(M, N, dtype, is_bwd) -> rmsnorm_config:
 
 
 def rmsn_probe_copy(src, dst, nbytes, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_copy", lib.rmsn_probe_copy(_arg(src, "src", nbytes=int(nbytes)),
+    _check("rmsn_probe_copy", bench_lib().rmsn_probe_copy(_arg(src, "src", nbytes=int(nbytes)),
                                                   _arg(dst, "dst", nbytes=int(nbytes)), int(nbytes), int(grid),
                                                   int(variant), _stream(stream)))
 
 
 def rmsn_probe_write(dst, nbytes, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_write", lib.rmsn_probe_write(_arg(dst, "dst", nbytes=int(nbytes)), int(nbytes), int(grid),
+    _check("rmsn_probe_write", bench_lib().rmsn_probe_write(_arg(dst, "dst", nbytes=int(nbytes)), int(nbytes), int(grid),
                                                     int(variant), _stream(stream)))
 
 
 def rmsn_probe_read(src, nbytes, sink, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_read", lib.rmsn_probe_read(_arg(src, "src", nbytes=int(nbytes)), int(nbytes), int(grid),
+    _check("rmsn_probe_read", bench_lib().rmsn_probe_read(_arg(src, "src", nbytes=int(nbytes)), int(nbytes), int(grid),
                                                   int(variant), _arg(sink, "sink", nbytes=16), _stream(stream)))
 
 
 def rmsn_probe_add(a, b, c, nbytes, grid=0, variant=0, stream=None) -> None:
-    _check("rmsn_probe_add", lib.rmsn_probe_add(_arg(a, "a", nbytes=int(nbytes)), _arg(b, "b", nbytes=int(nbytes)),
+    _check("rmsn_probe_add", bench_lib().rmsn_probe_add(_arg(a, "a", nbytes=int(nbytes)), _arg(b, "b", nbytes=int(nbytes)),
                                                 _arg(c, "c", nbytes=int(nbytes)), int(nbytes), int(grid),
                                                 int(variant), _stream(stream)))
 
 
 def rmsn_unfused_fwd(x, w, eps, M, N, dtype, y, rstd, stream=None) -> None:
     mn = _mn(M, N)
-    _check("rmsn_unfused_fwd", lib.rmsn_unfused_fwd(_arg(x, "x", "act", dtype, mn),
+    _check("rmsn_unfused_fwd", bench_lib().rmsn_unfused_fwd(_arg(x, "x", "act", dtype, mn),
                                                     _arg(w, "w", "weight", dtype, int(N)), float(eps), int(M),
                                                     int(N), int(dtype), _arg(y, "y", "act", dtype, mn),
                                                     _arg(rstd, "rstd", "f32", count=int(M)), _stream(stream)))
 
 
 def rmsn_unfused_bwd_workspace_bytes(M, N, dtype) -> int:
-    n = int(lib.rmsn_unfused_bwd_workspace_bytes(int(M), int(N), int(dtype)))
+    n = int(bench_lib().rmsn_unfused_bwd_workspace_bytes(int(M), int(N), int(dtype)))
     if n < 0:
         raise RmsnormError("rmsn_unfused_bwd_workspace_bytes", n, rmsnorm_status_str(n))
     return n
@@ -349,7 +379,7 @@ def rmsn_unfused_bwd_workspace_bytes(M, N, dtype) -> int:
 
 def rmsn_unfused_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_bytes, stream=None) -> None:
     mn = _mn(M, N)
-    _check("rmsn_unfused_bwd", lib.rmsn_unfused_bwd(_arg(x, "x", "act", dtype, mn),
+    _check("rmsn_unfused_bwd", bench_lib().rmsn_unfused_bwd(_arg(x, "x", "act", dtype, mn),
                                                     _arg(w, "w", "weight", dtype, int(N)),
                                                     _arg(dy, "dy", "act", dtype, mn),
                                                     _arg(rstd, "rstd", "f32", count=int(M)), int(M), int(N),
@@ -360,5 +390,5 @@ def rmsn_unfused_bwd(x, w, dy, rstd, M, N, dtype, dx, dw, workspace, workspace_b
 
 
 def rmsn_add(a, b, c, n, dtype, stream=None) -> None:
-    _check("rmsn_add", lib.rmsn_add(_arg(a, "a", "act", dtype, int(n)), _arg(b, "b", "act", dtype, int(n)),
+    _check("rmsn_add", bench_lib().rmsn_add(_arg(a, "a", "act", dtype, int(n)), _arg(b, "b", "act", dtype, int(n)),
                                     _arg(c, "c", "act", dtype, int(n)), int(n), int(dtype), _stream(stream)))

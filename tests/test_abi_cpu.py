@@ -12,10 +12,10 @@ import memory_bound_normalization_rmsnorm_amd as rn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
+def declared_functions(headers=None):
     names = set()
     for h in os.listdir(os.path.join(ROOT, "include")):
-        if h.endswith(".h"):
+        if h.endswith(".h") and (headers is None or h in headers):
             src = open(os.path.join(ROOT, "include", h)).read()
             src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
             names |= set(re.findall(r"\b(rmsn\w*)\s*\(", src))
@@ -23,11 +23,21 @@ def declared_functions():
 
 
 def test_exports_every_declared_symbol():
-    names = declared_functions()
+    """The product library exports every function include/rmsnorm.h declares
+    and no measurement code; the measurement library exports the probes and
+    the unfused reference kernels."""
+    names = declared_functions({"rmsnorm.h"})
     assert "rmsnorm_fwd" in names and "rmsnorm_bwd" in names
     for n in names:
         assert hasattr(rn.lib, n), f"{n} declared but not exported"
     assert set(names) == set(rn.EXPORTED)
+    bench = declared_functions({"rmsnorm_probe.h", "rmsnorm_baseline.h"})
+    assert set(bench) == set(rn.BENCH_EXPORTED)
+    for n in bench:
+        assert hasattr(rn.bench_lib(), n), f"{n} declared but not exported by the measurement library"
+        with pytest.raises(AttributeError):
+            getattr(rn.lib, n)
+    assert set(declared_functions()) == set(names) | set(bench)
 
 
 def test_build_info_and_status_strings():
@@ -91,9 +101,9 @@ def test_noalloc_argument_errors():
 
 
 def test_unfused_baseline_argument_errors():
-    # the unfused reference calls take the 16-byte vector layout only; all of
-    # these are rejected before any HIP call
-    L = rn.lib
+    # the unfused reference calls (the measurement library) take the 16-byte
+    # vector layout only; all of these are rejected before any HIP call
+    L = rn.bench_lib()
     assert L.rmsn_unfused_fwd(FAKE, FAKE, 1e-5, 4, 12, rn.BF16, FAKE, FAKE, None) == rn.EINVAL   # 24 B rows
     assert L.rmsn_unfused_fwd(FAKE + 2, FAKE, 1e-5, 4, 16, rn.BF16, FAKE, FAKE, None) == rn.EINVAL
     assert L.rmsn_unfused_fwd(FAKE, FAKE, 1e-5, 4, 16, rn.BF16, FAKE, None, None) == rn.EINVAL    # rstd required
