@@ -108,6 +108,20 @@ def launch_key(cfg: dict) -> list:
                                   "stream_loads", "grid")] + ([1] if cfg.get("copy_mode") else [])
 
 
+def row_kernel_name(cfg: dict) -> str:
+    """The backward row kernel a launch configuration runs (its template's name)."""
+    vp = int(cfg["vector_path"])
+    if vp == 0:
+        return "bwd_scalar"
+    if vp == 3:
+        return "bwd_elem"
+    if vp == 4:
+        return "bwd_split"
+    if vp == 2:
+        return "bwd_wide_lds" if cfg.get("copy_mode") else "bwd_wide"
+    return "bwd_lds" if cfg.get("copy_mode") else "bwd_vec"
+
+
 def graph_launches(nbytes: int) -> int:
     """Launches per timing graph for a kernel moving `nbytes` per launch."""
     est_us = max(5.0, nbytes / (GRAPH_EST_GBPS * 1e3))
@@ -622,7 +636,7 @@ def main(argv=None):
         "config": {"workload": f"RMSNorm fwd+bwd {wl.dtype} M={M} N={N} eps={wl.eps}", "M": M, "N": N,
                    "eps": wl.eps, "rotation_sets": R, "fwd_launch": cfg_f, "bwd_launch": cfg_b},
         "roofline": {
-            "kernel": "bwd_vec (backward row kernel)",
+            "kernel": f"{row_kernel_name(cfg_b)} (backward row kernel)",
             "bound": "hbm",
             "achieved": round(rows_gbps, 1),
             "peak": HBM_PEAK_GBPS,

@@ -27,6 +27,17 @@ def test_launch_key(bench):
     assert bench.launch_key(CFG) == [1, 512, 1, 512, 2, 0, 256]
 
 
+def test_row_kernel_name(bench):
+    base = dict(vector_path=1, copy_mode=0)
+    assert bench.row_kernel_name(base) == "bwd_vec"
+    assert bench.row_kernel_name(dict(base, copy_mode=1)) == "bwd_lds"
+    assert bench.row_kernel_name(dict(vector_path=2, copy_mode=0)) == "bwd_wide"
+    assert bench.row_kernel_name(dict(vector_path=2, copy_mode=1)) == "bwd_wide_lds"
+    assert bench.row_kernel_name(dict(vector_path=3, copy_mode=0)) == "bwd_elem"
+    assert bench.row_kernel_name(dict(vector_path=4, copy_mode=0)) == "bwd_split"
+    assert bench.row_kernel_name(dict(vector_path=0, copy_mode=0)) == "bwd_scalar"
+
+
 def test_source_hash_covers_kernels_not_the_host_ladder(bench, tmp_path, monkeypatch):
     """Counters stay valid across host-only changes (the ladder, the launches)
     and not across kernel changes."""
