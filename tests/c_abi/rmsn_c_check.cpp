@@ -286,6 +286,8 @@ int main(int argc, char **argv) {
     bool ok = true;
     ok &= run_case<uint16_t>(257, 4096, true, 1);    // vector path, ragged row count
     ok &= run_case<uint16_t>(64, 32768, true, 2);    // wide-row backward
+    ok &= run_case<uint16_t>(40, 65536, true, 9);    // split-row backward (exchange slots in the workspace)
+    ok &= run_case<float>(6, 131072, false, 10);     // two-pass forward, split fp32 backward
     ok &= run_case<uint16_t>(1000, 128, true, 3);    // several rows per wavefront
     ok &= run_case<float>(33, 257, false, 4);        // element kernels (row not a multiple of 16 bytes)
     ok &= run_case<uint16_t>(9, 4100, true, 6);      // element kernels, 4 elements per access

@@ -21,7 +21,10 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("M,N,residual", [(4096, 4096, False), (1, 4096, False), (1000, 128, False),
-                                          (777, 5120, True), (333, 4100, False), (129, 4095, True)])
+                                          (777, 5120, True), (333, 4100, False), (129, 4095, True),
+                                          (300, 65536, False),   # split rows (fill kernel + exchange)
+                                          (64, 262144, False),   # two-pass forward, 16 split members
+                                          (100, 98304, True)])   # residual two-pass forward and split rows
 def test_graph_replay_matches_eager(M, N, residual):
     print(f"graph M={M} N={N} residual={residual}", flush=True)
     g = torch.Generator(device="cuda")
