@@ -320,7 +320,12 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Al
         return;
     }
     if (!is_bwd && nvec > kMaxVecLanes * vmax) {
-        set_loop_shape(kLoopChunk, c);
+        // the two-pass kernel addresses a row with 32-bit byte offsets (a 4
+        // GiB fp32 row of 2^30 columns does not fit: the scalar kernel)
+        if (nvec * 16 > (int64_t)UINT32_MAX)
+            set_scalar_shape(c);
+        else
+            set_loop_shape(kLoopChunk, c);
         return;
     }
     if (nvec > kMaxVecLanes * vmax) {
@@ -784,7 +789,8 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         return RMSN_ECONFIG;
     } else if (req->vector_path == kLoopPath) {
         // the forward's two-pass kernel: 1024 lanes, vecs_per_lane per chunk
-        if (is_bwd || !vector_ok(N, dtype, a) || req->lanes_per_row != kMaxVecLanes ||
+        if (is_bwd || !vector_ok(N, dtype, a) || N * elem_size(dtype) > (int64_t)UINT32_MAX ||
+            req->lanes_per_row != kMaxVecLanes ||
             (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes) || req->prefetch != 0 ||
             req->copy_mode != 0 || req->stream_loads < 0 || req->stream_loads > 1)
             return RMSN_ECONFIG;

@@ -294,6 +294,15 @@ def test_ladder_forward_two_pass_rows(N, dtype):
     assert (r["vector_path"], r["vecs_per_lane"]) == (1, 16)
 
 
+def test_ladder_forward_rows_beyond_32_bit_offsets():
+    """The two-pass kernel addresses a row with 32-bit byte offsets: the one
+    row size that does not fit (fp32, 2^30 columns = 4 GiB) takes the scalar
+    kernel; one vector less still takes the two-pass kernel."""
+    assert cfg(1, 1 << 30, rn.F32, 0)["vector_path"] == 0
+    assert cfg(1, (1 << 30) - 4, rn.F32, 0)["vector_path"] == 5
+    assert cfg(1, 1 << 30, rn.BF16, 0)["vector_path"] == 5
+
+
 def test_explicit_loop_config_errors():
     """Two-pass configurations (vector_path 5) are forward only, on 1024 lanes,
     without prefetch or LDS copies, and only for built chunk sizes."""
