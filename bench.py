@@ -356,7 +356,7 @@ def main(argv=None):
     if args.mode == "cells":
         return run_cells(args, torch, rn, timer)
 
-    wl = si.WORKLOADS[args.workload]
+    wl = si.workload(args.workload)
     dt = rn.F32 if wl.dtype == "f32" else rn.BF16
     tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     M, N = wl.M, wl.N

@@ -18,6 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import threading
 
 import numpy as np
 
@@ -33,7 +34,7 @@ _STORAGE = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64, "f16": np.f
 def build(source: str = SOURCE, out: str = LIB_PATH, extra_flags=()) -> str:
     """Compile the oracle with gcc into a shared library and return its path."""
     os.makedirs(os.path.dirname(out), exist_ok=True)
-    tmp = out + ".tmp"
+    tmp = f"{out}.tmp{os.getpid()}"
     cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-Wall", "-Werror",
            *extra_flags, source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
@@ -147,16 +148,20 @@ class Oracle:
 
 
 _default = None
+_lock = threading.Lock()
 
 
 def get() -> Oracle:
-    """The oracle built from ``rmsnorm_oracle.c`` (compiled on first use if absent)."""
+    """The oracle built from ``rmsnorm_oracle.c`` (compiled on first use if
+    absent). Thread-safe: the first callers of a process (for instance the
+    worker threads of a row-blocked comparison) build and load it once."""
     global _default
-    if _default is None:
-        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
-            build()
-        _default = Oracle(LIB_PATH)
-    return _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
+                build()
+            _default = Oracle(LIB_PATH)
+        return _default
 
 
 def fwd(x, w, eps, dtype, rows=None, want_y=True, wdtype=None):

@@ -129,6 +129,27 @@ WORKLOADS = {
 }
 
 
+# Rows wider than one workgroup holds (the backward's split rows, the forward's
+# 16 vectors per lane and its two-pass kernel): benchmarked and profiled with
+# `bench.py --workload`, and checked at full size, beside the workloads above.
+WIDE_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("bf16_4096x65536", "bf16", 4096, 65536, 1e-5, "uniform", 1e-2, 540,
+                 description="wide row bf16 4096x65536, eps 1e-5; x~N(0,1), w~U(0.5,1.5), dy~1e-2 N(0,1)"),
+        Workload("bf16_1024x262144", "bf16", 1024, 262144, 1e-5, "uniform", 1e-2, 550,
+                 description="wide row bf16 1024x262144, eps 1e-5; x~N(0,1), w~U(0.5,1.5), dy~1e-2 N(0,1)"),
+    ]
+}
+
+
+def workload(name: str) -> Workload:
+    """A workload of WORKLOADS or WIDE_WORKLOADS by name."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    return WIDE_WORKLOADS[name]
+
+
 def _normal_f32(seed: int, shape) -> np.ndarray:
     return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape, dtype=np.float32)
 

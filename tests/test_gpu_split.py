@@ -239,3 +239,30 @@ def test_ladder_wide_rows_against_oracle(fmt, M, N, res):
         dx2, dw2 = gpu_bwd(x, w, dy, rstd, act)
     assert np.array_equal(dw.view(np.uint32), dw2.view(np.uint32)), "dW differs between two runs"
     assert np.array_equal(dx.view(np.uint8), dx2.view(np.uint8)), "dx differs between two runs"
+
+
+@pytest.mark.parametrize("name", list(si.WIDE_WORKLOADS))
+def test_full_size_wide_workload(name):
+    """The wide-row workloads the benchmark can time (bf16 4096x65536: split
+    rows over 4 workgroups, the forward at 8 vectors per lane; bf16
+    1024x262144: 16 split-row members, the two-pass forward) at full size in
+    the ladder's configuration: every row of y and dx against the oracle,
+    every rstd, every dW column."""
+    wl = si.WIDE_WORKLOADS[name]
+    _say(f"wide workload {name}: generating inputs")
+    x, w, dy = si.make_inputs(wl)
+    eps = si.eps_f32(wl.eps)
+    _say(f"wide workload {name}: gpu")
+    y, rstd = gpu_fwd(x, w, eps, wl.dtype)
+    dx, dw = gpu_bwd(x, w, dy, rstd, wl.dtype)
+    _say(f"wide workload {name}: oracle, every row")
+    orr = np.empty(wl.M)
+    for rows, oy, r, odx in oracle_row_blocks(x, w, dy, eps, wl.dtype, block=128):
+        orr[rows] = r
+        check_rows(y[rows], oy, wl.dtype, "y")
+        idx = np.arange(rows.start, rows.stop)
+        check_rows(dx[rows], odx, wl.dtype, "dx", floor=term_rms(x, w, dy, r, wl.dtype, rows=idx))
+    check_rstd(rstd, orr)
+    check_dw(dw, oracle.bwd_dw(x, dy, eps, wl.dtype), wl.dtype)
+    assert np.all(np.isfinite(widen(y, wl.dtype))) and np.all(np.isfinite(widen(dx, wl.dtype)))
+
