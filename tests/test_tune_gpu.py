@@ -18,7 +18,8 @@ from parity_util import check_dw, check_rows, check_rstd, gpu_bwd, gpu_fwd, term
 
 
 @pytest.mark.parametrize("is_bwd", [0, 1])
-@pytest.mark.parametrize("M,N", [(2048, 1024), (1000, 4100)])   # 4100: the element kernels
+@pytest.mark.parametrize("M,N", [(2048, 1024), (1000, 4100),   # 4100: the element kernels
+                                 (64, 65536), (16, 262144)])   # split rows; the two-pass forward
 def test_tuned_config_is_correct_and_cached(is_bwd, M, N, tmp_path):
     dtype = "bf16"
     print(f"tune M={M} N={N} is_bwd={is_bwd}", flush=True)
