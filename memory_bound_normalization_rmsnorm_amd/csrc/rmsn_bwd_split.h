@@ -41,9 +41,19 @@ struct SplitSlot {
     uint64_t word[2];
 };
 
-// Polls of a partner's word before giving up (each poll followed by a short
-// sleep); far beyond any real wait (microseconds), well under a second.
+// Polls of partners' words over a member's whole walk before it gives up
+// (each poll a device-scope load and a short sleep, about a microsecond):
+// about a second in all, far beyond any real wait (microseconds).
 constexpr uint32_t kSplitSpinLimit = 1u << 20;
+
+// Weight vectors per lane kept in registers at two workgroups per CU. Keeping
+// the two of a 16-bit row costs a 12-16 byte spill at 64 VGPRs, and still
+// measured 5-7% faster than re-reading them from cache each row without the
+// spill (bf16 4096 x 65536: 297.3 against 318.0 us; 1024 x 262144: 387.1
+// against 411.0; the residual backward 373.3 against 391.3).
+#ifndef RMSN_SPLIT_KEEP_W_TWO
+#define RMSN_SPLIT_KEEP_W_TWO 2
+#endif
 
 // Waves per SIMD a member asks for: two workgroups per CU (64 VGPRs each)
 // when its dW sums take at most 64 KiB of LDS (2 vectors of 8 16-bit
@@ -61,9 +71,10 @@ bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict
     constexpr int EPV = E::kPerVec;
     constexpr int Q = EPV / 4;  // float4 words of dW sums per vector
     // weights kept in registers as by the wide-row kernel; at two workgroups
-    // per CU (64 VGPRs) only up to 2 weight vectors per lane
+    // per CU (64 VGPRs) only up to RMSN_SPLIT_KEEP_W_TWO weight vectors per lane
     constexpr bool kTwoPerCU = split_waves_per_eu(VPT, EPV) > kWideLanes / 256;
-    constexpr bool kKeepW = wide_keeps_w<T, TW, VPT, PF>() && (!kTwoPerCU || VPT * WV::kVecs <= 2);
+    constexpr bool kKeepW =
+        wide_keeps_w<T, TW, VPT, PF>() && (!kTwoPerCU || VPT * WV::kVecs <= RMSN_SPLIT_KEEP_W_TWO);
     static_assert(VPT * EPV * LPR * 4 <= kWideLdsBytes, "dW sums must fit in LDS");
     __shared__ float slots[2 * (LPR / 64)];
     __shared__ float total[2];
