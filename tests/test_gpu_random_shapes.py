@@ -47,12 +47,17 @@ def _cases(n=48, seed=20261202, max_elems=3 << 20):
 # Fixed cases for the families a random draw rarely reaches: whole-wavefront
 # backward rows (320, 384, 640 and 768 lanes), the mid-size forward grid, the
 # element kernels at 2 and 4 elements per access (4100 and 4098 columns; the
-# 16-bit forward on a resident grid), and the resident forward grid of fp32
-# weights (more than 8 row blocks per compute unit).
+# 16-bit forward on a resident grid), the resident forward grid of fp32
+# weights (more than 8 row blocks per compute unit), and rows wider than a
+# workgroup: split-row backwards of 3 to 13 members (two per CU for 16-bit
+# rows, one per CU for fp32), the two-pass forward (plain and residual), and
+# an unvectorisable row beyond the element kernels (the scalar kernels).
 CASES = _cases() + [(2048, 2560, "bf16", False), (1000, 3072, "f16", True), (600, 5120, "bf16", False),
                     (500, 6144, "f16", True), (2048, 4096, "f16", False), (4096, 2048, "bf16w32", False),
                     (3000, 4100, "bf16", False), (777, 4098, "f32", True), (1500, 2050, "bf16w32", False),
-                    (4500, 4096, "f16w32", False)]
+                    (4500, 4096, "f16w32", False),
+                    (40, 36864, "f32", False), (20, 49160, "bf16", False), (12, 131080, "f16", True),
+                    (6, 200000, "bf16w32", False), (5, 70000, "f32", True), (3, 300001, "f32", False)]
 
 
 def _say(msg):
