@@ -217,7 +217,10 @@ int rmsnorm_bwd_combine(const void *workspace, int64_t partial_rows, int64_t N, 
  * other fields are derived. For searching the configuration space ("What a tuned RMSNorm
  * kernel actually costs on Hopper", section 06: the memory-path knobs belong
  * in the search space). Returns RMSN_ECONFIG when the configuration does not
- * cover the row or its kernel is not built. The backward workspace must hold
+ * cover the row or its kernel is not built, or (split rows) when the grid is
+ * more workgroups than the current device keeps resident at once, which is
+ * the one check that queries the device (occupancy; nothing is launched
+ * before it). The backward workspace must hold
  * grid * partial_stride floats (partial_stride = N rounded up to 64); split
  * rows (vector_path 4): (grid / K) * partial_stride floats, then 16 bytes per
  * workgroup rounded up to 256 (the exchange slots, zeroed by the call). dW
