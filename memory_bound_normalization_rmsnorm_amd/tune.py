@@ -199,7 +199,8 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
         for K in sorted(ks):
             if K > SPLIT_MAX:
                 continue
-            vpt = -(-(-(-nvec // K)) // WIDE_LANES)
+            slice_vecs = -(-nvec // K)  # vectors of each member's column slice
+            vpt = -(-slice_vecs // WIDE_LANES)
             if vpt not in SPLIT_BUILT[dtype]:
                 continue
             per_cu = 2 if vpt <= two else 1
