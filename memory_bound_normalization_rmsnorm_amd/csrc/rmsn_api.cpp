@@ -397,9 +397,9 @@ int deep_prefetch(int is_bwd, int64_t N, int dtype, const rmsnorm_config *c) {
 
 // Wide rows (the wide-row kernel) with 16-bit activations and weights over
 // walks of at least kWideLongWalk rows per compute unit: two workgroups per CU
-// (past what stays resident at 4 vectors per lane, whose dW sums fill LDS:
-// the second half of the grid then runs as the first drains), no prefetch at
-// 2 or 3 vectors per lane. Measured (whole rmsnorm_bwd calls, graph-timed,
+// (past what stays resident at 3 or 4 vectors per lane, whose dW sums leave
+// LDS for one: the second half of the grid then runs as the first drains),
+// no prefetch at 2 or 3 vectors per lane. Measured (whole rmsnorm_bwd calls, graph-timed,
 // rotating inputs; bf16): 16384 x 16384 286.1 -> 273.0 us, 32768 x 16384
 // 577.6 -> 534.6, 32768 x 24576 844.0 -> 819.2, 16384 x 32768 593.2 -> 566.1,
 // 32768 x 32768 1162.1 -> 1105.5; fp16 likewise. Shorter walks keep one
