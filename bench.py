@@ -763,6 +763,7 @@ def run_cells(args, torch, rn, timer):
         rn.rmsn_probe_read(flush_a, GIB, flush_sink, 0)
 
     rows, failures = [], []
+    sized = {}  # size-matched probes per tensor size
     for group in groups:
         for name, fmt, M, N in CELL_GROUPS[group]:
             act, es, wsz = FMT[fmt]
@@ -836,12 +837,21 @@ def run_cells(args, torch, rn, timer):
                     rec[which + "_GBps"] = round(nbytes / (best * 1e-6) / 1e9, 1)
                     rec[which + "_pct_roofline"] = round(100 * nbytes / (best * 1e-6) / 1e9 / measured, 1)
                     rec[which + "_bytes"] = nbytes
+                if not small:
+                    # against streaming probes on tensors of the cell's own size: copy for the
+                    # forward, 2-read-1-write for the backward
+                    tb = M * N * es
+                    if tb not in sized:
+                        sized[tb] = size_matched_probes(torch, rn, tb)
+                    rec["fwd_pct_size_matched"] = round(100 * rec["fwd_GBps"] / sized[tb]["copy_GBps"], 1)
+                    rec["bwd_pct_size_matched"] = round(100 * rec["bwd_GBps"] / sized[tb]["2r1w_GBps"], 1)
                 rows.append(rec)
                 log(json.dumps(rec))
             del sets, base, ws, dw, ref
             torch.cuda.empty_cache()
     del flush_a, flush_sink
     out = {"mode": "cells", "roofline": roof, "cells": rows, "parity_failures": failures,
+           "size_matched": {str(k): v for k, v in sized.items()},
            "timing": f"cells under {SMALL_CELL_BYTES >> 20} MiB per rotation set: the median of "
                      f"{args.isolated_reps} single calls, each between two HIP events after a 1 GiB "
                      "cache-flushing read (warm graph-replay times beside them); larger cells: rotation "
