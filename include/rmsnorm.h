@@ -93,8 +93,9 @@ typedef struct {
                                 device at once); 5: the forward's two-pass kernel (rows
                                 wider than 16 vectors per lane on 1024 lanes, 8 with the
                                 residual add: one row per 1024-lane workgroup, read in chunks
-                                of vecs_per_lane = 4, 8 or 16 (residual: 4 or 8) vectors per
-                                lane, twice); 3: element kernel (rows
+                                of vecs_per_lane vectors per lane; the first kept_vecs vectors
+                                per lane stay in registers between the passes, the rest is read
+                                twice); 3: element kernel (rows
                                 that are not a multiple of 16 bytes or not 16-byte aligned,
                                 up to 16384 columns: lanes_per_row = wg_threads = 64, 128, 256,
                                 512 or 1024, vecs_per_lane accesses of elems_per_access
@@ -129,6 +130,14 @@ typedef struct {
                                 6, 8), 1024 lanes (2-4) and whole-wavefront rows on the
                                 workgroup (2-4); with the fused residual add 2-3 stages (512
                                 lanes: 2, 3, 4, 6). 0 on every other path */
+    int32_t kept_vecs;       /* two-pass forward (vector_path 5): vectors per lane kept in
+                                registers from the first pass for the second, a multiple of
+                                vecs_per_lane. Built as (vecs_per_lane, kept_vecs): 16-bit
+                                (4, 0), (8, 0), (16, 0), (4, 16), (4, 12), residual (4, 0),
+                                (8, 0), (2, 16), (4, 12); fp32 (4, 0), (8, 0), (16, 0), (2, 14),
+                                (4, 12), residual (4, 0), (8, 0), (2, 12), (4, 8); 16-bit with
+                                fp32 weights (4, 0), (8, 0), (2, 14), residual (4, 0), (8, 0),
+                                (4, 8). 0 on every other path */
     int64_t grid;            /* workgroups launched */
     int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid; split
                                 rows: grid / K, one per group of K workgroups) */

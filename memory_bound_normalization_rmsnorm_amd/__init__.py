@@ -63,6 +63,7 @@ class rmsnorm_config(ctypes.Structure):
         ("stream_loads", ctypes.c_int32),
         ("elems_per_access", ctypes.c_int32),
         ("copy_mode", ctypes.c_int32),
+        ("kept_vecs", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("partial_rows", ctypes.c_int64),
         ("partial_stride", ctypes.c_int64),

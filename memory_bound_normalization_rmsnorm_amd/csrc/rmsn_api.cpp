@@ -151,11 +151,36 @@ constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row bac
 constexpr int kSplitPath = 4;  // rmsnorm_config::vector_path of the split-row backward kernels
 constexpr int kFwdXWideVecs = 16;  // vectors per lane of the widest plain forward rows
 constexpr int kLoopPath = 5;  // rmsnorm_config::vector_path of the forward's two-pass kernels
-// Vectors per lane per chunk the ladder picks for them: 4 (two workgroups per
-// CU) was the fastest or tied against 8 and 16 (graph-timed, rotating inputs;
-// bf16 1024 x 262144 246.6 us against 258.0 and 284.1, with the residual add
-// 534.5 against 600.3; fp32 2048 x 131072 502.7 against 502.5 and 564.7).
-constexpr int kLoopChunk = 4;
+// The chunk and the vectors kept in registers between the passes (both in
+// vectors per lane) that the ladder picks for them: the most each format
+// keeps without spilling, at one workgroup per CU, and with the residual
+// add, for 16-bit rows of at most 12 vectors per lane, a shape that keeps
+// the whole row. Graph-timed, rotating inputs, against chunks of 4 with
+// nothing kept at two workgroups per CU (which had been the fastest or tied
+// against chunks of 8 and 16): bf16 1024 x 262144 242.2 -> 224.5 us, 4096 x
+// 262144 952.2 -> 889.8, 2048 x 196608 352.3 -> 287.1; fp32 2048 x 131072
+// 501.1 -> 434.3; bf16 with fp32 weights 1024 x 262144 277.3 -> 226.8; with
+// the residual add bf16 1024 x 262144 524.3 -> 485.2 and 2048 x 98304 345.4 ->
+// 285.4, fp32 2048 x 65536 471.7 -> 389.9, fp16 with fp32 weights 2048 x
+// 98304 351.0 -> 283.8. Every shape's outputs are bit-identical.
+void loop_choice(int dtype, int res, int64_t nvec, int *ch, int *kv) {
+    const bool w32 = dtype == RMSN_BF16_WF32 || dtype == RMSN_F16_WF32;
+    if (!res) {
+        *ch = dtype == RMSN_F32 || w32 ? 2 : 4;
+        *kv = dtype == RMSN_F32 || w32 ? 14 : 16;
+    } else if (w32) {
+        *ch = 4;
+        *kv = 8;
+    } else if (dtype == RMSN_F32) {
+        *ch = 2;
+        *kv = 12;
+    } else {
+        const bool whole = nvec <= 12 * kMaxVecLanes;
+        *ch = whole ? 4 : 2;
+        *kv = whole ? 12 : 16;
+    }
+}
+
 constexpr int kCopyLds = 1;   // rmsnorm_config::copy_mode of the LDS-staged backward kernels
 constexpr int kMaxLdsStages = 8;
 constexpr int kLdsStages = 2;  // LDS stages the ladder picks
@@ -274,10 +299,11 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
 }
 
 // Forward two-pass rows: one row per 1024-lane workgroup, `ch` vectors per
-// lane per chunk (rmsn_fwd_loop.h).
-void set_loop_shape(int ch, rmsnorm_config *c) {
+// lane per chunk, `kv` of them kept in registers (rmsn_fwd_loop.h).
+void set_loop_shape(int ch, int kv, rmsnorm_config *c) {
     set_vector_shape(kMaxVecLanes, ch, rmsn::kWideLanes, 0, c);
     c->vector_path = kLoopPath;
+    c->kept_vecs = kv;
 }
 
 // Split rows of two workgroups per CU: vectors per lane of the slices (their
@@ -322,10 +348,13 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Al
     if (!is_bwd && nvec > kMaxVecLanes * vmax) {
         // the two-pass kernel addresses a row with 32-bit byte offsets (a 4
         // GiB fp32 row of 2^30 columns does not fit: the scalar kernel)
-        if (nvec * 16 > (int64_t)UINT32_MAX)
+        if (nvec * 16 > (int64_t)UINT32_MAX) {
             set_scalar_shape(c);
-        else
-            set_loop_shape(kLoopChunk, c);
+        } else {
+            int ch = 0, kv = 0;
+            loop_choice(dtype, res, nvec, &ch, &kv);
+            set_loop_shape(ch, kv, c);
+        }
         return;
     }
     if (nvec > kMaxVecLanes * vmax) {
@@ -638,7 +667,7 @@ const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd
         if (is_bwd || c.copy_mode != 0 || c.lanes_per_row != kMaxVecLanes || c.wg_threads != rmsn::kWideLanes ||
             c.prefetch != 0)
             return nullptr;
-        const KernelEntry *e = rmsn::fwd_loop_kernel(dtype, res, c.vecs_per_lane);
+        const KernelEntry *e = rmsn::fwd_loop_kernel(dtype, res, c.vecs_per_lane, c.kept_vecs);
         return e ? e->fn : nullptr;
     }
     if (c.vector_path == kSplitPath) {
@@ -775,6 +804,7 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     std::memset(c, 0, sizeof *c);
     if (req->grid < 1 || req->grid > INT32_MAX) return RMSN_ECONFIG;
     if (req->vector_path < 0 || req->vector_path > kLoopPath) return RMSN_ECONFIG;
+    if (req->kept_vecs != 0 && req->vector_path != kLoopPath) return RMSN_ECONFIG;
     if (req->vector_path == kElemPath) {
         const int64_t k = req->vecs_per_lane;
         const int64_t g = req->elems_per_access ? req->elems_per_access : elem_group(N, dtype, a);
@@ -792,9 +822,9 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         if (is_bwd || !vector_ok(N, dtype, a) || N * elem_size(dtype) > (int64_t)UINT32_MAX ||
             req->lanes_per_row != kMaxVecLanes ||
             (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes) || req->prefetch != 0 ||
-            req->copy_mode != 0 || req->stream_loads < 0 || req->stream_loads > 1)
+            req->copy_mode != 0 || req->stream_loads < 0 || req->stream_loads > 1 || req->kept_vecs < 0)
             return RMSN_ECONFIG;
-        set_loop_shape(req->vecs_per_lane, c);
+        set_loop_shape(req->vecs_per_lane, req->kept_vecs, c);
     } else if (req->vector_path == kSplitPath) {
         // K = lanes_per_row / 1024 members per row; the grid whole groups,
         // all resident at once on the current device

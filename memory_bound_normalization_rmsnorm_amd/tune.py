@@ -56,8 +56,12 @@ LDS_BUILT = {(256, 1024): (2, 3, 4), (512, 512): (2, 3, 4, 6, 8), (1024, 1024): 
 WIDE_LDS_BUILT = ((1024, 2, 1), (1024, 2, 2), (1024, 3, 1), (512, 4, 1), (512, 4, 2), (512, 6, 1))
 # vectors per lane of the plain forward's widest rows (1024 lanes)
 FWD_XWIDE_VPT = 16
-# chunk sizes (vectors per lane) of the plain forward's two-pass kernels (vector_path 5)
-FWD_LOOP_CHUNKS = {BF16: (4, 8, 16), F16: (4, 8, 16), F32: (4, 8, 16), BF16_WF32: (4, 8), F16_WF32: (4, 8)}
+# the plain forward's two-pass kernels (vector_path 5): (chunk, vectors kept in
+# registers between the passes), both in vectors per lane
+_LOOP_16 = ((4, 0), (8, 0), (16, 0), (4, 16), (4, 12))
+_LOOP_W32 = ((4, 0), (8, 0), (2, 14))
+FWD_LOOP_BUILT = {BF16: _LOOP_16, F16: _LOOP_16, F32: ((4, 0), (8, 0), (16, 0), (2, 14), (4, 12)),
+                  BF16_WF32: _LOOP_W32, F16_WF32: _LOOP_W32}
 # split-row backward kernels (vector_path 4): per format, vectors per lane -> prefetch variants
 SPLIT_MAX = 16
 SPLIT_BUILT = {
@@ -179,13 +183,13 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             for sl in (0, 1):
                 out.append(rmsnorm_config(vector_path=1, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
                                           wg_threads=WIDE_LANES, stream_loads=sl, grid=g))
-    # the forward's two-pass kernel, every built chunk size, for rows beyond
-    # 8 vectors per lane (beyond 16 it is the only vector kernel)
+    # the forward's two-pass kernel, every built (chunk, kept) pair, for rows
+    # beyond 8 vectors per lane (beyond 16 it is the only vector kernel)
     if not is_bwd and nvec > WIDE_LANES * MAX_VPT:
-        for ch in FWD_LOOP_CHUNKS[dtype]:
+        for ch, kv in FWD_LOOP_BUILT[dtype]:
             for g in sorted(x for x in {M, 2 * num_cus} if 1 <= x <= M):
                 out.append(rmsnorm_config(vector_path=5, lanes_per_row=WIDE_LANES, vecs_per_lane=ch,
-                                          wg_threads=WIDE_LANES, grid=g))
+                                          wg_threads=WIDE_LANES, kept_vecs=kv, grid=g))
     # backward rows beyond the wide kernels: split over K workgroups, the
     # fewest K whose slices fit at one and at two members per CU, and one
     # more of each, every built prefetch; groups of K as many as stay resident
@@ -217,7 +221,7 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
 
 def _key(c: rmsnorm_config):
     return (c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads, c.prefetch, c.grid, c.stream_loads,
-            c.elems_per_access, c.copy_mode)
+            c.elems_per_access, c.copy_mode, c.kept_vecs)
 
 
 class _Bench:

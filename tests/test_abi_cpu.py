@@ -276,18 +276,22 @@ def test_explicit_config_errors():
     assert fwd(vector_path=2, lanes_per_row=1024, vecs_per_lane=1, wg_threads=1024) == rn.ECONFIG  # backward only
     assert fwd(vector_path=3) == rn.ECONFIG
     assert fwd(prefetch=2) == rn.ECONFIG
+    assert fwd(kept_vecs=16) == rn.ECONFIG   # a field of the two-pass kernel only
 
 
 @pytest.mark.parametrize("N,dtype", [(131072 + 8, rn.BF16), (65536 + 4, rn.F32), (1 << 20, rn.BF16_WF32),
                                      (1 << 22, rn.F16)])
 def test_ladder_forward_two_pass_rows(N, dtype):
     """Forward rows wider than 16 vectors on each of 1024 lanes: the two-pass
-    kernel (vector_path 5), one row per 1024-lane workgroup, 4 vectors per
-    lane per chunk, a workgroup per row."""
+    kernel (vector_path 5), one row per 1024-lane workgroup, a workgroup per
+    row; 16-bit rows in chunks of 4 vectors per lane with 16 kept in
+    registers between the passes, fp32 activations or weights in chunks of 2
+    with 14 kept (the most each keeps without spilling)."""
+    ch, kv = (2, 14) if dtype in (rn.F32, rn.BF16_WF32, rn.F16_WF32) else (4, 16)
     for M in (1, 300, 4096):
         c = cfg(M, N, dtype, 0)
-        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"]) == \
-            (5, 1024, 4, 1024, 0)
+        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"],
+                c["kept_vecs"]) == (5, 1024, ch, 1024, 0, kv)
         assert c["grid"] == M and c["rows_per_wg"] == 1
     # one vector per lane fewer: the register-held row
     r = cfg(64, 131072 if dtype != rn.F32 else 65536, dtype, 0)
@@ -321,6 +325,9 @@ def test_explicit_loop_config_errors():
     assert fwd(copy_mode=1) == rn.ECONFIG
     assert fwd(vecs_per_lane=5) == rn.ECONFIG      # not built
     assert fwd(grid=0) == rn.ECONFIG
+    assert fwd(kept_vecs=8) == rn.ECONFIG          # not built for chunks of 8
+    assert fwd(vecs_per_lane=4, kept_vecs=14) == rn.ECONFIG   # not whole chunks
+    assert fwd(vecs_per_lane=4, kept_vecs=-4) == rn.ECONFIG
     c = C(vector_path=5, lanes_per_row=1024, vecs_per_lane=8, wg_threads=1024, grid=4)
     assert L.rmsnorm_bwd_with_config(FAKE, FAKE, FAKE, FAKE, M, N, rn.BF16, FAKE, FAKE, FAKE, 1 << 30, c,
                                      None) == rn.ECONFIG

@@ -9,7 +9,8 @@ the C ABI:
     in use), groups without rows, and K from 2 to 16;
   * the plain forward's rows of 9 to 16 vectors per lane on 1024 lanes;
   * the forward's two-pass kernels (vector_path 5: rows beyond those, read
-    in chunks, twice), every built chunk size, plain and residual-fused;
+    in chunks, the first ones kept in registers, the rest read twice), every
+    built (chunk, kept) pair, plain and residual-fused;
   * the ladder's own choice at 65536 and 131072 columns (bf16, fp16 with fp32
     weights, fp32, the residual-fused pair), every row and every dW column,
     and dW bit-identical on reruns.
@@ -162,42 +163,59 @@ def test_forward_rows_of_9_to_16_vectors_per_lane(fmt):
         check_rstd(rstd, orr)
 
 
-# chunk sizes (vectors per lane) of the two-pass forward kernels per format (rmsn_instances.h)
-LOOP_CHUNKS = {"bf16": ([4, 8, 16], [4, 8]), "f16": ([4, 8, 16], [4, 8]), "f32": ([4, 8, 16], [4, 8]),
-               "bf16w32": ([4, 8], [4, 8]), "f16w32": ([4, 8], [4, 8])}
+# (chunk, kept) pairs (vectors per lane) of the two-pass forward kernels per
+# format, plain and residual-fused (rmsn_instances.h)
+_L16 = [(4, 0), (8, 0), (16, 0), (4, 16), (4, 12)]
+_R16 = [(4, 0), (8, 0), (2, 16), (4, 12)]
+LOOP_SHAPES = {"bf16": (_L16, _R16), "f16": (_L16, _R16),
+               "f32": ([(4, 0), (8, 0), (16, 0), (2, 14), (4, 12)], [(4, 0), (8, 0), (2, 12), (4, 8)]),
+               "bf16w32": ([(4, 0), (8, 0), (2, 14)], [(4, 0), (8, 0), (4, 8)]),
+               "f16w32": ([(4, 0), (8, 0), (2, 14)], [(4, 0), (8, 0), (4, 8)])}
+
+
+def _loop_rows(ch, kv):
+    """Row lengths (vectors) for a two-pass shape: the kept chunks full, then
+    two and a half reloaded chunks and a ragged wavefront; and for shapes that
+    keep vectors, a row that ends inside the kept part (nothing reloaded)."""
+    rows = [kv * 1024 + 2 * ch * 1024 + ch * 512 + 37]
+    if kv:
+        rows.append(kv * 1024 - ch * 512 - 37)
+    return rows
 
 
 @pytest.mark.parametrize("res", [False, True], ids=["plain", "residual"])
-@pytest.mark.parametrize("fmt", list(LOOP_CHUNKS))
+@pytest.mark.parametrize("fmt", list(LOOP_SHAPES))
 def test_every_forward_two_pass_kernel(fmt, res):
-    """Every built chunk size on a row of two and a half chunks plus a ragged
-    wavefront, 5 rows on 3 workgroups (a workgroup takes a second row): y and
-    rstd against the oracle, and with the residual add h bit-exact."""
+    """Every built (chunk, kept) pair, 5 rows on 3 workgroups (a workgroup
+    takes a second row), on rows that reload chunks after the kept ones and
+    rows that end inside the kept part: y and rstd against the oracle, and
+    with the residual add h bit-exact."""
     act, wdt, epv = _fmt(fmt)
-    for ch in LOOP_CHUNKS[fmt][1 if res else 0]:
-        nvec = 2 * ch * 1024 + ch * 512 + 37
-        N, M = nvec * epv, 5
-        x, w, _ = si.random_case(M, N, act, seed=ch + 31 * res, wdtype=wdt)
-        eps = si.eps_f32(1e-6)
-        cfg = rn.rmsnorm_config(vector_path=5, lanes_per_row=1024, vecs_per_lane=ch, wg_threads=1024, grid=3)
-        _say(f"two-pass forward {fmt} res={res} chunk={ch} N={N}")
-        if res:
-            r_in = si.random_tensor((M, N), act, seed=ch + 7)
-            h, y, rstd = gpu_fwd_residual(x, r_in, w, eps, act, cfg=cfg)
-            oh, oy, orr = oracle.fwd_residual(x, r_in, w, eps, act, wdtype=wdt)
-            assert np.array_equal(widen(h, act), oh), "h differs from round(x + res)"
-        else:
-            y, rstd = gpu_fwd(x, w, eps, act, cfg=cfg)
-            oy, orr = oracle.fwd(x, w, eps, act, wdtype=wdt)
-        check_rows(y, oy, act, "y")
-        check_rstd(rstd, orr)
+    for ch, kv in LOOP_SHAPES[fmt][1 if res else 0]:
+        for nvec in _loop_rows(ch, kv):
+            N, M = nvec * epv, 5
+            x, w, _ = si.random_case(M, N, act, seed=ch + kv + 31 * res, wdtype=wdt)
+            eps = si.eps_f32(1e-6)
+            cfg = rn.rmsnorm_config(vector_path=5, lanes_per_row=1024, vecs_per_lane=ch, wg_threads=1024,
+                                    kept_vecs=kv, grid=3)
+            _say(f"two-pass forward {fmt} res={res} chunk={ch} kept={kv} N={N}")
+            if res:
+                r_in = si.random_tensor((M, N), act, seed=ch + kv + 7)
+                h, y, rstd = gpu_fwd_residual(x, r_in, w, eps, act, cfg=cfg)
+                oh, oy, orr = oracle.fwd_residual(x, r_in, w, eps, act, wdtype=wdt)
+                assert np.array_equal(widen(h, act), oh), "h differs from round(x + res)"
+            else:
+                y, rstd = gpu_fwd(x, w, eps, act, cfg=cfg)
+                oy, orr = oracle.fwd(x, w, eps, act, wdtype=wdt)
+            check_rows(y, oy, act, "y")
+            check_rstd(rstd, orr)
 
 
 # (format, M, N, residual): the ladder's own configuration
 LADDER_CASES = [("bf16", 1024, 65536, False), ("bf16", 512, 131072, False), ("f16w32", 512, 131072, False),
                 ("f32", 512, 65536, False), ("bf16", 512, 65536, True), ("bf16", 300, 131072 + 8, False),
                 ("bf16", 1, 131072, False), ("bf16", 64, 262144, False), ("f32", 64, 131072, False),
-                ("bf16", 64, 98304, True)]
+                ("bf16", 64, 98304, True), ("bf16", 64, 131072 + 8, True), ("f32", 64, 65536, True)]
 
 
 @pytest.mark.parametrize("fmt,M,N,res", LADDER_CASES, ids=lambda v: str(v))
