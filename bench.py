@@ -103,9 +103,12 @@ def source_hash() -> str:
 
 
 def launch_key(cfg: dict) -> list:
-    """The fields of a launch configuration that decide a kernel's traffic."""
+    """The fields of a launch configuration that decide a kernel's traffic: a
+    trailing 1 for the LDS-staged backward (copy_mode 1), or the two-pass
+    forward's vectors per lane kept in registers."""
     return [int(cfg[k]) for k in ("vector_path", "lanes_per_row", "vecs_per_lane", "wg_threads", "prefetch",
-                                  "stream_loads", "grid")] + ([1] if cfg.get("copy_mode") else [])
+                                  "stream_loads", "grid")] + ([1] if cfg.get("copy_mode") else []) + \
+        ([int(cfg["kept_vecs"])] if cfg.get("kept_vecs") else [])
 
 
 def row_kernel_name(cfg: dict) -> str:

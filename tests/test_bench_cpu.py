@@ -25,6 +25,9 @@ CFG = {"vector_path": 1, "lanes_per_row": 512, "vecs_per_lane": 1, "wg_threads":
 
 def test_launch_key(bench):
     assert bench.launch_key(CFG) == [1, 512, 1, 512, 2, 0, 256]
+    loop = dict(CFG, vector_path=5, lanes_per_row=1024, vecs_per_lane=4, wg_threads=1024, prefetch=0, grid=64,
+                kept_vecs=16)
+    assert bench.launch_key(loop) == [5, 1024, 4, 1024, 0, 0, 64, 16]
 
 
 def test_row_kernel_name(bench):
