@@ -8,13 +8,13 @@
  * page "Profiling, GPU utilisation and writing a fused kernel", Problem 15
  * ("The concepts").
  *
- * Backward: with V_ij = dy_ij * w_j ("the incoming gradient after applying the
- * gain", "RMSNorm backward (almost) without the column reduction", section
+ * Backward: with V_ij = dy_ij * w_j, the upstream gradient scaled by the
+ * weight ("RMSNorm backward (almost) without the column reduction", section
  * "The backward pass"),
  *     dx_ij = rstd_i * V_ij - x_ij * rstd_i^3 * (sum_j V_ij x_ij) / N
  *     dW_j  = sum_i dy_ij * x_ij * rstd_i
- * The page's formula images are lost; this is the derivative of the forward
- * and matches the page's kernels. dW is reduced without atomics in a fixed
+ * This is the derivative of the forward, written out here; it matches what
+ * the page's kernels compute. dW is reduced without atomics in a fixed
  * order, so it is bit-identical from run to run on the same device (same
  * page, section "The problem: summing across rows"). The backward reads the
  * fp32 rstd the forward wrote, as the Quack study describes its backward

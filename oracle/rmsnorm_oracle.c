@@ -18,11 +18,11 @@
  *       y_ij = x_ij * r_i * w_j              (w is per column, shared by rows)
  *
  *   Backward -- "RMSNorm backward (almost) without the column reduction",
- *   sections "The backward pass" and "The naive kernel". The page's formula
- *   images are lost; the expression below is the derivative of the forward
- *   definition (d r_i / d x_ik = -r_i^3 x_ik / N), which is also what the
- *   page's kernels compute:
- *       V_ij  = dy_ij * w_j                  ("incoming gradient after the gain")
+ *   sections "The backward pass" and "The naive kernel". The expression
+ *   below is written out as the derivative of the forward definition
+ *   (d r_i / d x_ik = -r_i^3 x_ik / N); it is also what the page's kernels
+ *   compute:
+ *       V_ij  = dy_ij * w_j                  (the upstream gradient times the weight)
  *       S_i   = sum_j V_ij * x_ij
  *       dx_ij = r_i * V_ij - x_ij * r_i^3 * S_i / N
  *       dW_j  = sum_i dy_ij * x_ij * r_i     (rows ascending)
