@@ -18,8 +18,9 @@
 // Exchange: member k of group g owns slot g * K + k, two 64-bit words. For
 // its i-th row it stores, in one relaxed atomic store at device scope, the
 // word (i + 1) << 32 | bits(part) into word[i & 1]; readers poll their
-// partners' word[i & 1] with relaxed atomic loads at device scope until its
-// high half reads i + 1, and take the low half. Tag and value travel in one
+// partners' word[i & 1] with relaxed atomic loads at device scope (one lane
+// per partner, all partners in each polling round) until the high half reads
+// i + 1, and take the low half. Tag and value travel in one
 // word, so no fence orders them, and device-scope accesses are coherent
 // across the XCDs' separate L2 caches. Two words suffice: a member reaches
 // its row i + 2 only after every partner published row i + 1, which each
@@ -41,9 +42,10 @@ struct SplitSlot {
     uint64_t word[2];
 };
 
-// Polls of partners' words over a member's whole walk before it gives up
-// (each poll a device-scope load and a short sleep, about a microsecond):
-// about a second in all, far beyond any real wait (microseconds).
+// Polling rounds over a member's whole walk before it gives up (each round a
+// device-scope load per partner not yet seen and a short sleep, about a
+// microsecond): about a second in all, far beyond any real wait
+// (microseconds).
 constexpr uint32_t kSplitSpinLimit = 1u << 20;
 
 // Weight vectors per lane kept in registers at two workgroups per CU. Keeping
@@ -127,7 +129,7 @@ bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict
     SplitSlot *const group = xch + g * K;
     int parity = 0;
     uint32_t it = 0;
-    uint32_t spins = 0;  // polls so far (lane 0) over the whole walk; at the limit every later sum is NaN
+    uint32_t spins = 0;  // polling rounds so far (wavefront 0) over the whole walk; at the limit every later sum is NaN
     int64_t row = g;
     u32x4 xn[VPT], gn[VPT];
     float rn = 0.f;
@@ -164,26 +166,32 @@ bwd_split(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict
         s = row_sum<LPR, LPR>(s, slots, parity);
         parity ^= 1;
         // Publish this slice's part, wait for the others, add all K in member
-        // order; one lane does it and hands the sum to the workgroup.
-        if (lane == 0) {
+        // order. Wavefront 0 does it: lane p < K polls member p's word, all
+        // partners at once, until every tag reads this row's; the K parts are
+        // then added in member order and handed to the workgroup.
+        if (lane < 64) {
             const uint64_t tag = (uint64_t)(it + 1u) << 32;
-            __hip_atomic_store(&mine->word[it & 1u], tag | as_u32(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            float t = 0.f;
-            for (int p = 0; p < K; ++p) {
-                float part = s;
-                if (p != k) {
-                    uint64_t v = 0;
-                    while (spins < kSplitSpinLimit) {
-                        v = __hip_atomic_load(&group[p].word[it & 1u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if ((v & ~uint64_t(0xffffffffu)) == tag) break;
-                        ++spins;
-                        __builtin_amdgcn_s_sleep(2);
+            if (lane == 0)
+                __hip_atomic_store(&mine->word[it & 1u], tag | as_u32(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool ready = lane >= K || lane == k;
+            float part = s;
+            while (spins < kSplitSpinLimit) {
+                if (!ready) {
+                    const uint64_t v =
+                        __hip_atomic_load(&group[lane].word[it & 1u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((v & ~uint64_t(0xffffffffu)) == tag) {
+                        ready = true;
+                        part = __uint_as_float((uint32_t)v);
                     }
-                    part = spins < kSplitSpinLimit ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
                 }
-                t += part;
+                if (__all(ready)) break;
+                ++spins;
+                __builtin_amdgcn_s_sleep(2);
             }
-            total[it & 1u] = t;
+            if (!ready) part = __builtin_nanf("");
+            float t = 0.f;
+            for (int p = 0; p < K; ++p) t += __shfl(part, p);
+            if (lane == 0) total[it & 1u] = t;
         }
         __syncthreads();
         const float S = total[it & 1u];
