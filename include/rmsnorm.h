@@ -94,8 +94,9 @@ typedef struct {
                                 wider than 16 vectors per lane on 1024 lanes, 8 with the
                                 residual add: one row per 1024-lane workgroup, read in chunks
                                 of vecs_per_lane vectors per lane; the first kept_vecs vectors
-                                per lane stay in registers between the passes, the rest is read
-                                twice); 3: element kernel (rows
+                                per lane stay in registers between the passes, with copy_mode 1
+                                the next 8 in LDS, and the rest is read twice); 3: element
+                                kernel (rows
                                 that are not a multiple of 16 bytes or not 16-byte aligned,
                                 up to 16384 columns: lanes_per_row = wg_threads = 64, 128, 256,
                                 512 or 1024, vecs_per_lane accesses of elems_per_access
@@ -120,8 +121,10 @@ typedef struct {
                                 elems_per_access is at most 16 and covers N / 1024. The ladder
                                 takes the largest; 0 in an explicit element configuration asks
                                 for that one. 0 on the other paths */
-    int32_t copy_mode;       /* backward, vector path, one vector per lane: how the row blocks
-                                ahead arrive. 0: loaded into registers (the register ring);
+    int32_t copy_mode;       /* two-pass forward (vector_path 5): 1 holds 8 vectors per lane
+                                after the kept ones in LDS (128 KiB) between the passes, 0
+                                none. Backward, vector path, one vector per lane: how the row
+                                blocks ahead arrive. 0: loaded into registers (the register ring);
                                 1: copied global->LDS by 16-byte direct-to-LDS loads into a ring
                                 of `prefetch` LDS stages ("What a tuned RMSNorm kernel actually
                                 costs on Hopper", sections 06 and 09: the copy path and the
@@ -132,12 +135,15 @@ typedef struct {
                                 lanes: 2, 3, 4, 6). 0 on every other path */
     int32_t kept_vecs;       /* two-pass forward (vector_path 5): vectors per lane kept in
                                 registers from the first pass for the second, a multiple of
-                                vecs_per_lane. Built as (vecs_per_lane, kept_vecs): 16-bit
-                                (4, 0), (8, 0), (16, 0), (4, 16), (4, 12), residual (4, 0),
-                                (8, 0), (2, 16), (4, 12); fp32 (4, 0), (8, 0), (16, 0), (2, 14),
-                                (4, 12), residual (4, 0), (8, 0), (2, 12), (4, 8); 16-bit with
-                                fp32 weights (4, 0), (8, 0), (2, 14), residual (4, 0), (8, 0),
-                                (4, 8). 0 on every other path */
+                                vecs_per_lane. Built as (vecs_per_lane, kept_vecs, copy_mode):
+                                16-bit (4, 0, 0), (8, 0, 0), (16, 0, 0), (4, 16, 0), (4, 12, 0),
+                                (2, 16, 1), (4, 16, 1), (4, 12, 1), residual (4, 0, 0),
+                                (8, 0, 0), (2, 16, 0), (4, 12, 0), (2, 16, 1), (4, 12, 1); fp32
+                                (4, 0, 0), (8, 0, 0), (16, 0, 0), (2, 14, 0), (4, 12, 0),
+                                (2, 14, 1), residual (4, 0, 0), (8, 0, 0), (2, 12, 0), (4, 8, 0),
+                                (2, 12, 1); 16-bit with fp32 weights (4, 0, 0), (8, 0, 0),
+                                (2, 14, 0), (2, 10, 1), residual (4, 0, 0), (8, 0, 0), (4, 8, 0),
+                                (4, 8, 1). 0 on every other path */
     int64_t grid;            /* workgroups launched */
     int64_t partial_rows;    /* backward: fp32 dW partial rows in the workspace (= grid; split
                                 rows: grid / K, one per group of K workgroups) */

@@ -151,37 +151,58 @@ constexpr int kWidePath = 2;  // rmsnorm_config::vector_path of the wide-row bac
 constexpr int kSplitPath = 4;  // rmsnorm_config::vector_path of the split-row backward kernels
 constexpr int kFwdXWideVecs = 16;  // vectors per lane of the widest plain forward rows
 constexpr int kLoopPath = 5;  // rmsnorm_config::vector_path of the forward's two-pass kernels
-// The chunk and the vectors kept in registers between the passes (both in
-// vectors per lane) that the ladder picks for them: the most each format
-// keeps without spilling, at one workgroup per CU, and with the residual
-// add, for 16-bit rows of at most 12 vectors per lane, a shape that keeps
-// the whole row. Graph-timed, rotating inputs, against chunks of 4 with
-// nothing kept at two workgroups per CU (which had been the fastest or tied
-// against chunks of 8 and 16): bf16 1024 x 262144 242.2 -> 224.5 us, 4096 x
-// 262144 952.2 -> 889.8, 2048 x 196608 352.3 -> 287.1; fp32 2048 x 131072
-// 501.1 -> 434.3; bf16 with fp32 weights 1024 x 262144 277.3 -> 226.8; with
-// the residual add bf16 1024 x 262144 524.3 -> 485.2 and 2048 x 98304 345.4 ->
-// 285.4, fp32 2048 x 65536 471.7 -> 389.9, fp16 with fp32 weights 2048 x
-// 98304 351.0 -> 283.8. Every shape's outputs are bit-identical.
-void loop_choice(int dtype, int res, int64_t nvec, int *ch, int *kv) {
+// vectors per lane the two-pass kernels with copy_mode 1 hold in LDS (128 KiB)
+constexpr int kLoopLdsVecs = 8;
+// The two-pass kernel's shape the ladder picks, by format, residual add and
+// v = vectors per lane of the row: the chunk, the vectors kept in registers
+// between the passes (the most each format keeps without spilling at one
+// workgroup per CU) and whether the next kLoopLdsVecs are held in LDS.
+// Holding pays where much of the row would be read again; a remainder of up
+// to about 4-6 vectors per lane is cheaper to read again from the cache.
+// Graph-timed, rotating inputs, us (every shape's outputs bit-identical):
+//   16-bit:   v = 20: (4, 16) 225.6, (4, 12) + LDS 232.0; v = 22: 267.0 and
+//             257.3; v = 24 (bf16 2048 x 196608): 288.1 and 272.2; v = 32
+//             (1024 x 262144): (4, 16) 225.0, (2, 16) + LDS 193.6, (4, 12) +
+//             LDS 218.0; 4096 x 262144: 901.4 and 794.1.
+//   fp32:     v = 18: (2, 14) 228.0, + LDS 239.8; v = 20: 252.2 and 257.6;
+//             v = 24: 313.8 and 297.4; v = 32: 424.6 and 396.3.
+//   16-bit with fp32 weights: v = 18: (2, 14) 235.8, (2, 10) + LDS 244.7;
+//             v = 20: 246.8 and 245.7; v = 32: 229.9 and 221.5.
+//   residual, 16-bit: v <= 12 keeps the whole row at (4, 12); v = 16 (2, 16)
+//             407.6 (whole row); v = 20: 503.6 against (4, 12) + LDS 473.0;
+//             v = 28: 777.4 and 675.5; v = 32: 462.8 and 430.4.
+//   residual, fp32: v = 18: (2, 12) 459.7, + LDS 484.9; v = 20: 503.4 and
+//             515.7; v = 32: 502.9 and 461.5.
+//   residual, fp32 weights: (4, 8) + LDS 381.2 against 420.4 without (v =
+//             16), 587.8 against 637.4 (v = 24), ties at v = 12 and 32.
+// Against the earlier choice of chunks of 4 with nothing kept, at two
+// workgroups per CU: bf16 1024 x 262144 242.2 us, 4096 x 262144 952.2, 2048 x
+// 196608 352.3; fp32 2048 x 131072 501.1; residual bf16 1024 x 262144 524.3.
+void loop_choice(int dtype, int res, int64_t nvec, int *ch, int *kv, int *lds) {
     const bool w32 = dtype == RMSN_BF16_WF32 || dtype == RMSN_F16_WF32;
+    const int64_t v = (nvec + kMaxVecLanes - 1) / kMaxVecLanes;
+    auto pick = [&](int c, int k, int l) {
+        *ch = c;
+        *kv = k;
+        *lds = l;
+    };
     if (!res) {
-        *ch = dtype == RMSN_F32 || w32 ? 2 : 4;
-        *kv = dtype == RMSN_F32 || w32 ? 14 : 16;
+        if (w32)
+            v <= 20 ? pick(2, 14, 0) : pick(2, 10, 1);
+        else if (dtype == RMSN_F32)
+            v <= 20 ? pick(2, 14, 0) : pick(2, 14, 1);
+        else
+            v <= 20 ? pick(4, 16, 0) : v <= 28 ? pick(4, 12, 1) : pick(2, 16, 1);
     } else if (w32) {
-        *ch = 4;
-        *kv = 8;
+        pick(4, 8, 1);
     } else if (dtype == RMSN_F32) {
-        *ch = 2;
-        *kv = 12;
+        v <= 20 ? pick(2, 12, 0) : pick(2, 12, 1);
     } else {
-        const bool whole = nvec <= 12 * kMaxVecLanes;
-        *ch = whole ? 4 : 2;
-        *kv = whole ? 12 : 16;
+        v <= 12 ? pick(4, 12, 0) : v <= 16 ? pick(2, 16, 0) : pick(4, 12, 1);
     }
 }
 
-constexpr int kCopyLds = 1;   // rmsnorm_config::copy_mode of the LDS-staged backward kernels
+constexpr int kCopyLds = 1;   // rmsnorm_config::copy_mode of the LDS-staged kernels (backward rings, two-pass forward)
 constexpr int kMaxLdsStages = 8;
 constexpr int kLdsStages = 2;  // LDS stages the ladder picks
 constexpr int kElemPath = 3;  // rmsnorm_config::vector_path of the element kernels
@@ -299,11 +320,13 @@ int64_t rowwg_lanes(int64_t M, int64_t nvec, int dtype, int64_t cus) {
 }
 
 // Forward two-pass rows: one row per 1024-lane workgroup, `ch` vectors per
-// lane per chunk, `kv` of them kept in registers (rmsn_fwd_loop.h).
-void set_loop_shape(int ch, int kv, rmsnorm_config *c) {
+// lane per chunk, `kv` of them kept in registers and, with `lds`, the next
+// kLoopLdsVecs held in LDS (copy_mode 1; rmsn_fwd_loop.h).
+void set_loop_shape(int ch, int kv, int lds, rmsnorm_config *c) {
     set_vector_shape(kMaxVecLanes, ch, rmsn::kWideLanes, 0, c);
     c->vector_path = kLoopPath;
     c->kept_vecs = kv;
+    c->copy_mode = lds ? kCopyLds : 0;
 }
 
 // Split rows of two workgroups per CU: vectors per lane of the slices (their
@@ -351,9 +374,9 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Al
         if (nvec * 16 > (int64_t)UINT32_MAX) {
             set_scalar_shape(c);
         } else {
-            int ch = 0, kv = 0;
-            loop_choice(dtype, res, nvec, &ch, &kv);
-            set_loop_shape(ch, kv, c);
+            int ch = 0, kv = 0, lds = 0;
+            loop_choice(dtype, res, nvec, &ch, &kv, &lds);
+            set_loop_shape(ch, kv, lds, c);
         }
         return;
     }
@@ -664,10 +687,11 @@ const void *kernel_for(const rmsnorm_config &c, int64_t N, int dtype, int is_bwd
     if (!c.vector_path) return rmsn::scalar_kernel(dtype, is_bwd, res, N <= rmsn::kScalarLdsCols ? 1 : 0);
     if (c.vector_path == kElemPath) return rmsn::elem_kernel(dtype, is_bwd, res, c.vecs_per_lane, c.elems_per_access, c.lanes_per_row);
     if (c.vector_path == kLoopPath) {
-        if (is_bwd || c.copy_mode != 0 || c.lanes_per_row != kMaxVecLanes || c.wg_threads != rmsn::kWideLanes ||
-            c.prefetch != 0)
+        if (is_bwd || (c.copy_mode != 0 && c.copy_mode != kCopyLds) || c.lanes_per_row != kMaxVecLanes ||
+            c.wg_threads != rmsn::kWideLanes || c.prefetch != 0)
             return nullptr;
-        const KernelEntry *e = rmsn::fwd_loop_kernel(dtype, res, c.vecs_per_lane, c.kept_vecs);
+        const KernelEntry *e =
+            rmsn::fwd_loop_kernel(dtype, res, c.vecs_per_lane, c.kept_vecs, c.copy_mode ? kLoopLdsVecs : 0);
         return e ? e->fn : nullptr;
     }
     if (c.vector_path == kSplitPath) {
@@ -822,9 +846,10 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
         if (is_bwd || !vector_ok(N, dtype, a) || N * elem_size(dtype) > (int64_t)UINT32_MAX ||
             req->lanes_per_row != kMaxVecLanes ||
             (req->wg_threads != 0 && req->wg_threads != rmsn::kWideLanes) || req->prefetch != 0 ||
-            req->copy_mode != 0 || req->stream_loads < 0 || req->stream_loads > 1 || req->kept_vecs < 0)
+            (req->copy_mode != 0 && req->copy_mode != kCopyLds) || req->stream_loads < 0 || req->stream_loads > 1 ||
+            req->kept_vecs < 0)
             return RMSN_ECONFIG;
-        set_loop_shape(req->vecs_per_lane, req->kept_vecs, c);
+        set_loop_shape(req->vecs_per_lane, req->kept_vecs, req->copy_mode, c);
     } else if (req->vector_path == kSplitPath) {
         // K = lanes_per_row / 1024 members per row; the grid whole groups,
         // all resident at once on the current device

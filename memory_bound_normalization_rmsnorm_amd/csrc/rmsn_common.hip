@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(256) fill_zero(float *__restrict__ p, int64_t 
     const KernelEntry *bwd_lds_kernel_##tag(int res, int lpr, int wg, int st);           \
     const KernelEntry *bwd_wide_lds_kernel_##tag(int lpr, int vpt, int st);            \
     const KernelEntry *bwd_split_kernel_##tag(int res, int vpt, int pf);               \
-    const KernelEntry *fwd_loop_kernel_##tag(int res, int ch, int kv);
+    const KernelEntry *fwd_loop_kernel_##tag(int res, int ch, int kv, int lv);
 RMSN_FORMATS(RMSN_DECL)
 #undef RMSN_DECL
 
@@ -135,13 +135,13 @@ const KernelEntry *bwd_lds_kernel(int dtype, int res, int lpr, int wg, int st) {
     }
 }
 
-const KernelEntry *fwd_loop_kernel(int dtype, int res, int ch, int kv) {
+const KernelEntry *fwd_loop_kernel(int dtype, int res, int ch, int kv, int lv) {
     switch (dtype) {
-    case 0: return fwd_loop_kernel_f32(res, ch, kv);
-    case 1: return fwd_loop_kernel_bf16(res, ch, kv);
-    case 2: return fwd_loop_kernel_f16(res, ch, kv);
-    case 3: return fwd_loop_kernel_bf16w32(res, ch, kv);
-    case 4: return fwd_loop_kernel_f16w32(res, ch, kv);
+    case 0: return fwd_loop_kernel_f32(res, ch, kv, lv);
+    case 1: return fwd_loop_kernel_bf16(res, ch, kv, lv);
+    case 2: return fwd_loop_kernel_f16(res, ch, kv, lv);
+    case 3: return fwd_loop_kernel_bf16w32(res, ch, kv, lv);
+    case 4: return fwd_loop_kernel_f16w32(res, ch, kv, lv);
     default: return nullptr;
     }
 }

@@ -31,7 +31,7 @@ struct LoadAux {
     static constexpr int value = A;
 };
 
-template <typename T, typename TW, bool RES, int CH, int WPE, int KV>
+template <typename T, typename TW, bool RES, int CH, int WPE, int KV, int LV>
 __global__ void __launch_bounds__(kWideLanes) __attribute__((amdgpu_waves_per_eu(WPE)))
 fwd_loop(const T *__restrict__ x, const T *__restrict__ res, const TW *__restrict__ w, T *__restrict__ h,
          T *__restrict__ y, float *__restrict__ rstd, float eps, int64_t M, int32_t N, int32_t nvec,
@@ -40,10 +40,13 @@ fwd_loop(const T *__restrict__ x, const T *__restrict__ res, const TW *__restric
     using WV = WeightVec<T, TW>;
     constexpr int LPR = kWideLanes;
     constexpr int EPV = E::kPerVec;
-    static_assert(KV % CH == 0, "whole chunks are kept");
+    static_assert(KV % CH == 0 && LV % CH == 0, "whole chunks are kept");
     constexpr int KEEP = KV / CH;           // chunks kept in registers
     constexpr int KC = KEEP > 0 ? KEEP : 1;
+    constexpr int HOLD = LV / CH;           // chunks after those held in LDS
+    static_assert(LV * LPR * 16 <= kWideLdsBytes, "held chunks fit in LDS");
     __shared__ float slots[2 * (LPR / 64)];
+    __shared__ u32x4 held[LV > 0 ? LV * LPR : 1];  // lane l's vector v at v * LPR + l
 
     const int lane = threadIdx.x;
     const float n = (float)N;
@@ -122,7 +125,14 @@ fwd_loop(const T *__restrict__ x, const T *__restrict__ res, const TW *__restric
             const int c0 = ci * CH * LPR;
             uint32_t off[CH];
             u32x4 v[CH];
-            load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_NARROW_LOAD_AUX>{});
+            if (ci < KEEP + HOLD) {
+                // held in this lane's own LDS slots for pass 2, so no barrier
+                load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_LOAD_AUX>{});
+#pragma unroll
+                for (int k = 0; k < CH; ++k) held[((ci - KEEP) * CH + k) * LPR + lane] = v[k];
+            } else {
+                load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_NARROW_LOAD_AUX>{});
+            }
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 if constexpr (RES) hb.store16<RMSN_FWD_STORE_AUX>(off[k], v[k]);
@@ -149,7 +159,13 @@ fwd_loop(const T *__restrict__ x, const T *__restrict__ res, const TW *__restric
             const int c0 = ci * CH * LPR;
             uint32_t off[CH];
             u32x4 v[CH];
-            load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_LOAD_AUX>{});
+            if (ci < KEEP + HOLD) {
+                chunk_offsets(c0, off);
+#pragma unroll
+                for (int k = 0; k < CH; ++k) v[k] = held[((ci - KEEP) * CH + k) * LPR + lane];
+            } else {
+                load_chunk(xb, rb, c0, off, v, LoadAux<RMSN_FWD_LOAD_AUX>{});
+            }
             finish_chunk(yb, r, c0, off, v);
         }
     }

@@ -89,16 +89,20 @@
 // 16 vectors per lane on 1024 lanes, 8 with the residual add): the two-pass
 // kernel (rmsn_fwd_loop.h), as (vectors per lane per chunk, waves per SIMD:
 // 8 for two workgroups per CU, 4 for one, vectors per lane kept in registers
-// between the passes), per format (16-bit, fp32, 16-bit with fp32 weights),
-// plain and residual-fused. The kept vectors are the most each format holds
-// without spilling at one workgroup per CU; the shapes that keep none run two
-// per CU wherever the kernel fits 64 VGPRs.
-#define RMSN_FWD_LOOP_SHAPES_16(X) X(4, 8, 0) X(8, 8, 0) X(16, 4, 0) X(4, 4, 16) X(4, 4, 12)
-#define RMSN_FWD_LOOP_SHAPES_32(X) X(4, 8, 0) X(8, 4, 0) X(16, 4, 0) X(2, 4, 14) X(4, 4, 12)
-#define RMSN_FWD_LOOP_SHAPES_W32(X) X(4, 8, 0) X(8, 8, 0) X(2, 4, 14)
-#define RMSN_FWD_LOOP_RES_SHAPES_16(X) X(4, 8, 0) X(8, 4, 0) X(2, 4, 16) X(4, 4, 12)
-#define RMSN_FWD_LOOP_RES_SHAPES_32(X) X(4, 8, 0) X(8, 4, 0) X(2, 4, 12) X(4, 4, 8)
-#define RMSN_FWD_LOOP_RES_SHAPES_W32(X) X(4, 4, 0) X(8, 4, 0) X(4, 4, 8)
+// between the passes, vectors per lane held in LDS after those), per format
+// (16-bit, fp32, 16-bit with fp32 weights), plain and residual-fused. The
+// kept vectors are the most each format holds without spilling at one
+// workgroup per CU; the held ones fill 128 KiB of LDS. The shapes that keep
+// none run two per CU wherever the kernel fits 64 VGPRs.
+#define RMSN_FWD_LOOP_SHAPES_16(X) X(4, 8, 0, 0) X(8, 8, 0, 0) X(16, 4, 0, 0) X(4, 4, 16, 0) X(4, 4, 12, 0) \
+    X(2, 4, 16, 8) X(4, 4, 16, 8) X(4, 4, 12, 8)
+#define RMSN_FWD_LOOP_SHAPES_32(X) X(4, 8, 0, 0) X(8, 4, 0, 0) X(16, 4, 0, 0) X(2, 4, 14, 0) X(4, 4, 12, 0) \
+    X(2, 4, 14, 8)
+#define RMSN_FWD_LOOP_SHAPES_W32(X) X(4, 8, 0, 0) X(8, 8, 0, 0) X(2, 4, 14, 0) X(2, 4, 10, 8)
+#define RMSN_FWD_LOOP_RES_SHAPES_16(X) X(4, 8, 0, 0) X(8, 4, 0, 0) X(2, 4, 16, 0) X(4, 4, 12, 0) X(2, 4, 16, 8) \
+    X(4, 4, 12, 8)
+#define RMSN_FWD_LOOP_RES_SHAPES_32(X) X(4, 8, 0, 0) X(8, 4, 0, 0) X(2, 4, 12, 0) X(4, 4, 8, 0) X(2, 4, 12, 8)
+#define RMSN_FWD_LOOP_RES_SHAPES_W32(X) X(4, 4, 0, 0) X(8, 4, 0, 0) X(4, 4, 8, 0) X(4, 4, 8, 8)
 
 // Backward rows split over K workgroups (rmsn_bwd_split.h), as (vectors per
 // lane, prefetch). Two workgroups per CU: 2 vectors per lane of 16-bit

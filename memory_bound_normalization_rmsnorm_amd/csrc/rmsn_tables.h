@@ -52,6 +52,7 @@ struct KernelEntry {
     int pf;          // 1: next row's loads issued before the current row's arithmetic
     const void *fn;  // __global__ function
     int kv = 0;      // two-pass forward: vectors per lane kept in registers between the passes
+    int lv = 0;      // two-pass forward: vectors per lane held in LDS after the kept ones
 };
 
 // dtype: an rmsn_dtype code (activation and weight formats); res: 1 for the
@@ -71,8 +72,9 @@ const KernelEntry *bwd_wide_lds_kernel(int dtype, int lpr, int vpt, int st);
 // `vpt` vectors per lane of the workgroup's slice
 const KernelEntry *bwd_split_kernel(int dtype, int res, int vpt, int pf);
 // forward rows beyond the vector kernels: the two-pass kernel of `ch` vectors
-// per lane per chunk, `kv` of them kept in registers (rmsn_fwd_loop.h)
-const KernelEntry *fwd_loop_kernel(int dtype, int res, int ch, int kv);
+// per lane per chunk, `kv` of them kept in registers and the next `lv` held
+// in LDS (rmsn_fwd_loop.h)
+const KernelEntry *fwd_loop_kernel(int dtype, int res, int ch, int kv, int lv);
 // bytes of one workgroup's exchange slot of the split backward
 constexpr int kSplitSlotBytes = 16;
 // most workgroups a split row may take

@@ -57,10 +57,12 @@ WIDE_LDS_BUILT = ((1024, 2, 1), (1024, 2, 2), (1024, 3, 1), (512, 4, 1), (512, 4
 # vectors per lane of the plain forward's widest rows (1024 lanes)
 FWD_XWIDE_VPT = 16
 # the plain forward's two-pass kernels (vector_path 5): (chunk, vectors kept in
-# registers between the passes), both in vectors per lane
-_LOOP_16 = ((4, 0), (8, 0), (16, 0), (4, 16), (4, 12))
-_LOOP_W32 = ((4, 0), (8, 0), (2, 14))
-FWD_LOOP_BUILT = {BF16: _LOOP_16, F16: _LOOP_16, F32: ((4, 0), (8, 0), (16, 0), (2, 14), (4, 12)),
+# registers between the passes, both in vectors per lane; copy_mode 1: the next
+# 8 held in LDS)
+_LOOP_16 = ((4, 0, 0), (8, 0, 0), (16, 0, 0), (4, 16, 0), (4, 12, 0), (2, 16, 1), (4, 16, 1), (4, 12, 1))
+_LOOP_W32 = ((4, 0, 0), (8, 0, 0), (2, 14, 0), (2, 10, 1))
+FWD_LOOP_BUILT = {BF16: _LOOP_16, F16: _LOOP_16,
+                  F32: ((4, 0, 0), (8, 0, 0), (16, 0, 0), (2, 14, 0), (4, 12, 0), (2, 14, 1)),
                   BF16_WF32: _LOOP_W32, F16_WF32: _LOOP_W32}
 # split-row backward kernels (vector_path 4): per format, vectors per lane -> prefetch variants
 SPLIT_MAX = 16
@@ -183,13 +185,13 @@ def candidates(M: int, N: int, dtype: int, is_bwd: int, num_cus: int, default: r
             for sl in (0, 1):
                 out.append(rmsnorm_config(vector_path=1, lanes_per_row=WIDE_LANES, vecs_per_lane=vpt,
                                           wg_threads=WIDE_LANES, stream_loads=sl, grid=g))
-    # the forward's two-pass kernel, every built (chunk, kept) pair, for rows
+    # the forward's two-pass kernel, every built (chunk, kept, LDS) shape, for rows
     # beyond 8 vectors per lane (beyond 16 it is the only vector kernel)
     if not is_bwd and nvec > WIDE_LANES * MAX_VPT:
-        for ch, kv in FWD_LOOP_BUILT[dtype]:
+        for ch, kv, lds in FWD_LOOP_BUILT[dtype]:
             for g in sorted(x for x in {M, 2 * num_cus} if 1 <= x <= M):
                 out.append(rmsnorm_config(vector_path=5, lanes_per_row=WIDE_LANES, vecs_per_lane=ch,
-                                          wg_threads=WIDE_LANES, kept_vecs=kv, grid=g))
+                                          wg_threads=WIDE_LANES, kept_vecs=kv, copy_mode=lds, grid=g))
     # backward rows beyond the wide kernels: split over K workgroups, the
     # fewest K whose slices fit at one and at two members per CU, and one
     # more of each, every built prefetch; groups of K as many as stay resident

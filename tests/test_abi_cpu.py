@@ -280,18 +280,28 @@ def test_explicit_config_errors():
 
 
 @pytest.mark.parametrize("N,dtype", [(131072 + 8, rn.BF16), (65536 + 4, rn.F32), (1 << 20, rn.BF16_WF32),
-                                     (1 << 22, rn.F16)])
+                                     (1 << 22, rn.F16), (163840, rn.BF16), (163840 + 8, rn.BF16),
+                                     (229376, rn.F16), (229376 + 8, rn.BF16), (81920, rn.F32), (81920 + 4, rn.F32),
+                                     (163840, rn.F16_WF32), (163840 + 8, rn.BF16_WF32)])
 def test_ladder_forward_two_pass_rows(N, dtype):
     """Forward rows wider than 16 vectors on each of 1024 lanes: the two-pass
     kernel (vector_path 5), one row per 1024-lane workgroup, a workgroup per
-    row; 16-bit rows in chunks of 4 vectors per lane with 16 kept in
-    registers between the passes, fp32 activations or weights in chunks of 2
-    with 14 kept (the most each keeps without spilling)."""
-    ch, kv = (2, 14) if dtype in (rn.F32, rn.BF16_WF32, rn.F16_WF32) else (4, 16)
+    row. Up to 20 vectors per lane: 16-bit rows in chunks of 4 with 16 kept
+    in registers between the passes, fp32 activations or weights in chunks of
+    2 with 14 kept (the most each keeps without spilling). Wider: 8 more held
+    in LDS (copy_mode 1), 16-bit rows of 21-28 vectors per lane keeping 12,
+    wider ones 16 in chunks of 2; fp32 14; fp32 weights 10."""
+    v = -(-(N * (4 if dtype == rn.F32 else 2) // 16) // 1024)
+    if dtype == rn.F32:
+        want = (2, 14, 0) if v <= 20 else (2, 14, 1)
+    elif dtype in (rn.BF16_WF32, rn.F16_WF32):
+        want = (2, 14, 0) if v <= 20 else (2, 10, 1)
+    else:
+        want = (4, 16, 0) if v <= 20 else (4, 12, 1) if v <= 28 else (2, 16, 1)
     for M in (1, 300, 4096):
         c = cfg(M, N, dtype, 0)
-        assert (c["vector_path"], c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"],
-                c["kept_vecs"]) == (5, 1024, ch, 1024, 0, kv)
+        assert (c["vector_path"], c["lanes_per_row"], c["wg_threads"], c["prefetch"]) == (5, 1024, 1024, 0)
+        assert (c["vecs_per_lane"], c["kept_vecs"], c["copy_mode"]) == want
         assert c["grid"] == M and c["rows_per_wg"] == 1
     # one vector per lane fewer: the register-held row
     r = cfg(64, 131072 if dtype != rn.F32 else 65536, dtype, 0)
@@ -309,7 +319,8 @@ def test_ladder_forward_rows_beyond_32_bit_offsets():
 
 def test_explicit_loop_config_errors():
     """Two-pass configurations (vector_path 5) are forward only, on 1024 lanes,
-    without prefetch or LDS copies, and only for built chunk sizes."""
+    without prefetch, with copy_mode 0 or 1 (LDS-held vectors), and only for
+    built (chunk, kept, LDS) shapes."""
     L, C = rn.lib, rn.rmsnorm_config
     M, N = 64, 262144
 
@@ -322,10 +333,12 @@ def test_explicit_loop_config_errors():
     assert fwd(lanes_per_row=512) == rn.ECONFIG
     assert fwd(wg_threads=512) == rn.ECONFIG
     assert fwd(prefetch=1) == rn.ECONFIG
-    assert fwd(copy_mode=1) == rn.ECONFIG
     assert fwd(vecs_per_lane=5) == rn.ECONFIG      # not built
     assert fwd(grid=0) == rn.ECONFIG
     assert fwd(kept_vecs=8) == rn.ECONFIG          # not built for chunks of 8
+    assert fwd(copy_mode=1) == rn.ECONFIG          # nothing kept: no LDS-held shape built
+    assert fwd(copy_mode=2) == rn.ECONFIG
+    assert fwd(vecs_per_lane=2, kept_vecs=14, copy_mode=1) == rn.ECONFIG   # built for fp32 only
     assert fwd(vecs_per_lane=4, kept_vecs=14) == rn.ECONFIG   # not whole chunks
     assert fwd(vecs_per_lane=4, kept_vecs=-4) == rn.ECONFIG
     c = C(vector_path=5, lanes_per_row=1024, vecs_per_lane=8, wg_threads=1024, grid=4)

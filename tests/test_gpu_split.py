@@ -9,8 +9,9 @@ the C ABI:
     in use), groups without rows, and K from 2 to 16;
   * the plain forward's rows of 9 to 16 vectors per lane on 1024 lanes;
   * the forward's two-pass kernels (vector_path 5: rows beyond those, read
-    in chunks, the first ones kept in registers, the rest read twice), every
-    built (chunk, kept) pair, plain and residual-fused;
+    in chunks, the first ones kept in registers, the next ones held in LDS,
+    the rest read twice), every built (chunk, kept, LDS) shape, plain and
+    residual-fused;
   * the ladder's own choice at 65536 and 131072 columns (bf16, fp16 with fp32
     weights, fp32, the residual-fused pair), every row and every dW column,
     and dW bit-identical on reruns.
@@ -163,44 +164,51 @@ def test_forward_rows_of_9_to_16_vectors_per_lane(fmt):
         check_rstd(rstd, orr)
 
 
-# (chunk, kept) pairs (vectors per lane) of the two-pass forward kernels per
-# format, plain and residual-fused (rmsn_instances.h)
-_L16 = [(4, 0), (8, 0), (16, 0), (4, 16), (4, 12)]
-_R16 = [(4, 0), (8, 0), (2, 16), (4, 12)]
+# (chunk, kept, LDS-held) shapes (vectors per lane) of the two-pass forward
+# kernels per format, plain and residual-fused (rmsn_instances.h); copy_mode 1
+# holds 8 vectors per lane in LDS
+_L16 = [(4, 0, 0), (8, 0, 0), (16, 0, 0), (4, 16, 0), (4, 12, 0), (2, 16, 8), (4, 16, 8), (4, 12, 8)]
+_R16 = [(4, 0, 0), (8, 0, 0), (2, 16, 0), (4, 12, 0), (2, 16, 8), (4, 12, 8)]
+_LW = [(4, 0, 0), (8, 0, 0), (2, 14, 0), (2, 10, 8)]
+_RW = [(4, 0, 0), (8, 0, 0), (4, 8, 0), (4, 8, 8)]
 LOOP_SHAPES = {"bf16": (_L16, _R16), "f16": (_L16, _R16),
-               "f32": ([(4, 0), (8, 0), (16, 0), (2, 14), (4, 12)], [(4, 0), (8, 0), (2, 12), (4, 8)]),
-               "bf16w32": ([(4, 0), (8, 0), (2, 14)], [(4, 0), (8, 0), (4, 8)]),
-               "f16w32": ([(4, 0), (8, 0), (2, 14)], [(4, 0), (8, 0), (4, 8)])}
+               "f32": ([(4, 0, 0), (8, 0, 0), (16, 0, 0), (2, 14, 0), (4, 12, 0), (2, 14, 8)],
+                       [(4, 0, 0), (8, 0, 0), (2, 12, 0), (4, 8, 0), (2, 12, 8)]),
+               "bf16w32": (_LW, _RW), "f16w32": (_LW, _RW)}
 
 
-def _loop_rows(ch, kv):
-    """Row lengths (vectors) for a two-pass shape: the kept chunks full, then
-    two and a half reloaded chunks and a ragged wavefront; and for shapes that
-    keep vectors, a row that ends inside the kept part (nothing reloaded)."""
-    rows = [kv * 1024 + 2 * ch * 1024 + ch * 512 + 37]
+def _loop_rows(ch, kv, lv):
+    """Row lengths (vectors) for a two-pass shape: the kept and held chunks
+    full, then two and a half reloaded chunks and a ragged wavefront; for
+    shapes that keep vectors, a row that ends inside the kept part; for shapes
+    that hold vectors in LDS, one that ends inside the held part."""
+    rows = [(kv + lv) * 1024 + 2 * ch * 1024 + ch * 512 + 37]
     if kv:
         rows.append(kv * 1024 - ch * 512 - 37)
+    if lv:
+        rows.append(kv * 1024 + lv * 512 + 37)
     return rows
 
 
 @pytest.mark.parametrize("res", [False, True], ids=["plain", "residual"])
 @pytest.mark.parametrize("fmt", list(LOOP_SHAPES))
 def test_every_forward_two_pass_kernel(fmt, res):
-    """Every built (chunk, kept) pair, 5 rows on 3 workgroups (a workgroup
-    takes a second row), on rows that reload chunks after the kept ones and
-    rows that end inside the kept part: y and rstd against the oracle, and
-    with the residual add h bit-exact."""
+    """Every built (chunk, kept, LDS-held) shape, 5 rows on 3 workgroups (a
+    workgroup takes a second row), on rows that reload chunks after the kept
+    and held ones, rows that end inside the kept part and rows that end
+    inside the held part: y and rstd against the oracle, and with the
+    residual add h bit-exact."""
     act, wdt, epv = _fmt(fmt)
-    for ch, kv in LOOP_SHAPES[fmt][1 if res else 0]:
-        for nvec in _loop_rows(ch, kv):
+    for ch, kv, lv in LOOP_SHAPES[fmt][1 if res else 0]:
+        for nvec in _loop_rows(ch, kv, lv):
             N, M = nvec * epv, 5
-            x, w, _ = si.random_case(M, N, act, seed=ch + kv + 31 * res, wdtype=wdt)
+            x, w, _ = si.random_case(M, N, act, seed=ch + kv + lv + 31 * res, wdtype=wdt)
             eps = si.eps_f32(1e-6)
             cfg = rn.rmsnorm_config(vector_path=5, lanes_per_row=1024, vecs_per_lane=ch, wg_threads=1024,
-                                    kept_vecs=kv, grid=3)
-            _say(f"two-pass forward {fmt} res={res} chunk={ch} kept={kv} N={N}")
+                                    kept_vecs=kv, copy_mode=1 if lv else 0, grid=3)
+            _say(f"two-pass forward {fmt} res={res} chunk={ch} kept={kv} lds={lv} N={N}")
             if res:
-                r_in = si.random_tensor((M, N), act, seed=ch + kv + 7)
+                r_in = si.random_tensor((M, N), act, seed=ch + kv + lv + 7)
                 h, y, rstd = gpu_fwd_residual(x, r_in, w, eps, act, cfg=cfg)
                 oh, oy, orr = oracle.fwd_residual(x, r_in, w, eps, act, wdtype=wdt)
                 assert np.array_equal(widen(h, act), oh), "h differs from round(x + res)"
@@ -215,7 +223,9 @@ def test_every_forward_two_pass_kernel(fmt, res):
 LADDER_CASES = [("bf16", 1024, 65536, False), ("bf16", 512, 131072, False), ("f16w32", 512, 131072, False),
                 ("f32", 512, 65536, False), ("bf16", 512, 65536, True), ("bf16", 300, 131072 + 8, False),
                 ("bf16", 1, 131072, False), ("bf16", 64, 262144, False), ("f32", 64, 131072, False),
-                ("bf16", 64, 98304, True), ("bf16", 64, 131072 + 8, True), ("f32", 64, 65536, True)]
+                ("bf16", 64, 98304, True), ("bf16", 64, 131072 + 8, True), ("f32", 64, 65536, True),
+                ("bf16", 64, 196608, False), ("f16w32", 64, 196608, False), ("bf16", 32, 262144, True),
+                ("f32", 32, 98304, True)]
 
 
 @pytest.mark.parametrize("fmt,M,N,res", LADDER_CASES, ids=lambda v: str(v))

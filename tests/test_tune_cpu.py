@@ -105,9 +105,10 @@ def test_candidates_include_split_rows_and_the_widest_forward():
     fwd = [c for c in tune.candidates(M, 131072, rn.BF16, 0, 256) if c.vector_path == 1 and c.vecs_per_lane > 8]
     assert fwd and all((c.vector_path, c.lanes_per_row, c.vecs_per_lane, c.wg_threads) == (1, 1024, 16, 1024)
                        for c in fwd)
-    # the two-pass forward: every built (chunk, kept) pair, a workgroup per row or two per CU
-    loop = {(c.vecs_per_lane, c.kept_vecs, c.grid) for c in tune.candidates(M, 262144, rn.BF16, 0, 256)
+    # the two-pass forward: every built (chunk, kept, LDS) shape, a workgroup per row or two per CU
+    loop = {(c.vecs_per_lane, c.kept_vecs, c.copy_mode, c.grid) for c in tune.candidates(M, 262144, rn.BF16, 0, 256)
             if c.vector_path == 5}
-    assert loop == {(ch, kv, g) for ch, kv in ((4, 0), (8, 0), (16, 0), (4, 16), (4, 12)) for g in (4096, 512)}
-    assert {(c.vecs_per_lane, c.kept_vecs) for c in tune.candidates(M, 262144, rn.BF16_WF32, 0, 256)
-            if c.vector_path == 5} == {(4, 0), (8, 0), (2, 14)}
+    assert loop == {(ch, kv, l, g) for ch, kv, l in ((4, 0, 0), (8, 0, 0), (16, 0, 0), (4, 16, 0), (4, 12, 0),
+                                                     (2, 16, 1), (4, 16, 1), (4, 12, 1)) for g in (4096, 512)}
+    assert {(c.vecs_per_lane, c.kept_vecs, c.copy_mode) for c in tune.candidates(M, 262144, rn.BF16_WF32, 0, 256)
+            if c.vector_path == 5} == {(4, 0, 0), (8, 0, 0), (2, 14, 0), (2, 10, 1)}
