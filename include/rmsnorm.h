@@ -216,8 +216,9 @@ int rmsnorm_bwd_residual(const void *h, const void *w, const void *dy, const voi
  * split rows) in the workspace (rows of round_up(N, 64) floats);
  * *partial_rows receives how many (0 when M == 0).
  * rmsnorm_bwd_combine then writes dW[j] = sum over p < partial_rows of
- * partial[p][j] in a fixed order. Same arguments, checks and workspace
- * contract as rmsnorm_bwd; rmsnorm_bwd(...) equals rows followed by combine.
+ * partial[p][j] in an order fixed by (partial_rows, N). Same arguments,
+ * checks and workspace contract as rmsnorm_bwd; rmsnorm_bwd(...) equals rows
+ * followed by combine.
  */
 int rmsnorm_bwd_rows(const void *x, const void *w, const void *dy, const float *rstd, int64_t M,
                      int64_t N, int dtype, void *dx, void *workspace, size_t workspace_bytes,

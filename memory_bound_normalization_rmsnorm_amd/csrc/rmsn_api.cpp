@@ -935,6 +935,24 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
     return launch(fn, c.grid, c.wg_threads, args, static_cast<hipStream_t>(stream));
 }
 
+// Partial rows the combine sums side by side: the fewest of 8, 16 and 32
+// that leave each lane at most 16 rows and still launch at least 128
+// workgroups, else 64. Fewer slices mean fewer, wider workgroups, which pays
+// for wide rows with few partial rows; narrow rows are launch-bound and keep
+// 64. Measured per launch (us, slices 64 / 32 / 16 / 8): P = 32, N = 262144:
+// 12.65 / 7.10 / 4.75 / 3.67; P = 64, N = 131072: 7.45 / 4.95 / 3.84 / 4.01;
+// P = 128, N = 65536: 5.08 / 3.83 / 3.59 / 3.41; P = 256, N = 32768: 3.89 /
+// 3.54 / 3.49 / 4.19; P = 256, N = 8192: 2.74 / 2.68 / 3.04 / 3.87; P = 256,
+// N = 4096: 2.66 / 2.60 / 3.01 / 3.87; P = 512, N = 2048: 2.65 / 3.05 / 3.88
+// / 5.54.
+int combine_slices(int64_t P, int64_t N) {
+    for (int S : {8, 16, 32}) {
+        const int64_t cols = 4 * rmsn::kCombineWG / S;
+        if (P <= 16 * S && (N + cols - 1) / cols >= 128) return S;
+    }
+    return 64;
+}
+
 int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStream_t s) {
     if (N < 1 || N > kMaxN || P < 0) return RMSN_EINVAL;
     if (!dw || !aligned4(dw)) return RMSN_EINVAL;
@@ -943,8 +961,9 @@ int combine_impl(const void *workspace, int64_t P, int64_t N, float *dw, hipStre
     int64_t ldp = (N + rmsn::kPartialAlign - 1) / rmsn::kPartialAlign * rmsn::kPartialAlign;
     int32_t n32 = (int32_t)N;
     void *cargs[] = {(void *)&cpartial, (void *)&ldp, (void *)&P, (void *)&n32, (void *)&dw};
-    return launch(rmsn::dw_combine_kernel(), (N + rmsn::kCombineCols - 1) / rmsn::kCombineCols,
-                  rmsn::kCombineWG, cargs, s);
+    const int S = combine_slices(P, N);
+    const int64_t cols = 4 * rmsn::kCombineWG / S;
+    return launch(rmsn::dw_combine_kernel(S), (N + cols - 1) / cols, rmsn::kCombineWG, cargs, s);
 }
 
 // dw_direct: when not NULL and the grid writes a single partial row (one

@@ -6,28 +6,31 @@
 
 namespace rmsn {
 
-// dW[col] = sum over p of partial[p][col]; kCombineCols (32) columns per
-// workgroup, so each partial row contributes one whole 128-byte cache line to
-// one workgroup (narrower strips made two workgroups, usually on different
-// XCDs, fetch the same line). Lane (slice s, quad c) sums rows p = s, s + S,
-// s + 2S, ... (S = kCombineSlices = 64) in ascending order for columns
-// 4c..4c+3; the S slice sums are then folded by a fixed binary tree in LDS.
-// A lane issues the loads of kCombineUnroll of its rows before adding them
-// (still in ascending order), so the partial rows stream in with that many
-// loads in flight per lane instead of one memory latency per row.
-// Rows are padded to ldp floats (a multiple of 64) and 256-byte aligned, so
-// the float4 loads stay inside the workspace.
+// dW[col] = sum over p of partial[p][col]. A workgroup of kCombineWG lanes
+// takes Q = kCombineWG / S lanes per slice and 4 Q columns (each partial row
+// contributes whole 128-byte cache lines to one workgroup only; narrower
+// strips made two workgroups, usually on different XCDs, fetch the same
+// line). Lane (slice s, quad c) sums rows p = s, s + S, s + 2S, ... in
+// ascending order for columns 4c..4c+3; the S slice sums are then folded by a
+// fixed binary tree in LDS. A lane issues the loads of kCombineUnroll of its
+// rows before adding them (still in ascending order), so the partial rows
+// stream in with that many loads in flight per lane instead of one memory
+// latency per row. S is chosen by the host from P and N (fewer slices give
+// fewer, wider workgroups); for a given S the order is fixed, so dW is
+// bit-identical from run to run. Rows are padded to ldp floats (a multiple of
+// 64) and 256-byte aligned, so the float4 loads stay inside the workspace.
+template <int S>
 __global__ void __launch_bounds__(kCombineWG)
-dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
-           float *__restrict__ dw) {
-    __shared__ float4 red[kCombineSlices][kCombineLanes];
-    const int quad = threadIdx.x % kCombineLanes;
-    const int slice = threadIdx.x / kCombineLanes;
-    const int64_t col = (int64_t)blockIdx.x * kCombineCols + 4 * quad;
+dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N, float *__restrict__ dw) {
+    constexpr int Q = kCombineWG / S;
+    static_assert(Q * S == kCombineWG && Q >= 8, "whole 128-byte lines per slice");
+    __shared__ float4 red[S][Q];
+    const int quad = threadIdx.x % Q;
+    const int slice = threadIdx.x / Q;
+    const int64_t col = (int64_t)blockIdx.x * (4 * Q) + 4 * quad;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     if (col < N) {
         constexpr int U = kCombineUnroll;
-        constexpr int S = kCombineSlices;
         int64_t p = slice;
         for (; p + (U - 1) * S < P; p += U * S) {
             float4 v[U];
@@ -52,7 +55,7 @@ dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
     red[slice][quad] = a;
     __syncthreads();
 #pragma unroll
-    for (int h = kCombineSlices / 2; h >= 1; h >>= 1) {
+    for (int h = S / 2; h >= 1; h >>= 1) {
         if (slice < h) {
             float4 u = red[slice][quad];
             const float4 v = red[slice + h][quad];
@@ -192,7 +195,15 @@ const void *scalar_kernel(int dtype, int is_bwd, int res, int lds) {
     }
 }
 
-const void *dw_combine_kernel() { return reinterpret_cast<const void *>(&dw_combine); }
+const void *dw_combine_kernel(int slices) {
+    switch (slices) {
+    case 8: return reinterpret_cast<const void *>(&dw_combine<8>);
+    case 16: return reinterpret_cast<const void *>(&dw_combine<16>);
+    case 32: return reinterpret_cast<const void *>(&dw_combine<32>);
+    case 64: return reinterpret_cast<const void *>(&dw_combine<64>);
+    default: return nullptr;
+    }
+}
 const void *fill_zero_kernel() { return reinterpret_cast<const void *>(&fill_zero); }
 
 }  // namespace rmsn

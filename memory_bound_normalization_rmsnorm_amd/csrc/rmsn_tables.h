@@ -15,9 +15,6 @@ constexpr int kElemMinLanes = 64;
 constexpr int kElemMaxLanes = 1024;
 constexpr int kElemMaxK = 16;
 constexpr int kCombineWG = 512;
-constexpr int kCombineCols = 32;     // dW columns per combine workgroup: one 128-byte line per partial row
-constexpr int kCombineLanes = kCombineCols / 4;           // lanes per slice, 4 columns each
-constexpr int kCombineSlices = kCombineWG / kCombineLanes;  // partial rows summed side by side
 constexpr int kCombineUnroll = 8;    // partial-row loads a combine lane has in flight
 constexpr int kPartialAlign = 64;    // partial rows are padded to a multiple of 64 floats
 
@@ -85,7 +82,9 @@ const void *scalar_kernel(int dtype, int is_bwd, int res, int lds);
 // accesses of g elements per lane (g 1, 2, 4 or 8, at most 16 bytes per
 // access; k * g at most kElemMaxK), nullptr otherwise
 const void *elem_kernel(int dtype, int is_bwd, int res, int k, int g, int lanes);
-const void *dw_combine_kernel();
+// the fixed-order dW combine summing `slices` (8, 16, 32 or 64) partial rows
+// side by side, 4 * kCombineWG / slices columns per workgroup; nullptr otherwise
+const void *dw_combine_kernel(int slices);
 const void *fill_zero_kernel();
 
 // Device address of the current device `dev`'s copy of the static workspace
