@@ -11,8 +11,10 @@
 // rstd and the weights and stores y. A row of 262144 16-bit columns is 512
 // KiB, more than a workgroup's registers and LDS hold, so part of the row is
 // read twice: the first KV vectors per lane stay in registers from pass 1
-// (packed, KV / CH chunks; loaded with the streaming hint, as they are not
-// read again), pass 2 scales them first and then loads the rest of the row
+// (packed, KV / CH chunks), the next LV in the lane's own LDS slots (LV / CH
+// chunks; a lane reads back only what it wrote, so no barrier), both loaded
+// with the streaming hint as they are not read again; pass 2 scales the kept
+// chunks first, then the held ones, and then loads the rest of the row
 // again. Pass 1's loads of that rest carry no streaming hint, so pass 2
 // finds it in the caches (a CU's row in the MALL) rather than in HBM. With
 // RES, pass 2 recomputes h from x and res (both read-only) instead of
