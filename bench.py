@@ -9,8 +9,9 @@ Measurement, following the Quack Hopper study ("What a tuned RMSNorm kernel
 actually costs on Hopper", section 02):
   * the roofline denominator is measured in the same run: the best of a
     copy, a pure write and a two-read-one-write probe over 2 GiB buffers,
-    probed again at the end; the closing/opening ratio flags a drifting
-    (shared) device;
+    probed again at the end (each pass after a short untimed load that
+    brings the clocks up); the closing/opening ratio flags a drifting
+    (shared) device, and the larger of the two passes is the denominator;
   * inputs rotate through R cloned sets that together exceed the last-level
     caches, and the backward of step k uses a different set than its
     forward, so no kernel reads data an earlier kernel just left in cache;
@@ -45,6 +46,7 @@ METRIC = "RMSNorm fwd/bwd achieved GB/s and % of measured HBM roofline, 1 MI355X
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 GIB = 1 << 30
 SETTLE_S = 0.25  # untimed steps before the warmup steps (clock settle after the CPU leg)
+PROBE_SETTLE_S = 0.3  # untimed copies before each roofline probe pass (clock settle)
 CELL_SETTLE_S = 0.05  # untimed graph replays before each cell's timed replays
 # Per-kernel graph length: launches per HIP graph, sized from the kernel's
 # bytes so that one replay lasts about GRAPH_TARGET_MS (at least
@@ -238,16 +240,24 @@ class Timer:
         return statistics.median(times), times
 
 
-def probe_roofline(torch, rn, timer, gib):
+def probe_roofline(torch, rn, timer, gib, settle_s=PROBE_SETTLE_S):
     """Best of copy, pure write and 2-read-1-write over several grid sizes and
     cache hints (non-temporal loads and/or stores) (GB/s). A pure-read probe is
-    reported beside them."""
+    reported beside them. Copies run untimed for settle_s of wall time first:
+    a device that has just been idle (start-up, the CPU leg) needs tens of
+    milliseconds of load before its clocks reach the level the timed kernels
+    run at."""
     nbytes = int(gib * GIB) // 256 * 256
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     c = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b.fill_(2)
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle_s:
+        for _ in range(8):
+            rn.rmsn_probe_copy(a, c, nbytes, 0, 0)
+        torch.cuda.synchronize()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grids = [0, cus * 4, cus * 8, cus * 16, cus * 32]
     probes = {
@@ -614,7 +624,9 @@ def main(argv=None):
     log(f"size-matched probes: {sized}")
     closing = probe_roofline(torch, rn, timer, args.probe_gib)
     drift = closing["best_GBps"] / opening["best_GBps"]
-    measured = opening["best_GBps"]
+    # the denominator is the best the hardware showed in either pass, so a
+    # slow opening pass cannot inflate the percentages
+    measured = max(opening["best_GBps"], closing["best_GBps"])
 
     fwd_gbps = fwd_bytes / (f_us * 1e-6) / 1e9
     bwd_call_us = r_us + c_us
@@ -649,8 +661,9 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": rows_bytes,
             "avg_launch_us": round(r_us, 2),
         },
-        "measured_roofline": {"opening": opening, "closing_GBps": closing["best_GBps"], "drift": round(drift, 4),
-                              "drift_ok": 0.99 <= drift <= 1.01},
+        "measured_roofline": {"GBps": measured, "opening": opening, "closing_GBps": closing["best_GBps"],
+                              "drift": round(drift, 4), "drift_ok": 0.99 <= drift <= 1.01,
+                              "denominator": "the larger of the opening and closing passes' best probe"},
         "size_matched_roofline": dict(sized, fwd_pct_of_copy=round(100 * fwd_gbps / sized["copy_GBps"], 1),
                                       bwd_rows_pct_of_2r1w=round(100 * rows_gbps / sized["2r1w_GBps"], 1)),
         "fwd": {"avg_us": round(f_us, 2), "GBps": round(fwd_gbps, 1), "pct_measured_roofline": round(100 * fwd_gbps / measured, 1),
