@@ -37,6 +37,28 @@ constexpr int bwd_packed_per_slot() {
     return in * (1 + PF) + WeightVec<T, TW>::kVecs;
 }
 
+// Registers beyond the packed vectors that bwd_vec's estimate counts: the
+// residual's and the second prefetch slot's unpacked temporaries.
+template <typename T, bool RES, int PF>
+constexpr int bwd_vec_extra() {
+    return (RES ? 2 * Elem<T>::kPerVec : 0) + (PF == 2 ? 2 * Elem<T>::kPerVec : 0);
+}
+
+// Whether bwd_vec keeps fp64 dW totals (DwSums): at most 8 sums per lane, and
+// only where they cost no resident workgroup: with two blocks prefetched (the
+// ladder runs those one per CU), or where the occupancy target still admits
+// two workgroups per CU. Elsewhere (1024-lane workgroups without deep
+// prefetch, which the ladder may run two per CU) the sums stay fp32.
+template <typename T, typename TW, bool RES, int VPT, int WG, int PF>
+constexpr bool bwd_vec_dw_f64() {
+    constexpr int nv = VPT * Elem<T>::kPerVec;
+    if (nv > 8) return false;
+    if (PF == 2) return true;
+    constexpr int two = 2 * WG / 256 < 8 ? 2 * WG / 256 : 8;
+    return waves_for(VPT * bwd_packed_per_slot<T, TW, RES, PF>(), dw_sum_regs(nv, true), VPT, WG,
+                     bwd_vec_extra<T, RES, PF>()) >= two;
+}
+
 // PF: row blocks loaded ahead of the one being computed (0, 1 or 2; a
 // register ring, the loop unrolled so every slot index is static).
 // LPR = 0: the row is the whole workgroup, whose size (a multiple of 64 up to
@@ -45,8 +67,9 @@ constexpr int bwd_packed_per_slot() {
 template <typename T, typename TW, bool RES, int LPR, int VPT, int WG, int PF>
 __global__ void __launch_bounds__(WG)
 __attribute__((amdgpu_waves_per_eu(waves_for(VPT * bwd_packed_per_slot<T, TW, RES, PF>(),
-                                             VPT * Elem<T>::kPerVec, VPT, WG,
-                                             (RES ? 2 * Elem<T>::kPerVec : 0) + (PF == 2 ? 2 * Elem<T>::kPerVec : 0)))))
+                                             dw_sum_regs(VPT * Elem<T>::kPerVec,
+                                                         bwd_vec_dw_f64<T, TW, RES, VPT, WG, PF>()),
+                                             VPT, WG, bwd_vec_extra<T, RES, PF>()))))
 bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__ dy, const T *__restrict__ dh,
         const float *__restrict__ rstd, T *__restrict__ dx, float *__restrict__ partial, int64_t ldp, int64_t M,
         int32_t N, int32_t nvec) {
@@ -78,11 +101,9 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
         off[v] = in ? (uint32_t)grp * row_bytes + (uint32_t)idx * 16u : kOff;
         wv[v].load(wb, idx, in);
     }
-    float acc[VPT][EPV];
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) acc[v][k] = 0.f;
+    constexpr bool kDwF64 = bwd_vec_dw_f64<T, TW, RES, VPT, WG, PF>();
+    DwSums<VPT * EPV, kDwF64> acc;  // sum v * EPV + k: element k of the lane's vector v
+    acc.init();
 
     // rows of the block starting at b that exist (0 past the end)
     auto rows_at = [&](int64_t b) -> uint32_t {
@@ -126,7 +147,7 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
                 s = __builtin_fmaf(fg[k] * fw[k], fx[k], s);
-                acc[v][k] = __builtin_fmaf(fg[k] * fx[k], r, acc[v][k]);
+                if constexpr (!kDwF64) acc.add(v * EPV + k, fg[k] * fx[k], r);
             }
         }
         if constexpr (kRowIsWG)
@@ -156,7 +177,13 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
                 for (int k = 0; k < EPV; ++k) o[k] += fh[k];
             }
             db.store16<RMSN_BWD_STORE_AUX>(off[v], E::pack(o));
+            // fp64 totals: the dW terms after the store, off the path to the row sum
+            if constexpr (kDwF64) {
+#pragma unroll
+                for (int k = 0; k < EPV; ++k) acc.add(v * EPV + k, fg[k] * fx[k], r);
+            }
         }
+        acc.end_row();
     };
     auto copy = [&](u32x4 (&xo)[VPT], u32x4 (&go)[VPT], u32x4 (&ho)[VPT], const u32x4 (&xi)[VPT],
                     const u32x4 (&gi)[VPT], const u32x4 (&hi)[VPT]) {
@@ -212,6 +239,7 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
         }
     }
 
+    acc.fold();
     float *prow = partial + (int64_t)blockIdx.x * ldp;
     if constexpr (RPW == 1) {
         const Buf pb(prow, (uint32_t)nvec * (uint32_t)(EPV * 4));
@@ -222,10 +250,10 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
 #pragma unroll
                 for (int q = 0; q < EPV / 4; ++q) {
                     u32x4 o;
-                    o.x = as_u32(acc[v][4 * q]);
-                    o.y = as_u32(acc[v][4 * q + 1]);
-                    o.z = as_u32(acc[v][4 * q + 2]);
-                    o.w = as_u32(acc[v][4 * q + 3]);
+                    o.x = as_u32(acc.get(v * EPV + 4 * q));
+                    o.y = as_u32(acc.get(v * EPV + 4 * q + 1));
+                    o.z = as_u32(acc.get(v * EPV + 4 * q + 2));
+                    o.w = as_u32(acc.get(v * EPV + 4 * q + 3));
                     pb.store16<RMSN_BWD_PARTIAL_AUX>((uint32_t)(idx * EPV + 4 * q) * 4u, o);
                 }
             }
@@ -238,15 +266,16 @@ bwd_vec(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
             float4 *mine = reinterpret_cast<float4 *>(comb + threadIdx.x * EPV);
 #pragma unroll
             for (int q = 0; q < EPV / 4; ++q)
-                mine[q] = make_float4(acc[v][4 * q], acc[v][4 * q + 1], acc[v][4 * q + 2], acc[v][4 * q + 3]);
+                mine[q] = make_float4(acc.get(v * EPV + 4 * q), acc.get(v * EPV + 4 * q + 1),
+                                      acc.get(v * EPV + 4 * q + 2), acc.get(v * EPV + 4 * q + 3));
             __syncthreads();
             for (int q = threadIdx.x; q < kSlotCols; q += WG) {
                 const int col = v * kSlotCols + q;
                 if (col < N) {
-                    float t = comb[q];
+                    double t = comb[q];
 #pragma unroll
                     for (int g = 1; g < RPW; ++g) t += comb[g * kSlotCols + q];
-                    prow[col] = t;
+                    prow[col] = (float)t;
                 }
             }
             __syncthreads();

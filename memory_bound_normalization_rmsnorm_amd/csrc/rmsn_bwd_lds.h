@@ -189,9 +189,8 @@ bwd_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
     const bool vin = lane < nvec;
     const uint32_t off = vin ? (uint32_t)grp * row_bytes + (uint32_t)lane * 16u : kOff;
 
-    float acc[EPV];
-#pragma unroll
-    for (int k = 0; k < EPV; ++k) acc[k] = 0.f;
+    DwSums<EPV, true> acc;  // one workgroup per CU: the fp64 totals cost no residency
+    acc.init();
 
     const int64_t step = (int64_t)gridDim.x * RPW;
     int64_t base = (int64_t)blockIdx.x * RPW;
@@ -273,10 +272,7 @@ bwd_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
             E::unpack(gv, fg);
             wv.unpack(fw);
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                sacc = __builtin_fmaf(fg[k] * fw[k], fx[k], sacc);
-                acc[k] = __builtin_fmaf(fg[k] * fx[k], r, acc[k]);
-            }
+            for (int k = 0; k < EPV; ++k) sacc = __builtin_fmaf(fg[k] * fw[k], fx[k], sacc);
         }
         if constexpr (kRowIsWG)
             sacc = wg_sum_nf<WG>(sacc, slots, parity);
@@ -301,7 +297,12 @@ bwd_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
         }
         const Buf db(dx + base * N, rows_at(base) * row_bytes);
         db.store16<RMSN_BWD_STORE_AUX>(off, E::pack(o));
+        // the dW terms after the row's store, off the path to the row sum
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) acc.add(k, fg[k] * fx[k], r);
+        acc.end_row();
     }
+    acc.fold();
     // every copy has landed before LDS is reused or the workgroup ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -312,10 +313,10 @@ bwd_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
 #pragma unroll
             for (int q = 0; q < EPV / 4; ++q) {
                 u32x4 o;
-                o.x = as_u32(acc[4 * q]);
-                o.y = as_u32(acc[4 * q + 1]);
-                o.z = as_u32(acc[4 * q + 2]);
-                o.w = as_u32(acc[4 * q + 3]);
+                o.x = as_u32(acc.get(4 * q));
+                o.y = as_u32(acc.get(4 * q + 1));
+                o.z = as_u32(acc.get(4 * q + 2));
+                o.w = as_u32(acc.get(4 * q + 3));
                 pb.store16<RMSN_BWD_PARTIAL_AUX>((uint32_t)(lane * EPV + 4 * q) * 4u, o);
             }
         }
@@ -327,15 +328,15 @@ bwd_lds(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict__
         float4 *mine = reinterpret_cast<float4 *>(comb + threadIdx.x * EPV);
 #pragma unroll
         for (int q = 0; q < EPV / 4; ++q)
-            mine[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+            mine[q] = make_float4(acc.get(4 * q), acc.get(4 * q + 1), acc.get(4 * q + 2), acc.get(4 * q + 3));
         __syncthreads();
         constexpr int kSlotCols = LPR * EPV;
         for (int q = threadIdx.x; q < kSlotCols; q += WG) {
             if (q < N) {
-                float t = comb[q];
+                double t = comb[q];
 #pragma unroll
                 for (int g = 1; g < RPW; ++g) t += comb[g * kSlotCols + q];
-                prow[q] = t;
+                prow[q] = (float)t;
             }
         }
     }

@@ -24,11 +24,11 @@ __global__ void __launch_bounds__(kCombineWG)
 dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N, float *__restrict__ dw) {
     constexpr int Q = kCombineWG / S;
     static_assert(Q * S == kCombineWG && Q >= 8, "whole 128-byte lines per slice");
-    __shared__ float4 red[S][Q];
+    __shared__ double4 red[S][Q];
     const int quad = threadIdx.x % Q;
     const int slice = threadIdx.x / Q;
     const int64_t col = (int64_t)blockIdx.x * (4 * Q) + 4 * quad;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    double4 a = make_double4(0.0, 0.0, 0.0, 0.0);
     if (col < N) {
         constexpr int U = kCombineUnroll;
         int64_t p = slice;
@@ -38,18 +38,18 @@ dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
             for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float4 *>(partial + (p + u * S) * ldp + col);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                a.x += v[u].x;
-                a.y += v[u].y;
-                a.z += v[u].z;
-                a.w += v[u].w;
+                a.x += (double)v[u].x;
+                a.y += (double)v[u].y;
+                a.z += (double)v[u].z;
+                a.w += (double)v[u].w;
             }
         }
         for (; p < P; p += S) {
             const float4 v = *reinterpret_cast<const float4 *>(partial + p * ldp + col);
-            a.x += v.x;
-            a.y += v.y;
-            a.z += v.z;
-            a.w += v.w;
+            a.x += (double)v.x;
+            a.y += (double)v.y;
+            a.z += (double)v.z;
+            a.w += (double)v.w;
         }
     }
     red[slice][quad] = a;
@@ -57,8 +57,8 @@ dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
 #pragma unroll
     for (int h = S / 2; h >= 1; h >>= 1) {
         if (slice < h) {
-            float4 u = red[slice][quad];
-            const float4 v = red[slice + h][quad];
+            double4 u = red[slice][quad];
+            const double4 v = red[slice + h][quad];
             u.x += v.x;
             u.y += v.y;
             u.z += v.z;
@@ -68,8 +68,8 @@ dw_combine(const float *__restrict__ partial, int64_t ldp, int64_t P, int32_t N,
         __syncthreads();
     }
     if (slice == 0 && col < N) {
-        const float4 u = red[0][quad];
-        const float o[4] = {u.x, u.y, u.z, u.w};
+        const double4 u = red[0][quad];
+        const float o[4] = {(float)u.x, (float)u.y, (float)u.z, (float)u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (col + e < N) dw[col + e] = o[e];

@@ -40,6 +40,62 @@ struct f16_t {
     uint16_t bits;
 };
 
+// registers a lane's NV dW sums take, for occupancy estimates (with F64, the
+// fp32 block sums, the fp64 totals, the fold's conversions and the fp64
+// pairs' alignment)
+constexpr int dw_sum_regs(int nv, bool f64) { return f64 ? 3 * nv + 8 : nv; }
+
+constexpr int kDwBlockRows = 8;  // rows (row blocks) summed in fp32 before each fp64 fold
+
+// One lane's dW running sums over the rows a workgroup walks, for NV columns.
+// With F64, each row's term dy * x * rstd is added with an fp32 fma into a
+// block sum, and every kDwBlockRows rows the block sums are added into fp64
+// totals. Summed in fp32 alone over a walk of tens of rows, a column's
+// rounding error grows with the walk and shows on columns whose total nearly
+// cancels; the fp32 blocks keep the per-row cost to one fma (an fp64 fma per
+// row measured 2-8% slower on several shapes). The workgroup's rows are the
+// same for all its lanes, so the fold is taken uniformly. With F64 false the
+// lane keeps plain fp32 sums (for kernels where the fp64 totals would cost
+// resident workgroups).
+template <int NV, bool F64>
+struct DwSums {
+    static constexpr bool kF64 = F64;
+    float blk[NV];
+    double tot[F64 ? NV : 1];
+    int in_blk;
+
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) blk[i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < (F64 ? NV : 1); ++i) tot[i] = 0.0;
+        in_blk = 0;
+    }
+    // term i of the current row: (dy * x) * rstd, gx = dy * x (exact for 16-bit inputs)
+    __device__ __forceinline__ void add(int i, float gx, float r) { blk[i] = __builtin_fmaf(gx, r, blk[i]); }
+    __device__ __forceinline__ void fold() {
+        if constexpr (F64) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                tot[i] += (double)blk[i];
+                blk[i] = 0.f;
+            }
+        }
+        in_blk = 0;
+    }
+    // after each row (block of rows) the workgroup has added
+    __device__ __forceinline__ void end_row() {
+        if constexpr (F64) {
+            if (++in_blk == kDwBlockRows) fold();
+        }
+    }
+    // the sums, rounded to fp32 (call fold() first)
+    __device__ __forceinline__ float get(int i) const {
+        if constexpr (F64) return (float)tot[i];
+        else return blk[i];
+    }
+};
+
 template <typename T>
 struct Elem;
 

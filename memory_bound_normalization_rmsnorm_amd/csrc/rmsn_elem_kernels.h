@@ -177,10 +177,9 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
     __shared__ float slots[2 * (L / 64)];
     const float n = (float)N;
     Packed<TW, G> gw[K];
-    float acc[K * G];
+    DwSums<K * G, true> acc;  // sum k * G + i: element i of the lane's access k (at most 12)
     load_row<TW, L, K, G>(w, N, gw);
-#pragma unroll
-    for (int e = 0; e < K * G; ++e) acc[e] = 0.f;
+    acc.init();
     int parity = 0;
     Packed<T, G> gx[K], gg[K];  // the row's x and dy
     float r = 0.f;              // and rstd
@@ -219,13 +218,14 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
                     const float fx = gx[k].get(i), fg = gg[k].get(i);
                     g[i] = __builtin_fmaf(-fx, c, r * (fg * gw[k].get(i)));
                     if constexpr (RES) g[i] += d.get(i);
-                    acc[k * G + i] = __builtin_fmaf(fg * fx, r, acc[k * G + i]);
+                    acc.add(k * G + i, fg * fx, r);
                 }
                 Packed<T, G> out;
                 out.set(g);
                 out.store(dx + o + j);
             }
         }
+        acc.end_row();
         const int64_t next = row + gridDim.x;
         if (next < M) {
             load_row<T, L, K, G>(x + next * (int64_t)N, N, gx);
@@ -236,6 +236,7 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
     // the partial row is 256-byte aligned (or dW itself, 16-byte aligned):
     // stores of up to 4 floats
     constexpr int PG = G < 4 ? G : 4;
+    acc.fold();
     float *prow = partial + (int64_t)blockIdx.x * ldp;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -243,8 +244,11 @@ bwd_elem(const T *__restrict__ x, const TW *__restrict__ w, const T *__restrict_
         if (j < N) {
 #pragma unroll
             for (int i = 0; i < G; i += PG) {
+                float t[PG];
+#pragma unroll
+                for (int e = 0; e < PG; ++e) t[e] = acc.get(k * G + i + e);
                 Packed<float, PG> a;
-                a.set(&acc[k * G + i]);
+                a.set(t);
                 a.store(prow + j + i);
             }
         }
