@@ -216,7 +216,8 @@ int rmsnorm_bwd_residual(const void *h, const void *w, const void *dy, const voi
  * split rows) in the workspace (rows of round_up(N, 64) floats);
  * *partial_rows receives how many (0 when M == 0).
  * rmsnorm_bwd_combine then writes dW[j] = sum over p < partial_rows of
- * partial[p][j] in an order fixed by (partial_rows, N). Same arguments,
+ * partial[p][j], added in fp64 in an order fixed by (partial_rows, N) and
+ * rounded once to fp32. Same arguments,
  * checks and workspace contract as rmsnorm_bwd; rmsnorm_bwd(...) equals rows
  * followed by combine.
  */
