@@ -47,6 +47,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 GIB = 1 << 30
 SETTLE_S = 0.25  # untimed steps before the warmup steps (clock settle after the CPU leg)
 PROBE_SETTLE_S = 0.3  # untimed copies before each roofline probe pass (clock settle)
+PROBE_REPS = 25  # timed calls per probe variant and grid (median): with 11 the write probe's best moved ~1% between passes
 CELL_SETTLE_S = 0.05  # untimed graph replays before each cell's timed replays
 # Per-kernel graph length: launches per HIP graph, sized from the kernel's
 # bytes so that one replay lasts about GRAPH_TARGET_MS (at least
@@ -240,19 +241,29 @@ class Timer:
         return statistics.median(times), times
 
 
-def probe_roofline(torch, rn, timer, gib, settle_s=PROBE_SETTLE_S):
-    """Best of copy, pure write and 2-read-1-write over several grid sizes and
-    cache hints (non-temporal loads and/or stores) (GB/s). A pure-read probe is
-    reported beside them. Copies run untimed for settle_s of wall time first:
-    a device that has just been idle (start-up, the CPU leg) needs tens of
-    milliseconds of load before its clocks reach the level the timed kernels
-    run at."""
+def probe_buffers(torch, gib):
+    """The three probe buffers of `gib` GiB each (two inputs filled, one output)."""
     nbytes = int(gib * GIB) // 256 * 256
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     c = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b.fill_(2)
+    return a, b, c
+
+
+def probe_roofline(torch, rn, timer, gib, settle_s=PROBE_SETTLE_S, bufs=None):
+    """Best of copy, pure write and 2-read-1-write over several grid sizes and
+    cache hints (non-temporal loads and/or stores) (GB/s). A pure-read probe is
+    reported beside them. Copies run untimed for settle_s of wall time first:
+    a device that has just been idle (start-up, the CPU leg) needs tens of
+    milliseconds of load before its clocks reach the level the timed kernels
+    run at. `bufs` (from probe_buffers) lets two passes probe the same memory:
+    the same probe on another 2 GiB allocation can differ by 1-2% with where
+    the buffers land, which a drift check must not mistake for the device."""
+    own = bufs is None
+    a, b, c = probe_buffers(torch, gib) if own else bufs
+    nbytes = a.numel()
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < settle_s:
         for _ in range(8):
@@ -271,7 +282,7 @@ def probe_roofline(torch, rn, timer, gib, settle_s=PROBE_SETTLE_S):
         best = None
         for v in variants[name]:
             for g in grids:
-                med, _ = timer.median_ms(lambda: fn(g, v), reps=11, warmup=2)
+                med, _ = timer.median_ms(lambda: fn(g, v), reps=PROBE_REPS, warmup=2)
                 gbps = moved / (med * 1e-3) / 1e9
                 if best is None or gbps > best[0]:
                     best = (gbps, g, v, med)
@@ -281,13 +292,14 @@ def probe_roofline(torch, rn, timer, gib, settle_s=PROBE_SETTLE_S):
     best = None
     for v in (0, 1):
         for g in grids:
-            med, _ = timer.median_ms(lambda: rn.rmsn_probe_read(a, nbytes, sink, g, v), reps=11, warmup=2)
+            med, _ = timer.median_ms(lambda: rn.rmsn_probe_read(a, nbytes, sink, g, v), reps=PROBE_REPS, warmup=2)
             gbps = nbytes / (med * 1e-3) / 1e9
             if best is None or gbps > best[0]:
                 best = (gbps, g, v, med)
     read = {"GBps": round(best[0], 1), "grid": best[1], "nt_variant": best[2], "median_ms": round(best[3], 4)}
     del a, b, c
-    torch.cuda.empty_cache()
+    if own:
+        torch.cuda.empty_cache()
     best_name = max(out, key=lambda k: out[k]["GBps"])
     return {"best_GBps": out[best_name]["GBps"], "best_probe": best_name, "probes": out, "read_GBps": read,
             "buffer_GiB": gib}
@@ -392,7 +404,9 @@ def main(argv=None):
     log(f"device {props.name} ({props.multi_processor_count} CUs), library {rn.LIB_PATH}")
 
     do_full = args.mode == "bench"
-    opening = probe_roofline(torch, rn, timer, args.probe_gib) if do_full else None
+    # the opening and closing passes probe the same buffers, held for the run
+    probe_bufs = probe_buffers(torch, args.probe_gib) if do_full else None
+    opening = probe_roofline(torch, rn, timer, args.probe_gib, bufs=probe_bufs) if do_full else None
     if opening:
         log(f"opening roofline {opening['best_GBps']} GB/s ({opening['best_probe']})")
 
@@ -622,7 +636,8 @@ def main(argv=None):
 
     sized = size_matched_probes(torch, rn, M * N * es)
     log(f"size-matched probes: {sized}")
-    closing = probe_roofline(torch, rn, timer, args.probe_gib)
+    closing = probe_roofline(torch, rn, timer, args.probe_gib, bufs=probe_bufs)
+    del probe_bufs
     drift = closing["best_GBps"] / opening["best_GBps"]
     # the denominator is the best the hardware showed in either pass, so a
     # slow opening pass cannot inflate the percentages
