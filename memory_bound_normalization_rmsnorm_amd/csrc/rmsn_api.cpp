@@ -936,27 +936,29 @@ int fwd_impl(const void *x, const void *res, const void *w, float eps, int64_t M
 }
 
 // Partial rows the combine sums side by side: the fewest of 8, 16 and 32
-// that leave each lane at most 16 rows and still launch at least 128
-// workgroups; else 32 if that leaves at most 16 rows per lane on at least 64
-// workgroups; else 64. Fewer slices mean fewer, wider workgroups and a
-// shallower fixed tree (its adds are fp64, twice the LDS bytes of fp32),
-// which pays for wide rows with few partial rows; narrow rows are
-// launch-bound and keep 64. Measured per launch with the fp64 sums (us,
-// slices 8 / 16 / 32 / 64, graph-replayed): P = 256, N = 4096: 3.82 / 3.00 /
-// 2.56 / 2.72; N = 5120: 3.78 / 3.02 / 2.58 / 2.73; N = 7168: 3.82 / 3.02 /
-// 2.61 / 2.78; N = 8192: 3.82 / 3.02 / 2.61 / 2.79; N = 32768: 4.30 / 3.58 /
-// 3.69 / 4.62; P = 768, N = 128: 6.97 / 4.60 / 3.39 / 3.11; P = 64, N = 1024:
-// 2.31 / 2.43 / 2.29 / 2.27. With fp32 sums (us, 64 / 32 / 16 / 8): P = 32,
-// N = 262144: 12.65 / 7.10 / 4.75 / 3.67; P = 64, N = 131072: 7.45 / 4.95 /
-// 3.84 / 4.01; P = 128, N = 65536: 5.08 / 3.83 / 3.59 / 3.41; P = 512, N =
-// 2048: 2.65 / 3.05 / 3.88 / 5.54.
+// that launch at least 16 workgroups and leave each lane at most 8 partial
+// rows (16 when they launch at least 256 workgroups); else 64. A lane adds its
+// rows one after another and the S slice sums then go through a fixed tree
+// of log2(S) levels in LDS (fp64, twice the bytes of fp32): fewer slices mean
+// fewer, wider workgroups and a shallower tree, more slices shorter chains.
+// Measured per launch with the fp64 sums (us, slices 8 / 16 / 32 / 64,
+// graph-replayed): P = 256, N = 4096: 3.81 / 3.02 / 2.57 / 2.72; N = 2560:
+// 3.78 / 2.98 / 2.56 / 2.70; N = 7168: 3.82 / 3.02 / 2.61 / 2.78; N = 8192:
+// 3.82 / 3.02 / 2.61 / 2.79; N = 32768: 4.30 / 3.58 / 3.69 / 4.62; P = 512,
+// N = 4100: 8.29 / 3.91 / 3.10 / 2.67; N = 8192: 5.63 / 3.97 / 3.13 / 2.79;
+// P = 384, N = 4096: 4.74 / 3.39 / 3.12 / 2.97; P = 320, N = 4096: 4.18 /
+// 3.58 / 2.86 / 2.84; P = 128, N = 4096: 2.93 / 2.49 / 2.62 / 2.49; P = 768,
+// N = 128: 6.97 / 4.60 / 3.39 / 3.11; P = 64, N = 1024: 2.31 / 2.43 / 2.29 /
+// 2.27. With fp32 sums (us, 64 / 32 / 16 / 8): P = 32, N = 262144: 12.65 /
+// 7.10 / 4.75 / 3.67; P = 64, N = 131072: 7.45 / 4.95 / 3.84 / 4.01; P = 128,
+// N = 65536: 5.08 / 3.83 / 3.59 / 3.41.
 int combine_slices(int64_t P, int64_t N) {
     for (int S : {8, 16, 32}) {
         const int64_t cols = 4 * rmsn::kCombineWG / S;
-        if (P <= 16 * S && (N + cols - 1) / cols >= 128) return S;
+        const int64_t wgs = (N + cols - 1) / cols;
+        const int64_t rows = (P + S - 1) / S;
+        if (wgs >= 16 && rows <= (wgs >= 256 ? 16 : 8)) return S;
     }
-    const int64_t cols32 = 4 * rmsn::kCombineWG / 32;
-    if (P <= 16 * 32 && (N + cols32 - 1) / cols32 >= 64) return 32;
     return 64;
 }
 
