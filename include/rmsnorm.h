@@ -177,8 +177,8 @@ int64_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t N, int dtype);
  * single workgroup (a few rows) and dW is 16-byte aligned, that workgroup's
  * partial row is dW and only the row kernel is enqueued. With M == 0, dW is
  * still written (zeros) when N >= 1 and dW is not NULL. dW's summation order
- * depends only on (M, N, dtype) and the device's compute-unit count, so the
- * same call gives the same bits every time; each lane's running sums over its
+ * depends only on (M, N, dtype), the pointers' alignment class and the
+ * device, so the same call gives the same bits every time; each lane's running sums over its
  * rows are fp32 blocks of 8 rows folded into fp64 totals in the register
  * kernels that have room for them (plain fp32 in the others), and the
  * partial rows are added in fp64 and rounded once.
