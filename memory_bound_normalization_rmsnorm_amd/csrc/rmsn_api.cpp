@@ -577,6 +577,19 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         if (want > resident) want = resident;
         if (wide_long_walk(M, dtype, cus, c)) want = 2 * cus;
         grid = row_blocks < want ? row_blocks : want;
+        // Rows narrower than a wavefront take three workgroups per CU. When
+        // the row blocks do not split evenly over them, some walk one block
+        // more and finish alone, their CU half idle meanwhile; two per CU
+        // then carry the same blocks per CU in fuller walks. Taken when it
+        // cuts the largest blocks per CU (walk x workgroups per CU) by at
+        // least 5%: bf16 16384 x 128 8.45 -> 7.14 us (6 -> 4 blocks per CU),
+        // 65536 x 128 14.78 -> 14.11 (18 -> 16). 1M x 128 keeps three (258
+        // against 256 blocks; two per CU measured 136.0 against 130.8 us).
+        if (c->vector_path == 1 && c->lanes_per_row < 64 && grid == 3 * cus) {
+            const int64_t load3 = (row_blocks + 3 * cus - 1) / (3 * cus) * 3;
+            const int64_t load2 = (row_blocks + 2 * cus - 1) / (2 * cus) * 2;
+            if (20 * load2 <= 19 * load3) grid = 2 * cus;
+        }
         // A few rows (a decode step's): one workgroup walks them all and
         // writes dW itself, with no combine launch. Faster while M * N is at
         // most kBwdSingleElems and the walk at most kBwdSinglePasses row

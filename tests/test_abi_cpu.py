@@ -527,6 +527,9 @@ def test_ladder_grid_and_workspace_shape():
     assert cfg(4096, 32768, rn.BF16, 1, cus=256, blocks=2)["grid"] == 256
     # ... three per compute unit for rows narrower than a wavefront
     assert cfg(1 << 20, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 768
+    # ... two when three would leave some walks a block longer (1024 blocks: 6 -> 4 per CU)
+    assert cfg(16384, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 512
+    assert cfg(131072, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 768
     c = cfg(10, 4096, rn.BF16, 1, cus=256, blocks=2)      # fewer row blocks than workgroups wanted
     assert c["grid"] == (10 + c["rows_per_wg"] - 1) // c["rows_per_wg"]
     # forward: one row block per workgroup
