@@ -494,11 +494,26 @@ void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, int64_t cus, r
 // 8.5 against 8.8 us) and for rows of 320 vectors (2560 bf16 columns); the
 // residual-fused backward measured within noise either way and keeps it.
 constexpr int64_t kLdsMinVecs = 384, kLdsMinWalk = 8, kLdsMaxWalk = 64;
+// Rows of exactly 256 vectors (bf16 2048, fp32 1024 columns), four per
+// 1024-lane workgroup, take the opposite turn: the LDS ring wins over long
+// walks, from kLds256MinWalk rows per CU (two stages, one workgroup per CU,
+// against the register ring's two per CU; bf16 32768 x 2048 71.2 -> 69.3 us,
+// 65536 x 2048 139.7 -> 132.1, 131072 x 2048 280.6 -> 260.7, fp32 65536 x
+// 1024 138.1 -> 131.1; at 64 rows per CU within 1.1% either way, at 32 1%
+// slower).
+constexpr int64_t kLds256MinWalk = 128;
 
 
 void ladder_copy(int64_t M, int64_t N, int dtype, int is_bwd, int res, int64_t cus, rmsnorm_config *c) {
     if (!is_bwd || res || c->vector_path != 1 || cus < 1) return;
     const int64_t nvec = N * elem_size(dtype) / 16;
+    if (nvec == 256 && M >= kLds256MinWalk * cus) {
+        set_vector_shape(256, 1, kMaxVecLanes, kLdsStages, c);
+        c->copy_mode = kCopyLds;
+        c->grid = cus;
+        c->partial_rows = c->grid;
+        return;
+    }
     if (nvec < kLdsMinVecs || nvec > kMaxVecLanes || M < kLdsMinWalk * cus || M > kLdsMaxWalk * cus) return;
     const int64_t lanes = nvec <= 512 ? 512 : dtype == RMSN_F32 ? kMaxVecLanes : (nvec + 63) / 64 * 64;
     set_vector_shape(lanes, 1, (int)lanes, kLdsStages, c);
@@ -590,6 +605,15 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             const int64_t load2 = (row_blocks + 2 * cus - 1) / (2 * cus) * 2;
             if (20 * load2 <= 19 * load3) grid = 2 * cus;
         }
+        // 1024-lane workgroups at two per CU that would each walk a single
+        // row block: one per CU walking two, the second block's loads issued
+        // before the first's arithmetic, and half the partial rows (bf16 4096
+        // x 1024 10.29 -> 9.55 us, 8192 x 512 10.11 -> 9.98; fp32 2048 x 1024
+        // 10.36 -> 8.80, 4096 x 512 9.99 -> 9.27). Uneven walks of one or two
+        // blocks went either way (bf16 6144 x 1024 2.6% slower at one per CU).
+        if (c->vector_path == 1 && c->wg_threads == kMaxVecLanes && !deep && grid == 2 * cus &&
+            row_blocks <= 2 * cus)
+            grid = std::max<int64_t>(cus, (row_blocks + 1) / 2);
         // A few rows (a decode step's): one workgroup walks them all and
         // writes dW itself, with no combine launch. Faster while M * N is at
         // most kBwdSingleElems and the walk at most kBwdSinglePasses row

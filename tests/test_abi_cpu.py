@@ -530,6 +530,13 @@ def test_ladder_grid_and_workspace_shape():
     # ... two when three would leave some walks a block longer (1024 blocks: 6 -> 4 per CU)
     assert cfg(16384, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 512
     assert cfg(131072, 128, rn.BF16, 1, cus=256, blocks=8)["grid"] == 768
+    # ... 1024-lane workgroups that would each walk one row block: one per CU walking two
+    assert cfg(4096, 1024, rn.BF16, 1, cus=256, blocks=8)["grid"] == 256
+    assert cfg(6144, 1024, rn.BF16, 1, cus=256, blocks=8)["grid"] == 512
+    # ... rows of 256 vectors over long walks: the LDS-staged kernel, one per CU
+    c = cfg(65536, 2048, rn.BF16, 1, cus=256, blocks=8)
+    assert (c["copy_mode"], c["lanes_per_row"], c["wg_threads"], c["grid"], c["prefetch"]) == (1, 256, 1024, 256, 2)
+    assert cfg(16384, 2048, rn.BF16, 1, cus=256, blocks=8)["copy_mode"] == 0
     c = cfg(10, 4096, rn.BF16, 1, cus=256, blocks=2)      # fewer row blocks than workgroups wanted
     assert c["grid"] == (10 + c["rows_per_wg"] - 1) // c["rows_per_wg"]
     # forward: one row block per workgroup
