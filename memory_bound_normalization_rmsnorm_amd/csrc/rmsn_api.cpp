@@ -467,13 +467,29 @@ bool wide_long_walk(int64_t M, int dtype, int64_t cus, const rmsnorm_config *c) 
 // per row (one or two vectors per lane; the prefetching kernels with more
 // vectors spill): 1 when each workgroup walks at most kShortWalk rows, else 0.
 // Needs the grid, so it runs after ladder_grid.
-void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, int64_t cus, rmsnorm_config *c) {
+// 16-bit rows of 64 or 128 lanes, several to a 1024-lane workgroup (plain
+// call): no prefetch once each workgroup walks kNoPfMinBlocks row blocks or
+// more, where the two resident workgroups per CU already keep enough loads in
+// flight (bf16, graph-timed, against depth 1: 32768 x 512 22.4 -> 21.8 us,
+// 65536 x 512 39.6 -> 37.4, 131072 x 512 75.8 -> 70.4, 16384 x 1024 23.2 ->
+// 22.8, 65536 x 1024 71.6 -> 70.4, 131072 x 1024 141.5 -> 133.1; at a walk of
+// 2 blocks depth 1 was 0.9% faster; fp32 rows measured within 0.6% and keep
+// it).
+constexpr int64_t kNoPfMinBlocks = 4;
+
+void ladder_prefetch(int64_t M, int64_t N, int dtype, int is_bwd, int64_t cus, rmsnorm_config *c, int res = 0) {
     if (deep_prefetch(is_bwd, N, dtype, c))
         c->prefetch = 2;
     else if (is_bwd && c->vector_path == 1 && c->lanes_per_row == kMaxVecLanes && c->vecs_per_lane <= 2)
         c->prefetch = M <= kShortWalk * c->grid ? 1 : 0;
     else if (is_bwd && wide_long_walk(M, dtype, cus, c) && c->vecs_per_lane <= 3)
         c->prefetch = 0;
+    else if (is_bwd && !res && c->vector_path == 1 && c->copy_mode == 0 && elem_size(dtype) == 2 &&
+             c->wg_threads == kMaxVecLanes && c->vecs_per_lane == 1 && c->lanes_per_row >= 64 &&
+             c->lanes_per_row <= 128 && c->grid > 0) {
+        const int64_t blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
+        if ((blocks + c->grid - 1) / c->grid >= kNoPfMinBlocks) c->prefetch = 0;
+    }
 }
 
 // Backward memory path. Rows of one vector per lane from 384 to 1024 vectors
@@ -775,7 +791,7 @@ int resolve_uncached(int dev, int64_t M, int64_t N, int dtype, int is_bwd, int r
     st = occupancy(dev, k, c->wg_threads, &blocks);
     if (st != RMSN_OK) return st;
     ladder_grid(M, N, dtype, is_bwd, res, cus, blocks, c);
-    ladder_prefetch(M, N, dtype, is_bwd, cus, c);
+    ladder_prefetch(M, N, dtype, is_bwd, cus, c, res);
     ladder_copy(M, N, dtype, is_bwd, res, cus, c);
     k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;

@@ -195,10 +195,14 @@ def test_ladder_backward_grid_and_prefetch():
     # fp32, two vectors per lane: the short-walk rule; 3 or more never prefetch
     assert cfg(4096, 8192, rn.F32, 1)["prefetch"] == 1
     assert cfg(4096, 12288, rn.F32, 1)["prefetch"] == 0
-    # rows of 64..256 lanes: 1024-lane workgroups, prefetching one block
-    for N, lpr in ((512, 64), (1024, 128), (2048, 256)):
+    # rows of 64..256 lanes: 1024-lane workgroups, prefetching one block; 16-bit rows of
+    # 64 or 128 lanes stop prefetching from walks of 4 row blocks (16384 x 1024: 4)
+    for N, lpr, pf in ((512, 64, 1), (1024, 128, 0), (2048, 256, 1)):
         c = cfg(16384, N, rn.BF16, 1)
-        assert (c["lanes_per_row"], c["wg_threads"], c["rows_per_wg"], c["prefetch"]) == (lpr, 1024, 1024 // lpr, 1)
+        assert (c["lanes_per_row"], c["wg_threads"], c["rows_per_wg"], c["prefetch"]) == (lpr, 1024, 1024 // lpr, pf)
+    assert cfg(8192, 1024, rn.BF16, 1)["prefetch"] == 1           # a walk of 2 blocks
+    assert cfg(65536, 512, rn.BF16, 1)["prefetch"] == 0           # 8 blocks
+    assert cfg(65536, 512, rn.F32, 1)["prefetch"] == 1            # fp32 keeps it
     c = cfg(16384, 4096, rn.BF16, 1)
     assert (c["lanes_per_row"], c["wg_threads"], c["prefetch"], c["grid"]) == (512, 512, 2, 256)
 
