@@ -100,7 +100,9 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     per wavefront, e.g. QK-norm's 128 bf16 = 16 lanes, 4 rows per wave);
 //     one row block per workgroup (grid = row blocks), so the hardware
 //     dispatcher balances the tail; mid-size inputs of the plain call take a
-//     prefetching grid of three per compute unit instead (see ladder_grid).
+//     prefetching grid of three per compute unit instead (see ladder_grid),
+//     and 16-bit rows of 8192 columns over 32768 rows or more one row per
+//     1024-lane workgroup, two rows walked per workgroup (see fwd_row_walk).
 //   Backward: one vector per lane up to 1024 lanes per row (more lanes, fewer
 //     registers, more rows in flight); workgroups of 1024 lanes for rows of
 //     64 to 256 lanes (4 to 16 rows per pass), of the row itself otherwise
@@ -214,6 +216,9 @@ constexpr int64_t kFwdExactVecs = 5;  // forward rows that split exactly into th
 constexpr int64_t kFwdMidLo = 4, kFwdMidHi = 8, kFwdMidPerCU = 3;
 constexpr int64_t kFwdWidePerCU = 2;     // resident forward workgroups per CU with fp32 weights
 constexpr int64_t kFwdWideMinLanes = 128;  // ... for rows of at least this many lanes
+// plain forward rows of 1024 16-bit vectors over at least kFwdLongRows rows
+// walk kFwdLongWalk rows per 1024-lane workgroup (fwd_row_walk)
+constexpr int64_t kFwdLongRows = 32768, kFwdLongWalk = 2;
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
@@ -347,6 +352,22 @@ int64_t split_members(const rmsnorm_config &c) {
     return c.vector_path == kSplitPath ? c.lanes_per_row / rmsn::kWideLanes : 1;
 }
 
+// Plain forward rows of exactly 1024 16-bit vectors (8192 columns, 16-bit
+// weights) over many rows: one row per 1024-lane workgroup, each walking
+// kFwdLongWalk rows with the next row's loads issued before the current
+// row's arithmetic, instead of a row per 256-lane workgroup at 4 vectors per
+// lane. Graph-timed, rotating inputs, three buffer placements each (us):
+// bf16 32768 x 8192 176.9-178.4 -> 175.0-175.5, 65536 x 8192 362.0-373.4 ->
+// 349.5-351.3, 131072 x 8192 752.3-785.4 -> 700.2-706.2; fp16 32768 x 8192
+// 176.7-178.7 -> 175.7-176.2. At 24576 rows a tie (-0.2..-0.5%), at 16384
+// 2.5% slower, so from kFwdLongRows. Walks of 3 or 4 rows were slower than 2
+// (131072 x 8192: -8.1% and -5.5% against -9.6%); two rows of 512 lanes x 2
+// per workgroup won at 32768-49152 rows and lost at 131072 (+4.5%); rows of
+// 512 or 2048 vectors gained nothing consistent.
+bool fwd_row_walk(int64_t M, int64_t nvec, int dtype, int res) {
+    return !res && nvec == kMaxVecLanes && elem_size(dtype) == 2 && w_size(dtype) == 2 && M >= kFwdLongRows;
+}
+
 void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Align &a, int64_t cus,
                   rmsnorm_config *c) {
     const int64_t nvec = N * elem_size(dtype) / 16;
@@ -424,7 +445,10 @@ void ladder_shape(int64_t M, int64_t N, int dtype, int is_bwd, int res, const Al
     }
     vpt = (nvec + lpr - 1) / lpr;
     if (!is_bwd) {
-        set_vector_shape(lpr, vpt, rmsn::wg_for_lpr((int)lpr), 0, c);
+        if (fwd_row_walk(M, nvec, dtype, res))
+            set_vector_shape(kMaxVecLanes, 1, kMaxVecLanes, 1, c);
+        else
+            set_vector_shape(lpr, vpt, rmsn::wg_for_lpr((int)lpr), 0, c);
         return;
     }
     const int wg = (lpr >= 64 && lpr <= 256) ? kBwdGroupLanes : rmsn::wg_for_lpr((int)lpr);
@@ -540,7 +564,8 @@ void ladder_copy(int64_t M, int64_t N, int dtype, int is_bwd, int res, int64_t c
 
 // Grid. Forward: one row block per workgroup (capped at 2^20 workgroups,
 // which then loop), except mid-size inputs of the plain call (res: the
-// residual-fused kernel), which get a prefetching grid of three per CU.
+// residual-fused kernel), which get a prefetching grid of three per CU, and
+// the long walks of fwd_row_walk (half the rows).
 // Backward (persistent, one partial dW row per workgroup): see the ladder
 // comment; `blocks_per_cu` caps it at what stays resident.
 void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_cus, int blocks_per_cu,
@@ -585,6 +610,8 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             grid = row_blocks < resident ? row_blocks : resident;
             c->prefetch = 0;
         }
+        if (c->vector_path == 1 && fwd_row_walk(M, N * elem_size(dtype) / 16, dtype, res))
+            grid = std::min<int64_t>(kMaxGrid, (row_blocks + kFwdLongWalk - 1) / kFwdLongWalk);
         // Element kernels keep a workgroup per row. On rows sized by
         // elem_lanes a resident grid walking the rows was as fast or slower
         // (bf16 16384 x 12002: 138 us against 148; 16384 x 4100: 52.5 against

@@ -812,3 +812,28 @@ def test_ladder_wide_rows_long_walks(M, N, dtype, vpt, pf, grid):
     lane), prefetch off at 2-3 vectors per lane."""
     c = cfg(M, N, dtype, 1, blocks=1)
     assert (c["vector_path"], c["vecs_per_lane"], c["prefetch"], c["grid"]) == (2, vpt, pf, grid)
+
+
+@pytest.mark.parametrize("M,N,dtype,walk", [
+    (32768, 8192, rn.BF16, True), (65536, 8192, rn.F16, True), (131072, 8192, rn.BF16, True),
+    (24576, 8192, rn.BF16, False),       # fewer rows: a row per 256-lane workgroup
+    (32768, 4096, rn.F32, False),        # fp32 rows of 1024 vectors keep it
+    (32768, 8192, rn.BF16_WF32, False),  # fp32 weights: the resident grid
+    (32768, 16384, rn.BF16, False), (65536, 4096, rn.BF16, False),
+])
+def test_ladder_forward_row_walk(M, N, dtype, walk):
+    """Plain forward rows of 1024 16-bit vectors over 32768 rows or more: one
+    row per 1024-lane workgroup, each walking two rows with the next one's
+    loads issued first; everything else keeps its shape."""
+    c = cfg(M, N, dtype, 0)
+    got = (c["lanes_per_row"], c["vecs_per_lane"], c["wg_threads"], c["prefetch"], c["grid"])
+    if walk:
+        assert got == (1024, 1, 1024, 1, M // 2)
+    else:
+        assert got[0] != 1024 or got[3] == 0
+
+
+def test_ladder_forward_row_walk_grid_cap():
+    """The walk's grid stays within 2^20 workgroups; beyond that each walks more rows."""
+    c = cfg(4 << 20, 8192, rn.BF16, 0)
+    assert (c["lanes_per_row"], c["prefetch"], c["grid"]) == (1024, 1, 1 << 20)
