@@ -568,6 +568,37 @@ void ladder_copy(int64_t M, int64_t N, int dtype, int is_bwd, int res, int64_t c
 // the long walks of fwd_row_walk (half the rows).
 // Backward (persistent, one partial dW row per workgroup): see the ladder
 // comment; `blocks_per_cu` caps it at what stays resident.
+// Mid-size plain forward inputs: 1024-lane workgroups (four 256-lane row
+// blocks each), one per CU, each walking two with the second's loads issued
+// first, instead of three prefetching 256-lane workgroups per CU. Taken where
+// every workgroup walks exactly two blocks, and for 64-lane rows of one
+// vector from more than 6 blocks of 256 lanes per CU. Graph-timed, rotating
+// inputs, two buffer placements, us: walks of exactly two: bf16 8192 x 512
+// 4.92-5.08 -> 4.16-4.20, 8192 x 1024 7.21 -> 6.62-6.66, 4096 x 3072 9.83 ->
+// 8.70, 4096 x 4096 12.38-12.73 -> 11.10-11.18, 2048 x 6144 9.77-9.85 ->
+// 8.78-8.84, 2048 x 8192 12.22 -> 11.46; fp32 8192 x 256 4.90 -> 4.00-4.06,
+// 8192 x 512 7.15-7.24 -> 6.52, 4096 x 2048 12.13-12.21 -> 11.12-11.23, 2048
+// x 4096 12.65 -> 11.33-11.44; fp16 8192 x 512 4.78-4.92 -> 4.16-4.19; bf16
+// with fp32 weights 8192 x 512 4.85-4.92 -> 4.24. 64-lane rows of one vector
+// with some walks of one: bf16 6400 x 512 4.60-4.66 -> 4.00-4.02, 7168 x 512
+// 4.51 -> 3.98. Not taken: walks of one and two on wider rows (bf16 6656 x
+// 1024 +5.5%, 3584 x 4096 -1.1%, 1792 x 8192 +1.9%; at 6 blocks per CU, half
+// the workgroups walking one, +3-17%); 64-lane rows of more than two vectors
+// (bf16 8192 x 2048 +10%, fp32 8192 x 1024 +15%); shapes whose 1024-lane
+// kernel is not built for the format.
+void fwd_mid_wide(int64_t M, int dtype, int64_t cus, rmsnorm_config *c, int64_t *grid) {
+    if (c->lanes_per_row == 64 && c->vecs_per_lane > 2) return;
+    const int64_t per = kMaxVecLanes / c->lanes_per_row;  // rows per 1024-lane workgroup
+    const int64_t blocks = (M + per - 1) / per;
+    const bool even = blocks == 2 * cus;
+    const bool narrow = c->lanes_per_row == 64 && c->vecs_per_lane == 1 && 2 * blocks > 3 * cus && blocks <= 2 * cus;
+    if (!even && !narrow) return;
+    if (!rmsn::fwd_vec_kernel(dtype, 0, c->lanes_per_row, c->vecs_per_lane, (int)kMaxVecLanes, 1)) return;
+    c->wg_threads = (int32_t)kMaxVecLanes;
+    c->rows_per_wg = (int32_t)per;
+    *grid = cus;
+}
+
 void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_cus, int blocks_per_cu,
                  rmsnorm_config *c) {
     const int64_t row_blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
@@ -587,6 +618,7 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             row_blocks >= kFwdMidLo * cus && row_blocks <= kFwdMidHi * cus) {
             grid = kFwdMidPerCU * cus;
             c->prefetch = 1;
+            fwd_mid_wide(M, dtype, cus, c, &grid);
         }
         // non-temporal row loads for rows of a wavefront or more: measured with
         // inputs that are not cache-resident (the benchmark's regime), they are

@@ -433,7 +433,10 @@ def cfg(M, N, dtype, is_bwd, aligned=1, cus=256, blocks=2):
     (24, rn.BF16, 0, 4, 1),        # 3 vectors -> 4 lanes, one masked
 ])
 def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
-    c = cfg(4096, N, dtype, is_bwd)
+    # the forward at 16384 rows, beyond the mid-size grids (which may change
+    # the workgroup, not the row's shape)
+    M = 4096 if is_bwd else 16384
+    c = cfg(M, N, dtype, is_bwd)
     assert c["vector_path"] == 1
     assert (c["lanes_per_row"], c["vecs_per_lane"]) == (lpr, vpt)
     # backward rows of 64 to 256 lanes share 1024-lane workgroups
@@ -442,8 +445,8 @@ def test_ladder_shapes(N, dtype, is_bwd, lpr, vpt):
     nv = N * (4 if dtype == rn.F32 else 2) // 16
     assert c["copy_mode"] == (1 if is_bwd and 384 <= nv <= 1024 else 0)
     # the forward streams rows of a wavefront or more with non-temporal loads
-    # (4096 rows: every input here exceeds the 4 MiB threshold but N = 8, 24)
-    big = 4096 * N * (4 if dtype == rn.F32 else 2) >= 4 << 20
+    # (every forward input here reaches the 4 MiB threshold but N = 8, 24)
+    big = M * N * (4 if dtype == rn.F32 else 2) >= 4 << 20
     assert c["stream_loads"] == (1 if not is_bwd and lpr >= 64 and big else 0)
     # a decode step's few rows stay on plain loads
     assert cfg(16, N, dtype, 0)["stream_loads"] == 0
@@ -687,12 +690,16 @@ def test_ladder_forward_mid_size_grid(dtype):
     workgroups: a grid of three per CU prefetching the next block; fewer row
     blocks keep one block per workgroup without prefetch, and so do more,
     except rows of 128 lanes or more with fp32 weights and 16-bit
-    activations (two per CU)."""
+    activations (two per CU). Where one 1024-lane workgroup per CU would walk
+    exactly two blocks (fp32 2048 x 4096 and 4096 x 2048 here), that instead."""
     es = 4 if dtype == rn.F32 else 2
     w32 = dtype in (rn.BF16_WF32, rn.F16_WF32)
     for M, N in ((2048, 4096), (4096, 2048), (8192, 2048), (1024, 8192)):
         c = cfg(M, N, dtype, 0)
         rb = -(-M // c["rows_per_wg"])
+        if c["wg_threads"] == 1024 and c["lanes_per_row"] < 1024:
+            assert es == 4 and (c["grid"], c["prefetch"], rb) == (256, 1, 512), (M, N, c)
+            continue
         mid = c["wg_threads"] <= 256 and 4 * 256 <= rb <= 8 * 256
         assert (c["grid"], c["prefetch"]) == ((768, 1) if mid else (rb, 0)), (M, N, c)
         if es == 2:
@@ -837,3 +844,24 @@ def test_ladder_forward_row_walk_grid_cap():
     """The walk's grid stays within 2^20 workgroups; beyond that each walks more rows."""
     c = cfg(4 << 20, 8192, rn.BF16, 0)
     assert (c["lanes_per_row"], c["prefetch"], c["grid"]) == (1024, 1, 1 << 20)
+
+
+@pytest.mark.parametrize("M,N,dtype,wide", [
+    (8192, 512, rn.BF16, True), (8192, 1024, rn.BF16, True), (4096, 4096, rn.BF16, True),
+    (2048, 8192, rn.BF16, True), (8192, 256, rn.F32, True), (8192, 512, rn.F16, True),
+    (8192, 512, rn.BF16_WF32, True), (7168, 512, rn.BF16, True),
+    (6144, 512, rn.BF16, False),     # 6 blocks per CU: three 256-lane walkers per CU split evenly
+    (4096, 512, rn.BF16, False),
+    (8192, 2048, rn.BF16, False),    # 64-lane rows of 4 vectors keep the 256-lane grid
+    (8192, 1024, rn.F16, False),     # no 1024-lane fp16 kernel of 2 vectors per lane
+    (16384, 4096, rn.BF16, False),   # beyond the mid-size range
+])
+def test_ladder_forward_mid_wide(M, N, dtype, wide):
+    """Mid-size plain forward inputs of more than 6 row blocks per CU: one
+    prefetching 1024-lane workgroup per CU walking two blocks."""
+    c = cfg(M, N, dtype, 0)
+    if wide:
+        assert (c["wg_threads"], c["rows_per_wg"], c["prefetch"], c["grid"]) == \
+            (1024, 1024 // c["lanes_per_row"], 1, 256)
+    else:
+        assert c["wg_threads"] != 1024 or c["lanes_per_row"] == 1024

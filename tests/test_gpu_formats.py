@@ -395,16 +395,25 @@ def test_every_workgroup_row_kernel_formats(fmt, residual):
 
 @pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_forward_mid_size_grid(fmt):
-    """Mid-size inputs (4 to 8 row blocks per compute unit): the ladder's
-    forward runs a prefetching grid of three workgroups per CU, so most
-    workgroups loop over two or three row blocks; every row of y and every
-    rstd against the oracle. The residual-fused call at the same sizes keeps
-    one block per workgroup."""
+    """Mid-size inputs (4 to 8 row blocks of 256 lanes per compute unit): the
+    ladder's forward runs a prefetching grid of three 256-lane workgroups per
+    CU, or one 1024-lane workgroup per CU walking two blocks, so workgroups
+    loop over several row blocks; every row of y and every rstd against the
+    oracle. The residual-fused call at the same sizes keeps one block per
+    workgroup. Rows of 64 to 256 lanes: 8192 x 512 (16-bit) and 8192 x 256
+    (fp32) take the 1024-lane grid in every format."""
     act, wst, code = FORMATS[fmt]
-    for M, N in ((2048, 4096), (4096, 2048)):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wide_n = 256 if act == "f32" else 512
+    for M, N in ((2048, 4096), (4096, 2048), (32 * cus, wide_n)):
         c = rn.rmsnorm_query_config(M, N, code, 0)
-        assert (c.grid, c.prefetch) == (3 * torch.cuda.get_device_properties(0).multi_processor_count, 1), c.as_dict()
-        _say(f"mid-size forward {fmt} {M}x{N} grid={c.grid}")
+        if c.wg_threads == 1024:
+            assert (c.grid, c.prefetch, c.rows_per_wg) == (cus, 1, 1024 // c.lanes_per_row), c.as_dict()
+        else:
+            assert (c.grid, c.prefetch) == (3 * cus, 1), c.as_dict()
+        if N == wide_n:
+            assert c.wg_threads == 1024, c.as_dict()
+        _say(f"mid-size forward {fmt} {M}x{N} wg={c.wg_threads} grid={c.grid}")
         _, _, x, w, dy = _case(M, N, fmt, seed=9990 + M)
         eps = si.eps_f32(1e-6)
         y, rstd = gpu_fwd(x, w, eps, act)
