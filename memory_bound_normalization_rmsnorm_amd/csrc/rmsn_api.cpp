@@ -219,6 +219,9 @@ constexpr int64_t kFwdWideMinLanes = 128;  // ... for rows of at least this many
 // plain forward rows of 1024 16-bit vectors over at least kFwdLongRows rows
 // walk kFwdLongWalk rows per 1024-lane workgroup (fwd_row_walk)
 constexpr int64_t kFwdLongRows = 32768, kFwdLongWalk = 2;
+// plain forward rows of exactly 64 vectors beyond this many 256-lane row blocks
+// per CU run 16 rows per 1024-lane workgroup
+constexpr int64_t kFwdRows64MinBlocks = 16;
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
@@ -641,6 +644,23 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             if (resident > kFwdWidePerCU * cus) resident = kFwdWidePerCU * cus;
             grid = row_blocks < resident ? row_blocks : resident;
             c->prefetch = 0;
+        }
+        // Rows of exactly 64 vectors (16-bit 512, fp32 256 columns) on 64 lanes,
+        // beyond 16 row blocks of 256 lanes per CU: 16 rows per 1024-lane
+        // workgroup, one block each. Graph-timed, rotating inputs, two buffer
+        // placements, us: bf16 24576 x 512 10.88-10.95 -> 10.25-10.33, 32768 x
+        // 512 13.97-14.01 -> 12.90-12.94, 65536 x 512 24.53-24.65 -> 23.91-23.99,
+        // 131072 x 512 45.08-45.13 -> 44.38-44.51; fp32 32768 x 256 13.92 ->
+        // 13.37-13.39, 65536 x 256 24.75 -> 23.98-24.15; fp16 32768 x 512 14.01-
+        // 14.08 -> 12.98-13.03; bf16 with fp32 weights 13.27 against 14.10. At
+        // 16384 rows and below within 2% either way; rows of 48 vectors (bf16
+        // 384 columns, a quarter of the lanes idle) 2.5% slower.
+        if (!res && c->vector_path == 1 && c->lanes_per_row == 64 && c->vecs_per_lane == 1 &&
+            c->wg_threads == 256 && N * elem_size(dtype) / 16 == 64 && row_blocks > kFwdRows64MinBlocks * cus) {
+            c->wg_threads = (int32_t)kMaxVecLanes;
+            c->rows_per_wg = (int32_t)(kMaxVecLanes / 64);
+            const int64_t blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
+            grid = blocks < kMaxGrid ? blocks : kMaxGrid;
         }
         if (c->vector_path == 1 && fwd_row_walk(M, N * elem_size(dtype) / 16, dtype, res))
             grid = std::min<int64_t>(kMaxGrid, (row_blocks + kFwdLongWalk - 1) / kFwdLongWalk);

@@ -865,3 +865,21 @@ def test_ladder_forward_mid_wide(M, N, dtype, wide):
             (1024, 1024 // c["lanes_per_row"], 1, 256)
     else:
         assert c["wg_threads"] != 1024 or c["lanes_per_row"] == 1024
+
+
+@pytest.mark.parametrize("M,N,dtype,wide", [
+    (24576, 512, rn.BF16, True), (32768, 512, rn.F16, True), (131072, 512, rn.BF16, True),
+    (32768, 256, rn.F32, True), (32768, 512, rn.BF16_WF32, True),
+    (16384, 512, rn.BF16, False),   # 16 blocks of 256 lanes per CU: a tie, not taken
+    (32768, 384, rn.BF16, False),   # 48 vectors on 64 lanes
+    (32768, 1024, rn.BF16, False),  # two vectors per lane
+])
+def test_ladder_forward_rows64(M, N, dtype, wide):
+    """Plain forward rows of exactly 64 vectors beyond 16 row blocks of 256
+    lanes per CU: 16 rows per 1024-lane workgroup, one block each."""
+    c = cfg(M, N, dtype, 0)
+    assert c["lanes_per_row"] == 64
+    if wide:
+        assert (c["wg_threads"], c["rows_per_wg"], c["prefetch"], c["grid"]) == (1024, 16, 0, M // 16)
+    else:
+        assert c["wg_threads"] == 256
