@@ -1030,11 +1030,19 @@ int explicit_config(const rmsnorm_config *req, int64_t M, int64_t N, int dtype, 
     }
     const void *k = kernel_for(*c, N, dtype, is_bwd, res);
     if (!k) return RMSN_ECONFIG;
+    // ladder_grid fills the derived fields; its rules may also reshape the
+    // ladder's own choice (the workgroup of some forward rows), which an
+    // explicit configuration does not take: the kernel above was chosen for
+    // the requested workgroup, and launching it on another would be refused
+    const int32_t wg = c->wg_threads, rows = c->rows_per_wg;
     ladder_grid(M, N, dtype, is_bwd, res, 1, 1, c);
+    c->wg_threads = wg;
+    c->rows_per_wg = rows;
     c->grid = req->grid;
     c->prefetch = req->vector_path ? req->prefetch : 0;  // as requested (the kernel above was chosen by it)
     c->partial_rows = req->grid / split_members(*c);
     c->stream_loads = req->vector_path ? req->stream_loads : 0;
+    if (kernel_for(*c, N, dtype, is_bwd, res) != k) return RMSN_ECONFIG;
     *fn = k;
     return RMSN_OK;
 }

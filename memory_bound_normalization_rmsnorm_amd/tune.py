@@ -34,7 +34,7 @@ import time
 
 import torch
 
-from . import (BF16, BF16_WF32, F16, F16_WF32, F32, LIB_PATH, RmsnormError, lib, rmsnorm_bwd_with_config,
+from . import (BF16, BF16_WF32, ECONFIG, F16, F16_WF32, F32, LIB_PATH, RmsnormError, lib, rmsnorm_bwd_with_config,
                rmsnorm_build_info, rmsnorm_config, rmsnorm_fwd_with_config, rmsnorm_query_config)
 
 # activation element bytes, activation torch dtype and weight torch dtype of each format
@@ -325,7 +325,9 @@ def tune(M: int, N: int, dtype: int, is_bwd: int, budget_s: float = 60.0, K: int
             break
         try:
             us = bench.time_us(cfg, is_bwd, K=K)
-        except RmsnormError:
+        except RmsnormError as e:
+            if e.status != ECONFIG:  # a HIP runtime error is not a shape that is not built
+                raise
             continue
         results.append((us, cfg))
         if verbose:

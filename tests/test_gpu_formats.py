@@ -428,6 +428,34 @@ def test_forward_mid_size_grid(fmt):
         check_rstd(rstd2, orr2)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
+def test_forward_explicit_config_keeps_workgroup(fmt):
+    """An explicit forward configuration runs on the workgroup it names, also
+    where the ladder's grid rules would reshape the ladder's own choice (rows
+    of exactly 64 vectors beyond 16 row blocks of 256 lanes per CU, and
+    mid-size inputs that take one 1024-lane workgroup per CU): the same rows
+    on 256- and on 1024-lane workgroups, each against the oracle, and the
+    ladder's own configuration passed back explicitly."""
+    act, wst, code = FORMATS[fmt]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 256 if act == "f32" else 512  # 64 vectors: 64 lanes of one vector
+    for M in (32 * cus, 128 * cus):
+        _, _, x, w, _ = _case(M, N, fmt, seed=9970 + M)
+        eps = si.eps_f32(1e-6)
+        oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
+        lad = rn.rmsnorm_query_config(M, N, code, 0)
+        variants = [("ladder", lad)]
+        for wg in (256, 1024):
+            c = rn.rmsnorm_config(vector_path=1, lanes_per_row=64, vecs_per_lane=1, wg_threads=wg,
+                                  prefetch=0, stream_loads=1, grid=-(-M // (wg // 64)))
+            variants.append((f"wg{wg}", c))
+        for name, c in variants:
+            _say(f"explicit forward {fmt} {M}x{N} {name} wg={c.wg_threads} grid={c.grid}")
+            y, rstd = gpu_fwd(x, w, eps, act, cfg=c)
+            check_rows(y, oy, act, f"y ({name})")
+            check_rstd(rstd, orr)
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS)
 @pytest.mark.parametrize("residual", [False, True])
 def test_every_element_kernel(fmt, residual):
