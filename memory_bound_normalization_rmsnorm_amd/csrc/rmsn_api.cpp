@@ -222,6 +222,9 @@ constexpr int64_t kFwdLongRows = 32768, kFwdLongWalk = 2;
 // plain forward rows of exactly 64 vectors beyond this many 256-lane row blocks
 // per CU run 16 rows per 1024-lane workgroup
 constexpr int64_t kFwdRows64MinBlocks = 16;
+// plain forward 64-lane rows of one (two) vectors up to this many 256-lane row
+// blocks per CU, beyond the mid-size range, run 512-lane workgroups (fwd_rows64_512)
+constexpr int64_t kFwd512MaxBlocks1 = 20, kFwd512MaxBlocks2 = 16;
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
@@ -602,6 +605,30 @@ void fwd_mid_wide(int64_t M, int dtype, int64_t cus, rmsnorm_config *c, int64_t 
     *grid = cus;
 }
 
+// 64-lane rows of one or two vectors just beyond the mid-size range: 512-lane
+// workgroups (8 rows each), three per CU, each loading its next block ahead.
+// Graph-timed, rotating inputs, two buffer placements, against one block per
+// 256-lane workgroup (us; n blocks of 256 lanes per CU): bf16 x 512 at 10,
+// 12, 14, 16: 5.46-5.49 -> 4.58-4.59, 6.40-6.43 -> 5.38-5.39, 7.31-7.36 ->
+// 6.22-6.25, 7.81-7.82 -> 6.90-6.91; x 1024: 8.81-8.84 -> 7.87-7.91,
+// 10.42-10.46 -> 9.58-9.64, 11.64-11.65 -> 10.92-10.99, 12.85-12.87 ->
+// 12.01-12.05; fp32 x 256: -10% to -17%, x 512: -3% to -9%. One-vector rows
+// at 18 and 20 against the 1024-lane grid of rows of 64 vectors: 5.6-7.7%
+// faster; at 24 mixed (bf16 +1.2%, fp32 -4%). Two-vector rows from 18:
+// within 1.4% either way. Rows of four vectors lose (bf16 8192 x 2048 +7%
+// at two per CU). Only where the format has the kernel (bf16, fp32).
+bool fwd_rows64_512(int dtype, int64_t cus, int64_t row_blocks, rmsnorm_config *c, int64_t *grid) {
+    if (c->lanes_per_row != 64 || c->vecs_per_lane > 2 || c->wg_threads != 256) return false;
+    const int64_t hi = c->vecs_per_lane == 1 ? kFwd512MaxBlocks1 : kFwd512MaxBlocks2;
+    if (row_blocks <= kFwdMidHi * cus || row_blocks > hi * cus) return false;
+    if (!rmsn::fwd_vec_kernel(dtype, 0, 64, c->vecs_per_lane, 512, 1)) return false;
+    c->wg_threads = 512;
+    c->rows_per_wg = 512 / 64;
+    c->prefetch = 1;
+    *grid = kFwdMidPerCU * cus;
+    return true;
+}
+
 void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_cus, int blocks_per_cu,
                  rmsnorm_config *c) {
     const int64_t row_blocks = (M + c->rows_per_wg - 1) / c->rows_per_wg;
@@ -645,6 +672,7 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             grid = row_blocks < resident ? row_blocks : resident;
             c->prefetch = 0;
         }
+        if (!res && c->vector_path == 1) fwd_rows64_512(dtype, cus, row_blocks, c, &grid);
         // Rows of exactly 64 vectors (16-bit 512, fp32 256 columns) on 64 lanes,
         // beyond 16 row blocks of 256 lanes per CU: 16 rows per 1024-lane
         // workgroup, one block each. Graph-timed, rotating inputs, two buffer
@@ -654,7 +682,9 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
         // 13.37-13.39, 65536 x 256 24.75 -> 23.98-24.15; fp16 32768 x 512 14.01-
         // 14.08 -> 12.98-13.03; bf16 with fp32 weights 13.27 against 14.10. At
         // 16384 rows and below within 2% either way; rows of 48 vectors (bf16
-        // 384 columns, a quarter of the lanes idle) 2.5% slower.
+        // 384 columns, a quarter of the lanes idle) 2.5% slower. Where the
+        // 512-lane grid above is built (bf16, fp32) it takes these rows up to 20
+        // blocks per CU.
         if (!res && c->vector_path == 1 && c->lanes_per_row == 64 && c->vecs_per_lane == 1 &&
             c->wg_threads == 256 && N * elem_size(dtype) / 16 == 64 && row_blocks > kFwdRows64MinBlocks * cus) {
             c->wg_threads = (int32_t)kMaxVecLanes;

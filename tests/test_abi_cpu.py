@@ -870,7 +870,7 @@ def test_ladder_forward_mid_wide(M, N, dtype, wide):
 @pytest.mark.parametrize("M,N,dtype,wide", [
     (24576, 512, rn.BF16, True), (32768, 512, rn.F16, True), (131072, 512, rn.BF16, True),
     (32768, 256, rn.F32, True), (32768, 512, rn.BF16_WF32, True),
-    (16384, 512, rn.BF16, False),   # 16 blocks of 256 lanes per CU: a tie, not taken
+    (16384, 512, rn.F16, False),    # 16 blocks of 256 lanes per CU: a tie, not taken
     (32768, 384, rn.BF16, False),   # 48 vectors on 64 lanes
     (32768, 1024, rn.BF16, False),  # two vectors per lane
 ])
@@ -883,3 +883,25 @@ def test_ladder_forward_rows64(M, N, dtype, wide):
         assert (c["wg_threads"], c["rows_per_wg"], c["prefetch"], c["grid"]) == (1024, 16, 0, M // 16)
     else:
         assert c["wg_threads"] == 256
+
+
+@pytest.mark.parametrize("M,N,dtype,wide", [
+    (10240, 512, rn.BF16, True), (16384, 512, rn.BF16, True), (20480, 512, rn.BF16, True),
+    (16384, 1024, rn.BF16, True), (12288, 256, rn.F32, True), (16384, 512, rn.F32, True),
+    (24576, 512, rn.BF16, False),   # beyond 20 blocks per CU: the 1024-lane grid
+    (18432, 1024, rn.BF16, False),  # two vectors per lane: up to 16 blocks per CU
+    (16384, 2048, rn.BF16, False),  # four vectors per lane
+    (16384, 512, rn.F16, False),    # no 512-lane fp16 kernel
+    (8192, 512, rn.BF16, False),    # the mid-size range (its 1024-lane grid)
+])
+def test_ladder_forward_rows64_512(M, N, dtype, wide):
+    """64-lane forward rows of one vector from 9 to 20 row blocks of 256 lanes
+    per CU (of two vectors: to 16): 512-lane workgroups, three per CU,
+    prefetching."""
+    c = cfg(M, N, dtype, 0)
+    assert c["lanes_per_row"] == 64
+    got = (c["wg_threads"], c["rows_per_wg"], c["prefetch"], c["grid"])
+    if wide:
+        assert got == (512, 8, 1, 768)
+    else:
+        assert got[0] != 512

@@ -432,14 +432,15 @@ def test_forward_mid_size_grid(fmt):
 def test_forward_explicit_config_keeps_workgroup(fmt):
     """An explicit forward configuration runs on the workgroup it names, also
     where the ladder's grid rules would reshape the ladder's own choice (rows
-    of exactly 64 vectors beyond 16 row blocks of 256 lanes per CU, and
-    mid-size inputs that take one 1024-lane workgroup per CU): the same rows
+    of exactly 64 vectors on 512-lane workgroups at 16 row blocks of 256 lanes
+    per CU and on 1024-lane ones beyond 20, and mid-size inputs that take one
+    1024-lane workgroup per CU): the same rows
     on 256- and on 1024-lane workgroups, each against the oracle, and the
     ladder's own configuration passed back explicitly."""
     act, wst, code = FORMATS[fmt]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     N = 256 if act == "f32" else 512  # 64 vectors: 64 lanes of one vector
-    for M in (32 * cus, 128 * cus):
+    for M in (32 * cus, 64 * cus, 128 * cus):
         _, _, x, w, _ = _case(M, N, fmt, seed=9970 + M)
         eps = si.eps_f32(1e-6)
         oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
