@@ -225,6 +225,9 @@ constexpr int64_t kFwdRows64MinBlocks = 16;
 // plain forward 64-lane rows of one (two) vectors up to this many 256-lane row
 // blocks per CU, beyond the mid-size range, run 512-lane workgroups (fwd_rows64_512)
 constexpr int64_t kFwd512MaxBlocks1 = 20, kFwd512MaxBlocks2 = 16;
+// plain forward rows narrower than a wavefront, beyond the mid-size range up to this
+// many row blocks per CU: a prefetching grid of kFwdNarrowPerCU per CU
+constexpr int64_t kFwdNarrowMaxBlocks = 24, kFwdNarrowPerCU = 4;
 constexpr int kBwdGroupLanes = 1024;  // backward workgroup for rows of 64 to 256 lanes
 constexpr int64_t kPartialShare = 6;  // partial-row traffic at most 1/kPartialShare of the bytes
 constexpr int64_t kShortWalk = 16;    // rows per workgroup up to which 1024-lane rows prefetch
@@ -673,6 +676,23 @@ void ladder_grid(int64_t M, int64_t N, int dtype, int is_bwd, int res, int num_c
             c->prefetch = 0;
         }
         if (!res && c->vector_path == 1) fwd_rows64_512(dtype, cus, row_blocks, c, &grid);
+        // Rows narrower than a wavefront (one vector per lane, 8 to 32 lanes,
+        // several rows per 256-lane workgroup) from 9 to 24 row blocks per CU:
+        // four workgroups per CU, each loading its next block ahead. Graph-timed,
+        // rotating inputs, two buffer placements, against one block per
+        // workgroup: 4.5-10.5% faster at every one of 10, 12, 14, 16, 18, 20
+        // and 24 blocks per CU for bf16 x 64, x 128, x 256 and fp32 x 64 (bf16
+        // 65536 x 128 6.61-6.64 -> 6.18-6.21 us, 73728 x 128 7.45-7.50 ->
+        // 6.71-6.72; fp32 73728 x 64 7.37-7.38 -> 6.65-6.66); at 32 and 64
+        // blocks per CU within 2% either way, at 8 per CU 6-7% slower.
+        // fp16 takes it unmeasured (the bf16 kernel with another conversion);
+        // fp32 weights with 16-bit rows and the residual add keep their grids.
+        if (!res && c->vector_path == 1 && c->lanes_per_row < 64 && c->wg_threads == 256 &&
+            w_size(dtype) == elem_size(dtype) && row_blocks > kFwdMidHi * cus &&
+            row_blocks <= kFwdNarrowMaxBlocks * cus) {
+            grid = kFwdNarrowPerCU * cus;
+            c->prefetch = 1;
+        }
         // Rows of exactly 64 vectors (16-bit 512, fp32 256 columns) on 64 lanes,
         // beyond 16 row blocks of 256 lanes per CU: 16 rows per 1024-lane
         // workgroup, one block each. Graph-timed, rotating inputs, two buffer

@@ -905,3 +905,23 @@ def test_ladder_forward_rows64_512(M, N, dtype, wide):
         assert got == (512, 8, 1, 768)
     else:
         assert got[0] != 512
+
+
+@pytest.mark.parametrize("M,N,dtype,taken", [
+    (40960, 128, rn.BF16, True), (65536, 128, rn.BF16, True), (98304, 128, rn.BF16, True),
+    (131072, 64, rn.BF16, True), (65536, 64, rn.F32, True), (32768, 256, rn.BF16, True), (65536, 128, rn.F16, True),
+    (32768, 128, rn.BF16, False),     # 8 blocks per CU
+    (131072, 128, rn.BF16, False),    # 32 blocks per CU
+    (1 << 20, 128, rn.BF16, False),   # QK-norm rows
+    (65536, 128, rn.BF16_WF32, False),
+])
+def test_ladder_forward_narrow_grid(M, N, dtype, taken):
+    """Forward rows narrower than a wavefront from 9 to 24 row blocks per CU:
+    a prefetching grid of four workgroups per CU."""
+    c = cfg(M, N, dtype, 0)
+    assert c["lanes_per_row"] < 64 and c["wg_threads"] == 256
+    rb = -(-M // c["rows_per_wg"])
+    if taken:
+        assert (c["grid"], c["prefetch"]) == (1024, 1)
+    else:
+        assert (c["grid"], c["prefetch"]) == (rb, 0)

@@ -429,6 +429,26 @@ def test_forward_mid_size_grid(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
+def test_forward_narrow_rows_grid(fmt):
+    """Rows narrower than a wavefront at 16 row blocks per CU: the ladder's
+    prefetching grid of four workgroups per CU, each walking four blocks;
+    every row of y and every rstd against the oracle."""
+    act, wst, code = FORMATS[fmt]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 64 if act == "f32" else 128  # 16 vectors: 16 lanes, 16 rows per workgroup
+    M = 16 * 16 * cus
+    c = rn.rmsnorm_query_config(M, N, code, 0)
+    assert (c.lanes_per_row, c.grid, c.prefetch) == (16, 4 * cus, 1), c.as_dict()
+    _say(f"narrow forward {fmt} {M}x{N} grid={c.grid}")
+    _, _, x, w, _ = _case(M, N, fmt, seed=9960)
+    eps = si.eps_f32(1e-6)
+    y, rstd = gpu_fwd(x, w, eps, act)
+    oy, orr = oracle.fwd(x, w, eps, act, wdtype=wst)
+    check_rows(y, oy, act, "y (narrow grid)")
+    check_rstd(rstd, orr)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
 def test_forward_explicit_config_keeps_workgroup(fmt):
     """An explicit forward configuration runs on the workgroup it names, also
     where the ladder's grid rules would reshape the ladder's own choice (rows
