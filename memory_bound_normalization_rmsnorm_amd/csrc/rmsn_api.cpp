@@ -100,9 +100,15 @@ int check_shape(int64_t M, int64_t N, int dtype) {
 //     per wavefront, e.g. QK-norm's 128 bf16 = 16 lanes, 4 rows per wave);
 //     one row block per workgroup (grid = row blocks), so the hardware
 //     dispatcher balances the tail; mid-size inputs of the plain call take a
-//     prefetching grid of three per compute unit instead (see ladder_grid),
-//     and 16-bit rows of 8192 columns over 32768 rows or more one row per
-//     1024-lane workgroup, two rows walked per workgroup (see fwd_row_walk).
+//     prefetching grid of three per compute unit instead (see ladder_grid;
+//     one 1024-lane workgroup per CU where each would walk exactly two
+//     blocks, see fwd_mid_wide), as do 64-lane rows of one or two vectors a
+//     little beyond that range on 512-lane workgroups (fwd_rows64_512); rows
+//     narrower than a wavefront from 9 to 24 blocks per CU take four per CU,
+//     rows of exactly 64 vectors further out 16 rows per 1024-lane
+//     workgroup, and 16-bit rows of 8192 columns over 32768 rows or more one
+//     row per 1024-lane workgroup, two rows walked per workgroup (see
+//     fwd_row_walk).
 //   Backward: one vector per lane up to 1024 lanes per row (more lanes, fewer
 //     registers, more rows in flight); workgroups of 1024 lanes for rows of
 //     64 to 256 lanes (4 to 16 rows per pass), of the row itself otherwise
